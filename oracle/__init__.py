@@ -1,0 +1,163 @@
+"""Python face of the CPU oracle (``oracle.c``) for MoE mul_mat_id.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the GPU library never does, and the
+two share no code. Every function takes and returns numpy arrays; results are
+float64.
+
+Parity of this oracle is pinned in tests/test_oracle.py against brute force,
+invariants, numpy/torch library routines and hand-derived fixtures.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, Q8_0 = 0, 1, 2
+_TYPES = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2 -fopenmp, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", tmp,
+                               _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        _lib.oracle_half_to_double.restype = ctypes.c_double
+        _lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        _lib.oracle_bf16_to_double.restype = ctypes.c_double
+        _lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        _lib.oracle_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P]
+        _lib.oracle_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P]
+        _lib.oracle_mul_mat_id.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, ctypes.c_int, I32,
+                                           P, I64, I32, P, P]
+        _lib.oracle_ffn.argtypes = ([ctypes.c_int] + [P] * 6 + [I64] * 3 + [P] * 6 + [I64] * 2 +
+                                    [P, ctypes.c_int, P, P, I64, I32, P])
+        for f in (_lib.oracle_dequant, _lib.oracle_row_ids, _lib.oracle_mul_mat_id, _lib.oracle_ffn):
+            f.restype = ctypes.c_int
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def half_to_double(bits: int) -> float:
+    return lib().oracle_half_to_double(int(bits) & 0xFFFF)
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(int(bits) & 0xFFFF)
+
+
+def dequant(qs_or_w, d=None) -> np.ndarray:
+    """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]) or widen
+    float32 weights, to float64 of the same shape."""
+    a = np.asarray(qs_or_w)
+    shape = a.shape
+    a3 = a.reshape((-1,) + shape[-2:])
+    out = np.empty(a3.shape, np.float64)
+    if d is None:
+        w = _c(a3, np.float32)
+        rc = lib().oracle_dequant(F32, _p(w), None, a3.shape[0], a3.shape[1], a3.shape[2], _p(out))
+    else:
+        q = _c(a3, np.int8)
+        s = _c(np.asarray(d).view(np.uint16).reshape(a3.shape[0], a3.shape[1], -1), np.uint16)
+        rc = lib().oracle_dequant(Q8_0, _p(q), _p(s), a3.shape[0], a3.shape[1], a3.shape[2], _p(out))
+    if rc:
+        raise ValueError("oracle_dequant rejected its arguments (%d)" % rc)
+    return out.reshape(shape)
+
+
+def row_ids(ids: np.ndarray, n_experts: int, src1_rows_per_token: int = 1):
+    """(ids_src1, ids_dst, expert_bounds) for ids int32 [T][k]."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    s1 = np.empty(T * k, np.int32)
+    dd = np.empty(T * k, np.int32)
+    b = np.empty(n_experts + 1, np.int32)
+    rc = lib().oracle_row_ids(_p(ids), T, k, n_experts, src1_rows_per_token, _p(s1), _p(dd), _p(b))
+    if rc:
+        raise ValueError("oracle_row_ids rejected its arguments (%d)" % rc)
+    return s1, dd, b
+
+
+def _weights(qs_or_w, d):
+    if d is None:
+        return F32, _c(qs_or_w, np.float32), None
+    return Q8_0, _c(qs_or_w, np.int8), _c(np.asarray(d).view(np.uint16), np.uint16)
+
+
+def mul_mat_id(w, w_d, src1, src1_type: str, ids, route_w=None, src1_rows_per_token: int = 1):
+    """Per-slot dst float64 [T][k][N], or the route_w-weighted [T][N].
+    ``w`` is float32 [E][N][K] (w_d None) or Q8_0 qs [E][N][K] with scales w_d.
+    ``src1`` is [T*B][K] (float32, or bf16 bits as uint16)."""
+    wt, wq, ws = _weights(w, w_d)
+    E, N, K = wq.shape
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    st = _TYPES[src1_type]
+    src = _c(src1, np.float32 if st == F32 else np.uint16)
+    rw = _c(route_w, np.float32)
+    out = np.empty((T, N) if rw is not None else (T, k, N), np.float64)
+    rc = lib().oracle_mul_mat_id(wt, _p(wq), _p(ws), E, N, K, _p(src), st, src1_rows_per_token,
+                                 _p(ids), T, k, _p(rw), _p(out))
+    if rc:
+        raise ValueError("oracle_mul_mat_id rejected its arguments (%d)" % rc)
+    return out
+
+
+def ffn(inp: dict, token_rows=None) -> np.ndarray:
+    """Fused MoE FFN output float64 [T][n_embd] for a workload dict from ``synth``.
+    ``token_rows`` (optional index array) restricts the computation to those tokens;
+    every token's output depends only on its own row of x, ids and route_w."""
+    ids, rw, x = inp["ids"], inp["route_w"], inp["x"]
+    if token_rows is not None:
+        token_rows = np.asarray(token_rows)
+        ids, rw, x = ids[token_rows], rw[token_rows], x[token_rows]
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    xt = _TYPES[inp.get("xtype", "bf16")]
+    x = _c(x, np.float32 if xt == F32 else np.uint16)
+    rw = _c(rw, np.float32)
+    wt, g, gs = _weights(inp["gate_qs"], inp.get("gate_d"))
+    _, u, us = _weights(inp["up_qs"], inp.get("up_d"))
+    _, dn, dns = _weights(inp["down_qs"], inp.get("down_d"))
+    E, n_ff, n_embd = g.shape
+    S, n_ff_sh = 0, 0
+    sg = sgs = su = sus = sd = sds = None
+    if inp.get("sh_gate_qs") is not None:
+        _, sg, sgs = _weights(inp["sh_gate_qs"], inp.get("sh_gate_d"))
+        _, su, sus = _weights(inp["sh_up_qs"], inp.get("sh_up_d"))
+        _, sd, sds = _weights(inp["sh_down_qs"], inp.get("sh_down_d"))
+        S, n_ff_sh = sg.shape[0], sg.shape[1]
+    out = np.empty((T, n_embd), np.float64)
+    rc = lib().oracle_ffn(wt, _p(g), _p(gs), _p(u), _p(us), _p(dn), _p(dns), E, n_ff, n_embd,
+                          _p(sg), _p(sgs), _p(su), _p(sus), _p(sd), _p(sds), S, n_ff_sh,
+                          _p(x), xt, _p(ids), _p(rw), T, k, _p(out))
+    if rc:
+        raise ValueError("oracle_ffn rejected its arguments (%d)" % rc)
+    return out

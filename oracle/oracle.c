@@ -1,0 +1,321 @@
+/*
+ * CPU oracle for the MoE indirect matrix multiplication (mul_mat_id).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load
+ * this file or the library built from it; only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg do. It shares no code, header, table or
+ * helper with the GPU library.
+ *
+ * What it computes is the plain definition of the operation, in float64, with a
+ * fixed summation order and nothing blocked, fused or reordered:
+ *
+ *  - The op has three inputs: stacked expert weights, activations, and an integer
+ *    ids table naming which experts each token uses; each token is multiplied only
+ *    by the weight matrices of the experts the ids name for it
+ *    ("CUDA: better MoE implementation" (ik_llama.cpp PR #283 write-up), section 1.2).
+ *  - The fast path first builds three maps from ids -- a reordering of the
+ *    flattened src1 rows so rows are grouped by expert, the same reordering
+ *    applied to dst, and each expert's bounds in the reordered buffer -- and then
+ *    does the reorder and reduction by those maps (same page, section 2.1 and
+ *    the summary in section 6). Here the maps are built by plain enumeration.
+ *  - Experts may be Q8_0-quantized (section 2.1 names Q8_0): blocks of 32 int8
+ *    values sharing one fp16 scale, value = d * q. Dequantization is exact in
+ *    float64 (an 11-bit by 8-bit product).
+ *  - The fused MoE FFN applies gate and up projections, SiLU(gate) * up, then the
+ *    down projection (section 4.2 names the fused up/gate MoE forward), weights each
+ *    routed slot's result by its routing weight and adds always-on shared experts,
+ *    which are computed in the same operation ("CUDA: fuse shared experts into
+ *    MMVQ", release b11370; the TensorSharp MoE-offload page lists the shared
+ *    expert among the tensors that stay on the accelerator).
+ *
+ * Readings where the pages are silent (stated once here, used below):
+ *  - Weights are row-major W[E][rows][cols] (ggml ne order, fastest dimension last
+ *    here); Q8_0 scales are a separate fp16 array d[E][rows][cols/32].
+ *  - src1 is [T][B][K] with B = 1 (every slot reads the token's row) or B = k (one
+ *    row per slot); ids is [T][k].
+ *  - Inside an expert segment, rows are ordered by token index then slot index.
+ *  - An id outside [0, E) selects no expert: that slot's output row is zero and it
+ *    contributes nothing; its map entries go after all expert segments, in
+ *    (token, slot) order, so the maps stay a permutation.
+ *  - SiLU(z) = z / (1 + exp(-z)); shared experts have weight 1 and are added after
+ *    the routed slots, in index order.
+ *
+ * Types: 0 = float32, 1 = bfloat16 (uint16 bit pattern), 2 = Q8_0 (int8 + fp16).
+ * All entry points return 0 on success and a negative value on bad arguments.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_Q8_0 2
+
+/* IEEE binary16 -> double, written from the format's definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits). */
+double oracle_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int fr = h & 0x3ff;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -24); /* subnormal: fr * 2^-14 * 2^-10 */
+    else if (ex == 31)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr + 1024), ex - 25); /* (1 + fr/1024) * 2^(ex-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double: the upper half of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* One weight element w(e, n, c) of a stacked matrix, as a double. */
+static double weight_at(int type, const void *data, const void *scales, int64_t rows,
+                        int64_t cols, int64_t e, int64_t n, int64_t c) {
+    int64_t idx = (e * rows + n) * cols + c;
+    if (type == OR_F32) return (double)((const float *)data)[idx];
+    /* Q8_0: value = d * q, one fp16 scale per 32 consecutive columns of a row. */
+    int8_t q = ((const int8_t *)data)[idx];
+    uint16_t d = ((const uint16_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
+    return oracle_half_to_double(d) * (double)q;
+}
+
+/* Activation element as a double. */
+static double act_at(int type, const void *src, int64_t idx) {
+    if (type == OR_F32) return (double)((const float *)src)[idx];
+    return oracle_bf16_to_double(((const uint16_t *)src)[idx]);
+}
+
+/* Dequantize (or widen) a whole stack of matrices into out[n_mat*rows*cols]. */
+int oracle_dequant(int type, const void *data, const void *scales, int64_t n_mat, int64_t rows,
+                   int64_t cols, double *out) {
+    if (!data || !out || (type != OR_F32 && type != OR_Q8_0)) return -1;
+    if (type == OR_Q8_0 && (!scales || cols % 32)) return -1;
+    for (int64_t e = 0; e < n_mat; e++)
+        for (int64_t n = 0; n < rows; n++)
+            for (int64_t c = 0; c < cols; c++)
+                out[(e * rows + n) * cols + c] = weight_at(type, data, scales, rows, cols, e, n, c);
+    return 0;
+}
+
+/*
+ * The three maps of section 2.1, built by enumeration:
+ *   for each expert e ascending: bounds[e] = running count; then every (t, s) with
+ *   ids[t][s] == e, t ascending then s ascending, takes the next slot j, with
+ *   ids_src1[j] = t*B + (s mod B) (the src1 row it reads) and ids_dst[j] = t*k + s
+ *   (the dst row it writes).
+ *   bounds[E] = number of valid entries; entries with ids outside [0, E) follow.
+ */
+int oracle_row_ids(const int32_t *ids, int64_t T, int32_t k, int32_t E, int32_t B,
+                   int32_t *ids_src1, int32_t *ids_dst, int32_t *bounds) {
+    if (!ids || !ids_src1 || !ids_dst || !bounds || T < 0 || k <= 0 || E <= 0) return -1;
+    if (B != 1 && B != k) return -1;
+    int64_t j = 0;
+    for (int32_t e = 0; e < E; e++) {
+        bounds[e] = (int32_t)j;
+        for (int64_t t = 0; t < T; t++)
+            for (int32_t s = 0; s < k; s++)
+                if (ids[t * k + s] == e) {
+                    ids_src1[j] = (int32_t)(t * B + s % B);
+                    ids_dst[j] = (int32_t)(t * k + s);
+                    j++;
+                }
+    }
+    bounds[E] = (int32_t)j;
+    for (int64_t t = 0; t < T; t++)
+        for (int32_t s = 0; s < k; s++) {
+            int32_t e = ids[t * k + s];
+            if (e < 0 || e >= E) {
+                ids_src1[j] = (int32_t)(t * B + s % B);
+                ids_dst[j] = (int32_t)(t * k + s);
+                j++;
+            }
+        }
+    return 0;
+}
+
+/*
+ * y[n] = sum over c ascending of w(e, n, c) * a[c], for n in [0, rows).
+ * Each weight is formed as d * q (exact) before it multiplies a[c]; four rows are
+ * accumulated side by side only to keep the CPU busy -- every row still has its
+ * own accumulator and its own ascending-c order.
+ */
+static void matvec(int type, const void *data, const void *scales, int64_t rows, int64_t cols,
+                   int64_t e, const double *a, double *y) {
+    int64_t n = 0;
+    if (type == OR_F32) {
+        const float *w = (const float *)data + e * rows * cols;
+        for (; n < rows; n++) {
+            const float *wr = w + n * cols;
+            double acc = 0.0;
+            for (int64_t c = 0; c < cols; c++) acc += (double)wr[c] * a[c];
+            y[n] = acc;
+        }
+        return;
+    }
+    const int8_t *q = (const int8_t *)data + e * rows * cols;
+    const uint16_t *ds = (const uint16_t *)scales + e * rows * (cols / 32);
+    int64_t nb = cols / 32;
+    for (; n + 4 <= rows; n += 4) {
+        const int8_t *q0 = q + n * cols, *q1 = q0 + cols, *q2 = q1 + cols, *q3 = q2 + cols;
+        const uint16_t *d0 = ds + n * nb, *d1 = d0 + nb, *d2 = d1 + nb, *d3 = d2 + nb;
+        double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+        for (int64_t b = 0; b < nb; b++) {
+            double s0 = oracle_half_to_double(d0[b]), s1 = oracle_half_to_double(d1[b]);
+            double s2 = oracle_half_to_double(d2[b]), s3 = oracle_half_to_double(d3[b]);
+            for (int64_t c = b * 32; c < b * 32 + 32; c++) {
+                acc0 += (s0 * (double)q0[c]) * a[c];
+                acc1 += (s1 * (double)q1[c]) * a[c];
+                acc2 += (s2 * (double)q2[c]) * a[c];
+                acc3 += (s3 * (double)q3[c]) * a[c];
+            }
+        }
+        y[n] = acc0;
+        y[n + 1] = acc1;
+        y[n + 2] = acc2;
+        y[n + 3] = acc3;
+    }
+    for (; n < rows; n++) {
+        const int8_t *qr = q + n * cols;
+        const uint16_t *dr = ds + n * nb;
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; b++) {
+            double sc = oracle_half_to_double(dr[b]);
+            for (int64_t c = b * 32; c < b * 32 + 32; c++) acc += (sc * (double)qr[c]) * a[c];
+        }
+        y[n] = acc;
+    }
+}
+
+/*
+ * mul_mat_id (section 1.2): dst[t][s][n] = sum_c W[ids[t][s]][n][c] * src1[t][s mod B][c],
+ * c ascending, in float64; a slot whose id is outside [0, E) gives a zero row.
+ * With route_w, the per-slot rows are combined: dst[t][n] = sum over s ascending of
+ * route_w[t][s] * (per-slot row).
+ * Weights: n_mat = E, rows = N, cols = K.
+ */
+int oracle_mul_mat_id(int w_type, const void *w_data, const void *w_scales, int64_t E, int64_t N,
+                      int64_t K, const void *src1, int src1_type, int32_t B, const int32_t *ids,
+                      int64_t T, int32_t k, const float *route_w, double *dst) {
+    if (!w_data || !src1 || !ids || !dst || E <= 0 || N <= 0 || K <= 0 || T < 0 || k <= 0) return -1;
+    if (w_type != OR_F32 && w_type != OR_Q8_0) return -1;
+    if (w_type == OR_Q8_0 && (!w_scales || K % 32)) return -1;
+    if (src1_type != OR_F32 && src1_type != OR_BF16) return -1;
+    if (B != 1 && B != k) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < T; t++) {
+        double *a = (double *)malloc(sizeof(double) * (size_t)K);
+        double *y = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!a || !y) {
+            bad = 1;
+            free(a);
+            free(y);
+            continue;
+        }
+        double *out_t = dst + t * (route_w ? N : (int64_t)k * N);
+        if (route_w)
+            for (int64_t n = 0; n < N; n++) out_t[n] = 0.0;
+        for (int32_t s = 0; s < k; s++) {
+            int32_t e = ids[t * k + s];
+            double *row = route_w ? y : out_t + (int64_t)s * N;
+            if (e < 0 || e >= E) {
+                if (!route_w)
+                    for (int64_t n = 0; n < N; n++) row[n] = 0.0;
+                continue;
+            }
+            int64_t r = t * B + s % B;
+            for (int64_t c = 0; c < K; c++) a[c] = act_at(src1_type, src1, r * K + c);
+            matvec(w_type, w_data, w_scales, N, K, e, a, row);
+            if (route_w) {
+                double wt = (double)route_w[t * k + s];
+                for (int64_t n = 0; n < N; n++) out_t[n] += wt * y[n];
+            }
+        }
+        free(a);
+        free(y);
+    }
+    return bad ? -2 : 0;
+}
+
+/* One expert's FFN on one activation vector: y = Wd (silu(Wg x) * (Wu x)). */
+static void expert_ffn(int type, const void *g_data, const void *g_scales, const void *u_data,
+                       const void *u_scales, const void *d_data, const void *d_scales, int64_t n_ff,
+                       int64_t n_embd, int64_t e, const double *x, double *g, double *u,
+                       double *y) {
+    matvec(type, g_data, g_scales, n_ff, n_embd, e, x, g);
+    matvec(type, u_data, u_scales, n_ff, n_embd, e, x, u);
+    for (int64_t i = 0; i < n_ff; i++) g[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+    matvec(type, d_data, d_scales, n_embd, n_ff, e, g, y);
+}
+
+/*
+ * Fused MoE FFN: for each token t, for s ascending with e = ids[t][s] in [0, E):
+ *   out[t] += route_w[t][s] * Wd_e (silu(Wg_e x_t) * (Wu_e x_t));
+ * then for each shared expert j ascending: out[t] += Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
+ * Routed gate/up: [E][n_ff][n_embd]; routed down: [E][n_embd][n_ff].
+ * Shared gate/up: [S][n_ff_sh][n_embd]; shared down: [S][n_embd][n_ff_sh]. S may be 0.
+ */
+int oracle_ffn(int w_type, const void *g_data, const void *g_scales, const void *u_data,
+               const void *u_scales, const void *d_data, const void *d_scales, int64_t E,
+               int64_t n_ff, int64_t n_embd, const void *sg_data, const void *sg_scales,
+               const void *su_data, const void *su_scales, const void *sd_data,
+               const void *sd_scales, int64_t S, int64_t n_ff_sh, const void *x, int x_type,
+               const int32_t *ids, const float *route_w, int64_t T, int32_t k, double *out) {
+    if (!g_data || !u_data || !d_data || !x || !ids || !route_w || !out) return -1;
+    if (E <= 0 || n_ff <= 0 || n_embd <= 0 || T < 0 || k <= 0 || S < 0) return -1;
+    if (w_type != OR_F32 && w_type != OR_Q8_0) return -1;
+    if (x_type != OR_F32 && x_type != OR_BF16) return -1;
+    if (w_type == OR_Q8_0 && (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32))
+        return -1;
+    if (S > 0 && (!sg_data || !su_data || !sd_data || n_ff_sh <= 0)) return -1;
+    if (S > 0 && w_type == OR_Q8_0 && (!sg_scales || !su_scales || !sd_scales || n_ff_sh % 32))
+        return -1;
+    int64_t ffmax = n_ff > n_ff_sh ? n_ff : n_ff_sh;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < T; t++) {
+        double *xv = (double *)malloc(sizeof(double) * (size_t)n_embd);
+        double *g = (double *)malloc(sizeof(double) * (size_t)ffmax);
+        double *u = (double *)malloc(sizeof(double) * (size_t)ffmax);
+        double *y = (double *)malloc(sizeof(double) * (size_t)n_embd);
+        if (!xv || !g || !u || !y) {
+            bad = 1;
+            free(xv);
+            free(g);
+            free(u);
+            free(y);
+            continue;
+        }
+        double *o = out + t * n_embd;
+        for (int64_t c = 0; c < n_embd; c++) {
+            xv[c] = act_at(x_type, x, t * n_embd + c);
+            o[c] = 0.0;
+        }
+        for (int32_t s = 0; s < k; s++) {
+            int32_t e = ids[t * k + s];
+            if (e < 0 || e >= E) continue;
+            expert_ffn(w_type, g_data, g_scales, u_data, u_scales, d_data, d_scales, n_ff, n_embd,
+                       e, xv, g, u, y);
+            double wt = (double)route_w[t * k + s];
+            for (int64_t c = 0; c < n_embd; c++) o[c] += wt * y[c];
+        }
+        for (int64_t j = 0; j < S; j++) {
+            expert_ffn(w_type, sg_data, sg_scales, su_data, su_scales, sd_data, sd_scales, n_ff_sh,
+                       n_embd, j, xv, g, u, y);
+            for (int64_t c = 0; c < n_embd; c++) o[c] += y[c];
+        }
+        free(xv);
+        free(g);
+        free(u);
+        free(y);
+    }
+    return bad ? -2 : 0;
+}

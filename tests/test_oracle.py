@@ -1,0 +1,382 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself.
+
+  * number formats: hand-derived bit patterns (tests/golden) and numpy's own
+    float16 / float32 decoders over all 65536 patterns;
+  * row-id maps: exhaustive brute force by a stable sort on tiny inputs, numpy's
+    stable argsort on random ones, and the invariants of the maps;
+  * mul_mat_id: the dense all-experts product (numpy matmul) masked by ids, plain
+    GEMM when E = k = 1, exact doubling when x doubles;
+  * FFN: a dense MoE written with torch's matmul and silu, the shared-expert
+    concatenation identity, one-hot routing, and a hand-derived worked example in
+    closed form.
+The op being pinned: "CUDA: better MoE implementation" (ik_llama.cpp PR #283
+write-up), sections 1.2 (operands and semantics) and 2.1 (the three row maps).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_pairs(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            b, v = line.split()
+            rows.append((int(b, 16), float(v)))
+    return rows
+
+
+def normwise(got, ref):
+    ref = np.asarray(ref, np.float64)
+    den = np.abs(ref).max()
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / (den if den > 0 else 1.0))
+
+
+# --------------------------------------------------------------------- formats
+
+def test_half_fixture():
+    for bits, val in _read_pairs("fp16_values.txt"):
+        got = oracle.half_to_double(bits)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), hex(bits)
+
+
+def test_bf16_fixture():
+    for bits, val in _read_pairs("bf16_values.txt"):
+        assert oracle.bf16_to_double(bits) == val, hex(bits)
+
+
+def test_half_all_patterns_match_numpy():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[np.isinf(ref)], ref[np.isinf(ref)])
+
+
+def test_bf16_sampled_patterns_match_numpy():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_q8_0_dequant_fixture_and_numpy():
+    # One block: scale 2^-10 (0x1400), q = -127..-96 and a second row 0..31.
+    qs = np.stack([np.arange(-127, -95), np.arange(0, 32)]).astype(np.int8)[None]
+    d = np.array([[[0x1400], [0x1418]]], np.uint16).view(np.float16)
+    got = oracle.dequant(qs, d)
+    assert np.array_equal(got[0, 0], np.arange(-127, -95) / 1024.0)
+    assert np.array_equal(got[0, 1], np.arange(0, 32) * 0.00099945068359375)
+    rng = np.random.default_rng(0)
+    qs, d = synth.gen.draw_q8_0(rng, 5, 96)
+    ref = qs.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.array_equal(oracle.dequant(qs, d), ref)
+
+
+# --------------------------------------------------------------------- row ids
+
+def _brute_maps(ids, E, B):
+    T, k = ids.shape
+    flat = [(t, s) for t in range(T) for s in range(k)]
+
+    def bucket(ts):
+        e = ids[ts]
+        return e if 0 <= e < E else E
+
+    order = sorted(range(T * k), key=lambda i: (bucket(flat[i]), i))
+    s1 = [flat[i][0] * B + flat[i][1] % B for i in order]
+    dd = [flat[i][0] * k + flat[i][1] for i in order]
+    bounds = [sum(1 for ts in flat if bucket(ts) < e) for e in range(E + 1)]
+    return np.array(s1), np.array(dd), np.array(bounds)
+
+
+def _check_invariants(ids, E, B, s1, dd, b):
+    T, k = ids.shape
+    n = T * k
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    assert b[0] == 0 and np.all(np.diff(b) >= 0) and b[E] == int(valid.sum())
+    assert np.array_equal(np.diff(b), np.bincount(flat[valid], minlength=E))
+    assert np.array_equal(np.sort(dd), np.arange(n))           # bijection onto [0, T*k)
+    if B == 1:
+        assert np.array_equal(s1, dd // k)
+    else:
+        assert np.array_equal(s1, dd)
+    for e in range(E):
+        seg = dd[b[e]:b[e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)                          # stable: (t, s) ascending
+    tail = dd[b[E]:]
+    assert np.all(~valid[tail]) and np.all(np.diff(tail) > 0)
+    # gather by ids_src1 then scatter by ids_dst reproduces the per-slot source rows
+    rows = np.arange(T * B)
+    gathered = rows[s1]
+    back = np.empty(n, np.int64)
+    back[dd] = gathered
+    want = (np.arange(n) // k) * B + (np.arange(n) % k) % B
+    assert np.array_equal(back, want)
+
+
+@pytest.mark.parametrize("E,T,k", [(1, 3, 1), (2, 2, 2), (3, 2, 2), (4, 3, 2), (2, 3, 3)])
+def test_row_ids_exhaustive(E, T, k):
+    values = list(range(-1, E + 1))       # includes out-of-range ids on both sides
+    for combo in itertools.product(values, repeat=T * k):
+        ids = np.array(combo, np.int32).reshape(T, k)
+        for B in sorted({1, k}):
+            s1, dd, b = oracle.row_ids(ids, E, B)
+            r1, rd, rb = _brute_maps(ids, E, B)
+            assert np.array_equal(s1, r1) and np.array_equal(dd, rd) and np.array_equal(b, rb)
+
+
+@pytest.mark.parametrize("E,T,k,seed", [(8, 16, 2, 1), (64, 512, 6, 2), (128, 333, 8, 3),
+                                        (512, 97, 12, 4), (1, 50, 1, 5), (5, 40, 7, 6)])
+def test_row_ids_random_vs_stable_argsort(E, T, k, seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, size=(T, k)).astype(np.int32)   # duplicates and invalids
+    for B in sorted({1, k}):
+        s1, dd, b = oracle.row_ids(ids, E, B)
+        flat = ids.reshape(-1)
+        key = np.where((flat >= 0) & (flat < E), flat, E)
+        order = np.argsort(key, kind="stable")
+        assert np.array_equal(dd, order)
+        assert np.array_equal(b, np.searchsorted(np.sort(key), np.arange(E + 1), side="left"))
+        _check_invariants(ids, E, B, s1, dd, b)
+
+
+@pytest.mark.parametrize("name", ["tiny", "lite", "dec1", "dec8", "skew"])
+def test_row_ids_configs_invariants(name):
+    cfg = synth.CONFIGS[name]
+    ids = synth.make_inputs(cfg)["ids"] if cfg.kind == "mmid" else None
+    if ids is None:
+        ids = (synth.draw_ids_zipf(cfg.seed, cfg.n_tokens, cfg.n_experts, cfg.n_used, cfg.zipf_s)
+               if cfg.routing == "zipf" else
+               synth.draw_ids_uniform(cfg.seed, cfg.n_tokens, cfg.n_experts, cfg.n_used))
+    s1, dd, b = oracle.row_ids(ids, cfg.n_experts, 1)
+    assert b[-1] == cfg.n_tokens * cfg.n_used        # bounds' counts sum to T*k
+    _check_invariants(ids, cfg.n_experts, 1, s1, dd, b)
+
+
+# ------------------------------------------------------------------ mul_mat_id
+
+def _numpy_dequant(qs, d):
+    return qs.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=-1)
+
+
+def _dense_masked(W, X, ids, B):
+    """Y_all[e][r] = W_e x_r for every expert and every src1 row (numpy matmul),
+    then dst[t][s] = Y_all[ids[t][s]][t*B + s%B], zero for invalid ids."""
+    E = W.shape[0]
+    T, k = ids.shape
+    Y_all = np.einsum("enk,rk->ern", W, X)
+    out = np.zeros((T, k, W.shape[1]))
+    for t in range(T):
+        for s in range(k):
+            e = ids[t, s]
+            if 0 <= e < E:
+                out[t, s] = Y_all[e, t * B + s % B]
+    return out
+
+
+@pytest.mark.parametrize("B_is_k", [False, True])
+def test_mul_mat_id_q8_vs_dense_masked(B_is_k):
+    rng = np.random.default_rng(11)
+    E, N, K, T, k = 6, 40, 96, 9, 3
+    qs, d = synth.gen.draw_q8_0_stack(7, 2, 0, E, N, K)
+    B = k if B_is_k else 1
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T * B, K)).astype(np.float32))
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    rw = synth.draw_route_w(3, T, k)
+    got = oracle.mul_mat_id(qs, d, x, "bf16", ids, None, B)
+    ref = _dense_masked(_numpy_dequant(qs, d), synth.bf16_bits_to_f32(x).astype(np.float64), ids, B)
+    assert normwise(got, ref) < 1e-13
+    assert np.all(got[(ids < 0) | (ids >= E)] == 0.0)
+    gw = oracle.mul_mat_id(qs, d, x, "bf16", ids, rw, B)
+    refw = np.einsum("tsn,ts->tn", ref, rw.astype(np.float64))
+    assert normwise(gw, refw) < 1e-13
+
+
+def test_mul_mat_id_f32_tiny_vs_dense_masked():
+    inp = synth.make_inputs("tiny")
+    got = oracle.mul_mat_id(inp["w"], None, inp["x"], "f32", inp["ids"])
+    ref = _dense_masked(inp["w"].astype(np.float64), inp["x"].astype(np.float64), inp["ids"], 1)
+    assert normwise(got, ref) < 1e-14
+    assert got.shape == (16, 2, 32)
+
+
+def test_mul_mat_id_plain_gemm_when_one_expert():
+    rng = np.random.default_rng(5)
+    N, K, T = 33, 64, 7
+    qs, d = synth.gen.draw_q8_0_stack(9, 2, 0, 1, N, K)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    got = oracle.mul_mat_id(qs, d, x, "bf16", np.zeros((T, 1), np.int32))[:, 0, :]
+    ref = synth.bf16_bits_to_f32(x).astype(np.float64) @ _numpy_dequant(qs, d)[0].T
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_mul_mat_id_doubling_x_doubles_exactly():
+    rng = np.random.default_rng(8)
+    E, N, K, T, k = 4, 16, 64, 5, 2
+    qs, d = synth.gen.draw_q8_0_stack(4, 2, 0, E, N, K)
+    xf = rng.standard_normal((T, K)).astype(np.float32)
+    x1 = synth.f32_to_bf16_bits(xf)
+    x2 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x1) * 2)
+    ids = synth.draw_ids_uniform(1, T, E, k)
+    assert np.array_equal(oracle.mul_mat_id(qs, d, x2, "bf16", ids),
+                          2 * oracle.mul_mat_id(qs, d, x1, "bf16", ids))
+
+
+# ------------------------------------------------------------------------- FFN
+
+def _torch_dense_moe(inp):
+    """Dense MoE in float64 with torch: every expert on every token, then masked
+    by ids and weighted; shared experts added. Library matmul and silu only."""
+    import torch
+    F = torch.nn.functional
+
+    def deq(name):
+        return torch.from_numpy(_numpy_dequant(inp[name + "_qs"], inp[name + "_d"]))
+
+    x = torch.from_numpy(synth.bf16_bits_to_f32(inp["x"]).astype(np.float64))
+    G, U, D = deq("gate"), deq("up"), deq("down")
+    E = G.shape[0]
+    Y = torch.stack([(F.silu(x @ G[e].T) * (x @ U[e].T)) @ D[e].T for e in range(E)])  # [E][T][n_embd]
+    ids = torch.from_numpy(inp["ids"].astype(np.int64))
+    rw = torch.from_numpy(inp["route_w"].astype(np.float64))
+    T, k = ids.shape
+    out = torch.zeros(T, x.shape[1], dtype=torch.float64)
+    for s in range(k):
+        e = ids[:, s]
+        ok = (e >= 0) & (e < E)
+        sel = Y[e.clamp(0, E - 1), torch.arange(T)]
+        out += torch.where(ok[:, None], rw[:, s:s + 1] * sel, torch.zeros_like(sel))
+    if inp.get("sh_gate_qs") is not None:
+        SG, SU, SD = deq("sh_gate"), deq("sh_up"), deq("sh_down")
+        for j in range(SG.shape[0]):
+            out += (F.silu(x @ SG[j].T) * (x @ SU[j].T)) @ SD[j].T
+    return out.numpy()
+
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [(4, 4, 6, 64, 32, 0), (8, 3, 10, 96, 64, 2),
+                                                  (16, 2, 5, 64, 96, 1)])
+def test_ffn_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
+    inp = synth.make_custom_ffn(21 + E, E, k, T, n_embd, n_ff, S)
+    got = oracle.ffn(inp)
+    ref = _torch_dense_moe(inp)
+    assert normwise(got, ref) < 1e-12
+
+
+def test_ffn_invalid_ids_contribute_nothing():
+    inp = synth.make_custom_ffn(3, 6, 3, 7, 64, 32, 1)
+    ids = inp["ids"].copy()
+    ids[0, 1], ids[3, 0], ids[5, 2] = -1, 6, 1000
+    inp["ids"] = ids
+    assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
+
+
+def test_ffn_two_shared_equal_one_concatenated():
+    inp = synth.make_custom_ffn(5, 8, 2, 6, 64, 32, 2)
+    cat = dict(inp)
+    cat["sh_gate_qs"] = inp["sh_gate_qs"].reshape(1, 64, 64)
+    cat["sh_gate_d"] = inp["sh_gate_d"].reshape(1, 64, 2)
+    cat["sh_up_qs"] = inp["sh_up_qs"].reshape(1, 64, 64)
+    cat["sh_up_d"] = inp["sh_up_d"].reshape(1, 64, 2)
+    cat["sh_down_qs"] = np.concatenate([inp["sh_down_qs"][0], inp["sh_down_qs"][1]], axis=1)[None]
+    cat["sh_down_d"] = np.concatenate([inp["sh_down_d"][0], inp["sh_down_d"][1]], axis=1)[None]
+    assert normwise(oracle.ffn(cat), oracle.ffn(inp)) < 1e-13
+
+
+def test_ffn_one_hot_routing_isolates_a_slot():
+    import torch
+    F = torch.nn.functional
+    inp = synth.make_custom_ffn(9, 8, 3, 5, 64, 32, 0)
+    for s in range(3):
+        one = dict(inp)
+        rw = np.zeros_like(inp["route_w"])
+        rw[:, s] = 1.0
+        one["route_w"] = rw
+        got = oracle.ffn(one)
+        x = torch.from_numpy(synth.bf16_bits_to_f32(inp["x"]).astype(np.float64))
+        ref = np.zeros_like(got)
+        for t in range(5):
+            e = inp["ids"][t, s]
+            G, U, D = (torch.from_numpy(_numpy_dequant(inp[n + "_qs"][e], inp[n + "_d"][e]))
+                       for n in ("gate", "up", "down"))
+            ref[t] = ((F.silu(x[t] @ G.T) * (x[t] @ U.T)) @ D.T).numpy()
+        assert normwise(got, ref) < 1e-13
+
+
+def test_ffn_worked_example_closed_form():
+    """Hand-built Q8_0 layer, n_embd = n_ff = 32, x = e_0 (bf16 1.0):
+    expert 0: g_0 = 64*2^-6 = 1, u_0 = 32*2^-5 = 1, down column 0 = (c-16)*2^-4
+        -> y_c = (c-16)/16 * silu(1) = (c-16)/16 * e/(1+e)
+    expert 1: g_0 = -1, u_0 = 2, down column 0 = 1*2^-4
+        -> y_c = silu(-1) * 2 / 16 = -1/(8(1+e))
+    shared:   g_0 = 2, u_0 = 1, down column 0 = 16*2^-4 = 1 -> y_c = silu(2) = 2e^2/(1+e^2)
+    every other gate row is zero, so silu(0) = 0 kills the rest.
+    route_w = (0.75, 0.25) over experts (0, 1)."""
+    n = 32
+
+    def zeros():
+        return np.zeros((1, n, n), np.int8), np.zeros((1, n, 1), np.uint16)
+
+    def h(bits):
+        return np.uint16(bits)
+
+    gq, gd = [], []
+    uq, ud = [], []
+    dq, dd = [], []
+    for g0, u0, dcol, dscale in ((64, 32, np.arange(n) - 16, 0x2C00), (-64, 64, np.ones(n), 0x2C00)):
+        q, s = zeros(); q[0, 0, 0] = g0; s[0, 0, 0] = h(0x2400); gq.append(q); gd.append(s)   # 2^-6
+        q, s = zeros(); q[0, 0, 0] = u0; s[0, 0, 0] = h(0x2800); uq.append(q); ud.append(s)   # 2^-5
+        q, s = zeros(); q[0, :, 0] = dcol; s[0, :, 0] = h(dscale); dq.append(q); dd.append(s)  # 2^-4
+    inp = {
+        "gate_qs": np.concatenate(gq), "gate_d": np.concatenate(gd).view(np.float16),
+        "up_qs": np.concatenate(uq), "up_d": np.concatenate(ud).view(np.float16),
+        "down_qs": np.concatenate(dq), "down_d": np.concatenate(dd).view(np.float16),
+        "x": np.array([[0x3F80] + [0] * (n - 1)], np.uint16), "xtype": "bf16",
+        "ids": np.array([[0, 1]], np.int32), "route_w": np.array([[0.75, 0.25]], np.float32),
+    }
+    q, s = zeros(); q[0, 0, 0] = 64; s[0, 0, 0] = h(0x2800); inp["sh_gate_qs"], inp["sh_gate_d"] = q, s.view(np.float16)
+    q, s = zeros(); q[0, 0, 0] = 32; s[0, 0, 0] = h(0x2800); inp["sh_up_qs"], inp["sh_up_d"] = q, s.view(np.float16)
+    q, s = zeros(); q[0, :, 0] = 16; s[0, :, 0] = h(0x2C00); inp["sh_down_qs"], inp["sh_down_d"] = q, s.view(np.float16)
+    e = math.e
+    c = np.arange(n)
+    want = 0.75 * (c - 16) / 16 * e / (1 + e) + 0.25 * (-1 / (8 * (1 + e))) + 2 * e * e / (1 + e * e)
+    got = oracle.ffn(inp)[0]
+    np.testing.assert_allclose(got, want, rtol=0, atol=4e-16 * 4)
+
+
+# ------------------------------------------------------------------- generator
+
+def test_generator_is_deterministic_and_in_range():
+    a = synth.make_custom_ffn(17, 8, 2, 9, 64, 32, 1)
+    b = synth.make_custom_ffn(17, 8, 2, 9, 64, 32, 1)
+    for key in a:
+        if isinstance(a[key], np.ndarray):
+            assert np.array_equal(a[key], b[key]), key
+    assert a["gate_qs"].min() >= -127 and a["gate_qs"].max() <= 127
+    d = a["gate_d"].astype(np.float64)
+    assert d.min() >= 0.5e-3 - 1e-6 and d.max() <= 1.5e-3 + 1e-6
+    assert np.allclose(a["route_w"].astype(np.float64).sum(axis=1), 1.0, atol=1e-6)
+    assert all(len(set(r)) == len(r) for r in a["ids"].tolist())   # without replacement
+
+
+def test_zipf_routing_is_skewed():
+    cfg = synth.CONFIGS["skew"]
+    ids = synth.draw_ids_zipf(cfg.seed, cfg.n_tokens, cfg.n_experts, cfg.n_used, cfg.zipf_s)
+    cnt = np.bincount(ids.ravel(), minlength=cfg.n_experts)
+    assert cnt.sum() == cfg.n_tokens * cfg.n_used
+    assert cnt.max() > 10 * cnt.mean() / 1.5 and cnt.min() < cnt.mean() / 2
+    assert all(len(set(r)) == len(r) for r in ids.tolist())
