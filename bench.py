@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE indirect matmul hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config lite|dec1|dec8|skew|v3|tiny]
+
+A step is one full pass of the hot path -- row ids, gate/up grouped GEMM, down
+grouped GEMM, fixed-order reduce (or the GEMV decode kernels) -- over one batch of
+synthetic input already resident in HBM. The default workload is the
+DeepSeek-Lite-shaped PP512 layer (E64 k6 + 2 shared, n_embd 2048, n_ff 1408,
+Q8_0, 512 tokens). Weights are rotated through R copies so the set read per step
+is not served from the 256 MB last-level cache.
+
+Prints ONE JSON line: tokens/s (value), TFLOP/s, GB/s, a roofline entry for the
+dominant kernel (timed with HIP events on the launch stream) and the CPU oracle
+timed on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+Q8_BYTES = 34.0 / 32.0      # Q8_0: 32 int8 + one fp16 scale per 32 weights
+
+STAGES = {1: ["row_ids", "gemm_gate_up", "gemm_down", "reduce"],
+          2: ["gemv_gate_up", "gemv_down", "reduce"]}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="lite")
+    p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
+    p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def workload_stats(inp, cfg):
+    """Algorithmic work of one step (flops, bytes) and per-kernel bytes."""
+    T, k = inp["ids"].shape
+    E, n_embd, n_ff, S = cfg.n_experts, cfg.n_embd, cfg.n_ff, cfg.n_shared
+    ids = inp["ids"].ravel()
+    touched = len(np.unique(ids[(ids >= 0) & (ids < E)]))
+    rows_routed = int(((ids >= 0) & (ids < E)).sum())
+    flops = 2.0 * (rows_routed + T * S) * 3 * n_embd * n_ff
+    w_gu = (touched + S) * 2 * n_ff * n_embd * Q8_BYTES
+    w_dn = (touched + S) * n_embd * n_ff * Q8_BYTES
+    x_b = T * n_embd * 2
+    out_b = T * n_embd * 4
+    return {
+        "flops": flops, "bytes": w_gu + w_dn + x_b + out_b, "touched": touched,
+        "gate_up": {"bytes": w_gu + x_b, "flops": 2.0 * (rows_routed + T * S) * 2 * n_embd * n_ff},
+        "down": {"bytes": w_dn, "flops": 2.0 * (rows_routed + T * S) * n_embd * n_ff},
+    }
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle, as it stands, on a bounded token sample: tokens/s on this host."""
+    import oracle
+    oracle.lib()
+    T = inp["ids"].shape[0]
+    n = min(T, 4)
+    while True:
+        rows = np.arange(n)
+        t0 = time.perf_counter()
+        oracle.ffn(inp, token_rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= T:
+            break
+        n = min(T, max(n * 2, int(n * budget_s / 4 / max(dt, 1e-3))))
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d tokens, full layer (all experts and shared), fp64, %.1f s"
+                      % (n, T, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(see the sharding notes in DESIGN.md)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.kind != "ffn":
+        print("bench.py: --config must be an FFN workload", file=sys.stderr)
+        sys.exit(2)
+    inp = synth.make_inputs(cfg)
+    T, k = inp["ids"].shape
+    st = workload_stats(inp, cfg)
+    dev = torch.device("cuda:0")
+
+    def up(qs, d):
+        return moe.weights_from_numpy(qs, d)
+
+    R = args.rotate or (1 if st["bytes"] > 2e9 else max(4, int(np.ceil(1.2e9 / st["bytes"]))))
+    sets = []
+    base = [up(inp[n + "_qs"], inp[n + "_d"]) for n in ("gate", "up", "down")]
+    sh = ([up(inp["sh_" + n + "_qs"], inp["sh_" + n + "_d"]) for n in ("gate", "up", "down")]
+          if cfg.n_shared else None)
+    for r in range(R):
+        if r == 0:
+            sets.append((base, sh))
+        else:
+            cl = lambda w: moe.Weights(w.data.clone(), w.scales.clone())
+            sets.append(([cl(w) for w in base], [cl(w) for w in sh] if sh else None))
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(inp["ids"]).to(dev)
+    rw = torch.from_numpy(inp["route_w"]).to(dev)
+    out = torch.empty((T, cfg.n_embd), dtype=torch.float32, device=dev)
+    path = moe.moe_select_path(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), path=args.path)
+    need = moe.moe_ffn_fused_workspace_size(base[0], sh[0] if sh else None, T, k, path=args.path)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        (g, u, d), s = sets[i % R]
+        moe.moe_ffn_fused(g, u, d, x, ids, rw, shared=s, path=args.path, out=out, workspace=ws,
+                          stream=stream, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+
+    # per-kernel durations: HIP events recorded by the library around each stage
+    names = STAGES[path]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+           for _ in range(args.steps)]
+    for row in evs:          # torch creates the underlying hipEvent on first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=[e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    stage_ms = {n: float(np.mean([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1])
+                                  for i in range(args.steps)])) for j, n in enumerate(names)}
+    dom = max(stage_ms, key=stage_ms.get)
+    kern = {"gemm_gate_up": "gate_up", "gemv_gate_up": "gate_up", "gemm_down": "down",
+            "gemv_down": "down"}.get(dom)
+    mfma_bound = path == 1 and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
+    if kern is None:
+        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": None, "traffic": None, "kernel": dom}
+    elif mfma_bound:
+        a = st[kern]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / BF16_PEAK_TFLOPS, "traffic": None, "kernel": dom}
+    else:
+        a = st[kern]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+
+    res = {
+        "metric": "MoE mul_mat_id tokens/s + TFLOP/s (PP512/PP4096) and decode GB/s, 1 MI355X",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if path == 1 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.desc, "n_tokens": T, "n_experts": cfg.n_experts,
+                   "n_used": k, "n_shared": cfg.n_shared, "n_embd": cfg.n_embd, "n_ff": cfg.n_ff,
+                   "path": "gemm" if path == 1 else "gemv", "weight_copies": R,
+                   "parallelism": "single GPU"},
+        "tflops": st["flops"] / (ms * 1e-3) / 1e12,
+        "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
+        "stage_ms": stage_ms,
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * moe.h -- C ABI of libmoe, the MI355X (gfx950) Mixture-of-Experts indirect
+ * matrix multiplication (mul_mat_id) library.
+ *
+ * The operation. mul_mat_id takes stacked expert weights, activations and an
+ * integer ids table; every token is multiplied only by the weight matrices of the
+ * experts its ids row names ("CUDA: better MoE implementation", the ik_llama.cpp
+ * PR #283 write-up, section 1.2). The deterministic fast path first turns ids into
+ * three maps -- the src1 rows reordered so each expert's rows are contiguous, the
+ * same reordering for dst, and each expert's bounds in that order -- and then
+ * reorders and reduces by those maps with no atomic slot counters (same page,
+ * sections 2 and 2.1; summary in section 6). The fused MoE FFN adds gate/up with
+ * SiLU(gate) * up (section 4.2 names the fused up/gate forward) and always-on
+ * shared experts computed in the same operation ("CUDA: fuse shared experts into
+ * MMVQ", llama.cpp release b11370: fused shared experts, optional buffers checked
+ * for null).
+ *
+ * Layouts (row-major, last index contiguous):
+ *   weights  W[n_mat][rows][cols]; Q8_0: int8 qs[n_mat][rows][cols] plus fp16
+ *            scales d[n_mat][rows][cols/32], value = d * q (32 values per scale).
+ *   ids      int32 [n_tokens][n_used]; route_w float32 [n_tokens][n_used].
+ *   src1     [n_tokens][B][K] with B = src1_rows_per_token in {1, n_used}:
+ *            slot s of token t reads row t*B + (s mod B).
+ *   x        [n_tokens][n_embd]; bf16 tensors are raw 16-bit patterns.
+ *
+ * Ownership and ordering. Every tensor pointer is a caller-owned DEVICE pointer;
+ * the library never allocates, frees or keeps one. Structs passed by pointer
+ * (moe_weights, moe_options) are read before the call returns, so host memory is
+ * never touched after return. Work is enqueued on `stream` (a hipStream_t; NULL =
+ * the default stream) and the call returns without synchronising. The workspace
+ * `ws` is caller-owned device memory of at least the size the matching
+ * *_workspace_size function reports; its contents are undefined on entry and on
+ * exit, and two calls in flight at once must not share one.
+ *
+ * Errors. Arguments are validated before anything is enqueued; on any status other
+ * than MOE_OK nothing was enqueued and outputs are untouched (MOE_EHIP: a launch
+ * failed; earlier launches of the same call may have run). moe_last_error()
+ * returns a thread-local description of the last failure.
+ *
+ * Determinism. No floating-point or placement atomics are used: for identical
+ * inputs, shapes, options and device, outputs are bitwise identical run to run.
+ *
+ * Ids outside [0, n_experts) are a caller error that does not fault: such an entry
+ * joins no expert segment (expert_bounds[n_experts] counts valid entries only),
+ * its per-slot output row is zero and it contributes nothing to weighted sums.
+ * Duplicate ids within a token are legal; every (token, slot) is its own row.
+ *
+ * Limits (MOE_ELIMIT): n_tokens < 2^22 and n_used < 2^10 (the bounds the page
+ * above quotes for safe 32-bit packing, section 2.1), n_tokens * n_used < 2^31,
+ * n_experts <= 1024, Q8_0 cols % 32 == 0.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,     /* null pointer, bad size, unsupported dtype combination */
+    MOE_ELIMIT = -2,     /* a size limit above is exceeded                         */
+    MOE_EWORKSPACE = -3, /* ws_bytes smaller than the required workspace           */
+    MOE_EHIP = -4        /* a HIP launch failed                                    */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2 } moe_dtype;
+
+/* n_mat stacked matrices of rows x cols. */
+typedef struct {
+    moe_dtype type;     /* MOE_F32 or MOE_Q8_0                                   */
+    const void *data;   /* F32: float[n_mat][rows][cols]; Q8_0: int8 qs[...]     */
+    const void *scales; /* Q8_0: uint16 (fp16) d[n_mat][rows][cols/32]; F32: NULL */
+    int64_t n_mat, rows, cols;
+} moe_weights;
+
+/* Path selection (the pages' backend picks its quantized grouped path by comparing
+ * the token count with a threshold times the expert count, section 2.1):
+ * GEMM when n_tokens >= tau * n_experts, else the GEMV (decode) path.
+ * Optional per-kernel timing: when timing_events is non-NULL it points to
+ * n_timing_events hipEvent_t handles; the call records events[2i] before and
+ * events[2i+1] after its i-th kernel launch on `stream` (while 2i+1 <
+ * n_timing_events). Kernel order -- moe_ffn_fused GEMM path: row ids, gate/up
+ * grouped GEMM, down grouped GEMM, reduce; GEMV path: gate/up GEMV, down GEMV,
+ * reduce. moe_mul_mat_id GEMM path: row ids, grouped GEMM, fix-up/reduce;
+ * GEMV path: GEMV, fix-up/reduce. */
+typedef struct {
+    int32_t path; /* 0 auto, 1 force grouped GEMM, 2 force GEMV (decode)        */
+    float tau;    /* <= 0 means the default, 1.0                                 */
+    int32_t reserved[6];
+    void *const *timing_events;
+    int32_t n_timing_events;
+    int32_t reserved2;
+} moe_options;
+
+/*
+ * moe_row_ids -- the three maps of section 2.1 of the PR #283 write-up.
+ *   ids              device int32 [n_tokens][n_used]
+ *   ids_src1, ids_dst device int32 [n_tokens * n_used] (written)
+ *   expert_bounds    device int32 [n_experts + 1] (written)
+ * Position j enumerates experts ascending, and inside an expert its entries by
+ * token then slot (a stable counting sort): ids_src1[j] = t*B + (s mod B) is the
+ * src1 row entry j reads, ids_dst[j] = t*n_used + s the dst row it writes, and
+ * expert e owns [expert_bounds[e], expert_bounds[e+1]). Entries with invalid ids
+ * follow position expert_bounds[n_experts], in (t, s) order.
+ * n_tokens = 0 is allowed (all bounds 0). Workspace: moe_row_ids_workspace_size.
+ */
+moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int32_t n_experts,
+                       int32_t src1_rows_per_token, int32_t *ids_src1, int32_t *ids_dst,
+                       int32_t *expert_bounds, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
+ *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
+ *            src1) on the MFMA grouped GEMM or the GEMV path; (F32 w, F32 src1).
+ *   src1     device [n_tokens][B][K], B = src1_rows_per_token in {1, n_used}
+ *   ids      device int32 [n_tokens][n_used]
+ *   route_w  NULL: dst = float32 [n_tokens][n_used][N], dst[t][s] = W_{ids[t][s]} src1_row;
+ *            else device float32 [n_tokens][n_used] and dst = float32 [n_tokens][N],
+ *            dst[t] = sum over s ascending of route_w[t][s] * (slot s's row).
+ * Outputs are overwritten, never accumulated into. n_tokens = 0 is a no-op.
+ */
+moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1_type,
+                          int32_t src1_rows_per_token, const int32_t *ids, int64_t n_tokens,
+                          int32_t n_used, const float *route_w, float *dst, const moe_options *opt,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_ffn_fused -- MoE FFN layer on the indirect matmul:
+ *   out[t] = sum_{s ascending, valid} route_w[t][s] * Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),
+ *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
+ *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
+ *   sh_gate, sh_up Q8_0 [S][n_ff_sh][n_embd]; sh_down Q8_0 [S][n_embd][n_ff_sh];
+ *             all three NULL (or n_mat == 0) = no shared experts; giving only some of
+ *             them is MOE_EINVAL.
+ *   x         device BF16 [n_tokens][n_embd]; ids, route_w as above.
+ *   out       device float32 [n_tokens][n_embd] (overwritten).
+ * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights d*q rounded
+ * to nearest-even, bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
+ * results; GEMV path -- fp32 throughout.
+ */
+moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const moe_weights *down,
+                         const moe_weights *sh_gate, const moe_weights *sh_up,
+                         const moe_weights *sh_down, const void *x, moe_dtype x_type,
+                         const int32_t *ids, const float *route_w, int64_t n_tokens, int32_t n_used,
+                         float *out, const moe_options *opt, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Workspace sizes in bytes for the calls above with the same arguments (0 if the
+ * arguments are invalid; a valid call may also need 0 bytes, then ws may be NULL). */
+size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_experts);
+size_t moe_mul_mat_id_workspace_size(const moe_weights *w, moe_dtype src1_type,
+                                     int32_t src1_rows_per_token, int64_t n_tokens,
+                                     int32_t n_used, const moe_options *opt);
+size_t moe_ffn_fused_workspace_size(const moe_weights *gate, const moe_weights *sh_gate,
+                                    moe_dtype x_type, int64_t n_tokens, int32_t n_used,
+                                    const moe_options *opt);
+
+/* Which path a call with these sizes takes: 1 grouped GEMM, 2 GEMV (decode), or a
+ * negative moe_status for invalid arguments. act_width is the widest activation
+ * row a GEMV kernel would stage (mul_mat_id: K; FFN: max(n_embd, n_ff, n_ff_sh)).
+ * Auto: GEMV when n_tokens < tau * n_experts, n_tokens * n_used <= 256 and
+ * act_width <= 16384; forcing GEMV outside the last two bounds is MOE_EINVAL.
+ * Pure host function. */
+int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
+                        const moe_options *opt);
+
+const char *moe_status_string(moe_status s);
+const char *moe_last_error(void); /* thread-local detail of the last failure ("" if none) */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,266 @@
+"""MI355X (gfx950) MoE indirect matrix multiplication -- Python binding of libmoe.
+
+A thin ctypes layer over the C ABI in include/moe.h with the same entry-point
+names. It only marshals arguments: torch tensors supply device memory (outputs and
+the workspace are allocated with torch) and the current HIP stream; every step of
+the computation runs in the library's HIP kernels. If libmoe.so is missing the
+import fails -- there is no fallback.
+
+    import indirect_expert_matmul_amd as moe
+    out = moe.moe_ffn_fused(gate, up, down, x, ids, route_w, shared=(sg, su, sd))
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ELIMIT, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_Q8_0 = 0, 1, 2
+PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
+
+# Every symbol include/moe.h declares.
+EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_row_ids_workspace_size",
+           "moe_mul_mat_id_workspace_size", "moe_ffn_fused_workspace_size", "moe_select_path",
+           "moe_status_string", "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (fn, _status_name(status), detail))
+
+
+class c_moe_weights(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int), ("data", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("n_mat", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class c_moe_options(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("tau", ctypes.c_float),
+                ("reserved", ctypes.c_int32 * 6), ("timing_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_timing_events", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoe.so is not built (%s); run `python -m indirect_expert_matmul_amd.build`"
+                          % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    W = ctypes.POINTER(c_moe_weights)
+    O = ctypes.POINTER(c_moe_options)
+    lib.moe_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.moe_mul_mat_id.argtypes = [W, P, ctypes.c_int, I32, P, I64, I32, P, P, O, P, SZ, P]
+    lib.moe_ffn_fused.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P, SZ, P]
+    for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused):
+        f.restype = ctypes.c_int
+    lib.moe_row_ids_workspace_size.argtypes = [I64, I32, I32]
+    lib.moe_mul_mat_id_workspace_size.argtypes = [W, ctypes.c_int, I32, I64, I32, O]
+    lib.moe_ffn_fused_workspace_size.argtypes = [W, W, ctypes.c_int, I64, I32, O]
+    for f in (lib.moe_row_ids_workspace_size, lib.moe_mul_mat_id_workspace_size,
+              lib.moe_ffn_fused_workspace_size):
+        f.restype = SZ
+    lib.moe_select_path.argtypes = [I64, I32, I32, I64, O]
+    lib.moe_select_path.restype = I32
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return lib.moe_status_string(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib.moe_last_error().decode()
+
+
+def _check(status: int, fn: str):
+    if status != MOE_OK:
+        raise MoeError(status, fn, last_error())
+
+
+@dataclass
+class Weights:
+    """Stacked expert matrices on the GPU. Q8_0: ``data`` int8 [n_mat][rows][cols] and
+    ``scales`` float16 (or its uint16 bits) [n_mat][rows][cols/32]; F32: ``data``
+    float32 [n_mat][rows][cols] and ``scales`` None."""
+    data: torch.Tensor
+    scales: Optional[torch.Tensor] = None
+
+    @property
+    def type(self) -> int:
+        return MOE_F32 if self.scales is None else MOE_Q8_0
+
+    def c(self) -> c_moe_weights:
+        d = self.data
+        if d.dim() != 3:
+            raise ValueError("weights must be [n_mat][rows][cols]")
+        if self.scales is None:
+            if d.dtype != torch.float32:
+                raise ValueError("float weights must be float32")
+        else:
+            if d.dtype != torch.int8 or self.scales.element_size() != 2:
+                raise ValueError("Q8_0 weights: int8 qs with 16-bit scales")
+            if not self.scales.is_contiguous():
+                raise ValueError("scales must be contiguous")
+        if not d.is_contiguous():
+            raise ValueError("weights must be contiguous")
+        return c_moe_weights(self.type, d.data_ptr(),
+                             None if self.scales is None else self.scales.data_ptr(),
+                             d.shape[0], d.shape[1], d.shape[2])
+
+
+def _options(path: int = PATH_AUTO, tau: float = 0.0, events: Optional[Sequence[int]] = None):
+    o = c_moe_options()
+    o.path = path
+    o.tau = tau
+    if events:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        o.timing_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        o.n_timing_events = len(events)
+        o._keep = arr
+    return o
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _dev_check(*tensors):
+    for t in tensors:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous device tensors")
+
+
+def _xtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MOE_BF16
+    raise ValueError("activations must be float32 or bfloat16 (or its 16-bit patterns)")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small: need %d bytes" % nbytes)
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moe_select_path(n_tokens: int, n_used: int, n_experts: int, act_width: int,
+                    path: int = PATH_AUTO, tau: float = 0.0) -> int:
+    r = lib.moe_select_path(n_tokens, n_used, n_experts, act_width, ctypes.byref(_options(path, tau)))
+    if r < 0:
+        raise MoeError(r, "moe_select_path", last_error())
+    return r
+
+
+def moe_row_ids(ids: torch.Tensor, n_experts: int, src1_rows_per_token: int = 1, stream=None,
+                workspace: Optional[torch.Tensor] = None):
+    """(ids_src1, ids_dst, expert_bounds) for ids int32 [T][k] on the GPU."""
+    _dev_check(ids)
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be int32 [n_tokens][n_used]")
+    T, k = ids.shape
+    dev = ids.device
+    s1 = torch.empty(T * k, dtype=torch.int32, device=dev)
+    dd = torch.empty(T * k, dtype=torch.int32, device=dev)
+    b = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    need = lib.moe_row_ids_workspace_size(T, k, n_experts)
+    ws = _workspace(need, dev, workspace)
+    _check(lib.moe_row_ids(ids.data_ptr(), T, k, n_experts, src1_rows_per_token, s1.data_ptr(),
+                           dd.data_ptr(), b.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                           _stream(stream)), "moe_row_ids")
+    return s1, dd, b
+
+
+def moe_mul_mat_id_workspace_size(w: Weights, src1_type: int, src1_rows_per_token: int,
+                                  n_tokens: int, n_used: int, path: int = PATH_AUTO,
+                                  tau: float = 0.0) -> int:
+    cw = w.c()
+    return lib.moe_mul_mat_id_workspace_size(ctypes.byref(cw), src1_type, src1_rows_per_token,
+                                             n_tokens, n_used, ctypes.byref(_options(path, tau)))
+
+
+def moe_mul_mat_id(w: Weights, src1: torch.Tensor, ids: torch.Tensor,
+                   route_w: Optional[torch.Tensor] = None, src1_rows_per_token: int = 1,
+                   path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+    """GGML_OP_MUL_MAT_ID: float32 [T][k][N] per slot, or [T][N] weighted by route_w."""
+    _dev_check(src1, ids, route_w, out)
+    T, k = ids.shape
+    cw = w.c()
+    N = cw.rows
+    if out is None:
+        shape = (T, N) if route_w is not None else (T, k, N)
+        out = torch.empty(shape, dtype=torch.float32, device=ids.device)
+    st = _xtype(src1)
+    opt = _options(path, tau, events)
+    need = lib.moe_mul_mat_id_workspace_size(ctypes.byref(cw), st, src1_rows_per_token, T, k,
+                                             ctypes.byref(opt))
+    ws = _workspace(need, ids.device, workspace)
+    _check(lib.moe_mul_mat_id(ctypes.byref(cw), src1.data_ptr(), st, src1_rows_per_token,
+                              ids.data_ptr(), T, k,
+                              None if route_w is None else route_w.data_ptr(), out.data_ptr(),
+                              ctypes.byref(opt), ws.data_ptr(), ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_mul_mat_id")
+    return out
+
+
+def moe_ffn_fused_workspace_size(gate: Weights, sh_gate: Optional[Weights], n_tokens: int,
+                                 n_used: int, path: int = PATH_AUTO, tau: float = 0.0) -> int:
+    cg = gate.c()
+    cs = sh_gate.c() if sh_gate is not None else None
+    return lib.moe_ffn_fused_workspace_size(ctypes.byref(cg), ctypes.byref(cs) if cs else None,
+                                            MOE_BF16, n_tokens, n_used,
+                                            ctypes.byref(_options(path, tau)))
+
+
+def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, ids: torch.Tensor,
+                  route_w: torch.Tensor, shared: Optional[Sequence[Weights]] = None,
+                  path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None, events=None):
+    """Fused MoE FFN: float32 [T][n_embd]."""
+    _dev_check(x, ids, route_w, out)
+    T, k = ids.shape
+    cg, cu, cd = gate.c(), up.c(), down.c()
+    cs = [s.c() for s in shared] if shared else [None, None, None]
+    if out is None:
+        out = torch.empty((T, cg.cols), dtype=torch.float32, device=x.device)
+    opt = _options(path, tau, events)
+    need = lib.moe_ffn_fused_workspace_size(ctypes.byref(cg),
+                                            ctypes.byref(cs[0]) if cs[0] is not None else None,
+                                            MOE_BF16, T, k, ctypes.byref(opt))
+    ws = _workspace(need, x.device, workspace)
+    ref = [ctypes.byref(c) if c is not None else None for c in cs]
+    _check(lib.moe_ffn_fused(ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd), ref[0], ref[1],
+                             ref[2], x.data_ptr(), _xtype(x), ids.data_ptr(), route_w.data_ptr(), T,
+                             k, out.data_ptr(), ctypes.byref(opt), ws.data_ptr(),
+                             ws.numel() * ws.element_size(), _stream(stream)), "moe_ffn_fused")
+    return out
+
+
+def weights_from_numpy(qs_or_w, d=None, device="cuda") -> Weights:
+    """Upload numpy weights (from ``synth``) as a Weights pair."""
+    import numpy as np
+    if d is None:
+        return Weights(torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.float32)).to(device))
+    q = torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.int8)).to(device)
+    s = torch.from_numpy(np.ascontiguousarray(np.asarray(d).view(np.int16))).to(device)
+    return Weights(q, s)

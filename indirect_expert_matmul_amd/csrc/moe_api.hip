@@ -1,0 +1,644 @@
+// libmoe C ABI: argument validation, limits, workspace carving, path selection and
+// the launch sequence of each entry point (declared and documented in moe.h).
+//
+// Host-side rules taken from the pages' account of the CUDA implementation
+// ("CUDA: better MoE implementation"):
+//   * the three row maps are built on the device, so no host buffer has to outlive
+//     an asynchronous copy (section 5 discusses exactly that hazard with host-side
+//     mapping buffers) -- this file never copies host data to the device and never
+//     synchronises;
+//   * the grouped (GEMM) path serves batches whose token count is large relative to
+//     the expert count, the mat-vec path the small ones (section 2.1's threshold
+//     test, read here as n_tokens >= tau * n_experts);
+//   * the packing limits n_tokens < 2^22 and n_used < 2^10 (section 2.1).
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base((char*)b) {}
+    void* take(size_t bytes) {
+        off = (off + kAlign - 1) / kAlign * kAlign;
+        void* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    }
+};
+
+struct Timer {
+    void* const* ev;
+    int n;
+    int stage = 0;
+    hipStream_t st;
+    Timer(const moe_options* o, hipStream_t s)
+        : ev(o ? o->timing_events : nullptr), n(o ? o->n_timing_events : 0), st(s) {}
+    void begin() {
+        if (ev && 2 * stage + 1 < n) hipEventRecord((hipEvent_t)ev[2 * stage], st);
+    }
+    void end() {
+        if (ev && 2 * stage + 1 < n) hipEventRecord((hipEvent_t)ev[2 * stage + 1], st);
+        stage++;
+    }
+};
+
+moe_status hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return MOE_OK;
+}
+
+moe_status check_tokens(int64_t T, int32_t k) {
+    if (T < 0) return fail(MOE_EINVAL, "n_tokens must be >= 0 (got %lld)", (long long)T);
+    if (k <= 0) return fail(MOE_EINVAL, "n_used must be > 0 (got %d)", k);
+    if (T >= (1LL << 22)) return fail(MOE_ELIMIT, "n_tokens must be < 2^22 (got %lld)", (long long)T);
+    if (k >= (1 << 10)) return fail(MOE_ELIMIT, "n_used must be < 2^10 (got %d)", k);
+    if (T * (int64_t)k >= (1LL << 31))
+        return fail(MOE_ELIMIT, "n_tokens * n_used must be < 2^31");
+    return MOE_OK;
+}
+
+moe_status check_experts(int64_t E) {
+    if (E <= 0) return fail(MOE_EINVAL, "n_experts must be > 0 (got %lld)", (long long)E);
+    if (E > kMaxExperts) return fail(MOE_ELIMIT, "n_experts must be <= %d (got %lld)", kMaxExperts, (long long)E);
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_weights* w, const char* name, bool allow_f32) {
+    if (!w) return fail(MOE_EINVAL, "%s: weights struct is NULL", name);
+    if (!w->data) return fail(MOE_EINVAL, "%s: data is NULL", name);
+    if (w->n_mat <= 0 || w->rows <= 0 || w->cols <= 0)
+        return fail(MOE_EINVAL, "%s: sizes must be > 0", name);
+    if (w->rows > INT32_MAX || w->cols > INT32_MAX)
+        return fail(MOE_ELIMIT, "%s: rows and cols must fit in int32", name);
+    if (w->type == MOE_Q8_0) {
+        if (!w->scales) return fail(MOE_EINVAL, "%s: Q8_0 scales are NULL", name);
+        if (w->cols % 32) return fail(MOE_ELIMIT, "%s: Q8_0 needs cols %% 32 == 0 (got %lld)", name, (long long)w->cols);
+    } else if (w->type == MOE_F32) {
+        if (!allow_f32) return fail(MOE_EINVAL, "%s: float32 weights are not supported here", name);
+    } else {
+        return fail(MOE_EINVAL, "%s: unsupported weight type %d", name, (int)w->type);
+    }
+    return MOE_OK;
+}
+
+float tau_of(const moe_options* o) { return (o && o->tau > 0.f) ? o->tau : 1.0f; }
+
+// 1 = GEMM, 2 = GEMV, or a negative status.
+int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_options* o) {
+    const int32_t force = o ? o->path : 0;
+    const bool dec_ok = T * (int64_t)k <= kDecMaxSlots && act_width <= kDecMaxWidth;
+    if (force == 1) return 1;
+    if (force == 2) {
+        if (!dec_ok)
+            return fail(MOE_EINVAL, "GEMV path needs n_tokens*n_used <= %d and activation width <= %lld",
+                        kDecMaxSlots, (long long)kDecMaxWidth);
+        return 2;
+    }
+    if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
+    return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
+}
+
+int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n : E); }
+
+// ---------------------------------------------------------------- workspace plans
+struct RowIdsPlan {
+    int32_t *ids_src1, *ids_dst, *bounds, *tile_a, *chunk_cnt, *bucket_tot;
+};
+RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, bool tiles) {
+    RowIdsPlan p{};
+    if (maps) {
+        p.ids_src1 = (int32_t*)c.take(sizeof(int32_t) * n);
+        p.ids_dst = (int32_t*)c.take(sizeof(int32_t) * n);
+        p.bounds = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
+    }
+    if (tiles) p.tile_a = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
+    const size_t sb = row_ids_scratch_bytes(n, E);
+    if (sb) {
+        const int64_t nc = (int64_t)(sb - (size_t)(E + 1) * sizeof(int32_t)) / sizeof(int32_t);
+        p.chunk_cnt = (int32_t*)c.take(sizeof(int32_t) * nc);
+        p.bucket_tot = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
+    }
+    return p;
+}
+
+struct FfnDims {
+    int64_t T;
+    int32_t k, E, n_embd, n_ff, S, n_ff_sh;
+};
+
+struct FfnPlan {
+    int path;
+    int msub;
+    RowIdsPlan r;
+    void *h, *hsh, *y, *ysh;
+};
+
+FfnPlan carve_ffn(Carve& c, const FfnDims& d, int path) {
+    FfnPlan p{};
+    p.path = path;
+    const int64_t n = d.T * d.k;
+    if (path == 1) {
+        p.msub = gemm_pick_msub((double)n / d.E);
+        p.r = carve_row_ids(c, n, d.E, true, true);
+        p.h = c.take((size_t)n * d.n_ff * 2);
+        p.hsh = c.take((size_t)d.S * d.T * d.n_ff_sh * 2);
+    } else {
+        p.h = c.take((size_t)n * d.n_ff * 4);
+        p.hsh = c.take((size_t)d.S * d.T * d.n_ff_sh * 4);
+    }
+    p.y = c.take((size_t)n * d.n_embd * 4);
+    p.ysh = c.take((size_t)d.S * d.T * d.n_embd * 4);
+    return p;
+}
+
+struct MmidPlan {
+    int path;
+    int msub;
+    RowIdsPlan r;
+    void* y;
+};
+
+MmidPlan carve_mmid(Carve& c, int64_t T, int32_t k, int32_t E, int64_t N, bool weighted, bool q8, int path) {
+    MmidPlan p{};
+    p.path = path;
+    const int64_t n = T * k;
+    if (!q8 || path == 1) {
+        p.msub = gemm_pick_msub((double)n / E);
+        p.r = carve_row_ids(c, n, E, true, q8);
+    }
+    if (weighted) p.y = c.take((size_t)n * N * 4);
+    return p;
+}
+
+moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const moe_weights* down,
+                        const moe_weights* sg, const moe_weights* su, const moe_weights* sd,
+                        moe_dtype x_type, int64_t T, int32_t k, FfnDims* d) {
+    moe_status s;
+    if ((s = check_tokens(T, k))) return s;
+    if ((s = check_weights(gate, "gate", false))) return s;
+    if ((s = check_weights(up, "up", false))) return s;
+    if ((s = check_weights(down, "down", false))) return s;
+    if ((s = check_experts(gate->n_mat))) return s;
+    if (x_type != MOE_BF16) return fail(MOE_EINVAL, "x must be BF16 (Q8_0 experts run bf16 activations)");
+    if (up->n_mat != gate->n_mat || down->n_mat != gate->n_mat || up->rows != gate->rows ||
+        up->cols != gate->cols || down->rows != gate->cols || down->cols != gate->rows)
+        return fail(MOE_EINVAL, "gate/up must be [E][n_ff][n_embd] and down [E][n_embd][n_ff]");
+    d->T = T;
+    d->k = k;
+    d->E = (int32_t)gate->n_mat;
+    d->n_ff = (int32_t)gate->rows;
+    d->n_embd = (int32_t)gate->cols;
+    const bool any_sh = (sg && sg->n_mat) || (su && su->n_mat) || (sd && sd->n_mat);
+    d->S = 0;
+    d->n_ff_sh = 0;
+    if (any_sh) {
+        if (!sg || !su || !sd || !sg->n_mat || !su->n_mat || !sd->n_mat)
+            return fail(MOE_EINVAL, "shared experts: give all of sh_gate, sh_up and sh_down, or none");
+        if ((s = check_weights(sg, "sh_gate", false))) return s;
+        if ((s = check_weights(su, "sh_up", false))) return s;
+        if ((s = check_weights(sd, "sh_down", false))) return s;
+        if (su->n_mat != sg->n_mat || sd->n_mat != sg->n_mat || su->rows != sg->rows ||
+            su->cols != sg->cols || sg->cols != gate->cols || sd->rows != gate->cols ||
+            sd->cols != sg->rows)
+            return fail(MOE_EINVAL, "shared gate/up must be [S][n_ff_sh][n_embd], shared down [S][n_embd][n_ff_sh]");
+        if (sg->n_mat > 64) return fail(MOE_ELIMIT, "at most 64 shared experts");
+        d->S = (int32_t)sg->n_mat;
+        d->n_ff_sh = (int32_t)sg->rows;
+    }
+    return MOE_OK;
+}
+
+int64_t ffn_act_width(const FfnDims& d) {
+    int64_t w = d.n_embd > d.n_ff ? d.n_embd : d.n_ff;
+    return w > d.n_ff_sh ? w : d.n_ff_sh;
+}
+
+moe_status validate_mmid(const moe_weights* w, moe_dtype st, int32_t B, int64_t T, int32_t k) {
+    moe_status s;
+    if ((s = check_tokens(T, k))) return s;
+    if ((s = check_weights(w, "w", true))) return s;
+    if ((s = check_experts(w->n_mat))) return s;
+    if (B != 1 && B != k) return fail(MOE_EINVAL, "src1_rows_per_token must be 1 or n_used (got %d)", B);
+    if (w->type == MOE_Q8_0 && st != MOE_BF16) return fail(MOE_EINVAL, "Q8_0 weights need BF16 src1");
+    if (w->type == MOE_F32 && st != MOE_F32) return fail(MOE_EINVAL, "F32 weights need F32 src1");
+    return MOE_OK;
+}
+
+RowIdsArgs row_ids_args(const int32_t* ids, int64_t n, int32_t k, int32_t E, int32_t B,
+                        const RowIdsPlan& p) {
+    RowIdsArgs a{};
+    a.ids = ids;
+    a.n = n;
+    a.k = k;
+    a.E = E;
+    a.B = B;
+    a.ids_src1 = p.ids_src1;
+    a.ids_dst = p.ids_dst;
+    a.bounds = p.bounds;
+    a.chunk_cnt = p.chunk_cnt;
+    a.bucket_tot = p.bucket_tot;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+        case MOE_ELIMIT: return "MOE_ELIMIT: size limit exceeded";
+        case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+        case MOE_EHIP: return "MOE_EHIP: HIP launch failed";
+    }
+    return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
+                        const moe_options* opt) {
+    moe_status s;
+    if ((s = check_tokens(n_tokens, n_used))) return s;
+    if ((s = check_experts(n_experts))) return s;
+    if (act_width <= 0) return fail(MOE_EINVAL, "act_width must be > 0");
+    return select_path(n_tokens, n_used, n_experts, act_width, opt);
+}
+
+size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_experts) {
+    if (check_tokens(n_tokens, n_used) || check_experts(n_experts)) return 0;
+    Carve c(nullptr);
+    carve_row_ids(c, n_tokens * n_used, n_experts, false, false);
+    return c.off;
+}
+
+moe_status moe_row_ids(const int32_t* ids, int64_t n_tokens, int32_t n_used, int32_t n_experts,
+                       int32_t src1_rows_per_token, int32_t* ids_src1, int32_t* ids_dst,
+                       int32_t* expert_bounds, void* ws, size_t ws_bytes, void* stream) {
+    moe_status s;
+    g_err.clear();
+    if ((s = check_tokens(n_tokens, n_used))) return s;
+    if ((s = check_experts(n_experts))) return s;
+    if (src1_rows_per_token != 1 && src1_rows_per_token != n_used)
+        return fail(MOE_EINVAL, "src1_rows_per_token must be 1 or n_used");
+    if (!expert_bounds || (n_tokens > 0 && (!ids || !ids_src1 || !ids_dst)))
+        return fail(MOE_EINVAL, "NULL pointer argument");
+    const size_t need = moe_row_ids_workspace_size(n_tokens, n_used, n_experts);
+    if (need > ws_bytes || (need && !ws)) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
+    Carve c(ws);
+    RowIdsPlan p = carve_row_ids(c, n_tokens * n_used, n_experts, false, false);
+    p.ids_src1 = ids_src1;
+    p.ids_dst = ids_dst;
+    p.bounds = expert_bounds;
+    const RowIdsArgs a = row_ids_args(ids, n_tokens * n_used, n_used, n_experts, src1_rows_per_token, p);
+    return hip_check(launch_row_ids(a, (hipStream_t)stream, nullptr), "row ids");
+}
+
+size_t moe_ffn_fused_workspace_size(const moe_weights* gate, const moe_weights* sh_gate,
+                                    moe_dtype x_type, int64_t n_tokens, int32_t n_used,
+                                    const moe_options* opt) {
+    if (!gate) return 0;
+    FfnDims d{};
+    const moe_weights up = *gate;
+    moe_weights down = *gate;
+    down.rows = gate->cols;
+    down.cols = gate->rows;
+    const moe_weights* su = nullptr;
+    moe_weights sup{}, sdown{};
+    if (sh_gate && sh_gate->n_mat) {
+        sup = *sh_gate;
+        sdown = *sh_gate;
+        sdown.rows = sh_gate->cols;
+        sdown.cols = sh_gate->rows;
+        su = &sup;
+    }
+    if (validate_ffn(gate, &up, &down, (su ? sh_gate : nullptr), su, (su ? &sdown : nullptr),
+                     x_type, n_tokens, n_used, &d))
+        return 0;
+    const int path = select_path(d.T, d.k, d.E, ffn_act_width(d), opt);
+    if (path < 0) return 0;
+    Carve c(nullptr);
+    carve_ffn(c, d, path);
+    return c.off;
+}
+
+moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const moe_weights* down,
+                         const moe_weights* sh_gate, const moe_weights* sh_up,
+                         const moe_weights* sh_down, const void* x, moe_dtype x_type,
+                         const int32_t* ids, const float* route_w, int64_t n_tokens, int32_t n_used,
+                         float* out, const moe_options* opt, void* ws, size_t ws_bytes,
+                         void* stream) {
+    g_err.clear();
+    FfnDims d{};
+    moe_status s = validate_ffn(gate, up, down, sh_gate, sh_up, sh_down, x_type, n_tokens, n_used, &d);
+    if (s) return s;
+    if (n_tokens == 0) return MOE_OK;
+    if (!x || !ids || !route_w || !out) return fail(MOE_EINVAL, "NULL pointer argument");
+    const int path = select_path(d.T, d.k, d.E, ffn_act_width(d), opt);
+    if (path < 0) return (moe_status)path;
+    Carve sz(nullptr);
+    carve_ffn(sz, d, path);
+    if (sz.off > ws_bytes || !ws) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", sz.off);
+    Carve c(ws);
+    const FfnPlan p = carve_ffn(c, d, path);
+    const hipStream_t st = (hipStream_t)stream;
+    Timer tm(opt, st);
+    const int64_t n = d.T * d.k;
+    const bool shared = d.S > 0;
+
+    if (path == 1) {
+        const int bm = gemm_tile_m(p.msub);
+        RowIdsArgs ra = row_ids_args(ids, n, d.k, d.E, 1, p.r);
+        ra.tile_off[0] = p.r.tile_a;
+        ra.tile_m[0] = bm;
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+
+        GemmArgs g{};
+        g.mode = 1;
+        g.n_prob = shared ? 2 : 1;
+        GemmProblem& r = g.p[0];
+        r.qs1 = (const int8_t*)gate->data;
+        r.d1 = (const uint16_t*)gate->scales;
+        r.qs2 = (const int8_t*)up->data;
+        r.d2 = (const uint16_t*)up->scales;
+        r.N = d.n_ff;
+        r.K = d.n_embd;
+        r.bounds = p.r.bounds;
+        r.tile_off = p.r.tile_a;
+        r.n_seg = d.E;
+        r.m_tiles_max = (int32_t)m_tiles_bound(n, d.E, bm);
+        r.A = (const uint16_t*)x;
+        r.lda = d.n_embd;
+        r.a_rows = p.r.ids_src1;
+        r.out = p.h;
+        r.ldo = d.n_ff;
+        if (shared) {
+            GemmProblem& q = g.p[1];
+            q.qs1 = (const int8_t*)sh_gate->data;
+            q.d1 = (const uint16_t*)sh_gate->scales;
+            q.qs2 = (const int8_t*)sh_up->data;
+            q.d2 = (const uint16_t*)sh_up->scales;
+            q.N = d.n_ff_sh;
+            q.K = d.n_embd;
+            q.n_seg = d.S;
+            q.seg_len = (int32_t)d.T;
+            q.m_tiles_max = (int32_t)(d.S * ((d.T + bm - 1) / bm));
+            q.A = (const uint16_t*)x;
+            q.lda = d.n_embd;
+            q.a_row_mod = (int32_t)d.T;
+            q.out = p.hsh;
+            q.ldo = d.n_ff_sh;
+        }
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "gate/up grouped GEMM"))) return s;
+        tm.end();
+
+        GemmArgs g2{};
+        g2.mode = 0;
+        g2.n_prob = shared ? 2 : 1;
+        GemmProblem& r2 = g2.p[0];
+        r2.qs1 = (const int8_t*)down->data;
+        r2.d1 = (const uint16_t*)down->scales;
+        r2.N = d.n_embd;
+        r2.K = d.n_ff;
+        r2.bounds = p.r.bounds;
+        r2.tile_off = p.r.tile_a;
+        r2.n_seg = d.E;
+        r2.m_tiles_max = r.m_tiles_max;
+        r2.A = (const uint16_t*)p.h;
+        r2.lda = d.n_ff;
+        r2.out = p.y;
+        r2.ldo = d.n_embd;
+        r2.out_rows = p.r.ids_dst;
+        if (shared) {
+            GemmProblem& q = g2.p[1];
+            q.qs1 = (const int8_t*)sh_down->data;
+            q.d1 = (const uint16_t*)sh_down->scales;
+            q.N = d.n_embd;
+            q.K = d.n_ff_sh;
+            q.n_seg = d.S;
+            q.seg_len = (int32_t)d.T;
+            q.m_tiles_max = g.p[1].m_tiles_max;
+            q.A = (const uint16_t*)p.hsh;
+            q.lda = d.n_ff_sh;
+            q.out = p.ysh;
+            q.ldo = d.n_embd;
+        }
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8(g2, p.msub, st), "down grouped GEMM"))) return s;
+        tm.end();
+    } else {
+        DecArgs a{};
+        a.ids = ids;
+        a.T = (int32_t)d.T;
+        a.k = d.k;
+        a.E = d.E;
+        a.rw = DecWeights{(const int8_t*)gate->data, (const uint16_t*)gate->scales,
+                          (const int8_t*)up->data, (const uint16_t*)up->scales, d.E, d.n_ff, d.n_embd};
+        if (shared)
+            a.sw = DecWeights{(const int8_t*)sh_gate->data, (const uint16_t*)sh_gate->scales,
+                              (const int8_t*)sh_up->data, (const uint16_t*)sh_up->scales, d.S,
+                              d.n_ff_sh, d.n_embd};
+        a.act = x;
+        a.act_type = 1;
+        a.act_B = 1;
+        a.sact = x;
+        a.sact_type = 1;
+        a.sact_jstride = 0;
+        a.out = (float*)p.h;
+        a.sout = (float*)p.hsh;
+        a.mode = 1;
+        a.d_max = (int32_t)(n < d.E ? n : d.E);
+        a.rows_per_block = 16;
+        tm.begin();
+        if ((s = hip_check(launch_decode(a, st), "gate/up GEMV"))) return s;
+        tm.end();
+
+        DecArgs b{};
+        b.ids = ids;
+        b.T = (int32_t)d.T;
+        b.k = d.k;
+        b.E = d.E;
+        b.rw = DecWeights{(const int8_t*)down->data, (const uint16_t*)down->scales, nullptr, nullptr,
+                          d.E, d.n_embd, d.n_ff};
+        if (shared)
+            b.sw = DecWeights{(const int8_t*)sh_down->data, (const uint16_t*)sh_down->scales, nullptr,
+                              nullptr, d.S, d.n_embd, d.n_ff_sh};
+        b.act = p.h;
+        b.act_type = 0;
+        b.act_B = d.k;
+        b.sact = p.hsh;
+        b.sact_type = 0;
+        b.sact_jstride = d.T;
+        b.out = (float*)p.y;
+        b.sout = (float*)p.ysh;
+        b.mode = 0;
+        b.d_max = a.d_max;
+        b.rows_per_block = 16;
+        tm.begin();
+        if ((s = hip_check(launch_decode(b, st), "down GEMV"))) return s;
+        tm.end();
+    }
+    ReduceArgs rd{};
+    rd.ids = ids;
+    rd.route_w = route_w;
+    rd.T = (int32_t)d.T;
+    rd.k = d.k;
+    rd.E = d.E;
+    rd.N = d.n_embd;
+    rd.y = (const float*)p.y;
+    rd.ysh = (const float*)p.ysh;
+    rd.S = d.S;
+    rd.out = out;
+    rd.mode = 0;
+    tm.begin();
+    if ((s = hip_check(launch_reduce(rd, st), "reduce"))) return s;
+    tm.end();
+    return MOE_OK;
+}
+
+size_t moe_mul_mat_id_workspace_size(const moe_weights* w, moe_dtype src1_type,
+                                     int32_t src1_rows_per_token, int64_t n_tokens,
+                                     int32_t n_used, const moe_options* opt) {
+    if (validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used)) return 0;
+    const bool q8 = w->type == MOE_Q8_0;
+    const int path = q8 ? select_path(n_tokens, n_used, (int32_t)w->n_mat, w->cols, opt) : 1;
+    if (path < 0) return 0;
+    // the weighted and unweighted calls use the same plan size when weighted
+    Carve c(nullptr);
+    carve_mmid(c, n_tokens, n_used, (int32_t)w->n_mat, w->rows, true, q8, path);
+    return c.off;
+}
+
+moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1_type,
+                          int32_t src1_rows_per_token, const int32_t* ids, int64_t n_tokens,
+                          int32_t n_used, const float* route_w, float* dst, const moe_options* opt,
+                          void* ws, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    moe_status s = validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used);
+    if (s) return s;
+    if (n_tokens == 0) return MOE_OK;
+    if (!src1 || !ids || !dst) return fail(MOE_EINVAL, "NULL pointer argument");
+    const bool q8 = w->type == MOE_Q8_0;
+    const int32_t E = (int32_t)w->n_mat, N = (int32_t)w->rows, K = (int32_t)w->cols;
+    const int32_t B = src1_rows_per_token, k = n_used;
+    const int path = q8 ? select_path(n_tokens, k, E, K, opt) : 1;
+    if (path < 0) return (moe_status)path;
+    const bool weighted = route_w != nullptr;
+    Carve sz(nullptr);
+    carve_mmid(sz, n_tokens, k, E, N, weighted, q8, path);
+    if (sz.off > ws_bytes || (sz.off && !ws)) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", sz.off);
+    Carve c(ws);
+    const MmidPlan p = carve_mmid(c, n_tokens, k, E, N, weighted, q8, path);
+    const hipStream_t st = (hipStream_t)stream;
+    Timer tm(opt, st);
+    const int64_t n = n_tokens * k;
+    float* slot_out = weighted ? (float*)p.y : dst;  // per-slot rows [T*k][N]
+
+    if (!q8 || path == 1) {
+        const int bm = gemm_tile_m(p.msub);
+        RowIdsArgs ra = row_ids_args(ids, n, k, E, B, p.r);
+        if (q8) {
+            ra.tile_off[0] = p.r.tile_a;
+            ra.tile_m[0] = bm;
+        }
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+        if (q8) {
+            GemmArgs g{};
+            g.mode = 0;
+            g.n_prob = 1;
+            GemmProblem& r = g.p[0];
+            r.qs1 = (const int8_t*)w->data;
+            r.d1 = (const uint16_t*)w->scales;
+            r.N = N;
+            r.K = K;
+            r.bounds = p.r.bounds;
+            r.tile_off = p.r.tile_a;
+            r.n_seg = E;
+            r.m_tiles_max = (int32_t)m_tiles_bound(n, E, bm);
+            r.A = (const uint16_t*)src1;
+            r.lda = K;
+            r.a_rows = p.r.ids_src1;
+            r.out = slot_out;
+            r.ldo = N;
+            r.out_rows = p.r.ids_dst;
+            tm.begin();
+            if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "grouped GEMM"))) return s;
+            tm.end();
+        } else {
+            GemmF32Args g{};
+            g.W = (const float*)w->data;
+            g.A = (const float*)src1;
+            g.ids = ids;
+            g.ids_src1 = p.r.ids_src1;
+            g.ids_dst = p.r.ids_dst;
+            g.bounds = p.r.bounds;
+            g.n_slots = n;
+            g.E = E;
+            g.N = N;
+            g.K = K;
+            g.out = slot_out;
+            tm.begin();
+            if ((s = hip_check(launch_gemm_f32(g, st), "fp32 grouped matmul"))) return s;
+            tm.end();
+        }
+    } else {
+        DecArgs a{};
+        a.ids = ids;
+        a.T = (int32_t)n_tokens;
+        a.k = k;
+        a.E = E;
+        a.rw = DecWeights{(const int8_t*)w->data, (const uint16_t*)w->scales, nullptr, nullptr, E, N, K};
+        a.act = src1;
+        a.act_type = 1;
+        a.act_B = B;
+        a.out = slot_out;
+        a.mode = 0;
+        a.d_max = (int32_t)(n < E ? n : E);
+        a.rows_per_block = 16;
+        tm.begin();
+        if ((s = hip_check(launch_decode(a, st), "GEMV"))) return s;
+        tm.end();
+    }
+    ReduceArgs rd{};
+    rd.ids = ids;
+    rd.route_w = route_w;
+    rd.T = (int32_t)n_tokens;
+    rd.k = k;
+    rd.E = E;
+    rd.N = N;
+    rd.y = slot_out;
+    rd.out = dst;
+    rd.mode = weighted ? 0 : 1;
+    tm.begin();
+    if ((s = hip_check(launch_reduce(rd, st), weighted ? "reduce" : "zero invalid slots"))) return s;
+    tm.end();
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,284 @@
+// Row-id pass (K1): the three maps of the deterministic MoE path -- src1 rows
+// reordered so every expert's rows are contiguous (ids_src1), the same order for
+// dst (ids_dst) and each expert's bounds (expert_bounds) -- built without any
+// atomic slot counter ("CUDA: better MoE implementation", sections 2 and 2.1: the
+// old gather claimed destination slots with an atomic increment, which was slow
+// and made the row order, hence the float summation order, change run to run).
+//
+// gfx950 design: a stable counting sort built from wavefront primitives.
+//   * Each wave owns a contiguous range of entries (t*k + s order) and walks it 64
+//     at a time. Lanes holding the same bucket find each other with one ballot per
+//     bit of the bucket id; the group's lowest lane adds the group size to the
+//     wave's LDS counter (one writer per counter, so no atomics), and a lane's rank
+//     inside its group is a masked bit count (mbcnt).
+//   * Per-bucket exclusive scans over waves (and, for large inputs, over
+//     workgroups), then over buckets, give every (wave, bucket) its first output
+//     position; a second walk over the same range places every entry. Entries keep
+//     their (t, s) order inside a bucket, so the result is unique.
+//   * Bucket E collects ids outside [0, E): they land after all expert segments.
+//   * Inputs up to kRowIdsOneBlockMax entries run as one 512-thread workgroup (one
+//     launch); larger ones use count / scan-over-chunks / scan-over-buckets / place.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBatchesPerWave = 16;                    // multi-block chunk geometry
+constexpr int64_t kChunk = (int64_t)kWaves * 64 * kBatchesPerWave;
+
+__device__ __forceinline__ int bucket_of(int32_t e, int32_t E) {
+    return (e >= 0 && e < E) ? e : E;
+}
+
+// Lanes (among `active`) whose bucket equals this lane's bucket.
+__device__ __forceinline__ uint64_t match_bucket(int b, uint64_t active, int nbits) {
+    uint64_t m = active;
+    for (int i = 0; i < nbits; i++) {
+        const int bit = (b >> i) & 1;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// Number of set bits of m strictly below this lane.
+__device__ __forceinline__ int rank_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Histogram of entries [beg, end) into this wave's counter row (no atomics: each
+// bucket present in a batch has exactly one leader lane).
+__device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t end, int32_t E,
+                           int nbits, int32_t* cnt_w) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t base = beg; base < end; base += 64) {
+        const int64_t i = base + lane;
+        const bool act = i < end;
+        const int b = act ? bucket_of(ids[i], E) : 0;
+        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
+    }
+}
+
+// Place entries [beg, end): position = base[b] + running[b] + rank in batch.
+__device__ void wave_place(const RowIdsArgs& a, int64_t beg, int64_t end, int nbits,
+                           const int32_t* base, int32_t* run_w) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t bb = beg; bb < end; bb += 64) {
+        const int64_t i = bb + lane;
+        const bool act = i < end;
+        const int b = act ? bucket_of(a.ids[i], a.E) : 0;
+        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        int32_t prev = 0;
+        if (act) {
+            prev = run_w[b];
+            const int32_t pos = base[b] + prev + rank_below(m);
+            const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
+            const int32_t t = ii / a.k;
+            const int32_t s = ii - t * a.k;
+            a.ids_src1[pos] = t * a.B + s % a.B;
+            a.ids_dst[pos] = ii;
+            if (a.inv) a.inv[i] = pos;
+        }
+        // every lane has read its counter before the group's leader bumps it
+        __builtin_amdgcn_wave_barrier();
+        if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// In-place exclusive scan of v[0, n) (LDS) by all threads of the block; returns the
+// total. wsum: LDS scratch of kWaves ints.
+__device__ int32_t block_scan(int32_t* v, int n, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int per = (n + kThreads - 1) / kThreads;
+    const int beg = min(tid * per, n), end = min(beg + per, n);
+    int32_t s = 0;
+    for (int i = beg; i < end; i++) s += v[i];
+    int32_t x = s;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t pre = 0, total = 0;
+    for (int j = 0; j < kWaves; j++) {
+        if (j < w) pre += wsum[j];
+        total += wsum[j];
+    }
+    int32_t run = pre + x - s;
+    for (int i = beg; i < end; i++) {
+        const int32_t t = v[i];
+        v[i] = run;
+        run += t;
+    }
+    __syncthreads();
+    return total;
+}
+
+// bstart[0..NB) holds bucket starts: write bounds and the M-tile prefixes.
+__device__ void write_bounds_and_tiles(const RowIdsArgs& a, const int32_t* bstart, int32_t* tmp,
+                                       int32_t* wsum) {
+    const int E = a.E, NB = E + 1;
+    for (int b = threadIdx.x; b < NB; b += kThreads) a.bounds[b] = bstart[b];
+    for (int q = 0; q < 2; q++) {
+        if (!a.tile_off[q]) continue;  // uniform across the block
+        const int tm = a.tile_m[q];
+        for (int b = threadIdx.x; b < NB; b += kThreads)
+            tmp[b] = b < E ? (bstart[b + 1] - bstart[b] + tm - 1) / tm : 0;
+        __syncthreads();
+        block_scan(tmp, NB, wsum);
+        for (int b = threadIdx.x; b < NB; b += kThreads) a.tile_off[q][b] = tmp[b];
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ int bucket_bits(int NB) { return 32 - __clz(NB - 1); }
+
+// ---------------------------------------------------------------- one workgroup
+__global__ __launch_bounds__(kThreads) void k_row_ids_single(RowIdsArgs a) {
+    __shared__ int32_t cnt[kWaves * kMaxBuckets];
+    __shared__ int32_t bstart[kMaxBuckets + 1];
+    __shared__ int32_t tmp[kMaxBuckets + 1];
+    __shared__ int32_t wsum[kWaves];
+    const int NB = a.E + 1, nbits = bucket_bits(NB);
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t per = ((a.n + kWaves * 64 - 1) / (kWaves * 64)) * 64;
+    const int64_t beg = min((int64_t)w * per, a.n), end = min(beg + per, a.n);
+    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
+    __syncthreads();
+    for (int b = threadIdx.x; b < NB; b += kThreads) {
+        int32_t run = 0;
+        for (int v = 0; v < kWaves; v++) {
+            const int32_t t = cnt[v * NB + b];
+            cnt[v * NB + b] = run;
+            run += t;
+        }
+        bstart[b] = run;
+    }
+    __syncthreads();
+    block_scan(bstart, NB, wsum);
+    write_bounds_and_tiles(a, bstart, tmp, wsum);
+    wave_place(a, beg, end, nbits, bstart, cnt + w * NB);
+}
+
+// ---------------------------------------------------------------- multi-block
+__global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
+    __shared__ int32_t cnt[kWaves * kMaxBuckets];
+    const int NB = a.E + 1, nbits = bucket_bits(NB);
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const int64_t per = (int64_t)64 * kBatchesPerWave;
+    const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
+    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
+    __syncthreads();
+    for (int b = threadIdx.x; b < NB; b += kThreads) {
+        int32_t s = 0;
+        for (int v = 0; v < kWaves; v++) s += cnt[v * NB + b];
+        a.chunk_cnt[(int64_t)blockIdx.x * NB + b] = s;
+    }
+}
+
+// One block per bucket: exclusive scan of that bucket's per-chunk counts.
+__global__ __launch_bounds__(kThreads) void k_row_ids_scan_chunks(RowIdsArgs a) {
+    __shared__ int32_t wsum[kWaves];
+    const int NB = a.E + 1, b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t nc = a.n_chunks;
+    const int64_t per = (nc + kThreads - 1) / kThreads;
+    const int64_t beg = min((int64_t)tid * per, nc), end = min(beg + per, nc);
+    int32_t s = 0;
+    for (int64_t c = beg; c < end; c++) s += a.chunk_cnt[c * NB + b];
+    int32_t x = s;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t pre = 0, total = 0;
+    for (int j = 0; j < kWaves; j++) {
+        if (j < w) pre += wsum[j];
+        total += wsum[j];
+    }
+    int32_t run = pre + x - s;
+    for (int64_t c = beg; c < end; c++) {
+        const int32_t t = a.chunk_cnt[c * NB + b];
+        a.chunk_cnt[c * NB + b] = run;
+        run += t;
+    }
+    if (tid == 0) a.bucket_tot[b] = total;
+}
+
+// Single block: bucket starts, bounds, tile prefixes; bucket_tot becomes the starts.
+__global__ __launch_bounds__(kThreads) void k_row_ids_scan_buckets(RowIdsArgs a) {
+    __shared__ int32_t bstart[kMaxBuckets + 1];
+    __shared__ int32_t tmp[kMaxBuckets + 1];
+    __shared__ int32_t wsum[kWaves];
+    const int NB = a.E + 1;
+    for (int b = threadIdx.x; b < NB; b += kThreads) bstart[b] = a.bucket_tot[b];
+    __syncthreads();
+    block_scan(bstart, NB, wsum);
+    write_bounds_and_tiles(a, bstart, tmp, wsum);
+    for (int b = threadIdx.x; b < NB; b += kThreads) a.bucket_tot[b] = bstart[b];
+}
+
+__global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
+    __shared__ int32_t cnt[kWaves * kMaxBuckets];
+    __shared__ int32_t base[kMaxBuckets];
+    const int NB = a.E + 1, nbits = bucket_bits(NB);
+    const int w = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+    const int64_t per = (int64_t)64 * kBatchesPerWave;
+    const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
+    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
+    __syncthreads();
+    for (int b = threadIdx.x; b < NB; b += kThreads) {
+        int32_t run = 0;
+        for (int v = 0; v < kWaves; v++) {
+            const int32_t t = cnt[v * NB + b];
+            cnt[v * NB + b] = run;
+            run += t;
+        }
+        base[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)blockIdx.x * NB + b];
+    }
+    __syncthreads();
+    wave_place(a, beg, end, nbits, base, cnt + w * NB);
+}
+
+}  // namespace
+
+size_t row_ids_scratch_bytes(int64_t n, int32_t E) {
+    if (n <= kRowIdsOneBlockMax) return 0;
+    const int64_t nc = (n + kChunk - 1) / kChunk;
+    const size_t a = (size_t)nc * (size_t)(E + 1) * sizeof(int32_t);
+    return ((a + kAlign - 1) / kAlign) * kAlign + (size_t)(E + 1) * sizeof(int32_t);
+}
+
+hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches) {
+    RowIdsArgs a = a0;
+    if (a.n <= kRowIdsOneBlockMax) {
+        k_row_ids_single<<<1, kThreads, 0, st>>>(a);
+        if (n_launches) *n_launches = 1;
+        return hipGetLastError();
+    }
+    a.n_chunks = (a.n + kChunk - 1) / kChunk;
+    k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
+    k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
+    k_row_ids_scan_buckets<<<1, kThreads, 0, st>>>(a);
+    k_row_ids_place<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
+    if (n_launches) *n_launches = 4;
+    return hipGetLastError();
+}
+
+}  // namespace moe

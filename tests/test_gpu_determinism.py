@@ -1,0 +1,67 @@
+"""Run-to-run bit identity: the pages' reproducibility problem (same model, input and
+seed gave different outputs, "CUDA: better MoE implementation", section 1.1) must not
+exist here. Ten calls per workload, with the workspace overwritten by 0xFF bytes
+(NaN patterns) before every call, must give byte-identical outputs."""
+import numpy as np
+import pytest
+import torch
+
+import indirect_expert_matmul_amd as moe
+import synth
+from moe_testutil import run_ffn, upload_ffn, upload_mmid
+
+pytestmark = pytest.mark.gpu
+
+
+def _same_bytes(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("name,path", [("lite", moe.PATH_AUTO), ("dec1", moe.PATH_AUTO),
+                                       ("dec8", moe.PATH_AUTO), ("dec8", moe.PATH_GEMM),
+                                       ("skew", moe.PATH_AUTO)])
+def test_ffn_ten_runs_bit_identical(name, path):
+    inp = synth.make_inputs(name)
+    dv = upload_ffn(inp)
+    T, k = inp["ids"].shape
+    need = moe.moe_ffn_fused_workspace_size(dv["gate"], dv["shared"][0] if dv["shared"] else None,
+                                            T, k, path=path)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(10):
+        ws.fill_(255)
+        outs.append(run_ffn(dv, path=path, workspace=ws))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    for o in outs[1:]:
+        assert _same_bytes(o, outs[0])
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_tiny_ten_runs_bit_identical(weighted):
+    inp = synth.make_inputs("tiny")
+    dv = upload_mmid(inp)
+    rw = dv["route_w"] if weighted else None
+    outs = [moe.moe_mul_mat_id(dv["w"], dv["x"], dv["ids"], route_w=rw) for _ in range(10)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert _same_bytes(o, outs[0])
+
+
+def test_streams_interleaved_calls_stay_identical():
+    """Many calls queued back to back on two streams with separate workspaces (the
+    stream-order lifetime question the pages discuss in section 5): every result must
+    equal the single-call result."""
+    inp = synth.make_inputs("lite")
+    dv = upload_ffn(inp)
+    ref = run_ffn(dv)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(20):
+        st = s1 if i % 2 == 0 else s2
+        with torch.cuda.stream(st):
+            outs.append(run_ffn(dv, stream=st))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert _same_bytes(o, ref)

@@ -1,0 +1,160 @@
+"""GPU parity of moe_mul_mat_id and moe_ffn_fused against the fp64 oracle.
+
+Tolerances (normwise max relative error per output tensor, as the op's accuracy
+contract states): 2e-2 on the bf16-MFMA grouped GEMM path, 1e-5 on the fp32 paths
+(fp32 mul_mat_id and the fp32 GEMV decode path). Expected errors are about 2e-3 and
+1e-6; the gates leave room for rounding-order differences only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import indirect_expert_matmul_amd as moe
+import oracle
+import synth
+from moe_testutil import (TOL_FP32, TOL_MFMA, dev_bf16, dev_f32, dev_i32, normwise, run_ffn,
+                          upload_ffn, upload_mmid)
+
+pytestmark = pytest.mark.gpu
+
+
+def _tol(path):
+    return TOL_MFMA if path == moe.PATH_GEMM else TOL_FP32
+
+
+# ------------------------------------------------------------------ mul_mat_id
+
+def test_tiny_fp32_mul_mat_id():
+    inp = synth.make_inputs("tiny")
+    dv = upload_mmid(inp)
+    per_slot = moe.moe_mul_mat_id(dv["w"], dv["x"], dv["ids"])
+    weighted = moe.moe_mul_mat_id(dv["w"], dv["x"], dv["ids"], route_w=dv["route_w"])
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w"], None, inp["x"], "f32", inp["ids"])
+    refw = oracle.mul_mat_id(inp["w"], None, inp["x"], "f32", inp["ids"], inp["route_w"])
+    assert per_slot.shape == (16, 2, 32)
+    assert normwise(per_slot.cpu().numpy(), ref) <= TOL_FP32
+    assert normwise(weighted.cpu().numpy(), refw) <= TOL_FP32
+
+
+@pytest.mark.parametrize("path", [moe.PATH_GEMM, moe.PATH_GEMV])
+@pytest.mark.parametrize("E,k,T,K,N,B_is_k,bad", [
+    (6, 3, 9, 96, 40, False, False),     # K tail (96 = 64 + 32), ragged N
+    (6, 3, 9, 96, 40, True, True),       # one src1 row per slot, invalid ids
+    (16, 2, 50, 256, 300, False, False), # several N tiles plus a ragged one
+    (4, 4, 60, 128, 64, False, True),    # k = E, several M tiles per expert
+])
+def test_q8_mul_mat_id(path, E, k, T, K, N, B_is_k, bad):
+    if path == moe.PATH_GEMV and T * k > 256:
+        pytest.skip("GEMV path bound")
+    rng = np.random.default_rng(E * 1000 + T)
+    ids = synth.draw_ids_uniform(3, T, E, k)
+    if bad:
+        ids[0, 0], ids[T // 2, k - 1] = -1, E + 3
+    inp = synth.make_custom_mmid(7, E, k, T, K, N, ids=ids)
+    B = k if B_is_k else 1
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T * B, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), src1_rows_per_token=B, path=path)
+    gotw = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                              src1_rows_per_token=B, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, None, B)
+    refw = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], B)
+    g = got.cpu().numpy()
+    assert normwise(g, ref) <= _tol(path)
+    assert normwise(gotw.cpu().numpy(), refw) <= _tol(path)
+    invalid = (ids < 0) | (ids >= E)
+    assert np.all(g[invalid] == 0.0)
+
+
+# ------------------------------------------------------------------------- FFN
+
+@pytest.mark.parametrize("path", [moe.PATH_GEMM, moe.PATH_GEMV])
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [
+    (8, 2, 12, 96, 64, 0),       # K tails on both projections
+    (8, 3, 20, 128, 96, 2),      # shared experts, ragged N tiles
+    (32, 4, 8, 256, 160, 1),
+    (4, 6, 10, 64, 32, 1),       # n_used > n_experts: duplicate experts inside tokens
+    (16, 1, 1, 320, 192, 2),     # a single token
+])
+def test_ffn_small_shapes(path, E, k, T, n_embd, n_ff, S):
+    if path == moe.PATH_GEMV and T * k > 256:
+        pytest.skip("GEMV path bound")
+    ids = np.random.default_rng(T * 31 + E).integers(0, E, size=(T, k)).astype(np.int32)
+    inp = synth.make_custom_ffn(11 + E, E, k, T, n_embd, n_ff, S, ids=ids)
+    got = run_ffn(upload_ffn(inp), path=path)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= _tol(path)
+
+
+def test_ffn_invalid_ids_and_shared_width():
+    """Out-of-range ids contribute nothing; shared experts of a different width."""
+    E, k, T, n_embd, n_ff = 8, 3, 24, 128, 64
+    ids = synth.draw_ids_uniform(5, T, E, k)
+    ids[1, 0], ids[7, 2], ids[20, 1] = -5, E, 1 << 20
+    inp = synth.make_custom_ffn(5, E, k, T, n_embd, n_ff, 0, ids=ids)
+    sh = synth.make_custom_ffn(6, 2, 1, T, n_embd, 96, 0)
+    for n in ("gate", "up", "down"):
+        inp["sh_" + n + "_qs"], inp["sh_" + n + "_d"] = sh[n + "_qs"], sh[n + "_d"]
+    ref = oracle.ffn(inp)
+    dv = upload_ffn(inp)
+    for path in (moe.PATH_GEMM, moe.PATH_GEMV):
+        got = run_ffn(dv, path=path)
+        torch.cuda.synchronize()
+        assert normwise(got.cpu().numpy(), ref) <= _tol(path), path
+
+
+def test_lite_full():
+    inp = synth.make_inputs("lite")
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("lite normwise error %.3g" % err)
+    assert err <= TOL_MFMA
+
+
+@pytest.mark.parametrize("name", ["dec1", "dec8"])
+@pytest.mark.parametrize("path", [moe.PATH_AUTO, moe.PATH_GEMM])
+def test_decode_full(name, path):
+    inp = synth.make_inputs(name)
+    got = run_ffn(upload_ffn(inp), path=path)
+    torch.cuda.synchronize()
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("%s path %d normwise error %.3g" % (name, path, err))
+    assert err <= (TOL_FP32 if path == moe.PATH_AUTO else TOL_MFMA)
+
+
+def _sample_tokens(ids, n, seed):
+    """Tokens for sampled checks: random ones plus the first tokens of the largest
+    and smallest expert segments and the first and last token."""
+    T = ids.shape[0]
+    rng = np.random.default_rng(seed)
+    cnt = np.bincount(ids.ravel()[ids.ravel() >= 0])
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    for e in (int(np.argmax(cnt)), int(np.argmin(np.where(cnt > 0, cnt, 1 << 30)))):
+        pick.add(int(np.nonzero((ids == e).any(axis=1))[0][0]))
+    return np.array(sorted(pick))
+
+
+def test_skew_full_size_sampled():
+    inp = synth.make_inputs("skew")
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    rows = _sample_tokens(inp["ids"], 160, 1)
+    err = normwise(got.cpu().numpy()[rows], oracle.ffn(inp, token_rows=rows))
+    print("skew sampled normwise error %.3g" % err)
+    assert err <= TOL_MFMA
+    assert torch.isfinite(got).all()
+
+
+def test_v3_full_size_sampled():
+    inp = synth.make_inputs("v3")
+    dv = upload_ffn(inp)
+    got = run_ffn(dv).cpu().numpy()
+    rows = _sample_tokens(inp["ids"], 24, 2)
+    ref = oracle.ffn(inp, token_rows=rows)
+    err = normwise(got[rows], ref)
+    print("v3 sampled normwise error %.3g" % err)
+    assert err <= TOL_MFMA
+    assert np.isfinite(got).all()
