@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="first run one device-to-device copy of this many MiB (a known-size "
+                        "kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -128,6 +131,12 @@ def main():
     need = moe.moe_ffn_fused_workspace_size(base[0], sh[0] if sh else None, T, k, path=args.path)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(i, events=None):
         (g, u, d), s = sets[i % R]
