@@ -26,8 +26,8 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxP = 8;               // activation rows staged per pass
-constexpr int kActLds = 48 * 1024;     // LDS bytes for staged activations
+constexpr int kR = 8;    // weight rows (row pairs for gate/up) per block
+constexpr int kSP = 1;   // token slots per pass
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -38,22 +38,41 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
-// padded LDS index of element k of a staged row (16 floats + 4 pad per group)
-__device__ __forceinline__ int xpad(int k) { return (k >> 4) * 20 + (k & 15); }
-__host__ __device__ __forceinline__ int padded_width(int K) { return ((K + 15) >> 4) * 20; }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+// Sum over the 64 lanes of a wave with DPP moves (no LDS traffic), in a fixed
+// tree: within each row of 16 lanes by shifts of 1, 2, 4, 8, then across rows by
+// the row broadcasts of lanes 15 and 31. The total lands in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_term(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 ROW_MASK, 0xf, true));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_term(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, true);
+}
+// Bitwise OR over the 64 lanes (same DPP tree as the sum), returned to every lane.
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+    v |= dpp_or_term<0x111, 0xf>(v);
+    v |= dpp_or_term<0x112, 0xf>(v);
+    v |= dpp_or_term<0x114, 0xf>(v);
+    v |= dpp_or_term<0x118, 0xf>(v);
+    v |= dpp_or_term<0x142, 0xa>(v);
+    v |= dpp_or_term<0x143, 0xc>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float wave_sum_lane63(float v) {
+    v += dpp_term<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_term<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_term<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_term<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_term<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_term<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
 
-// 16 int8 in q (four dwords) dotted with 16 staged floats at xs.
-__device__ __forceinline__ float dot16(const i32x4& q, const float* xs) {
-    const f32x4 x0 = *(const f32x4*)(xs + 0);
-    const f32x4 x1 = *(const f32x4*)(xs + 4);
-    const f32x4 x2 = *(const f32x4*)(xs + 8);
-    const f32x4 x3 = *(const f32x4*)(xs + 12);
+// 16 int8 in q (four dwords) dotted with 16 floats.
+__device__ __forceinline__ float dot16(const i32x4& q, const f32x4& x0, const f32x4& x1,
+                                       const f32x4& x2, const f32x4& x3) {
     float s = 0.f;
     s = fmaf((float)(int8_t)(q[0]), x0[0], s);
     s = fmaf((float)(int8_t)(q[0] >> 8), x0[1], s);
@@ -74,18 +93,24 @@ __device__ __forceinline__ float dot16(const i32x4& q, const float* xs) {
     return s;
 }
 
+// Block = 4 waves; it owns kR rows (row pairs in gate/up mode) of one expert and
+// every token slot routed to that expert. Wave w covers the 1024-wide K slices
+// w, w+4, ...: per slice each lane loads 16 int8 of each of the block's rows, their
+// fp16 scales, and 16 activation values of each slot, all issued back to back, then
+// accumulates in fp32. Lane sums use DPP; the 4 waves' partial sums are added in
+// wave order through LDS.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a, int P) {
-    extern __shared__ __attribute__((aligned(16))) float xs[];
+__global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
+    constexpr int M = MODE == 1 ? 2 : 1;  // weight matrices per row (gate and up)
     __shared__ int32_t s_ids[kDecMaxSlots];
     __shared__ int32_t s_first[kDecMaxSlots];
     __shared__ int32_t s_slots[kDecMaxSlots];
     __shared__ int32_t s_wcnt[kThreads / 64];
     __shared__ int32_t s_e;
+    __shared__ float s_red[kThreads / 64][kR][M][kSP];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int RB = a.rows_per_block;
-    const int nch_r = (a.rw.N + RB - 1) / RB;
+    const int nch_r = (a.rw.N + kR - 1) / kR;
     const int nb_r = a.d_max * nch_r;
     const bool routed = (int)blockIdx.x < nb_r;
     const DecWeights& W = routed ? a.rw : a.sw;
@@ -135,117 +160,327 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a, int P) {
         }
         __syncthreads();
     } else {
-        const int nch_s = (a.sw.N + RB - 1) / RB;
+        const int nch_s = (a.sw.N + kR - 1) / kR;
         const int b = blockIdx.x - nb_r;
         e = b / nch_s;
         chunk = b - e * nch_s;
         cnt = a.T;
     }
 
-    const int KP = padded_width(K);
-    const int n_lo = chunk * RB, n_hi = min(n_lo + RB, N);
+    const int n_lo = chunk * kR;
     const int n_it = (K + 1023) >> 10;
     const int64_t KB = K >> 5;
-    for (int p0 = 0; p0 < cnt; p0 += P) {
-        const int pc = min(P, cnt - p0);
-        // ---- stage activation rows p0 .. p0+pc-1 (fp32, padded)
-        for (int idx = tid; idx < pc * (K >> 2); idx += kThreads) {
-            const int p = idx / (K >> 2);
-            const int k = (idx - p * (K >> 2)) << 2;
-            const int slot = routed ? s_slots[p0 + p] : (p0 + p);
-            f32x4 v;
-            if (routed) {
-                const int t = slot / a.k, s = slot - t * a.k;
-                const int64_t row = (int64_t)t * a.act_B + s % a.act_B;
-                if (a.act_type == 1) {
-                    const uint16_t* src = (const uint16_t*)a.act + row * K + k;
-                    v = f32x4{bf16_bits_to_float(src[0]), bf16_bits_to_float(src[1]),
-                              bf16_bits_to_float(src[2]), bf16_bits_to_float(src[3])};
-                } else {
-                    v = *(const f32x4*)((const float*)a.act + row * K + k);
-                }
-            } else {
-                const int64_t row = (int64_t)e * a.sact_jstride + slot;
-                if (a.sact_type == 1) {
-                    const uint16_t* src = (const uint16_t*)a.sact + row * K + k;
-                    v = f32x4{bf16_bits_to_float(src[0]), bf16_bits_to_float(src[1]),
-                              bf16_bits_to_float(src[2]), bf16_bits_to_float(src[3])};
-                } else {
-                    v = *(const f32x4*)((const float*)a.sact + row * K + k);
-                }
-            }
-            *(f32x4*)(xs + p * KP + xpad(k)) = v;
+    const void* src = routed ? a.act : a.sact;
+    const int atype = routed ? a.act_type : a.sact_type;
+    // source activation row of slot p of this block
+    auto src_row = [&](int p) -> int64_t {
+        if (routed) {
+            const int slot = s_slots[p];
+            const int t = slot / a.k, s = slot - t * a.k;
+            return (int64_t)t * a.act_B + s % a.act_B;
         }
-        __syncthreads();
-        // ---- stream weight rows
-        for (int nrow = n_lo + wv; nrow < n_hi; nrow += kThreads / 64) {
-            float acc1[kMaxP], acc2[kMaxP];
+        return (int64_t)e * a.sact_jstride + p;
+    };
+
+    for (int p0 = 0; p0 < cnt; p0 += kSP) {
+        const int pc = min(kSP, cnt - p0);
+        float acc[kR][M][kSP];
 #pragma unroll
-            for (int p = 0; p < kMaxP; p++) acc1[p] = acc2[p] = 0.f;
-            const int64_t wrow = (int64_t)e * N + nrow;
-            const int8_t* q1 = W.qs1 + wrow * K;
-            const uint16_t* d1 = W.d1 + wrow * KB;
-            const int8_t* q2 = MODE == 1 ? W.qs2 + wrow * K : nullptr;
-            const uint16_t* d2 = MODE == 1 ? W.d2 + wrow * KB : nullptr;
-            for (int it = 0; it < n_it; it++) {
-                const int k = (it << 10) + (lane << 4);
-                if (k < K) {
-                    const i32x4 qa = *(const i32x4*)(q1 + k);
-                    const float da = half_bits_to_float(d1[k >> 5]);
-                    i32x4 qb;
-                    float db = 0.f;
-                    if (MODE == 1) {
-                        qb = *(const i32x4*)(q2 + k);
-                        db = half_bits_to_float(d2[k >> 5]);
-                    }
-                    const float* xk = xs + xpad(k);
+        for (int r = 0; r < kR; r++)
 #pragma unroll
-                    for (int p = 0; p < kMaxP; p++) {
-                        if (p < pc) {
-                            acc1[p] = fmaf(da, dot16(qa, xk + p * KP), acc1[p]);
-                            if (MODE == 1) acc2[p] = fmaf(db, dot16(qb, xk + p * KP), acc2[p]);
-                        }
-                    }
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int p = 0; p < kSP; p++) acc[r][m][p] = 0.f;
+        for (int it = wv; it < n_it; it += kThreads / 64) {
+            const int k = (it << 10) + (lane << 4);
+            const int kc = k < K ? k : 0;  // past K: a valid address, result unused
+            i32x4 q[kR][M];
+            uint32_t dsc[kR][M];
+#pragma unroll
+            for (int r = 0; r < kR; r++) {
+                const int64_t wr = (int64_t)e * N + min(n_lo + r, N - 1);
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    q[r][m] = *(const i32x4*)((m == 0 ? W.qs1 : W.qs2) + wr * K + kc);
+                    dsc[r][m] = (m == 0 ? W.d1 : W.d2)[wr * KB + (kc >> 5)];
                 }
             }
+            f32x4 xv[kSP][4];
 #pragma unroll
-            for (int p = 0; p < kMaxP; p++) {
-                if (p < pc) {
-                    const float g = wave_sum(acc1[p]);
-                    float r = g;
-                    if (MODE == 1) {
-                        const float u = wave_sum(acc2[p]);
-                        r = g / (1.0f + __expf(-g)) * u;
+            for (int p = 0; p < kSP; p++) {
+                const int64_t off = src_row(p0 + min(p, pc - 1)) * K + kc;
+                if (atype == 1) {
+                    const i32x4 r0 = *(const i32x4*)((const uint16_t*)src + off);
+                    const i32x4 r1 = *(const i32x4*)((const uint16_t*)src + off + 8);
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        const i32x4& rr = h ? r1 : r0;
+                        xv[p][2 * h] = f32x4{__builtin_bit_cast(float, (uint32_t)rr[0] << 16),
+                                             __builtin_bit_cast(float, (uint32_t)rr[0] & 0xffff0000u),
+                                             __builtin_bit_cast(float, (uint32_t)rr[1] << 16),
+                                             __builtin_bit_cast(float, (uint32_t)rr[1] & 0xffff0000u)};
+                        xv[p][2 * h + 1] = f32x4{__builtin_bit_cast(float, (uint32_t)rr[2] << 16),
+                                                 __builtin_bit_cast(float, (uint32_t)rr[2] & 0xffff0000u),
+                                                 __builtin_bit_cast(float, (uint32_t)rr[3] << 16),
+                                                 __builtin_bit_cast(float, (uint32_t)rr[3] & 0xffff0000u)};
                     }
-                    if (lane == 0) {
-                        if (routed) a.out[(int64_t)s_slots[p0 + p] * N + nrow] = r;
-                        else a.sout[((int64_t)e * a.T + p0 + p) * N + nrow] = r;
+                } else {
+                    const float* xp = (const float*)src + off;
+#pragma unroll
+                    for (int c = 0; c < 4; c++) xv[p][c] = *(const f32x4*)(xp + 4 * c);
+                }
+            }
+            {
+#pragma unroll
+                for (int r = 0; r < kR; r++)
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        const float d = k < K ? half_bits_to_float((uint16_t)dsc[r][m]) : 0.f;
+#pragma unroll
+                        for (int p = 0; p < kSP; p++)
+                            if (p < pc)
+                                acc[r][m][p] = fmaf(d, dot16(q[r][m], xv[p][0], xv[p][1], xv[p][2], xv[p][3]),
+                                                    acc[r][m][p]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kR; r++)
+#pragma unroll
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int p = 0; p < kSP; p++) {
+                    if (p < pc) {
+                        const float v = wave_sum_lane63(acc[r][m][p]);
+                        if (lane == 63) s_red[wv][r][m][p] = v;
                     }
                 }
+        __syncthreads();
+        if (tid < kR * pc) {
+            const int r = tid / pc, p = tid - r * pc;
+            const int nrow = n_lo + r;
+            float g = 0.f, u = 0.f;
+            for (int w = 0; w < kThreads / 64; w++) {
+                g += s_red[w][r][0][p];
+                if (MODE == 1) u += s_red[w][r][M - 1][p];
+            }
+            const float res = MODE == 1 ? g / (1.0f + __expf(-g)) * u : g;
+            if (nrow < N) {
+                if (routed) a.out[(int64_t)s_slots[p0 + p] * N + nrow] = res;
+                else a.sout[((int64_t)e * a.T + p0 + p) * N + nrow] = res;
             }
         }
         __syncthreads();
     }
 }
 
+// ---------------------------------------------------------------- wave-level fast path
+// For n_tokens * n_used <= 64: every wave is an independent unit (no LDS, no
+// barriers). Wave g of the grid owns kWR rows of one expert: it loads the ids table
+// (one entry per lane), finds the distinct experts present with per-word ballots,
+// takes the d-th, and collects that expert's slots as a lane mask. Then it issues,
+// back to back, the loads of its rows (all of K when K <= 4096), their scales and the
+// activation rows of up to P slots, accumulates in fp32, sums lanes with DPP and
+// lane 63 writes the results.
+constexpr int kWR = 1;      // rows (row pairs in gate/up mode) per wave
+constexpr int kWIT = 3;     // 1024-wide K iterations loaded at once
+
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+    for (int i = 0; i < n; i++) m &= m - 1;
+    return __ffsll((unsigned long long)m) - 1;
+}
+
+template <int MODE, int P, bool XBF16>
+__global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
+    constexpr int M = MODE == 1 ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
+    const int nch_r = (a.rw.N + kWR - 1) / kWR;
+    const int nw_r = a.d_max * nch_r;
+    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kWR - 1) / kWR) : 0;
+    if (gw >= nw_r + nw_s) return;
+    const bool routed = gw < nw_r;
+    const DecWeights& W = routed ? a.rw : a.sw;
+    const int N = W.N, K = W.K;
+    int e, chunk, cnt;
+    uint64_t smask = 0;  // routed: lanes (entries t*k+s) of this expert
+    if (routed) {
+        const int d = gw / nch_r;
+        chunk = gw - d * nch_r;
+        const int n = a.T * a.k;
+        int v = lane < n ? a.ids[lane] : -1;
+        if (v >= a.E) v = -1;
+        // distinct experts present: a 64-expert bitmap word at a time (wave OR), the
+        // d-th set bit over the words in ascending order is this wave's expert
+        e = -1;
+        int seen = 0;
+        for (int w0 = 0; w0 < a.E && e < 0; w0 += 64) {
+            const int rel = v - w0;
+            const bool in = v >= 0 && rel >= 0 && rel < 64;
+            const uint32_t lo = wave_or_u32(in && rel < 32 ? 1u << rel : 0u);
+            const uint32_t hi = wave_or_u32(in && rel >= 32 ? 1u << (rel - 32) : 0u);
+            const uint64_t present = ((uint64_t)hi << 32) | lo;
+            const int c = __popcll(present);
+            if (d < seen + c) e = w0 + nth_set_bit(present, d - seen);
+            seen += c;
+        }
+        if (e < 0) return;  // fewer distinct experts than the grid allows for
+        smask = __ballot(v == e);
+        cnt = __popcll(smask);
+    } else {
+        const int nch_s = (a.sw.N + kWR - 1) / kWR;
+        const int b = gw - nw_r;
+        e = b / nch_s;
+        chunk = b - e * nch_s;
+        cnt = a.T;
+    }
+    const int n_lo = chunk * kWR;
+    const int n_it = (K + 1023) >> 10;
+    const int64_t KB = K >> 5;
+    const void* src = routed ? a.act : a.sact;
+    constexpr int atype = XBF16 ? 1 : 0;  // activation type (the launcher checks both kinds agree)
+    auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
+    auto src_row = [&](int p) -> int64_t {
+        if (routed) {
+            const int slot = slot_of(p);
+            const int t = slot / a.k, s = slot - t * a.k;
+            return (int64_t)t * a.act_B + s % a.act_B;
+        }
+        return (int64_t)e * a.sact_jstride + p;
+    };
+
+    for (int p0 = 0; p0 < cnt; p0 += P) {
+        const int pc = min(P, cnt - p0);
+        float acc[kWR][M][P];
+#pragma unroll
+        for (int r = 0; r < kWR; r++)
+#pragma unroll
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int p = 0; p < P; p++) acc[r][m][p] = 0.f;
+        int64_t xrow[P];
+#pragma unroll
+        for (int p = 0; p < P; p++) xrow[p] = src_row(p0 + min(p, pc - 1));
+        for (int it0 = 0; it0 < n_it; it0 += kWIT) {
+            i32x4 q[kWR][M][kWIT];
+            uint32_t dsc[kWR][M][kWIT];
+            i32x4 xr[P][kWIT][XBF16 ? 2 : 1];  // bf16: 2 x 16 bytes per lane
+            f32x4 xf[P][kWIT][XBF16 ? 1 : 4];  // fp32: 4 x 16 bytes per lane
+#pragma unroll
+            for (int u = 0; u < kWIT; u++) {
+                const int k = ((it0 + u) << 10) + (lane << 4);
+                const int kc = k < K ? k : 0;  // past K: a valid address, result unused
+#pragma unroll
+                for (int r = 0; r < kWR; r++) {
+                    const int64_t wr = (int64_t)e * N + min(n_lo + r, N - 1);
+#pragma unroll
+                    for (int m = 0; m < M; m++) {
+                        q[r][m][u] = *(const i32x4*)((m == 0 ? W.qs1 : W.qs2) + wr * K + kc);
+                        dsc[r][m][u] = (m == 0 ? W.d1 : W.d2)[wr * KB + (kc >> 5)];
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < P; p++) {
+                    if constexpr (XBF16) {
+                        const uint16_t* xp = (const uint16_t*)src + xrow[p] * K + kc;
+                        xr[p][u][0] = *(const i32x4*)(xp);
+                        xr[p][u][1] = *(const i32x4*)(xp + 8);
+                    } else {
+                        const float* xp = (const float*)src + xrow[p] * K + kc;
+#pragma unroll
+                        for (int c = 0; c < 4; c++) xf[p][u][c] = *(const f32x4*)(xp + 4 * c);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kWIT; u++) {
+                // lanes past K add 0 (a zero scale) instead of branching: a lane-divergent
+                // branch here would let the compiler sink the loads into it
+                const bool kin = ((it0 + u) << 10) + (lane << 4) < K;
+#pragma unroll
+                for (int p = 0; p < P; p++) {
+                    if (p >= pc) continue;
+                    f32x4 x0, x1, x2, x3;
+                    if constexpr (XBF16) {
+                        const i32x4& r0 = xr[p][u][0];
+                        const i32x4& r1 = xr[p][u][1];
+                        x0 = f32x4{__builtin_bit_cast(float, (uint32_t)r0[0] << 16), __builtin_bit_cast(float, (uint32_t)r0[0] & 0xffff0000u),
+                                   __builtin_bit_cast(float, (uint32_t)r0[1] << 16), __builtin_bit_cast(float, (uint32_t)r0[1] & 0xffff0000u)};
+                        x1 = f32x4{__builtin_bit_cast(float, (uint32_t)r0[2] << 16), __builtin_bit_cast(float, (uint32_t)r0[2] & 0xffff0000u),
+                                   __builtin_bit_cast(float, (uint32_t)r0[3] << 16), __builtin_bit_cast(float, (uint32_t)r0[3] & 0xffff0000u)};
+                        x2 = f32x4{__builtin_bit_cast(float, (uint32_t)r1[0] << 16), __builtin_bit_cast(float, (uint32_t)r1[0] & 0xffff0000u),
+                                   __builtin_bit_cast(float, (uint32_t)r1[1] << 16), __builtin_bit_cast(float, (uint32_t)r1[1] & 0xffff0000u)};
+                        x3 = f32x4{__builtin_bit_cast(float, (uint32_t)r1[2] << 16), __builtin_bit_cast(float, (uint32_t)r1[2] & 0xffff0000u),
+                                   __builtin_bit_cast(float, (uint32_t)r1[3] << 16), __builtin_bit_cast(float, (uint32_t)r1[3] & 0xffff0000u)};
+                    } else {
+                        x0 = xf[p][u][0];
+                        x1 = xf[p][u][XBF16 ? 0 : 1];
+                        x2 = xf[p][u][XBF16 ? 0 : 2];
+                        x3 = xf[p][u][XBF16 ? 0 : 3];
+                    }
+#pragma unroll
+                    for (int r = 0; r < kWR; r++)
+#pragma unroll
+                        for (int m = 0; m < M; m++) {
+                            const float dd = kin ? half_bits_to_float((uint16_t)dsc[r][m][u]) : 0.f;
+                            acc[r][m][p] = fmaf(dd, dot16(q[r][m][u], x0, x1, x2, x3), acc[r][m][p]);
+                        }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kWR; r++) {
+            const int nrow = n_lo + r;
+#pragma unroll
+            for (int p = 0; p < P; p++) {
+                if (p >= pc) continue;
+                const float g = wave_sum_lane63(acc[r][0][p]);
+                float res = g;
+                if (MODE == 1) {
+                    const float u = wave_sum_lane63(acc[r][M - 1][p]);
+                    res = g / (1.0f + __expf(-g)) * u;
+                }
+                if (lane == 63 && nrow < N) {
+                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + nrow] = res;
+                    else a.sout[((int64_t)e * a.T + p0 + p) * N + nrow] = res;
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, bool XBF16>
+hipError_t launch_wave(const DecArgs& a, int slots_max, hipStream_t st) {
+    const int nw = a.d_max * ((a.rw.N + kWR - 1) / kWR) +
+                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kWR - 1) / kWR) : 0);
+    if (nw <= 0) return hipSuccess;
+    const int grid = (nw + 3) / 4;
+    if (slots_max <= 1) k_decode_wave<MODE, 1, XBF16><<<grid, 256, 0, st>>>(a);
+    else k_decode_wave<MODE, 2, XBF16><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t st) {
-    const int RB = a.rows_per_block;
-    const int nb_r = a.d_max * ((a.rw.N + RB - 1) / RB);
-    const int nb_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + RB - 1) / RB) : 0;
+    if ((int64_t)a.T * a.k <= 64) {
+        // activation rows per pass: an expert usually serves each token at most once,
+        // so up to n_tokens rows; more (repeated ids) take further passes. Two rows per
+        // pass keep the register budget at two or more waves per SIMD.
+        const int slots = a.T;
+        const bool same_type = a.sw.n_mat == 0 || a.sact_type == a.act_type;
+        if (same_type) {
+            if (a.mode == 1) return a.act_type == 1 ? launch_wave<1, true>(a, slots, st)
+                                                    : launch_wave<1, false>(a, slots, st);
+            return a.act_type == 1 ? launch_wave<0, true>(a, slots, st) : launch_wave<0, false>(a, slots, st);
+        }
+    }
+    const int nb_r = a.d_max * ((a.rw.N + kR - 1) / kR);
+    const int nb_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kR - 1) / kR) : 0;
     const int grid = nb_r + nb_s;
     if (grid <= 0) return hipSuccess;
-    // rows staged per pass: enough for every slot of an expert when it fits
-    int P = a.act_B == 1 ? a.T : a.T * a.k;
-    if (nb_s && a.T > P) P = a.T;
-    if (P > kMaxP) P = kMaxP;
-    const int64_t wmax = (nb_s && a.sw.K > a.rw.K) ? a.sw.K : a.rw.K;
-    const int64_t row_bytes = (int64_t)padded_width((int)wmax) * 4;
-    while (P > 1 && P * row_bytes > kActLds) P--;
-    const size_t lds = (size_t)(P * row_bytes);
-    if (a.mode == 1) k_decode<1><<<grid, kThreads, lds, st>>>(a, P);
-    else k_decode<0><<<grid, kThreads, lds, st>>>(a, P);
+    if (a.mode == 1) k_decode<1><<<grid, kThreads, 0, st>>>(a);
+    else k_decode<0><<<grid, kThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 

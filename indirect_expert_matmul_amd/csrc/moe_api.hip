@@ -472,7 +472,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         a.sout = (float*)p.hsh;
         a.mode = 1;
         a.d_max = (int32_t)(n < d.E ? n : d.E);
-        a.rows_per_block = 16;
+        a.rows_per_block = 32;
         tm.begin();
         if ((s = hip_check(launch_decode(a, st), "gate/up GEMV"))) return s;
         tm.end();
@@ -497,7 +497,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         b.sout = (float*)p.ysh;
         b.mode = 0;
         b.d_max = a.d_max;
-        b.rows_per_block = 16;
+        b.rows_per_block = 32;
         tm.begin();
         if ((s = hip_check(launch_decode(b, st), "down GEMV"))) return s;
         tm.end();
@@ -620,7 +620,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         a.out = slot_out;
         a.mode = 0;
         a.d_max = (int32_t)(n < E ? n : E);
-        a.rows_per_block = 16;
+        a.rows_per_block = 32;
         tm.begin();
         if ((s = hip_check(launch_decode(a, st), "GEMV"))) return s;
         tm.end();

@@ -10,7 +10,7 @@ namespace moe {
 // ---------------------------------------------------------------- limits
 constexpr int kMaxExperts = 1024;          // row-id pass keeps per-wave counters in LDS
 constexpr int kMaxBuckets = kMaxExperts + 1;  // + one bucket for out-of-range ids
-constexpr int64_t kRowIdsOneBlockMax = 32768;  // entries handled by the single-workgroup pass
+constexpr int64_t kRowIdsOneBlockMax = 4096;   // entries handled by the single-workgroup pass
 constexpr int kDecMaxSlots = 256;          // GEMV path: n_tokens * n_used
 constexpr int64_t kDecMaxWidth = 16384;    // GEMV path: widest staged activation row
 constexpr int kAlign = 256;                // workspace sub-buffer alignment

@@ -15,19 +15,68 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kU = 8;  // slots whose rows are loaded together
+
+// Block = one token x 1024 columns; each thread owns 4 consecutive columns. The
+// token's ids and weights are block-uniform; the k slot rows are loaded kU at a
+// time before they are summed in slot order.
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (idx >= (int64_t)a.T * a.N) return;
-    const int t = (int)(idx / a.N), c = (int)(idx - (int64_t)t * a.N);
-    float acc = 0.f;
-    for (int s = 0; s < a.k; s++) {
-        const int32_t e = a.ids[(int64_t)t * a.k + s];
-        if (e < 0 || e >= a.E) continue;
-        const float w = a.route_w ? a.route_w[(int64_t)t * a.k + s] : 1.0f;
-        acc = fmaf(w, a.y[((int64_t)t * a.k + s) * a.N + c], acc);
+    const int ncb = (a.N + 4 * kThreads - 1) / (4 * kThreads);
+    const int t = blockIdx.x / ncb;
+    const int c = ((blockIdx.x - t * ncb) * kThreads + threadIdx.x) * 4;
+    if (c >= a.N) return;
+    const int64_t tk = (int64_t)t * a.k;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.k; s0 += kU) {
+        f32x4 v[kU];
+        float w[kU];
+        bool okv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int s = s0 + u;
+            const int32_t e = s < a.k ? a.ids[tk + s] : -1;
+            const bool ok = e >= 0 && e < a.E;
+            okv[u] = ok;
+            w[u] = ok ? (a.route_w ? a.route_w[tk + s] : 1.0f) : 0.f;
+            const float* y = a.y + (tk + (ok ? s : 0)) * a.N + c;
+            if (VEC) {
+                v[u] = ok ? *(const f32x4*)y : f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+                for (int q = 0; q < 4; q++) v[u][q] = (ok && c + q < a.N) ? y[q] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            if (okv[u]) {
+                acc[0] = fmaf(w[u], v[u][0], acc[0]);
+                acc[1] = fmaf(w[u], v[u][1], acc[1]);
+                acc[2] = fmaf(w[u], v[u][2], acc[2]);
+                acc[3] = fmaf(w[u], v[u][3], acc[3]);
+            }
+        }
     }
-    for (int j = 0; j < a.S; j++) acc += a.ysh[((int64_t)j * a.T + t) * a.N + c];
-    a.out[idx] = acc;
+    for (int j = 0; j < a.S; j++) {
+        const float* y = a.ysh + ((int64_t)j * a.T + t) * a.N + c;
+        if (VEC) {
+            const f32x4 v = *(const f32x4*)y;
+            acc[0] += v[0];
+            acc[1] += v[1];
+            acc[2] += v[2];
+            acc[3] += v[3];
+        } else {
+            for (int q = 0; q < 4; q++)
+                if (c + q < a.N) acc[q] += y[q];
+        }
+    }
+    float* o = a.out + (int64_t)t * a.N + c;
+    if (VEC) {
+        *(f32x4*)o = acc;
+    } else {
+        for (int q = 0; q < 4; q++)
+            if (c + q < a.N) o[q] = acc[q];
+    }
 }
 
 // Per-slot output: rows of slots whose id is out of range are zero.
@@ -44,9 +93,12 @@ __global__ __launch_bounds__(kThreads) void k_zero_invalid(ReduceArgs a) {
 
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st) {
     if (a.mode == 0) {
-        const int64_t n = (int64_t)a.T * a.N;
-        if (n == 0) return hipSuccess;
-        k_reduce_weighted<<<(unsigned)((n + kThreads - 1) / kThreads), kThreads, 0, st>>>(a);
+        if ((int64_t)a.T * a.N == 0) return hipSuccess;
+        const int64_t ncb = (a.N + 4 * kThreads - 1) / (4 * kThreads);
+        const unsigned grid = (unsigned)(ncb * a.T);
+        const bool vec = (a.N % 4) == 0;  // 16-byte aligned rows (buffers are 256-byte aligned)
+        if (vec) k_reduce_weighted<true><<<grid, kThreads, 0, st>>>(a);
+        else k_reduce_weighted<false><<<grid, kThreads, 0, st>>>(a);
     } else {
         const int64_t n = (int64_t)a.T * a.k * a.N;
         if (n == 0) return hipSuccess;

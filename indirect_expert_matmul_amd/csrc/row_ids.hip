@@ -25,7 +25,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBatchesPerWave = 16;                    // multi-block chunk geometry
+constexpr int kBatchesPerWave = 2;                     // multi-block chunk geometry
 constexpr int64_t kChunk = (int64_t)kWaves * 64 * kBatchesPerWave;
 
 __device__ __forceinline__ int bucket_of(int32_t e, int32_t E) {
@@ -49,17 +49,35 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+constexpr int kPre = 8;  // batches of ids loaded ahead of their use
+
+// Loads of batches [bb, bb + kPre*64): one id per lane per batch, bucket E past the end.
+__device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, int64_t bb,
+                                             int64_t end, int32_t E, int (&b)[kPre]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPre; q++) {
+        const int64_t i = bb + q * 64 + lane;
+        b[q] = i < end ? bucket_of(ids[i], E) : -1;
+    }
+}
+
 // Histogram of entries [beg, end) into this wave's counter row (no atomics: each
 // bucket present in a batch has exactly one leader lane).
 __device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t end, int32_t E,
                            int nbits, int32_t* cnt_w) {
     const int lane = threadIdx.x & 63;
-    for (int64_t base = beg; base < end; base += 64) {
-        const int64_t i = base + lane;
-        const bool act = i < end;
-        const int b = act ? bucket_of(ids[i], E) : 0;
-        const uint64_t m = match_bucket(b, __ballot(act), nbits);
-        if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
+    for (int64_t base = beg; base < end; base += kPre * 64) {
+        int bk[kPre];
+        load_batches(ids, base, end, E, bk);
+#pragma unroll
+        for (int q = 0; q < kPre; q++) {
+            if (base + q * 64 >= end) break;  // uniform
+            const bool act = bk[q] >= 0;
+            const int b = act ? bk[q] : 0;
+            const uint64_t m = match_bucket(b, __ballot(act), nbits);
+            if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
+        }
     }
 }
 
@@ -67,26 +85,33 @@ __device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t
 __device__ void wave_place(const RowIdsArgs& a, int64_t beg, int64_t end, int nbits,
                            const int32_t* base, int32_t* run_w) {
     const int lane = threadIdx.x & 63;
-    for (int64_t bb = beg; bb < end; bb += 64) {
-        const int64_t i = bb + lane;
-        const bool act = i < end;
-        const int b = act ? bucket_of(a.ids[i], a.E) : 0;
-        const uint64_t m = match_bucket(b, __ballot(act), nbits);
-        int32_t prev = 0;
-        if (act) {
-            prev = run_w[b];
-            const int32_t pos = base[b] + prev + rank_below(m);
-            const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
-            const int32_t t = ii / a.k;
-            const int32_t s = ii - t * a.k;
-            a.ids_src1[pos] = t * a.B + s % a.B;
-            a.ids_dst[pos] = ii;
-            if (a.inv) a.inv[i] = pos;
+    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
+        int bk[kPre];
+        load_batches(a.ids, b0, end, a.E, bk);
+#pragma unroll
+        for (int q = 0; q < kPre; q++) {
+            const int64_t bb = b0 + q * 64;
+            if (bb >= end) break;  // uniform
+            const int64_t i = bb + lane;
+            const bool act = bk[q] >= 0;
+            const int b = act ? bk[q] : 0;
+            const uint64_t m = match_bucket(b, __ballot(act), nbits);
+            int32_t prev = 0;
+            if (act) {
+                prev = run_w[b];
+                const int32_t pos = base[b] + prev + rank_below(m);
+                const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
+                const int32_t t = ii / a.k;
+                const int32_t s = ii - t * a.k;
+                a.ids_src1[pos] = t * a.B + s % a.B;
+                a.ids_dst[pos] = ii;
+                if (a.inv) a.inv[i] = pos;
+            }
+            // every lane has read its counter before the group's leader bumps it
+            __builtin_amdgcn_wave_barrier();
+            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
         }
-        // every lane has read its counter before the group's leader bumps it
-        __builtin_amdgcn_wave_barrier();
-        if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
