@@ -94,10 +94,11 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
         : "memory");
 }
 // Wait until at most N of this wave's vector-memory operations are outstanding,
-// then meet the other waves at the barrier (LDS DMA data of every wave landed).
+// and until this wave's LDS reads returned, then meet the other waves at the barrier
+// (LDS DMA data of every wave landed; no wave still reads a buffer about to be refilled).
 template <int N>
 __device__ __forceinline__ void wait_stage_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -106,10 +107,15 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// LDS swizzles (16-byte chunk index XOR a function of the row), chosen so the 8 / 16
+// rows one ds_read_b128 phase touches fall on distinct banks (measured on gfx950).
+__device__ __forceinline__ int swz_a(int r) { return (r & 7) ^ ((r >> 3) & 1); }   // 8 chunks/row
+__device__ __forceinline__ int swz_b(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }  // 4 chunks/row
+
 // Block tile: BM = 32*MSUB activation rows (one expert segment) x 256 weight rows
 // (4 waves x 2 column groups x 32). One pipeline stage = one 64-wide K step:
-//   A  BM rows x 128 B (bf16), 16-byte chunk c of row r stored at chunk c ^ (r & 7)
-//   B  256 weight rows x 64 B (int8), chunk c of local row r stored at c ^ (r & 3)
+//   A  BM rows x 128 B (bf16), 16-byte chunk c of row r stored at chunk c ^ swz_a(r)
+//   B  256 weight rows x 64 B (int8), chunk c of local row r stored at c ^ swz_b(r)
 //   S  256 rows x 2 half-steps: the 4-byte aligned word holding that fp16 scale
 // NS stages live in LDS at once; stage s+NS-1 is being fetched while s computes.
 // Block -> tile: XCD x (= block index mod 8, how the dispatcher deals blocks) owns
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < MSUB; i++) {
         const int R = (wv * MSUB + i) * 8 + (lane >> 3);  // tile row this lane fetches
-        const int lc = (lane & 7) ^ (R & 7);               // logical 16-byte chunk
+        const int lc = (lane & 7) ^ swz_a(R);              // logical 16-byte chunk
         const int j = m0 + min(R, m_len - 1);
         const int64_t src = P.a_rows ? (int64_t)P.a_rows[j]
                                      : (int64_t)(P.a_row_mod ? j % P.a_row_mod : j);
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs args) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int lr = 16 * i + (lane >> 2);
-        const int lc = (lane & 3) ^ (lr & 3);
+        const int lc = (lane & 3) ^ swz_b(lr);
         b_off[i] = (uint32_t)((int64_t)wrow(wv, lr) * K + lc * 16);
         b_lc[i] = lc;
     }
@@ -266,25 +272,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs args) {
 #pragma unroll
     for (int c = 0; c < 2; c++) {
         const int lr = c * 32 + l32;
-        bq_off[c][0] = A_BYTES + wv * 4096 + lr * 64 + (((2 * h) ^ (lr & 3)) << 4);
-        bq_off[c][1] = A_BYTES + wv * 4096 + lr * 64 + (((2 * h + 1) ^ (lr & 3)) << 4);
+        bq_off[c][0] = A_BYTES + wv * 4096 + lr * 64 + (((2 * h) ^ swz_b(lr)) << 4);
+        bq_off[c][1] = A_BYTES + wv * 4096 + lr * 64 + (((2 * h + 1) ^ swz_b(lr)) << 4);
         sc_off[c] = A_BYTES + B_BYTES + wv * 512 + (lr * 2 + h) * 4;
         const uint32_t sbyte = (uint32_t)(((int64_t)wrow(wv, lr) * KB + h) * 2);
         sc_shift[c] = (sbyte & 2) ? 16 : 0;  // which half of the aligned word holds it
     }
 
-    for (int s = 0; s < NS - 1 && s < nsteps; s++) issue(s);
-
-    for (int s = 0; s < nsteps; s++) {
-        const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
-        if (ahead >= 2) wait_stage_and_barrier<2 * L>();
-        else if (ahead == 1) wait_stage_and_barrier<L>();
-        else wait_stage_and_barrier<0>();
-        if (s + NS - 1 < nsteps) issue(s + NS - 1);
-
+    // dequantize B of stage s (already in LDS) into MFMA operand registers
+    auto dequant = [&](int s, bf16x8 (&bf)[2][4]) {
         const uint8_t* st = smem + (s % NS) * STAGE;
         const bool in_k = s * 64 + 32 * h < K;   // false only for the upper half past K
-        bf16x8 bf[2][4];
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const i32x4 q0 = *(const i32x4*)(st + bq_off[c][0]);
@@ -297,17 +295,32 @@ __global__ __launch_bounds__(kThreads) void k_gemm_q8(GemmArgs args) {
             bf[c][2] = dequant8(q1[0], q1[1], d);
             bf[c][3] = dequant8(q1[2], q1[3], d);
         }
+    };
+    auto mfma_step = [&](int s, const bf16x8 (&bf)[2][4]) {
+        const uint8_t* st = smem + (s % NS) * STAGE;
 #pragma unroll
         for (int i = 0; i < MSUB; i++) {
             const int r = i * 32 + l32;
 #pragma unroll
             for (int ss = 0; ss < 4; ss++) {
-                const int chunk = (4 * h + ss) ^ (r & 7);
+                const int chunk = (4 * h + ss) ^ swz_a(r);
                 const bf16x8 af = *(const bf16x8*)(st + r * 128 + (chunk << 4));
                 acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[0][ss], acc[i][0], 0, 0, 0);
                 acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[1][ss], acc[i][1], 0, 0, 0);
             }
         }
+    };
+    for (int s = 0; s < NS - 1 && s < nsteps; s++) issue(s);
+    for (int s = 0; s < nsteps; s++) {
+        const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
+        if (ahead >= 2) wait_stage_and_barrier<2 * L>();
+        else if (ahead == 1) wait_stage_and_barrier<L>();
+        else wait_stage_and_barrier<0>();
+        // the buffer refilled here held step s-1, which every wave finished
+        if (s + NS - 1 < nsteps) issue(s + NS - 1);
+        bf16x8 bf[2][4];
+        dequant(s, bf);
+        mfma_step(s, bf);
     }
 
     // ---- epilogue. Accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4 of
