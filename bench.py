@@ -51,27 +51,37 @@ def parse():
     return p.parse_args()
 
 
-def workload_stats(inp, cfg):
-    """Algorithmic work of one step (flops, bytes) and per-kernel bytes."""
+def workload_stats(inp, cfg, h_bytes=2):
+    """Algorithmic work of one step (flops, bytes) and per-kernel bytes: the weights of
+    the experts the batch touches (each once), activations read once, results written
+    once."""
     T, k = inp["ids"].shape
     E, n_embd, n_ff, S = cfg.n_experts, cfg.n_embd, cfg.n_ff, cfg.n_shared
     ids = inp["ids"].ravel()
     touched = len(np.unique(ids[(ids >= 0) & (ids < E)]))
     rows_routed = int(((ids >= 0) & (ids < E)).sum())
-    flops = 2.0 * (rows_routed + T * S) * 3 * n_embd * n_ff
+    rows = rows_routed + T * S                      # routed slots + shared-expert rows
+    flops = 2.0 * rows * 3 * n_embd * n_ff
     w_gu = (touched + S) * 2 * n_ff * n_embd * Q8_BYTES
     w_dn = (touched + S) * n_embd * n_ff * Q8_BYTES
-    x_b = T * n_embd * 2
-    out_b = T * n_embd * 4
+    x_b = T * n_embd * 2                            # bf16 input
+    out_b = T * n_embd * 4                          # fp32 layer output
     return {
         "flops": flops, "bytes": w_gu + w_dn + x_b + out_b, "touched": touched,
-        "gate_up": {"bytes": w_gu + x_b, "flops": 2.0 * (rows_routed + T * S) * 2 * n_embd * n_ff},
-        "down": {"bytes": w_dn, "flops": 2.0 * (rows_routed + T * S) * n_embd * n_ff},
+        # gate/up: weights + x in, h = silu(g)*u out (bf16 on the GEMM path, fp32 on
+        # the GEMV path)
+        "gate_up": {"bytes": w_gu + x_b + rows * n_ff * h_bytes,
+                    "flops": 2.0 * rows * 2 * n_embd * n_ff},
+        # down: weights + h in, per-row fp32 results out
+        "down": {"bytes": w_dn + rows * n_ff * h_bytes + rows * n_embd * 4,
+                 "flops": 2.0 * rows * n_embd * n_ff},
     }
 
 
 def cpu_baseline(inp, budget_s):
-    """The oracle, as it stands, on a bounded token sample: tokens/s on this host."""
+    """The oracle, as it stands, on a bounded token sample: tokens/s on this host.
+    The sample grows until one pass takes about a quarter of the budget; when the
+    whole batch is faster than that, whole-batch passes repeat until the budget."""
     import oracle
     oracle.lib()
     T = inp["ids"].shape[0]
@@ -84,17 +94,44 @@ def cpu_baseline(inp, budget_s):
         if dt >= budget_s / 4 or n >= T:
             break
         n = min(T, max(n * 2, int(n * budget_s / 4 / max(dt, 1e-3))))
+    reps, total = 1, dt
+    while total < budget_s and n >= T:
+        t0 = time.perf_counter()
+        oracle.ffn(inp, token_rows=np.arange(n))
+        total += time.perf_counter() - t0
+        reps += 1
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of %d tokens, full layer (all experts and shared), fp64, %.1f s"
-                      % (n, T, dt)}
+    return {"value": n * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d tokens x %d pass(es), full layer (all experts and shared), "
+                      "fp64, %.1f s" % (n, T, reps, total)}
+
+
+def measured_traffic(config, stage):
+    """HBM bytes per launch of the dominant kernel, from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs summarised in profiles/hbm_traffic.md; None when no run covers this
+    workload and kernel, or the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    try:
+        m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+        ent = json.loads(m.group(1)).get(config)
+    except (OSError, AttributeError, ValueError):
+        return None
+    if not ent or ent.get("stage") != stage:
+        return None
+    src = open(os.path.join(ROOT, ent["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest()[:16] != ent["source_sha256_16"]:
+        return None
+    return float(ent["bytes"])
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(see the sharding notes in DESIGN.md)" % args.gpus, file=sys.stderr)
+        print("bench.py: this implementation runs on one GPU; --gpus %d is not supported "
+              "(the path would shard by expert with two all-to-all exchanges)" % args.gpus,
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import indirect_expert_matmul_amd as moe
@@ -106,12 +143,13 @@ def main():
         sys.exit(2)
     inp = synth.make_inputs(cfg)
     T, k = inp["ids"].shape
-    st = workload_stats(inp, cfg)
     dev = torch.device("cuda:0")
 
     def up(qs, d):
         return moe.weights_from_numpy(qs, d)
 
+    path = moe.moe_select_path(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), path=args.path)
+    st = workload_stats(inp, cfg, 2 if path == 1 else 4)
     R = args.rotate or (1 if st["bytes"] > 2e9 else max(4, int(np.ceil(1.2e9 / st["bytes"]))))
     sets = []
     base = [up(inp[n + "_qs"], inp[n + "_d"]) for n in ("gate", "up", "down")]
@@ -127,7 +165,6 @@ def main():
     ids = torch.from_numpy(inp["ids"]).to(dev)
     rw = torch.from_numpy(inp["route_w"]).to(dev)
     out = torch.empty((T, cfg.n_embd), dtype=torch.float32, device=dev)
-    path = moe.moe_select_path(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), path=args.path)
     need = moe.moe_ffn_fused_workspace_size(base[0], sh[0] if sh else None, T, k, path=args.path)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -170,17 +207,18 @@ def main():
     kern = {"gemm_gate_up": "gate_up", "gemv_gate_up": "gate_up", "gemm_down": "down",
             "gemv_down": "down"}.get(dom)
     mfma_bound = path == 1 and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
+    traffic = measured_traffic(args.config, dom)
     if kern is None:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dom}
     elif mfma_bound:
         a = st[kern]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": a / BF16_PEAK_TFLOPS, "traffic": None, "kernel": dom}
+                "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
     else:
         a = st[kern]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+                "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom}
 
     res = {
         "metric": "MoE mul_mat_id tokens/s + TFLOP/s (PP512/PP4096) and decode GB/s, 1 MI355X",

@@ -66,7 +66,6 @@ struct GemmArgs {
 // Block tile height for a given average rows-per-expert (host heuristic).
 int gemm_pick_msub(double avg_rows);
 int gemm_tile_m(int msub);
-int64_t gemm_n_tiles(int mode, int32_t N);
 hipError_t launch_gemm_q8(const GemmArgs& a, int msub, hipStream_t st);
 
 // ---------------------------------------------------------------- fp32 grouped matmul (Tiny)
