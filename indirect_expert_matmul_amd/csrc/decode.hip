@@ -275,29 +275,30 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
 }
 
 // ---------------------------------------------------------------- wave-level fast path
-// For n_tokens * n_used <= 64: every wave is an independent unit (no LDS, no
-// barriers). Wave g of the grid owns kWR rows of one expert: it loads the ids table
-// (one entry per lane), finds the distinct experts present with per-word ballots,
-// takes the d-th, and collects that expert's slots as a lane mask. Then it issues,
-// back to back, the loads of its rows (all of K when K <= 4096), their scales and the
-// activation rows of up to P slots, accumulates in fp32, sums lanes with DPP and
-// lane 63 writes the results.
-constexpr int kWR = 1;      // rows (row pairs in gate/up mode) per wave
-constexpr int kWIT = 3;     // 1024-wide K iterations loaded at once
-
+// For n_tokens * n_used <= 64 and K <= 4096: every wave is an independent unit (no
+// LDS, no barriers). Wave g of the grid owns R consecutive rows (row pairs in gate/up
+// mode) of one expert. It loads the ids table (one entry per lane), finds the distinct
+// experts present with a wave OR of per-word bitmaps, takes the d-th, and collects
+// that expert's slots as a lane mask. It then loads the activation rows of up to P of
+// those slots into registers once (lane l holds k = 1024i + 16l .. +15 of each), and
+// streams its R weight rows against them: per row all NIT 16-byte pieces and scales
+// are loaded back to back, converted exactly to fp32 and accumulated per slot in fp32;
+// lanes are summed with DPP and lane 63 writes. The activations are read once per R
+// rows instead of once per row.
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
     for (int i = 0; i < n; i++) m &= m - 1;
     return __ffsll((unsigned long long)m) - 1;
 }
 
-template <int MODE, int P, bool XBF16>
+template <int MODE, int P, bool XBF16, int NIT>
 __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
     constexpr int M = MODE == 1 ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
-    const int nch_r = (a.rw.N + kWR - 1) / kWR;
+    const int R = a.rows_per_block;  // rows per wave
+    const int nch_r = (a.rw.N + R - 1) / R;
     const int nw_r = a.d_max * nch_r;
-    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kWR - 1) / kWR) : 0;
+    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0;
     if (gw >= nw_r + nw_s) return;
     const bool routed = gw < nw_r;
     const DecWeights& W = routed ? a.rw : a.sw;
@@ -328,17 +329,16 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
         smask = __ballot(v == e);
         cnt = __popcll(smask);
     } else {
-        const int nch_s = (a.sw.N + kWR - 1) / kWR;
+        const int nch_s = (a.sw.N + R - 1) / R;
         const int b = gw - nw_r;
         e = b / nch_s;
         chunk = b - e * nch_s;
         cnt = a.T;
     }
-    const int n_lo = chunk * kWR;
-    const int n_it = (K + 1023) >> 10;
+    const int n_lo = chunk * R;
+    const int n_hi = min(n_lo + R, N);
     const int64_t KB = K >> 5;
     const void* src = routed ? a.act : a.sact;
-    constexpr int atype = XBF16 ? 1 : 0;  // activation type (the launcher checks both kinds agree)
     auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
     auto src_row = [&](int p) -> int64_t {
         if (routed) {
@@ -348,122 +348,156 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
         }
         return (int64_t)e * a.sact_jstride + p;
     };
+    // lane's K pieces: k = 1024*i + 16*lane; pieces past K read column 0 (a valid
+    // address) and get a zero scale
+    int kc[NIT];
+    bool kin[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; i++) {
+        const int k = (i << 10) + (lane << 4);
+        kin[i] = k < K;
+        kc[i] = kin[i] ? k : 0;
+    }
+    const int8_t* q1 = W.qs1 + (int64_t)e * N * K;
+    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * K : q1;
+    const uint16_t* d1 = W.d1 + (int64_t)e * N * KB;
+    const uint16_t* d2 = MODE == 1 ? W.d2 + (int64_t)e * N * KB : d1;
+
+    // one weight row (pair): NIT 16-byte pieces per matrix and their scales
+    struct Row {
+        i32x4 q[M][NIT];
+        uint32_t d[M][NIT];
+    };
+    auto load_row = [&](int n, Row& w) {
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const int8_t* qr = (m == 0 ? q1 : q2) + (int64_t)n * K;
+            const uint16_t* dr = (m == 0 ? d1 : d2) + (int64_t)n * KB;
+#pragma unroll
+            for (int i = 0; i < NIT; i++) {
+                w.q[m][i] = *(const i32x4*)(qr + kc[i]);
+                w.d[m][i] = dr[kc[i] >> 5];
+            }
+        }
+    };
 
     for (int p0 = 0; p0 < cnt; p0 += P) {
         const int pc = min(P, cnt - p0);
-        float acc[kWR][M][P];
+        // activations of this pass's slots, exact fp32
+        float x[P][NIT][16];
 #pragma unroll
-        for (int r = 0; r < kWR; r++)
+        for (int p = 0; p < P; p++) {
+            const int64_t row = src_row(p0 + min(p, pc - 1));
 #pragma unroll
-            for (int m = 0; m < M; m++)
+            for (int i = 0; i < NIT; i++) {
+                if constexpr (XBF16) {
+                    const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
+                    const i32x4 r0 = *(const i32x4*)(xp);
+                    const i32x4 r1 = *(const i32x4*)(xp + 8);
 #pragma unroll
-                for (int p = 0; p < P; p++) acc[r][m][p] = 0.f;
-        int64_t xrow[P];
-#pragma unroll
-        for (int p = 0; p < P; p++) xrow[p] = src_row(p0 + min(p, pc - 1));
-        for (int it0 = 0; it0 < n_it; it0 += kWIT) {
-            i32x4 q[kWR][M][kWIT];
-            uint32_t dsc[kWR][M][kWIT];
-            i32x4 xr[P][kWIT][XBF16 ? 2 : 1];  // bf16: 2 x 16 bytes per lane
-            f32x4 xf[P][kWIT][XBF16 ? 1 : 4];  // fp32: 4 x 16 bytes per lane
-#pragma unroll
-            for (int u = 0; u < kWIT; u++) {
-                const int k = ((it0 + u) << 10) + (lane << 4);
-                const int kc = k < K ? k : 0;  // past K: a valid address, result unused
-#pragma unroll
-                for (int r = 0; r < kWR; r++) {
-                    const int64_t wr = (int64_t)e * N + min(n_lo + r, N - 1);
-#pragma unroll
-                    for (int m = 0; m < M; m++) {
-                        q[r][m][u] = *(const i32x4*)((m == 0 ? W.qs1 : W.qs2) + wr * K + kc);
-                        dsc[r][m][u] = (m == 0 ? W.d1 : W.d2)[wr * KB + (kc >> 5)];
+                    for (int c = 0; c < 8; c++) {
+                        const uint32_t w = (uint32_t)(c < 4 ? r0[c] : r1[c - 4]);
+                        x[p][i][2 * c] = __builtin_bit_cast(float, w << 16);
+                        x[p][i][2 * c + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
                     }
-                }
+                } else {
+                    const float* xp = (const float*)src + row * K + kc[i];
 #pragma unroll
-                for (int p = 0; p < P; p++) {
-                    if constexpr (XBF16) {
-                        const uint16_t* xp = (const uint16_t*)src + xrow[p] * K + kc;
-                        xr[p][u][0] = *(const i32x4*)(xp);
-                        xr[p][u][1] = *(const i32x4*)(xp + 8);
-                    } else {
-                        const float* xp = (const float*)src + xrow[p] * K + kc;
+                    for (int c = 0; c < 4; c++) {
+                        const f32x4 v = *(const f32x4*)(xp + 4 * c);
 #pragma unroll
-                        for (int c = 0; c < 4; c++) xf[p][u][c] = *(const f32x4*)(xp + 4 * c);
+                        for (int j = 0; j < 4; j++) x[p][i][4 * c + j] = v[j];
                     }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kWIT; u++) {
-                // lanes past K add 0 (a zero scale) instead of branching: a lane-divergent
-                // branch here would let the compiler sink the loads into it
-                const bool kin = ((it0 + u) << 10) + (lane << 4) < K;
-#pragma unroll
-                for (int p = 0; p < P; p++) {
-                    if (p >= pc) continue;
-                    f32x4 x0, x1, x2, x3;
-                    if constexpr (XBF16) {
-                        const i32x4& r0 = xr[p][u][0];
-                        const i32x4& r1 = xr[p][u][1];
-                        x0 = f32x4{__builtin_bit_cast(float, (uint32_t)r0[0] << 16), __builtin_bit_cast(float, (uint32_t)r0[0] & 0xffff0000u),
-                                   __builtin_bit_cast(float, (uint32_t)r0[1] << 16), __builtin_bit_cast(float, (uint32_t)r0[1] & 0xffff0000u)};
-                        x1 = f32x4{__builtin_bit_cast(float, (uint32_t)r0[2] << 16), __builtin_bit_cast(float, (uint32_t)r0[2] & 0xffff0000u),
-                                   __builtin_bit_cast(float, (uint32_t)r0[3] << 16), __builtin_bit_cast(float, (uint32_t)r0[3] & 0xffff0000u)};
-                        x2 = f32x4{__builtin_bit_cast(float, (uint32_t)r1[0] << 16), __builtin_bit_cast(float, (uint32_t)r1[0] & 0xffff0000u),
-                                   __builtin_bit_cast(float, (uint32_t)r1[1] << 16), __builtin_bit_cast(float, (uint32_t)r1[1] & 0xffff0000u)};
-                        x3 = f32x4{__builtin_bit_cast(float, (uint32_t)r1[2] << 16), __builtin_bit_cast(float, (uint32_t)r1[2] & 0xffff0000u),
-                                   __builtin_bit_cast(float, (uint32_t)r1[3] << 16), __builtin_bit_cast(float, (uint32_t)r1[3] & 0xffff0000u)};
-                    } else {
-                        x0 = xf[p][u][0];
-                        x1 = xf[p][u][XBF16 ? 0 : 1];
-                        x2 = xf[p][u][XBF16 ? 0 : 2];
-                        x3 = xf[p][u][XBF16 ? 0 : 3];
-                    }
-#pragma unroll
-                    for (int r = 0; r < kWR; r++)
-#pragma unroll
-                        for (int m = 0; m < M; m++) {
-                            const float dd = kin ? half_bits_to_float((uint16_t)dsc[r][m][u]) : 0.f;
-                            acc[r][m][p] = fmaf(dd, dot16(q[r][m][u], x0, x1, x2, x3), acc[r][m][p]);
-                        }
                 }
             }
         }
+        auto compute_row = [&](int n, const Row& w) {
+            float acc[M][P];
 #pragma unroll
-        for (int r = 0; r < kWR; r++) {
-            const int nrow = n_lo + r;
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int p = 0; p < P; p++) acc[m][p] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NIT; i++)
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    // lanes past K add 0 through a zero scale instead of branching
+                    const float dd = kin[i] ? half_bits_to_float((uint16_t)w.d[m][i]) : 0.f;
+#pragma unroll
+                    for (int p = 0; p < P; p++) {
+                        const float* xv = x[p][i];
+                        acc[m][p] = fmaf(dd, dot16(w.q[m][i], f32x4{xv[0], xv[1], xv[2], xv[3]},
+                                                   f32x4{xv[4], xv[5], xv[6], xv[7]},
+                                                   f32x4{xv[8], xv[9], xv[10], xv[11]},
+                                                   f32x4{xv[12], xv[13], xv[14], xv[15]}),
+                                         acc[m][p]);
+                    }
+                }
 #pragma unroll
             for (int p = 0; p < P; p++) {
                 if (p >= pc) continue;
-                const float g = wave_sum_lane63(acc[r][0][p]);
+                const float g = wave_sum_lane63(acc[0][p]);
                 float res = g;
                 if (MODE == 1) {
-                    const float u = wave_sum_lane63(acc[r][M - 1][p]);
+                    const float u = wave_sum_lane63(acc[M - 1][p]);
                     res = g / (1.0f + __expf(-g)) * u;
                 }
-                if (lane == 63 && nrow < N) {
-                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + nrow] = res;
-                    else a.sout[((int64_t)e * a.T + p0 + p) * N + nrow] = res;
+                if (lane == 63) {
+                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + n] = res;
+                    else a.sout[((int64_t)e * a.T + p0 + p) * N + n] = res;
                 }
             }
+        };
+        // rows in pairs, the next row's loads in flight while one computes; loads past
+        // the last row re-read the last row (unconditional, so the waits stay exact)
+        Row wa, wb;
+        load_row(n_lo, wa);
+        for (int n = n_lo; n < n_hi; n += 2) {
+            load_row(min(n + 1, n_hi - 1), wb);
+            compute_row(n, wa);
+            if (n + 1 >= n_hi) break;
+            load_row(min(n + 2, n_hi - 1), wa);
+            compute_row(n + 1, wb);
         }
     }
 }
 
-template <int MODE, bool XBF16>
-hipError_t launch_wave(const DecArgs& a, int slots_max, hipStream_t st) {
-    const int nw = a.d_max * ((a.rw.N + kWR - 1) / kWR) +
-                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kWR - 1) / kWR) : 0);
+// Rows per wave: enough waves to keep every SIMD streaming (about 8 per SIMD over the
+// whole chip when the grid's upper bound on experts is reached), at least 4 rows per
+// wave so the per-wave start (ids, expert search, activation loads) is amortised.
+int decode_rows_per_wave(const DecArgs& a) {
+    const int64_t rows = (int64_t)a.d_max * a.rw.N + (a.sw.n_mat > 0 ? (int64_t)a.sw.n_mat * a.sw.N : 0);
+    const int64_t target = 256 * 4 * 8;
+    int64_t r = (rows + target - 1) / target;
+    return (int)(r < 4 ? 4 : (r > 32 ? 32 : r));
+}
+
+template <int MODE, bool XBF16, int NIT>
+hipError_t launch_wave_nit(DecArgs a, int slots_max, hipStream_t st) {
+    a.rows_per_block = decode_rows_per_wave(a);
+    const int R = a.rows_per_block;
+    const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
+                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
     if (nw <= 0) return hipSuccess;
     const int grid = (nw + 3) / 4;
-    if (slots_max <= 1) k_decode_wave<MODE, 1, XBF16><<<grid, 256, 0, st>>>(a);
-    else k_decode_wave<MODE, 2, XBF16><<<grid, 256, 0, st>>>(a);
+    if (slots_max <= 1) k_decode_wave<MODE, 1, XBF16, NIT><<<grid, 256, 0, st>>>(a);
+    else k_decode_wave<MODE, 2, XBF16, NIT><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
+}
+
+template <int MODE, bool XBF16>
+hipError_t launch_wave(const DecArgs& a, int slots_max, hipStream_t st) {
+    const int kmax = max(a.rw.K, a.sw.n_mat > 0 ? a.sw.K : 0);
+    if (kmax <= 1024) return launch_wave_nit<MODE, XBF16, 1>(a, slots_max, st);
+    if (kmax <= 2048) return launch_wave_nit<MODE, XBF16, 2>(a, slots_max, st);
+    if (kmax <= 3072) return launch_wave_nit<MODE, XBF16, 3>(a, slots_max, st);
+    return launch_wave_nit<MODE, XBF16, 4>(a, slots_max, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecArgs& a, hipStream_t st) {
-    if ((int64_t)a.T * a.k <= 64) {
+    if ((int64_t)a.T * a.k <= 64 && a.rw.K <= 4096 && (a.sw.n_mat == 0 || a.sw.K <= 4096)) {
         // activation rows per pass: an expert usually serves each token at most once,
         // so up to n_tokens rows; more (repeated ids) take further passes. Two rows per
         // pass keep the register budget at two or more waves per SIMD.
