@@ -243,9 +243,13 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     const uint8_t* s_base1 = (const uint8_t*)uniform_ptr(P.d1 + (int64_t)e * N * KB);
     const uint8_t* s_base2 = MODE == 1 ? (const uint8_t*)uniform_ptr(P.d2 + (int64_t)e * N * KB) : s_base1;
     int s_row[2];
-#pragma unroll
-    for (int t = 0; t < 2; t++) s_row[t] = wrow(16 * t + (lane >> 2));
+    uint32_t s_word[2];  // aligned word of the scale at stage 0; stage s adds 8*s bytes
     const int s_blk = lane & 3;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        s_row[t] = wrow(16 * t + (lane >> 2));
+        s_word[t] = (uint32_t)(((int64_t)s_row[t] * KB + s_blk) * 2) & ~3u;
+    }
 
     // Issue the copies of stage s into LDS slot s % NS. The last stage may end inside
     // K: activation chunks past K re-read chunk 0 of the stage, weight chunks past K
@@ -254,24 +258,37 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     auto issue = [&](int s) {
         const uint32_t st = lds0 + (uint32_t)((s % NS) * STAGE);
         const int k0 = s * 128;
-        const bool full = k0 + 128 <= K;
+        if (k0 + 128 <= K) {   // wave-uniform: every stage but a partial last one
 #pragma unroll
-        for (int i = 0; i < NA; i++) {
-            const uint32_t adj = (!full && k0 + a_lc[i] * 8 >= K) ? (uint32_t)(a_lc[i] * 16) : 0u;
-            dma16(a_base + (int64_t)k0 * 2, a_off[i] - adj, st + (wv * NA + i) * 1024);
-        }
+            for (int i = 0; i < NA; i++)
+                dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t adj = (!full && k0 + b_lc[i] * 16 >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
-            const int8_t* bb = (MODE == 1 && i >= 2) ? b_base2 : b_base1;
-            dma16(bb + k0, b_off[i] - adj, st + A_BYTES + wv * 4096 + i * 1024);
-        }
+            for (int i = 0; i < 4; i++)
+                dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i],
+                      st + A_BYTES + wv * 4096 + i * 1024);
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-            const int blk = min(4 * s + s_blk, KB - 1);
-            const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * 2);
-            const uint8_t* sb = (MODE == 1 && t == 1) ? s_base2 : s_base1;
-            dma4(sb, byte & ~3u, st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+            for (int t = 0; t < 2; t++)
+                dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 8 * s,
+                     st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NA; i++) {
+                const uint32_t adj = (k0 + a_lc[i] * 8 >= K) ? (uint32_t)(a_lc[i] * 16) : 0u;
+                dma16(a_base + (int64_t)k0 * 2, a_off[i] - adj, st + (wv * NA + i) * 1024);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t adj = (k0 + b_lc[i] * 16 >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
+                dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i] - adj,
+                      st + A_BYTES + wv * 4096 + i * 1024);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int blk = min(4 * s + s_blk, KB - 1);
+                const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * 2);
+                dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, byte & ~3u,
+                     st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+            }
         }
     };
 
@@ -306,7 +323,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         const int k0 = s * 128;
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            if (u == 1 && k0 + 64 >= K) break;   // the stage ends after its first half
+            // both halves always run (a half past K has zero scales): a conditional
+            // MFMA would make the compiler copy the accumulators out of AGPRs each step
             const i32x4 q0 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
             const i32x4 q1 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
             const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);

@@ -105,6 +105,31 @@ def test_ffn_invalid_ids_and_shared_width():
         assert normwise(got.cpu().numpy(), ref) <= _tol(path), path
 
 
+@pytest.mark.parametrize("S", [0, 1])
+@pytest.mark.parametrize("which", ["some", "all"])
+def test_ffn_gemv_invalid_ids(S, which):
+    """Decode-sized batches (the GEMV path, whose down launch also does the weighted
+    reduce): out-of-range ids contribute nothing; with every id out of range the
+    routed part is zero and only the shared experts remain."""
+    E, k, T, n_embd, n_ff = 8, 4, 6, 192, 128
+    ids = synth.draw_ids_uniform(9, T, E, k)
+    if which == "some":
+        ids[0, 1], ids[3, 0], ids[5, 3] = -1, E, 1 << 30
+    else:
+        ids[:] = -7
+    inp = synth.make_custom_ffn(21, E, k, T, n_embd, n_ff, S, ids=ids)
+    ref = oracle.ffn(inp)
+    dv = upload_ffn(inp)
+    for path in (moe.PATH_GEMV, moe.PATH_GEMM):
+        got = run_ffn(dv, path=path)
+        torch.cuda.synchronize()
+        g = got.cpu().numpy()
+        if which == "all" and S == 0:
+            assert np.all(g == 0.0), path
+        else:
+            assert normwise(g, ref) <= _tol(path), path
+
+
 def test_lite_full():
     inp = synth.make_inputs("lite")
     got = run_ffn(upload_ffn(inp))
