@@ -52,7 +52,9 @@ def lib():
                                            P, I64, I32, P, P]
         _lib.oracle_ffn.argtypes = ([ctypes.c_int] + [P] * 6 + [I64] * 3 + [P] * 6 + [I64] * 2 +
                                     [P, ctypes.c_int, P, P, I64, I32, P])
-        for f in (_lib.oracle_dequant, _lib.oracle_row_ids, _lib.oracle_mul_mat_id, _lib.oracle_ffn):
+        _lib.oracle_router_topk.argtypes = [P, I64, I32, I32, P, P]
+        for f in (_lib.oracle_dequant, _lib.oracle_row_ids, _lib.oracle_mul_mat_id, _lib.oracle_ffn,
+                  _lib.oracle_router_topk):
             f.restype = ctypes.c_int
     return _lib
 
@@ -161,3 +163,17 @@ def ffn(inp: dict, token_rows=None) -> np.ndarray:
     if rc:
         raise ValueError("oracle_ffn rejected its arguments (%d)" % rc)
     return out
+
+
+def router_topk(logits: np.ndarray, n_used: int):
+    """(ids int32 [T][k], weights float64 [T][k]) for router logits float32 [T][E]:
+    the k largest logits per token (equal logits: lower index first), in descending
+    order, weighted by a softmax over the picked logits."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, n_used), np.int32)
+    w = np.empty((T, n_used), np.float64)
+    rc = lib().oracle_router_topk(_p(lg), T, E, n_used, _p(ids), _p(w))
+    if rc:
+        raise ValueError("oracle_router_topk rejected its arguments (%d)" % rc)
+    return ids, w

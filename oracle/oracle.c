@@ -319,3 +319,43 @@ int oracle_ffn(int w_type, const void *g_data, const void *g_scales, const void 
     }
     return bad ? -2 : 0;
 }
+
+/* Router (the step ahead of the indirect matmul): for each token pick the n_used
+ * experts with the largest logits and weight them by a softmax over the picked
+ * logits alone. The pages' op takes ids as given ("CUDA: better MoE implementation",
+ * section 1.2: ids names the experts each token uses); the weights follow the
+ * softmax renormalised over the picks. Picks are made one at a time, each the
+ * largest remaining logit, equal logits going to the lower expert index, so the
+ * order inside a token is descending logit. NaN logits rank below every number.
+ * ids int32[T][k], w float64[T][k]. */
+int oracle_router_topk(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *ids,
+                       double *w) {
+    if (!logits || !ids || !w || T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        char *taken = (char *)calloc((size_t)E, 1);
+        double *v = (double *)malloc(sizeof(double) * (size_t)k);
+        for (int32_t r = 0; r < k; r++) {
+            int32_t best = -1;
+            double bv = 0.0;
+            for (int32_t e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                double x = isnan(l[e]) ? -INFINITY : (double)l[e];
+                if (best < 0 || x > bv) { /* ties keep the lower index (found first) */
+                    best = e;
+                    bv = x;
+                }
+            }
+            taken[best] = 1;
+            ids[t * k + r] = best;
+            v[r] = bv;
+        }
+        double m = v[0], sum = 0.0;
+        for (int32_t r = 0; r < k; r++) sum += exp(v[r] - m);
+        for (int32_t r = 0; r < k; r++) w[t * k + r] = exp(v[r] - m) / sum;
+        free(taken);
+        free(v);
+    }
+    return 0;
+}

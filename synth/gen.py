@@ -35,7 +35,7 @@ import os
 import numpy as np
 
 # Stream ids for SeedSequence spawn keys.
-_S_IDS, _S_LOGITS, _S_ROUTED, _S_SHARED, _S_X, _S_ZIPF = 0, 1, 2, 3, 4, 5
+_S_IDS, _S_LOGITS, _S_ROUTED, _S_SHARED, _S_X, _S_ZIPF, _S_ROUTER = 0, 1, 2, 3, 4, 5, 6
 _M_GATE, _M_UP, _M_DOWN = 0, 1, 2
 
 
@@ -132,6 +132,15 @@ def draw_route_w(seed: int, n_tokens: int, n_used: int) -> np.ndarray:
     z = z - z.max(axis=1, keepdims=True)
     e = np.exp(z)
     return np.ascontiguousarray((e / e.sum(axis=1, keepdims=True)).astype(np.float32))
+
+
+def draw_router_logits(seed: int, n_tokens: int, n_experts: int, zipf_s: float = 0.0) -> np.ndarray:
+    """Router logits float32 [T][E]: N(0,1), plus log of a Zipf(s) expert popularity
+    over a seeded permutation when zipf_s > 0 (so top-k picks follow that popularity)."""
+    z = _rng(seed, _S_ROUTER).standard_normal((n_tokens, n_experts))
+    if zipf_s > 0:
+        z = z + np.log(zipf_popularity(seed, n_experts, zipf_s))[None, :]
+    return np.ascontiguousarray(z.astype(np.float32))
 
 
 def draw_q8_0(rng: np.random.Generator, rows: int, cols: int):

@@ -8,7 +8,9 @@
     GEMM when E = k = 1, exact doubling when x doubles;
   * FFN: a dense MoE written with torch's matmul and silu, the shared-expert
     concatenation identity, one-hot routing, and a hand-derived worked example in
-    closed form.
+    closed form;
+  * router (top-k + softmax over the picks): a full stable sort, numpy softmax,
+    tie order, shift invariance, k = 1 and k = E, and a hand-computed example.
 The op being pinned: "CUDA: better MoE implementation" (ik_llama.cpp PR #283
 write-up), sections 1.2 (operands and semantics) and 2.1 (the three row maps).
 """
@@ -380,3 +382,70 @@ def test_zipf_routing_is_skewed():
     assert cnt.sum() == cfg.n_tokens * cfg.n_used
     assert cnt.max() > 10 * cnt.mean() / 1.5 and cnt.min() < cnt.mean() / 2
     assert all(len(set(r)) == len(r) for r in ids.tolist())
+
+
+# ---------------------------------------------------------------------- router
+# The step ahead of the op: ids and routing weights from router logits (top-k,
+# softmax renormalised over the picks).
+
+def _softmax64(z):
+    z = np.asarray(z, np.float64)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(9, 8, 2, 1), (40, 64, 6, 2), (7, 256, 8, 3), (3, 1024, 32, 4),
+                                        (5, 33, 33, 5)])
+def test_router_topk_vs_sort(T, E, k, seed):
+    """Selection against a full stable sort by (-logit, index); weights against a
+    softmax of the selected logits written with numpy."""
+    lg = synth.draw_router_logits(seed, T, E)
+    ids, w = oracle.router_topk(lg, k)
+    order = np.array([np.lexsort((np.arange(E), -lg[t].astype(np.float64))) for t in range(T)])
+    assert np.array_equal(ids, order[:, :k])
+    want = _softmax64(np.take_along_axis(lg, ids, axis=1))
+    np.testing.assert_allclose(w, want, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_router_ties_go_to_the_lower_index():
+    # logits from a 3-value set: many ties; picks among equals in index order
+    lg = np.random.default_rng(7).integers(0, 3, size=(50, 40)).astype(np.float32)
+    ids, w = oracle.router_topk(lg, 12)
+    for t in range(50):
+        row = lg[t]
+        want = sorted(range(40), key=lambda e: (-row[e], e))[:12]
+        assert ids[t].tolist() == want
+        vals = row[ids[t]]
+        # equal logits get equal weights
+        for a in range(12):
+            for b in range(12):
+                if vals[a] == vals[b]:
+                    assert w[t, a] == w[t, b]
+
+
+def test_router_shift_invariance_and_special_cases():
+    # logits on a 2^-10 grid, so adding 8 is exact in float32
+    lg = (np.round(synth.draw_router_logits(11, 20, 32) * 1024) / 1024).astype(np.float32)
+    ids, w = oracle.router_topk(lg, 4)
+    ids2, w2 = oracle.router_topk(lg + np.float32(8.0), 4)
+    assert np.array_equal(ids, ids2)
+    np.testing.assert_allclose(w, w2, rtol=1e-12)
+    ids1, w1 = oracle.router_topk(lg, 1)
+    assert np.array_equal(ids1[:, 0], np.argmax(lg, axis=1)) and np.all(w1 == 1.0)
+    idsE, wE = oracle.router_topk(lg, 32)                 # k = E: every expert, by logit
+    assert all(sorted(r) == list(range(32)) for r in idsE.tolist())
+    np.testing.assert_allclose(wE, np.take_along_axis(_softmax64(lg), idsE, axis=1), rtol=1e-13)
+
+
+def test_router_worked_example():
+    """Hand-computed: logits (1, ln 3, 0, ln 3) with k = 3 pick expert 1, then its
+    equal expert 3, then expert 0, weighted e^{ln3}, e^{ln3}, e^1 over their sum."""
+    l3 = np.float32(math.log(3.0))
+    lg = np.array([[1.0, l3, 0.0, l3]], np.float32)
+    ids, w = oracle.router_topk(lg, 3)
+    assert ids.tolist() == [[1, 3, 0]]
+    a = math.exp(float(l3))
+    s = 2 * a + math.e
+    np.testing.assert_allclose(w[0], [a / s, a / s, math.e / s], rtol=1e-15)
