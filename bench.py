@@ -220,6 +220,22 @@ def main():
         roof = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom}
 
+    # the router top-k that produces ids / route_w ahead of the layer (not part of the
+    # step): timed on logits of the same shape, reported separately
+    lg = torch.from_numpy(synth.draw_router_logits(cfg.seed, T, cfg.n_experts)).to(dev)
+    for _ in range(3):
+        moe.moe_router_topk(lg, k, stream=stream)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    n_router = 20
+    for _ in range(n_router):
+        moe.moe_router_topk(lg, k, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    router_us = r0.elapsed_time(r1) * 1e3 / n_router
+    router = {"us": router_us, "gbps": (T * cfg.n_experts * 4 + T * k * 8) / (router_us * 1e-6) / 1e9,
+              "n_experts": cfg.n_experts, "n_used": k}
+
     res = {
         "metric": "MoE mul_mat_id tokens/s + TFLOP/s (PP512/PP4096) and decode GB/s, 1 MI355X",
         "value": T / (ms * 1e-3),
@@ -235,6 +251,7 @@ def main():
         "tflops": st["flops"] / (ms * 1e-3) / 1e12,
         "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
         "stage_ms": stage_ms,
+        "router": router,
         "roofline": roof,
         "cpu_baseline": None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds),
     }

@@ -149,6 +149,23 @@ moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const m
                          float *out, const moe_options *opt, void *ws, size_t ws_bytes,
                          void *stream);
 
+/*
+ * moe_router_topk -- the step ahead of the op: the ids table the op consumes (section
+ * 1.2 of the PR #283 write-up: ids names the experts each token uses) and routing
+ * weights, from router logits.
+ *   logits   device float32 [n_tokens][n_experts]
+ *   ids      device int32 [n_tokens][n_used] (written): the n_used largest logits of
+ *            each token in descending order, equal logits taken lower index first;
+ *            NaN logits rank below every number
+ *   route_w  device float32 [n_tokens][n_used] (written): softmax over the picked
+ *            logits only (exp(v_r - v_0) / sum_r exp(v_r - v_0)), the weighting the
+ *            DeepSeek-V3-shaped configuration calls softmax renormalised over the picks
+ * Requires 1 <= n_used <= n_experts <= 1024 (MOE_EINVAL / MOE_ELIMIT otherwise) and
+ * n_tokens < 2^22. No workspace. Deterministic. n_tokens = 0 is a no-op.
+ */
+moe_status moe_router_topk(const float *logits, int64_t n_tokens, int32_t n_experts, int32_t n_used,
+                           int32_t *ids, float *route_w, void *stream);
+
 /* Workspace sizes in bytes for the calls above with the same arguments (0 if the
  * arguments are invalid; a valid call may also need 0 bytes, then ws may be NULL). */
 size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_experts);

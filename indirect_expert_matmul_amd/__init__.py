@@ -26,9 +26,9 @@ MOE_F32, MOE_BF16, MOE_Q8_0 = 0, 1, 2
 PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_row_ids_workspace_size",
-           "moe_mul_mat_id_workspace_size", "moe_ffn_fused_workspace_size", "moe_select_path",
-           "moe_status_string", "moe_last_error")
+EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
+           "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
+           "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -50,7 +50,7 @@ class c_moe_options(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libmoe.so is not built (%s); run `python -m indirect_expert_matmul_amd.build`"
+        raise ImportError("libmoe.so is not built (%s); run `python indirect_expert_matmul_amd/build.py`"
                           % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -59,7 +59,8 @@ def _load():
     lib.moe_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P, P, SZ, P]
     lib.moe_mul_mat_id.argtypes = [W, P, ctypes.c_int, I32, P, I64, I32, P, P, O, P, SZ, P]
     lib.moe_ffn_fused.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P, SZ, P]
-    for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused):
+    lib.moe_router_topk.argtypes = [P, I64, I32, I32, P, P, P]
+    for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused, lib.moe_router_topk):
         f.restype = ctypes.c_int
     lib.moe_row_ids_workspace_size.argtypes = [I64, I32, I32]
     lib.moe_mul_mat_id_workspace_size.argtypes = [W, ctypes.c_int, I32, I64, I32, O]
@@ -188,6 +189,28 @@ def moe_row_ids(ids: torch.Tensor, n_experts: int, src1_rows_per_token: int = 1,
                            dd.data_ptr(), b.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_row_ids")
     return s1, dd, b
+
+
+def moe_router_topk(logits: torch.Tensor, n_used: int, ids: Optional[torch.Tensor] = None,
+                    route_w: Optional[torch.Tensor] = None, stream=None):
+    """(ids int32 [T][k], route_w float32 [T][k]) from router logits float32 [T][E]:
+    the k largest logits per token (equal logits: lower index first), weighted by a
+    softmax over the picked logits."""
+    _dev_check(logits)
+    if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be contiguous float32 [n_tokens][n_experts]")
+    T, E = logits.shape
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((T, n_used), dtype=torch.int32, device=dev)
+    if route_w is None:
+        route_w = torch.empty((T, n_used), dtype=torch.float32, device=dev)
+    if ids.shape != (T, n_used) or ids.dtype != torch.int32 or route_w.shape != (T, n_used) \
+            or route_w.dtype != torch.float32:
+        raise ValueError("ids / route_w must be int32 / float32 [n_tokens][n_used]")
+    _check(lib.moe_router_topk(logits.data_ptr(), T, E, n_used, ids.data_ptr(), route_w.data_ptr(),
+                               _stream(stream)), "moe_router_topk")
+    return ids, route_w
 
 
 def moe_mul_mat_id_workspace_size(w: Weights, src1_type: int, src1_rows_per_token: int,

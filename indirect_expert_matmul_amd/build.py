@@ -1,6 +1,8 @@
 """Build libmoe.so (the gfx950 HIP kernels and the C ABI of include/moe.h) in-tree.
 
-    python -m indirect_expert_matmul_amd.build
+    python indirect_expert_matmul_amd/build.py
+
+(run as a file: importing the package loads the library this builds).
 
 Every HIP source is compiled for gfx950 with packed fp32 instructions disabled
 and linked into indirect_expert_matmul_amd/libmoe.so.

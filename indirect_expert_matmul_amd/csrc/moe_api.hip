@@ -641,4 +641,23 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     return MOE_OK;
 }
 
+moe_status moe_router_topk(const float* logits, int64_t n_tokens, int32_t n_experts, int32_t n_used,
+                           int32_t* ids, float* route_w, void* stream) {
+    moe_status s;
+    g_err.clear();
+    if ((s = check_tokens(n_tokens, n_used))) return s;
+    if ((s = check_experts(n_experts))) return s;
+    if (n_used > n_experts)
+        return fail(MOE_EINVAL, "n_used (%d) must not exceed n_experts (%d) for top-k", n_used, n_experts);
+    if (n_tokens > 0 && (!logits || !ids || !route_w)) return fail(MOE_EINVAL, "NULL pointer argument");
+    RouterArgs a{};
+    a.logits = logits;
+    a.T = n_tokens;
+    a.E = n_experts;
+    a.k = n_used;
+    a.ids = ids;
+    a.w = route_w;
+    return hip_check(launch_router(a, (hipStream_t)stream), "router top-k");
+}
+
 }  // extern "C"

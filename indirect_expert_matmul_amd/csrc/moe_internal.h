@@ -105,6 +105,17 @@ struct DecArgs {
 };
 hipError_t launch_decode(const DecArgs& a, hipStream_t st);
 
+// ---------------------------------------------------------------- router top-k
+struct RouterArgs {
+    const float* logits;  // [T][E]
+    int64_t T;
+    int32_t E;            // <= kMaxExperts
+    int32_t k;            // 1 <= k <= E
+    int32_t* ids;         // [T][k]
+    float* w;             // [T][k]
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- reduce / scatter (K5)
 struct ReduceArgs {
     const int32_t* ids;     // [T][k]

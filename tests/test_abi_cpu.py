@@ -118,3 +118,15 @@ def test_workspace_sizes_are_positive_and_monotone():
     assert moe.lib.moe_ffn_fused_workspace_size(ctypes.byref(g), None, moe.MOE_F32, 512, 6, None) == 0
     w = _w(n_mat=8, rows=32, cols=64, typ=moe.MOE_F32)
     assert moe.lib.moe_mul_mat_id_workspace_size(ctypes.byref(w), moe.MOE_F32, 1, 16, 2, None) > 0
+
+
+def test_router_validation():
+    f = moe.lib.moe_router_topk
+    assert f(FAKE, 16, 8, 9, FAKE, FAKE, None) == moe.MOE_EINVAL     # n_used > n_experts
+    assert f(FAKE, 16, 8, 0, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert f(FAKE, 16, 0, 1, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert f(FAKE, 16, 2048, 8, FAKE, FAKE, None) == moe.MOE_ELIMIT
+    assert f(FAKE, 1 << 22, 64, 8, FAKE, FAKE, None) == moe.MOE_ELIMIT
+    assert f(None, 16, 64, 8, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert f(FAKE, 16, 64, 8, FAKE, None, None) == moe.MOE_EINVAL
+    assert f(None, 0, 64, 8, None, None, None) == moe.MOE_OK                # empty batch: no-op
