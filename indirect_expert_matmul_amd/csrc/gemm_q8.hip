@@ -35,6 +35,8 @@
 //   * Block index -> tile is XCD-aware (see k_gemm_q8). Tiles are located on device
 //     from the row-id pass's M-tile prefix (no host readback); blocks past the real
 //     tile count exit at once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 #ifndef MOE_GEMM_CFG2
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int S_BYTES = W * 32 * 16;
     constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     constexpr int NA = BM / (4 * W);             // activation copies (1 KB) per wave per stage
-    constexpr int L = NA + 4 + 2;                // vector-memory instructions per wave per stage
+    static_assert(NS == 2, "the step sequence below runs a two-slot ring");
     static_assert(NA * 4 * W == BM, "activation rows must split evenly over the waves");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int32_t s_orow[BM];
@@ -255,8 +257,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     // K: activation chunks past K re-read chunk 0 of the stage, weight chunks past K
     // re-read the stage's first 16 bytes, scales past K re-read block KB-1 (all zeroed
     // at use), so every address stays inside its row.
-    auto issue = [&](int s) {
-        const uint32_t st = lds0 + (uint32_t)((s % NS) * STAGE);
+    auto issue = [&](int s, int slot) {
+        const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
         const int k0 = s * 128;
         if (k0 + 128 <= K) {   // wave-uniform: every stage but a partial last one
 #pragma unroll
@@ -310,16 +312,15 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     for (int u = 0; u < 2; u++)
         s_sh[u] = (((int64_t)wrow(l32) * KB + 2 * u + h) & 1) ? 16 : 0;
 
-    for (int s = 0; s < NS - 1 && s < nsteps; s++) issue(s);
-    for (int s = 0; s < nsteps; s++) {
-        const int ahead = min(NS - 2, nsteps - 1 - s);  // stages after s already issued
-        if (ahead >= 2) wait_stage_and_barrier<2 * L>();
-        else if (ahead == 1) wait_stage_and_barrier<L>();
-        else wait_stage_and_barrier<0>();
-        // the slot refilled here held step s-1, which every wave finished
-        if (s + NS - 1 < nsteps) issue(s + NS - 1);
-
-        const uint8_t* st = smem + (s % NS) * STAGE;
+    // One step: wait for stage s, send stage s+1 into the other slot, dequantize and
+    // multiply. SLOT is s % 2 as a constant, so the LDS offsets become immediates;
+    // CHECK_K zeroes the scales of blocks past K and is only needed on the last stage.
+    auto step = [&](int s, auto slot_c, auto check_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        constexpr bool CHECK_K = decltype(check_c)::value;
+        wait_stage_and_barrier<0>();   // stage s landed; nobody still reads the other slot
+        if (s + 1 < nsteps) issue(s + 1, SLOT ^ 1);
+        const uint8_t* st = smem + SLOT * STAGE;
         const int k0 = s * 128;
 #pragma unroll
         for (int u = 0; u < 2; u++) {
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             const i32x4 q1 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
             const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
             float d = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
-            d = (k0 + 64 * u + 32 * h < K) ? d : 0.f;
+            if constexpr (CHECK_K) d = (k0 + 64 * u + 32 * h < K) ? d : 0.f;
             bf16x8 bf[4];
             bf[0] = dequant8(q0[0], q0[1], d);
             bf[1] = dequant8(q0[2], q0[3], d);
@@ -346,6 +347,24 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 }
             }
         }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using NoCheck = std::integral_constant<bool, false>;
+    using Check = std::integral_constant<bool, true>;
+
+    issue(0, 0);
+    const int last = nsteps - 1;   // only this stage can end inside K
+    int s = 0;
+    for (; s + 1 < last; s += 2) {
+        step(s, S0{}, NoCheck{});
+        step(s + 1, S1{}, NoCheck{});
+    }
+    if (s < last) {
+        step(s, S0{}, NoCheck{});
+        step(s + 1, S1{}, Check{});
+    } else {
+        step(s, S0{}, Check{});
     }
 
     // ---- epilogue. Accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4 of
