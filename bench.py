@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--graph", type=int, default=0,
+                   help="1: time replays of one HIP graph per weight copy (each graph holds one "
+                        "step); 0: eager calls")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a known-size "
@@ -183,9 +186,28 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one captured step per weight copy, replayed in the same rotation
+        graphs = []
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    (gw, uw, dw), sw_ = sets[r]
+                    moe.moe_ffn_fused(gw, uw, dw, x, ids, rw, shared=sw_, path=args.path, out=out,
+                                      workspace=ws, stream=cap)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % R].replay()
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
@@ -247,6 +269,7 @@ def main():
         "config": {"workload": cfg.desc, "n_tokens": T, "n_experts": cfg.n_experts,
                    "n_used": k, "n_shared": cfg.n_shared, "n_embd": cfg.n_embd, "n_ff": cfg.n_ff,
                    "path": "gemm" if path == 1 else "gemv", "weight_copies": R,
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "parallelism": "single GPU"},
         "tflops": st["flops"] / (ms * 1e-3) / 1e12,
         "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
