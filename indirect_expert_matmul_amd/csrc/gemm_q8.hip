@@ -178,7 +178,12 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         if (q >= part || t >= total) return;
         const int mt = t / n_nt;
         nt = t - mt * n_nt;
-        if (P.bounds) {
+        if (P.tile_tab) {   // the row-id pass's per-tile table: one load
+            const int4 ti = *(const int4*)(P.tile_tab + 4 * (int64_t)mt);
+            e = ti.x;
+            m0 = ti.y;
+            m_len = ti.z;
+        } else if (P.bounds) {
             int lo = 0, hi = P.n_seg;  // tile_off[lo] <= mt < tile_off[hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;

@@ -122,16 +122,24 @@ int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n
 
 // ---------------------------------------------------------------- workspace plans
 struct RowIdsPlan {
-    int32_t *ids_src1, *ids_dst, *bounds, *tile_a, *chunk_cnt, *bucket_tot;
+    int32_t *ids_src1, *ids_dst, *bounds, *tile_a, *tile_tab, *chunk_cnt, *bucket_tot;
+    int32_t tile_cap;
 };
-RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, bool tiles) {
+// tile_m > 0: also room for the GEMM's M-tile prefix and per-tile table (tiles of
+// tile_m rows)
+RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, int tile_m) {
     RowIdsPlan p{};
+    const bool tiles = tile_m > 0;
     if (maps) {
         p.ids_src1 = (int32_t*)c.take(sizeof(int32_t) * n);
         p.ids_dst = (int32_t*)c.take(sizeof(int32_t) * n);
         p.bounds = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
     }
-    if (tiles) p.tile_a = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
+    if (tiles) {
+        p.tile_a = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
+        p.tile_cap = (int32_t)m_tiles_bound(n, E, tile_m);
+        p.tile_tab = (int32_t*)c.take(sizeof(int32_t) * 4 * (size_t)p.tile_cap);
+    }
     const size_t sb = row_ids_scratch_bytes(n, E);
     if (sb) {
         const int64_t nc = (int64_t)(sb - (size_t)(E + 1) * sizeof(int32_t)) / sizeof(int32_t);
@@ -159,7 +167,7 @@ FfnPlan carve_ffn(Carve& c, const FfnDims& d, int path) {
     const int64_t n = d.T * d.k;
     if (path == 1) {
         p.msub = gemm_pick_msub((double)n / d.E);
-        p.r = carve_row_ids(c, n, d.E, true, true);
+        p.r = carve_row_ids(c, n, d.E, true, gemm_tile_m(p.msub));
         p.h = c.take((size_t)n * d.n_ff * 2);
         p.hsh = c.take((size_t)d.S * d.T * d.n_ff_sh * 2);
     } else {
@@ -184,7 +192,7 @@ MmidPlan carve_mmid(Carve& c, int64_t T, int32_t k, int32_t E, int64_t N, bool w
     const int64_t n = T * k;
     if (!q8 || path == 1) {
         p.msub = gemm_pick_msub((double)n / E);
-        p.r = carve_row_ids(c, n, E, true, q8);
+        p.r = carve_row_ids(c, n, E, true, q8 ? gemm_tile_m(p.msub) : 0);
     }
     if (weighted) p.y = c.take((size_t)n * N * 4);
     return p;
@@ -289,7 +297,7 @@ int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int
 size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_experts) {
     if (check_tokens(n_tokens, n_used) || check_experts(n_experts)) return 0;
     Carve c(nullptr);
-    carve_row_ids(c, n_tokens * n_used, n_experts, false, false);
+    carve_row_ids(c, n_tokens * n_used, n_experts, false, 0);
     return c.off;
 }
 
@@ -307,7 +315,7 @@ moe_status moe_row_ids(const int32_t* ids, int64_t n_tokens, int32_t n_used, int
     const size_t need = moe_row_ids_workspace_size(n_tokens, n_used, n_experts);
     if (need > ws_bytes || (need && !ws)) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", need);
     Carve c(ws);
-    RowIdsPlan p = carve_row_ids(c, n_tokens * n_used, n_experts, false, false);
+    RowIdsPlan p = carve_row_ids(c, n_tokens * n_used, n_experts, false, 0);
     p.ids_src1 = ids_src1;
     p.ids_dst = ids_dst;
     p.bounds = expert_bounds;
@@ -372,6 +380,8 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         RowIdsArgs ra = row_ids_args(ids, n, d.k, d.E, 1, p.r);
         ra.tile_off[0] = p.r.tile_a;
         ra.tile_m[0] = bm;
+        ra.tile_tab[0] = p.r.tile_tab;
+        ra.tile_cap[0] = p.r.tile_cap;
         tm.begin();
         if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
         tm.end();
@@ -388,6 +398,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         r.K = d.n_embd;
         r.bounds = p.r.bounds;
         r.tile_off = p.r.tile_a;
+        r.tile_tab = p.r.tile_tab;
         r.n_seg = d.E;
         r.m_tiles_max = (int32_t)m_tiles_bound(n, d.E, bm);
         r.A = (const uint16_t*)x;
@@ -426,6 +437,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         r2.K = d.n_ff;
         r2.bounds = p.r.bounds;
         r2.tile_off = p.r.tile_a;
+        r2.tile_tab = p.r.tile_tab;
         r2.n_seg = d.E;
         r2.m_tiles_max = r.m_tiles_max;
         r2.A = (const uint16_t*)p.h;
@@ -564,6 +576,8 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         if (q8) {
             ra.tile_off[0] = p.r.tile_a;
             ra.tile_m[0] = bm;
+            ra.tile_tab[0] = p.r.tile_tab;
+            ra.tile_cap[0] = p.r.tile_cap;
         }
         tm.begin();
         if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
@@ -579,6 +593,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.K = K;
             r.bounds = p.r.bounds;
             r.tile_off = p.r.tile_a;
+            r.tile_tab = p.r.tile_tab;
             r.n_seg = E;
             r.m_tiles_max = (int32_t)m_tiles_bound(n, E, bm);
             r.A = (const uint16_t*)src1;
