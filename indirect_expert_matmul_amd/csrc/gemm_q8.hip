@@ -126,6 +126,11 @@ __device__ __forceinline__ int swz_b(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 template <int MODE, int W>
 constexpr int out_cols() { return MODE == 1 ? 16 * W : 32 * W; }
 
+#ifndef MOE_GEMM_MCHUNK
+#define MOE_GEMM_MCHUNK 4
+#endif
+constexpr int kMChunk = MOE_GEMM_MCHUNK;   // M tiles sharing each weight slab in turn
+
 // Per stage, in LDS (NS stages in a ring):
 //   A  BM rows x 256 B of bf16 activations (128 K columns)
 //   B  32*W weight rows x 128 B of int8
@@ -146,11 +151,12 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 
     // ---- tile of this block. The grid holds, per problem, 8 equal parts sized by an
     // upper bound on the tile count; part x runs on XCD x (the dispatcher deals block b
-    // to XCD b mod 8). The problem's real tiles, ordered (M tile, N tile) with the N
-    // tiles of an M tile adjacent, are cut into 8 contiguous ranges of equal length,
-    // one per XCD: all tiles of an expert run on one XCD at about the same time, so its
-    // weight lines are fetched from HBM once and shared in that XCD's L2, and the N
-    // tiles of an M tile share the activation rows there too.
+    // to XCD b mod 8). The problem's real tiles are ordered by expert, then by chunk of
+    // up to kMChunk M tiles, then N tile, then M tile inside the chunk, and cut into 8
+    // contiguous ranges, one per XCD: the M tiles of a chunk, which share each slab of
+    // weights, are dispatched back to back on one XCD, so the slab comes from HBM once
+    // per chunk, while the chunk's activation tiles stay in that XCD's L2 across the
+    // N tiles.
     int b = (int)blockIdx.x, pi = 0;
     {
         const GemmProblem& P0 = args.p[0];
@@ -165,39 +171,52 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     const int n_nt = (N + NTW - 1) / NTW;
     int e, m0, m_len, nt;
     {
-        int m_tiles;
-        if (P.bounds) {
-            m_tiles = P.tile_off[P.n_seg];
-        } else {
-            m_tiles = P.n_seg * ((P.seg_len + BM - 1) / BM);
-        }
+        const int m_tiles = P.bounds ? P.tile_off[P.n_seg] : P.n_seg * ((P.seg_len + BM - 1) / BM);
         const int total = m_tiles * n_nt;
         const int part = (total + 7) >> 3;
         const int q = b >> 3;
         const int t = (b & 7) * part + q;
         if (q >= part || t >= total) return;
-        const int mt = t / n_nt;
-        nt = t - mt * n_nt;
-        if (P.tile_tab) {   // the row-id pass's per-tile table: one load
-            const int4 ti = *(const int4*)(P.tile_tab + 4 * (int64_t)mt);
-            e = ti.x;
-            m0 = ti.y;
-            m_len = ti.z;
-        } else if (P.bounds) {
-            int lo = 0, hi = P.n_seg;  // tile_off[lo] <= mt < tile_off[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (P.tile_off[mid] <= mt) lo = mid; else hi = mid;
+        // expert e owns tiles [n_nt * first_e, n_nt * (first_e + tiles_e)), so the
+        // M tile index t / n_nt falls inside e's M-tile range
+        int first, tiles, row0, rows;
+        if (P.bounds) {
+            const int mt = t / n_nt;
+            if (P.tile_tab) {
+                const int4 ti = *(const int4*)(P.tile_tab + 4 * (int64_t)mt);
+                e = ti.x;
+                first = ti.y;
+                row0 = ti.z;
+                rows = ti.w;
+            } else {
+                int lo = 0, hi = P.n_seg;  // tile_off[lo] <= mt < tile_off[hi]
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (P.tile_off[mid] <= mt) lo = mid; else hi = mid;
+                }
+                e = lo;
+                first = P.tile_off[e];
+                row0 = P.bounds[e];
+                rows = P.bounds[e + 1] - row0;
             }
-            e = lo;
-            m0 = P.bounds[e] + (mt - P.tile_off[e]) * BM;
-            m_len = min(BM, P.bounds[e + 1] - m0);
+            tiles = (rows + BM - 1) / BM;
         } else {
-            const int tps = (P.seg_len + BM - 1) / BM;
-            e = mt / tps;
-            m0 = e * P.seg_len + (mt - e * tps) * BM;
-            m_len = min(BM, (e + 1) * P.seg_len - m0);
+            tiles = (P.seg_len + BM - 1) / BM;
+            e = t / (n_nt * tiles);
+            first = e * tiles;
+            row0 = e * P.seg_len;
+            rows = P.seg_len;
         }
+        // position inside the expert: M tiles in chunks of kMChunk; a chunk runs its N
+        // tiles in turn, each across the chunk's M tiles
+        const int r = t - n_nt * first;
+        const int c = r / (kMChunk * n_nt);
+        const int g = min(kMChunk, tiles - c * kMChunk);
+        const int rr = r - c * kMChunk * n_nt;
+        nt = rr / g;
+        const int j = c * kMChunk + (rr - nt * g);
+        m0 = row0 + j * BM;
+        m_len = min(BM, rows - j * BM);
     }
 
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;

@@ -26,8 +26,8 @@ struct RowIdsArgs {
     int32_t* inv;         // optional [n]: position of entry i in the sorted order
     int32_t* tile_off[2]; // optional [E + 1]: exclusive prefix of ceil(count_e / tile_m[i])
     int32_t tile_m[2];
-    // optional, with tile_off[i]: per M tile j, {expert, first sorted row, rows, 0};
-    // tile_cap[i] entries of room (an upper bound on the tile count)
+    // optional, with tile_off[i]: per M tile j, {expert e owning it, tile_off[e],
+    // bounds[e], rows of e}; tile_cap[i] entries of room (an upper bound on the count)
     int32_t* tile_tab[2];
     int32_t tile_cap[2];
     int32_t* chunk_cnt;   // multi-block scratch [n_chunks][E + 1]
@@ -50,7 +50,7 @@ struct GemmProblem {
     int32_t N, K;
     const int32_t* bounds;    // routed: [n_seg + 1]; nullptr: uniform segments
     const int32_t* tile_off;  // routed: [n_seg + 1] M-tile prefix (tile height = block M)
-    const int32_t* tile_tab;  // routed, optional: per M tile {expert, first row, rows, 0}
+    const int32_t* tile_tab;  // routed, optional: per M tile {expert, its first tile, first row, rows}
     int32_t n_seg;
     int32_t seg_len;          // uniform segments
     int32_t m_tiles_max;      // grid upper bound on M tiles of this problem

@@ -163,12 +163,11 @@ __device__ void write_bounds_and_tiles(const RowIdsArgs& a, const int32_t* bstar
             for (int b = threadIdx.x; b < E; b += kThreads) {
                 const int32_t lo = bstart[b], hi = bstart[b + 1];
                 for (int32_t j = tmp[b]; j < tmp[b + 1] && j < a.tile_cap[q]; j++) {
-                    const int32_t m0 = lo + (j - tmp[b]) * tm;
                     int32_t* t = a.tile_tab[q] + 4 * (int64_t)j;
                     t[0] = b;
-                    t[1] = m0;
-                    t[2] = min(tm, hi - m0);
-                    t[3] = 0;
+                    t[1] = tmp[b];
+                    t[2] = lo;
+                    t[3] = hi - lo;
                 }
             }
         }
