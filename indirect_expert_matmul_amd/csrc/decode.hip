@@ -462,19 +462,41 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
     }
 }
 
-// Rows per wave: enough waves to keep every SIMD streaming (about 8 per SIMD over the
-// whole chip when the grid's upper bound on experts is reached), at least 4 rows per
-// wave so the per-wave start (ids, expert search, activation loads) is amortised.
-int decode_rows_per_wave(const DecArgs& a) {
+// Waves of a kernel that fit on the chip at once (queried once per kernel).
+template <class Kern>
+int resident_waves(Kern kern, int& cache) {
+    if (cache == 0) {
+        int dev = 0, n_cu = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+            n_cu <= 0 || per_cu <= 0) {
+            n_cu = 256;
+            per_cu = 2;
+        }
+        cache = n_cu * per_cu * 4;
+    }
+    return cache;
+}
+
+// Rows per wave, at least 4 so the per-wave start (ids, expert search, activation
+// loads) is amortised. When one resident round of waves covers the grid's upper bound
+// on rows with at most 8 rows per wave, use exactly one round (no partial second
+// round); otherwise aim at about 8 waves per SIMD over the chip, several rounds, so
+// that grids sized for more experts than the batch uses still fill the chip.
+int rows_per_wave(const DecArgs& a, int waves) {
     const int64_t rows = (int64_t)a.d_max * a.rw.N + (a.sw.n_mat > 0 ? (int64_t)a.sw.n_mat * a.sw.N : 0);
-    const int64_t target = 256 * 4 * 8;
-    int64_t r = (rows + target - 1) / target;
+    const int64_t one_round = (rows + waves - 1) / waves;
+    int64_t r = one_round <= 8 ? one_round : (rows + 256 * 4 * 8 - 1) / (256 * 4 * 8);
     return (int)(r < 4 ? 4 : (r > 32 ? 32 : r));
 }
 
 template <int MODE, bool XBF16, int NIT>
 hipError_t launch_wave_nit(DecArgs a, int slots_max, hipStream_t st) {
-    a.rows_per_block = decode_rows_per_wave(a);
+    static int cache1 = 0, cache2 = 0;
+    const int waves = slots_max <= 1 ? resident_waves(k_decode_wave<MODE, 1, XBF16, NIT>, cache1)
+                                     : resident_waves(k_decode_wave<MODE, 2, XBF16, NIT>, cache2);
+    a.rows_per_block = rows_per_wave(a, waves);
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
