@@ -426,6 +426,341 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     }
 }
 
+// Direct global -> LDS copy of one dword per lane from a per-lane 64-bit address
+// (lanes may read different tensors, such as gate and up scales).
+__device__ __forceinline__ void dma4v(const void* addr, uint32_t lds_base) {
+    uint32_t tmp;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dword %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(tmp)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(addr)
+        : "memory");
+}
+
+// Same, 16 bytes per lane.
+__device__ __forceinline__ void dma16v(const void* addr, uint32_t lds_base) {
+    uint32_t tmp;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(tmp)
+        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(addr)
+        : "memory");
+}
+
+// ---------------------------------------------------------------- wide-N variant
+// Same product as k_gemm_q8 for 128-row tiles and K % 64 == 0, with a block tile of
+// 128 activation rows x 512 weight rows. Each of the 8 waves owns 64 weight rows (two
+// MFMA column groups) and all 128 rows, so every activation fragment read from LDS
+// feeds two MFMAs, and a stage of 64 K columns (16 KB activations, 32 KB int8
+// weights) is small enough for a three-slot ring: two stages are in flight while the
+// third is multiplied.
+//
+// Scales (SG): with one word per row per stage (SG = 1) every stage touches one cache
+// line per weight row just for 4 bytes, which costs as many memory requests as the
+// weights themselves. When K % 256 == 0 and the scale rows are 16-byte aligned, SG = 4
+// fetches 16 bytes per row (the blocks of four stages) into a two-slot ring instead.
+namespace wide {
+constexpr int BM = 128, W = 8, KS = 64, NS = 3;
+constexpr int BN = 64 * W;                  // weight rows per block
+constexpr int A_BYTES = BM * KS * 2;        // 128-byte rows, 8 chunks
+constexpr int B_BYTES = BN * KS;            // 64-byte rows, 4 chunks
+template <int SG>
+constexpr int stage_bytes() { return A_BYTES + B_BYTES + (SG == 1 ? BN * 4 : 0); }
+constexpr int SGROUP = BN * 16;             // SG = 4: one group of scales, 16 bytes per row
+template <int SG>
+constexpr int lds_bytes() { return NS * stage_bytes<SG>() + (SG == 4 ? 2 * SGROUP : 0); }
+template <int MODE>
+constexpr int out_cols() { return MODE == 1 ? BN / 2 : BN; }
+__device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
+}  // namespace wide
+
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int MODE, int SG>
+__global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
+    using namespace wide;
+    constexpr int NTW = wide::out_cols<MODE>();
+    constexpr int STAGE = stage_bytes<SG>();
+    // copies per wave per stage: 2 activation + 4 weight (+ 1 scale word if SG = 1);
+    // with SG = 4 every fourth stage also carries one scale-group copy
+    constexpr int VM_STAGE = SG == 1 ? 7 : 6;
+    static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    // ---- tile of this block: the same XCD-aware order as k_gemm_q8
+    int b = (int)blockIdx.x, pi = 0;
+    {
+        const GemmProblem& P0 = args.p[0];
+        const int reg0 = ((P0.m_tiles_max * ((P0.N + NTW - 1) / NTW) + 7) >> 3) * 8;
+        if (b >= reg0) {
+            pi = 1;
+            b -= reg0;
+        }
+    }
+    const GemmProblem& P = args.p[pi];
+    const int N = P.N, K = P.K;
+    const int n_nt = (N + NTW - 1) / NTW;
+    int e, m0, m_len, nt;
+    {
+        const int m_tiles = P.bounds ? P.tile_off[P.n_seg] : P.n_seg * ((P.seg_len + BM - 1) / BM);
+        const int total = m_tiles * n_nt;
+        const int part = (total + 7) >> 3;
+        const int q = b >> 3;
+        const int t = (b & 7) * part + q;
+        if (q >= part || t >= total) return;
+        int first, tiles, row0, rows;
+        if (P.bounds) {
+            const int mt = t / n_nt;
+            if (P.tile_tab) {
+                const int4 ti = *(const int4*)(P.tile_tab + 4 * (int64_t)mt);
+                e = ti.x;
+                first = ti.y;
+                row0 = ti.z;
+                rows = ti.w;
+            } else {
+                int lo = 0, hi = P.n_seg;
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (P.tile_off[mid] <= mt) lo = mid; else hi = mid;
+                }
+                e = lo;
+                first = P.tile_off[e];
+                row0 = P.bounds[e];
+                rows = P.bounds[e + 1] - row0;
+            }
+            tiles = (rows + BM - 1) / BM;
+        } else {
+            tiles = (P.seg_len + BM - 1) / BM;
+            e = t / (n_nt * tiles);
+            first = e * tiles;
+            row0 = e * P.seg_len;
+            rows = P.seg_len;
+        }
+        const int r = t - n_nt * first;
+        const int c = r / (kMChunk * n_nt);
+        const int g = min(kMChunk, tiles - c * kMChunk);
+        const int rr = r - c * kMChunk * n_nt;
+        nt = rr / g;
+        const int j = c * kMChunk + (rr - nt * g);
+        m0 = row0 + j * BM;
+        m_len = min(BM, rows - j * BM);
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nsteps = K / KS;
+    const int KB = K >> 5;
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+
+    // output column of block-local weight row R (0..BN-1). Gate/up mode: the rows of
+    // each 32-row column group are 16 gate rows then the 16 up rows of the same outputs.
+    auto wrow = [&](int R) -> int {
+        const int n = MODE == 1 ? nt * NTW + (R >> 5) * 16 + (R & 15) : nt * NTW + R;
+        return min(n, N - 1);
+    };
+
+    // ---- copy geometry (stage 0)
+    const uint8_t* a_base = (const uint8_t*)uniform_ptr(P.A);
+    uint32_t a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int R = (wv * 2 + i) * 8 + (lane >> 3);     // tile row this lane fetches
+        const int lc = (lane & 7) ^ swz_wa(R);
+        const int j = m0 + min(R, m_len - 1);
+        const int64_t src = P.a_rows ? (int64_t)P.a_rows[j]
+                                     : (int64_t)(P.a_row_mod ? j % P.a_row_mod : j);
+        a_off[i] = (uint32_t)(src * P.lda * 2 + lc * 16);
+    }
+    // weights: copy i of wave w covers rows 64w + 16i .. +15 (4 lanes x 16 B per row);
+    // in gate/up mode odd copies hold up rows
+    const int8_t* qg = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * K);
+    const int8_t* qu = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * K) : qg;
+    uint32_t b_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int R = wv * 64 + 16 * i + (lane >> 2);
+        const int lc = (lane & 3) ^ swz_wb(R);
+        b_off[i] = (uint32_t)((int64_t)wrow(R) * K + lc * 16);
+    }
+    // scales: lane l of wave w fetches for row 64w + l, from a per-lane address (gate
+    // and up rows sit in different tensors). SG = 1: the word of blocks 2s, 2s+1 at
+    // stage s (K % 64 == 0 keeps the pair inside one aligned word); SG = 4: the 16
+    // bytes of blocks 8g .. 8g+7 for stages 4g .. 4g+3.
+    const uint8_t* s_ptr;
+    {
+        const int R = wv * 64 + lane;
+        const uint16_t* dt = (MODE == 1 && (R & 16)) ? P.d2 : P.d1;
+        s_ptr = (const uint8_t*)(dt + ((int64_t)e * N + wrow(R)) * KB);
+    }
+    const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
+
+    auto issue = [&](int s, int slot) {
+        const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
+        const int k0 = s * KS;
+#pragma unroll
+        for (int i = 0; i < 2; i++) dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * 2 + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            dma16(((MODE == 1 && (i & 1)) ? qu : qg) + k0, b_off[i], st + A_BYTES + (wv * 4 + i) * 1024);
+        if (SG == 1) {
+            dma4v(s_ptr + 4 * s, st + A_BYTES + B_BYTES + wv * 256);
+        } else if ((s & 3) == 0) {
+            dma16v(s_ptr + 4 * s, sring + (uint32_t)(((s >> 2) & 1) * SGROUP) + wv * 1024);
+        }
+    };
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int c = 0; c < 2; c++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][c][v] = 0.f;
+
+    // One step: wait for stage s (stage s+1 may stay in flight), send stage s+2 into
+    // the slot that step s-1 read, dequantize and multiply.
+    auto step = [&](int s, auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
+        if (s + 1 >= nsteps) wait_vm_lgkm_barrier<0>();
+        else if (SG == 4 && ((s + 1) & 3) == 0) wait_vm_lgkm_barrier<VM_STAGE + 1>();
+        else wait_vm_lgkm_barrier<VM_STAGE>();
+        if (s + 2 < nsteps) issue(s + 2, (SLOT + 2) % NS);
+        const uint8_t* st = smem + SLOT * STAGE;
+        const uint8_t* sg = SG == 1 ? st + A_BYTES + B_BYTES
+                                    : smem + NS * STAGE + ((s >> 2) & 1) * SGROUP + (s & 3) * 4;
+        bf16x8 bf[2][4];
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int lr = wv * 64 + c * 32 + l32;
+            const uint8_t* rowp = st + A_BYTES + lr * 64;
+            const i32x4 q0 = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
+            const i32x4 q1 = *(const i32x4*)(rowp + (((2 * h + 1) ^ swz_wb(lr)) << 4));
+            const uint32_t sw = *(const uint32_t*)(sg + lr * (SG == 1 ? 4 : 16));
+            const float d = half_bits_to_float((uint16_t)(sw >> (16 * h)));
+            bf[c][0] = dequant8(q0[0], q0[1], d);
+            bf[c][1] = dequant8(q0[2], q0[3], d);
+            bf[c][2] = dequant8(q1[0], q1[1], d);
+            bf[c][3] = dequant8(q1[2], q1[3], d);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int r = i * 32 + l32;
+#pragma unroll
+            for (int ss = 0; ss < 4; ss++) {
+                const bf16x8 af = *(const bf16x8*)(st + r * 128 + (((4 * h + ss) ^ swz_wa(r)) << 4));
+#pragma unroll
+                for (int c = 0; c < 2; c++)
+                    acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[c][ss], acc[i][c], 0, 0, 0);
+            }
+        }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+
+    issue(0, 0);
+    if (nsteps > 1) issue(1, 1);
+    int s = 0;
+    for (; s + 3 <= nsteps; s += 3) {
+        step(s, S0{});
+        step(s + 1, S1{});
+        step(s + 2, S2{});
+    }
+    if (s < nsteps) step(s, S0{});
+    if (s + 1 < nsteps) step(s + 1, S1{});
+
+    // ---- output rows into the (now idle) ring: every copy has landed (the last step
+    // waited for all of them) and the barrier ends every wave's reads of the ring
+    int32_t* s_orow = (int32_t*)smem;
+    __syncthreads();
+    if (tid < BM) {
+        const int j = m0 + min(tid, m_len - 1);
+        s_orow[tid] = P.out_rows ? P.out_rows[j] : j;
+    }
+    __syncthreads();
+
+    // ---- epilogue. Accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4 of
+    // the 32x32 sub-tile and column l%32 of the column group.
+    if (MODE == 1) {
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int n = nt * NTW + wv * 32 + c * 16 + (l32 & 15);
+            const bool writer = l32 < 16 && n < N;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (i * 32 >= m_len) continue;
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const float up = __shfl_xor(acc[i][c][v], 16);
+                    const int row = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (writer && row < m_len) {
+                        const float g = acc[i][c][v];
+                        const float hv = g / (1.0f + __expf(-g)) * up;
+                        ((__bf16*)P.out)[(int64_t)s_orow[row] * P.ldo + n] = (__bf16)hv;
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int n = nt * NTW + wv * 64 + c * 32 + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                if (i * 32 >= m_len) continue;
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int row = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (row < m_len) ((float*)P.out)[(int64_t)s_orow[row] * P.ldo + n] = acc[i][c][v];
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, int SG>
+hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
+    constexpr int lds = wide::lds_bytes<SG>();
+    static_assert(lds <= 160 * 1024, "LDS ring exceeds 160 KB");
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    k_gemm_q8w<MODE, SG><<<grid, 64 * wide::W, lds, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
+    constexpr int ntw = wide::out_cols<MODE>();
+    int64_t total = 0;
+    bool groups = true;   // scale groups of four stages for every problem
+    for (int i = 0; i < a.n_prob; i++) {
+        const GemmProblem& p = a.p[i];
+        total += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
+        groups = groups && p.K % 256 == 0 && ((uintptr_t)p.d1 & 15) == 0 &&
+                 (MODE == 0 || ((uintptr_t)p.d2 & 15) == 0);
+    }
+    if (total <= 0) return hipSuccess;
+    GemmArgs g = a;
+    g.grid_real = (int32_t)total;
+    return groups ? launch_wide_sg<MODE, 4>(g, (int)total, st) : launch_wide_sg<MODE, 1>(g, (int)total, st);
+}
+
 template <int MSUB, int W, int NS>
 constexpr int stage_lds() { return NS * (32 * MSUB * 256 + W * 32 * 128 + W * 32 * 16); }
 
@@ -470,7 +805,14 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
     switch (msub) {
         case 2: return launch_cfg<2, MOE_GEMM_CFG2>(a, st);
-        case 4: return launch_cfg<4, MOE_GEMM_CFG4>(a, st);
+        case 4: {
+#ifndef MOE_GEMM_NO_WIDE
+            bool wide_ok = true;
+            for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
+            if (wide_ok) return a.mode == 1 ? launch_wide<1>(a, st) : launch_wide<0>(a, st);
+#endif
+            return launch_cfg<4, MOE_GEMM_CFG4>(a, st);
+        }
         default: return hipErrorInvalidValue;
     }
 }
