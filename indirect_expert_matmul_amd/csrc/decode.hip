@@ -7,19 +7,24 @@
 //
 // gfx950 design. Decode is a weight stream: every selected expert's Q8_0 rows are
 // read from HBM exactly once per launch and applied to every token slot that uses
-// that expert.
-//   * Block = 4 wavefronts; a block owns (one distinct expert, a chunk of rows).
-//     The distinct experts are found inside the block from ids (n_tokens * n_used
-//     <= 256 entries): no separate row-id launch on the latency-critical path.
-//   * The expert's activation rows (bf16 x, or fp32 h for the down projection) are
-//     staged once per block into LDS as fp32, padded by 16 bytes per 64 so the
-//     lanes' 16-float reads hit distinct banks.
-//   * A wave streams one weight row per step: each lane loads 16 contiguous int8
-//     (a half Q8_0 block) and its fp16 scale, converts q exactly to fp32 and does
-//     fp32 FMAs against every staged slot; the per-block scale multiplies the
-//     16-term partial sum. Cross-lane sums use shuffles. All arithmetic is fp32.
-//   * Results are written per slot; the fixed-order weighted reduction runs in
-//     the reduce kernel.
+// that expert. The distinct experts are found on the device from ids (a wave-wide
+// bitmap OR), so no row-id launch sits on the latency-critical path, and the grid is
+// sized for an upper bound on them.
+//   * One wave owns (one distinct expert, a chunk of R rows); R comes from the
+//     kernel's resident-wave count. Each lane takes 16 contiguous int8 of a row per
+//     1024-wide K piece, converts them exactly to fp32 and does fp32 FMAs against the
+//     slot's activations held in registers; the per-block scale multiplies the
+//     16-term partial sum. Lane sums use DPP; lane 63 writes the result.
+//   * One activation row per pass (single-token decode): rows are double-buffered in
+//     registers, which leaves room for two or more waves per SIMD.
+//   * Two per pass: the activations fill the register file, so the rows stream
+//     through a per-wave ring in LDS with direct global-to-LDS copies (the bytes in
+//     flight cost no registers).
+//   * For larger batches or K a block kernel (4 waves per chunk of rows, activations
+//     staged in LDS) takes over.
+//   * Results are written per slot; the fixed-order weighted reduction runs in the
+//     reduce kernel.
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,9 +39,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
-}
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
-    return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 // Sum over the 64 lanes of a wave with DPP moves (no LDS traffic), in a fixed
 // tree: within each row of 16 lanes by shifts of 1, 2, 4, 8, then across rows by
@@ -290,6 +292,20 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
     return __ffsll((unsigned long long)m) - 1;
 }
 
+// Streaming GEMV, one wave per (expert, chunk of R rows), for K <= 4096. The wave
+// copies its weight rows (a gate/up pair in gate/up mode) straight from global memory
+// into a ring of NR row slots in its own part of LDS, keeping NR-1 rows in flight
+// while it multiplies the oldest: the bytes in flight cost no registers, so the
+// occupancy is set by LDS, not by the row buffers. A wave only reads slots its own
+// copies wrote, so no barrier is needed; its vmcnt says when a row has landed.
+//
+// Slot layout per matrix: NIT KB of int8 (piece i at 1024*i, lane l's 16 bytes at
+// 16*l, the row's byte k at offset k) and 256 bytes for the row's fp16 scales (the
+// aligned dwords holding them; the row's first scale sits at byte (row offset & 3)).
+// Register-staged GEMV, one wave per (expert, chunk of R rows): the wave streams its
+// rows two at a time through registers (the next row's loads in flight while one
+// computes). With one activation row per pass it needs few registers and keeps two
+// or more waves per SIMD, which beats staging through LDS for single-token decode.
 template <int MODE, int P, bool XBF16, int NIT>
 __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
     constexpr int M = MODE == 1 ? 2 : 1;
@@ -462,14 +478,231 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
     }
 }
 
+// ring slots per wave (gate/up pairs, single rows) and blocks per CU the registers
+// are budgeted for
+#ifndef MOE_DEC_NR1
+#define MOE_DEC_NR1 3
+#endif
+#ifndef MOE_DEC_NR0
+#define MOE_DEC_NR0 5
+#endif
+#ifndef MOE_DEC_MINB
+#define MOE_DEC_MINB 2
+#endif
+
+// s_waitcnt vmcnt(after * D) for a run-time after in [0, MAXA].
+template <int D, int MAXA>
+__device__ __forceinline__ void wait_rows(int after) {
+    if constexpr (MAXA == 0) {
+        wait_vm<0>();
+    } else {
+        if (after >= MAXA) wait_vm<MAXA * D>();
+        else wait_rows<D, MAXA - 1>(after);
+    }
+}
+
+template <int MODE, int NIT>
+struct StreamSlot {
+    static constexpr int MAT = NIT * 1024 + 256;
+    static constexpr int BYTES = (MODE == 1 ? 2 : 1) * MAT;
+    static constexpr int NR_CFG = MODE == 1 ? MOE_DEC_NR1 : MOE_DEC_NR0;
+    static constexpr int NR_FIT = 160 * 1024 / (4 * BYTES);
+    static constexpr int NR = NR_CFG < NR_FIT ? NR_CFG : NR_FIT;   // ring slots per wave
+    static constexpr int LDS = 4 * NR * BYTES;       // 4 waves per block
+};
+
+template <int MODE, int P, bool XBF16, int NIT>
+__global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) {
+    constexpr int M = MODE == 1 ? 2 : 1;
+    using G = StreamSlot<MODE, NIT>;
+    constexpr int MAT = G::MAT, SLOT = G::BYTES, NR = G::NR;
+    constexpr int D = M * (NIT + 1);   // copies per row (pair)
+    static_assert((NR - 1) * D <= 63, "vmcnt counts to 63");
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
+    const int R = a.rows_per_block;  // rows per wave
+    const int nch_r = (a.rw.N + R - 1) / R;
+    const int nw_r = a.d_max * nch_r;
+    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0;
+    if (gw >= nw_r + nw_s) return;
+    const bool routed = gw < nw_r;
+    const DecWeights& W = routed ? a.rw : a.sw;
+    const int N = W.N, K = W.K;
+    int e, chunk, cnt;
+    uint64_t smask = 0;  // routed: lanes (entries t*k+s) of this expert
+    if (routed) {
+        const int d = gw / nch_r;
+        chunk = gw - d * nch_r;
+        const int n = a.T * a.k;
+        int v = lane < n ? a.ids[lane] : -1;
+        if (v >= a.E) v = -1;
+        // distinct experts present: a 64-expert bitmap word at a time (wave OR), the
+        // d-th set bit over the words in ascending order is this wave's expert
+        e = -1;
+        int seen = 0;
+        for (int w0 = 0; w0 < a.E && e < 0; w0 += 64) {
+            const int rel = v - w0;
+            const bool in = v >= 0 && rel >= 0 && rel < 64;
+            const uint32_t lo = wave_or_u32(in && rel < 32 ? 1u << rel : 0u);
+            const uint32_t hi = wave_or_u32(in && rel >= 32 ? 1u << (rel - 32) : 0u);
+            const uint64_t present = ((uint64_t)hi << 32) | lo;
+            const int c = __popcll(present);
+            if (d < seen + c) e = w0 + nth_set_bit(present, d - seen);
+            seen += c;
+        }
+        if (e < 0) return;  // fewer distinct experts than the grid allows for
+        smask = __ballot(v == e);
+        cnt = __popcll(smask);
+    } else {
+        const int nch_s = (a.sw.N + R - 1) / R;
+        const int b = gw - nw_r;
+        e = b / nch_s;
+        chunk = b - e * nch_s;
+        cnt = a.T;
+    }
+    const int n_lo = chunk * R;
+    const int n_hi = min(n_lo + R, N);
+    const int nrows = n_hi - n_lo;
+    const int KB = K >> 5;
+    const void* src = routed ? a.act : a.sact;
+    auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
+    auto src_row = [&](int p) -> int64_t {
+        if (routed) {
+            const int slot = slot_of(p);
+            const int t = slot / a.k, s = slot - t * a.k;
+            return (int64_t)t * a.act_B + s % a.act_B;
+        }
+        return (int64_t)e * a.sact_jstride + p;
+    };
+    // lane's K pieces: k = 1024*i + 16*lane. Pieces past K copy the row's last 16
+    // bytes (a valid address), read column 0 of the activations and get a zero scale.
+    int kc[NIT];
+    bool kin[NIT];
+    uint32_t qoff[NIT];
+#pragma unroll
+    for (int i = 0; i < NIT; i++) {
+        const int k = (i << 10) + (lane << 4);
+        kin[i] = k < K;
+        kc[i] = kin[i] ? k : 0;
+        qoff[i] = (uint32_t)(kin[i] ? k : K - 16);
+    }
+    const int8_t* q1 = W.qs1 + (int64_t)e * N * K;
+    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * K : q1;
+    const uint8_t* d1 = (const uint8_t*)(W.d1 + (int64_t)e * N * KB);
+    const uint8_t* d2 = MODE == 1 ? (const uint8_t*)(W.d2 + (int64_t)e * N * KB) : d1;
+    uint8_t* ring = smem + (threadIdx.x >> 6) * (NR * SLOT);
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+
+    // copies of row n into slot j: per matrix NIT 16-byte pieces and one word per lane
+    // of scales (lanes past the row's last word re-read it)
+    auto issue_row = [&](int n, int j) {
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const uint32_t dst = ring_lds + (uint32_t)(j * SLOT + m * MAT);
+            const int8_t* qrow = (const int8_t*)uniform_ptr((m == 0 ? q1 : q2) + (int64_t)n * K);
+#pragma unroll
+            for (int i = 0; i < NIT; i++) dma16(qrow, qoff[i], dst + i * 1024);
+            const uintptr_t sa = (uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * 2);  // first scale
+            const uint8_t* srow = (const uint8_t*)uniform_ptr((const void*)(sa & ~(uintptr_t)3));
+            const int last = ((int)(sa & 3) + 2 * KB - 1) >> 2;
+            dma4(srow, (uint32_t)(min(lane, last) * 4), dst + NIT * 1024);
+        }
+    };
+    // wait until row j of this pass has landed, given how many rows were sent after it
+    auto wait_row = [&](int after) { wait_rows<D, NR - 1>(after); };
+
+    for (int p0 = 0; p0 < cnt; p0 += P) {
+        const int pc = min(P, cnt - p0);
+        // activations of this pass's slots, exact fp32
+        float x[P][NIT][16];
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            const int64_t row = src_row(p0 + min(p, pc - 1));
+#pragma unroll
+            for (int i = 0; i < NIT; i++) {
+                if constexpr (XBF16) {
+                    const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
+                    const i32x4 r0 = *(const i32x4*)(xp);
+                    const i32x4 r1 = *(const i32x4*)(xp + 8);
+#pragma unroll
+                    for (int c = 0; c < 8; c++) {
+                        const uint32_t w = (uint32_t)(c < 4 ? r0[c] : r1[c - 4]);
+                        x[p][i][2 * c] = __builtin_bit_cast(float, w << 16);
+                        x[p][i][2 * c + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
+                    }
+                } else {
+                    const float* xp = (const float*)src + row * K + kc[i];
+#pragma unroll
+                    for (int c = 0; c < 4; c++) {
+                        const f32x4 v = *(const f32x4*)(xp + 4 * c);
+#pragma unroll
+                        for (int j = 0; j < 4; j++) x[p][i][4 * c + j] = v[j];
+                    }
+                }
+            }
+        }
+        auto compute_row = [&](int n, int j) {
+            const uint8_t* sl = ring + j * SLOT;
+            float acc[M][P];
+#pragma unroll
+            for (int m = 0; m < M; m++)
+#pragma unroll
+                for (int p = 0; p < P; p++) acc[m][p] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NIT; i++)
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    const uint8_t* mp = sl + m * MAT;
+                    const int s0 = (int)((uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * 2) & 3);
+                    const i32x4 q = *(const i32x4*)(mp + (i << 10) + (lane << 4));
+                    const uint16_t db = *(const uint16_t*)(mp + NIT * 1024 + s0 + 2 * (kc[i] >> 5));
+                    // lanes past K add 0 through a zero scale instead of branching
+                    const float dd = kin[i] ? half_bits_to_float(db) : 0.f;
+#pragma unroll
+                    for (int p = 0; p < P; p++) {
+                        const float* xv = x[p][i];
+                        acc[m][p] = fmaf(dd, dot16(q, f32x4{xv[0], xv[1], xv[2], xv[3]},
+                                                   f32x4{xv[4], xv[5], xv[6], xv[7]},
+                                                   f32x4{xv[8], xv[9], xv[10], xv[11]},
+                                                   f32x4{xv[12], xv[13], xv[14], xv[15]}),
+                                         acc[m][p]);
+                    }
+                }
+#pragma unroll
+            for (int p = 0; p < P; p++) {
+                if (p >= pc) continue;
+                const float g = wave_sum_lane63(acc[0][p]);
+                float res = g;
+                if (MODE == 1) {
+                    const float u = wave_sum_lane63(acc[M - 1][p]);
+                    res = g / (1.0f + __expf(-g)) * u;
+                }
+                if (lane == 63) {
+                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + n] = res;
+                    else a.sout[((int64_t)e * a.T + p0 + p) * N + n] = res;
+                }
+            }
+        };
+        // ring: rows 0 .. NR-2 in flight before the first multiply; row j+NR-1 goes
+        // into the slot row j-1 used (read completely before this point)
+        for (int j = 0; j < NR - 1 && j < nrows; j++) issue_row(n_lo + j, j);
+        for (int j = 0; j < nrows; j++) {
+            if (j + NR - 1 < nrows) issue_row(n_lo + j + NR - 1, (j + NR - 1) % NR);
+            wait_row(min(NR - 1, nrows - 1 - j));
+            compute_row(n_lo + j, j % NR);
+        }
+    }
+}
+
 // Waves of a kernel that fit on the chip at once (queried once per kernel).
 template <class Kern>
-int resident_waves(Kern kern, int& cache) {
+int resident_waves(Kern kern, size_t lds, int& cache) {
     if (cache == 0) {
         int dev = 0, n_cu = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess ||
             n_cu <= 0 || per_cu <= 0) {
             n_cu = 256;
             per_cu = 2;
@@ -491,20 +724,46 @@ int rows_per_wave(const DecArgs& a, int waves) {
     return (int)(r < 4 ? 4 : (r > 32 ? 32 : r));
 }
 
-template <int MODE, bool XBF16, int NIT>
-hipError_t launch_wave_nit(DecArgs a, int slots_max, hipStream_t st) {
-    static int cache1 = 0, cache2 = 0;
-    const int waves = slots_max <= 1 ? resident_waves(k_decode_wave<MODE, 1, XBF16, NIT>, cache1)
-                                     : resident_waves(k_decode_wave<MODE, 2, XBF16, NIT>, cache2);
-    a.rows_per_block = rows_per_wave(a, waves);
+template <int MODE, int P, bool XBF16, int NIT>
+hipError_t launch_stream(DecArgs a, hipStream_t st) {
+    constexpr int lds = StreamSlot<MODE, NIT>::LDS;
+    static_assert(lds <= 160 * 1024, "ring exceeds LDS");
+    static int cache = 0;
+    static bool attr_set = false;   // raise the dynamic LDS cap once per process
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute((const void*)k_decode_stream<MODE, P, XBF16, NIT>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_stream<MODE, P, XBF16, NIT>, lds, cache));
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
     if (nw <= 0) return hipSuccess;
     const int grid = (nw + 3) / 4;
-    if (slots_max <= 1) k_decode_wave<MODE, 1, XBF16, NIT><<<grid, 256, 0, st>>>(a);
-    else k_decode_wave<MODE, 2, XBF16, NIT><<<grid, 256, 0, st>>>(a);
+    k_decode_stream<MODE, P, XBF16, NIT><<<grid, 256, lds, st>>>(a);
     return hipGetLastError();
+}
+
+template <int MODE, bool XBF16, int NIT>
+hipError_t launch_regs(DecArgs a, hipStream_t st) {
+    static int cache = 0;
+    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_wave<MODE, 1, XBF16, NIT>, 0, cache));
+    const int R = a.rows_per_block;
+    const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
+                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
+    if (nw <= 0) return hipSuccess;
+    k_decode_wave<MODE, 1, XBF16, NIT><<<(nw + 3) / 4, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+// One activation row per pass: register staging. Two per pass: the two rows' fp32
+// activations take too many registers to also hold rows in flight, so the rows stream
+// through LDS.
+template <int MODE, bool XBF16, int NIT>
+hipError_t launch_wave_nit(const DecArgs& a, int slots_max, hipStream_t st) {
+    return slots_max <= 1 ? launch_regs<MODE, XBF16, NIT>(a, st) : launch_stream<MODE, 2, XBF16, NIT>(a, st);
 }
 
 template <int MODE, bool XBF16>

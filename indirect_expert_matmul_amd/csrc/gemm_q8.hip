@@ -37,6 +37,7 @@
 //     tile count exit at once.
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 #ifndef MOE_GEMM_CFG2
@@ -69,52 +70,6 @@ __device__ __forceinline__ bf16x8 dequant8(int lo, int hi, float d) {
     r[6] = (__bf16)((float)(int8_t)(hi >> 16) * d);
     r[7] = (__bf16)((float)(int8_t)(hi >> 24) * d);
     return r;
-}
-
-// LDS byte address of a shared-memory pointer (the M0 operand of an LDS DMA).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct global -> LDS copies. Lane i of the wave reads base + voff (a per-lane
-// 32-bit byte offset from a wave-uniform 64-bit base) and writes LDS
-// [lds_base + size*i, +size). Issued as inline asm so that the waits are ours: the
-// compiler would otherwise drain every outstanding load at each barrier. M0 is saved
-// and restored around the copy.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
-    uint32_t tmp;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base)
-        : "memory");
-}
-__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_base) {
-    uint32_t tmp;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dword %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base)
-        : "memory");
-}
-// Wait until at most N of this wave's vector-memory operations are outstanding
-// and until this wave's LDS reads returned, then meet the other waves at the barrier
-// (LDS DMA data of every wave landed; no wave still reads a buffer about to be refilled).
-template <int N>
-__device__ __forceinline__ void wait_stage_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Chunk swizzles. Activation rows are 256 bytes (16 chunks): chunk c of row r sits at
@@ -426,33 +381,6 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     }
 }
 
-// Direct global -> LDS copy of one dword per lane from a per-lane 64-bit address
-// (lanes may read different tensors, such as gate and up scales).
-__device__ __forceinline__ void dma4v(const void* addr, uint32_t lds_base) {
-    uint32_t tmp;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dword %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(addr)
-        : "memory");
-}
-
-// Same, 16 bytes per lane.
-__device__ __forceinline__ void dma16v(const void* addr, uint32_t lds_base) {
-    uint32_t tmp;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(addr)
-        : "memory");
-}
-
 // ---------------------------------------------------------------- wide-N variant
 // Same product as k_gemm_q8 for 128-row tiles and K % 64 == 0, with a block tile of
 // 128 activation rows x 512 weight rows. Each of the 8 waves owns 64 weight rows (two
@@ -480,11 +408,6 @@ constexpr int out_cols() { return MODE == 1 ? BN / 2 : BN; }
 __device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
 }  // namespace wide
-
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 template <int MODE, int SG>
 __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
@@ -631,37 +554,73 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
     // the slot that step s-1 read, dequantize and multiply.
     auto step = [&](int s, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
-        if (s + 1 >= nsteps) wait_vm_lgkm_barrier<0>();
-        else if (SG == 4 && ((s + 1) & 3) == 0) wait_vm_lgkm_barrier<VM_STAGE + 1>();
-        else wait_vm_lgkm_barrier<VM_STAGE>();
+        if (s + 1 >= nsteps) wait_stage_and_barrier<0>();
+        else if (SG == 4 && ((s + 1) & 3) == 0) wait_stage_and_barrier<VM_STAGE + 1>();
+        else wait_stage_and_barrier<VM_STAGE>();
         if (s + 2 < nsteps) issue(s + 2, (SLOT + 2) % NS);
         const uint8_t* st = smem + SLOT * STAGE;
         const uint8_t* sg = SG == 1 ? st + A_BYTES + B_BYTES
                                     : smem + NS * STAGE + ((s >> 2) & 1) * SGROUP + (s & 3) * 4;
-        bf16x8 bf[2][4];
+        // operands of the stage: both column groups' 32 int8 weights and scale, and
+        // the activation fragments of k sub-step 0
+        i32x4 q[2][2];
+        float d[2];
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int lr = wv * 64 + c * 32 + l32;
             const uint8_t* rowp = st + A_BYTES + lr * 64;
-            const i32x4 q0 = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
-            const i32x4 q1 = *(const i32x4*)(rowp + (((2 * h + 1) ^ swz_wb(lr)) << 4));
+            q[c][0] = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
+            q[c][1] = *(const i32x4*)(rowp + (((2 * h + 1) ^ swz_wb(lr)) << 4));
             const uint32_t sw = *(const uint32_t*)(sg + lr * (SG == 1 ? 4 : 16));
-            const float d = half_bits_to_float((uint16_t)(sw >> (16 * h)));
-            bf[c][0] = dequant8(q0[0], q0[1], d);
-            bf[c][1] = dequant8(q0[2], q0[3], d);
-            bf[c][2] = dequant8(q1[0], q1[1], d);
-            bf[c][3] = dequant8(q1[2], q1[3], d);
+            d[c] = half_bits_to_float((uint16_t)(sw >> (16 * h)));
         }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
+        auto afrag = [&](int i, int ss) -> bf16x8 {
             const int r = i * 32 + l32;
+            return *(const bf16x8*)(st + r * 128 + (((4 * h + ss) ^ swz_wa(r)) << 4));
+        };
+        auto deq = [&](int c, int ss) -> bf16x8 {
+            const i32x4& v = q[c][ss >> 1];
+            return (ss & 1) ? dequant8(v[2], v[3], d[c]) : dequant8(v[0], v[1], d[c]);
+        };
+        bf16x8 af[2][4], bf[2][2];
 #pragma unroll
-            for (int ss = 0; ss < 4; ss++) {
-                const bf16x8 af = *(const bf16x8*)(st + r * 128 + (((4 * h + ss) ^ swz_wa(r)) << 4));
+        for (int i = 0; i < 4; i++) af[0][i] = afrag(i, 0);
+        bf[0][0] = deq(0, 0);
+        bf[0][1] = deq(1, 0);
+        // k sub-step ss: its 8 MFMAs run while the next sub-step's weights are
+        // dequantized and its activation fragments read. Each sub-step is a
+        // scheduling region of its own, with the interleave pinned inside it; left
+        // alone the compiler runs all dequant work of the stage first, and the two
+        // waves of a SIMD, kept in step by the stage barrier, then contend for the
+        // vector ALU and the matrix unit at the same time instead of overlapping.
+#ifndef MOE_GEMM_NO_SCHED
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+#pragma unroll
+        for (int ss = 0; ss < 4; ss++) {
+            const int cur = ss & 1, nxt = cur ^ 1;
+            if (ss < 3) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) af[nxt][i] = afrag(i, ss + 1);
+                bf[nxt][0] = deq(0, ss + 1);
+                bf[nxt][1] = deq(1, ss + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int c = 0; c < 2; c++)
-                    acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[c][ss], acc[i][c], 0, 0, 0);
+                    acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][c], acc[i][c], 0, 0, 0);
+#ifndef MOE_GEMM_NO_SCHED
+            if (ss < 3) {
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                    if ((m & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
     using S0 = std::integral_constant<int, 0>;

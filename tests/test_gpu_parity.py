@@ -43,6 +43,7 @@ def test_tiny_fp32_mul_mat_id():
     (6, 3, 9, 96, 40, True, True),       # one src1 row per slot, invalid ids
     (16, 2, 50, 256, 300, False, False), # several N tiles plus a ragged one
     (4, 4, 60, 128, 64, False, True),    # k = E, several M tiles per expert
+    (5, 2, 7, 96, 45, False, False),     # odd N and K/32: rows of scales start at 2 mod 4
 ])
 def test_q8_mul_mat_id(path, E, k, T, K, N, B_is_k, bad):
     if path == moe.PATH_GEMV and T * k > 256:
