@@ -527,7 +527,7 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
     }
     const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
 
-    auto issue = [&](int s, int slot) {
+    auto issue = [&](int s, int slot) __attribute__((always_inline)) {
         const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
         const int k0 = s * KS;
 #pragma unroll
@@ -551,9 +551,12 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
             for (int v = 0; v < 16; v++) acc[i][c][v] = 0.f;
 
     // One step: wait for stage s (stage s+1 may stay in flight), send stage s+2 into
-    // the slot that step s-1 read, dequantize and multiply.
-    auto step = [&](int s, auto slot_c) {
+    // the slot that step s-1 read, dequantize and multiply. MACT = 32-row sub-tiles
+    // that hold rows of the tile: the last tile of an expert is often mostly empty,
+    // and its empty sub-tiles skip their fragment reads and MFMAs.
+    auto step = [&](int s, auto slot_c, auto mact_c) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
+        constexpr int MACT = decltype(mact_c)::value;
         if (s + 1 >= nsteps) wait_stage_and_barrier<0>();
         else if (SG == 4 && ((s + 1) & 3) == 0) wait_stage_and_barrier<VM_STAGE + 1>();
         else wait_stage_and_barrier<VM_STAGE>();
@@ -584,7 +587,7 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
         };
         bf16x8 af[2][4], bf[2][2];
 #pragma unroll
-        for (int i = 0; i < 4; i++) af[0][i] = afrag(i, 0);
+        for (int i = 0; i < MACT; i++) af[0][i] = afrag(i, 0);
         bf[0][0] = deq(0, 0);
         bf[0][1] = deq(1, 0);
         // k sub-step ss: its 8 MFMAs run while the next sub-step's weights are
@@ -601,21 +604,23 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
             const int cur = ss & 1, nxt = cur ^ 1;
             if (ss < 3) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) af[nxt][i] = afrag(i, ss + 1);
+                for (int i = 0; i < MACT; i++) af[nxt][i] = afrag(i, ss + 1);
                 bf[nxt][0] = deq(0, ss + 1);
                 bf[nxt][1] = deq(1, ss + 1);
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < MACT; i++)
 #pragma unroll
                 for (int c = 0; c < 2; c++)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][c], acc[i][c], 0, 0, 0);
 #ifndef MOE_GEMM_NO_SCHED
             if (ss < 3) {
+                // 2*MACT MFMAs share the sub-step's 40 dequant instructions
+                constexpr int VPM = (40 + 2 * MACT - 1) / (2 * MACT);
 #pragma unroll
-                for (int m = 0; m < 8; m++) {
+                for (int m = 0; m < 2 * MACT; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
                     if ((m & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
@@ -627,16 +632,23 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
 
-    issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
-    int s = 0;
-    for (; s + 3 <= nsteps; s += 3) {
-        step(s, S0{});
-        step(s + 1, S1{});
-        step(s + 2, S2{});
-    }
-    if (s < nsteps) step(s, S0{});
-    if (s + 1 < nsteps) step(s + 1, S1{});
+    auto k_loop = [&](auto mact_c) __attribute__((always_inline)) {
+        issue(0, 0);
+        if (nsteps > 1) issue(1, 1);
+        int s = 0;
+        for (; s + 3 <= nsteps; s += 3) {
+            step(s, S0{}, mact_c);
+            step(s + 1, S1{}, mact_c);
+            step(s + 2, S2{}, mact_c);
+        }
+        if (s < nsteps) step(s, S0{}, mact_c);
+        if (s + 1 < nsteps) step(s + 1, S1{}, mact_c);
+    };
+    const int mact = (m_len + 31) >> 5;   // block-uniform
+    if (mact >= 4) k_loop(std::integral_constant<int, 4>{});
+    else if (mact == 3) k_loop(std::integral_constant<int, 3>{});
+    else if (mact == 2) k_loop(std::integral_constant<int, 2>{});
+    else k_loop(std::integral_constant<int, 1>{});
 
     // ---- output rows into the (now idle) ring: every copy has landed (the last step
     // waited for all of them) and the barrier ends every wave's reads of the ring
