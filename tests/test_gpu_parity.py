@@ -69,6 +69,34 @@ def test_q8_mul_mat_id(path, E, k, T, K, N, B_is_k, bad):
     assert np.all(g[invalid] == 0.0)
 
 
+# Shapes whose segments average more than 64 rows take 128-row tiles: the wide
+# kernel (K % 64 == 0; scale groups of four stages when K % 256 == 0, else one scale
+# word per stage) or, for other K, the 128-row kernel with 256-row N tiles.
+@pytest.mark.parametrize("E,k,T,K,N,bad", [
+    (3, 2, 200, 192, 600, False),   # scale word per stage, N ragged over 512-row tiles
+    (5, 3, 300, 512, 520, True),    # scale groups, ragged N, partly filled sub-tiles, bad ids
+    (2, 2, 150, 96, 130, False),    # K % 64 != 0: the 128-row fallback
+])
+def test_q8_mul_mat_id_tall_tiles(E, k, T, K, N, bad):
+    ids = synth.draw_ids_uniform(17, T, E, k)
+    if bad:
+        ids[3, 1], ids[T - 1, 0] = -2, E
+    inp = synth.make_custom_mmid(19, E, k, T, K, N, ids=ids)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(T).standard_normal((T, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), path=moe.PATH_GEMM)
+    gotw = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                              path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, None, 1)
+    refw = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], 1)
+    g = got.cpu().numpy()
+    assert normwise(g, ref) <= TOL_MFMA
+    assert normwise(gotw.cpu().numpy(), refw) <= TOL_MFMA
+    invalid = (ids < 0) | (ids >= E)
+    assert np.all(g[invalid] == 0.0)
+
+
 # ------------------------------------------------------------------------- FFN
 
 @pytest.mark.parametrize("path", [moe.PATH_GEMM, moe.PATH_GEMV])
@@ -87,6 +115,19 @@ def test_ffn_small_shapes(path, E, k, T, n_embd, n_ff, S):
     got = run_ffn(upload_ffn(inp), path=path)
     torch.cuda.synchronize()
     assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= _tol(path)
+
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S,routing", [
+    (4, 2, 300, 256, 320, 1, "uniform"),   # gate/up with scale groups, down with words, ragged N
+    (6, 2, 400, 512, 768, 2, "zipf"),      # skewed segments: empty, tiny and oversized experts
+])
+def test_ffn_tall_tiles(E, k, T, n_embd, n_ff, S, routing):
+    ids = (synth.draw_ids_zipf(23, T, E, k, 1.1) if routing == "zipf"
+           else synth.draw_ids_uniform(23, T, E, k))
+    inp = synth.make_custom_ffn(29, E, k, T, n_embd, n_ff, S, ids=ids)
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_MFMA
 
 
 def test_ffn_invalid_ids_and_shared_width():
