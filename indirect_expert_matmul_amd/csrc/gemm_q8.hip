@@ -394,29 +394,39 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 // weights themselves. When K % 256 == 0 and the scale rows are 16-byte aligned, SG = 4
 // fetches 16 bytes per row (the blocks of four stages) into a two-slot ring instead.
 namespace wide {
-constexpr int BM = 128, W = 8, KS = 64, NS = 3;
-constexpr int BN = 64 * W;                  // weight rows per block
-constexpr int A_BYTES = BM * KS * 2;        // 128-byte rows, 8 chunks
-constexpr int B_BYTES = BN * KS;            // 64-byte rows, 4 chunks
-template <int SG>
-constexpr int stage_bytes() { return A_BYTES + B_BYTES + (SG == 1 ? BN * 4 : 0); }
-constexpr int SGROUP = BN * 16;             // SG = 4: one group of scales, 16 bytes per row
-template <int SG>
-constexpr int lds_bytes() { return NS * stage_bytes<SG>() + (SG == 4 ? 2 * SGROUP : 0); }
-template <int MODE>
-constexpr int out_cols() { return MODE == 1 ? BN / 2 : BN; }
+constexpr int KS = 64, NS = 3;
 __device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
+// Block tile 32*MSUB activation rows x 64*W weight rows, W waves.
+template <int MSUB, int W>
+struct Cfg {
+    static constexpr int BM = 32 * MSUB;
+    static constexpr int BN = 64 * W;                 // weight rows per block
+    static constexpr int A_BYTES = BM * KS * 2;       // 128-byte rows, 8 chunks
+    static constexpr int B_BYTES = BN * KS;           // 64-byte rows, 4 chunks
+    static constexpr int NA = BM / (8 * W);           // activation copies (8 rows) per wave
+    static constexpr int SGROUP = BN * 16;            // SG = 4: one group of scales
+    template <int SG>
+    static constexpr int stage_bytes() { return A_BYTES + B_BYTES + (SG == 1 ? BN * 4 : 0); }
+    template <int SG>
+    static constexpr int lds_bytes() { return NS * stage_bytes<SG>() + (SG == 4 ? 2 * SGROUP : 0); }
+    template <int MODE>
+    static constexpr int out_cols() { return MODE == 1 ? BN / 2 : BN; }
+};
 }  // namespace wide
 
-template <int MODE, int SG>
-__global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
+template <int MODE, int SG, int MSUB, int W>
+__global__ __launch_bounds__(64 * W) void k_gemm_q8w(GemmArgs args) {
     using namespace wide;
-    constexpr int NTW = wide::out_cols<MODE>();
-    constexpr int STAGE = stage_bytes<SG>();
-    // copies per wave per stage: 2 activation + 4 weight (+ 1 scale word if SG = 1);
+    using C = Cfg<MSUB, W>;
+    constexpr int BM = C::BM, A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, NA = C::NA;
+    constexpr int SGROUP = C::SGROUP;
+    constexpr int NTW = C::template out_cols<MODE>();
+    constexpr int STAGE = C::template stage_bytes<SG>();
+    static_assert(NA * 8 * W == BM, "activation rows must split evenly over the waves");
+    // copies per wave per stage: NA activation + 4 weight (+ 1 scale word if SG = 1);
     // with SG = 4 every fourth stage also carries one scale-group copy
-    constexpr int VM_STAGE = SG == 1 ? 7 : 6;
+    constexpr int VM_STAGE = NA + 4 + (SG == 1 ? 1 : 0);
     static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -494,10 +504,10 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
 
     // ---- copy geometry (stage 0)
     const uint8_t* a_base = (const uint8_t*)uniform_ptr(P.A);
-    uint32_t a_off[2];
+    uint32_t a_off[NA];
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int R = (wv * 2 + i) * 8 + (lane >> 3);     // tile row this lane fetches
+    for (int i = 0; i < NA; i++) {
+        const int R = (wv * NA + i) * 8 + (lane >> 3);    // tile row this lane fetches
         const int lc = (lane & 7) ^ swz_wa(R);
         const int j = m0 + min(R, m_len - 1);
         const int64_t src = P.a_rows ? (int64_t)P.a_rows[j]
@@ -531,7 +541,7 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
         const uint32_t st = lds0 + (uint32_t)(slot * STAGE);
         const int k0 = s * KS;
 #pragma unroll
-        for (int i = 0; i < 2; i++) dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * 2 + i) * 1024);
+        for (int i = 0; i < NA; i++) dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
 #pragma unroll
         for (int i = 0; i < 4; i++)
             dma16(((MODE == 1 && (i & 1)) ? qu : qg) + k0, b_off[i], st + A_BYTES + (wv * 4 + i) * 1024);
@@ -542,9 +552,9 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
         }
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[MSUB][2];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < MSUB; i++)
 #pragma unroll
         for (int c = 0; c < 2; c++)
 #pragma unroll
@@ -645,9 +655,9 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
         if (s + 1 < nsteps) step(s + 1, S1{}, mact_c);
     };
     const int mact = (m_len + 31) >> 5;   // block-uniform
-    if (mact >= 4) k_loop(std::integral_constant<int, 4>{});
-    else if (mact == 3) k_loop(std::integral_constant<int, 3>{});
-    else if (mact == 2) k_loop(std::integral_constant<int, 2>{});
+    if (mact >= MSUB) k_loop(std::integral_constant<int, MSUB>{});
+    else if (MSUB > 3 && mact == 3) k_loop(std::integral_constant<int, (MSUB > 3 ? 3 : 1)>{});
+    else if (MSUB > 2 && mact == 2) k_loop(std::integral_constant<int, (MSUB > 2 ? 2 : 1)>{});
     else k_loop(std::integral_constant<int, 1>{});
 
     // ---- output rows into the (now idle) ring: every copy has landed (the last step
@@ -668,7 +678,7 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
             const int n = nt * NTW + wv * 32 + c * 16 + (l32 & 15);
             const bool writer = l32 < 16 && n < N;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < MSUB; i++) {
                 if (i * 32 >= m_len) continue;
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
@@ -688,7 +698,7 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
             const int n = nt * NTW + wv * 64 + c * 32 + l32;
             if (n >= N) continue;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < MSUB; i++) {
                 if (i * 32 >= m_len) continue;
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
@@ -700,24 +710,24 @@ __global__ __launch_bounds__(64 * wide::W) void k_gemm_q8w(GemmArgs args) {
     }
 }
 
-template <int MODE, int SG>
+template <int MODE, int SG, int MSUB, int W>
 hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr int lds = wide::lds_bytes<SG>();
+    constexpr int lds = wide::Cfg<MSUB, W>::template lds_bytes<SG>();
     static_assert(lds <= 160 * 1024, "LDS ring exceeds 160 KB");
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG>,
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_gemm_q8w<MODE, SG><<<grid, 64 * wide::W, lds, st>>>(a);
+    k_gemm_q8w<MODE, SG, MSUB, W><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int MSUB, int W>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
-    constexpr int ntw = wide::out_cols<MODE>();
+    constexpr int ntw = wide::Cfg<MSUB, W>::template out_cols<MODE>();
     int64_t total = 0;
     bool groups = true;   // scale groups of four stages for every problem
     for (int i = 0; i < a.n_prob; i++) {
@@ -729,7 +739,8 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    return groups ? launch_wide_sg<MODE, 4>(g, (int)total, st) : launch_wide_sg<MODE, 1>(g, (int)total, st);
+    return groups ? launch_wide_sg<MODE, 4, MSUB, W>(g, (int)total, st)
+                  : launch_wide_sg<MODE, 1, MSUB, W>(g, (int)total, st);
 }
 
 template <int MSUB, int W, int NS>
@@ -774,16 +785,19 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     GemmArgs a = a0;
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
-    switch (msub) {
-        case 2: return launch_cfg<2, MOE_GEMM_CFG2>(a, st);
-        case 4: {
-#ifndef MOE_GEMM_NO_WIDE
-            bool wide_ok = true;
-            for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
-            if (wide_ok) return a.mode == 1 ? launch_wide<1>(a, st) : launch_wide<0>(a, st);
+    bool wide_ok = true;   // the wide kernels need whole 64-column stages
+    for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
+#ifdef MOE_GEMM_NO_WIDE
+    wide_ok = false;
 #endif
+    switch (msub) {
+        case 2:
+            // 64-row tiles stay on the narrow kernel: on segments of about 50 rows the
+            // wide one (Cfg<2, 4>) gives too few blocks per CU and was measured slower
+            return launch_cfg<2, MOE_GEMM_CFG2>(a, st);
+        case 4:
+            if (wide_ok) return a.mode == 1 ? launch_wide<1, 4, 8>(a, st) : launch_wide<0, 4, 8>(a, st);
             return launch_cfg<4, MOE_GEMM_CFG4>(a, st);
-        }
         default: return hipErrorInvalidValue;
     }
 }
