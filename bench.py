@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE indirect matmul hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config lite|dec1|dec8|skew|v3|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config lite|dec1|dec8|skew|v3|rowids]
 
 A step is one full pass of the hot path -- row ids, gate/up grouped GEMM, down
 grouped GEMM, fixed-order reduce (or the GEMV decode kernels) -- over one batch of
@@ -129,6 +129,64 @@ def measured_traffic(config, stage):
     return float(ent["bytes"])
 
 
+def bench_row_ids(args):
+    """The row-id pass alone at scale: T = 2^21 tokens, k = 8, E = 256, uniform ids
+    (seed 6). Algorithmic bytes = ids read + the two maps written + the bounds."""
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import oracle
+    import synth
+
+    T, k, E = 1 << 21, 8, 256
+    ids_np = synth.draw_ids_uniform(6, T, E, k)
+    dev = torch.device("cuda:0")
+    ids = torch.from_numpy(ids_np).to(dev)
+    ws = torch.empty(moe.lib.moe_row_ids_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_row_ids(ids, E, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        moe.moe_row_ids(ids, E, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 12.0 * T * k + 4.0 * (E + 1)
+    gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        # the oracle's enumeration on a bounded prefix of the same ids
+        n = 1 << 15
+        sub = np.ascontiguousarray(ids_np[:n])
+        t1 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - t1 < 2.0:
+            oracle.row_ids(sub, E, 1)
+            reps += 1
+        sec = (time.perf_counter() - t1) / reps
+        cpu = {"value": (12.0 * n * k + 4.0 * (E + 1)) / sec / 1e9, "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": "first %d of %d tokens, %d pass(es), single thread" % (n, T, reps)}
+    res = {
+        "metric": "MoE row-id pass GB/s (T=2^21, k8, E256), 1 MI355X",
+        "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "row ids: 2^21 tokens x 8 of 256 experts, uniform", "n_tokens": T,
+                   "n_experts": E, "n_used": k, "parallelism": "single GPU"},
+        "entries_per_s": T * k / (ev_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "row_ids"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -136,6 +194,9 @@ def main():
               "(the path would shard by expert with two all-to-all exchanges)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.config == "rowids":
+        bench_row_ids(args)
+        return
     import torch
     import indirect_expert_matmul_amd as moe
     import synth

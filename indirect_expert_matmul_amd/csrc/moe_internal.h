@@ -30,9 +30,10 @@ struct RowIdsArgs {
     // bounds[e], rows of e}; tile_cap[i] entries of room (an upper bound on the count)
     int32_t* tile_tab[2];
     int32_t tile_cap[2];
-    int32_t* chunk_cnt;   // multi-block scratch [n_chunks][E + 1]
+    int32_t* chunk_cnt;   // multi-block scratch [E + 1][n_chunks] (bucket-major)
     int32_t* bucket_tot;  // multi-block scratch [E + 1]
     int64_t n_chunks;
+    int64_t chunk;        // entries per chunk (multi-block)
 };
 size_t row_ids_scratch_bytes(int64_t n, int32_t E);
 hipError_t launch_row_ids(const RowIdsArgs& a, hipStream_t st, int* n_launches);

@@ -25,22 +25,35 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBatchesPerWave = 2;                     // multi-block chunk geometry
-constexpr int64_t kChunk = (int64_t)kWaves * 64 * kBatchesPerWave;
+constexpr int kMaxBatchesPerWave = 16;
+constexpr int64_t kMaxChunk = (int64_t)kThreads * kMaxBatchesPerWave;   // 8192 entries
+
+// Entries per chunk of the multi-block pass: about 2048 chunks, each wave walking 2 to
+// 16 batches of 64 (long enough walks keep the id loads ahead of their use, and few
+// chunks keep the per-chunk counts small).
+int64_t chunk_len(int64_t n) {
+    int64_t bpw = (n + 2048 * (int64_t)kThreads - 1) / (2048 * (int64_t)kThreads);
+    bpw = bpw < 2 ? 2 : (bpw > kMaxBatchesPerWave ? kMaxBatchesPerWave : bpw);
+    return bpw * kThreads;
+}
 
 __device__ __forceinline__ int bucket_of(int32_t e, int32_t E) {
     return (e >= 0 && e < E) ? e : E;
 }
 
-// Lanes (among `active`) whose bucket equals this lane's bucket.
+// Lanes (among `active`) whose bucket equals this lane's bucket: per bit of the bucket
+// id, keep the lanes that agree with this lane on that bit (the bit's ballot, inverted
+// where this lane's bit is 0).
 __device__ __forceinline__ uint64_t match_bucket(int b, uint64_t active, int nbits) {
-    uint64_t m = active;
+    uint32_t lo = (uint32_t)active, hi = (uint32_t)(active >> 32);
     for (int i = 0; i < nbits; i++) {
-        const int bit = (b >> i) & 1;
+        const uint32_t bit = ((uint32_t)b >> i) & 1u;
         const uint64_t bal = __ballot(bit);
-        m &= bit ? bal : ~bal;
+        const uint32_t flip = bit - 1u;   // 0 if the bit is set, all ones if not
+        lo &= (uint32_t)bal ^ flip;
+        hi &= (uint32_t)(bal >> 32) ^ flip;
     }
-    return m;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Number of set bits of m strictly below this lane.
@@ -213,28 +226,29 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
     const int w = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
     __syncthreads();
-    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-    const int64_t per = (int64_t)64 * kBatchesPerWave;
+    const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+    const int64_t per = a.chunk / kWaves;
     const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
     wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
     __syncthreads();
     for (int b = threadIdx.x; b < NB; b += kThreads) {
         int32_t s = 0;
         for (int v = 0; v < kWaves; v++) s += cnt[v * NB + b];
-        a.chunk_cnt[(int64_t)blockIdx.x * NB + b] = s;
+        a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x] = s;
     }
 }
 
 // One block per bucket: exclusive scan of that bucket's per-chunk counts.
 __global__ __launch_bounds__(kThreads) void k_row_ids_scan_chunks(RowIdsArgs a) {
     __shared__ int32_t wsum[kWaves];
-    const int NB = a.E + 1, b = blockIdx.x;
+    const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t nc = a.n_chunks;
     const int64_t per = (nc + kThreads - 1) / kThreads;
     const int64_t beg = min((int64_t)tid * per, nc), end = min(beg + per, nc);
+    int32_t* col = a.chunk_cnt + (int64_t)b * nc;   // this bucket's counts, chunk order
     int32_t s = 0;
-    for (int64_t c = beg; c < end; c++) s += a.chunk_cnt[c * NB + b];
+    for (int64_t c = beg; c < end; c++) s += col[c];
     int32_t x = s;
     for (int d = 1; d < 64; d <<= 1) {
         const int32_t y = __shfl_up(x, d);
@@ -249,8 +263,8 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_scan_chunks(RowIdsArgs a) 
     }
     int32_t run = pre + x - s;
     for (int64_t c = beg; c < end; c++) {
-        const int32_t t = a.chunk_cnt[c * NB + b];
-        a.chunk_cnt[c * NB + b] = run;
+        const int32_t t = col[c];
+        col[c] = run;
         run += t;
     }
     if (tid == 0) a.bucket_tot[b] = total;
@@ -269,36 +283,89 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_scan_buckets(RowIdsArgs a)
     for (int b = threadIdx.x; b < NB; b += kThreads) a.bucket_tot[b] = bstart[b];
 }
 
+// Places one chunk. The chunk's entries are first put in bucket order in LDS (their
+// position inside the chunk: the bucket's start in the chunk + the wave's offset +
+// the running count + the rank in the batch), then every bucket's run is written out
+// contiguously: consecutive output positions come from consecutive threads, instead of
+// each entry storing to a scattered position of its own.
 __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
-    __shared__ int32_t cnt[kWaves * kMaxBuckets];
-    __shared__ int32_t base[kMaxBuckets];
+    __shared__ int32_t wsum[kWaves];
+    // LDS, sized for this launch: per-wave offsets (then running counts) [kWaves][NB],
+    // bucket starts inside the chunk [NB + 1], global start of each bucket's run [NB],
+    // and the chunk in bucket order: entry index [chunk], bucket [chunk]
+    extern __shared__ __attribute__((aligned(16))) int32_t lds[];
     const int NB = a.E + 1, nbits = bucket_bits(NB);
-    const int w = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
+    int32_t* cnt = lds;
+    int32_t* cstart = cnt + kWaves * NB;
+    int32_t* gbase = cstart + NB + 1;
+    int32_t* st_i = gbase + NB;
+    uint16_t* st_bk = (uint16_t*)(st_i + a.chunk);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < kWaves * NB; i += kThreads) cnt[i] = 0;
     __syncthreads();
-    const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-    const int64_t per = (int64_t)64 * kBatchesPerWave;
+    const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+    const int64_t per = a.chunk / kWaves;
     const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
     wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
     __syncthreads();
-    for (int b = threadIdx.x; b < NB; b += kThreads) {
+    for (int b = tid; b < NB; b += kThreads) {
         int32_t run = 0;
         for (int v = 0; v < kWaves; v++) {
             const int32_t t = cnt[v * NB + b];
             cnt[v * NB + b] = run;
             run += t;
         }
-        base[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)blockIdx.x * NB + b];
+        cstart[b] = run;
     }
     __syncthreads();
-    wave_place(a, beg, end, nbits, base, cnt + w * NB);
+    const int32_t chunk_n = block_scan(cstart, NB, wsum);
+    for (int b = tid; b < NB; b += kThreads)
+        gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
+    __syncthreads();
+    int32_t* run_w = cnt + w * NB;
+    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
+        int bk[kPre];
+        load_batches(a.ids, b0, end, a.E, bk);
+#pragma unroll
+        for (int q = 0; q < kPre; q++) {
+            const int64_t bb = b0 + q * 64;
+            if (bb >= end) break;  // uniform
+            const int64_t i = bb + lane;
+            const bool act = bk[q] >= 0;
+            const int b = act ? bk[q] : 0;
+            const uint64_t m = match_bucket(b, __ballot(act), nbits);
+            int32_t prev = 0;
+            if (act) {
+                prev = run_w[b];
+                const int32_t lp = cstart[b] + prev + rank_below(m);   // position in the chunk
+                st_i[lp] = (int32_t)i;  // n < 2^31 is a validated limit
+                st_bk[lp] = (uint16_t)b;
+                if (a.inv) a.inv[i] = gbase[b] + lp - cstart[b];
+            }
+            // every lane has read its counter before the group's leader bumps it
+            __builtin_amdgcn_wave_barrier();
+            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    __syncthreads();
+    for (int32_t p = tid; p < chunk_n; p += kThreads) {
+        const int b = st_bk[p];
+        const int32_t g = gbase[b] + p - cstart[b];
+        const int32_t ii = st_i[p];
+        const int32_t t = ii / a.k;
+        const int32_t s = ii - t * a.k;
+        a.ids_src1[g] = t * a.B + s % a.B;
+        a.ids_dst[g] = ii;
+    }
 }
 
 }  // namespace
 
 size_t row_ids_scratch_bytes(int64_t n, int32_t E) {
     if (n <= kRowIdsOneBlockMax) return 0;
-    const int64_t nc = (n + kChunk - 1) / kChunk;
+    const int64_t ch = chunk_len(n);
+    const int64_t nc = (n + ch - 1) / ch;
     const size_t a = (size_t)nc * (size_t)(E + 1) * sizeof(int32_t);
     return ((a + kAlign - 1) / kAlign) * kAlign + (size_t)(E + 1) * sizeof(int32_t);
 }
@@ -310,11 +377,24 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
         if (n_launches) *n_launches = 1;
         return hipGetLastError();
     }
-    a.n_chunks = (a.n + kChunk - 1) / kChunk;
+    a.chunk = chunk_len(a.n);
+    a.n_chunks = (a.n + a.chunk - 1) / a.chunk;
+    // the place kernel's LDS: counters and starts for NB buckets, then the chunk in
+    // bucket order (an int and a short per entry)
+    const int64_t NB = a.E + 1;
+    const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 6;
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(
+            (const void*)k_row_ids_place, hipFuncAttributeMaxDynamicSharedMemorySize,
+            (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 6));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
     k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
     k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
     k_row_ids_scan_buckets<<<1, kThreads, 0, st>>>(a);
-    k_row_ids_place<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
+    k_row_ids_place<<<(unsigned)a.n_chunks, kThreads, stage, st>>>(a);
     if (n_launches) *n_launches = 4;
     return hipGetLastError();
 }
