@@ -90,14 +90,20 @@ constexpr int kMChunk = MOE_GEMM_MCHUNK;   // M tiles sharing each weight slab i
 //   A  BM rows x 256 B of bf16 activations (128 K columns)
 //   B  32*W weight rows x 128 B of int8
 //   S  32*W rows x 4 aligned 4-byte words, word i holding the fp16 scale of block i
-template <int MSUB, int MODE, int W, int NS>
+// SG = 1: each stage carries its rows' scales (one aligned word per block). SG = 4 (when
+// K % 512 == 0 and the scale rows are 16-byte aligned): the scales of four stages come
+// as 32 bytes per row into a two-slot ring, a quarter of the memory requests; one word
+// per row per stage costs as many requests as the weight rows themselves.
+template <int MSUB, int MODE, int W, int NS, int SG>
 __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int BM = 32 * MSUB;
     constexpr int NTW = out_cols<MODE, W>();     // output columns per block
     constexpr int A_BYTES = BM * 256;
     constexpr int B_BYTES = W * 32 * 128;
-    constexpr int S_BYTES = W * 32 * 16;
+    constexpr int S_BYTES = SG == 1 ? W * 32 * 16 : 0;
     constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    constexpr int SGROUP = W * 32 * 32;          // SG = 4: one group, 32 bytes per row
+    static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     constexpr int NA = BM / (4 * W);             // activation copies (1 KB) per wave per stage
     static_assert(NS == 2, "the step sequence below runs a two-slot ring");
     static_assert(NA * 4 * W == BM, "activation rows must split evenly over the waves");
@@ -231,6 +237,15 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         s_row[t] = wrow(16 * t + (lane >> 2));
         s_word[t] = (uint32_t)(((int64_t)s_row[t] * KB + s_blk) * 2) & ~3u;
     }
+    // SG = 4: lane l fetches 16 bytes (half l&1 of the group's 32) of local row l>>1,
+    // from the row's own tensor (gate and up rows sit in different tensors)
+    const uint8_t* sg_ptr;
+    {
+        const int l = lane >> 1;
+        const uint16_t* dt = (MODE == 1 && l >= 16) ? P.d2 : P.d1;
+        sg_ptr = (const uint8_t*)(dt + ((int64_t)e * N + wrow(l)) * KB) + 16 * (lane & 1);
+    }
+    const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
 
     // Issue the copies of stage s into LDS slot s % NS. The last stage may end inside
     // K: activation chunks past K re-read chunk 0 of the stage, weight chunks past K
@@ -247,10 +262,14 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             for (int i = 0; i < 4; i++)
                 dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i],
                       st + A_BYTES + wv * 4096 + i * 1024);
+            if (SG == 1) {
 #pragma unroll
-            for (int t = 0; t < 2; t++)
-                dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 8 * s,
-                     st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+                for (int t = 0; t < 2; t++)
+                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 8 * s,
+                         st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+            } else if ((s & 3) == 0) {
+                dma16v(sg_ptr + 8 * s, sring + (uint32_t)(((s >> 2) & 1) * SGROUP) + wv * 1024);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < NA; i++) {
@@ -263,12 +282,14 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i] - adj,
                       st + A_BYTES + wv * 4096 + i * 1024);
             }
+            if (SG == 1) {   // (SG = 4 needs K % 512 == 0: no partial stage)
 #pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int blk = min(4 * s + s_blk, KB - 1);
-                const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * 2);
-                dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, byte & ~3u,
-                     st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+                for (int t = 0; t < 2; t++) {
+                    const int blk = min(4 * s + s_blk, KB - 1);
+                    const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * 2);
+                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, byte & ~3u,
+                         st + A_BYTES + B_BYTES + wv * 512 + t * 256);
+                }
             }
         }
     };
@@ -307,8 +328,14 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             // MFMA would make the compiler copy the accumulators out of AGPRs each step
             const i32x4 q0 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
             const i32x4 q1 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
-            const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
-            float d = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+            float d;
+            if constexpr (SG == 1) {
+                const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
+                d = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+            } else {
+                d = half_bits_to_float(*(const uint16_t*)(smem + NS * STAGE + ((s >> 2) & 1) * SGROUP +
+                                                          lrow * 32 + (4 * (s & 3) + 2 * u + h) * 2));
+            }
             if constexpr (CHECK_K) d = (k0 + 64 * u + 32 * h < K) ? d : 0.f;
             bf16x8 bf[4];
             bf[0] = dequant8(q0[0], q0[1], d);
@@ -743,21 +770,24 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
                   : launch_wide_sg<MODE, 1, MSUB, W>(g, (int)total, st);
 }
 
-template <int MSUB, int W, int NS>
-constexpr int stage_lds() { return NS * (32 * MSUB * 256 + W * 32 * 128 + W * 32 * 16); }
+template <int MSUB, int W, int NS, int SG>
+constexpr int stage_lds() {
+    return NS * (32 * MSUB * 256 + W * 32 * 128 + (SG == 1 ? W * 32 * 16 : 0)) +
+           (SG == 4 ? 2 * W * 32 * 32 : 0);
+}
 
-template <int MSUB, int MODE, int W, int NS>
+template <int MSUB, int MODE, int W, int NS, int SG>
 hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr int lds = stage_lds<MSUB, W, NS>();
+    constexpr int lds = stage_lds<MSUB, W, NS, SG>();
     static_assert(lds + 32 * MSUB * 4 <= 160 * 1024, "LDS rings exceed 160 KB");
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8<MSUB, MODE, W, NS>,
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8<MSUB, MODE, W, NS, SG>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_gemm_q8<MSUB, MODE, W, NS><<<grid, 64 * W, lds, st>>>(a);
+    k_gemm_q8<MSUB, MODE, W, NS, SG><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
 }
 
@@ -765,13 +795,19 @@ template <int MSUB, int W, int NS>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
     const int ntw = a.mode == 1 ? out_cols<1, W>() : out_cols<0, W>();
     int64_t total = 0;
-    for (int i = 0; i < a.n_prob; i++)
-        total += ((int64_t)a.p[i].m_tiles_max * ((a.p[i].N + ntw - 1) / ntw) + 7) / 8 * 8;
+    bool groups = true;   // scale groups of four stages for every problem
+    for (int i = 0; i < a.n_prob; i++) {
+        const GemmProblem& p = a.p[i];
+        total += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
+        groups = groups && p.K % 512 == 0 && ((uintptr_t)p.d1 & 15) == 0 &&
+                 (a.mode == 0 || ((uintptr_t)p.d2 & 15) == 0);
+    }
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    if (a.mode == 1) return launch_one<MSUB, 1, W, NS>(g, (int)total, st);
-    return launch_one<MSUB, 0, W, NS>(g, (int)total, st);
+    if (a.mode == 1)
+        return groups ? launch_one<MSUB, 1, W, NS, 4>(g, (int)total, st) : launch_one<MSUB, 1, W, NS, 1>(g, (int)total, st);
+    return groups ? launch_one<MSUB, 0, W, NS, 4>(g, (int)total, st) : launch_one<MSUB, 0, W, NS, 1>(g, (int)total, st);
 }
 
 }  // namespace
