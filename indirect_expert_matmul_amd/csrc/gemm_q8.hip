@@ -322,36 +322,67 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         if (s + 1 < nsteps) issue(s + 1, SLOT ^ 1);
         const uint8_t* st = smem + SLOT * STAGE;
         const int k0 = s * 128;
+        // the stage's weights (both 64-column halves) and scales; both halves always
+        // run (a half past K has zero scales): a conditional MFMA would make the
+        // compiler copy the accumulators between register files each step
+        i32x4 q[2][2];
+        float d[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            // both halves always run (a half past K has zero scales): a conditional
-            // MFMA would make the compiler copy the accumulators out of AGPRs each step
-            const i32x4 q0 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
-            const i32x4 q1 = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
-            float d;
+            q[u][0] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
+            q[u][1] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
             if constexpr (SG == 1) {
                 const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
-                d = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+                d[u] = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
             } else {
-                d = half_bits_to_float(*(const uint16_t*)(smem + NS * STAGE + ((s >> 2) & 1) * SGROUP +
-                                                          lrow * 32 + (4 * (s & 3) + 2 * u + h) * 2));
+                d[u] = half_bits_to_float(*(const uint16_t*)(smem + NS * STAGE + ((s >> 2) & 1) * SGROUP +
+                                                             lrow * 32 + (4 * (s & 3) + 2 * u + h) * 2));
             }
-            if constexpr (CHECK_K) d = (k0 + 64 * u + 32 * h < K) ? d : 0.f;
-            bf16x8 bf[4];
-            bf[0] = dequant8(q0[0], q0[1], d);
-            bf[1] = dequant8(q0[2], q0[3], d);
-            bf[2] = dequant8(q1[0], q1[1], d);
-            bf[3] = dequant8(q1[2], q1[3], d);
+            if constexpr (CHECK_K) d[u] = (k0 + 64 * u + 32 * h < K) ? d[u] : 0.f;
+        }
+        // 8 k sub-steps (half u = t/4, ss = t%4): the MSUB MFMAs of sub-step t run while
+        // sub-step t+1's weights are dequantized and its activation fragments read;
+        // each sub-step is a scheduling region with that interleave pinned (left alone,
+        // the compiler issues all of a stage's dequant work before its MFMAs)
+        auto deq = [&](int t) -> bf16x8 {
+            const i32x4& v = q[t >> 2][(t & 3) >> 1];
+            return (t & 1) ? dequant8(v[2], v[3], d[t >> 2]) : dequant8(v[0], v[1], d[t >> 2]);
+        };
+        auto afrag = [&](int i, int t) -> bf16x8 {
+            const int r = i * 32 + l32;
+            const int chunk = (8 * (t >> 2) + 4 * h + (t & 3)) ^ swz_a(r);
+            return *(const bf16x8*)(st + r * 256 + (chunk << 4));
+        };
+        bf16x8 bf[2], af[2][MSUB];
+        bf[0] = deq(0);
 #pragma unroll
-            for (int i = 0; i < MSUB; i++) {
-                const int r = i * 32 + l32;
+        for (int i = 0; i < MSUB; i++) af[0][i] = afrag(i, 0);
+#ifndef MOE_GEMM_NO_SCHED
+        __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
-                for (int ss = 0; ss < 4; ss++) {
-                    const int chunk = (8 * u + 4 * h + ss) ^ swz_a(r);
-                    const bf16x8 af = *(const bf16x8*)(st + r * 256 + (chunk << 4));
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[ss], acc[i], 0, 0, 0);
+        for (int t = 0; t < 8; t++) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 7) {
+                bf[nxt] = deq(t + 1);
+#pragma unroll
+                for (int i = 0; i < MSUB; i++) af[nxt][i] = afrag(i, t + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < MSUB; i++)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur], acc[i], 0, 0, 0);
+#ifndef MOE_GEMM_NO_SCHED
+            if (t < 7) {
+                constexpr int VPM = (20 + MSUB - 1) / MSUB;   // dequant VALU per MFMA
+#pragma unroll
+                for (int m = 0; m < MSUB; m++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
     using S0 = std::integral_constant<int, 0>;
