@@ -44,6 +44,7 @@ def test_tiny_fp32_mul_mat_id():
     (16, 2, 50, 256, 300, False, False), # several N tiles plus a ragged one
     (4, 4, 60, 128, 64, False, True),    # k = E, several M tiles per expert
     (5, 2, 7, 96, 45, False, False),     # odd N and K/32: rows of scales start at 2 mod 4
+    (8, 2, 64, 512, 200, False, True),   # 64-row tiles with scale groups (K % 512 == 0)
 ])
 def test_q8_mul_mat_id(path, E, k, T, K, N, B_is_k, bad):
     if path == moe.PATH_GEMV and T * k > 256:
@@ -106,6 +107,7 @@ def test_q8_mul_mat_id_tall_tiles(E, k, T, K, N, bad):
     (32, 4, 8, 256, 160, 1),
     (4, 6, 10, 64, 32, 1),       # n_used > n_experts: duplicate experts inside tokens
     (16, 1, 1, 320, 192, 2),     # a single token
+    (8, 2, 24, 512, 160, 1),     # gate/up with scale groups on 64-row tiles, down without
 ])
 def test_ffn_small_shapes(path, E, k, T, n_embd, n_ff, S):
     if path == moe.PATH_GEMV and T * k > 256:
