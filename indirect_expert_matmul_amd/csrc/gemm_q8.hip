@@ -452,11 +452,11 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 // weights themselves. When K % 256 == 0 and the scale rows are 16-byte aligned, SG = 4
 // fetches 16 bytes per row (the blocks of four stages) into a two-slot ring instead.
 namespace wide {
-constexpr int KS = 64, NS = 3;
+constexpr int KS = 64;
 __device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
-// Block tile 32*MSUB activation rows x 64*W weight rows, W waves.
-template <int MSUB, int W>
+// Block tile 32*MSUB activation rows x 64*W weight rows, W waves, NS ring slots.
+template <int MSUB, int W, int NS>
 struct Cfg {
     static constexpr int BM = 32 * MSUB;
     static constexpr int BN = 64 * W;                 // weight rows per block
@@ -473,10 +473,11 @@ struct Cfg {
 };
 }  // namespace wide
 
-template <int MODE, int SG, int MSUB, int W>
-__global__ __launch_bounds__(64 * W) void k_gemm_q8w(GemmArgs args) {
+template <int MODE, int SG, int MSUB, int W, int NS>
+__global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs args) {
     using namespace wide;
-    using C = Cfg<MSUB, W>;
+    using C = Cfg<MSUB, W, NS>;
+    static_assert(NS == 2 || NS == 3, "two- or three-slot ring");
     constexpr int BM = C::BM, A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, NA = C::NA;
     constexpr int SGROUP = C::SGROUP;
     constexpr int NTW = C::template out_cols<MODE>();
@@ -625,10 +626,12 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8w(GemmArgs args) {
     auto step = [&](int s, auto slot_c, auto mact_c) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slot_c)::value;
         constexpr int MACT = decltype(mact_c)::value;
-        if (s + 1 >= nsteps) wait_stage_and_barrier<0>();
+        // copies still allowed in flight: those of stage s+1 with three slots (sent one
+        // step ago), none with two (stage s+1 is sent after this wait)
+        if (NS == 2 || s + 1 >= nsteps) wait_stage_and_barrier<0>();
         else if (SG == 4 && ((s + 1) & 3) == 0) wait_stage_and_barrier<VM_STAGE + 1>();
         else wait_stage_and_barrier<VM_STAGE>();
-        if (s + 2 < nsteps) issue(s + 2, (SLOT + 2) % NS);
+        if (s + NS - 1 < nsteps) issue(s + NS - 1, (SLOT + NS - 1) % NS);
         const uint8_t* st = smem + SLOT * STAGE;
         const uint8_t* sg = SG == 1 ? st + A_BYTES + B_BYTES
                                     : smem + NS * STAGE + ((s >> 2) & 1) * SGROUP + (s & 3) * 4;
@@ -702,15 +705,23 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8w(GemmArgs args) {
 
     auto k_loop = [&](auto mact_c) __attribute__((always_inline)) {
         issue(0, 0);
-        if (nsteps > 1) issue(1, 1);
         int s = 0;
-        for (; s + 3 <= nsteps; s += 3) {
-            step(s, S0{}, mact_c);
-            step(s + 1, S1{}, mact_c);
-            step(s + 2, S2{}, mact_c);
+        if constexpr (NS == 3) {
+            if (nsteps > 1) issue(1, 1);
+            for (; s + 3 <= nsteps; s += 3) {
+                step(s, S0{}, mact_c);
+                step(s + 1, S1{}, mact_c);
+                step(s + 2, S2{}, mact_c);
+            }
+            if (s < nsteps) step(s, S0{}, mact_c);
+            if (s + 1 < nsteps) step(s + 1, S1{}, mact_c);
+        } else {
+            for (; s + 2 <= nsteps; s += 2) {
+                step(s, S0{}, mact_c);
+                step(s + 1, S1{}, mact_c);
+            }
+            if (s < nsteps) step(s, S0{}, mact_c);
         }
-        if (s < nsteps) step(s, S0{}, mact_c);
-        if (s + 1 < nsteps) step(s + 1, S1{}, mact_c);
     };
     const int mact = (m_len + 31) >> 5;   // block-uniform
     if (mact >= MSUB) k_loop(std::integral_constant<int, MSUB>{});
@@ -768,24 +779,24 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8w(GemmArgs args) {
     }
 }
 
-template <int MODE, int SG, int MSUB, int W>
+template <int MODE, int SG, int MSUB, int W, int NS>
 hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr int lds = wide::Cfg<MSUB, W>::template lds_bytes<SG>();
+    constexpr int lds = wide::Cfg<MSUB, W, NS>::template lds_bytes<SG>();
     static_assert(lds <= 160 * 1024, "LDS ring exceeds 160 KB");
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W>,
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W, NS>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_gemm_q8w<MODE, SG, MSUB, W><<<grid, 64 * W, lds, st>>>(a);
+    k_gemm_q8w<MODE, SG, MSUB, W, NS><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
 }
 
-template <int MODE, int MSUB, int W>
+template <int MODE, int MSUB, int W, int NS>
 hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
-    constexpr int ntw = wide::Cfg<MSUB, W>::template out_cols<MODE>();
+    constexpr int ntw = wide::Cfg<MSUB, W, NS>::template out_cols<MODE>();
     int64_t total = 0;
     bool groups = true;   // scale groups of four stages for every problem
     for (int i = 0; i < a.n_prob; i++) {
@@ -797,8 +808,8 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    return groups ? launch_wide_sg<MODE, 4, MSUB, W>(g, (int)total, st)
-                  : launch_wide_sg<MODE, 1, MSUB, W>(g, (int)total, st);
+    return groups ? launch_wide_sg<MODE, 4, MSUB, W, NS>(g, (int)total, st)
+                  : launch_wide_sg<MODE, 1, MSUB, W, NS>(g, (int)total, st);
 }
 
 template <int MSUB, int W, int NS, int SG>
@@ -863,7 +874,11 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
             // wide one (Cfg<2, 4>) gives too few blocks per CU and was measured slower
             return launch_cfg<2, MOE_GEMM_CFG2>(a, st);
         case 4:
-            if (wide_ok) return a.mode == 1 ? launch_wide<1, 4, 8>(a, st) : launch_wide<0, 4, 8>(a, st);
+#ifndef MOE_GEMM_WIDE_CFG
+#define MOE_GEMM_WIDE_CFG 4, 2   // waves, ring slots of the 128-row wide kernel (2 blocks per CU)
+#endif
+            if (wide_ok) return a.mode == 1 ? launch_wide<1, 4, MOE_GEMM_WIDE_CFG>(a, st)
+                                            : launch_wide<0, 4, MOE_GEMM_WIDE_CFG>(a, st);
             return launch_cfg<4, MOE_GEMM_CFG4>(a, st);
         default: return hipErrorInvalidValue;
     }
