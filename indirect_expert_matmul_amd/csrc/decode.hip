@@ -277,71 +277,74 @@ __global__ __launch_bounds__(kThreads) void k_decode(DecArgs a) {
 }
 
 // ---------------------------------------------------------------- wave-level fast path
-// For n_tokens * n_used <= 64 and K <= 4096: every wave is an independent unit (no
-// LDS, no barriers). Wave g of the grid owns R consecutive rows (row pairs in gate/up
-// mode) of one expert. It loads the ids table (one entry per lane), finds the distinct
-// experts present with a wave OR of per-word bitmaps, takes the d-th, and collects
-// that expert's slots as a lane mask. It then loads the activation rows of up to P of
-// those slots into registers once (lane l holds k = 1024i + 16l .. +15 of each), and
-// streams its R weight rows against them: per row all NIT 16-byte pieces and scales
-// are loaded back to back, converted exactly to fp32 and accumulated per slot in fp32;
-// lanes are summed with DPP and lane 63 writes. The activations are read once per R
-// rows instead of once per row.
+// For n_tokens * n_used <= 64 and K <= 4096 the work is cut into units: one distinct
+// routed expert with the slots routed to it, or one shared expert with every token,
+// over a chunk of rows. A wave loads the ids table (one entry per lane), finds the
+// distinct experts present with a wave OR of per-word bitmaps, and collects an
+// expert's slots as a lane mask. It loads the activation rows of up to P of those
+// slots once (lane l holds k = 1024i + 16l .. +15 of each, exact fp32) and streams the
+// unit's weight rows against them: per row all NIT 16-byte pieces and scales, converted
+// exactly to fp32 and accumulated per slot in fp32; lanes are summed with DPP and lane
+// 63 hands each result to the caller. The activations are read once per chunk of rows
+// instead of once per row.
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
     for (int i = 0; i < n; i++) m &= m - 1;
     return __ffsll((unsigned long long)m) - 1;
 }
 
-// Streaming GEMV, one wave per (expert, chunk of R rows), for K <= 4096. The wave
-// copies its weight rows (a gate/up pair in gate/up mode) straight from global memory
-// into a ring of NR row slots in its own part of LDS, keeping NR-1 rows in flight
-// while it multiplies the oldest: the bytes in flight cost no registers, so the
-// occupancy is set by LDS, not by the row buffers. A wave only reads slots its own
-// copies wrote, so no barrier is needed; its vmcnt says when a row has landed.
-//
-// Slot layout per matrix: NIT KB of int8 (piece i at 1024*i, lane l's 16 bytes at
-// 16*l, the row's byte k at offset k) and 256 bytes for the row's fp16 scales (the
-// aligned dwords holding them; the row's first scale sits at byte (row offset & 3)).
-// Register-staged GEMV, one wave per (expert, chunk of R rows): the wave streams its
-// rows two at a time through registers (the next row's loads in flight while one
-// computes). With one activation row per pass it needs few registers and keeps two
-// or more waves per SIMD, which beats staging through LDS for single-token decode.
-template <int MODE, int P, bool XBF16, int NIT>
-__global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
-    constexpr int M = MODE == 1 ? 2 : 1;
+// This lane's entry of the ids table; lanes past n_tokens * n_used and ids outside
+// [0, E) hold -1.
+__device__ __forceinline__ int lane_expert(const DecArgs& a, int lane) {
+    const int v = lane < a.T * a.k ? a.ids[lane] : -1;
+    return (v >= 0 && v < a.E) ? v : -1;
+}
+
+// Experts w0 .. w0+63 present in the ids table, as a bitmap (the same on every lane).
+__device__ __forceinline__ uint64_t present_word(int v, int w0) {
+    const int rel = v - w0;
+    const bool in = v >= 0 && rel >= 0 && rel < 64;
+    const uint32_t lo = wave_or_u32(in && rel < 32 ? 1u << rel : 0u);
+    const uint32_t hi = wave_or_u32(in && rel >= 32 ? 1u << (rel - 32) : 0u);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// The d-th distinct expert present, in ascending order; -1 if fewer are present.
+__device__ __forceinline__ int nth_expert(int v, int E, int d) {
+    int e = -1, seen = 0;
+    for (int w0 = 0; w0 < E && e < 0; w0 += 64) {
+        const uint64_t present = present_word(v, w0);
+        const int c = __popcll(present);
+        if (d < seen + c) e = w0 + nth_set_bit(present, d - seen);
+        seen += c;
+    }
+    return e;
+}
+
+// Number of distinct experts present.
+__device__ __forceinline__ int count_experts(int v, int E) {
+    int seen = 0;
+    for (int w0 = 0; w0 < E; w0 += 64) seen += __popcll(present_word(v, w0));
+    return seen;
+}
+
+// The unit of global wave gw when every wave owns one unit of R rows: routed units
+// first (distinct expert d = gw / chunks), then the shared ones. Returns false for waves
+// past the last unit.
+__device__ __forceinline__ bool wave_unit(const DecArgs& a, int gw, int R, bool& routed, int& e,
+                                          uint64_t& smask, int& cnt, int& n_lo, int& n_hi) {
     const int lane = threadIdx.x & 63;
-    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
-    const int R = a.rows_per_block;  // rows per wave
     const int nch_r = (a.rw.N + R - 1) / R;
     const int nw_r = a.d_max * nch_r;
     const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0;
-    if (gw >= nw_r + nw_s) return;
-    const bool routed = gw < nw_r;
-    const DecWeights& W = routed ? a.rw : a.sw;
-    const int N = W.N, K = W.K;
-    int e, chunk, cnt;
-    uint64_t smask = 0;  // routed: lanes (entries t*k+s) of this expert
+    if (gw >= nw_r + nw_s) return false;
+    routed = gw < nw_r;
+    int chunk;
     if (routed) {
         const int d = gw / nch_r;
         chunk = gw - d * nch_r;
-        const int n = a.T * a.k;
-        int v = lane < n ? a.ids[lane] : -1;
-        if (v >= a.E) v = -1;
-        // distinct experts present: a 64-expert bitmap word at a time (wave OR), the
-        // d-th set bit over the words in ascending order is this wave's expert
-        e = -1;
-        int seen = 0;
-        for (int w0 = 0; w0 < a.E && e < 0; w0 += 64) {
-            const int rel = v - w0;
-            const bool in = v >= 0 && rel >= 0 && rel < 64;
-            const uint32_t lo = wave_or_u32(in && rel < 32 ? 1u << rel : 0u);
-            const uint32_t hi = wave_or_u32(in && rel >= 32 ? 1u << (rel - 32) : 0u);
-            const uint64_t present = ((uint64_t)hi << 32) | lo;
-            const int c = __popcll(present);
-            if (d < seen + c) e = w0 + nth_set_bit(present, d - seen);
-            seen += c;
-        }
-        if (e < 0) return;  // fewer distinct experts than the grid allows for
+        const int v = lane_expert(a, lane);
+        e = nth_expert(v, a.E, d);
+        if (e < 0) return false;  // fewer distinct experts than the grid allows for
         smask = __ballot(v == e);
         cnt = __popcll(smask);
     } else {
@@ -349,10 +352,28 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
         const int b = gw - nw_r;
         e = b / nch_s;
         chunk = b - e * nch_s;
+        smask = 0;
         cnt = a.T;
     }
-    const int n_lo = chunk * R;
-    const int n_hi = min(n_lo + R, N);
+    const int N = routed ? a.rw.N : a.sw.N;
+    n_lo = chunk * R;
+    n_hi = min(n_lo + R, N);
+    return true;
+}
+
+// Register-staged unit: rows [n_lo, n_hi) of routed expert e (slots in smask, cnt of
+// them) or of shared expert e (all tokens), streamed two at a time through registers (the
+// next row's loads in flight while one computes). With one activation row per pass it
+// needs few registers and keeps two or more waves per SIMD, which beats staging through
+// LDS for single-token decode. emit(idx, n, res) runs on lane 63; idx is the slot t*k+s
+// (routed) or the token (shared).
+template <int MODE, int P, bool XBF16, int NIT, class Emit>
+__device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, uint64_t smask, int cnt,
+                                          int n_lo, int n_hi, Emit&& emit) {
+    constexpr int M = MODE == 1 ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const DecWeights& W = routed ? a.rw : a.sw;
+    const int N = W.N, K = W.K;
     const int64_t KB = K >> 5;
     const void* src = routed ? a.act : a.sact;
     auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
@@ -458,10 +479,7 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
                     const float u = wave_sum_lane63(acc[M - 1][p]);
                     res = g / (1.0f + __expf(-g)) * u;
                 }
-                if (lane == 63) {
-                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + n] = res;
-                    else a.sout[((int64_t)e * a.T + p0 + p) * N + n] = res;
-                }
+                if (lane == 63) emit(slot_of(p0 + p), n, res);
             }
         };
         // rows in pairs, the next row's loads in flight while one computes; loads past
@@ -476,6 +494,29 @@ __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
             compute_row(n + 1, wb);
         }
     }
+}
+
+// Per-slot results: routed rows [n_tokens * n_used][N], shared rows [n_mat][T][N].
+struct EmitGlobal {
+    const DecArgs& a;
+    bool routed;
+    int e, N;
+    __device__ void operator()(int idx, int n, float res) const {
+        if (routed) a.out[(int64_t)idx * N + n] = res;
+        else a.sout[((int64_t)e * a.T + idx) * N + n] = res;
+    }
+};
+
+// One wave per unit, register-staged rows.
+template <int MODE, int P, bool XBF16, int NIT>
+__global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
+    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
+    bool routed;
+    int e, cnt, n_lo, n_hi;
+    uint64_t smask;
+    if (!wave_unit(a, gw, a.rows_per_block, routed, e, smask, cnt, n_lo, n_hi)) return;
+    unit_regs<MODE, P, XBF16, NIT>(a, routed, e, smask, cnt, n_lo, n_hi,
+                                   EmitGlobal{a, routed, e, routed ? a.rw.N : a.sw.N});
 }
 
 // ring slots per wave (gate/up pairs, single rows) and blocks per CU the registers
@@ -506,63 +547,32 @@ struct StreamSlot {
     static constexpr int MAT = NIT * 1024 + 256;
     static constexpr int BYTES = (MODE == 1 ? 2 : 1) * MAT;
     static constexpr int NR_CFG = MODE == 1 ? MOE_DEC_NR1 : MOE_DEC_NR0;
-    static constexpr int NR_FIT = 160 * 1024 / (4 * BYTES);
+    static constexpr int NR_FIT = 150 * 1024 / (4 * BYTES);
     static constexpr int NR = NR_CFG < NR_FIT ? NR_CFG : NR_FIT;   // ring slots per wave
     static constexpr int LDS = 4 * NR * BYTES;       // 4 waves per block
 };
 
-template <int MODE, int P, bool XBF16, int NIT>
-__global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) {
+// Streaming unit (same work as unit_regs): the wave copies its weight rows (a gate/up
+// pair in gate/up mode) straight from global memory into a ring of NR row slots in its
+// own part of LDS, keeping NR-1 rows in flight while it multiplies the oldest: the bytes
+// in flight cost no registers, so the occupancy is set by LDS, not by the row buffers. A
+// wave only reads slots its own copies wrote, so no barrier is needed; its vmcnt says
+// when a row has landed. Every copy has landed when the unit returns.
+//
+// Slot layout per matrix: NIT KB of int8 (piece i at 1024*i, lane l's 16 bytes at
+// 16*l, the row's byte k at offset k) and 256 bytes for the row's fp16 scales (the
+// aligned dwords holding them; the row's first scale sits at byte (row offset & 3)).
+template <int MODE, int P, bool XBF16, int NIT, class Emit>
+__device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e, uint64_t smask,
+                                            int cnt, int n_lo, int n_hi, uint8_t* ring, Emit&& emit) {
     constexpr int M = MODE == 1 ? 2 : 1;
     using G = StreamSlot<MODE, NIT>;
     constexpr int MAT = G::MAT, SLOT = G::BYTES, NR = G::NR;
     constexpr int D = M * (NIT + 1);   // copies per row (pair)
     static_assert((NR - 1) * D <= 63, "vmcnt counts to 63");
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
-    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
-    const int R = a.rows_per_block;  // rows per wave
-    const int nch_r = (a.rw.N + R - 1) / R;
-    const int nw_r = a.d_max * nch_r;
-    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0;
-    if (gw >= nw_r + nw_s) return;
-    const bool routed = gw < nw_r;
     const DecWeights& W = routed ? a.rw : a.sw;
     const int N = W.N, K = W.K;
-    int e, chunk, cnt;
-    uint64_t smask = 0;  // routed: lanes (entries t*k+s) of this expert
-    if (routed) {
-        const int d = gw / nch_r;
-        chunk = gw - d * nch_r;
-        const int n = a.T * a.k;
-        int v = lane < n ? a.ids[lane] : -1;
-        if (v >= a.E) v = -1;
-        // distinct experts present: a 64-expert bitmap word at a time (wave OR), the
-        // d-th set bit over the words in ascending order is this wave's expert
-        e = -1;
-        int seen = 0;
-        for (int w0 = 0; w0 < a.E && e < 0; w0 += 64) {
-            const int rel = v - w0;
-            const bool in = v >= 0 && rel >= 0 && rel < 64;
-            const uint32_t lo = wave_or_u32(in && rel < 32 ? 1u << rel : 0u);
-            const uint32_t hi = wave_or_u32(in && rel >= 32 ? 1u << (rel - 32) : 0u);
-            const uint64_t present = ((uint64_t)hi << 32) | lo;
-            const int c = __popcll(present);
-            if (d < seen + c) e = w0 + nth_set_bit(present, d - seen);
-            seen += c;
-        }
-        if (e < 0) return;  // fewer distinct experts than the grid allows for
-        smask = __ballot(v == e);
-        cnt = __popcll(smask);
-    } else {
-        const int nch_s = (a.sw.N + R - 1) / R;
-        const int b = gw - nw_r;
-        e = b / nch_s;
-        chunk = b - e * nch_s;
-        cnt = a.T;
-    }
-    const int n_lo = chunk * R;
-    const int n_hi = min(n_lo + R, N);
     const int nrows = n_hi - n_lo;
     const int KB = K >> 5;
     const void* src = routed ? a.act : a.sact;
@@ -591,7 +601,6 @@ __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) 
     const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * K : q1;
     const uint8_t* d1 = (const uint8_t*)(W.d1 + (int64_t)e * N * KB);
     const uint8_t* d2 = MODE == 1 ? (const uint8_t*)(W.d2 + (int64_t)e * N * KB) : d1;
-    uint8_t* ring = smem + (threadIdx.x >> 6) * (NR * SLOT);
     const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
 
     // copies of row n into slot j: per matrix NIT 16-byte pieces and one word per lane
@@ -678,10 +687,7 @@ __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) 
                     const float u = wave_sum_lane63(acc[M - 1][p]);
                     res = g / (1.0f + __expf(-g)) * u;
                 }
-                if (lane == 63) {
-                    if (routed) a.out[(int64_t)slot_of(p0 + p) * N + n] = res;
-                    else a.sout[((int64_t)e * a.T + p0 + p) * N + n] = res;
-                }
+                if (lane == 63) emit(slot_of(p0 + p), n, res);
             }
         };
         // ring: rows 0 .. NR-2 in flight before the first multiply; row j+NR-1 goes
@@ -692,6 +698,80 @@ __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) 
             wait_row(min(NR - 1, nrows - 1 - j));
             compute_row(n_lo + j, j % NR);
         }
+    }
+}
+
+// One wave per unit, rows streamed through a per-wave LDS ring.
+template <int MODE, int P, bool XBF16, int NIT>
+__global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) {
+    using G = StreamSlot<MODE, NIT>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
+    bool routed;
+    int e, cnt, n_lo, n_hi;
+    uint64_t smask;
+    if (!wave_unit(a, gw, a.rows_per_block, routed, e, smask, cnt, n_lo, n_hi)) return;
+    uint8_t* ring = smem + (threadIdx.x >> 6) * (G::NR * G::BYTES);
+    unit_stream<MODE, P, XBF16, NIT>(a, routed, e, smask, cnt, n_lo, n_hi, ring,
+                                     EmitGlobal{a, routed, e, routed ? a.rw.N : a.sw.N});
+}
+
+// ---------------------------------------------------------------- down with the reduce
+// D2 with the weighted reduction fused in (down mode, n_tokens * n_used <= 64): a block
+// owns a chunk of R output rows for every unit, the distinct routed experts and the
+// shared experts, which its 4 waves take in turn (unit u on wave u mod 4). Each result
+// (slot or shared token, row) goes to LDS; after one barrier, one thread per (token, row)
+// sums the token's slots in ascending slot order with their routing weights, then the
+// shared experts in index order, in fp32, and writes the output row once. The order and
+// the operations are those of the standalone reduce, so both give identical bits.
+constexpr int kFuseRows = 16;    // R, at most
+constexpr int kFuseSlots = 64;   // routed slots, and shared (expert, token) pairs, at most
+
+template <int P, bool XBF16, int NIT, bool STREAM>
+__global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_reduce(DecArgs a) {
+    using G = StreamSlot<0, NIT>;
+    __shared__ float s_part[kFuseSlots * kFuseRows];   // routed slot s, row r at s*kFuseRows + r
+    __shared__ float s_shp[kFuseSlots * kFuseRows];    // shared j, token t at (j*T + t)*kFuseRows + r
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int R = a.rows_per_block;
+    const int N = a.rw.N;
+    const int n_lo = (int)blockIdx.x * R, n_hi = min(n_lo + R, N);
+    const int v = lane_expert(a, lane);
+    const int D = count_experts(v, a.E);
+    const int S = a.sw.n_mat;
+    uint8_t* ring = smem + wv * (G::NR * G::BYTES);
+    for (int u = wv; u < D + S; u += 4) {
+        if (u < D) {
+            const int e = nth_expert(v, a.E, u);
+            const uint64_t sm = __ballot(v == e);
+            auto emit = [&](int slot, int n, float res) { s_part[slot * kFuseRows + (n - n_lo)] = res; };
+            if constexpr (STREAM)
+                unit_stream<0, P, XBF16, NIT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, ring, emit);
+            else
+                unit_regs<0, P, XBF16, NIT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, emit);
+        } else {
+            const int j = u - D;
+            auto emit = [&](int t, int n, float res) { s_shp[(j * a.T + t) * kFuseRows + (n - n_lo)] = res; };
+            if constexpr (STREAM)
+                unit_stream<0, P, XBF16, NIT>(a, false, j, 0, a.T, n_lo, n_hi, ring, emit);
+            else
+                unit_regs<0, P, XBF16, NIT>(a, false, j, 0, a.T, n_lo, n_hi, emit);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < a.T * R; i += 256) {
+        const int t = i / R, r = i - t * R, n = n_lo + r;
+        if (n >= N) continue;
+        float acc = 0.f;
+        for (int s = 0; s < a.k; s++) {
+            const int slot = t * a.k + s;
+            const int32_t e = a.ids[slot];
+            if (e >= 0 && e < a.E)
+                acc = fmaf(a.route_w ? a.route_w[slot] : 1.0f, s_part[slot * kFuseRows + r], acc);
+        }
+        for (int j = 0; j < S; j++) acc += s_shp[(j * a.T + t) * kFuseRows + r];
+        a.out_tok[(int64_t)t * N + n] = acc;
     }
 }
 
@@ -724,18 +804,33 @@ int rows_per_wave(const DecArgs& a, int waves) {
     return (int)(r < 4 ? 4 : (r > 32 ? 32 : r));
 }
 
+// Units per wave (routed experts plus shared experts over 4 waves) up to which the fused
+// down + reduce kernel is used; beyond it each wave would restart its row stream too often
+// and the per-unit kernels with the standalone reduce are faster.
+#ifndef MOE_DEC_FUSE_UPW
+#define MOE_DEC_FUSE_UPW 2
+#endif
+// Blocks the fused kernel aims at (R = N / blocks rows each, 1 <= R <= kFuseRows).
+#ifndef MOE_DEC_FUSE_BLOCKS
+#define MOE_DEC_FUSE_BLOCKS 512
+#endif
+
+template <bool STREAM>
+hipError_t set_stream_lds(const void* kern, int lds, bool& done) {
+    if (!STREAM || done) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
 template <int MODE, int P, bool XBF16, int NIT>
 hipError_t launch_stream(DecArgs a, hipStream_t st) {
     constexpr int lds = StreamSlot<MODE, NIT>::LDS;
-    static_assert(lds <= 160 * 1024, "ring exceeds LDS");
+    static_assert(lds <= 150 * 1024, "ring exceeds LDS");
     static int cache = 0;
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_decode_stream<MODE, P, XBF16, NIT>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    if (hipError_t e = set_stream_lds<true>((const void*)k_decode_stream<MODE, P, XBF16, NIT>, lds, attr_set))
+        return e;
     a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_stream<MODE, P, XBF16, NIT>, lds, cache));
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
@@ -758,36 +853,65 @@ hipError_t launch_regs(DecArgs a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <bool XBF16, int NIT, bool STREAM>
+hipError_t launch_down_reduce(DecArgs a, hipStream_t st) {
+    constexpr int lds = STREAM ? StreamSlot<0, NIT>::LDS : 0;
+    constexpr int P = STREAM ? 2 : 1;
+    static bool attr_set = false;
+    if (hipError_t e = set_stream_lds<STREAM>((const void*)k_decode_down_reduce<P, XBF16, NIT, STREAM>,
+                                              lds, attr_set))
+        return e;
+    const int N = a.rw.N;
+    int R = (N + MOE_DEC_FUSE_BLOCKS - 1) / MOE_DEC_FUSE_BLOCKS;
+    R = R < 1 ? 1 : (R > kFuseRows ? kFuseRows : R);
+    a.rows_per_block = R;
+    const int grid = (N + R - 1) / R;
+    if (grid <= 0) return hipSuccess;
+    k_decode_down_reduce<P, XBF16, NIT, STREAM><<<grid, 256, lds, st>>>(a);
+    return hipGetLastError();
+}
+
 // One activation row per pass: register staging. Two per pass: the two rows' fp32
 // activations take too many registers to also hold rows in flight, so the rows stream
 // through LDS.
 template <int MODE, bool XBF16, int NIT>
-hipError_t launch_wave_nit(const DecArgs& a, int slots_max, hipStream_t st) {
+hipError_t launch_wave_nit(const DecArgs& a, int slots_max, bool fuse, hipStream_t st) {
+    if constexpr (MODE == 0) {
+        if (fuse) return slots_max <= 1 ? launch_down_reduce<XBF16, NIT, false>(a, st)
+                                        : launch_down_reduce<XBF16, NIT, true>(a, st);
+    }
     return slots_max <= 1 ? launch_regs<MODE, XBF16, NIT>(a, st) : launch_stream<MODE, 2, XBF16, NIT>(a, st);
 }
 
 template <int MODE, bool XBF16>
-hipError_t launch_wave(const DecArgs& a, int slots_max, hipStream_t st) {
+hipError_t launch_wave(const DecArgs& a, int slots_max, bool fuse, hipStream_t st) {
     const int kmax = max(a.rw.K, a.sw.n_mat > 0 ? a.sw.K : 0);
-    if (kmax <= 1024) return launch_wave_nit<MODE, XBF16, 1>(a, slots_max, st);
-    if (kmax <= 2048) return launch_wave_nit<MODE, XBF16, 2>(a, slots_max, st);
-    if (kmax <= 3072) return launch_wave_nit<MODE, XBF16, 3>(a, slots_max, st);
-    return launch_wave_nit<MODE, XBF16, 4>(a, slots_max, st);
+    if (kmax <= 1024) return launch_wave_nit<MODE, XBF16, 1>(a, slots_max, fuse, st);
+    if (kmax <= 2048) return launch_wave_nit<MODE, XBF16, 2>(a, slots_max, fuse, st);
+    if (kmax <= 3072) return launch_wave_nit<MODE, XBF16, 3>(a, slots_max, fuse, st);
+    return launch_wave_nit<MODE, XBF16, 4>(a, slots_max, fuse, st);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecArgs& a, hipStream_t st) {
+hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced) {
+    if (reduced) *reduced = false;
     if ((int64_t)a.T * a.k <= 64 && a.rw.K <= 4096 && (a.sw.n_mat == 0 || a.sw.K <= 4096)) {
         // activation rows per pass: an expert usually serves each token at most once,
         // so up to n_tokens rows; more (repeated ids) take further passes. Two rows per
         // pass keep the register budget at two or more waves per SIMD.
         const int slots = a.T;
         const bool same_type = a.sw.n_mat == 0 || a.sact_type == a.act_type;
+        const int S = a.sw.n_mat > 0 ? a.sw.n_mat : 0;
+        const bool fuse = a.mode == 0 && a.out_tok != nullptr && same_type &&
+                          (S == 0 || a.sw.N == a.rw.N) && (int64_t)S * a.T <= kFuseSlots &&
+                          a.d_max + S <= 4 * MOE_DEC_FUSE_UPW;
         if (same_type) {
-            if (a.mode == 1) return a.act_type == 1 ? launch_wave<1, true>(a, slots, st)
-                                                    : launch_wave<1, false>(a, slots, st);
-            return a.act_type == 1 ? launch_wave<0, true>(a, slots, st) : launch_wave<0, false>(a, slots, st);
+            if (reduced) *reduced = fuse;
+            if (a.mode == 1) return a.act_type == 1 ? launch_wave<1, true>(a, slots, false, st)
+                                                    : launch_wave<1, false>(a, slots, false, st);
+            return a.act_type == 1 ? launch_wave<0, true>(a, slots, fuse, st)
+                                   : launch_wave<0, false>(a, slots, fuse, st);
         }
     }
     const int nb_r = a.d_max * ((a.rw.N + kR - 1) / kR);

@@ -374,6 +374,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
     Timer tm(opt, st);
     const int64_t n = d.T * d.k;
     const bool shared = d.S > 0;
+    bool reduced = false;
 
     if (path == 1) {
         const int bm = gemm_tile_m(p.msub);
@@ -510,9 +511,16 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         b.mode = 0;
         b.d_max = a.d_max;
         b.rows_per_block = 32;
+        b.route_w = route_w;
+        b.out_tok = out;
         tm.begin();
-        if ((s = hip_check(launch_decode(b, st), "down GEMV"))) return s;
+        if ((s = hip_check(launch_decode(b, st, &reduced), "down GEMV"))) return s;
         tm.end();
+    }
+    if (reduced) {   // the GEMV wrote out itself: the reduce stage is empty
+        tm.begin();
+        tm.end();
+        return MOE_OK;
     }
     ReduceArgs rd{};
     rd.ids = ids;
@@ -636,9 +644,19 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         a.mode = 0;
         a.d_max = (int32_t)(n < E ? n : E);
         a.rows_per_block = 32;
+        if (weighted) {
+            a.route_w = route_w;
+            a.out_tok = dst;
+        }
+        bool reduced = false;
         tm.begin();
-        if ((s = hip_check(launch_decode(a, st), "GEMV"))) return s;
+        if ((s = hip_check(launch_decode(a, st, &reduced), "GEMV"))) return s;
         tm.end();
+        if (reduced) {   // weighted sum written by the GEMV: the reduce stage is empty
+            tm.begin();
+            tm.end();
+            return MOE_OK;
+        }
     }
     ReduceArgs rd{};
     rd.ids = ids;

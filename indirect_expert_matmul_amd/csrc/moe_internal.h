@@ -108,8 +108,14 @@ struct DecArgs {
     int32_t mode;           // 0 raw, 1 silu(gate) * up
     int32_t d_max;          // upper bound on distinct experts (grid)
     int32_t rows_per_block;
+    // down mode, optional: the weighted sum over each token's slots (route_w, or weight 1
+    // when null) plus the shared experts, written to out_tok [T][N] by the GEMV itself
+    const float* route_w;
+    float* out_tok;
 };
-hipError_t launch_decode(const DecArgs& a, hipStream_t st);
+// *reduced (if given) tells whether out_tok was written (the reduction was fused); when
+// false the per-slot rows are in out / sout and the reduce kernel still has to run.
+hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced = nullptr);
 
 // ---------------------------------------------------------------- router top-k
 struct RouterArgs {

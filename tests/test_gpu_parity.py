@@ -152,9 +152,9 @@ def test_ffn_invalid_ids_and_shared_width():
 @pytest.mark.parametrize("S", [0, 1])
 @pytest.mark.parametrize("which", ["some", "all"])
 def test_ffn_gemv_invalid_ids(S, which):
-    """Decode-sized batches (the GEMV path, whose down launch also does the weighted
-    reduce): out-of-range ids contribute nothing; with every id out of range the
-    routed part is zero and only the shared experts remain."""
+    """Decode-sized batches (the GEMV path; without shared experts here the down launch
+    also does the weighted reduce): out-of-range ids contribute nothing; with every id
+    out of range the routed part is zero and only the shared experts remain."""
     E, k, T, n_embd, n_ff = 8, 4, 6, 192, 128
     ids = synth.draw_ids_uniform(9, T, E, k)
     if which == "some":
@@ -172,6 +172,30 @@ def test_ffn_gemv_invalid_ids(S, which):
             assert np.all(g == 0.0), path
         else:
             assert normwise(g, ref) <= _tol(path), path
+
+
+# Decode-sized batches whose routed experts plus shared experts fit two per wave run the
+# down projection and the weighted reduce in one launch (a block owns a chunk of output
+# rows for every expert and sums the slots through LDS). The cases vary the shared
+# experts (several tokens, a width of their own), output widths that leave a short last
+# chunk of rows, and two experts per wave.
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S,n_ff_sh", [
+    (4, 2, 3, 224, 96, 2, 96),       # shared experts on three tokens, one row per block
+    (6, 2, 2, 1120, 160, 1, 224),    # shared width of its own; 3-row chunks, last one short
+    (16, 8, 1, 2624, 256, 0, 0),     # eight experts, two per wave; 6-row chunks, last one short
+    (8, 4, 2, 640, 1056, 0, 0),      # K = 1056: two K pieces, the second mostly past K
+])
+def test_ffn_gemv_fused_reduce(E, k, T, n_embd, n_ff, S, n_ff_sh):
+    ids = np.stack([np.random.default_rng(100 + t).permutation(E)[:k] for t in range(T)]).astype(np.int32)
+    inp = synth.make_custom_ffn(41 + E, E, k, T, n_embd, n_ff, 0, ids=ids)
+    if S:
+        sh = synth.make_custom_ffn(43, S, 1, T, n_embd, n_ff_sh, 0)
+        for n in ("gate", "up", "down"):
+            inp["sh_" + n + "_qs"], inp["sh_" + n + "_d"] = sh[n + "_qs"], sh[n + "_d"]
+    ref = oracle.ffn(inp)
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), ref) <= TOL_FP32
 
 
 def test_lite_full():
