@@ -38,8 +38,10 @@ STAGES = {1: ["row_ids", "gemm_gate_up", "gemm_down", "reduce"],
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 20 steps and 0.2 s of them, "
+                        "so the GPU clocks have ramped up; the count is reported)")
     p.add_argument("--config", default="lite")
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
@@ -129,6 +131,22 @@ def measured_traffic(config, stage):
     return float(ent["bytes"])
 
 
+def warm_up(run, n):
+    """Untimed steps before the timed ones: exactly n if given, otherwise at least 20
+    steps and at least 0.2 s of them (from idle, the GPU clocks take some milliseconds
+    to ramp up, which a fixed handful of sub-millisecond steps does not cover).
+    Returns the number of steps run."""
+    import torch
+    done, t0 = 0, time.perf_counter()
+    while (done < n) if n is not None else (done < 20 or time.perf_counter() - t0 < 0.2):
+        for _ in range(10 if n is None else n - done):
+            run(done)
+            done += 1
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return done
+
+
 def bench_row_ids(args):
     """The row-id pass alone at scale: T = 2^21 tokens, k = 8, E = 256, uniform ids
     (seed 6). Algorithmic bytes = ids read + the two maps written + the bounds."""
@@ -143,9 +161,7 @@ def bench_row_ids(args):
     ids = torch.from_numpy(ids_np).to(dev)
     ws = torch.empty(moe.lib.moe_row_ids_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        moe.moe_row_ids(ids, E, workspace=ws, stream=stream)
-    torch.cuda.synchronize()
+    args.warmup = warm_up(lambda i: moe.moe_row_ids(ids, E, workspace=ws, stream=stream), args.warmup)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
@@ -244,9 +260,7 @@ def main():
         moe.moe_ffn_fused(g, u, d, x, ids, rw, shared=s, path=args.path, out=out, workspace=ws,
                           stream=stream, events=events)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     run = step
     if args.graph:
         # one captured step per weight copy, replayed in the same rotation
@@ -263,9 +277,7 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
         run = lambda i: graphs[i % R].replay()
-        for i in range(args.warmup):
-            run(i)
-        torch.cuda.synchronize()
+        warm_up(run, args.warmup)
     t0 = time.perf_counter()
     for i in range(args.steps):
         run(i)
@@ -284,11 +296,14 @@ def main():
     for i in range(args.steps):
         step(i, events=[e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
+    if moe.last_stage_count() < len(names):
+        # small decode batches: the down GEMV does the weighted reduce itself
+        names = names[:1] + ["gemv_down_reduce"]
     stage_ms = {n: float(np.mean([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1])
                                   for i in range(args.steps)])) for j, n in enumerate(names)}
     dom = max(stage_ms, key=stage_ms.get)
     kern = {"gemm_gate_up": "gate_up", "gemv_gate_up": "gate_up", "gemm_down": "down",
-            "gemv_down": "down"}.get(dom)
+            "gemv_down": "down", "gemv_down_reduce": "down"}.get(dom)
     mfma_bound = path == 1 and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
     traffic = measured_traffic(args.config, dom)
     if kern is None:

@@ -85,8 +85,11 @@ typedef struct {
  * events[2i+1] after its i-th kernel launch on `stream` (while 2i+1 <
  * n_timing_events). Kernel order -- moe_ffn_fused GEMM path: row ids, gate/up
  * grouped GEMM, down grouped GEMM, reduce; GEMV path: gate/up GEMV, down GEMV,
- * reduce. moe_mul_mat_id GEMM path: row ids, grouped GEMM, fix-up/reduce;
- * GEMV path: GEMV, fix-up/reduce. */
+ * reduce, where small batches (the distinct experts plus the shared ones fit two per
+ * wave) do the reduce inside the down GEMV and time two kernels only.
+ * moe_mul_mat_id GEMM path: row ids, grouped GEMM, fix-up/reduce; GEMV path: GEMV,
+ * fix-up/reduce (weighted calls of small batches: the GEMV alone).
+ * moe_last_stage_count() tells how many kernels the last call timed. */
 typedef struct {
     int32_t path; /* 0 auto, 1 force grouped GEMM, 2 force GEMV (decode)        */
     float tau;    /* <= 0 means the default, 1.0                                 */
@@ -187,6 +190,9 @@ int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int
 
 const char *moe_status_string(moe_status s);
 const char *moe_last_error(void); /* thread-local detail of the last failure ("" if none) */
+/* Kernels (timing-event pairs, see moe_options) enqueued by the last successful
+ * moe_mul_mat_id or moe_ffn_fused call on this thread; 0 before any such call. */
+int32_t moe_last_stage_count(void);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
            "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
-           "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error")
+           "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error",
+           "moe_last_stage_count")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +75,8 @@ def _load():
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_stage_count.argtypes = []
+    lib.moe_last_stage_count.restype = I32
     return lib
 
 
@@ -86,6 +89,12 @@ def _status_name(s: int) -> str:
 
 def last_error() -> str:
     return lib.moe_last_error().decode()
+
+
+def last_stage_count() -> int:
+    """Kernels (timing-event pairs) the last mul_mat_id / ffn_fused call on this thread
+    enqueued."""
+    return int(lib.moe_last_stage_count())
 
 
 def _check(status: int, fn: str):

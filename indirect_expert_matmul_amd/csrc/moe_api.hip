@@ -23,6 +23,7 @@ using namespace moe;
 namespace {
 
 thread_local std::string g_err;
+thread_local int32_t g_stages = 0;   // kernels timed by the last call
 
 moe_status fail(moe_status s, const char* fmt, ...) {
     char buf[512];
@@ -284,6 +285,7 @@ const char* moe_status_string(moe_status s) {
 }
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+int32_t moe_last_stage_count(void) { return g_stages; }
 
 int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
                         const moe_options* opt) {
@@ -361,7 +363,10 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
     FfnDims d{};
     moe_status s = validate_ffn(gate, up, down, sh_gate, sh_up, sh_down, x_type, n_tokens, n_used, &d);
     if (s) return s;
-    if (n_tokens == 0) return MOE_OK;
+    if (n_tokens == 0) {
+        g_stages = 0;
+        return MOE_OK;
+    }
     if (!x || !ids || !route_w || !out) return fail(MOE_EINVAL, "NULL pointer argument");
     const int path = select_path(d.T, d.k, d.E, ffn_act_width(d), opt);
     if (path < 0) return (moe_status)path;
@@ -517,9 +522,8 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         if ((s = hip_check(launch_decode(b, st, &reduced), "down GEMV"))) return s;
         tm.end();
     }
-    if (reduced) {   // the GEMV wrote out itself: the reduce stage is empty
-        tm.begin();
-        tm.end();
+    if (reduced) {   // the down GEMV wrote out itself
+        g_stages = tm.stage;
         return MOE_OK;
     }
     ReduceArgs rd{};
@@ -537,6 +541,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
     tm.begin();
     if ((s = hip_check(launch_reduce(rd, st), "reduce"))) return s;
     tm.end();
+    g_stages = tm.stage;
     return MOE_OK;
 }
 
@@ -560,7 +565,10 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     g_err.clear();
     moe_status s = validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used);
     if (s) return s;
-    if (n_tokens == 0) return MOE_OK;
+    if (n_tokens == 0) {
+        g_stages = 0;
+        return MOE_OK;
+    }
     if (!src1 || !ids || !dst) return fail(MOE_EINVAL, "NULL pointer argument");
     const bool q8 = w->type == MOE_Q8_0;
     const int32_t E = (int32_t)w->n_mat, N = (int32_t)w->rows, K = (int32_t)w->cols;
@@ -652,9 +660,8 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         tm.begin();
         if ((s = hip_check(launch_decode(a, st, &reduced), "GEMV"))) return s;
         tm.end();
-        if (reduced) {   // weighted sum written by the GEMV: the reduce stage is empty
-            tm.begin();
-            tm.end();
+        if (reduced) {   // the GEMV wrote the weighted sum itself
+            g_stages = tm.stage;
             return MOE_OK;
         }
     }
@@ -671,6 +678,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     tm.begin();
     if ((s = hip_check(launch_reduce(rd, st), weighted ? "reduce" : "zero invalid slots"))) return s;
     tm.end();
+    g_stages = tm.stage;
     return MOE_OK;
 }
 

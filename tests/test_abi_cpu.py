@@ -68,6 +68,7 @@ def test_ffn_validation():
     assert _ffn(T=100, k=8, path=2) == moe.MOE_EINVAL                     # GEMV forced past its bound
     assert "n_used" in moe.last_error() or "GEMV" in moe.last_error()
     assert _ffn(T=0) == moe.MOE_OK                                         # empty batch: no-op
+    assert moe.last_stage_count() == 0                                     # ... that timed nothing
 
 
 def test_mul_mat_id_validation():

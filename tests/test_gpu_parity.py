@@ -116,6 +116,8 @@ def test_ffn_small_shapes(path, E, k, T, n_embd, n_ff, S):
     inp = synth.make_custom_ffn(11 + E, E, k, T, n_embd, n_ff, S, ids=ids)
     got = run_ffn(upload_ffn(inp), path=path)
     torch.cuda.synchronize()
+    if path == moe.PATH_GEMM:
+        assert moe.last_stage_count() == 4   # row ids, gate/up, down, reduce
     assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= _tol(path)
 
 
@@ -195,6 +197,7 @@ def test_ffn_gemv_fused_reduce(E, k, T, n_embd, n_ff, S, n_ff_sh):
     ref = oracle.ffn(inp)
     got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
     torch.cuda.synchronize()
+    assert moe.last_stage_count() == 2   # gate/up GEMV, down GEMV with the reduce
     assert normwise(got.cpu().numpy(), ref) <= TOL_FP32
 
 
