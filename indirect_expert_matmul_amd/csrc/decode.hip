@@ -27,8 +27,18 @@
 #include "lds_dma.h"
 #include "moe_internal.h"
 
+// Weight loads carry the non-temporal hint: every weight row is read once per launch,
+// while the activation rows are read by every wave of their expert (measured on
+// single-token decode: 27.4 -> 26.1 us per layer; eight tokens: 122.7 -> 117.9 us).
+#ifndef MOE_DEC_W_NT
+#define MOE_DEC_W_NT 1
+#endif
+
 namespace moe {
 namespace {
+
+// weight loads carry the non-temporal hint
+constexpr bool kDecWeightsNT = MOE_DEC_W_NT != 0;
 
 constexpr int kThreads = 256;
 constexpr int kR = 8;    // weight rows (row pairs for gate/up) per block
@@ -412,7 +422,8 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
             const uint16_t* dr = (m == 0 ? d1 : d2) + (int64_t)n * KB;
 #pragma unroll
             for (int i = 0; i < NIT; i++) {
-                w.q[m][i] = *(const i32x4*)(qr + kc[i]);
+                if constexpr (kDecWeightsNT) w.q[m][i] = __builtin_nontemporal_load((const i32x4*)(qr + kc[i]));
+                else w.q[m][i] = *(const i32x4*)(qr + kc[i]);
                 w.d[m][i] = dr[kc[i] >> 5];
             }
         }
@@ -611,7 +622,7 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
             const uint32_t dst = ring_lds + (uint32_t)(j * SLOT + m * MAT);
             const int8_t* qrow = (const int8_t*)uniform_ptr((m == 0 ? q1 : q2) + (int64_t)n * K);
 #pragma unroll
-            for (int i = 0; i < NIT; i++) dma16(qrow, qoff[i], dst + i * 1024);
+            for (int i = 0; i < NIT; i++) dma16<kDecWeightsNT>(qrow, qoff[i], dst + i * 1024);
             const uintptr_t sa = (uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * 2);  // first scale
             const uint8_t* srow = (const uint8_t*)uniform_ptr((const void*)(sa & ~(uintptr_t)3));
             const int last = ((int)(sa & 3) + 2 * KB - 1) >> 2;

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "lds_dma.h"
+
 #include "moe_internal.h"
 
 #ifndef MOE_GEMM_CFG2
@@ -49,6 +50,12 @@
 
 namespace moe {
 namespace {
+
+// A weight copy, with the non-temporal hint when the slab is read once (wave-uniform).
+__device__ __forceinline__ void dma16_w(bool once, const void* base, uint32_t voff, uint32_t lds_base) {
+    if (once) dma16<true>(base, voff, lds_base);
+    else dma16<false>(base, voff, lds_base);
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -184,6 +191,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
     const int nsteps = (K + 127) >> 7;
     const int KB = K >> 5;
+    const bool w_once = P.w_once != 0;
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
 
     if (tid < BM) {
@@ -260,8 +268,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i],
-                      st + A_BYTES + wv * 4096 + i * 1024);
+                dma16_w(w_once, ((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i],
+                        st + A_BYTES + wv * 4096 + i * 1024);
             if (SG == 1) {
 #pragma unroll
                 for (int t = 0; t < 2; t++)
@@ -279,8 +287,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const uint32_t adj = (k0 + b_lc[i] * 16 >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
-                dma16(((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i] - adj,
-                      st + A_BYTES + wv * 4096 + i * 1024);
+                dma16_w(w_once, ((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i] - adj,
+                        st + A_BYTES + wv * 4096 + i * 1024);
             }
             if (SG == 1) {   // (SG = 4 needs K % 512 == 0: no partial stage)
 #pragma unroll

@@ -27,17 +27,30 @@ static __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// base: wave-uniform 64-bit address; voff: per-lane 32-bit byte offset.
+// base: wave-uniform 64-bit address; voff: per-lane 32-bit byte offset. NT marks
+// the lines as not expected to be read again (streamed weights), so the caches
+// replace them before lines that are (activation rows, scales).
+template <bool NT = false>
 static __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
     uint32_t tmp;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
-        : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base)
-        : "memory");
+    if constexpr (NT)
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "global_load_lds_dwordx4 %2, %3 nt\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(tmp)
+            : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base)
+            : "memory");
+    else
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "global_load_lds_dwordx4 %2, %3\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(tmp)
+            : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(base)
+            : "memory");
 }
 static __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_base) {
     uint32_t tmp;

@@ -412,6 +412,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         r.a_rows = p.r.ids_src1;
         r.out = p.h;
         r.ldo = d.n_ff;
+        r.w_once = n <= (int64_t)d.E * bm;   // at most one M tile per expert on average
         if (shared) {
             GemmProblem& q = g.p[1];
             q.qs1 = (const int8_t*)sh_gate->data;
@@ -428,6 +429,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
             q.a_row_mod = (int32_t)d.T;
             q.out = p.hsh;
             q.ldo = d.n_ff_sh;
+            q.w_once = d.T <= bm;
         }
         tm.begin();
         if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "gate/up grouped GEMM"))) return s;
@@ -451,6 +453,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         r2.out = p.y;
         r2.ldo = d.n_embd;
         r2.out_rows = p.r.ids_dst;
+        r2.w_once = r.w_once;
         if (shared) {
             GemmProblem& q = g2.p[1];
             q.qs1 = (const int8_t*)sh_down->data;
@@ -464,6 +467,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
             q.lda = d.n_ff_sh;
             q.out = p.ysh;
             q.ldo = d.n_embd;
+            q.w_once = d.T <= bm;
         }
         tm.begin();
         if ((s = hip_check(launch_gemm_q8(g2, p.msub, st), "down grouped GEMM"))) return s;
@@ -618,6 +622,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.out = slot_out;
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
+            r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
             tm.begin();
             if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "grouped GEMM"))) return s;
             tm.end();

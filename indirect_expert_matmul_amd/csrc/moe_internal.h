@@ -62,6 +62,11 @@ struct GemmProblem {
     void* out;
     int64_t ldo;
     const int32_t* out_rows;  // nullptr: row j; else out_rows[j]
+    // 1: segments average at most one M tile, so each weight slab is read once per
+    // launch and the 64-row kernel's copies of it carry the non-temporal hint (they
+    // leave L2 before the activation rows and scales that are read again). The 128-row
+    // kernel ignores it: its segments usually share each slab between M tiles.
+    int32_t w_once;
 };
 struct GemmArgs {
     GemmProblem p[2];
