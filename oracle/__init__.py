@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, Q8_0 = 0, 1, 2
+F32, BF16, Q8_0, MXFP4 = 0, 1, 2, 3
 _TYPES = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
 
 
@@ -46,6 +46,10 @@ def lib():
         _lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
         _lib.oracle_bf16_to_double.restype = ctypes.c_double
         _lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        _lib.oracle_e2m1_to_double.restype = ctypes.c_double
+        _lib.oracle_e2m1_to_double.argtypes = [ctypes.c_int]
+        _lib.oracle_e8m0_to_double.restype = ctypes.c_double
+        _lib.oracle_e8m0_to_double.argtypes = [ctypes.c_int]
         _lib.oracle_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P]
         _lib.oracle_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P]
         _lib.oracle_mul_mat_id.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, ctypes.c_int, I32,
@@ -75,10 +79,28 @@ def bf16_to_double(bits: int) -> float:
     return lib().oracle_bf16_to_double(int(bits) & 0xFFFF)
 
 
+def e2m1_to_double(code: int) -> float:
+    return lib().oracle_e2m1_to_double(int(code) & 15)
+
+
+def e8m0_to_double(x: int) -> float:
+    return lib().oracle_e8m0_to_double(int(x) & 0xFF)
+
+
 def dequant(qs_or_w, d=None) -> np.ndarray:
-    """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]) or widen
-    float32 weights, to float64 of the same shape."""
+    """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]) or MXFP4
+    (codes uint8 [..][rows][cols/2], E8M0 scales uint8 [..][rows][cols/32]), or widen
+    float32 weights, to float64 [..][rows][cols]."""
     a = np.asarray(qs_or_w)
+    if d is not None and a.dtype == np.uint8:
+        shape = a.shape[:-1] + (2 * a.shape[-1],)
+        a3 = _c(a.reshape((-1,) + a.shape[-2:]), np.uint8)
+        out = np.empty((a3.shape[0], a3.shape[1], 2 * a3.shape[2]), np.float64)
+        s = _c(np.asarray(d).reshape(a3.shape[0], a3.shape[1], -1), np.uint8)
+        rc = lib().oracle_dequant(MXFP4, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2], _p(out))
+        if rc:
+            raise ValueError("oracle_dequant rejected its arguments (%d)" % rc)
+        return out.reshape(shape)
     shape = a.shape
     a3 = a.reshape((-1,) + shape[-2:])
     out = np.empty(a3.shape, np.float64)
@@ -108,17 +130,23 @@ def row_ids(ids: np.ndarray, n_experts: int, src1_rows_per_token: int = 1):
 
 
 def _weights(qs_or_w, d):
+    """(type, data, scales, logical shape). MXFP4 is told apart by its uint8 codes."""
     if d is None:
-        return F32, _c(qs_or_w, np.float32), None
-    return Q8_0, _c(qs_or_w, np.int8), _c(np.asarray(d).view(np.uint16), np.uint16)
+        w = _c(qs_or_w, np.float32)
+        return F32, w, None, w.shape
+    if np.asarray(qs_or_w).dtype == np.uint8:
+        q = _c(qs_or_w, np.uint8)
+        return MXFP4, q, _c(d, np.uint8), q.shape[:-1] + (2 * q.shape[-1],)
+    q = _c(qs_or_w, np.int8)
+    return Q8_0, q, _c(np.asarray(d).view(np.uint16), np.uint16), q.shape
 
 
 def mul_mat_id(w, w_d, src1, src1_type: str, ids, route_w=None, src1_rows_per_token: int = 1):
     """Per-slot dst float64 [T][k][N], or the route_w-weighted [T][N].
-    ``w`` is float32 [E][N][K] (w_d None) or Q8_0 qs [E][N][K] with scales w_d.
-    ``src1`` is [T*B][K] (float32, or bf16 bits as uint16)."""
-    wt, wq, ws = _weights(w, w_d)
-    E, N, K = wq.shape
+    ``w`` is float32 [E][N][K] (w_d None), Q8_0 qs [E][N][K] with scales w_d, or MXFP4
+    codes [E][N][K/2] with E8M0 scales w_d. ``src1`` is [T*B][K] (float32, or bf16 bits
+    as uint16)."""
+    wt, wq, ws, (E, N, K) = _weights(w, w_d)
     ids = _c(ids, np.int32)
     T, k = ids.shape
     st = _TYPES[src1_type]
@@ -145,17 +173,15 @@ def ffn(inp: dict, token_rows=None) -> np.ndarray:
     xt = _TYPES[inp.get("xtype", "bf16")]
     x = _c(x, np.float32 if xt == F32 else np.uint16)
     rw = _c(rw, np.float32)
-    wt, g, gs = _weights(inp["gate_qs"], inp.get("gate_d"))
-    _, u, us = _weights(inp["up_qs"], inp.get("up_d"))
-    _, dn, dns = _weights(inp["down_qs"], inp.get("down_d"))
-    E, n_ff, n_embd = g.shape
+    wt, g, gs, (E, n_ff, n_embd) = _weights(inp["gate_qs"], inp.get("gate_d"))
+    _, u, us, _ = _weights(inp["up_qs"], inp.get("up_d"))
+    _, dn, dns, _ = _weights(inp["down_qs"], inp.get("down_d"))
     S, n_ff_sh = 0, 0
     sg = sgs = su = sus = sd = sds = None
     if inp.get("sh_gate_qs") is not None:
-        _, sg, sgs = _weights(inp["sh_gate_qs"], inp.get("sh_gate_d"))
-        _, su, sus = _weights(inp["sh_up_qs"], inp.get("sh_up_d"))
-        _, sd, sds = _weights(inp["sh_down_qs"], inp.get("sh_down_d"))
-        S, n_ff_sh = sg.shape[0], sg.shape[1]
+        _, sg, sgs, (S, n_ff_sh, _) = _weights(inp["sh_gate_qs"], inp.get("sh_gate_d"))
+        _, su, sus, _ = _weights(inp["sh_up_qs"], inp.get("sh_up_d"))
+        _, sd, sds, _ = _weights(inp["sh_down_qs"], inp.get("sh_down_d"))
     out = np.empty((T, n_embd), np.float64)
     rc = lib().oracle_ffn(wt, _p(g), _p(gs), _p(u), _p(us), _p(dn), _p(dns), E, n_ff, n_embd,
                           _p(sg), _p(sgs), _p(su), _p(sus), _p(sd), _p(sds), S, n_ff_sh,

@@ -21,6 +21,10 @@
  *  - Experts may be Q8_0-quantized (section 2.1 names Q8_0): blocks of 32 int8
  *    values sharing one fp16 scale, value = d * q. Dequantization is exact in
  *    float64 (an 11-bit by 8-bit product).
+ *  - Experts may be MXFP4 (the TensorSharp MoE-offload page lists GPT-OSS 20B as
+ *    "Q8_0 / MXFP4"; the pages do not define the format, so it is taken from the
+ *    OCP Microscaling (MX) v1.0 specification): blocks of 32 FP4 E2M1 elements
+ *    sharing one E8M0 scale, value = fp4(code) * 2^(scale - 127). Exact in float64.
  *  - The fused MoE FFN applies gate and up projections, SiLU(gate) * up, then the
  *    down projection (section 4.2 names the fused up/gate MoE forward), weights each
  *    routed slot's result by its routing weight and adds always-on shared experts,
@@ -40,7 +44,10 @@
  *  - SiLU(z) = z / (1 + exp(-z)); shared experts have weight 1 and are added after
  *    the routed slots, in index order.
  *
- * Types: 0 = float32, 1 = bfloat16 (uint16 bit pattern), 2 = Q8_0 (int8 + fp16).
+ * Types: 0 = float32, 1 = bfloat16 (uint16 bit pattern), 2 = Q8_0 (int8 + fp16),
+ * 3 = MXFP4 (two 4-bit codes per byte + one uint8 E8M0 scale per 32 elements). MXFP4
+ * storage (a reading; the pages fix none): codes [E][rows][cols/2] bytes, element 2i
+ * of a row in bits 0-3 of byte i and element 2i+1 in bits 4-7; scales [E][rows][cols/32].
  * All entry points return 0 on success and a negative value on bad arguments.
  */
 #include <math.h>
@@ -51,6 +58,7 @@
 #define OR_F32 0
 #define OR_BF16 1
 #define OR_Q8_0 2
+#define OR_MXFP4 3
 
 /* IEEE binary16 -> double, written from the format's definition
  * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits). */
@@ -76,11 +84,38 @@ double oracle_bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* FP4 E2M1 code -> double, from the format's definition: bit 3 sign, bits 2-1 exponent
+ * with bias 1, bit 0 mantissa; exponent 0 is subnormal (mantissa * 2^-1), otherwise
+ * (1 + mantissa/2) * 2^(exponent - 1). No infinities or NaN. */
+double oracle_e2m1_to_double(int code) {
+    int sign = (code >> 3) & 1;
+    int ex = (code >> 1) & 3;
+    int m = code & 1;
+    double v = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return sign ? -v : v;
+}
+
+/* E8M0 scale -> double: 2^(x - 127); x = 255 encodes NaN. */
+double oracle_e8m0_to_double(int x) {
+    if ((x & 0xff) == 255) return NAN;
+    return ldexp(1.0, (x & 0xff) - 127);
+}
+
+static int is_quant(int type) { return type == OR_Q8_0 || type == OR_MXFP4; }
+
 /* One weight element w(e, n, c) of a stacked matrix, as a double. */
 static double weight_at(int type, const void *data, const void *scales, int64_t rows,
                         int64_t cols, int64_t e, int64_t n, int64_t c) {
     int64_t idx = (e * rows + n) * cols + c;
     if (type == OR_F32) return (double)((const float *)data)[idx];
+    if (type == OR_MXFP4) {
+        /* two codes per byte, the even column in the low nibble; one E8M0 scale per
+         * 32 consecutive columns of a row */
+        uint8_t b = ((const uint8_t *)data)[(e * rows + n) * (cols / 2) + c / 2];
+        int code = (c & 1) ? (b >> 4) : (b & 15);
+        uint8_t x = ((const uint8_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
+        return oracle_e2m1_to_double(code) * oracle_e8m0_to_double(x);
+    }
     /* Q8_0: value = d * q, one fp16 scale per 32 consecutive columns of a row. */
     int8_t q = ((const int8_t *)data)[idx];
     uint16_t d = ((const uint16_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
@@ -96,8 +131,8 @@ static double act_at(int type, const void *src, int64_t idx) {
 /* Dequantize (or widen) a whole stack of matrices into out[n_mat*rows*cols]. */
 int oracle_dequant(int type, const void *data, const void *scales, int64_t n_mat, int64_t rows,
                    int64_t cols, double *out) {
-    if (!data || !out || (type != OR_F32 && type != OR_Q8_0)) return -1;
-    if (type == OR_Q8_0 && (!scales || cols % 32)) return -1;
+    if (!data || !out || (type != OR_F32 && !is_quant(type))) return -1;
+    if (is_quant(type) && (!scales || cols % 32)) return -1;
     for (int64_t e = 0; e < n_mat; e++)
         for (int64_t n = 0; n < rows; n++)
             for (int64_t c = 0; c < cols; c++)
@@ -160,6 +195,14 @@ static void matvec(int type, const void *data, const void *scales, int64_t rows,
         }
         return;
     }
+    if (type == OR_MXFP4) {
+        for (; n < rows; n++) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < cols; c++) acc += weight_at(type, data, scales, rows, cols, e, n, c) * a[c];
+            y[n] = acc;
+        }
+        return;
+    }
     const int8_t *q = (const int8_t *)data + e * rows * cols;
     const uint16_t *ds = (const uint16_t *)scales + e * rows * (cols / 32);
     int64_t nb = cols / 32;
@@ -205,8 +248,8 @@ int oracle_mul_mat_id(int w_type, const void *w_data, const void *w_scales, int6
                       int64_t K, const void *src1, int src1_type, int32_t B, const int32_t *ids,
                       int64_t T, int32_t k, const float *route_w, double *dst) {
     if (!w_data || !src1 || !ids || !dst || E <= 0 || N <= 0 || K <= 0 || T < 0 || k <= 0) return -1;
-    if (w_type != OR_F32 && w_type != OR_Q8_0) return -1;
-    if (w_type == OR_Q8_0 && (!w_scales || K % 32)) return -1;
+    if (w_type != OR_F32 && !is_quant(w_type)) return -1;
+    if (is_quant(w_type) && (!w_scales || K % 32)) return -1;
     if (src1_type != OR_F32 && src1_type != OR_BF16) return -1;
     if (B != 1 && B != k) return -1;
     int bad = 0;
@@ -271,12 +314,12 @@ int oracle_ffn(int w_type, const void *g_data, const void *g_scales, const void 
                const int32_t *ids, const float *route_w, int64_t T, int32_t k, double *out) {
     if (!g_data || !u_data || !d_data || !x || !ids || !route_w || !out) return -1;
     if (E <= 0 || n_ff <= 0 || n_embd <= 0 || T < 0 || k <= 0 || S < 0) return -1;
-    if (w_type != OR_F32 && w_type != OR_Q8_0) return -1;
+    if (w_type != OR_F32 && !is_quant(w_type)) return -1;
     if (x_type != OR_F32 && x_type != OR_BF16) return -1;
-    if (w_type == OR_Q8_0 && (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32))
+    if (is_quant(w_type) && (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32))
         return -1;
     if (S > 0 && (!sg_data || !su_data || !sd_data || n_ff_sh <= 0)) return -1;
-    if (S > 0 && w_type == OR_Q8_0 && (!sg_scales || !su_scales || !sd_scales || n_ff_sh % 32))
+    if (S > 0 && is_quant(w_type) && (!sg_scales || !su_scales || !sd_scales || n_ff_sh % 32))
         return -1;
     int64_t ffmax = n_ff > n_ff_sh ? n_ff : n_ff_sh;
     int bad = 0;

@@ -17,6 +17,10 @@ Workloads follow the shapes the pages discuss for mul_mat_id:
 Storage conventions (row-major, last index contiguous):
   * Q8_0-style weights: ``qs`` int8 [E][rows][cols] with q uniform in [-127, 127],
     ``d`` float16 [E][rows][cols // 32] uniform in (0.5, 1.5) * 1e-3, value = d * q.
+  * MXFP4 weights (the format GPT-OSS ships its experts in): ``qs`` uint8
+    [E][rows][cols // 2], two 4-bit E2M1 codes per byte (column 2i in the low nibble,
+    2i+1 in the high one), codes uniform over all 16; ``d`` uint8 [E][rows][cols // 32]
+    E8M0 scales uniform in {118, ..., 121} (2^-9 .. 2^-6), value = fp4(code) * 2^(d-127).
   * bf16 tensors are stored as their uint16 bit patterns (numpy has no bfloat16),
     rounded to nearest-even from float32.
   * ids int32 [T][k]; route_w float32 [T][k], softmax over each token's k picks
@@ -51,7 +55,7 @@ class Config:
     n_embd: int
     n_ff: int
     n_shared: int = 0
-    wtype: str = "q8_0"          # 'q8_0' or 'f32'
+    wtype: str = "q8_0"          # 'q8_0', 'mxfp4' or 'f32'
     routing: str = "uniform"     # 'uniform' or 'zipf'
     zipf_s: float = 1.1
     seed: int = 0
@@ -71,6 +75,11 @@ CONFIGS = {
                    desc="GPT-OSS-20B-shaped decode: E32 k4 T1 n_embd=n_ff=2880 Q8_0"),
     "dec8": Config("dec8", "ffn", 32, 4, 8, 2880, 2880, seed=3,
                    desc="GPT-OSS-20B-shaped decode: E32 k4 T8 n_embd=n_ff=2880 Q8_0"),
+    # The same decode shapes with MXFP4 experts (the format GPT-OSS ships them in).
+    "dec1x": Config("dec1x", "ffn", 32, 4, 1, 2880, 2880, wtype="mxfp4", seed=3,
+                    desc="GPT-OSS-20B-shaped decode: E32 k4 T1 n_embd=n_ff=2880 MXFP4"),
+    "dec8x": Config("dec8x", "ffn", 32, 4, 8, 2880, 2880, wtype="mxfp4", seed=3,
+                    desc="GPT-OSS-20B-shaped decode: E32 k4 T8 n_embd=n_ff=2880 MXFP4"),
     # Zipf(1.1)-skewed prefill, PP4096.
     "skew": Config("skew", "ffn", 128, 8, 4096, 2048, 768, routing="zipf", seed=4,
                    desc="Skewed prefill: E128 k8 T4096 n_embd2048 n_ff768 Zipf(1.1) Q8_0"),
@@ -153,18 +162,33 @@ def draw_q8_0(rng: np.random.Generator, rows: int, cols: int):
     return qs, d
 
 
+def draw_mxfp4(rng: np.random.Generator, rows: int, cols: int):
+    """One MXFP4 matrix: packed codes uint8 [rows][cols/2] (two uniform 4-bit codes per
+    byte), E8M0 scales uint8 [rows][cols/32] uniform in {118..121}."""
+    if cols % 32:
+        raise ValueError("MXFP4 needs cols % 32 == 0")
+    qs = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    d = rng.integers(118, 122, size=(rows, cols // 32), dtype=np.uint8)
+    return qs, d
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
 def draw_q8_0_stack(seed: int, stream: int, which: int, n_mat: int, rows: int, cols: int,
-                    qs_out: np.ndarray | None = None, d_out: np.ndarray | None = None):
-    """n_mat stacked Q8_0 matrices; matrix e comes from stream (seed, stream, e, which)."""
-    qs = qs_out if qs_out is not None else np.empty((n_mat, rows, cols), np.int8)
-    d = d_out if d_out is not None else np.empty((n_mat, rows, cols // 32), np.float16)
+                    qs_out: np.ndarray | None = None, d_out: np.ndarray | None = None,
+                    wtype: str = "q8_0"):
+    """n_mat stacked Q8_0 (or MXFP4) matrices; matrix e comes from stream
+    (seed, stream, e, which)."""
+    fp4 = wtype == "mxfp4"
+    qs = qs_out if qs_out is not None else (np.empty((n_mat, rows, cols // 2), np.uint8) if fp4
+                                             else np.empty((n_mat, rows, cols), np.int8))
+    d = d_out if d_out is not None else np.empty((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
+    draw = draw_mxfp4 if fp4 else draw_q8_0
 
     def one(e):
-        q, s = draw_q8_0(_rng(seed, stream, e, which), rows, cols)
+        q, s = draw(_rng(seed, stream, e, which), rows, cols)
         qs[e] = q
         d[e] = s
 
@@ -206,25 +230,28 @@ def make_inputs(cfg: Config | str, seed: int | None = None, n_tokens: int | None
             x = _rng(seed, _S_X).standard_normal((T, K), dtype=np.float32)
             out.update(w=w, x=x, wtype="f32", xtype="f32")
         else:
-            qs, d = draw_q8_0_stack(seed, _S_ROUTED, 0, E, N, K)
-            out.update(w_qs=qs, w_d=d, x=draw_x_bf16(seed, T, K), wtype="q8_0", xtype="bf16")
+            qs, d = draw_q8_0_stack(seed, _S_ROUTED, 0, E, N, K, wtype=cfg.wtype)
+            out.update(w_qs=qs, w_d=d, x=draw_x_bf16(seed, T, K), wtype=cfg.wtype, xtype="bf16")
         return out
     n_embd, n_ff, S = cfg.n_embd, cfg.n_ff, cfg.n_shared
     for name, which, rows, cols in (("gate", _M_GATE, n_ff, n_embd), ("up", _M_UP, n_ff, n_embd),
                                     ("down", _M_DOWN, n_embd, n_ff)):
-        out[name + "_qs"], out[name + "_d"] = draw_q8_0_stack(seed, _S_ROUTED, which, E, rows, cols)
+        out[name + "_qs"], out[name + "_d"] = draw_q8_0_stack(seed, _S_ROUTED, which, E, rows, cols,
+                                                              wtype=cfg.wtype)
         if S:
             out["sh_" + name + "_qs"], out["sh_" + name + "_d"] = draw_q8_0_stack(
-                seed, _S_SHARED, which, S, rows, cols)
+                seed, _S_SHARED, which, S, rows, cols, wtype=cfg.wtype)
     out["x"] = draw_x_bf16(seed, T, n_embd)
-    out.update(wtype="q8_0", xtype="bf16")
+    out.update(wtype=cfg.wtype, xtype="bf16")
     return out
 
 
 def make_custom_ffn(seed: int, E: int, k: int, T: int, n_embd: int, n_ff: int, S: int = 0,
-                    routing: str = "uniform", ids: np.ndarray | None = None) -> dict:
+                    routing: str = "uniform", ids: np.ndarray | None = None,
+                    wtype: str = "q8_0") -> dict:
     """An FFN workload of arbitrary shape (tests), same recipe as the named ones."""
-    cfg = Config("custom", "ffn", E, k, T, n_embd, n_ff, n_shared=S, routing=routing, seed=seed)
+    cfg = Config("custom", "ffn", E, k, T, n_embd, n_ff, n_shared=S, routing=routing, seed=seed,
+                 wtype=wtype)
     return make_inputs(cfg, seed, ids=ids)
 
 

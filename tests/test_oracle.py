@@ -1,7 +1,9 @@
 """Pins for the CPU oracle, each against something other than the oracle itself.
 
   * number formats: hand-derived bit patterns (tests/golden) and numpy's own
-    float16 / float32 decoders over all 65536 patterns;
+    float16 / float32 decoders over all 65536 patterns; MXFP4 (OCP Microscaling v1.0,
+    which the pages name but do not define): the E2M1 value table, the same codes
+    embedded in FP8 E4M3 and decoded by torch, and torch's own E8M0 decoder;
   * row-id maps: exhaustive brute force by a stable sort on tiny inputs, numpy's
     stable argsort on random ones, and the invariants of the maps;
   * mul_mat_id: the dense all-experts product (numpy matmul) masked by ids, plain
@@ -172,8 +174,64 @@ def test_row_ids_configs_invariants(name):
 
 # ------------------------------------------------------------------ mul_mat_id
 
+# FP4 E2M1 magnitudes by code 0..7, from the table of the OCP Microscaling (MX) v1.0
+# specification; codes 8..15 are the same values negated.
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _e8m0_torch(x):
+    """E8M0 bytes -> float64 through torch's float8_e8m0fnu decoder."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8))
+    return t.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+
+
 def _numpy_dequant(qs, d):
+    if qs.dtype == np.uint8:   # MXFP4: low nibble = even column; table lookup; torch E8M0
+        codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(qs.shape[:-1] + (2 * qs.shape[-1],))
+        table = np.array(_E2M1 + tuple(-v for v in _E2M1))
+        return table[codes] * np.repeat(_e8m0_torch(d), 32, axis=-1)
     return qs.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=-1)
+
+
+def test_e2m1_table_and_fp8_embedding():
+    """Every E2M1 code against the format's table (sign included), and against torch's
+    FP8 E4M3 decoder: E2M1 code (s, e, m) is the E4M3 pattern with the same sign, the
+    exponent rebased from bias 1 to bias 7 and the mantissa bit on top of E4M3's three
+    (the subnormal 0.5 is the normal E4M3 number 2^-1)."""
+    import torch
+    for c in range(16):
+        v = oracle.e2m1_to_double(c)
+        mag = _E2M1[c & 7]
+        assert v == (-mag if c & 8 else mag) and math.copysign(1.0, v) == (-1.0 if c & 8 else 1.0)
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e == 0:
+            bits = (s << 7) | ((6 << 3) if m else 0)
+        else:
+            bits = (s << 7) | ((e + 6) << 3) | (m << 2)
+        t = torch.tensor([bits], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+        assert float(t[0]) == v, c
+
+
+def test_e8m0_all_patterns_match_torch():
+    got = np.array([oracle.e8m0_to_double(x) for x in range(256)])
+    ref = _e8m0_torch(np.arange(256))
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[126] == 0.5
+
+
+def test_mxfp4_dequant_layout_and_values():
+    """Byte i of a row holds column 2i (low nibble) and 2i+1 (high nibble); the 32
+    columns of a block share one scale."""
+    q = np.array([[0x21, 0x8F] + [0] * 14 + [0x77] * 16], dtype=np.uint8)   # 1 row, 64 columns
+    d = np.array([[127, 129]], dtype=np.uint8)
+    w = oracle.dequant(q[None], d[None])[0, 0]
+    assert w.shape == (64,)
+    assert (w[0], w[1], w[2], w[3]) == (0.5, 1.0, -6.0, -0.0)
+    assert np.all(w[32:] == 6.0 * 4)     # code 7 = 6, scale 2^(129-127)
+    qs, dd = synth.gen.draw_q8_0_stack(5, 2, 1, 3, 7, 96, wtype="mxfp4")
+    assert np.array_equal(oracle.dequant(qs, dd), _numpy_dequant(qs, dd))
 
 
 def _dense_masked(W, X, ids, B):
@@ -207,6 +265,20 @@ def test_mul_mat_id_q8_vs_dense_masked(B_is_k):
     gw = oracle.mul_mat_id(qs, d, x, "bf16", ids, rw, B)
     refw = np.einsum("tsn,ts->tn", ref, rw.astype(np.float64))
     assert normwise(gw, refw) < 1e-13
+
+
+def test_mul_mat_id_mxfp4_vs_dense_masked():
+    rng = np.random.default_rng(12)
+    E, N, K, T, k = 5, 24, 128, 7, 2
+    qs, d = synth.gen.draw_q8_0_stack(8, 2, 0, E, N, K, wtype="mxfp4")
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    rw = synth.draw_route_w(4, T, k)
+    got = oracle.mul_mat_id(qs, d, x, "bf16", ids, None, 1)
+    ref = _dense_masked(_numpy_dequant(qs, d), synth.bf16_bits_to_f32(x).astype(np.float64), ids, 1)
+    assert normwise(got, ref) < 1e-13
+    gw = oracle.mul_mat_id(qs, d, x, "bf16", ids, rw, 1)
+    assert normwise(gw, np.einsum("tsn,ts->tn", ref, rw.astype(np.float64))) < 1e-13
 
 
 def test_mul_mat_id_f32_tiny_vs_dense_masked():
@@ -277,6 +349,13 @@ def test_ffn_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
     got = oracle.ffn(inp)
     ref = _torch_dense_moe(inp)
     assert normwise(got, ref) < 1e-12
+
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [(4, 2, 5, 64, 96, 1), (8, 4, 3, 128, 64, 0)])
+def test_ffn_mxfp4_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
+    inp = synth.make_custom_ffn(31 + E, E, k, T, n_embd, n_ff, S, wtype="mxfp4")
+    assert inp["gate_qs"].dtype == np.uint8 and inp["gate_qs"].shape == (E, n_ff, n_embd // 2)
+    assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
 
 
 def test_ffn_invalid_ids_contribute_nothing():
