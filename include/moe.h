@@ -18,6 +18,11 @@
  * Layouts (row-major, last index contiguous):
  *   weights  W[n_mat][rows][cols]; Q8_0: int8 qs[n_mat][rows][cols] plus fp16
  *            scales d[n_mat][rows][cols/32], value = d * q (32 values per scale).
+ *            MXFP4 (the format the TensorSharp page lists for GPT-OSS 20B experts;
+ *            defined by the OCP Microscaling v1.0 specification): uint8
+ *            codes[n_mat][rows][cols/2], two FP4 E2M1 codes per byte, column 2i in
+ *            bits 0-3 and column 2i+1 in bits 4-7, plus uint8 E8M0 scales
+ *            x[n_mat][rows][cols/32], value = e2m1(code) * 2^(x - 127) (x = 255: NaN).
  *   ids      int32 [n_tokens][n_used]; route_w float32 [n_tokens][n_used].
  *   src1     [n_tokens][B][K] with B = src1_rows_per_token in {1, n_used}:
  *            slot s of token t reads row t*B + (s mod B).
@@ -47,7 +52,7 @@
  *
  * Limits (MOE_ELIMIT): n_tokens < 2^22 and n_used < 2^10 (the bounds the page
  * above quotes for safe 32-bit packing, section 2.1), n_tokens * n_used < 2^31,
- * n_experts <= 1024, Q8_0 cols % 32 == 0.
+ * n_experts <= 1024, Q8_0 and MXFP4 cols % 32 == 0.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -67,13 +72,15 @@ typedef enum {
     MOE_EHIP = -4        /* a HIP launch failed                                    */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3 } moe_dtype;
 
 /* n_mat stacked matrices of rows x cols. */
 typedef struct {
-    moe_dtype type;     /* MOE_F32 or MOE_Q8_0                                   */
-    const void *data;   /* F32: float[n_mat][rows][cols]; Q8_0: int8 qs[...]     */
-    const void *scales; /* Q8_0: uint16 (fp16) d[n_mat][rows][cols/32]; F32: NULL */
+    moe_dtype type;     /* MOE_F32, MOE_Q8_0 or MOE_MXFP4                        */
+    const void *data;   /* F32: float[n_mat][rows][cols]; Q8_0: int8 qs[...];    */
+                        /* MXFP4: uint8 codes[n_mat][rows][cols/2]               */
+    const void *scales; /* Q8_0: uint16 (fp16) d[n_mat][rows][cols/32];          */
+                        /* MXFP4: uint8 E8M0 x[n_mat][rows][cols/32]; F32: NULL  */
     int64_t n_mat, rows, cols;
 } moe_weights;
 
@@ -118,7 +125,9 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
 /*
  * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
  *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
- *            src1) on the MFMA grouped GEMM or the GEMV path; (F32 w, F32 src1).
+ *            src1) on the MFMA grouped GEMM or the GEMV path; (MXFP4 w, BF16 src1)
+ *            on the GEMV path (n_tokens * n_used <= 64, K <= 4096; other sizes are
+ *            MOE_EINVAL); (F32 w, F32 src1).
  *   src1     device [n_tokens][B][K], B = src1_rows_per_token in {1, n_used}
  *   ids      device int32 [n_tokens][n_used]
  *   route_w  NULL: dst = float32 [n_tokens][n_used][N], dst[t][s] = W_{ids[t][s]} src1_row;
@@ -137,13 +146,15 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
  *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
  *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
  *   sh_gate, sh_up Q8_0 [S][n_ff_sh][n_embd]; sh_down Q8_0 [S][n_embd][n_ff_sh];
+ *             or all of them MXFP4 (GEMV path only: n_tokens * n_used <= 64 and
+ *             n_embd, n_ff, n_ff_sh <= 4096; other sizes are MOE_EINVAL);
  *             all three NULL (or n_mat == 0) = no shared experts; giving only some of
  *             them is MOE_EINVAL.
  *   x         device BF16 [n_tokens][n_embd]; ids, route_w as above.
  *   out       device float32 [n_tokens][n_embd] (overwritten).
  * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights d*q rounded
  * to nearest-even, bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
- * results; GEMV path -- fp32 throughout.
+ * results; GEMV path -- weights exact, fp32 accumulate throughout.
  */
 moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const moe_weights *down,
                          const moe_weights *sh_gate, const moe_weights *sh_up,

@@ -22,7 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ELIMIT, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_Q8_0 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_Q8_0, MOE_MXFP4 = 0, 1, 2, 3
 PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 
 # Every symbol include/moe.h declares.
@@ -105,14 +105,22 @@ def _check(status: int, fn: str):
 @dataclass
 class Weights:
     """Stacked expert matrices on the GPU. Q8_0: ``data`` int8 [n_mat][rows][cols] and
-    ``scales`` float16 (or its uint16 bits) [n_mat][rows][cols/32]; F32: ``data``
-    float32 [n_mat][rows][cols] and ``scales`` None."""
+    ``scales`` float16 (or its uint16 bits) [n_mat][rows][cols/32]; MXFP4: ``data`` uint8
+    [n_mat][rows][cols/2] (two E2M1 codes per byte, even column in the low nibble) and
+    ``scales`` uint8 E8M0 [n_mat][rows][cols/32]; F32: ``data`` float32
+    [n_mat][rows][cols] and ``scales`` None."""
     data: torch.Tensor
     scales: Optional[torch.Tensor] = None
 
     @property
     def type(self) -> int:
-        return MOE_F32 if self.scales is None else MOE_Q8_0
+        if self.scales is None:
+            return MOE_F32
+        return MOE_MXFP4 if self.data.dtype == torch.uint8 else MOE_Q8_0
+
+    @property
+    def cols(self) -> int:
+        return self.data.shape[2] * (2 if self.type == MOE_MXFP4 else 1)
 
     def c(self) -> c_moe_weights:
         d = self.data
@@ -122,7 +130,10 @@ class Weights:
             if d.dtype != torch.float32:
                 raise ValueError("float weights must be float32")
         else:
-            if d.dtype != torch.int8 or self.scales.element_size() != 2:
+            if d.dtype == torch.uint8:
+                if self.scales.dtype != torch.uint8:
+                    raise ValueError("MXFP4 weights: uint8 codes with uint8 E8M0 scales")
+            elif d.dtype != torch.int8 or self.scales.element_size() != 2:
                 raise ValueError("Q8_0 weights: int8 qs with 16-bit scales")
             if not self.scales.is_contiguous():
                 raise ValueError("scales must be contiguous")
@@ -130,7 +141,7 @@ class Weights:
             raise ValueError("weights must be contiguous")
         return c_moe_weights(self.type, d.data_ptr(),
                              None if self.scales is None else self.scales.data_ptr(),
-                             d.shape[0], d.shape[1], d.shape[2])
+                             d.shape[0], d.shape[1], self.cols)
 
 
 def _options(path: int = PATH_AUTO, tau: float = 0.0, events: Optional[Sequence[int]] = None):
@@ -289,10 +300,14 @@ def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, id
 
 
 def weights_from_numpy(qs_or_w, d=None, device="cuda") -> Weights:
-    """Upload numpy weights (from ``synth``) as a Weights pair."""
+    """Upload numpy weights (from ``synth``) as a Weights pair: float32; Q8_0 (int8 qs,
+    fp16 scales); or MXFP4 (uint8 codes, uint8 E8M0 scales)."""
     import numpy as np
     if d is None:
         return Weights(torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.float32)).to(device))
+    if np.asarray(qs_or_w).dtype == np.uint8:
+        q = torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.uint8)).to(device)
+        return Weights(q, torch.from_numpy(np.ascontiguousarray(d, dtype=np.uint8)).to(device))
     q = torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.int8)).to(device)
     s = torch.from_numpy(np.ascontiguousarray(np.asarray(d).view(np.int16))).to(device)
     return Weights(q, s)

@@ -24,6 +24,8 @@
 //     staged in LDS) takes over.
 //   * Results are written per slot; the fixed-order weighted reduction runs in the
 //     reduce kernel.
+#include <type_traits>
+
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -103,6 +105,99 @@ __device__ __forceinline__ float dot16(const i32x4& q, const f32x4& x0, const f3
     s = fmaf((float)(int8_t)(q[3] >> 16), x3[2], s);
     s = fmaf((float)(int8_t)(q[3] >> 24), x3[3], s);
     return s;
+}
+
+// Weight formats of the wave-level GEMV. In both, lane l of K piece i reads bytes
+// 1024*i + 16*l .. +15 of a weight row: 16 Q8_0 values (k = 1024*i + 16*l ..) or 32 MXFP4
+// values (k = 2048*i + 32*l .., exactly one block of 32 with one scale byte).
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> {   // Q8_0: int8 codes, one fp16 scale per 32
+    static constexpr int VPL = 16, PIECE = 1024, SB = 2;
+};
+template <> struct Fmt<1> {   // MXFP4: two E2M1 codes per byte (even column low), one E8M0 byte per 32
+    static constexpr int VPL = 32, PIECE = 2048, SB = 1;
+};
+
+// E8M0 scale byte -> 2^(x - 127) (x = 0 is the subnormal 2^-127; x = 255 is NaN).
+__device__ __forceinline__ float e8m0_to_float(uint32_t x) {
+    const uint32_t bits = x == 0 ? 0x00400000u : (x == 255 ? 0x7fc00000u : x << 23);
+    return __builtin_bit_cast(float, bits);
+}
+
+// 32 MXFP4 codes (16 bytes) dotted with 32 floats. The hardware conversion turns the
+// two codes of a byte into exact fp32 values (scale 1; the low nibble is the first);
+// the caller multiplies the sum by the block's power-of-two scale.
+__device__ __forceinline__ float dot32_fp4(const i32x4& q, const float* x) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const uint32_t u = (uint32_t)q[w];
+        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 0);
+        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 1);
+        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 2);
+        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 3);
+        s = fmaf(v0[0], x[8 * w + 0], s);
+        s = fmaf(v0[1], x[8 * w + 1], s);
+        s = fmaf(v1[0], x[8 * w + 2], s);
+        s = fmaf(v1[1], x[8 * w + 3], s);
+        s = fmaf(v2[0], x[8 * w + 4], s);
+        s = fmaf(v2[1], x[8 * w + 5], s);
+        s = fmaf(v3[0], x[8 * w + 6], s);
+        s = fmaf(v3[1], x[8 * w + 7], s);
+    }
+    return s;
+}
+
+// 32 MXFP4 codes (16 bytes) dotted with 32 bf16 activations held as 16 packed pairs (raw
+// dwords): each byte's two codes become an exact bf16 pair and one dot2 instruction
+// multiplies it with the matching activation pair, accumulating in fp32. The caller
+// multiplies the sum by the block's scale. (The pairs are kept in integer registers: held
+// in float slots and bit-cast to bf16 pairs, the compiler merged distinct pairs into one.)
+__device__ __forceinline__ float dot32_fp4_bf16(const i32x4& q, const uint32_t* xv) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const uint32_t u = (uint32_t)q[w];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 0),
+                                            __builtin_bit_cast(bf16x2, xv[4 * w + 0]), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 1),
+                                            __builtin_bit_cast(bf16x2, xv[4 * w + 1]), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 2),
+                                            __builtin_bit_cast(bf16x2, xv[4 * w + 2]), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 3),
+                                            __builtin_bit_cast(bf16x2, xv[4 * w + 3]), s, false);
+    }
+    return s;
+}
+
+// Activations of one lane's piece in registers: MXFP4 with bf16 activations keeps them as
+// packed pairs (VPL / 2 dwords); otherwise VPL exact fp32 values.
+template <int FMT, bool XBF16>
+struct XRegs {
+    static constexpr bool PACKED = FMT == 1 && XBF16;
+    static constexpr int N = PACKED ? Fmt<FMT>::VPL / 2 : Fmt<FMT>::VPL;
+    using T = std::conditional_t<PACKED, uint32_t, float>;
+};
+
+// One lane's share of a row piece: acc + scale * (codes q . activations xv), with one
+// rounding for the scaling add (fma). sb holds the raw scale bits (fp16 for Q8_0, E8M0
+// for MXFP4); pieces past K get a zero scale.
+template <int FMT, bool PACKED, class XT>
+__device__ __forceinline__ float piece_fma(const i32x4& q, const XT* xv, uint32_t sb, bool in, float acc) {
+    if constexpr (PACKED) {
+        const float sc = in ? e8m0_to_float(sb & 255u) : 0.f;
+        return fmaf(sc, dot32_fp4_bf16(q, xv), acc);
+    } else if constexpr (FMT == 0) {
+        const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
+        return fmaf(dd, dot16(q, f32x4{xv[0], xv[1], xv[2], xv[3]}, f32x4{xv[4], xv[5], xv[6], xv[7]},
+                              f32x4{xv[8], xv[9], xv[10], xv[11]}, f32x4{xv[12], xv[13], xv[14], xv[15]}),
+                    acc);
+    } else {
+        const float sc = in ? e8m0_to_float(sb & 255u) : 0.f;
+        return fmaf(sc, dot32_fp4(q, xv), acc);
+    }
 }
 
 // Block = 4 waves; it owns kR rows (row pairs in gate/up mode) of one expert and
@@ -377,14 +472,16 @@ __device__ __forceinline__ bool wave_unit(const DecArgs& a, int gw, int R, bool&
 // needs few registers and keeps two or more waves per SIMD, which beats staging through
 // LDS for single-token decode. emit(idx, n, res) runs on lane 63; idx is the slot t*k+s
 // (routed) or the token (shared).
-template <int MODE, int P, bool XBF16, int NIT, class Emit>
+template <int MODE, int P, bool XBF16, int NIT, int FMT, class Emit>
 __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, uint64_t smask, int cnt,
                                           int n_lo, int n_hi, Emit&& emit) {
     constexpr int M = MODE == 1 ? 2 : 1;
+    using F = Fmt<FMT>;
     const int lane = threadIdx.x & 63;
     const DecWeights& W = routed ? a.rw : a.sw;
     const int N = W.N, K = W.K;
     const int64_t KB = K >> 5;
+    const int64_t RB = (int64_t)K * 16 / F::VPL;   // bytes per weight row
     const void* src = routed ? a.act : a.sact;
     auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
     auto src_row = [&](int p) -> int64_t {
@@ -395,20 +492,20 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
         }
         return (int64_t)e * a.sact_jstride + p;
     };
-    // lane's K pieces: k = 1024*i + 16*lane; pieces past K read column 0 (a valid
-    // address) and get a zero scale
+    // lane's K pieces: first value k = PIECE*i + VPL*lane (bytes 1024*i + 16*lane of the
+    // row); pieces past K read column 0 (a valid address) and get a zero scale
     int kc[NIT];
     bool kin[NIT];
 #pragma unroll
     for (int i = 0; i < NIT; i++) {
-        const int k = (i << 10) + (lane << 4);
+        const int k = i * F::PIECE + lane * F::VPL;
         kin[i] = k < K;
         kc[i] = kin[i] ? k : 0;
     }
-    const int8_t* q1 = W.qs1 + (int64_t)e * N * K;
-    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * K : q1;
-    const uint16_t* d1 = W.d1 + (int64_t)e * N * KB;
-    const uint16_t* d2 = MODE == 1 ? W.d2 + (int64_t)e * N * KB : d1;
+    const int8_t* q1 = W.qs1 + (int64_t)e * N * RB;
+    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * RB : q1;
+    const uint8_t* d1 = (const uint8_t*)W.d1 + (int64_t)e * N * KB * F::SB;
+    const uint8_t* d2 = MODE == 1 ? (const uint8_t*)W.d2 + (int64_t)e * N * KB * F::SB : d1;
 
     // one weight row (pair): NIT 16-byte pieces per matrix and their scales
     struct Row {
@@ -418,13 +515,15 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
     auto load_row = [&](int n, Row& w) {
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            const int8_t* qr = (m == 0 ? q1 : q2) + (int64_t)n * K;
-            const uint16_t* dr = (m == 0 ? d1 : d2) + (int64_t)n * KB;
+            const int8_t* qr = (m == 0 ? q1 : q2) + (int64_t)n * RB;
+            const uint8_t* dr = (m == 0 ? d1 : d2) + (int64_t)n * KB * F::SB;
 #pragma unroll
             for (int i = 0; i < NIT; i++) {
-                if constexpr (kDecWeightsNT) w.q[m][i] = __builtin_nontemporal_load((const i32x4*)(qr + kc[i]));
-                else w.q[m][i] = *(const i32x4*)(qr + kc[i]);
-                w.d[m][i] = dr[kc[i] >> 5];
+                const i32x4* qp = (const i32x4*)(qr + kc[i] * 16 / F::VPL);
+                if constexpr (kDecWeightsNT) w.q[m][i] = __builtin_nontemporal_load(qp);
+                else w.q[m][i] = *qp;
+                if constexpr (FMT == 0) w.d[m][i] = *(const uint16_t*)(dr + 2 * (kc[i] >> 5));
+                else w.d[m][i] = dr[kc[i] >> 5];
             }
         }
     };
@@ -432,26 +531,36 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
     for (int p0 = 0; p0 < cnt; p0 += P) {
         const int pc = min(P, cnt - p0);
         // activations of this pass's slots, exact fp32
-        float x[P][NIT][16];
+        using XR = XRegs<FMT, XBF16>;
+        typename XR::T x[P][NIT][XR::N];
 #pragma unroll
         for (int p = 0; p < P; p++) {
             const int64_t row = src_row(p0 + min(p, pc - 1));
 #pragma unroll
             for (int i = 0; i < NIT; i++) {
-                if constexpr (XBF16) {
+                if constexpr (XR::PACKED) {
                     const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
-                    const i32x4 r0 = *(const i32x4*)(xp);
-                    const i32x4 r1 = *(const i32x4*)(xp + 8);
 #pragma unroll
-                    for (int c = 0; c < 8; c++) {
-                        const uint32_t w = (uint32_t)(c < 4 ? r0[c] : r1[c - 4]);
+                    for (int h = 0; h < F::VPL / 8; h++) {
+                        const i32x4 r = *(const i32x4*)(xp + 8 * h);
+#pragma unroll
+                        for (int c = 0; c < 4; c++) x[p][i][4 * h + c] = (uint32_t)r[c];
+                    }
+                } else if constexpr (XBF16) {
+                    const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
+                    i32x4 r[F::VPL / 8];
+#pragma unroll
+                    for (int h = 0; h < F::VPL / 8; h++) r[h] = *(const i32x4*)(xp + 8 * h);
+#pragma unroll
+                    for (int c = 0; c < F::VPL / 2; c++) {
+                        const uint32_t w = (uint32_t)r[c >> 2][c & 3];
                         x[p][i][2 * c] = __builtin_bit_cast(float, w << 16);
                         x[p][i][2 * c + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
                     }
                 } else {
                     const float* xp = (const float*)src + row * K + kc[i];
 #pragma unroll
-                    for (int c = 0; c < 4; c++) {
+                    for (int c = 0; c < F::VPL / 4; c++) {
                         const f32x4 v = *(const f32x4*)(xp + 4 * c);
 #pragma unroll
                         for (int j = 0; j < 4; j++) x[p][i][4 * c + j] = v[j];
@@ -468,19 +577,10 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
 #pragma unroll
             for (int i = 0; i < NIT; i++)
 #pragma unroll
-                for (int m = 0; m < M; m++) {
-                    // lanes past K add 0 through a zero scale instead of branching
-                    const float dd = kin[i] ? half_bits_to_float((uint16_t)w.d[m][i]) : 0.f;
+                for (int m = 0; m < M; m++)
 #pragma unroll
-                    for (int p = 0; p < P; p++) {
-                        const float* xv = x[p][i];
-                        acc[m][p] = fmaf(dd, dot16(w.q[m][i], f32x4{xv[0], xv[1], xv[2], xv[3]},
-                                                   f32x4{xv[4], xv[5], xv[6], xv[7]},
-                                                   f32x4{xv[8], xv[9], xv[10], xv[11]},
-                                                   f32x4{xv[12], xv[13], xv[14], xv[15]}),
-                                         acc[m][p]);
-                    }
-                }
+                    for (int p = 0; p < P; p++)   // lanes past K add 0 through a zero scale
+                        acc[m][p] = piece_fma<FMT, XR::PACKED>(w.q[m][i], x[p][i], w.d[m][i], kin[i], acc[m][p]);
 #pragma unroll
             for (int p = 0; p < P; p++) {
                 if (p >= pc) continue;
@@ -519,14 +619,14 @@ struct EmitGlobal {
 };
 
 // One wave per unit, register-staged rows.
-template <int MODE, int P, bool XBF16, int NIT>
+template <int MODE, int P, bool XBF16, int NIT, int FMT>
 __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
     const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
     bool routed;
     int e, cnt, n_lo, n_hi;
     uint64_t smask;
     if (!wave_unit(a, gw, a.rows_per_block, routed, e, smask, cnt, n_lo, n_hi)) return;
-    unit_regs<MODE, P, XBF16, NIT>(a, routed, e, smask, cnt, n_lo, n_hi,
+    unit_regs<MODE, P, XBF16, NIT, FMT>(a, routed, e, smask, cnt, n_lo, n_hi,
                                    EmitGlobal{a, routed, e, routed ? a.rw.N : a.sw.N});
 }
 
@@ -573,10 +673,11 @@ struct StreamSlot {
 // Slot layout per matrix: NIT KB of int8 (piece i at 1024*i, lane l's 16 bytes at
 // 16*l, the row's byte k at offset k) and 256 bytes for the row's fp16 scales (the
 // aligned dwords holding them; the row's first scale sits at byte (row offset & 3)).
-template <int MODE, int P, bool XBF16, int NIT, class Emit>
+template <int MODE, int P, bool XBF16, int NIT, int FMT, class Emit>
 __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e, uint64_t smask,
                                             int cnt, int n_lo, int n_hi, uint8_t* ring, Emit&& emit) {
     constexpr int M = MODE == 1 ? 2 : 1;
+    using F = Fmt<FMT>;
     using G = StreamSlot<MODE, NIT>;
     constexpr int MAT = G::MAT, SLOT = G::BYTES, NR = G::NR;
     constexpr int D = M * (NIT + 1);   // copies per row (pair)
@@ -586,6 +687,7 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
     const int N = W.N, K = W.K;
     const int nrows = n_hi - n_lo;
     const int KB = K >> 5;
+    const int RB = K * 16 / F::VPL;   // bytes per weight row
     const void* src = routed ? a.act : a.sact;
     auto slot_of = [&](int p) -> int { return routed ? nth_set_bit(smask, p) : p; };
     auto src_row = [&](int p) -> int64_t {
@@ -596,22 +698,23 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
         }
         return (int64_t)e * a.sact_jstride + p;
     };
-    // lane's K pieces: k = 1024*i + 16*lane. Pieces past K copy the row's last 16
-    // bytes (a valid address), read column 0 of the activations and get a zero scale.
+    // lane's K pieces: first value k = PIECE*i + VPL*lane, bytes 1024*i + 16*lane of the
+    // row. Pieces past K copy the row's last 16 bytes (a valid address), read column 0 of
+    // the activations and get a zero scale.
     int kc[NIT];
     bool kin[NIT];
     uint32_t qoff[NIT];
 #pragma unroll
     for (int i = 0; i < NIT; i++) {
-        const int k = (i << 10) + (lane << 4);
+        const int k = i * F::PIECE + lane * F::VPL;
         kin[i] = k < K;
         kc[i] = kin[i] ? k : 0;
-        qoff[i] = (uint32_t)(kin[i] ? k : K - 16);
+        qoff[i] = (uint32_t)(kin[i] ? (i << 10) + (lane << 4) : RB - 16);
     }
-    const int8_t* q1 = W.qs1 + (int64_t)e * N * K;
-    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * K : q1;
-    const uint8_t* d1 = (const uint8_t*)(W.d1 + (int64_t)e * N * KB);
-    const uint8_t* d2 = MODE == 1 ? (const uint8_t*)(W.d2 + (int64_t)e * N * KB) : d1;
+    const int8_t* q1 = W.qs1 + (int64_t)e * N * RB;
+    const int8_t* q2 = MODE == 1 ? W.qs2 + (int64_t)e * N * RB : q1;
+    const uint8_t* d1 = (const uint8_t*)W.d1 + (int64_t)e * N * KB * F::SB;
+    const uint8_t* d2 = MODE == 1 ? (const uint8_t*)W.d2 + (int64_t)e * N * KB * F::SB : d1;
     const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
 
     // copies of row n into slot j: per matrix NIT 16-byte pieces and one word per lane
@@ -620,12 +723,12 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
 #pragma unroll
         for (int m = 0; m < M; m++) {
             const uint32_t dst = ring_lds + (uint32_t)(j * SLOT + m * MAT);
-            const int8_t* qrow = (const int8_t*)uniform_ptr((m == 0 ? q1 : q2) + (int64_t)n * K);
+            const int8_t* qrow = (const int8_t*)uniform_ptr((m == 0 ? q1 : q2) + (int64_t)n * RB);
 #pragma unroll
             for (int i = 0; i < NIT; i++) dma16<kDecWeightsNT>(qrow, qoff[i], dst + i * 1024);
-            const uintptr_t sa = (uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * 2);  // first scale
+            const uintptr_t sa = (uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * F::SB);  // first scale
             const uint8_t* srow = (const uint8_t*)uniform_ptr((const void*)(sa & ~(uintptr_t)3));
-            const int last = ((int)(sa & 3) + 2 * KB - 1) >> 2;
+            const int last = ((int)(sa & 3) + F::SB * KB - 1) >> 2;
             dma4(srow, (uint32_t)(min(lane, last) * 4), dst + NIT * 1024);
         }
     };
@@ -635,26 +738,36 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
     for (int p0 = 0; p0 < cnt; p0 += P) {
         const int pc = min(P, cnt - p0);
         // activations of this pass's slots, exact fp32
-        float x[P][NIT][16];
+        using XR = XRegs<FMT, XBF16>;
+        typename XR::T x[P][NIT][XR::N];
 #pragma unroll
         for (int p = 0; p < P; p++) {
             const int64_t row = src_row(p0 + min(p, pc - 1));
 #pragma unroll
             for (int i = 0; i < NIT; i++) {
-                if constexpr (XBF16) {
+                if constexpr (XR::PACKED) {
                     const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
-                    const i32x4 r0 = *(const i32x4*)(xp);
-                    const i32x4 r1 = *(const i32x4*)(xp + 8);
 #pragma unroll
-                    for (int c = 0; c < 8; c++) {
-                        const uint32_t w = (uint32_t)(c < 4 ? r0[c] : r1[c - 4]);
+                    for (int h = 0; h < F::VPL / 8; h++) {
+                        const i32x4 r = *(const i32x4*)(xp + 8 * h);
+#pragma unroll
+                        for (int c = 0; c < 4; c++) x[p][i][4 * h + c] = (uint32_t)r[c];
+                    }
+                } else if constexpr (XBF16) {
+                    const uint16_t* xp = (const uint16_t*)src + row * K + kc[i];
+                    i32x4 r[F::VPL / 8];
+#pragma unroll
+                    for (int h = 0; h < F::VPL / 8; h++) r[h] = *(const i32x4*)(xp + 8 * h);
+#pragma unroll
+                    for (int c = 0; c < F::VPL / 2; c++) {
+                        const uint32_t w = (uint32_t)r[c >> 2][c & 3];
                         x[p][i][2 * c] = __builtin_bit_cast(float, w << 16);
                         x[p][i][2 * c + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
                     }
                 } else {
                     const float* xp = (const float*)src + row * K + kc[i];
 #pragma unroll
-                    for (int c = 0; c < 4; c++) {
+                    for (int c = 0; c < F::VPL / 4; c++) {
                         const f32x4 v = *(const f32x4*)(xp + 4 * c);
 #pragma unroll
                         for (int j = 0; j < 4; j++) x[p][i][4 * c + j] = v[j];
@@ -674,20 +787,13 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
 #pragma unroll
                 for (int m = 0; m < M; m++) {
                     const uint8_t* mp = sl + m * MAT;
-                    const int s0 = (int)((uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * 2) & 3);
+                    const int s0 = (int)((uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * F::SB) & 3);
                     const i32x4 q = *(const i32x4*)(mp + (i << 10) + (lane << 4));
-                    const uint16_t db = *(const uint16_t*)(mp + NIT * 1024 + s0 + 2 * (kc[i] >> 5));
-                    // lanes past K add 0 through a zero scale instead of branching
-                    const float dd = kin[i] ? half_bits_to_float(db) : 0.f;
+                    const uint8_t* sp = mp + NIT * 1024 + s0 + F::SB * (kc[i] >> 5);
+                    const uint32_t sb = FMT == 0 ? (uint32_t)*(const uint16_t*)sp : (uint32_t)*sp;
 #pragma unroll
-                    for (int p = 0; p < P; p++) {
-                        const float* xv = x[p][i];
-                        acc[m][p] = fmaf(dd, dot16(q, f32x4{xv[0], xv[1], xv[2], xv[3]},
-                                                   f32x4{xv[4], xv[5], xv[6], xv[7]},
-                                                   f32x4{xv[8], xv[9], xv[10], xv[11]},
-                                                   f32x4{xv[12], xv[13], xv[14], xv[15]}),
-                                         acc[m][p]);
-                    }
+                    for (int p = 0; p < P; p++)   // lanes past K add 0 through a zero scale
+                        acc[m][p] = piece_fma<FMT, XR::PACKED>(q, x[p][i], sb, kin[i], acc[m][p]);
                 }
 #pragma unroll
             for (int p = 0; p < P; p++) {
@@ -713,7 +819,7 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
 }
 
 // One wave per unit, rows streamed through a per-wave LDS ring.
-template <int MODE, int P, bool XBF16, int NIT>
+template <int MODE, int P, bool XBF16, int NIT, int FMT>
 __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) {
     using G = StreamSlot<MODE, NIT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -723,7 +829,7 @@ __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) 
     uint64_t smask;
     if (!wave_unit(a, gw, a.rows_per_block, routed, e, smask, cnt, n_lo, n_hi)) return;
     uint8_t* ring = smem + (threadIdx.x >> 6) * (G::NR * G::BYTES);
-    unit_stream<MODE, P, XBF16, NIT>(a, routed, e, smask, cnt, n_lo, n_hi, ring,
+    unit_stream<MODE, P, XBF16, NIT, FMT>(a, routed, e, smask, cnt, n_lo, n_hi, ring,
                                      EmitGlobal{a, routed, e, routed ? a.rw.N : a.sw.N});
 }
 
@@ -738,7 +844,7 @@ __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) 
 constexpr int kFuseRows = 16;    // R, at most
 constexpr int kFuseSlots = 64;   // routed slots, and shared (expert, token) pairs, at most
 
-template <int P, bool XBF16, int NIT, bool STREAM>
+template <int P, bool XBF16, int NIT, bool STREAM, int FMT>
 __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_reduce(DecArgs a) {
     using G = StreamSlot<0, NIT>;
     __shared__ float s_part[kFuseSlots * kFuseRows];   // routed slot s, row r at s*kFuseRows + r
@@ -758,16 +864,16 @@ __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_
             const uint64_t sm = __ballot(v == e);
             auto emit = [&](int slot, int n, float res) { s_part[slot * kFuseRows + (n - n_lo)] = res; };
             if constexpr (STREAM)
-                unit_stream<0, P, XBF16, NIT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, ring, emit);
+                unit_stream<0, P, XBF16, NIT, FMT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, ring, emit);
             else
-                unit_regs<0, P, XBF16, NIT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, emit);
+                unit_regs<0, P, XBF16, NIT, FMT>(a, true, e, sm, __popcll(sm), n_lo, n_hi, emit);
         } else {
             const int j = u - D;
             auto emit = [&](int t, int n, float res) { s_shp[(j * a.T + t) * kFuseRows + (n - n_lo)] = res; };
             if constexpr (STREAM)
-                unit_stream<0, P, XBF16, NIT>(a, false, j, 0, a.T, n_lo, n_hi, ring, emit);
+                unit_stream<0, P, XBF16, NIT, FMT>(a, false, j, 0, a.T, n_lo, n_hi, ring, emit);
             else
-                unit_regs<0, P, XBF16, NIT>(a, false, j, 0, a.T, n_lo, n_hi, emit);
+                unit_regs<0, P, XBF16, NIT, FMT>(a, false, j, 0, a.T, n_lo, n_hi, emit);
         }
     }
     __syncthreads();
@@ -834,42 +940,42 @@ hipError_t set_stream_lds(const void* kern, int lds, bool& done) {
     return e;
 }
 
-template <int MODE, int P, bool XBF16, int NIT>
+template <int MODE, int P, bool XBF16, int NIT, int FMT>
 hipError_t launch_stream(DecArgs a, hipStream_t st) {
     constexpr int lds = StreamSlot<MODE, NIT>::LDS;
     static_assert(lds <= 150 * 1024, "ring exceeds LDS");
     static int cache = 0;
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
-    if (hipError_t e = set_stream_lds<true>((const void*)k_decode_stream<MODE, P, XBF16, NIT>, lds, attr_set))
+    if (hipError_t e = set_stream_lds<true>((const void*)k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, attr_set))
         return e;
-    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_stream<MODE, P, XBF16, NIT>, lds, cache));
+    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, cache));
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
     if (nw <= 0) return hipSuccess;
     const int grid = (nw + 3) / 4;
-    k_decode_stream<MODE, P, XBF16, NIT><<<grid, 256, lds, st>>>(a);
+    k_decode_stream<MODE, P, XBF16, NIT, FMT><<<grid, 256, lds, st>>>(a);
     return hipGetLastError();
 }
 
-template <int MODE, bool XBF16, int NIT>
+template <int MODE, bool XBF16, int NIT, int FMT>
 hipError_t launch_regs(DecArgs a, hipStream_t st) {
     static int cache = 0;
-    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_wave<MODE, 1, XBF16, NIT>, 0, cache));
+    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_wave<MODE, 1, XBF16, NIT, FMT>, 0, cache));
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
     if (nw <= 0) return hipSuccess;
-    k_decode_wave<MODE, 1, XBF16, NIT><<<(nw + 3) / 4, 256, 0, st>>>(a);
+    k_decode_wave<MODE, 1, XBF16, NIT, FMT><<<(nw + 3) / 4, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
-template <bool XBF16, int NIT, bool STREAM>
+template <bool XBF16, int NIT, bool STREAM, int FMT>
 hipError_t launch_down_reduce(DecArgs a, hipStream_t st) {
     constexpr int lds = STREAM ? StreamSlot<0, NIT>::LDS : 0;
     constexpr int P = STREAM ? 2 : 1;
     static bool attr_set = false;
-    if (hipError_t e = set_stream_lds<STREAM>((const void*)k_decode_down_reduce<P, XBF16, NIT, STREAM>,
+    if (hipError_t e = set_stream_lds<STREAM>((const void*)k_decode_down_reduce<P, XBF16, NIT, STREAM, FMT>,
                                               lds, attr_set))
         return e;
     const int N = a.rw.N;
@@ -878,29 +984,46 @@ hipError_t launch_down_reduce(DecArgs a, hipStream_t st) {
     a.rows_per_block = R;
     const int grid = (N + R - 1) / R;
     if (grid <= 0) return hipSuccess;
-    k_decode_down_reduce<P, XBF16, NIT, STREAM><<<grid, 256, lds, st>>>(a);
+    k_decode_down_reduce<P, XBF16, NIT, STREAM, FMT><<<grid, 256, lds, st>>>(a);
     return hipGetLastError();
 }
 
 // One activation row per pass: register staging. Two per pass: the two rows' fp32
 // activations take too many registers to also hold rows in flight, so the rows stream
 // through LDS.
-template <int MODE, bool XBF16, int NIT>
+template <int MODE, bool XBF16, int NIT, int FMT>
 hipError_t launch_wave_nit(const DecArgs& a, int slots_max, bool fuse, hipStream_t st) {
     if constexpr (MODE == 0) {
-        if (fuse) return slots_max <= 1 ? launch_down_reduce<XBF16, NIT, false>(a, st)
-                                        : launch_down_reduce<XBF16, NIT, true>(a, st);
+        if (fuse) return slots_max <= 1 ? launch_down_reduce<XBF16, NIT, false, FMT>(a, st)
+                                        : launch_down_reduce<XBF16, NIT, true, FMT>(a, st);
     }
-    return slots_max <= 1 ? launch_regs<MODE, XBF16, NIT>(a, st) : launch_stream<MODE, 2, XBF16, NIT>(a, st);
+    return slots_max <= 1 ? launch_regs<MODE, XBF16, NIT, FMT>(a, st)
+                          : launch_stream<MODE, 2, XBF16, NIT, FMT>(a, st);
 }
 
-template <int MODE, bool XBF16>
+// K pieces per lane: ceil(K / 1024) for Q8_0, ceil(K / 2048) for MXFP4 (K <= 4096).
+template <int MODE, bool XBF16, int FMT>
 hipError_t launch_wave(const DecArgs& a, int slots_max, bool fuse, hipStream_t st) {
     const int kmax = max(a.rw.K, a.sw.n_mat > 0 ? a.sw.K : 0);
-    if (kmax <= 1024) return launch_wave_nit<MODE, XBF16, 1>(a, slots_max, fuse, st);
-    if (kmax <= 2048) return launch_wave_nit<MODE, XBF16, 2>(a, slots_max, fuse, st);
-    if (kmax <= 3072) return launch_wave_nit<MODE, XBF16, 3>(a, slots_max, fuse, st);
-    return launch_wave_nit<MODE, XBF16, 4>(a, slots_max, fuse, st);
+    const int pieces = (kmax + Fmt<FMT>::PIECE - 1) / Fmt<FMT>::PIECE;
+    if constexpr (FMT == 1) {
+        return pieces <= 1 ? launch_wave_nit<MODE, XBF16, 1, FMT>(a, slots_max, fuse, st)
+                           : launch_wave_nit<MODE, XBF16, 2, FMT>(a, slots_max, fuse, st);
+    } else {
+        if (pieces <= 1) return launch_wave_nit<MODE, XBF16, 1, FMT>(a, slots_max, fuse, st);
+        if (pieces <= 2) return launch_wave_nit<MODE, XBF16, 2, FMT>(a, slots_max, fuse, st);
+        if (pieces <= 3) return launch_wave_nit<MODE, XBF16, 3, FMT>(a, slots_max, fuse, st);
+        return launch_wave_nit<MODE, XBF16, 4, FMT>(a, slots_max, fuse, st);
+    }
+}
+
+// Gate/up mode always reads the bf16 layer input; down mode reads the fp32 h (or, for
+// mul_mat_id, bf16 src1).
+template <int FMT>
+hipError_t launch_wave_fmt(const DecArgs& a, int slots, bool fuse, hipStream_t st) {
+    if (a.mode == 1) return a.act_type == 1 ? launch_wave<1, true, FMT>(a, slots, false, st) : hipErrorInvalidValue;
+    return a.act_type == 1 ? launch_wave<0, true, FMT>(a, slots, fuse, st)
+                           : launch_wave<0, false, FMT>(a, slots, fuse, st);
 }
 
 }  // namespace
@@ -919,12 +1042,10 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced) {
                           a.d_max + S <= 4 * MOE_DEC_FUSE_UPW;
         if (same_type) {
             if (reduced) *reduced = fuse;
-            if (a.mode == 1) return a.act_type == 1 ? launch_wave<1, true>(a, slots, false, st)
-                                                    : launch_wave<1, false>(a, slots, false, st);
-            return a.act_type == 1 ? launch_wave<0, true>(a, slots, fuse, st)
-                                   : launch_wave<0, false>(a, slots, fuse, st);
+            return a.rw.fmt == 1 ? launch_wave_fmt<1>(a, slots, fuse, st) : launch_wave_fmt<0>(a, slots, fuse, st);
         }
     }
+    if (a.rw.fmt != 0) return hipErrorInvalidValue;   // MXFP4: the wave kernels only
     const int nb_r = a.d_max * ((a.rw.N + kR - 1) / kR);
     const int nb_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kR - 1) / kR) : 0;
     const int grid = nb_r + nb_s;

@@ -91,9 +91,11 @@ moe_status check_weights(const moe_weights* w, const char* name, bool allow_f32)
         return fail(MOE_EINVAL, "%s: sizes must be > 0", name);
     if (w->rows > INT32_MAX || w->cols > INT32_MAX)
         return fail(MOE_ELIMIT, "%s: rows and cols must fit in int32", name);
-    if (w->type == MOE_Q8_0) {
-        if (!w->scales) return fail(MOE_EINVAL, "%s: Q8_0 scales are NULL", name);
-        if (w->cols % 32) return fail(MOE_ELIMIT, "%s: Q8_0 needs cols %% 32 == 0 (got %lld)", name, (long long)w->cols);
+    if (w->type == MOE_Q8_0 || w->type == MOE_MXFP4) {
+        const char* fmt = w->type == MOE_Q8_0 ? "Q8_0" : "MXFP4";
+        if (!w->scales) return fail(MOE_EINVAL, "%s: %s scales are NULL", name, fmt);
+        if (w->cols % 32)
+            return fail(MOE_ELIMIT, "%s: %s needs cols %% 32 == 0 (got %lld)", name, fmt, (long long)w->cols);
     } else if (w->type == MOE_F32) {
         if (!allow_f32) return fail(MOE_EINVAL, "%s: float32 weights are not supported here", name);
     } else {
@@ -117,6 +119,18 @@ int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_op
     }
     if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
     return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
+}
+
+// MXFP4 experts run on the wave-level GEMV only: n_tokens * n_used <= 64 and every
+// activation width <= 4096.
+int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4, const moe_options* o) {
+    if (!fp4) return select_path(T, k, E, act_width, o);
+    const int32_t force = o ? o->path : 0;
+    if (force < 0 || force > 2) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
+    if (force == 1) return fail(MOE_EINVAL, "MXFP4 experts have no grouped GEMM path");
+    if (T * (int64_t)k > 64 || act_width > 4096)
+        return fail(MOE_EINVAL, "MXFP4 experts need n_tokens*n_used <= 64 and widths <= 4096 (the GEMV path)");
+    return 2;
 }
 
 int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n : E); }
@@ -153,6 +167,7 @@ RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, int tile_m) 
 struct FfnDims {
     int64_t T;
     int32_t k, E, n_embd, n_ff, S, n_ff_sh;
+    bool fp4;   // MXFP4 experts (else Q8_0)
 };
 
 struct FfnPlan {
@@ -209,6 +224,8 @@ moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const mo
     if ((s = check_weights(down, "down", false))) return s;
     if ((s = check_experts(gate->n_mat))) return s;
     if (x_type != MOE_BF16) return fail(MOE_EINVAL, "x must be BF16 (Q8_0 experts run bf16 activations)");
+    if (up->type != gate->type || down->type != gate->type)
+        return fail(MOE_EINVAL, "gate, up and down must have the same weight type");
     if (up->n_mat != gate->n_mat || down->n_mat != gate->n_mat || up->rows != gate->rows ||
         up->cols != gate->cols || down->rows != gate->cols || down->cols != gate->rows)
         return fail(MOE_EINVAL, "gate/up must be [E][n_ff][n_embd] and down [E][n_embd][n_ff]");
@@ -217,6 +234,7 @@ moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const mo
     d->E = (int32_t)gate->n_mat;
     d->n_ff = (int32_t)gate->rows;
     d->n_embd = (int32_t)gate->cols;
+    d->fp4 = gate->type == MOE_MXFP4;
     const bool any_sh = (sg && sg->n_mat) || (su && su->n_mat) || (sd && sd->n_mat);
     d->S = 0;
     d->n_ff_sh = 0;
@@ -226,6 +244,8 @@ moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const mo
         if ((s = check_weights(sg, "sh_gate", false))) return s;
         if ((s = check_weights(su, "sh_up", false))) return s;
         if ((s = check_weights(sd, "sh_down", false))) return s;
+        if (sg->type != gate->type || su->type != gate->type || sd->type != gate->type)
+            return fail(MOE_EINVAL, "shared experts must have the routed experts' weight type");
         if (su->n_mat != sg->n_mat || sd->n_mat != sg->n_mat || su->rows != sg->rows ||
             su->cols != sg->cols || sg->cols != gate->cols || sd->rows != gate->cols ||
             sd->cols != sg->rows)
@@ -249,6 +269,7 @@ moe_status validate_mmid(const moe_weights* w, moe_dtype st, int32_t B, int64_t 
     if ((s = check_experts(w->n_mat))) return s;
     if (B != 1 && B != k) return fail(MOE_EINVAL, "src1_rows_per_token must be 1 or n_used (got %d)", B);
     if (w->type == MOE_Q8_0 && st != MOE_BF16) return fail(MOE_EINVAL, "Q8_0 weights need BF16 src1");
+    if (w->type == MOE_MXFP4 && st != MOE_BF16) return fail(MOE_EINVAL, "MXFP4 weights need BF16 src1");
     if (w->type == MOE_F32 && st != MOE_F32) return fail(MOE_EINVAL, "F32 weights need F32 src1");
     return MOE_OK;
 }
@@ -346,7 +367,7 @@ size_t moe_ffn_fused_workspace_size(const moe_weights* gate, const moe_weights* 
     if (validate_ffn(gate, &up, &down, (su ? sh_gate : nullptr), su, (su ? &sdown : nullptr),
                      x_type, n_tokens, n_used, &d))
         return 0;
-    const int path = select_path(d.T, d.k, d.E, ffn_act_width(d), opt);
+    const int path = select_path_fmt(d.T, d.k, d.E, ffn_act_width(d), d.fp4, opt);
     if (path < 0) return 0;
     Carve c(nullptr);
     carve_ffn(c, d, path);
@@ -368,7 +389,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         return MOE_OK;
     }
     if (!x || !ids || !route_w || !out) return fail(MOE_EINVAL, "NULL pointer argument");
-    const int path = select_path(d.T, d.k, d.E, ffn_act_width(d), opt);
+    const int path = select_path_fmt(d.T, d.k, d.E, ffn_act_width(d), d.fp4, opt);
     if (path < 0) return (moe_status)path;
     Carve sz(nullptr);
     carve_ffn(sz, d, path);
@@ -478,12 +499,13 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         a.T = (int32_t)d.T;
         a.k = d.k;
         a.E = d.E;
+        const int32_t fmt = d.fp4 ? 1 : 0;
         a.rw = DecWeights{(const int8_t*)gate->data, (const uint16_t*)gate->scales,
-                          (const int8_t*)up->data, (const uint16_t*)up->scales, d.E, d.n_ff, d.n_embd};
+                          (const int8_t*)up->data, (const uint16_t*)up->scales, d.E, d.n_ff, d.n_embd, fmt};
         if (shared)
             a.sw = DecWeights{(const int8_t*)sh_gate->data, (const uint16_t*)sh_gate->scales,
                               (const int8_t*)sh_up->data, (const uint16_t*)sh_up->scales, d.S,
-                              d.n_ff_sh, d.n_embd};
+                              d.n_ff_sh, d.n_embd, fmt};
         a.act = x;
         a.act_type = 1;
         a.act_B = 1;
@@ -505,10 +527,10 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         b.k = d.k;
         b.E = d.E;
         b.rw = DecWeights{(const int8_t*)down->data, (const uint16_t*)down->scales, nullptr, nullptr,
-                          d.E, d.n_embd, d.n_ff};
+                          d.E, d.n_embd, d.n_ff, fmt};
         if (shared)
             b.sw = DecWeights{(const int8_t*)sh_down->data, (const uint16_t*)sh_down->scales, nullptr,
-                              nullptr, d.S, d.n_embd, d.n_ff_sh};
+                              nullptr, d.S, d.n_embd, d.n_ff_sh, fmt};
         b.act = p.h;
         b.act_type = 0;
         b.act_B = d.k;
@@ -553,8 +575,10 @@ size_t moe_mul_mat_id_workspace_size(const moe_weights* w, moe_dtype src1_type,
                                      int32_t src1_rows_per_token, int64_t n_tokens,
                                      int32_t n_used, const moe_options* opt) {
     if (validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used)) return 0;
-    const bool q8 = w->type == MOE_Q8_0;
-    const int path = q8 ? select_path(n_tokens, n_used, (int32_t)w->n_mat, w->cols, opt) : 1;
+    const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
+    const int path = q8 ? select_path_fmt(n_tokens, n_used, (int32_t)w->n_mat, w->cols,
+                                          w->type == MOE_MXFP4, opt)
+                        : 1;
     if (path < 0) return 0;
     // the weighted and unweighted calls use the same plan size when weighted
     Carve c(nullptr);
@@ -574,10 +598,10 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         return MOE_OK;
     }
     if (!src1 || !ids || !dst) return fail(MOE_EINVAL, "NULL pointer argument");
-    const bool q8 = w->type == MOE_Q8_0;
+    const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
     const int32_t E = (int32_t)w->n_mat, N = (int32_t)w->rows, K = (int32_t)w->cols;
     const int32_t B = src1_rows_per_token, k = n_used;
-    const int path = q8 ? select_path(n_tokens, k, E, K, opt) : 1;
+    const int path = q8 ? select_path_fmt(n_tokens, k, E, K, w->type == MOE_MXFP4, opt) : 1;
     if (path < 0) return (moe_status)path;
     const bool weighted = route_w != nullptr;
     Carve sz(nullptr);
@@ -649,7 +673,8 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         a.T = (int32_t)n_tokens;
         a.k = k;
         a.E = E;
-        a.rw = DecWeights{(const int8_t*)w->data, (const uint16_t*)w->scales, nullptr, nullptr, E, N, K};
+        a.rw = DecWeights{(const int8_t*)w->data, (const uint16_t*)w->scales, nullptr, nullptr, E, N, K,
+                          w->type == MOE_MXFP4 ? 1 : 0};
         a.act = src1;
         a.act_type = 1;
         a.act_B = B;

@@ -98,6 +98,10 @@ struct DecWeights {
     const int8_t* qs1; const uint16_t* d1;   // [n_mat][N][K]
     const int8_t* qs2; const uint16_t* d2;   // gate/up mode: up weights
     int32_t n_mat, N, K;
+    // 0: Q8_0 (int8 codes, fp16 scales); 1: MXFP4 -- qs holds two E2M1 codes per byte
+    // ([n_mat][N][K/2], even column in the low nibble) and d the E8M0 scale bytes
+    // ([n_mat][N][K/32]); the pointers are read as bytes
+    int32_t fmt;
 };
 struct DecArgs {
     const int32_t* ids;     // [T][k]

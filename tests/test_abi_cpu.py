@@ -33,7 +33,8 @@ def test_status_strings():
 
 
 def _w(n_mat=8, rows=64, cols=128, typ=moe.MOE_Q8_0, data=FAKE, scales=FAKE):
-    return moe.c_moe_weights(typ, data, scales if typ == moe.MOE_Q8_0 else None, n_mat, rows, cols)
+    return moe.c_moe_weights(typ, data, scales if typ in (moe.MOE_Q8_0, moe.MOE_MXFP4) else None,
+                             n_mat, rows, cols)
 
 
 def _ffn(gate=None, up=None, down=None, sh=(None, None, None), T=16, k=2, x_type=moe.MOE_BF16,
@@ -83,6 +84,29 @@ def test_mul_mat_id_validation():
     assert call(ws=8) == moe.MOE_EWORKSPACE
     assert call(T=1 << 22) == moe.MOE_ELIMIT
     assert call(T=0) == moe.MOE_OK
+
+
+def test_mxfp4_validation():
+    """MXFP4 experts: the decode-sized GEMV calls validate (they stop at the workspace
+    check here); larger calls, a forced GEMM path and mixed weight types are refused."""
+    fp4 = lambda **kw: _w(typ=moe.MOE_MXFP4, **kw)
+    dn = lambda **kw: fp4(rows=128, cols=64, **kw)
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=4, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=40, k=2) == moe.MOE_EINVAL     # 80 slots
+    assert "MXFP4" in moe.last_error()
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=4, k=2, path=1) == moe.MOE_EINVAL
+    assert _ffn(gate=fp4(), up=_w(), down=dn(), T=4, k=2) == moe.MOE_EINVAL       # mixed types
+    assert _ffn(gate=fp4(scales=None), up=fp4(), down=dn(), T=4, k=2) == moe.MOE_EINVAL
+    assert _ffn(gate=fp4(cols=100), up=fp4(cols=100), down=fp4(rows=100, cols=64), T=4, k=2) == moe.MOE_ELIMIT
+    sh = (fp4(n_mat=1), fp4(n_mat=1), dn(n_mat=1))
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), sh=sh, T=4, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    shq = (_w(n_mat=1), _w(n_mat=1), _w(n_mat=1, rows=128, cols=64))
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), sh=shq, T=4, k=2) == moe.MOE_EINVAL
+    w = fp4()
+    mm = moe.lib.moe_mul_mat_id_workspace_size
+    assert mm(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) == 0             # past the GEMV bound
+    assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
+                                  None, FAKE, 1 << 30, None) == moe.MOE_EINVAL   # needs BF16 src1
 
 
 def test_row_ids_validation():

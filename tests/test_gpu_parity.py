@@ -254,3 +254,73 @@ def test_v3_full_size_sampled():
     print("v3 sampled normwise error %.3g" % err)
     assert err <= TOL_MFMA
     assert np.isfinite(got).all()
+
+
+# ------------------------------------------------------------------------- MXFP4 experts
+# GEMV path only (n_tokens * n_used <= 64, widths <= 4096). Weights are exact (E2M1 code
+# times a power of two); bf16 activations meet them in bf16 pair dot products with fp32
+# accumulation, fp32 activations (the down projection's h) in fp32 FMAs.
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [
+    (8, 2, 1, 2880, 2880, 0),     # single token: register rows; K = 2880 ends inside the second piece
+    (8, 2, 1, 512, 256, 2),       # shared experts, fused reduce (2 + 2 units)
+    (16, 4, 6, 448, 1056, 1),     # several tokens: LDS ring, two slots per pass; 17 units: separate reduce
+    (4, 3, 5, 2048, 2080, 0),     # duplicate experts inside tokens; K exactly one piece / just past it
+])
+def test_ffn_mxfp4_gemv(E, k, T, n_embd, n_ff, S):
+    ids = np.random.default_rng(T * 7 + E).integers(0, E, size=(T, k)).astype(np.int32)
+    inp = synth.make_custom_ffn(51 + E, E, k, T, n_embd, n_ff, S, ids=ids, wtype="mxfp4")
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_FP32
+
+
+def test_ffn_mxfp4_extreme_scales_and_invalid_ids():
+    """Scale byte 0 (the subnormal 2^-127) and large scales, plus out-of-range ids."""
+    E, k, T, n_embd, n_ff = 6, 2, 3, 256, 128
+    ids = synth.draw_ids_uniform(4, T, E, k)
+    ids[1, 0] = -2
+    ids[2, 1] = E + 5
+    inp = synth.make_custom_ffn(61, E, k, T, n_embd, n_ff, 1, ids=ids, wtype="mxfp4")
+    inp["gate_d"][0, :, 0] = 0
+    inp["up_d"][1, ::3, 2] = 140
+    inp["down_d"][2, 5, :] = 0
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_FP32
+
+
+@pytest.mark.parametrize("E,k,T,K,N,B_is_k,bad", [
+    (6, 3, 9, 96, 40, False, True),      # one 2048 piece, mostly past K; invalid ids
+    (8, 4, 5, 3008, 70, True, False),    # one src1 row per slot, K in the second piece
+])
+def test_mxfp4_mul_mat_id_gemv(E, k, T, K, N, B_is_k, bad):
+    rng = np.random.default_rng(E * 100 + T)
+    ids = synth.draw_ids_uniform(5, T, E, k)
+    if bad:
+        ids[0, 0], ids[T - 1, k - 1] = -1, E + 1
+    inp = synth.make_custom_mmid(17, E, k, T, K, N, wtype="mxfp4", ids=ids)
+    B = k if B_is_k else 1
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T * B, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    assert w.type == moe.MOE_MXFP4
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), src1_rows_per_token=B)
+    gotw = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                              src1_rows_per_token=B)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, None, B)
+    refw = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], B)
+    g = got.cpu().numpy()
+    assert normwise(g, ref) <= TOL_FP32
+    assert normwise(gotw.cpu().numpy(), refw) <= TOL_FP32
+    assert np.all(g[(ids < 0) | (ids >= E)] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["dec1x", "dec8x"])
+def test_decode_mxfp4_full(name):
+    inp = synth.make_inputs(name)
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("%s normwise error %.3g" % (name, err))
+    assert err <= TOL_FP32
