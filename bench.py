@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 Q8_BYTES = 34.0 / 32.0      # Q8_0: 32 int8 + one fp16 scale per 32 weights
+MXFP4_BYTES = 17.0 / 32.0   # MXFP4: 32 four-bit codes + one E8M0 scale byte per 32 weights
 
 STAGES = {1: ["row_ids", "gemm_gate_up", "gemm_down", "reduce"],
           2: ["gemv_gate_up", "gemv_down", "reduce"]}
@@ -67,8 +68,9 @@ def workload_stats(inp, cfg, h_bytes=2):
     rows_routed = int(((ids >= 0) & (ids < E)).sum())
     rows = rows_routed + T * S                      # routed slots + shared-expert rows
     flops = 2.0 * rows * 3 * n_embd * n_ff
-    w_gu = (touched + S) * 2 * n_ff * n_embd * Q8_BYTES
-    w_dn = (touched + S) * n_embd * n_ff * Q8_BYTES
+    wb = MXFP4_BYTES if cfg.wtype == "mxfp4" else Q8_BYTES
+    w_gu = (touched + S) * 2 * n_ff * n_embd * wb
+    w_dn = (touched + S) * n_embd * n_ff * wb
     x_b = T * n_embd * 2                            # bf16 input
     out_b = T * n_embd * 4                          # fp32 layer output
     return {

@@ -125,9 +125,10 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
 /*
  * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
  *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
- *            src1) on the MFMA grouped GEMM or the GEMV path; (MXFP4 w, BF16 src1)
- *            on the GEMV path (n_tokens * n_used <= 64, K <= 4096; other sizes are
- *            MOE_EINVAL); (F32 w, F32 src1).
+ *            src1) or (MXFP4 w, BF16 src1) on the MFMA grouped GEMM or the GEMV path
+ *            (MXFP4 on the GEMV path: n_tokens * n_used <= 64 and K <= 4096, else the
+ *            GEMM path is taken, and forcing the GEMV path is MOE_EINVAL); (F32 w, F32
+ *            src1).
  *   src1     device [n_tokens][B][K], B = src1_rows_per_token in {1, n_used}
  *   ids      device int32 [n_tokens][n_used]
  *   route_w  NULL: dst = float32 [n_tokens][n_used][N], dst[t][s] = W_{ids[t][s]} src1_row;
@@ -146,14 +147,14 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
  *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
  *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
  *   sh_gate, sh_up Q8_0 [S][n_ff_sh][n_embd]; sh_down Q8_0 [S][n_embd][n_ff_sh];
- *             or all of them MXFP4 (GEMV path only: n_tokens * n_used <= 64 and
- *             n_embd, n_ff, n_ff_sh <= 4096; other sizes are MOE_EINVAL);
+ *             or all of them MXFP4 (its GEMV path needs n_tokens * n_used <= 64 and
+ *             n_embd, n_ff, n_ff_sh <= 4096; larger calls take the grouped GEMM);
  *             all three NULL (or n_mat == 0) = no shared experts; giving only some of
  *             them is MOE_EINVAL.
  *   x         device BF16 [n_tokens][n_embd]; ids, route_w as above.
  *   out       device float32 [n_tokens][n_embd] (overwritten).
- * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights d*q rounded
- * to nearest-even, bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
+ * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights (Q8_0: d*q
+ * rounded to nearest-even; MXFP4: exact), bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
  * results; GEMV path -- weights exact, fp32 accumulate throughout.
  */
 moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const moe_weights *down,

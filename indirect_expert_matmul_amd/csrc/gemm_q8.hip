@@ -85,6 +85,23 @@ __device__ __forceinline__ bf16x8 dequant8(int lo, int hi, float d) {
 __device__ __forceinline__ int swz_a(int r) { return r & 15; }
 __device__ __forceinline__ int swz_b(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// MXFP4 weight rows are 64 bytes per stage (4 chunks, 4 rows per 256-byte bank row):
+// chunk c of row r sits at c ^ ((r >> 2) & 3), so 16 rows reading the same logical
+// chunk hit 16 different bank groups.
+__device__ __forceinline__ int swz_b4(int r) { return (r >> 2) & 3; }
+
+// 8 MXFP4 codes (one dword, even value in each low nibble) -> 8 bf16. The E8M0 scale
+// byte x goes into the exponent field of the conversion's scale operand, which the
+// hardware applies as 2^(x - 127); fp4 times a power of two is exact in bf16.
+__device__ __forceinline__ bf16x8 dequant8_fp4(uint32_t w, float sc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 template <int MODE, int W>
 constexpr int out_cols() { return MODE == 1 ? 16 * W : 32 * W; }
 
@@ -101,12 +118,15 @@ constexpr int kMChunk = MOE_GEMM_MCHUNK;   // M tiles sharing each weight slab i
 // K % 512 == 0 and the scale rows are 16-byte aligned): the scales of four stages come
 // as 32 bytes per row into a two-slot ring, a quarter of the memory requests; one word
 // per row per stage costs as many requests as the weight rows themselves.
-template <int MSUB, int MODE, int W, int NS, int SG>
+// FMT = 1: MXFP4 experts (64-byte weight rows per stage, E8M0 scale bytes, SG = 1).
+template <int MSUB, int MODE, int W, int NS, int SG, int FMT>
 __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int BM = 32 * MSUB;
     constexpr int NTW = out_cols<MODE, W>();     // output columns per block
     constexpr int A_BYTES = BM * 256;
-    constexpr int B_BYTES = W * 32 * 128;
+    constexpr int WROW = FMT == 1 ? 64 : 128;    // weight bytes per row per stage
+    constexpr int B_BYTES = W * 32 * WROW;
+    static_assert(FMT == 0 || SG == 1, "MXFP4 scales come one word per block per stage");
     constexpr int S_BYTES = SG == 1 ? W * 32 * 16 : 0;
     constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     constexpr int SGROUP = W * 32 * 32;          // SG = 4: one group, 32 bytes per row
@@ -222,28 +242,34 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     }
     // weights: copy i covers local rows 8i..8i+7 (8 lanes x 16 B per row); in gate/up
     // mode copies 0-1 read gate rows and 2-3 up rows
-    const int8_t* b_base1 = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * K);
-    const int8_t* b_base2 = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * K) : b_base1;
-    uint32_t b_off[4];
-    int b_lc[4];
+    // (MXFP4: copy i covers local rows 16i..16i+15, 4 lanes x 16 B per row; copy 0 the
+    // gate rows and 1 the up rows)
+    constexpr int NB = FMT == 1 ? 2 : 4;           // weight copies per wave per stage
+    const int64_t RB = FMT == 1 ? K / 2 : K;       // bytes per weight row
+    const int8_t* b_base1 = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * RB);
+    const int8_t* b_base2 = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * RB) : b_base1;
+    uint32_t b_off[NB];
+    int b_lc[NB];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int l = 8 * i + (lane >> 3);
-        const int lc = (lane & 7) ^ swz_b(wv * 32 + l);
-        b_off[i] = (uint32_t)((int64_t)wrow(l) * K + lc * 16);
+    for (int i = 0; i < NB; i++) {
+        const int l = FMT == 1 ? 16 * i + (lane >> 2) : 8 * i + (lane >> 3);
+        const int lc = FMT == 1 ? (lane & 3) ^ swz_b4(wv * 32 + l) : (lane & 7) ^ swz_b(wv * 32 + l);
+        b_off[i] = (uint32_t)((int64_t)wrow(l) * RB + lc * 16);
         b_lc[i] = lc;
     }
     // scales: copy t covers local rows 16t..16t+15, lane -> (row 16t + lane/4, block
     // lane%4 of the stage); the copy fetches the aligned word holding that fp16
-    const uint8_t* s_base1 = (const uint8_t*)uniform_ptr(P.d1 + (int64_t)e * N * KB);
-    const uint8_t* s_base2 = MODE == 1 ? (const uint8_t*)uniform_ptr(P.d2 + (int64_t)e * N * KB) : s_base1;
+    constexpr int SB = FMT == 1 ? 1 : 2;          // scale bytes per block
+    const uint8_t* s_base1 = (const uint8_t*)uniform_ptr((const uint8_t*)P.d1 + (int64_t)e * N * KB * SB);
+    const uint8_t* s_base2 =
+        MODE == 1 ? (const uint8_t*)uniform_ptr((const uint8_t*)P.d2 + (int64_t)e * N * KB * SB) : s_base1;
     int s_row[2];
-    uint32_t s_word[2];  // aligned word of the scale at stage 0; stage s adds 8*s bytes
+    uint32_t s_word[2];  // aligned word of the scale at stage 0; stage s adds 4*SB*s bytes
     const int s_blk = lane & 3;
 #pragma unroll
     for (int t = 0; t < 2; t++) {
         s_row[t] = wrow(16 * t + (lane >> 2));
-        s_word[t] = (uint32_t)(((int64_t)s_row[t] * KB + s_blk) * 2) & ~3u;
+        s_word[t] = (uint32_t)(((int64_t)s_row[t] * KB + s_blk) * SB) & ~3u;
     }
     // SG = 4: lane l fetches 16 bytes (half l&1 of the group's 32) of local row l>>1,
     // from the row's own tensor (gate and up rows sit in different tensors)
@@ -251,7 +277,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     {
         const int l = lane >> 1;
         const uint16_t* dt = (MODE == 1 && l >= 16) ? P.d2 : P.d1;
-        sg_ptr = (const uint8_t*)(dt + ((int64_t)e * N + wrow(l)) * KB) + 16 * (lane & 1);
+        sg_ptr = FMT == 1 ? nullptr : (const uint8_t*)(dt + ((int64_t)e * N + wrow(l)) * KB) + 16 * (lane & 1);
     }
     const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
 
@@ -267,13 +293,13 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             for (int i = 0; i < NA; i++)
                 dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                dma16_w(w_once, ((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i],
-                        st + A_BYTES + wv * 4096 + i * 1024);
+            for (int i = 0; i < NB; i++)
+                dma16_w(w_once, ((MODE == 1 && i >= NB / 2) ? b_base2 : b_base1) + k0 * WROW / 128, b_off[i],
+                        st + A_BYTES + wv * 32 * WROW + i * 1024);
             if (SG == 1) {
 #pragma unroll
                 for (int t = 0; t < 2; t++)
-                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 8 * s,
+                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 4 * SB * s,
                          st + A_BYTES + B_BYTES + wv * 512 + t * 256);
             } else if ((s & 3) == 0) {
                 dma16v(sg_ptr + 8 * s, sring + (uint32_t)(((s >> 2) & 1) * SGROUP) + wv * 1024);
@@ -285,16 +311,17 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 dma16(a_base + (int64_t)k0 * 2, a_off[i] - adj, st + (wv * NA + i) * 1024);
             }
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const uint32_t adj = (k0 + b_lc[i] * 16 >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
-                dma16_w(w_once, ((MODE == 1 && i >= 2) ? b_base2 : b_base1) + k0, b_off[i] - adj,
-                        st + A_BYTES + wv * 4096 + i * 1024);
+            for (int i = 0; i < NB; i++) {
+                // chunk lc holds columns k0 + lc*16 (Q8_0) or k0 + lc*32 (MXFP4) on
+                const uint32_t adj = (k0 + b_lc[i] * (FMT == 1 ? 32 : 16) >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
+                dma16_w(w_once, ((MODE == 1 && i >= NB / 2) ? b_base2 : b_base1) + k0 * WROW / 128, b_off[i] - adj,
+                        st + A_BYTES + wv * 32 * WROW + i * 1024);
             }
             if (SG == 1) {   // (SG = 4 needs K % 512 == 0: no partial stage)
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
                     const int blk = min(4 * s + s_blk, KB - 1);
-                    const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * 2);
+                    const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * SB);
                     dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, byte & ~3u,
                          st + A_BYTES + B_BYTES + wv * 512 + t * 256);
                 }
@@ -311,14 +338,16 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     // dequant geometry of this lane: local weight row l32; in half u it takes the
     // 32-byte block 2u + h of the stage = chunks 4u + 2h and 4u + 2h + 1
     const int lrow = wv * 32 + l32;
-    const int b_rd = A_BYTES + lrow * 128;
+    const int b_rd = A_BYTES + lrow * WROW;
     const int s_rd = A_BYTES + B_BYTES + wv * 512 + l32 * 16;
-    // which half of each aligned scale word holds the scale (constant over stages:
-    // stages start at a multiple of 4 blocks)
+    // where in each aligned scale word the scale sits (constant over stages: stages
+    // start at a multiple of 4 blocks): the half (fp16) or the byte (E8M0)
     int s_sh[2];
 #pragma unroll
-    for (int u = 0; u < 2; u++)
-        s_sh[u] = (((int64_t)wrow(l32) * KB + 2 * u + h) & 1) ? 16 : 0;
+    for (int u = 0; u < 2; u++) {
+        const int64_t sidx = (int64_t)wrow(l32) * KB + 2 * u + h;
+        s_sh[u] = FMT == 1 ? (int)(sidx & 3) * 8 : ((sidx & 1) ? 16 : 0);
+    }
 
     // One step: wait for stage s, send stage s+1 into the other slot, dequantize and
     // multiply. SLOT is s % 2 as a constant, so the LDS offsets become immediates;
@@ -337,22 +366,33 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         float d[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            q[u][0] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
-            q[u][1] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
-            if constexpr (SG == 1) {
+            if constexpr (FMT == 1) {
+                // one 16-byte chunk = this lane's block of 32 codes; blocks past K get zero
+                // codes (a zero scale operand would still mean 2^-127)
+                q[u][0] = *(const i32x4*)(st + b_rd + (((2 * u + h) ^ swz_b4(lrow)) << 4));
                 const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
-                d[u] = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+                d[u] = __builtin_bit_cast(float, ((sw >> s_sh[u]) & 255u) << 23);
+                if constexpr (CHECK_K)
+                    if (!(k0 + 64 * u + 32 * h < K)) q[u][0] = i32x4{0, 0, 0, 0};
             } else {
-                d[u] = half_bits_to_float(*(const uint16_t*)(smem + NS * STAGE + ((s >> 2) & 1) * SGROUP +
-                                                             lrow * 32 + (4 * (s & 3) + 2 * u + h) * 2));
+                q[u][0] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
+                q[u][1] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
+                if constexpr (SG == 1) {
+                    const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
+                    d[u] = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+                } else {
+                    d[u] = half_bits_to_float(*(const uint16_t*)(smem + NS * STAGE + ((s >> 2) & 1) * SGROUP +
+                                                                 lrow * 32 + (4 * (s & 3) + 2 * u + h) * 2));
+                }
+                if constexpr (CHECK_K) d[u] = (k0 + 64 * u + 32 * h < K) ? d[u] : 0.f;
             }
-            if constexpr (CHECK_K) d[u] = (k0 + 64 * u + 32 * h < K) ? d[u] : 0.f;
         }
         // 8 k sub-steps (half u = t/4, ss = t%4): the MSUB MFMAs of sub-step t run while
         // sub-step t+1's weights are dequantized and its activation fragments read;
         // each sub-step is a scheduling region with that interleave pinned (left alone,
         // the compiler issues all of a stage's dequant work before its MFMAs)
         auto deq = [&](int t) -> bf16x8 {
+            if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[t >> 2][0][t & 3], d[t >> 2]);
             const i32x4& v = q[t >> 2][(t & 3) >> 1];
             return (t & 1) ? dequant8(v[2], v[3], d[t >> 2]) : dequant8(v[0], v[1], d[t >> 2]);
         };
@@ -381,7 +421,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur], acc[i], 0, 0, 0);
 #ifndef MOE_GEMM_NO_SCHED
             if (t < 7) {
-                constexpr int VPM = (20 + MSUB - 1) / MSUB;   // dequant VALU per MFMA
+                constexpr int VPM = ((FMT == 1 ? 4 : 20) + MSUB - 1) / MSUB;   // dequant VALU per MFMA
 #pragma unroll
                 for (int m = 0; m < MSUB; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -820,25 +860,41 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
                   : launch_wide_sg<MODE, 1, MSUB, W, NS>(g, (int)total, st);
 }
 
-template <int MSUB, int W, int NS, int SG>
+template <int MSUB, int W, int NS, int SG, int FMT>
 constexpr int stage_lds() {
-    return NS * (32 * MSUB * 256 + W * 32 * 128 + (SG == 1 ? W * 32 * 16 : 0)) +
+    return NS * (32 * MSUB * 256 + W * 32 * (FMT == 1 ? 64 : 128) + (SG == 1 ? W * 32 * 16 : 0)) +
            (SG == 4 ? 2 * W * 32 * 32 : 0);
 }
 
-template <int MSUB, int MODE, int W, int NS, int SG>
+template <int MSUB, int MODE, int W, int NS, int SG, int FMT>
 hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr int lds = stage_lds<MSUB, W, NS, SG>();
+    constexpr int lds = stage_lds<MSUB, W, NS, SG, FMT>();
     static_assert(lds + 32 * MSUB * 4 <= 160 * 1024, "LDS rings exceed 160 KB");
     static bool attr_set = false;   // raise the dynamic LDS cap once per process
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8<MSUB, MODE, W, NS, SG>,
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8<MSUB, MODE, W, NS, SG, FMT>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_gemm_q8<MSUB, MODE, W, NS, SG><<<grid, 64 * W, lds, st>>>(a);
+    k_gemm_q8<MSUB, MODE, W, NS, SG, FMT><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
+}
+
+// MXFP4 experts: the same kernel with 64-byte weight rows and per-stage scale words.
+template <int MSUB, int W, int NS>
+hipError_t launch_cfg_fp4(const GemmArgs& a, hipStream_t st) {
+    const int ntw = a.mode == 1 ? out_cols<1, W>() : out_cols<0, W>();
+    int64_t total = 0;
+    for (int i = 0; i < a.n_prob; i++) {
+        const GemmProblem& p = a.p[i];
+        total += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
+    }
+    if (total <= 0) return hipSuccess;
+    GemmArgs g = a;
+    g.grid_real = (int32_t)total;
+    return a.mode == 1 ? launch_one<MSUB, 1, W, NS, 1, 1>(g, (int)total, st)
+                       : launch_one<MSUB, 0, W, NS, 1, 1>(g, (int)total, st);
 }
 
 template <int MSUB, int W, int NS>
@@ -856,8 +912,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
     if (a.mode == 1)
-        return groups ? launch_one<MSUB, 1, W, NS, 4>(g, (int)total, st) : launch_one<MSUB, 1, W, NS, 1>(g, (int)total, st);
-    return groups ? launch_one<MSUB, 0, W, NS, 4>(g, (int)total, st) : launch_one<MSUB, 0, W, NS, 1>(g, (int)total, st);
+        return groups ? launch_one<MSUB, 1, W, NS, 4, 0>(g, (int)total, st)
+                      : launch_one<MSUB, 1, W, NS, 1, 0>(g, (int)total, st);
+    return groups ? launch_one<MSUB, 0, W, NS, 4, 0>(g, (int)total, st)
+                  : launch_one<MSUB, 0, W, NS, 1, 0>(g, (int)total, st);
 }
 
 }  // namespace
@@ -871,6 +929,13 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     GemmArgs a = a0;
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
+    if (a.fmt == 1) {   // MXFP4 experts: the 64- and 128-row tiles of the narrow kernel
+        switch (msub) {
+            case 2: return launch_cfg_fp4<2, MOE_GEMM_CFG2>(a, st);
+            case 4: return launch_cfg_fp4<4, MOE_GEMM_CFG4>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     bool wide_ok = true;   // the wide kernels need whole 64-column stages
     for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
 #ifdef MOE_GEMM_NO_WIDE

@@ -121,16 +121,20 @@ int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_op
     return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
 }
 
-// MXFP4 experts run on the wave-level GEMV only: n_tokens * n_used <= 64 and every
-// activation width <= 4096.
+// MXFP4 experts: the GEMV path only through its wave-level kernels (n_tokens * n_used
+// <= 64 and every activation width <= 4096); otherwise the grouped GEMM.
 int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4, const moe_options* o) {
     if (!fp4) return select_path(T, k, E, act_width, o);
     const int32_t force = o ? o->path : 0;
-    if (force < 0 || force > 2) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
-    if (force == 1) return fail(MOE_EINVAL, "MXFP4 experts have no grouped GEMM path");
-    if (T * (int64_t)k > 64 || act_width > 4096)
-        return fail(MOE_EINVAL, "MXFP4 experts need n_tokens*n_used <= 64 and widths <= 4096 (the GEMV path)");
-    return 2;
+    const bool dec_ok = T * (int64_t)k <= 64 && act_width <= 4096;
+    if (force == 1) return 1;
+    if (force == 2) {
+        if (!dec_ok)
+            return fail(MOE_EINVAL, "GEMV path with MXFP4 experts needs n_tokens*n_used <= 64 and widths <= 4096");
+        return 2;
+    }
+    if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
+    return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
 }
 
 int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n : E); }
@@ -415,6 +419,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
 
         GemmArgs g{};
         g.mode = 1;
+        g.fmt = d.fp4 ? 1 : 0;
         g.n_prob = shared ? 2 : 1;
         GemmProblem& r = g.p[0];
         r.qs1 = (const int8_t*)gate->data;
@@ -458,6 +463,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
 
         GemmArgs g2{};
         g2.mode = 0;
+        g2.fmt = g.fmt;
         g2.n_prob = shared ? 2 : 1;
         GemmProblem& r2 = g2.p[0];
         r2.qs1 = (const int8_t*)down->data;
@@ -629,6 +635,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         if (q8) {
             GemmArgs g{};
             g.mode = 0;
+            g.fmt = w->type == MOE_MXFP4 ? 1 : 0;
             g.n_prob = 1;
             GemmProblem& r = g.p[0];
             r.qs1 = (const int8_t*)w->data;

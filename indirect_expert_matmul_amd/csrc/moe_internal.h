@@ -73,6 +73,9 @@ struct GemmArgs {
     int32_t n_prob;
     int32_t mode;             // 0: fp32 out = acc; 1: bf16 out = silu(acc_gate) * acc_up
     int32_t grid_real;        // blocks carrying tiles (before padding to a multiple of 8)
+    // 0: Q8_0 experts; 1: MXFP4 -- qs1/qs2 hold two E2M1 codes per byte ([n_mat][N][K/2],
+    // even column in the low nibble), d1/d2 the E8M0 scale bytes ([n_mat][N][K/32])
+    int32_t fmt;
 };
 // Block tile height for a given average rows-per-expert (host heuristic).
 int gemm_pick_msub(double avg_rows);

@@ -80,6 +80,9 @@ CONFIGS = {
                     desc="GPT-OSS-20B-shaped decode: E32 k4 T1 n_embd=n_ff=2880 MXFP4"),
     "dec8x": Config("dec8x", "ffn", 32, 4, 8, 2880, 2880, wtype="mxfp4", seed=3,
                     desc="GPT-OSS-20B-shaped decode: E32 k4 T8 n_embd=n_ff=2880 MXFP4"),
+    # GPT-OSS-20B-shaped prefill, PP4096, MXFP4 experts.
+    "ppx": Config("ppx", "ffn", 32, 4, 4096, 2880, 2880, wtype="mxfp4", seed=7,
+                  desc="GPT-OSS-20B-shaped prefill: E32 k4 T4096 n_embd=n_ff=2880 MXFP4"),
     # Zipf(1.1)-skewed prefill, PP4096.
     "skew": Config("skew", "ffn", 128, 8, 4096, 2048, 768, routing="zipf", seed=4,
                    desc="Skewed prefill: E128 k8 T4096 n_embd2048 n_ff768 Zipf(1.1) Q8_0"),

@@ -87,14 +87,15 @@ def test_mul_mat_id_validation():
 
 
 def test_mxfp4_validation():
-    """MXFP4 experts: the decode-sized GEMV calls validate (they stop at the workspace
-    check here); larger calls, a forced GEMM path and mixed weight types are refused."""
+    """MXFP4 experts: both paths validate (the calls stop at the workspace check here);
+    the GEMV path forced past its wave-kernel bound and mixed weight types are refused."""
     fp4 = lambda **kw: _w(typ=moe.MOE_MXFP4, **kw)
     dn = lambda **kw: fp4(rows=128, cols=64, **kw)
     assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=4, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
-    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=40, k=2) == moe.MOE_EINVAL     # 80 slots
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=40, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=4, k=2, path=1, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=40, k=2, path=2) == moe.MOE_EINVAL   # 80 slots
     assert "MXFP4" in moe.last_error()
-    assert _ffn(gate=fp4(), up=fp4(), down=dn(), T=4, k=2, path=1) == moe.MOE_EINVAL
     assert _ffn(gate=fp4(), up=_w(), down=dn(), T=4, k=2) == moe.MOE_EINVAL       # mixed types
     assert _ffn(gate=fp4(scales=None), up=fp4(), down=dn(), T=4, k=2) == moe.MOE_EINVAL
     assert _ffn(gate=fp4(cols=100), up=fp4(cols=100), down=fp4(rows=100, cols=64), T=4, k=2) == moe.MOE_ELIMIT
@@ -104,7 +105,7 @@ def test_mxfp4_validation():
     assert _ffn(gate=fp4(), up=fp4(), down=dn(), sh=shq, T=4, k=2) == moe.MOE_EINVAL
     w = fp4()
     mm = moe.lib.moe_mul_mat_id_workspace_size
-    assert mm(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) == 0             # past the GEMV bound
+    assert mm(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) > 0              # the GEMM path
     assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
                                   None, FAKE, 1 << 30, None) == moe.MOE_EINVAL   # needs BF16 src1
 

@@ -324,3 +324,66 @@ def test_decode_mxfp4_full(name):
     err = normwise(got.cpu().numpy(), oracle.ffn(inp))
     print("%s normwise error %.3g" % (name, err))
     assert err <= TOL_FP32
+
+
+# MXFP4 on the grouped GEMM: weights are exact in bf16, so the error is that of the bf16
+# activations and the bf16 h, as on the Q8_0 GEMM path.
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S,routing", [
+    (8, 2, 40, 256, 192, 1, "uniform"),   # 64-row tiles; down K = 192 ends inside a stage; ragged N
+    (4, 2, 300, 512, 160, 0, "uniform"),  # 128-row tiles; down K = 160
+    (6, 3, 100, 96, 64, 2, "uniform"),    # single partial stages both ways, duplicate experts
+    (16, 4, 200, 384, 224, 1, "zipf"),    # skewed segments: empty, tiny and oversized experts
+])
+def test_ffn_mxfp4_gemm(E, k, T, n_embd, n_ff, S, routing):
+    ids = (synth.draw_ids_zipf(33, T, E, k, 1.1) if routing == "zipf"
+           else np.random.default_rng(T + E).integers(0, E, size=(T, k)).astype(np.int32))
+    inp = synth.make_custom_ffn(71 + E, E, k, T, n_embd, n_ff, S, ids=ids, wtype="mxfp4")
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    assert moe.last_stage_count() == 4
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_MFMA
+
+
+def test_ffn_mxfp4_gemm_invalid_ids_and_scale_zero():
+    E, k, T, n_embd, n_ff = 8, 2, 70, 128, 96
+    ids = synth.draw_ids_uniform(8, T, E, k)
+    ids[3, 0], ids[40, 1], ids[69, 0] = -1, E, 1 << 20
+    inp = synth.make_custom_ffn(81, E, k, T, n_embd, n_ff, 1, ids=ids, wtype="mxfp4")
+    inp["gate_d"][2, :, 1] = 0          # scale 2^-127: those blocks contribute ~nothing
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_MFMA
+
+
+@pytest.mark.parametrize("E,k,T,K,N,B_is_k", [(6, 3, 50, 96, 45, False), (8, 2, 200, 640, 200, True)])
+def test_mxfp4_mul_mat_id_gemm(E, k, T, K, N, B_is_k):
+    rng = np.random.default_rng(E + T)
+    ids = synth.draw_ids_uniform(6, T, E, k)
+    ids[1, 0] = -3
+    inp = synth.make_custom_mmid(19, E, k, T, K, N, wtype="mxfp4", ids=ids)
+    B = k if B_is_k else 1
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T * B, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), src1_rows_per_token=B, path=moe.PATH_GEMM)
+    gotw = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                              src1_rows_per_token=B, path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, None, B)
+    refw = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], B)
+    g = got.cpu().numpy()
+    assert normwise(g, ref) <= TOL_MFMA
+    assert normwise(gotw.cpu().numpy(), refw) <= TOL_MFMA
+    assert np.all(g[(ids < 0) | (ids >= E)] == 0.0)
+
+
+def test_ppx_full_size_sampled():
+    """GPT-OSS-20B-shaped PP4096 prefill with MXFP4 experts (128-row tiles)."""
+    inp = synth.make_inputs("ppx")
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    assert moe.last_stage_count() == 4
+    rows = _sample_tokens(inp["ids"], 96, 2)
+    err = normwise(got.cpu().numpy()[rows], oracle.ffn(inp, token_rows=rows))
+    print("ppx sampled normwise error %.3g" % err)
+    assert err <= TOL_MFMA
+    assert torch.isfinite(got).all()
