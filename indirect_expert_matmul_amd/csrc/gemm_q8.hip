@@ -132,7 +132,11 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int SGROUP = W * 32 * 32;          // SG = 4: one group, 32 bytes per row
     static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     constexpr int NA = BM / (4 * W);             // activation copies (1 KB) per wave per stage
-    static_assert(NS == 2, "the step sequence below runs a two-slot ring");
+    // copies per wave per stage with per-stage scales: NA activation, the weight copies
+    // and two scale-word copies
+    constexpr int VM_STAGE = NA + (FMT == 1 ? 2 : 4) + 2;
+    static_assert(NS == 2 || (NS == 3 && SG == 1),
+                  "a two-slot ring, or a three-slot one with a fixed copy count per stage");
     static_assert(NA * 4 * W == BM, "activation rows must split evenly over the waves");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int32_t s_orow[BM];
@@ -355,8 +359,16 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     auto step = [&](int s, auto slot_c, auto check_c) {
         constexpr int SLOT = decltype(slot_c)::value;
         constexpr bool CHECK_K = decltype(check_c)::value;
-        wait_stage_and_barrier<0>();   // stage s landed; nobody still reads the other slot
-        if (s + 1 < nsteps) issue(s + 1, SLOT ^ 1);
+        if constexpr (NS == 2) {
+            wait_stage_and_barrier<0>();   // stage s landed; nobody still reads the other slot
+            if (s + 1 < nsteps) issue(s + 1, SLOT ^ 1);
+        } else {
+            // stage s landed (stage s+1 may still be in flight: its copies are the last
+            // VM_STAGE of this wave); nobody still reads slot (s+2) % 3, used by stage s-1
+            if (s + 1 < nsteps) wait_stage_and_barrier<VM_STAGE>();
+            else wait_stage_and_barrier<0>();
+            if (s + 2 < nsteps) issue(s + 2, (SLOT + 2) % 3);
+        }
         const uint8_t* st = smem + SLOT * STAGE;
         const int k0 = s * 128;
         // the stage's weights (both 64-column halves) and scales; both halves always
@@ -438,18 +450,40 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     using NoCheck = std::integral_constant<bool, false>;
     using Check = std::integral_constant<bool, true>;
 
-    issue(0, 0);
     const int last = nsteps - 1;   // only this stage can end inside K
     int s = 0;
-    for (; s + 1 < last; s += 2) {
-        step(s, S0{}, NoCheck{});
-        step(s + 1, S1{}, NoCheck{});
-    }
-    if (s < last) {
-        step(s, S0{}, NoCheck{});
-        step(s + 1, S1{}, Check{});
+    if constexpr (NS == 2) {
+        issue(0, 0);
+        for (; s + 1 < last; s += 2) {
+            step(s, S0{}, NoCheck{});
+            step(s + 1, S1{}, NoCheck{});
+        }
+        if (s < last) {
+            step(s, S0{}, NoCheck{});
+            step(s + 1, S1{}, Check{});
+        } else {
+            step(s, S0{}, Check{});
+        }
     } else {
-        step(s, S0{}, Check{});
+        using S2 = std::integral_constant<int, 2>;
+        issue(0, 0);
+        if (nsteps > 1) issue(1, 1);
+        for (; s + 2 < last; s += 3) {
+            step(s, S0{}, NoCheck{});
+            step(s + 1, S1{}, NoCheck{});
+            step(s + 2, S2{}, NoCheck{});
+        }
+        // stages s .. last (one to three), slots 0, 1, 2 in turn
+        if (s == last) {
+            step(s, S0{}, Check{});
+        } else if (s + 1 == last) {
+            step(s, S0{}, NoCheck{});
+            step(s + 1, S1{}, Check{});
+        } else {
+            step(s, S0{}, NoCheck{});
+            step(s + 1, S1{}, NoCheck{});
+            step(s + 2, S2{}, Check{});
+        }
     }
 
     // ---- epilogue. Accumulator v of lane l holds row 8*(v/4) + 4*(l/32) + v%4 of
@@ -881,15 +915,24 @@ hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-// MXFP4 experts: the same kernel with 64-byte weight rows and per-stage scale words.
-template <int MSUB, int W, int NS>
-hipError_t launch_cfg_fp4(const GemmArgs& a, hipStream_t st) {
+// Grid of the narrow kernel with W waves: per problem, an upper bound on its tiles,
+// rounded up to a multiple of 8 (one part per XCD).
+template <int W>
+int64_t narrow_grid(const GemmArgs& a) {
     const int ntw = a.mode == 1 ? out_cols<1, W>() : out_cols<0, W>();
     int64_t total = 0;
     for (int i = 0; i < a.n_prob; i++) {
         const GemmProblem& p = a.p[i];
         total += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
     }
+    return total;
+}
+
+// MXFP4 experts: the same kernel with 64-byte weight rows and per-stage scale words.
+// An MXFP4 stage is small enough for a three-slot ring at two 4-wave blocks per CU.
+template <int MSUB, int W, int NS>
+hipError_t launch_cfg_fp4(const GemmArgs& a, hipStream_t st) {
+    const int64_t total = narrow_grid<W>(a);
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
@@ -931,8 +974,16 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
     if (a.fmt == 1) {   // MXFP4 experts: the 64- and 128-row tiles of the narrow kernel
         switch (msub) {
-            case 2: return launch_cfg_fp4<2, MOE_GEMM_CFG2>(a, st);
-            case 4: return launch_cfg_fp4<4, MOE_GEMM_CFG4>(a, st);
+            case 2:
+                // 64-row tiles: 8 waves (256 weight rows) with three slots, one block per
+                // CU, when that still leaves some 8 rounds of blocks (V3-shaped layers);
+                // otherwise 4 waves with three slots, two blocks per CU. Measured on
+                // MXFP4 layers: V3-shaped T=2048 step 3708 -> 3205 us with 8 waves,
+                // Lite- and GPT-OSS-shaped PP512 1-3% better with 4.
+                if (narrow_grid<8>(a) >= 2048) return launch_cfg_fp4<2, 8, 3>(a, st);
+                return launch_cfg_fp4<2, 4, 3>(a, st);
+            case 4:   // 128-row tiles: three slots measured no better than two here
+                return launch_cfg_fp4<4, 8, 2>(a, st);
             default: return hipErrorInvalidValue;
         }
     }

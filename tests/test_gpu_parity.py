@@ -387,3 +387,16 @@ def test_ppx_full_size_sampled():
     print("ppx sampled normwise error %.3g" % err)
     assert err <= TOL_MFMA
     assert torch.isfinite(got).all()
+
+
+def test_ffn_mxfp4_gemm_large_grid_sampled():
+    """64-row tiles with a grid of 2048 or more 8-wave tiles: gate/up runs 256 weight
+    rows per block with a three-slot ring; down (few N tiles) stays on 4 waves."""
+    E, k, T, n_embd, n_ff = 128, 2, 2048, 512, 2048
+    inp = synth.make_custom_ffn(91, E, k, T, n_embd, n_ff, 0, wtype="mxfp4")
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    rows = _sample_tokens(inp["ids"], 64, 3)
+    err = normwise(got.cpu().numpy()[rows], oracle.ffn(inp, token_rows=rows))
+    assert err <= TOL_MFMA
+    assert torch.isfinite(got).all()
