@@ -133,6 +133,48 @@ def measured_traffic(config, stage):
     return float(ent["bytes"])
 
 
+class KernelEvent:
+    """A HIP timing event without the end-of-record system-scope memory fence
+    (hipEventDisableSystemFence). That fence makes every stop event wait for a
+    system-wide cache write-back, which adds about 2 us to each timed interval,
+    as much as an eighth of a decode GEMV. Without it the interval matches the
+    kernel duration that rocprofv3 reports. The handle goes to the library, which
+    records it on its own stream around each stage."""
+    _hip = None
+    FLAGS = 0x20000000   # hipEventDefault | hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        import torch  # noqa: F401  (loads the HIP runtime this process uses)
+        if KernelEvent._hip is None:
+            KernelEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+        h = ctypes.c_void_p()
+        rc = KernelEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self.FLAGS))
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+        self.cuda_event = h.value
+
+    def record(self, stream):
+        import ctypes
+        rc = KernelEvent._hip.hipEventRecord(ctypes.c_void_p(self.cuda_event), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_time(self, end):
+        import ctypes
+        ms = ctypes.c_float()
+        rc = KernelEvent._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.cuda_event),
+                                                  ctypes.c_void_p(end.cuda_event))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def __del__(self):
+        import ctypes
+        if KernelEvent._hip is not None and self.cuda_event:
+            KernelEvent._hip.hipEventDestroy(ctypes.c_void_p(self.cuda_event))
+
+
 def warm_up(run, n):
     """Untimed steps before the timed ones: exactly n if given, otherwise at least 20
     steps and at least 0.2 s of them (from idle, the GPU clocks take some milliseconds
@@ -164,7 +206,7 @@ def bench_row_ids(args):
     ws = torch.empty(moe.lib.moe_row_ids_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     args.warmup = warm_up(lambda i: moe.moe_row_ids(ids, E, workspace=ws, stream=stream), args.warmup)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = KernelEvent(), KernelEvent()
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
@@ -289,11 +331,7 @@ def main():
 
     # per-kernel durations: HIP events recorded by the library around each stage
     names = STAGES[path]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
-           for _ in range(args.steps)]
-    for row in evs:          # torch creates the underlying hipEvent on first record
-        for e in row:
-            e.record(stream)
+    evs = [[KernelEvent() for _ in range(2 * len(names))] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, events=[e.cuda_event for e in evs[i]])
@@ -325,7 +363,7 @@ def main():
     lg = torch.from_numpy(synth.draw_router_logits(cfg.seed, T, cfg.n_experts)).to(dev)
     for _ in range(3):
         moe.moe_router_topk(lg, k, stream=stream)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0, r1 = KernelEvent(), KernelEvent()
     r0.record(stream)
     n_router = 20
     for _ in range(n_router):
