@@ -16,7 +16,7 @@
 //     position; a second walk over the same range places every entry. Entries keep
 //     their (t, s) order inside a bucket, so the result is unique.
 //   * Bucket E collects ids outside [0, E): they land after all expert segments.
-//   * Inputs up to kRowIdsOneBlockMax entries run as one 512-thread workgroup (one
+//   * Inputs up to kRowIdsOneBlockMax entries run as one 1024-thread workgroup (one
 //     launch); larger ones use count / scan-over-chunks / scan-over-buckets / place.
 #include "moe_internal.h"
 
@@ -75,64 +75,79 @@ __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, in
     }
 }
 
-// Histogram of entries [beg, end) into this wave's counter row (no atomics: each
-// bucket present in a batch has exactly one leader lane).
-__device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t end, int32_t E,
-                           int nbits, int32_t* cnt_w) {
+// Histogram of the loaded batches starting at entry b0 (entries from `end` on are
+// skipped) into this wave's counter row. No atomics: each bucket present in a batch
+// has exactly one leader lane.
+__device__ __forceinline__ void count_batches(const int (&bk)[kPre], int64_t b0, int64_t end, int nbits,
+                                              int32_t* cnt_w) {
     const int lane = threadIdx.x & 63;
-    for (int64_t base = beg; base < end; base += kPre * 64) {
-        int bk[kPre];
-        load_batches(ids, base, end, E, bk);
 #pragma unroll
-        for (int q = 0; q < kPre; q++) {
-            if (base + q * 64 >= end) break;  // uniform
-            const bool act = bk[q] >= 0;
-            const int b = act ? bk[q] : 0;
-            const uint64_t m = match_bucket(b, __ballot(act), nbits);
-            if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
-        }
+    for (int q = 0; q < kPre; q++) {
+        if (b0 + q * 64 >= end) break;  // uniform
+        const bool act = bk[q] >= 0;
+        const int b = act ? bk[q] : 0;
+        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
     }
 }
 
-// Place entries [beg, end): position = base[b] + running[b] + rank in batch.
+// Places the loaded batches starting at entry b0: position = base[b] + running[b] +
+// rank in batch.
+__device__ __forceinline__ void place_batches(const RowIdsArgs& a, const int (&bk)[kPre], int64_t b0,
+                                              int64_t end, int nbits, const int32_t* base, int32_t* run_w) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPre; q++) {
+        const int64_t bb = b0 + q * 64;
+        if (bb >= end) break;  // uniform
+        const int64_t i = bb + lane;
+        const bool act = bk[q] >= 0;
+        const int b = act ? bk[q] : 0;
+        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        int32_t prev = 0;
+        if (act) {
+            prev = run_w[b];
+            const int32_t pos = base[b] + prev + rank_below(m);
+            const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
+            const int32_t t = ii / a.k;
+            const int32_t s = ii - t * a.k;
+            a.ids_src1[pos] = t * a.B + s % a.B;
+            a.ids_dst[pos] = ii;
+            if (a.inv) a.inv[i] = pos;
+        }
+        // every lane has read its counter before the group's leader bumps it
+        __builtin_amdgcn_wave_barrier();
+        if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Histogram of entries [beg, end) into this wave's counter row.
+__device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t end, int32_t E,
+                           int nbits, int32_t* cnt_w) {
+    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
+        int bk[kPre];
+        load_batches(ids, b0, end, E, bk);
+        count_batches(bk, b0, end, nbits, cnt_w);
+    }
+}
+
+// Places entries [beg, end).
 __device__ void wave_place(const RowIdsArgs& a, int64_t beg, int64_t end, int nbits,
                            const int32_t* base, int32_t* run_w) {
-    const int lane = threadIdx.x & 63;
     for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
         int bk[kPre];
         load_batches(a.ids, b0, end, a.E, bk);
-#pragma unroll
-        for (int q = 0; q < kPre; q++) {
-            const int64_t bb = b0 + q * 64;
-            if (bb >= end) break;  // uniform
-            const int64_t i = bb + lane;
-            const bool act = bk[q] >= 0;
-            const int b = act ? bk[q] : 0;
-            const uint64_t m = match_bucket(b, __ballot(act), nbits);
-            int32_t prev = 0;
-            if (act) {
-                prev = run_w[b];
-                const int32_t pos = base[b] + prev + rank_below(m);
-                const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
-                const int32_t t = ii / a.k;
-                const int32_t s = ii - t * a.k;
-                a.ids_src1[pos] = t * a.B + s % a.B;
-                a.ids_dst[pos] = ii;
-                if (a.inv) a.inv[i] = pos;
-            }
-            // every lane has read its counter before the group's leader bumps it
-            __builtin_amdgcn_wave_barrier();
-            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
-            __builtin_amdgcn_wave_barrier();
-        }
+        place_batches(a, bk, b0, end, nbits, base, run_w);
     }
 }
 
-// In-place exclusive scan of v[0, n) (LDS) by all threads of the block; returns the
-// total. wsum: LDS scratch of kWaves ints.
+// In-place exclusive scan of v[0, n) (LDS) by all NT threads of the block; returns the
+// total. wsum: LDS scratch of NT / 64 ints.
+template <int NT = kThreads>
 __device__ int32_t block_scan(int32_t* v, int n, int32_t* wsum) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = (n + NT - 1) / NT;
     const int beg = min(tid * per, n), end = min(beg + per, n);
     int32_t s = 0;
     for (int i = beg; i < end; i++) s += v[i];
@@ -144,7 +159,7 @@ __device__ int32_t block_scan(int32_t* v, int n, int32_t* wsum) {
     if (lane == 63) wsum[w] = x;
     __syncthreads();
     int32_t pre = 0, total = 0;
-    for (int j = 0; j < kWaves; j++) {
+    for (int j = 0; j < NT / 64; j++) {
         if (j < w) pre += wsum[j];
         total += wsum[j];
     }
@@ -158,22 +173,23 @@ __device__ int32_t block_scan(int32_t* v, int n, int32_t* wsum) {
     return total;
 }
 
-// bstart[0..NB) holds bucket starts: write bounds and the M-tile prefixes.
+// bstart[0..NB) holds bucket starts: write bounds and the M-tile prefixes (NT threads).
+template <int NT = kThreads>
 __device__ void write_bounds_and_tiles(const RowIdsArgs& a, const int32_t* bstart, int32_t* tmp,
                                        int32_t* wsum) {
     const int E = a.E, NB = E + 1;
-    for (int b = threadIdx.x; b < NB; b += kThreads) a.bounds[b] = bstart[b];
+    for (int b = threadIdx.x; b < NB; b += NT) a.bounds[b] = bstart[b];
     for (int q = 0; q < 2; q++) {
         if (!a.tile_off[q]) continue;  // uniform across the block
         const int tm = a.tile_m[q];
-        for (int b = threadIdx.x; b < NB; b += kThreads)
+        for (int b = threadIdx.x; b < NB; b += NT)
             tmp[b] = b < E ? (bstart[b + 1] - bstart[b] + tm - 1) / tm : 0;
         __syncthreads();
-        block_scan(tmp, NB, wsum);
-        for (int b = threadIdx.x; b < NB; b += kThreads) a.tile_off[q][b] = tmp[b];
+        block_scan<NT>(tmp, NB, wsum);
+        for (int b = threadIdx.x; b < NB; b += NT) a.tile_off[q][b] = tmp[b];
         if (a.tile_tab[q]) {
             // one entry per M tile, so the GEMM finds its tile with a single load
-            for (int b = threadIdx.x; b < E; b += kThreads) {
+            for (int b = threadIdx.x; b < E; b += NT) {
                 const int32_t lo = bstart[b], hi = bstart[b + 1];
                 for (int32_t j = tmp[b]; j < tmp[b + 1] && j < a.tile_cap[q]; j++) {
                     int32_t* t = a.tile_tab[q] + 4 * (int64_t)j;
@@ -191,32 +207,53 @@ __device__ void write_bounds_and_tiles(const RowIdsArgs& a, const int32_t* bstar
 __device__ __forceinline__ int bucket_bits(int NB) { return 32 - __clz(NB - 1); }
 
 // ---------------------------------------------------------------- one workgroup
-__global__ __launch_bounds__(kThreads) void k_row_ids_single(RowIdsArgs a) {
-    __shared__ int32_t cnt[kWaves * kMaxBuckets];
-    __shared__ int32_t bstart[kMaxBuckets + 1];
-    __shared__ int32_t tmp[kMaxBuckets + 1];
-    __shared__ int32_t wsum[kWaves];
+// 16 waves (the most one workgroup holds), so each wave walks at most four batches:
+// with 8 waves the two serial walks (count, place) of 6 batches each took 3.3 and
+// 3.6 us of an 11.8 us pass on 3072 entries; with 16 waves and the ids kept in
+// registers between the walks, the pass takes about 7 us.
+constexpr int kSingleWaves = 16;
+static_assert(kRowIdsOneBlockMax <= (int64_t)kSingleWaves * 64 * kPre,
+              "the one-workgroup pass keeps each wave's ids in kPre registers");
+
+// LDS of the one-workgroup pass: per-wave counters [kSingleWaves][NB], then bucket
+// starts [NB + 1] and tile counts [NB + 1].
+size_t single_lds_bytes(int NB) { return ((size_t)kSingleWaves * NB + 2 * ((size_t)NB + 1)) * sizeof(int32_t); }
+
+__global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs a) {
+    constexpr int NW = kSingleWaves, NT = NW * 64;
+    extern __shared__ __attribute__((aligned(16))) int32_t lds_single[];
+    __shared__ int32_t wsum[NW];
     const int NB = a.E + 1, nbits = bucket_bits(NB);
+    int32_t* cnt = lds_single;
+    int32_t* bstart = cnt + NW * NB;
+    int32_t* tmp = bstart + NB + 1;
     const int w = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
+    for (int i = threadIdx.x; i < NW * NB; i += NT) cnt[i] = 0;
     __syncthreads();
-    const int64_t per = ((a.n + kWaves * 64 - 1) / (kWaves * 64)) * 64;
+    const int64_t per = ((a.n + NW * 64 - 1) / (NW * 64)) * 64;
     const int64_t beg = min((int64_t)w * per, a.n), end = min(beg + per, a.n);
-    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
+    int bk[kPre];   // this wave's ids (per <= kPre batches), kept for the placement
+    load_batches(a.ids, beg, end, a.E, bk);
+    count_batches(bk, beg, end, nbits, cnt + w * NB);
     __syncthreads();
-    for (int b = threadIdx.x; b < NB; b += kThreads) {
-        int32_t run = 0;
-        for (int v = 0; v < kWaves; v++) {
-            const int32_t t = cnt[v * NB + b];
-            cnt[v * NB + b] = run;
-            run += t;
+    // per bucket, exclusive scan of the wave counters: 16 consecutive lanes hold one
+    // bucket's counters (wave order) and scan them with shuffles
+    for (int idx = threadIdx.x; idx < NB * NW; idx += NT) {
+        const int b = idx / NW, v = idx - b * NW;
+        const int32_t c = cnt[v * NB + b];
+        int32_t x = c;
+#pragma unroll
+        for (int d = 1; d < NW; d <<= 1) {
+            const int32_t y = __shfl_up(x, d, NW);
+            if (v >= d) x += y;
         }
-        bstart[b] = run;
+        cnt[v * NB + b] = x - c;
+        if (v == NW - 1) bstart[b] = x;
     }
     __syncthreads();
-    block_scan(bstart, NB, wsum);
-    write_bounds_and_tiles(a, bstart, tmp, wsum);
-    wave_place(a, beg, end, nbits, bstart, cnt + w * NB);
+    block_scan<NT>(bstart, NB, wsum);
+    write_bounds_and_tiles<NT>(a, bstart, tmp, wsum);
+    place_batches(a, bk, beg, end, nbits, bstart, cnt + w * NB);
 }
 
 // ---------------------------------------------------------------- multi-block
@@ -373,7 +410,15 @@ size_t row_ids_scratch_bytes(int64_t n, int32_t E) {
 hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches) {
     RowIdsArgs a = a0;
     if (a.n <= kRowIdsOneBlockMax) {
-        k_row_ids_single<<<1, kThreads, 0, st>>>(a);
+        static bool attr_set = false;   // raise the dynamic LDS cap once per process
+        if (!attr_set) {
+            const hipError_t e = hipFuncSetAttribute((const void*)k_row_ids_single,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)single_lds_bytes(kMaxBuckets));
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        k_row_ids_single<<<1, kSingleWaves * 64, single_lds_bytes(a.E + 1), st>>>(a);
         if (n_launches) *n_launches = 1;
         return hipGetLastError();
     }
