@@ -523,11 +523,12 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 
 // ---------------------------------------------------------------- wide-N variant
 // Same product as k_gemm_q8 for 128-row tiles and K % 64 == 0, with a block tile of
-// 128 activation rows x 512 weight rows. Each of the 8 waves owns 64 weight rows (two
-// MFMA column groups) and all 128 rows, so every activation fragment read from LDS
-// feeds two MFMAs, and a stage of 64 K columns (16 KB activations, 32 KB int8
-// weights) is small enough for a three-slot ring: two stages are in flight while the
-// third is multiplied.
+// 128 activation rows x 64*W weight rows. Each wave owns 64 weight rows (two MFMA column
+// groups) and all 128 rows, so every activation fragment read from LDS feeds two MFMAs.
+// A stage is 64 K columns: 16 KB of activations and, for 4 waves, 16 KB of int8 weights
+// (8 KB of MXFP4 codes). It is dispatched with 4 waves and a two-slot ring, so two
+// independent blocks share a CU and one block's barrier waits, prologue and epilogue
+// overlap the other's multiplies.
 //
 // Scales (SG): with one word per row per stage (SG = 1) every stage touches one cache
 // line per weight row just for 4 bytes, which costs as many memory requests as the
@@ -537,13 +538,15 @@ namespace wide {
 constexpr int KS = 64;
 __device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
-// Block tile 32*MSUB activation rows x 64*W weight rows, W waves, NS ring slots.
-template <int MSUB, int W, int NS>
+// Block tile 32*MSUB activation rows x 64*W weight rows, W waves, NS ring slots; FMT = 1
+// for MXFP4 weights (32-byte rows per stage, two E8M0 scale bytes per row per stage).
+template <int MSUB, int W, int NS, int FMT = 0>
 struct Cfg {
     static constexpr int BM = 32 * MSUB;
     static constexpr int BN = 64 * W;                 // weight rows per block
     static constexpr int A_BYTES = BM * KS * 2;       // 128-byte rows, 8 chunks
-    static constexpr int B_BYTES = BN * KS;           // 64-byte rows, 4 chunks
+    static constexpr int WROW = FMT == 1 ? KS / 2 : KS;   // weight bytes per row per stage
+    static constexpr int B_BYTES = BN * WROW;         // 64-byte rows, 4 chunks (MXFP4: 32, 2)
     static constexpr int NA = BM / (8 * W);           // activation copies (8 rows) per wave
     static constexpr int SGROUP = BN * 16;            // SG = 4: one group of scales
     template <int SG>
@@ -555,11 +558,12 @@ struct Cfg {
 };
 }  // namespace wide
 
-template <int MODE, int SG, int MSUB, int W, int NS>
+template <int MODE, int SG, int MSUB, int W, int NS, int FMT>
 __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs args) {
     using namespace wide;
-    using C = Cfg<MSUB, W, NS>;
+    using C = Cfg<MSUB, W, NS, FMT>;
     static_assert(NS == 2 || NS == 3, "two- or three-slot ring");
+    static_assert(FMT == 0 || (SG == 1 && NS == 2), "MXFP4: per-stage scale words, two slots");
     constexpr int BM = C::BM, A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, NA = C::NA;
     constexpr int SGROUP = C::SGROUP;
     constexpr int NTW = C::template out_cols<MODE>();
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     static_assert(NA * 8 * W == BM, "activation rows must split evenly over the waves");
     // copies per wave per stage: NA activation + 4 weight (+ 1 scale word if SG = 1);
     // with SG = 4 every fourth stage also carries one scale-group copy
-    constexpr int VM_STAGE = NA + 4 + (SG == 1 ? 1 : 0);
+    constexpr int VM_STAGE = NA + (FMT == 1 ? 2 : 4) + (SG == 1 ? 1 : 0);
     static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -657,8 +661,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     }
     // weights: copy i of wave w covers rows 64w + 16i .. +15 (4 lanes x 16 B per row);
     // in gate/up mode odd copies hold up rows
-    const int8_t* qg = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * K);
-    const int8_t* qu = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * K) : qg;
+    const int64_t RB = FMT == 1 ? K / 2 : K;   // bytes per weight row
+    const int8_t* qg = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * RB);
+    const int8_t* qu = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * RB) : qg;
     uint32_t b_off[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -666,15 +671,39 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         const int lc = (lane & 3) ^ swz_wb(R);
         b_off[i] = (uint32_t)((int64_t)wrow(R) * K + lc * 16);
     }
+    // MXFP4: copy i of wave w covers rows 64w + 32i .. +31 (2 lanes x 16 B per row, no
+    // swizzle). Its lanes 0-31 and 32-63 read rows of different matrices in gate/up
+    // mode, so each lane carries its own 64-bit address.
+    const int8_t* b_ptr[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int R = wv * 64 + 32 * i + (lane >> 1);
+        b_ptr[i] = ((MODE == 1 && (R & 16)) ? qu : qg) + (int64_t)wrow(R) * RB + (lane & 1) * 16;
+    }
     // scales: lane l of wave w fetches for row 64w + l, from a per-lane address (gate
     // and up rows sit in different tensors). SG = 1: the word of blocks 2s, 2s+1 at
     // stage s (K % 64 == 0 keeps the pair inside one aligned word); SG = 4: the 16
     // bytes of blocks 8g .. 8g+7 for stages 4g .. 4g+3.
+    // MXFP4: the aligned word holding the row's two scale bytes of stage s (blocks 2s,
+    // 2s + 1: an even byte offset, since K % 64 == 0 makes KB even, so both bytes sit in
+    // one aligned word)
     const uint8_t* s_ptr;
     {
         const int R = wv * 64 + lane;
         const uint16_t* dt = (MODE == 1 && (R & 16)) ? P.d2 : P.d1;
-        s_ptr = (const uint8_t*)(dt + ((int64_t)e * N + wrow(R)) * KB);
+        s_ptr = FMT == 1 ? (const uint8_t*)dt + ((int64_t)e * N + wrow(R)) * KB
+                         : (const uint8_t*)(dt + ((int64_t)e * N + wrow(R)) * KB);
+    }
+    // MXFP4: where the scale row of this lane's weight row in column group c sits
+    // within its aligned word (0 or 2); stage s's bytes start at that + 2s, mod 4
+    int s_al[2] = {0, 0};
+    if constexpr (FMT == 1) {
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int lr = wv * 64 + c * 32 + l32;
+            const uint16_t* dt = (MODE == 1 && (lr & 16)) ? P.d2 : P.d1;
+            s_al[c] = (int)((uintptr_t)((const uint8_t*)dt + ((int64_t)e * N + wrow(lr)) * KB) & 3);
+        }
     }
     const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
 
@@ -683,10 +712,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         const int k0 = s * KS;
 #pragma unroll
         for (int i = 0; i < NA; i++) dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
+        if constexpr (FMT == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            dma16(((MODE == 1 && (i & 1)) ? qu : qg) + k0, b_off[i], st + A_BYTES + (wv * 4 + i) * 1024);
-        if (SG == 1) {
+            for (int i = 0; i < 2; i++) dma16v(b_ptr[i] + k0 / 2, st + A_BYTES + (wv * 2 + i) * 1024);
+            dma4v((const void*)((uintptr_t)(s_ptr + 2 * s) & ~(uintptr_t)3), st + A_BYTES + B_BYTES + wv * 256);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                dma16(((MODE == 1 && (i & 1)) ? qu : qg) + k0, b_off[i], st + A_BYTES + (wv * 4 + i) * 1024);
+        }
+        if (FMT == 1) {
+        } else if (SG == 1) {
             dma4v(s_ptr + 4 * s, st + A_BYTES + B_BYTES + wv * 256);
         } else if ((s & 3) == 0) {
             dma16v(s_ptr + 4 * s, sring + (uint32_t)(((s >> 2) & 1) * SGROUP) + wv * 1024);
@@ -719,22 +755,34 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
                                     : smem + NS * STAGE + ((s >> 2) & 1) * SGROUP + (s & 3) * 4;
         // operands of the stage: both column groups' 32 int8 weights and scale, and
         // the activation fragments of k sub-step 0
+        // The lane's k columns: half h of the stage (k 32h .. 32h + 31, block 2s + h),
+        // 8 of them per k sub-step ss (k 32h + 8ss ..), as the activation fragments
+        // below take them.
         i32x4 q[2][2];
         float d[2];
 #pragma unroll
         for (int c = 0; c < 2; c++) {
             const int lr = wv * 64 + c * 32 + l32;
-            const uint8_t* rowp = st + A_BYTES + lr * 64;
-            q[c][0] = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
-            q[c][1] = *(const i32x4*)(rowp + (((2 * h + 1) ^ swz_wb(lr)) << 4));
-            const uint32_t sw = *(const uint32_t*)(sg + lr * (SG == 1 ? 4 : 16));
-            d[c] = half_bits_to_float((uint16_t)(sw >> (16 * h)));
+            if constexpr (FMT == 1) {
+                // chunk h of the row holds the 32 codes; sub-step ss takes its dword ss
+                q[c][0] = *(const i32x4*)(st + A_BYTES + lr * 32 + 16 * h);
+                const uint32_t sw = *(const uint32_t*)(sg + lr * 4);
+                const int sh = ((s_al[c] + 2 * s) & 3) * 8 + 8 * h;
+                d[c] = __builtin_bit_cast(float, ((sw >> sh) & 255u) << 23);
+            } else {
+                const uint8_t* rowp = st + A_BYTES + lr * 64;
+                q[c][0] = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
+                q[c][1] = *(const i32x4*)(rowp + (((2 * h + 1) ^ swz_wb(lr)) << 4));
+                const uint32_t sw = *(const uint32_t*)(sg + lr * (SG == 1 ? 4 : 16));
+                d[c] = half_bits_to_float((uint16_t)(sw >> (16 * h)));
+            }
         }
         auto afrag = [&](int i, int ss) -> bf16x8 {
             const int r = i * 32 + l32;
             return *(const bf16x8*)(st + r * 128 + (((4 * h + ss) ^ swz_wa(r)) << 4));
         };
         auto deq = [&](int c, int ss) -> bf16x8 {
+            if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[c][0][ss], d[c]);
             const i32x4& v = q[c][ss >> 1];
             return (ss & 1) ? dequant8(v[2], v[3], d[c]) : dequant8(v[0], v[1], d[c]);
         };
@@ -768,8 +816,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
                     acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][c], acc[i][c], 0, 0, 0);
 #ifndef MOE_GEMM_NO_SCHED
             if (ss < 3) {
-                // 2*MACT MFMAs share the sub-step's 40 dequant instructions
-                constexpr int VPM = (40 + 2 * MACT - 1) / (2 * MACT);
+                // 2*MACT MFMAs share the sub-step's dequant instructions (Q8_0: 40,
+                // MXFP4: 8)
+                constexpr int VPM = ((FMT == 1 ? 8 : 40) + 2 * MACT - 1) / (2 * MACT);
 #pragma unroll
                 for (int m = 0; m < 2 * MACT; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -861,19 +910,34 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     }
 }
 
-template <int MODE, int SG, int MSUB, int W, int NS>
+template <int MODE, int SG, int MSUB, int W, int NS, int FMT = 0>
 hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
-    constexpr int lds = wide::Cfg<MSUB, W, NS>::template lds_bytes<SG>();
+    constexpr int lds = wide::Cfg<MSUB, W, NS, FMT>::template lds_bytes<SG>();
     static_assert(lds <= 160 * 1024, "LDS ring exceeds 160 KB");
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W, NS>,
+        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W, NS, FMT>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    k_gemm_q8w<MODE, SG, MSUB, W, NS><<<grid, 64 * W, lds, st>>>(a);
+    k_gemm_q8w<MODE, SG, MSUB, W, NS, FMT><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
+}
+
+// MXFP4 experts on the wide kernel (per-stage scale words only).
+template <int MODE, int MSUB, int W, int NS>
+hipError_t launch_wide_fp4(const GemmArgs& a, hipStream_t st) {
+    constexpr int ntw = wide::Cfg<MSUB, W, NS, 1>::template out_cols<MODE>();
+    int64_t total = 0;
+    for (int i = 0; i < a.n_prob; i++) {
+        const GemmProblem& p = a.p[i];
+        total += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
+    }
+    if (total <= 0) return hipSuccess;
+    GemmArgs g = a;
+    g.grid_real = (int32_t)total;
+    return launch_wide_sg<MODE, 1, MSUB, W, NS, 1>(g, (int)total, st);
 }
 
 template <int MODE, int MSUB, int W, int NS>
@@ -890,8 +954,8 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    return groups ? launch_wide_sg<MODE, 4, MSUB, W, NS>(g, (int)total, st)
-                  : launch_wide_sg<MODE, 1, MSUB, W, NS>(g, (int)total, st);
+    return groups ? launch_wide_sg<MODE, 4, MSUB, W, NS, 0>(g, (int)total, st)
+                  : launch_wide_sg<MODE, 1, MSUB, W, NS, 0>(g, (int)total, st);
 }
 
 template <int MSUB, int W, int NS, int SG, int FMT>
@@ -972,7 +1036,12 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     GemmArgs a = a0;
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
-    if (a.fmt == 1) {   // MXFP4 experts: the 64- and 128-row tiles of the narrow kernel
+    bool wide_ok = true;   // the wide kernels need whole 64-column stages
+    for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
+#ifdef MOE_GEMM_NO_WIDE
+    wide_ok = false;
+#endif
+    if (a.fmt == 1) {   // MXFP4 experts: 64-row tiles on the narrow kernel, 128-row on the wide one
         switch (msub) {
             case 2:
                 // 64-row tiles: 8 waves (256 weight rows) with three slots, one block per
@@ -982,16 +1051,22 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
                 // Lite- and GPT-OSS-shaped PP512 1-3% better with 4.
                 if (narrow_grid<8>(a) >= 2048) return launch_cfg_fp4<2, 8, 3>(a, st);
                 return launch_cfg_fp4<2, 4, 3>(a, st);
-            case 4:   // 128-row tiles: three slots measured no better than two here
+            case 4: {
+                // 128-row tiles: the wide kernel, two blocks per CU. Its per-stage scale
+                // word holds both scale bytes of the stage when the scale rows start at
+                // even addresses. Otherwise the narrow kernel with 8 waves (three slots
+                // measured no better than two there).
+                bool even = true;
+                for (int i = 0; i < a.n_prob; i++)
+                    even = even && ((uintptr_t)a.p[i].d1 & 1) == 0 &&
+                           (a.mode == 0 || ((uintptr_t)a.p[i].d2 & 1) == 0);
+                if (wide_ok && even) return a.mode == 1 ? launch_wide_fp4<1, 4, 4, 2>(a, st)
+                                                        : launch_wide_fp4<0, 4, 4, 2>(a, st);
                 return launch_cfg_fp4<4, 8, 2>(a, st);
+            }
             default: return hipErrorInvalidValue;
         }
     }
-    bool wide_ok = true;   // the wide kernels need whole 64-column stages
-    for (int i = 0; i < a.n_prob; i++) wide_ok = wide_ok && a.p[i].K % wide::KS == 0;
-#ifdef MOE_GEMM_NO_WIDE
-    wide_ok = false;
-#endif
     switch (msub) {
         case 2:
             // 64-row tiles stay on the narrow kernel: on segments of about 50 rows the
