@@ -344,6 +344,36 @@ def test_ffn_mxfp4_gemm(E, k, T, n_embd, n_ff, S, routing):
     assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_MFMA
 
 
+def _odd_offset_scales(w):
+    """The same weights with the scale bytes moved to an odd address (a view one byte
+    into a larger buffer)."""
+    flat = w.scales.reshape(-1)
+    buf = torch.empty(flat.numel() + 1, dtype=torch.uint8, device=flat.device)
+    buf[1:].copy_(flat)
+    return moe.Weights(w.data, buf[1:].view(w.scales.shape))
+
+
+def test_ffn_mxfp4_gemm_128_row_tiles_both_kernels():
+    # 128-row tiles with K % 64 == 0 run the wide kernel when the scale rows start at even
+    # addresses, the narrow one otherwise; both take the same k groups in the same order
+    E, k, T, n_embd, n_ff = 4, 2, 300, 512, 256
+    ids = synth.draw_ids_uniform(12, T, E, k)
+    inp = synth.make_custom_ffn(93, E, k, T, n_embd, n_ff, 1, ids=ids, wtype="mxfp4")
+    dv = upload_ffn(inp)
+    wide = run_ffn(dv, path=moe.PATH_GEMM)
+    odd = dict(dv)
+    for n in ("gate", "up", "down"):
+        odd[n] = _odd_offset_scales(dv[n])
+        assert odd[n].scales.data_ptr() % 2 == 1
+    odd["shared"] = [_odd_offset_scales(w) for w in dv["shared"]]
+    narrow = run_ffn(odd, path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    ref = oracle.ffn(inp)
+    assert normwise(wide.cpu().numpy(), ref) <= TOL_MFMA
+    assert normwise(narrow.cpu().numpy(), ref) <= TOL_MFMA
+    assert torch.equal(wide, narrow)
+
+
 def test_ffn_mxfp4_gemm_invalid_ids_and_scale_zero():
     E, k, T, n_embd, n_ff = 8, 2, 70, 128, 96
     ids = synth.draw_ids_uniform(8, T, E, k)
