@@ -16,11 +16,16 @@ namespace {
 constexpr int kThreads = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kU = 8;  // slots whose rows are loaded together
+constexpr int kU = 8;   // slots whose rows are loaded together
+constexpr int kSh = 2;  // shared-expert rows loaded together with the first slots
 
 // Block = one token x 1024 columns; each thread owns 4 consecutive columns. The
 // token's ids and weights are block-uniform; the k slot rows are loaded kU at a
-// time before they are summed in slot order.
+// time before they are summed in slot order, and the first kSh shared-expert rows
+// are loaded with the first of those batches. Every row is read once and every
+// output written once, so both go through non-temporal accesses: they do not
+// displace lines that other kernels will read again (V3-shaped layer, 2.35 GB
+// moved: 453 -> 379 us).
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
     const int ncb = (a.N + 4 * kThreads - 1) / (4 * kThreads);
@@ -29,6 +34,13 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
     if (c >= a.N) return;
     const int64_t tk = (int64_t)t * a.k;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 vsh[kSh];
+    if (VEC) {
+#pragma unroll
+        for (int j = 0; j < kSh; j++)
+            vsh[j] = j < a.S ? __builtin_nontemporal_load((const f32x4*)(a.ysh + ((int64_t)j * a.T + t) * a.N + c))
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int s0 = 0; s0 < a.k; s0 += kU) {
         f32x4 v[kU];
         float w[kU];
@@ -42,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
             w[u] = ok ? (a.route_w ? a.route_w[tk + s] : 1.0f) : 0.f;
             const float* y = a.y + (tk + (ok ? s : 0)) * a.N + c;
             if (VEC) {
-                v[u] = ok ? *(const f32x4*)y : f32x4{0.f, 0.f, 0.f, 0.f};
+                v[u] = ok ? __builtin_nontemporal_load((const f32x4*)y) : f32x4{0.f, 0.f, 0.f, 0.f};
             } else {
                 for (int q = 0; q < 4; q++) v[u][q] = (ok && c + q < a.N) ? y[q] : 0.f;
             }
@@ -60,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
     for (int j = 0; j < a.S; j++) {
         const float* y = a.ysh + ((int64_t)j * a.T + t) * a.N + c;
         if (VEC) {
-            const f32x4 v = *(const f32x4*)y;
+            const f32x4 v = j < kSh ? vsh[j] : __builtin_nontemporal_load((const f32x4*)y);
             acc[0] += v[0];
             acc[1] += v[1];
             acc[2] += v[2];
@@ -72,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
     }
     float* o = a.out + (int64_t)t * a.N + c;
     if (VEC) {
-        *(f32x4*)o = acc;
+        __builtin_nontemporal_store(acc, (f32x4*)o);
     } else {
         for (int q = 0; q < 4; q++)
             if (c + q < a.N) o[q] = acc[q];
