@@ -174,34 +174,42 @@ __device__ int32_t block_scan(int32_t* v, int n, int32_t* wsum) {
 }
 
 // bstart[0..NB) holds bucket starts: write bounds and the M-tile prefixes (NT threads).
+// tmp[0..E] holds tile table q's exclusive M-tile prefix: one entry per M tile, so the
+// GEMM finds its tile with a single load (NT threads).
+template <int NT = kThreads>
+__device__ void write_tile_tab(const RowIdsArgs& a, int q, const int32_t* bstart, const int32_t* tmp) {
+    for (int b = threadIdx.x; b < a.E; b += NT) {
+        const int32_t lo = bstart[b], hi = bstart[b + 1];
+        for (int32_t j = tmp[b]; j < tmp[b + 1] && j < a.tile_cap[q]; j++) {
+            int32_t* t = a.tile_tab[q] + 4 * (int64_t)j;
+            t[0] = b;
+            t[1] = tmp[b];
+            t[2] = lo;
+            t[3] = hi - lo;
+        }
+    }
+}
+
+// M-tile prefix and tile table q from the bucket starts (NT threads, tmp: LDS scratch).
+template <int NT = kThreads>
+__device__ void write_tiles(const RowIdsArgs& a, int q, const int32_t* bstart, int32_t* tmp, int32_t* wsum) {
+    const int E = a.E, NB = E + 1;
+    const int tm = a.tile_m[q];
+    for (int b = threadIdx.x; b < NB; b += NT)
+        tmp[b] = b < E ? (bstart[b + 1] - bstart[b] + tm - 1) / tm : 0;
+    __syncthreads();
+    block_scan<NT>(tmp, NB, wsum);
+    for (int b = threadIdx.x; b < NB; b += NT) a.tile_off[q][b] = tmp[b];
+    if (a.tile_tab[q]) write_tile_tab<NT>(a, q, bstart, tmp);
+    __syncthreads();
+}
+
 template <int NT = kThreads>
 __device__ void write_bounds_and_tiles(const RowIdsArgs& a, const int32_t* bstart, int32_t* tmp,
                                        int32_t* wsum) {
-    const int E = a.E, NB = E + 1;
-    for (int b = threadIdx.x; b < NB; b += NT) a.bounds[b] = bstart[b];
-    for (int q = 0; q < 2; q++) {
-        if (!a.tile_off[q]) continue;  // uniform across the block
-        const int tm = a.tile_m[q];
-        for (int b = threadIdx.x; b < NB; b += NT)
-            tmp[b] = b < E ? (bstart[b + 1] - bstart[b] + tm - 1) / tm : 0;
-        __syncthreads();
-        block_scan<NT>(tmp, NB, wsum);
-        for (int b = threadIdx.x; b < NB; b += NT) a.tile_off[q][b] = tmp[b];
-        if (a.tile_tab[q]) {
-            // one entry per M tile, so the GEMM finds its tile with a single load
-            for (int b = threadIdx.x; b < E; b += NT) {
-                const int32_t lo = bstart[b], hi = bstart[b + 1];
-                for (int32_t j = tmp[b]; j < tmp[b + 1] && j < a.tile_cap[q]; j++) {
-                    int32_t* t = a.tile_tab[q] + 4 * (int64_t)j;
-                    t[0] = b;
-                    t[1] = tmp[b];
-                    t[2] = lo;
-                    t[3] = hi - lo;
-                }
-            }
-        }
-        __syncthreads();
-    }
+    for (int b = threadIdx.x; b < a.E + 1; b += NT) a.bounds[b] = bstart[b];
+    for (int q = 0; q < 2; q++)
+        if (a.tile_off[q]) write_tiles<NT>(a, q, bstart, tmp, wsum);  // uniform across the block
 }
 
 __device__ __forceinline__ int bucket_bits(int NB) { return 32 - __clz(NB - 1); }
@@ -251,8 +259,48 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
         if (v == NW - 1) bstart[b] = x;
     }
     __syncthreads();
-    block_scan<NT>(bstart, NB, wsum);
-    write_bounds_and_tiles<NT>(a, bstart, tmp, wsum);
+    // wave 0 alone: exclusive scans of the bucket counts (into bucket starts and bounds)
+    // and, for the first tile table, of the experts' M-tile counts, with shuffles and no
+    // block barrier (two block-wide scans took about 2 us of the pass)
+    const int tm0 = a.tile_off[0] ? a.tile_m[0] : 0;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int per = (NB + 63) >> 6;
+        const int b0 = min(lane * per, NB), b1 = min(b0 + per, NB);
+        int32_t sc = 0, stl = 0;
+        for (int b = b0; b < b1; b++) {
+            const int32_t c = bstart[b];
+            sc += c;
+            if (tm0 && b < a.E) stl += (c + tm0 - 1) / tm0;
+        }
+        int32_t xc = sc, xt = stl;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t yc = __shfl_up(xc, d), yt = __shfl_up(xt, d);
+            if (lane >= d) {
+                xc += yc;
+                xt += yt;
+            }
+        }
+        int32_t rc = xc - sc, rt = xt - stl;
+        for (int b = b0; b < b1; b++) {
+            const int32_t c = bstart[b];
+            bstart[b] = rc;
+            a.bounds[b] = rc;
+            rc += c;
+            if (tm0) {
+                tmp[b] = rt;
+                a.tile_off[0][b] = rt;
+                if (b < a.E) rt += (c + tm0 - 1) / tm0;
+            }
+        }
+    }
+    __syncthreads();
+    if (tm0 && a.tile_tab[0]) write_tile_tab<NT>(a, 0, bstart, tmp);
+    if (a.tile_off[1]) {   // a second tile table: the block-wide path (tmp is reused)
+        __syncthreads();
+        write_tiles<NT>(a, 1, bstart, tmp, wsum);
+    }
     place_batches(a, bk, beg, end, nbits, bstart, cnt + w * NB);
 }
 
