@@ -46,6 +46,9 @@ def test_row_ids_configs_bit_exact(name, B_is_k):
     (64, 3000, 12, 0, 64, 6),    # 36000 entries: the multi-workgroup pass
     (256, 9000, 8, -3, 260, 7),  # multi-workgroup with invalid ids
     (5, 1, 3, 0, 5, 8),          # a single token
+    (64, 512, 8, -1, 65, 9),     # 4096 entries: the largest one-workgroup input (4 batches a wave)
+    (1024, 1024, 4, 0, 1024, 10),  # 4096 entries over 1025 buckets: 17 buckets per lane in the scan
+    (64, 4097, 1, 0, 64, 11),    # 4097 entries: the smallest multi-workgroup input
 ])
 def test_row_ids_random_shapes(E, T, k, lo, hi, seed):
     ids = np.random.default_rng(seed).integers(lo, hi, size=(T, k)).astype(np.int32)
