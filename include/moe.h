@@ -52,7 +52,10 @@
  *
  * Limits (MOE_ELIMIT): n_tokens < 2^22 and n_used < 2^10 (the bounds the page
  * above quotes for safe 32-bit packing, section 2.1), n_tokens * n_used < 2^31,
- * n_experts <= 1024, Q8_0 and MXFP4 cols % 32 == 0.
+ * n_experts <= 1024, Q8_0 and MXFP4 cols % 32 == 0. On the grouped GEMM path the
+ * activation tensor whose rows are gathered through the row map (moe_ffn_fused: x;
+ * moe_mul_mat_id: src1) must be under 4 GiB, and each GEMM launch must hold fewer
+ * than 2^32 work-items; float32 moe_mul_mat_id needs n_tokens * n_used * N < 2^32.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -128,7 +131,8 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
  *            src1) or (MXFP4 w, BF16 src1) on the MFMA grouped GEMM or the GEMV path
  *            (MXFP4 on the GEMV path: n_tokens * n_used <= 64 and K <= 4096, else the
  *            GEMM path is taken, and forcing the GEMV path is MOE_EINVAL); (F32 w, F32
- *            src1).
+ *            src1), which has one path, the fp32 grouped product: opt->path must be
+ *            0 or 1 (else MOE_EINVAL).
  *   src1     device [n_tokens][B][K], B = src1_rows_per_token in {1, n_used}
  *   ids      device int32 [n_tokens][n_used]
  *   route_w  NULL: dst = float32 [n_tokens][n_used][N], dst[t][s] = W_{ids[t][s]} src1_row;
@@ -142,7 +146,12 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
- * moe_ffn_fused -- MoE FFN layer on the indirect matmul:
+ * moe_ffn_fused -- MoE FFN layer on the indirect matmul: the gate and up projections
+ * with the fused up/gate forward SiLU(gate) * up ("CUDA: better MoE implementation",
+ * section 4.2), the down projection, and the deterministic reorder and fixed-order
+ * reduction of the routed slots (sections 2.1 and 6), plus the always-on shared
+ * experts computed in the same operation ("CUDA: fuse shared experts into MMVQ",
+ * llama.cpp release b11370; optional, so checked for null):
  *   out[t] = sum_{s ascending, valid} route_w[t][s] * Wd_e (silu(Wg_e x_t) * (Wu_e x_t)),
  *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
  *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
@@ -171,10 +180,15 @@ moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const m
  *   logits   device float32 [n_tokens][n_experts]
  *   ids      device int32 [n_tokens][n_used] (written): the n_used largest logits of
  *            each token in descending order, equal logits taken lower index first;
- *            NaN logits rank below every number
+ *            NaN logits rank strictly below every number, -inf included (NaNs among
+ *            themselves: lower index first)
  *   route_w  device float32 [n_tokens][n_used] (written): softmax over the picked
  *            logits only (exp(v_r - v_0) / sum_r exp(v_r - v_0)), the weighting the
- *            DeepSeek-V3-shaped configuration calls softmax renormalised over the picks
+ *            DeepSeek-V3-shaped configuration calls softmax renormalised over the
+ *            picks. A NaN pick is weighted as -inf (weight 0). When the largest pick
+ *            v_0 is +inf or -inf the softmax's limit is used: the c picks equal to v_0
+ *            get 1/c each and the others 0 (a token whose picks are all -inf or NaN
+ *            gets 1/n_used on every pick)
  * Requires 1 <= n_used <= n_experts <= 1024 (MOE_EINVAL / MOE_ELIMIT otherwise) and
  * n_tokens < 2^22. No workspace. Deterministic. n_tokens = 0 is a no-op.
  */

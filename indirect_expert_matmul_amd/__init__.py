@@ -176,12 +176,47 @@ def _xtype(t: torch.Tensor) -> int:
     raise ValueError("activations must be float32 or bfloat16 (or its 16-bit patterns)")
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], stream=None):
+    """The caller's workspace, or a temporary one. A temporary is allocated by torch's
+    caching allocator on its current stream; when the kernels run on another stream it
+    is marked as used there (record_stream), so its memory is not handed out again
+    before those kernels have finished with it."""
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes:
             raise ValueError("workspace too small: need %d bytes" % nbytes)
         return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _keep_alive(stream, t)
+    return t
+
+
+def _keep_alive(stream, *tensors):
+    """Mark torch-allocated tensors as in use on ``stream`` when it is not torch's current
+    stream (the kernels are enqueued there, asynchronously)."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream(tensors[0].device if tensors else None)
+    if stream.cuda_stream != cur.cuda_stream:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(stream)
+
+
+def _check_ids(ids: torch.Tensor, route_w: Optional[torch.Tensor] = None):
+    """ids must be int32 [T][k] (torch.topk gives int64, which would be read as wrong
+    experts), route_w float32 of the same shape."""
+    if ids.dtype != torch.int32 or ids.dim() != 2:
+        raise ValueError("ids must be int32 [n_tokens][n_used] (got %s of shape %s)"
+                         % (ids.dtype, tuple(ids.shape)))
+    if route_w is not None and (route_w.dtype != torch.float32 or tuple(route_w.shape) != tuple(ids.shape)):
+        raise ValueError("route_w must be float32 [n_tokens][n_used] like ids (got %s of shape %s)"
+                         % (route_w.dtype, tuple(route_w.shape)))
+
+
+def _check_out(out: Optional[torch.Tensor], shape):
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != tuple(shape)):
+        raise ValueError("out must be float32 of shape %s (got %s of shape %s)"
+                         % (tuple(shape), out.dtype, tuple(out.shape)))
 
 
 def moe_select_path(n_tokens: int, n_used: int, n_experts: int, act_width: int,
@@ -195,16 +230,16 @@ def moe_select_path(n_tokens: int, n_used: int, n_experts: int, act_width: int,
 def moe_row_ids(ids: torch.Tensor, n_experts: int, src1_rows_per_token: int = 1, stream=None,
                 workspace: Optional[torch.Tensor] = None):
     """(ids_src1, ids_dst, expert_bounds) for ids int32 [T][k] on the GPU."""
+    _check_ids(ids)
     _dev_check(ids)
-    if ids.dtype != torch.int32 or ids.dim() != 2:
-        raise ValueError("ids must be int32 [n_tokens][n_used]")
     T, k = ids.shape
     dev = ids.device
     s1 = torch.empty(T * k, dtype=torch.int32, device=dev)
     dd = torch.empty(T * k, dtype=torch.int32, device=dev)
     b = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    _keep_alive(stream, s1, dd, b)
     need = lib.moe_row_ids_workspace_size(T, k, n_experts)
-    ws = _workspace(need, dev, workspace)
+    ws = _workspace(need, dev, workspace, stream)
     _check(lib.moe_row_ids(ids.data_ptr(), T, k, n_experts, src1_rows_per_token, s1.data_ptr(),
                            dd.data_ptr(), b.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_row_ids")
@@ -216,18 +251,21 @@ def moe_router_topk(logits: torch.Tensor, n_used: int, ids: Optional[torch.Tenso
     """(ids int32 [T][k], route_w float32 [T][k]) from router logits float32 [T][E]:
     the k largest logits per token (equal logits: lower index first), weighted by a
     softmax over the picked logits."""
-    _dev_check(logits)
     if logits.dtype != torch.float32 or logits.dim() != 2 or not logits.is_contiguous():
         raise ValueError("logits must be contiguous float32 [n_tokens][n_experts]")
+    _dev_check(logits)
     T, E = logits.shape
     dev = logits.device
     if ids is None:
         ids = torch.empty((T, n_used), dtype=torch.int32, device=dev)
+        _keep_alive(stream, ids)
     if route_w is None:
         route_w = torch.empty((T, n_used), dtype=torch.float32, device=dev)
+        _keep_alive(stream, route_w)
     if ids.shape != (T, n_used) or ids.dtype != torch.int32 or route_w.shape != (T, n_used) \
             or route_w.dtype != torch.float32:
         raise ValueError("ids / route_w must be int32 / float32 [n_tokens][n_used]")
+    _dev_check(ids, route_w)
     _check(lib.moe_router_topk(logits.data_ptr(), T, E, n_used, ids.data_ptr(), route_w.data_ptr(),
                                _stream(stream)), "moe_router_topk")
     return ids, route_w
@@ -246,18 +284,24 @@ def moe_mul_mat_id(w: Weights, src1: torch.Tensor, ids: torch.Tensor,
                    path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None, events=None):
     """GGML_OP_MUL_MAT_ID: float32 [T][k][N] per slot, or [T][N] weighted by route_w."""
-    _dev_check(src1, ids, route_w, out)
+    _check_ids(ids, route_w)
     T, k = ids.shape
     cw = w.c()
     N = cw.rows
+    shape = (T, N) if route_w is not None else (T, k, N)
+    _check_out(out, shape)
+    if src1.dim() < 2 or src1.numel() != T * src1_rows_per_token * cw.cols:
+        raise ValueError("src1 must hold [n_tokens][src1_rows_per_token][K] = %d x %d x %d elements"
+                         % (T, src1_rows_per_token, cw.cols))
+    _dev_check(src1, ids, route_w, out)
     if out is None:
-        shape = (T, N) if route_w is not None else (T, k, N)
         out = torch.empty(shape, dtype=torch.float32, device=ids.device)
+        _keep_alive(stream, out)
     st = _xtype(src1)
     opt = _options(path, tau, events)
     need = lib.moe_mul_mat_id_workspace_size(ctypes.byref(cw), st, src1_rows_per_token, T, k,
                                              ctypes.byref(opt))
-    ws = _workspace(need, ids.device, workspace)
+    ws = _workspace(need, ids.device, workspace, stream)
     _check(lib.moe_mul_mat_id(ctypes.byref(cw), src1.data_ptr(), st, src1_rows_per_token,
                               ids.data_ptr(), T, k,
                               None if route_w is None else route_w.data_ptr(), out.data_ptr(),
@@ -280,17 +324,22 @@ def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, id
                   path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None, events=None):
     """Fused MoE FFN: float32 [T][n_embd]."""
-    _dev_check(x, ids, route_w, out)
+    _check_ids(ids, route_w)
     T, k = ids.shape
     cg, cu, cd = gate.c(), up.c(), down.c()
+    _check_out(out, (T, cg.cols))
+    if x.dim() != 2 or tuple(x.shape) != (T, cg.cols):
+        raise ValueError("x must be [n_tokens][n_embd] = [%d][%d] (got %s)" % (T, cg.cols, tuple(x.shape)))
+    _dev_check(x, ids, route_w, out)
     cs = [s.c() for s in shared] if shared else [None, None, None]
     if out is None:
         out = torch.empty((T, cg.cols), dtype=torch.float32, device=x.device)
+        _keep_alive(stream, out)
     opt = _options(path, tau, events)
     need = lib.moe_ffn_fused_workspace_size(ctypes.byref(cg),
                                             ctypes.byref(cs[0]) if cs[0] is not None else None,
                                             MOE_BF16, T, k, ctypes.byref(opt))
-    ws = _workspace(need, x.device, workspace)
+    ws = _workspace(need, x.device, workspace, stream)
     ref = [ctypes.byref(c) if c is not None else None for c in cs]
     _check(lib.moe_ffn_fused(ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd), ref[0], ref[1],
                              ref[2], x.data_ptr(), _xtype(x), ids.data_ptr(), route_w.data_ptr(), T,

@@ -892,10 +892,10 @@ __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_
     }
 }
 
-// Waves of a kernel that fit on the chip at once (queried once per kernel).
+// Waves of a kernel that fit on the chip at once (queried once per kernel and device).
 template <class Kern>
-int resident_waves(Kern kern, size_t lds, int& cache) {
-    if (cache == 0) {
+hipError_t resident_waves(Kern kern, size_t lds, PerDeviceOnce& cache, int* waves) {
+    return once_per_device(cache, [&](int& v) {
         int dev = 0, n_cu = 0, per_cu = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -904,9 +904,9 @@ int resident_waves(Kern kern, size_t lds, int& cache) {
             n_cu = 256;
             per_cu = 2;
         }
-        cache = n_cu * per_cu * 4;
-    }
-    return cache;
+        v = n_cu * per_cu * 4;
+        return hipSuccess;
+    }, waves);
 }
 
 // Rows per wave, at least 4 so the per-wave start (ids, expert search, activation
@@ -932,23 +932,16 @@ int rows_per_wave(const DecArgs& a, int waves) {
 #define MOE_DEC_FUSE_BLOCKS 512
 #endif
 
-template <bool STREAM>
-hipError_t set_stream_lds(const void* kern, int lds, bool& done) {
-    if (!STREAM || done) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 template <int MODE, int P, bool XBF16, int NIT, int FMT>
 hipError_t launch_stream(DecArgs a, hipStream_t st) {
     constexpr int lds = StreamSlot<MODE, NIT>::LDS;
     static_assert(lds <= 150 * 1024, "ring exceeds LDS");
-    static int cache = 0;
-    static bool attr_set = false;   // raise the dynamic LDS cap once per process
-    if (hipError_t e = set_stream_lds<true>((const void*)k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, attr_set))
-        return e;
-    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, cache));
+    static PerDeviceOnce lds_cap, occ;   // dynamic LDS cap, resident waves: once per device
+    const void* kern = (const void*)k_decode_stream<MODE, P, XBF16, NIT, FMT>;
+    if (hipError_t e = set_lds_cap(lds_cap, kern, lds)) return e;
+    int waves = 0;
+    if (hipError_t e = resident_waves(k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, occ, &waves)) return e;
+    a.rows_per_block = rows_per_wave(a, waves);
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
@@ -960,8 +953,10 @@ hipError_t launch_stream(DecArgs a, hipStream_t st) {
 
 template <int MODE, bool XBF16, int NIT, int FMT>
 hipError_t launch_regs(DecArgs a, hipStream_t st) {
-    static int cache = 0;
-    a.rows_per_block = rows_per_wave(a, resident_waves(k_decode_wave<MODE, 1, XBF16, NIT, FMT>, 0, cache));
+    static PerDeviceOnce occ;
+    int waves = 0;
+    if (hipError_t e = resident_waves(k_decode_wave<MODE, 1, XBF16, NIT, FMT>, 0, occ, &waves)) return e;
+    a.rows_per_block = rows_per_wave(a, waves);
     const int R = a.rows_per_block;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
                    (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
@@ -974,10 +969,11 @@ template <bool XBF16, int NIT, bool STREAM, int FMT>
 hipError_t launch_down_reduce(DecArgs a, hipStream_t st) {
     constexpr int lds = STREAM ? StreamSlot<0, NIT>::LDS : 0;
     constexpr int P = STREAM ? 2 : 1;
-    static bool attr_set = false;
-    if (hipError_t e = set_stream_lds<STREAM>((const void*)k_decode_down_reduce<P, XBF16, NIT, STREAM, FMT>,
-                                              lds, attr_set))
-        return e;
+    if constexpr (STREAM) {
+        static PerDeviceOnce lds_cap;
+        if (hipError_t e = set_lds_cap(lds_cap, (const void*)k_decode_down_reduce<P, XBF16, NIT, STREAM, FMT>, lds))
+            return e;
+    }
     const int N = a.rw.N;
     int R = (N + MOE_DEC_FUSE_BLOCKS - 1) / MOE_DEC_FUSE_BLOCKS;
     R = R < 1 ? 1 : (R > kFuseRows ? kFuseRows : R);

@@ -230,8 +230,13 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         return min(n, N - 1);
     };
 
-    // ---- copy geometry: wave-uniform bases, per-lane 32-bit byte offsets (stage 0)
-    const uint8_t* a_base = (const uint8_t*)uniform_ptr(P.A);
+    // ---- copy geometry: wave-uniform bases, per-lane 32-bit byte offsets (stage 0).
+    // Rows that are not gathered sit next to each other inside the tile and are
+    // addressed from the tile's first row, so their offsets stay small whatever the
+    // size of A; gathered rows are addressed from A itself (the host keeps a gathered
+    // A under 4 GiB).
+    const int64_t a_row0 = P.a_rows ? 0 : (P.a_row_mod ? m0 % P.a_row_mod : m0);
+    const uint8_t* a_base = (const uint8_t*)uniform_ptr((const uint8_t*)P.A + a_row0 * P.lda * 2);
     uint32_t a_off[NA];
     int a_lc[NA];
 #pragma unroll
@@ -239,8 +244,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         const int R = (wv * NA + i) * 4 + (lane >> 4);  // tile row this lane fetches
         const int lc = (lane & 15) ^ swz_a(R);           // logical 16-byte chunk
         const int j = m0 + min(R, m_len - 1);
-        const int64_t src = P.a_rows ? (int64_t)P.a_rows[j]
-                                     : (int64_t)(P.a_row_mod ? j % P.a_row_mod : j);
+        const int64_t src = P.a_rows ? (int64_t)P.a_rows[j] : (int64_t)(j - m0);
         a_off[i] = (uint32_t)(src * P.lda * 2 + lc * 16);
         a_lc[i] = lc;
     }
@@ -653,16 +657,17 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         return min(n, N - 1);
     };
 
-    // ---- copy geometry (stage 0)
-    const uint8_t* a_base = (const uint8_t*)uniform_ptr(P.A);
+    // ---- copy geometry (stage 0); rows that are not gathered are addressed from the
+    // tile's first row, as in k_gemm_q8
+    const int64_t a_row0 = P.a_rows ? 0 : (P.a_row_mod ? m0 % P.a_row_mod : m0);
+    const uint8_t* a_base = (const uint8_t*)uniform_ptr((const uint8_t*)P.A + a_row0 * P.lda * 2);
     uint32_t a_off[NA];
 #pragma unroll
     for (int i = 0; i < NA; i++) {
         const int R = (wv * NA + i) * 8 + (lane >> 3);    // tile row this lane fetches
         const int lc = (lane & 7) ^ swz_wa(R);
         const int j = m0 + min(R, m_len - 1);
-        const int64_t src = P.a_rows ? (int64_t)P.a_rows[j]
-                                     : (int64_t)(P.a_row_mod ? j % P.a_row_mod : j);
+        const int64_t src = P.a_rows ? (int64_t)P.a_rows[j] : (int64_t)(j - m0);
         a_off[i] = (uint32_t)(src * P.lda * 2 + lc * 16);
     }
     // weights: copy i of wave w covers rows 64w + 16i .. +15 (4 lanes x 16 B per row);
@@ -920,13 +925,9 @@ template <int MODE, int SG, int MSUB, int W, int NS, int FMT = 0>
 hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
     constexpr int lds = wide::Cfg<MSUB, W, NS, FMT>::template lds_bytes<SG>();
     static_assert(lds <= 160 * 1024, "LDS ring exceeds 160 KB");
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8w<MODE, SG, MSUB, W, NS, FMT>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static PerDeviceOnce lds_cap;
+    if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_gemm_q8w<MODE, SG, MSUB, W, NS, FMT>, lds))
+        return e;
     k_gemm_q8w<MODE, SG, MSUB, W, NS, FMT><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
 }
@@ -974,13 +975,9 @@ template <int MSUB, int MODE, int W, int NS, int SG, int FMT>
 hipError_t launch_one(const GemmArgs& a, int grid, hipStream_t st) {
     constexpr int lds = stage_lds<MSUB, W, NS, SG, FMT>();
     static_assert(lds + 32 * MSUB * 4 <= 160 * 1024, "LDS rings exceed 160 KB");
-    static bool attr_set = false;   // raise the dynamic LDS cap once per process
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute((const void*)k_gemm_q8<MSUB, MODE, W, NS, SG, FMT>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static PerDeviceOnce lds_cap;   // raise the dynamic LDS cap once per device
+    if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_gemm_q8<MSUB, MODE, W, NS, SG, FMT>, lds))
+        return e;
     k_gemm_q8<MSUB, MODE, W, NS, SG, FMT><<<grid, 64 * W, lds, st>>>(a);
     return hipGetLastError();
 }
@@ -1032,6 +1029,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int64_t gemm_q8_max_threads(const GemmArgs& a0, int msub) {
+    GemmArgs a = a0;
+    if (a.n_prob < 2) a.p[1] = GemmProblem{};
+    // every kernel variant the dispatch below may pick for this tile height
+    int64_t wide = 0;
+    for (int i = 0; i < a.n_prob; i++) {
+        const GemmProblem& p = a.p[i];
+        const int ntw = a.mode == 1 ? 128 : 256;   // the wide kernel's 256 weight rows
+        wide += ((int64_t)p.m_tiles_max * ((p.N + ntw - 1) / ntw) + 7) / 8 * 8;
+    }
+    int64_t t = narrow_grid<8>(a) * 512;
+    if (msub == 2) t = t > narrow_grid<4>(a) * 256 ? t : narrow_grid<4>(a) * 256;
+    else t = t > wide * 256 ? t : wide * 256;
+    return t;
+}
 
 int gemm_pick_msub(double avg_rows) {
     if (avg_rows <= 64) return 2;

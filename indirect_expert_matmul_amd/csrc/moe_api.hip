@@ -294,6 +294,21 @@ RowIdsArgs row_ids_args(const int32_t* ids, int64_t n, int32_t k, int32_t E, int
     return a;
 }
 
+constexpr int64_t k4GiB = 1LL << 32;
+
+// Launch limits of the grouped GEMM path, checked before anything is enqueued:
+// activation rows gathered through the row map are addressed by 32-bit byte offsets
+// from the tensor's start, and one dispatch holds fewer than 2^32 work-items.
+moe_status check_gemm_limits(const GemmArgs& g, int msub, int64_t gathered_rows, int64_t lda,
+                             const char* what) {
+    if (gathered_rows * lda * 2 > k4GiB - 256)
+        return fail(MOE_ELIMIT, "%s: the gathered bf16 activation tensor must be under 4 GiB "
+                    "(%lld rows x %lld columns)", what, (long long)gathered_rows, (long long)lda);
+    if (gemm_q8_max_threads(g, msub) >= k4GiB)
+        return fail(MOE_ELIMIT, "%s: the grouped GEMM grid exceeds 2^32 work-items", what);
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -413,9 +428,6 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         ra.tile_m[0] = bm;
         ra.tile_tab[0] = p.r.tile_tab;
         ra.tile_cap[0] = p.r.tile_cap;
-        tm.begin();
-        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
-        tm.end();
 
         GemmArgs g{};
         g.mode = 1;
@@ -457,9 +469,6 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
             q.ldo = d.n_ff_sh;
             q.w_once = d.T <= bm;
         }
-        tm.begin();
-        if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "gate/up grouped GEMM"))) return s;
-        tm.end();
 
         GemmArgs g2{};
         g2.mode = 0;
@@ -496,6 +505,16 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
             q.ldo = d.n_embd;
             q.w_once = d.T <= bm;
         }
+        // x is gathered through the row map; h and the shared rows are read in order
+        if ((s = check_gemm_limits(g, p.msub, d.T, d.n_embd, "gate/up"))) return s;
+        if ((s = check_gemm_limits(g2, p.msub, 0, d.n_ff, "down"))) return s;
+
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "gate/up grouped GEMM"))) return s;
+        tm.end();
         tm.begin();
         if ((s = hip_check(launch_gemm_q8(g2, p.msub, st), "down grouped GEMM"))) return s;
         tm.end();
@@ -582,6 +601,7 @@ size_t moe_mul_mat_id_workspace_size(const moe_weights* w, moe_dtype src1_type,
                                      int32_t n_used, const moe_options* opt) {
     if (validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used)) return 0;
     const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
+    if (!q8 && opt && opt->path != 0 && opt->path != 1) return 0;
     const int path = q8 ? select_path_fmt(n_tokens, n_used, (int32_t)w->n_mat, w->cols,
                                           w->type == MOE_MXFP4, opt)
                         : 1;
@@ -607,6 +627,11 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
     const int32_t E = (int32_t)w->n_mat, N = (int32_t)w->rows, K = (int32_t)w->cols;
     const int32_t B = src1_rows_per_token, k = n_used;
+    if (!q8 && opt && opt->path != 0 && opt->path != 1)
+        return fail(MOE_EINVAL, "float32 experts run the grouped fp32 product only: options.path "
+                    "must be 0 or 1 (got %d)", opt->path);
+    if (!q8 && n_tokens * k * (int64_t)N >= k4GiB - 256)
+        return fail(MOE_ELIMIT, "float32 mul_mat_id: n_tokens * n_used * N must be under 2^32");
     const int path = q8 ? select_path_fmt(n_tokens, k, E, K, w->type == MOE_MXFP4, opt) : 1;
     if (path < 0) return (moe_status)path;
     const bool weighted = route_w != nullptr;
@@ -623,17 +648,12 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     if (!q8 || path == 1) {
         const int bm = gemm_tile_m(p.msub);
         RowIdsArgs ra = row_ids_args(ids, n, k, E, B, p.r);
+        GemmArgs g{};
         if (q8) {
             ra.tile_off[0] = p.r.tile_a;
             ra.tile_m[0] = bm;
             ra.tile_tab[0] = p.r.tile_tab;
             ra.tile_cap[0] = p.r.tile_cap;
-        }
-        tm.begin();
-        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
-        tm.end();
-        if (q8) {
-            GemmArgs g{};
             g.mode = 0;
             g.fmt = w->type == MOE_MXFP4 ? 1 : 0;
             g.n_prob = 1;
@@ -654,24 +674,30 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
+            if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
+        }
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+        if (q8) {
             tm.begin();
             if ((s = hip_check(launch_gemm_q8(g, p.msub, st), "grouped GEMM"))) return s;
             tm.end();
         } else {
-            GemmF32Args g{};
-            g.W = (const float*)w->data;
-            g.A = (const float*)src1;
-            g.ids = ids;
-            g.ids_src1 = p.r.ids_src1;
-            g.ids_dst = p.r.ids_dst;
-            g.bounds = p.r.bounds;
-            g.n_slots = n;
-            g.E = E;
-            g.N = N;
-            g.K = K;
-            g.out = slot_out;
+            GemmF32Args gf{};
+            gf.W = (const float*)w->data;
+            gf.A = (const float*)src1;
+            gf.ids = ids;
+            gf.ids_src1 = p.r.ids_src1;
+            gf.ids_dst = p.r.ids_dst;
+            gf.bounds = p.r.bounds;
+            gf.n_slots = n;
+            gf.E = E;
+            gf.N = N;
+            gf.K = K;
+            gf.out = slot_out;
             tm.begin();
-            if ((s = hip_check(launch_gemm_f32(g, st), "fp32 grouped matmul"))) return s;
+            if ((s = hip_check(launch_gemm_f32(gf, st), "fp32 grouped matmul"))) return s;
             tm.end();
         }
     } else {

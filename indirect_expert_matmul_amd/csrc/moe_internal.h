@@ -5,7 +5,50 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace moe {
+
+// ---------------------------------------------------------------- per-device set-up
+// One-time set-up that depends on the device (raising a kernel's dynamic LDS cap, an
+// occupancy query): each kernel keeps one PerDeviceOnce. The first call on a device
+// runs the set-up under the lock and stores its int result; later calls on that device
+// read it without locking. Safe to call from several host threads at once.
+constexpr int kMaxDevices = 64;
+struct PerDeviceOnce {
+    std::mutex mu;
+    std::atomic<int> done[kMaxDevices];
+    int value[kMaxDevices];
+};
+// f(int& value) -> hipError_t runs once per device (the current one); on success the
+// stored value is returned through *value (if given). A failed set-up is retried by
+// the next call.
+template <class F>
+hipError_t once_per_device(PerDeviceOnce& o, F&& f, int* value = nullptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (o.done[dev].load(std::memory_order_acquire) == 0) {
+        std::lock_guard<std::mutex> g(o.mu);
+        if (o.done[dev].load(std::memory_order_relaxed) == 0) {
+            int v = 0;
+            e = f(v);
+            if (e != hipSuccess) return e;
+            o.value[dev] = v;
+            o.done[dev].store(1, std::memory_order_release);
+        }
+    }
+    if (value) *value = o.value[dev];
+    return hipSuccess;
+}
+// Raise kern's dynamic LDS cap to bytes, once per device.
+inline hipError_t set_lds_cap(PerDeviceOnce& o, const void* kern, int bytes) {
+    return once_per_device(o, [&](int&) {
+        return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    });
+}
 
 // ---------------------------------------------------------------- limits
 constexpr int kMaxExperts = 1024;          // row-id pass keeps per-wave counters in LDS
@@ -81,6 +124,9 @@ struct GemmArgs {
 int gemm_pick_msub(double avg_rows);
 int gemm_tile_m(int msub);
 hipError_t launch_gemm_q8(const GemmArgs& a, int msub, hipStream_t st);
+// Upper bound on the work-items launch_gemm_q8 would launch for these arguments (a
+// dispatch holds fewer than 2^32).
+int64_t gemm_q8_max_threads(const GemmArgs& a, int msub);
 
 // ---------------------------------------------------------------- fp32 grouped matmul (Tiny)
 struct GemmF32Args {

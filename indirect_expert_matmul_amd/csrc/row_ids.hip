@@ -458,14 +458,10 @@ size_t row_ids_scratch_bytes(int64_t n, int32_t E) {
 hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches) {
     RowIdsArgs a = a0;
     if (a.n <= kRowIdsOneBlockMax) {
-        static bool attr_set = false;   // raise the dynamic LDS cap once per process
-        if (!attr_set) {
-            const hipError_t e = hipFuncSetAttribute((const void*)k_row_ids_single,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)single_lds_bytes(kMaxBuckets));
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static PerDeviceOnce lds_cap;   // raise the dynamic LDS cap once per device
+        if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_single,
+                                             (int)single_lds_bytes(kMaxBuckets)))
+            return e;
         k_row_ids_single<<<1, kSingleWaves * 64, single_lds_bytes(a.E + 1), st>>>(a);
         if (n_launches) *n_launches = 1;
         return hipGetLastError();
@@ -476,14 +472,10 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
     // bucket order (an int and a short per entry)
     const int64_t NB = a.E + 1;
     const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 6;
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(
-            (const void*)k_row_ids_place, hipFuncAttributeMaxDynamicSharedMemorySize,
-            (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 6));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static PerDeviceOnce lds_cap;
+    if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place,
+                                         (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 6)))
+        return e;
     k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
     k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
     k_row_ids_scan_buckets<<<1, kThreads, 0, st>>>(a);

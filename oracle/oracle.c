@@ -367,10 +367,23 @@ int oracle_ffn(int w_type, const void *g_data, const void *g_scales, const void 
  * experts with the largest logits and weight them by a softmax over the picked
  * logits alone. The pages' op takes ids as given ("CUDA: better MoE implementation",
  * section 1.2: ids names the experts each token uses); the weights follow the
- * softmax renormalised over the picks. Picks are made one at a time, each the
- * largest remaining logit, equal logits going to the lower expert index, so the
- * order inside a token is descending logit. NaN logits rank below every number.
+ * softmax renormalised over the picks.
+ *
+ * Order: picks are made one at a time, each the largest remaining logit, equal
+ * logits going to the lower expert index, so the order inside a token is descending
+ * logit. NaN ranks strictly below every number, -inf included; NaNs among
+ * themselves go lower index first.
+ *
+ * Weights (a reading: the pages define no weights for non-finite logits): a NaN pick
+ * counts as -inf. With v_0 the first (largest) pick:
+ *   v_0 finite:   w_r = exp(v_r - v_0) / sum_q exp(v_q - v_0)   (-inf picks get 0);
+ *   v_0 = +-inf:  the softmax's limit -- the c picks equal to v_0 get 1/c each, the
+ *                 rest 0 (all picks -inf or NaN: every pick gets 1/k).
  * ids int32[T][k], w float64[T][k]. */
+
+/* Rank key of a logit: 0 for NaN, 1 for every number (compared first). */
+static int router_rank_class(float x) { return isnan(x) ? 0 : 1; }
+
 int oracle_router_topk(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *ids,
                        double *w) {
     if (!logits || !ids || !w || T < 0 || E <= 0 || k <= 0 || k > E) return -1;
@@ -381,22 +394,30 @@ int oracle_router_topk(const float *logits, int64_t T, int32_t E, int32_t k, int
         double *v = (double *)malloc(sizeof(double) * (size_t)k);
         for (int32_t r = 0; r < k; r++) {
             int32_t best = -1;
-            double bv = 0.0;
             for (int32_t e = 0; e < E; e++) {
                 if (taken[e]) continue;
-                double x = isnan(l[e]) ? -INFINITY : (double)l[e];
-                if (best < 0 || x > bv) { /* ties keep the lower index (found first) */
+                if (best < 0) {
                     best = e;
-                    bv = x;
+                    continue;
                 }
+                /* strictly better only: ties keep the lower index (found first) */
+                int ce = router_rank_class(l[e]), cb = router_rank_class(l[best]);
+                if (ce > cb || (ce == 1 && cb == 1 && l[e] > l[best])) best = e;
             }
             taken[best] = 1;
             ids[t * k + r] = best;
-            v[r] = bv;
+            v[r] = isnan(l[best]) ? -INFINITY : (double)l[best];
         }
-        double m = v[0], sum = 0.0;
-        for (int32_t r = 0; r < k; r++) sum += exp(v[r] - m);
-        for (int32_t r = 0; r < k; r++) w[t * k + r] = exp(v[r] - m) / sum;
+        double m = v[0];
+        if (isfinite(m)) {
+            double sum = 0.0;
+            for (int32_t r = 0; r < k; r++) sum += exp(v[r] - m);
+            for (int32_t r = 0; r < k; r++) w[t * k + r] = exp(v[r] - m) / sum;
+        } else {
+            int32_t c = 0;
+            for (int32_t r = 0; r < k; r++) c += v[r] == m;
+            for (int32_t r = 0; r < k; r++) w[t * k + r] = v[r] == m ? 1.0 / c : 0.0;
+        }
         free(taken);
         free(v);
     }

@@ -156,3 +156,58 @@ def test_router_validation():
     assert f(None, 16, 64, 8, FAKE, FAKE, None) == moe.MOE_EINVAL
     assert f(FAKE, 16, 64, 8, FAKE, None, None) == moe.MOE_EINVAL
     assert f(None, 0, 64, 8, None, None, None) == moe.MOE_OK                # empty batch: no-op
+
+
+def test_gathered_activation_limit_and_f32_path():
+    """The grouped GEMM gathers activation rows through 32-bit byte offsets from the
+    tensor's start: a gathered tensor of 4 GiB or more is MOE_ELIMIT, caught before
+    anything is enqueued. h (the down projection's input, read in order) has no such
+    limit. A float32 mul_mat_id has only the grouped fp32 product: forcing the GEMV
+    path (or an unknown path) is MOE_EINVAL."""
+    g = _w(n_mat=1, rows=64, cols=1024)
+    d = _w(n_mat=1, rows=1024, cols=64)
+    assert _ffn(gate=g, up=_w(n_mat=1, rows=64, cols=1024), down=d, T=1 << 21, k=1) == moe.MOE_ELIMIT
+    assert "4 GiB" in moe.last_error()
+    # just under: the same layer with one token fewer gets past the limit checks
+    # (it then fails on the fake workspace size)
+    assert _ffn(gate=g, up=_w(n_mat=1, rows=64, cols=1024), down=d, T=(1 << 21) - 1, k=1,
+                ws_bytes=16) == moe.MOE_EWORKSPACE
+    w = _w(n_mat=1, rows=64, cols=1024)
+    assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_BF16, 1, FAKE, 1 << 21, 1, None, FAKE,
+                                  None, FAKE, 1 << 40, None) == moe.MOE_ELIMIT
+    f32 = _w(n_mat=8, rows=32, cols=64, typ=moe.MOE_F32)
+    for path, want in ((2, moe.MOE_EINVAL), (5, moe.MOE_EINVAL), (1, moe.MOE_EWORKSPACE)):
+        opt = moe._options(path)
+        assert moe.lib.moe_mul_mat_id(ctypes.byref(f32), FAKE, moe.MOE_F32, 1, FAKE, 16, 2, None, FAKE,
+                                      ctypes.byref(opt), FAKE, 16, None) == want, path
+        size = moe.lib.moe_mul_mat_id_workspace_size(ctypes.byref(f32), moe.MOE_F32, 1, 16, 2,
+                                                      ctypes.byref(opt))
+        assert (size > 0) == (want != moe.MOE_EINVAL), path
+
+
+def test_binding_rejects_wrong_dtypes_and_shapes():
+    """The Python binding checks dtypes and shapes before anything reaches the library:
+    int64 ids (what torch.topk returns), float64 routing weights, an output of the wrong
+    shape or dtype, and activations of the wrong size."""
+    import torch
+    w = moe.Weights(torch.zeros((4, 32, 64), dtype=torch.int8), torch.zeros((4, 32, 2), dtype=torch.int16))
+    x = torch.zeros((8, 64), dtype=torch.int16)
+    ids = torch.zeros((8, 2), dtype=torch.int32)
+    rw = torch.zeros((8, 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="ids must be int32"):
+        moe.moe_ffn_fused(w, w, w, x, ids.long(), rw)
+    with pytest.raises(ValueError, match="route_w must be float32"):
+        moe.moe_ffn_fused(w, w, w, x, ids, rw.double())
+    with pytest.raises(ValueError, match="route_w must be float32"):
+        moe.moe_mul_mat_id(w, x, ids, route_w=rw[:4])
+    with pytest.raises(ValueError, match="out must be float32"):
+        moe.moe_mul_mat_id(w, x, ids, out=torch.zeros((8, 32), dtype=torch.float32))
+    with pytest.raises(ValueError, match="out must be float32"):
+        moe.moe_mul_mat_id(w, x, ids, route_w=rw, out=torch.zeros((8, 32), dtype=torch.float16))
+    with pytest.raises(ValueError, match="src1 must hold"):
+        moe.moe_mul_mat_id(w, x[:4], ids)
+    with pytest.raises(ValueError, match="ids must be int32"):
+        moe.moe_row_ids(ids.long(), 4)
+    with pytest.raises(ValueError, match="x must be"):
+        moe.moe_ffn_fused(w, w, moe.Weights(torch.zeros((4, 64, 32), dtype=torch.int8),
+                                            torch.zeros((4, 64, 1), dtype=torch.int16)), x[:5], ids, rw)

@@ -56,6 +56,33 @@ def test_router_ties_and_nan():
     assert ids.cpu().numpy()[3, 0] == 7
 
 
+def test_router_non_finite_rows():
+    """NaN strictly below -inf, all-NaN and all -inf rows (weight 1/k on every pick),
+    +inf picks sharing the weight, and -0 equal to +0 (a tie: lower index first)."""
+    nan, inf = np.nan, np.inf
+    lg = np.zeros((8, 70), np.float32)
+    lg[0, :6] = [nan, 1.0, 2.0, 3.0, 4.0, -inf]
+    lg[0, 6:] = -inf
+    lg[1, :] = nan
+    lg[2, :] = -inf
+    lg[2, 65] = nan
+    lg[3, 1], lg[3, 66] = inf, inf
+    lg[4, :] = -1.0
+    lg[4, 3], lg[4, 2] = 0.0, -0.0
+    lg[5, ::2] = nan
+    lg[5, 1::2] = -inf
+    lg[6] = synth.draw_router_logits(13, 1, 70)[0]
+    lg[6, 64:] = nan
+    lg[7, 0] = np.float32(1e-40)                # a subnormal above +0
+    for k in (1, 3, 6, 70):
+        ids, w = _check(lg, k)
+    ids = ids.cpu().numpy()
+    assert ids[0, :6].tolist() == [4, 3, 2, 1, 5, 6]
+    assert ids[0, 69] == 0                        # the NaN comes after every -inf
+    assert ids[4, :2].tolist() == [2, 3]          # -0 == +0: lower index first
+    assert ids[7, 0] == 0
+
+
 def test_router_empty_and_repeatable():
     ids, w = moe.moe_router_topk(torch.zeros((0, 16), dtype=torch.float32, device="cuda"), 4)
     assert ids.shape == (0, 4)

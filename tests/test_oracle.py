@@ -528,3 +528,37 @@ def test_router_worked_example():
     a = math.exp(float(l3))
     s = 2 * a + math.e
     np.testing.assert_allclose(w[0], [a / s, a / s, math.e / s], rtol=1e-15)
+
+
+def test_router_nan_ranks_below_minus_inf():
+    """Hand-derived: NaN ranks strictly below -inf (a NaN at index 0 against -inf at
+    index 5), and non-finite picks get weight 0 when the largest pick is finite."""
+    nan, inf = float("nan"), float("inf")
+    lg = np.array([[nan, 1.0, 2.0, 3.0, 4.0, -inf]], np.float32)
+    ids, w = oracle.router_topk(lg, 6)
+    assert ids.tolist() == [[4, 3, 2, 1, 5, 0]]
+    e = np.exp(np.array([0.0, -1.0, -2.0, -3.0]))
+    np.testing.assert_allclose(w[0, :4], e / e.sum(), rtol=1e-15)
+    assert w[0, 4] == 0.0 and w[0, 5] == 0.0
+    # NaNs among themselves: lower index first, after every number
+    lg2 = np.array([[nan, -inf, nan, 0.5, -inf]], np.float32)
+    ids2, _ = oracle.router_topk(lg2, 5)
+    assert ids2.tolist() == [[3, 1, 4, 0, 2]]
+
+
+def test_router_non_finite_largest_pick():
+    """Hand-derived limits of the softmax: an all-NaN row and an all -inf row weight
+    every pick 1/k; with +inf picks, those share the weight and the rest get 0."""
+    nan, inf = float("nan"), float("inf")
+    ids, w = oracle.router_topk(np.full((1, 5), nan, np.float32), 3)
+    assert ids.tolist() == [[0, 1, 2]]
+    assert np.all(w == 1.0 / 3.0)
+    ids, w = oracle.router_topk(np.array([[-inf, nan, -inf, -inf]], np.float32), 3)
+    assert ids.tolist() == [[0, 2, 3]]
+    assert np.all(w == 1.0 / 3.0)
+    ids, w = oracle.router_topk(np.array([[-inf, nan, -inf]], np.float32), 3)
+    assert ids.tolist() == [[0, 2, 1]]          # the NaN last, weighted as -inf
+    assert np.all(w == 1.0 / 3.0)
+    ids, w = oracle.router_topk(np.array([[1.0, inf, 3.0, inf, nan]], np.float32), 3)
+    assert ids.tolist() == [[1, 3, 2]]
+    assert w.tolist() == [[0.5, 0.5, 0.0]]
