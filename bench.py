@@ -12,7 +12,9 @@ is not served from the 256 MB last-level cache.
 
 Prints ONE JSON line: tokens/s (value), TFLOP/s, GB/s, a roofline entry for the
 dominant kernel (timed with HIP events on the launch stream) and the CPU oracle
-timed on a bounded sample of the same workload on this host.
+timed on a bounded sample of the same workload on this host. The same line carries,
+under "workloads", the Zipf-skewed PP4096 prefill and the GPT-OSS-20B-shaped decode
+batches of 1 and 8 tokens (--extra), each with its own dominant-kernel roofline.
 """
 from __future__ import annotations
 
@@ -51,6 +53,11 @@ def parse():
                    help="1: time replays of one HIP graph per weight copy (each graph holds one "
                         "step); 0: eager calls")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--extra", default="skew,dec1,dec8",
+                   help="further workloads reported on the same line under 'workloads' "
+                        "(comma-separated; empty for none)")
+    p.add_argument("--extra-cpu-seconds", type=float, default=3.0,
+                   help="CPU oracle budget for each further workload")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a known-size "
                         "kernel for scaling HBM byte counters)")
@@ -58,9 +65,11 @@ def parse():
 
 
 def workload_stats(inp, cfg, h_bytes=2):
-    """Algorithmic work of one step (flops, bytes) and per-kernel bytes: the weights of
-    the experts the batch touches (each once), activations read once, results written
-    once."""
+    """Algorithmic work of one step (flops, bytes) and per-kernel algorithmic bytes,
+    counted by one rule: the weights of the experts the batch touches (each once) and
+    the shared experts' weights, the layer input x read once, the layer output written
+    once. Intermediates (h, the per-slot down results) are implementation traffic and
+    are not credited; their bytes are reported beside ("intermediate_bytes")."""
     T, k = inp["ids"].shape
     E, n_embd, n_ff, S = cfg.n_experts, cfg.n_embd, cfg.n_ff, cfg.n_shared
     ids = inp["ids"].ravel()
@@ -73,42 +82,72 @@ def workload_stats(inp, cfg, h_bytes=2):
     w_dn = (touched + S) * n_embd * n_ff * wb
     x_b = T * n_embd * 2                            # bf16 input
     out_b = T * n_embd * 4                          # fp32 layer output
+    h_b = rows * n_ff * h_bytes                     # silu(g)*u, written once and read once
+    y_b = rows * n_embd * 4                         # per-slot fp32 down results
     return {
         "flops": flops, "bytes": w_gu + w_dn + x_b + out_b, "touched": touched,
-        # gate/up: weights + x in, h = silu(g)*u out (bf16 on the GEMM path, fp32 on
-        # the GEMV path)
-        "gate_up": {"bytes": w_gu + x_b + rows * n_ff * h_bytes,
-                    "flops": 2.0 * rows * 2 * n_embd * n_ff},
-        # down: weights + h in, per-row fp32 results out
-        "down": {"bytes": w_dn + rows * n_ff * h_bytes + rows * n_embd * 4,
-                 "flops": 2.0 * rows * n_embd * n_ff},
+        "gate_up": {"bytes": w_gu + x_b, "flops": 2.0 * rows * 2 * n_embd * n_ff,
+                    "intermediate_bytes": h_b},
+        "down": {"bytes": w_dn, "flops": 2.0 * rows * n_embd * n_ff,
+                 "intermediate_bytes": h_b + y_b},
+        # decode batches whose down GEMV also does the weighted reduce and writes out
+        "down_reduce": {"bytes": w_dn + out_b, "flops": 2.0 * rows * n_embd * n_ff,
+                        "intermediate_bytes": h_b},
+        "reduce": {"bytes": out_b, "flops": 0.0, "intermediate_bytes": y_b},
     }
 
 
-def cpu_baseline(inp, budget_s):
-    """The oracle, as it stands, on a bounded token sample: tokens/s on this host.
-    The sample grows until one pass takes about a quarter of the budget; when the
-    whole batch is faster than that, whole-batch passes repeat until the budget."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _omp_threads(n):
+    """Set the OpenMP thread count of this process (the oracle's parallel loops)."""
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+    except OSError:
+        pass
+
+
+def cpu_baseline(inp, budget_s, flops_per_token, threads=None):
+    """The oracle, as it stands, on a bounded token sample: tokens/s and fp64 GFLOP/s
+    (the same algorithmic flops as the GPU figures) on this host. The sample grows until
+    one pass takes about a quarter of the budget; when the whole batch is faster than
+    that, whole-batch passes repeat until the budget."""
     import oracle
     oracle.lib()
-    T = inp["ids"].shape[0]
-    n = min(T, 4)
-    while True:
-        rows = np.arange(n)
-        t0 = time.perf_counter()
-        oracle.ffn(inp, token_rows=rows)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s / 4 or n >= T:
-            break
-        n = min(T, max(n * 2, int(n * budget_s / 4 / max(dt, 1e-3))))
-    reps, total = 1, dt
-    while total < budget_s and n >= T:
-        t0 = time.perf_counter()
-        oracle.ffn(inp, token_rows=np.arange(n))
-        total += time.perf_counter() - t0
-        reps += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": n * reps / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    all_threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
+    used = threads or all_threads
+    _omp_threads(used)
+    try:
+        T = inp["ids"].shape[0]
+        n = min(T, 4)
+        while True:
+            rows = np.arange(n)
+            t0 = time.perf_counter()
+            oracle.ffn(inp, token_rows=rows)
+            dt = time.perf_counter() - t0
+            if dt >= budget_s / 4 or n >= T:
+                break
+            n = min(T, max(n * 2, int(n * budget_s / 4 / max(dt, 1e-3))))
+        reps, total = 1, dt
+        while total < budget_s and n >= T:
+            t0 = time.perf_counter()
+            oracle.ffn(inp, token_rows=np.arange(n))
+            total += time.perf_counter() - t0
+            reps += 1
+    finally:
+        _omp_threads(all_threads)
+    tps = n * reps / total
+    return {"value": tps, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "gflops_fp64": tps * flops_per_token / 1e9, "cpu_model": cpu_model(),
             "sample": "first %d of %d tokens x %d pass(es), full layer (all experts and shared), "
                       "fp64, %.1f s" % (n, T, reps, total)}
 
@@ -247,24 +286,19 @@ def bench_row_ids(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py: this implementation runs on one GPU; --gpus %d is not supported "
-              "(the path would shard by expert with two all-to-all exchanges)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-    if args.config == "rowids":
-        bench_row_ids(args)
-        return
+def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=False,
+                     before_warmup=None):
+    """Time one FFN workload: warm-up, then `steps` timed steps (each one full layer
+    call on inputs resident in HBM, weights rotated through R copies), then one pass
+    with per-kernel HIP events. `before_warmup` (optional) runs once the inputs are on
+    the device, just before the warm-up. Returns the measurements as a dict."""
     import torch
     import indirect_expert_matmul_amd as moe
     import synth
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.CONFIGS[name]
     if cfg.kind != "ffn":
-        print("bench.py: --config must be an FFN workload", file=sys.stderr)
-        sys.exit(2)
+        raise SystemExit("bench.py: %s is not an FFN workload" % name)
     inp = synth.make_inputs(cfg)
     T, k = inp["ids"].shape
     dev = torch.device("cuda:0")
@@ -304,7 +338,8 @@ def main():
         moe.moe_ffn_fused(g, u, d, x, ids, rw, shared=s, path=args.path, out=out, workspace=ws,
                           stream=stream, events=events)
 
-    args.warmup = warm_up(step, args.warmup)
+    pre = before_warmup() if before_warmup else None
+    warmup = warm_up(step, warmup)
     run = step
     if args.graph:
         # one captured step per weight copy, replayed in the same rotation
@@ -321,78 +356,159 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
         run = lambda i: graphs[i % R].replay()
-        warm_up(run, args.warmup)
+        warm_up(run, warmup)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         run(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = elapsed * 1e3 / args.steps
+    ms = elapsed * 1e3 / steps
 
-    # per-kernel durations: HIP events recorded by the library around each stage
+    # per-kernel durations: HIP events recorded by the library around each stage, on
+    # the stream the kernels run on
     names = STAGES[path]
-    evs = [[KernelEvent() for _ in range(2 * len(names))] for _ in range(args.steps)]
+    evs = [[KernelEvent() for _ in range(2 * len(names))] for _ in range(steps)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, events=[e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
     if moe.last_stage_count() < len(names):
         # small decode batches: the down GEMV does the weighted reduce itself
         names = names[:1] + ["gemv_down_reduce"]
     stage_ms = {n: float(np.mean([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1])
-                                  for i in range(args.steps)])) for j, n in enumerate(names)}
+                                  for i in range(steps)])) for j, n in enumerate(names)}
     dom = max(stage_ms, key=stage_ms.get)
     kern = {"gemm_gate_up": "gate_up", "gemv_gate_up": "gate_up", "gemm_down": "down",
-            "gemv_down": "down", "gemv_down_reduce": "down"}.get(dom)
+            "gemv_down": "down", "gemv_down_reduce": "down_reduce", "reduce": "reduce"}.get(dom)
     mfma_bound = path == 1 and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
-    traffic = measured_traffic(args.config, dom)
+    traffic = measured_traffic(name, dom)
     if kern is None:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dom}
     elif mfma_bound:
         a = st[kern]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
+                "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes": st[kern]["bytes"], "intermediate_bytes": st[kern]["intermediate_bytes"]}
     else:
         a = st[kern]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom}
+                "frac": a / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes": st[kern]["bytes"], "intermediate_bytes": st[kern]["intermediate_bytes"]}
 
-    # the router top-k that produces ids / route_w ahead of the layer (not part of the
-    # step): timed on logits of the same shape, reported separately
+    res = {
+        "workload": cfg.desc, "name": name, "n_tokens": T, "path": "gemm" if path == 1 else "gemv",
+        "weight_copies": R, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+        "tokens_per_s": T / (ms * 1e-3),
+        "tflops": st["flops"] / (ms * 1e-3) / 1e12,
+        "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
+        "stage_ms": stage_ms, "roofline": roof,
+        "dtype": "bf16" if path == 1 else "f32",
+        "cfg": cfg, "inp": inp, "stats": st, "stream": stream, "pre": pre,
+    }
+    if cpu_seconds > 0:
+        fpt = st["flops"] / T
+        res["cpu_baseline"] = cpu_baseline(inp, cpu_seconds, fpt)
+        if single_thread_cpu:
+            res["cpu_baseline"]["single_thread"] = {
+                k2: v for k2, v in cpu_baseline(inp, min(cpu_seconds, 3.0), fpt, threads=1).items()
+                if k2 in ("value", "gflops_fp64", "sample")}
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def time_router(cfg, stream, seconds=0.25):
+    """The router top-k that produces ids / route_w ahead of the layer (not part of the
+    step), timed on logits of the workload's shape for about `seconds` of back-to-back
+    calls, and reported beside the layer. It runs first: from idle the GPU clocks take
+    some milliseconds to ramp up, and this keeps them up for the layer's warm-up."""
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import synth
+    T, k = cfg.n_tokens, cfg.n_used
+    dev = torch.device("cuda:0")
     lg = torch.from_numpy(synth.draw_router_logits(cfg.seed, T, cfg.n_experts)).to(dev)
     for _ in range(3):
         moe.moe_router_topk(lg, k, stream=stream)
+    torch.cuda.synchronize()
+    n_router, t0 = 0, time.perf_counter()
     r0, r1 = KernelEvent(), KernelEvent()
     r0.record(stream)
-    n_router = 20
-    for _ in range(n_router):
-        moe.moe_router_topk(lg, k, stream=stream)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            moe.moe_router_topk(lg, k, stream=stream)
+        n_router += 50
     r1.record(stream)
     torch.cuda.synchronize()
     router_us = r0.elapsed_time(r1) * 1e3 / n_router
-    router = {"us": router_us, "gbps": (T * cfg.n_experts * 4 + T * k * 8) / (router_us * 1e-6) / 1e9,
-              "n_experts": cfg.n_experts, "n_used": k}
+    return {"us": router_us, "gbps": (T * cfg.n_experts * 4 + T * k * 8) / (router_us * 1e-6) / 1e9,
+            "n_experts": cfg.n_experts, "n_used": k, "calls": n_router}
 
+
+def _public(r):
+    """The JSON-ready part of a workload result."""
+    return {k: v for k, v in r.items() if k not in ("cfg", "inp", "stats", "stream", "pre")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this implementation runs on one GPU; --gpus %d is not supported "
+              "(the path would shard by expert with two all-to-all exchanges)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if args.config == "rowids":
+        bench_row_ids(args)
+        return
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    T, k = cfg.n_tokens, cfg.n_used
+    stream = torch.cuda.current_stream()
+    r = run_ffn_workload(args, args.config, args.steps, args.warmup,
+                         0 if args.no_cpu else args.cpu_seconds,
+                         single_thread_cpu=cfg.n_tokens <= 16,
+                         before_warmup=lambda: time_router(cfg, stream))
+    router = r["pre"]
+
+    # the other workloads of the metric (PP4096 prefill, decode batches of 1 and 8), on
+    # the same line: each with its own dominant-kernel roofline
+    extras = {}
+    names = [n for n in (args.extra.split(",") if args.extra else []) if n and n != args.config]
+    del r["inp"]
+    for n in names:
+        e = run_ffn_workload(args, n, max(10, args.steps // 2) if n in ("skew", "v3") else args.steps,
+                             args.warmup, 0 if args.no_cpu else args.extra_cpu_seconds,
+                             single_thread_cpu=synth.CONFIGS[n].n_tokens <= 16)
+        extras[n] = _public(e)
+        del e
+        torch.cuda.empty_cache()
+
+    ms = r["ms_per_step"]
     res = {
         "metric": "MoE mul_mat_id tokens/s + TFLOP/s (PP512/PP4096) and decode GB/s, 1 MI355X",
         "value": T / (ms * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": r["warmup"], "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if path == 1 else "f32",
+        "dtype": r["dtype"],
         "data": "synthetic",
         "config": {"workload": cfg.desc, "n_tokens": T, "n_experts": cfg.n_experts,
                    "n_used": k, "n_shared": cfg.n_shared, "n_embd": cfg.n_embd, "n_ff": cfg.n_ff,
-                   "path": "gemm" if path == 1 else "gemv", "weight_copies": R,
+                   "path": r["path"], "weight_copies": r["weight_copies"],
                    "launch": "hip graph replay" if args.graph else "eager",
                    "parallelism": "single GPU"},
-        "tflops": st["flops"] / (ms * 1e-3) / 1e12,
-        "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
-        "stage_ms": stage_ms,
+        "tflops": r["tflops"],
+        "gbps": r["gbps"],
+        "stage_ms": r["stage_ms"],
         "router": router,
-        "roofline": roof,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(inp, args.cpu_seconds),
+        "roofline": r["roofline"],
+        "cpu_baseline": r["cpu_baseline"],
+        "workloads": extras,
     }
     print(json.dumps(res), flush=True)
 

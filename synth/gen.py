@@ -181,13 +181,15 @@ def _threads() -> int:
 
 def draw_q8_0_stack(seed: int, stream: int, which: int, n_mat: int, rows: int, cols: int,
                     qs_out: np.ndarray | None = None, d_out: np.ndarray | None = None,
-                    wtype: str = "q8_0"):
+                    wtype: str = "q8_0", only=None):
     """n_mat stacked Q8_0 (or MXFP4) matrices; matrix e comes from stream
-    (seed, stream, e, which)."""
+    (seed, stream, e, which). ``only`` (optional) lists the matrices to draw; the
+    others are left zero (a drawn matrix has the same values either way)."""
     fp4 = wtype == "mxfp4"
-    qs = qs_out if qs_out is not None else (np.empty((n_mat, rows, cols // 2), np.uint8) if fp4
-                                             else np.empty((n_mat, rows, cols), np.int8))
-    d = d_out if d_out is not None else np.empty((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
+    alloc = np.empty if only is None else np.zeros
+    qs = qs_out if qs_out is not None else (alloc((n_mat, rows, cols // 2), np.uint8) if fp4
+                                             else alloc((n_mat, rows, cols), np.int8))
+    d = d_out if d_out is not None else alloc((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
     draw = draw_mxfp4 if fp4 else draw_q8_0
 
     def one(e):
@@ -196,7 +198,7 @@ def draw_q8_0_stack(seed: int, stream: int, which: int, n_mat: int, rows: int, c
         d[e] = s
 
     with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(one, range(n_mat)))
+        list(ex.map(one, range(n_mat) if only is None else only))
     return qs, d
 
 
@@ -207,11 +209,14 @@ def draw_x_bf16(seed: int, n_tokens: int, n_embd: int) -> np.ndarray:
 
 
 def make_inputs(cfg: Config | str, seed: int | None = None, n_tokens: int | None = None,
-                ids: np.ndarray | None = None) -> dict:
+                ids: np.ndarray | None = None, touched_only: bool = False) -> dict:
     """All inputs of one workload as numpy arrays (see module docstring).
 
     ``ids`` overrides the drawn routing table (shape [T][k]; entries may repeat or
-    fall outside [0, E) for edge-case tests); everything else is drawn as usual."""
+    fall outside [0, E) for edge-case tests); everything else is drawn as usual.
+    ``touched_only`` draws the routed experts' weights only for the experts the ids
+    name and leaves the others zero (decode-sized batches of wide layers: nothing
+    reads the untouched experts, and the touched ones get the same values)."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     seed = cfg.seed if seed is None else seed
@@ -237,10 +242,14 @@ def make_inputs(cfg: Config | str, seed: int | None = None, n_tokens: int | None
             out.update(w_qs=qs, w_d=d, x=draw_x_bf16(seed, T, K), wtype=cfg.wtype, xtype="bf16")
         return out
     n_embd, n_ff, S = cfg.n_embd, cfg.n_ff, cfg.n_shared
+    only = None
+    if touched_only:
+        v = out["ids"].ravel()
+        only = sorted(set(v[(v >= 0) & (v < E)].tolist()))
     for name, which, rows, cols in (("gate", _M_GATE, n_ff, n_embd), ("up", _M_UP, n_ff, n_embd),
                                     ("down", _M_DOWN, n_embd, n_ff)):
         out[name + "_qs"], out[name + "_d"] = draw_q8_0_stack(seed, _S_ROUTED, which, E, rows, cols,
-                                                              wtype=cfg.wtype)
+                                                              wtype=cfg.wtype, only=only)
         if S:
             out["sh_" + name + "_qs"], out["sh_" + name + "_d"] = draw_q8_0_stack(
                 seed, _S_SHARED, which, S, rows, cols, wtype=cfg.wtype)
@@ -251,11 +260,11 @@ def make_inputs(cfg: Config | str, seed: int | None = None, n_tokens: int | None
 
 def make_custom_ffn(seed: int, E: int, k: int, T: int, n_embd: int, n_ff: int, S: int = 0,
                     routing: str = "uniform", ids: np.ndarray | None = None,
-                    wtype: str = "q8_0") -> dict:
+                    wtype: str = "q8_0", touched_only: bool = False) -> dict:
     """An FFN workload of arbitrary shape (tests), same recipe as the named ones."""
     cfg = Config("custom", "ffn", E, k, T, n_embd, n_ff, n_shared=S, routing=routing, seed=seed,
                  wtype=wtype)
-    return make_inputs(cfg, seed, ids=ids)
+    return make_inputs(cfg, seed, ids=ids, touched_only=touched_only)
 
 
 def make_custom_mmid(seed: int, E: int, k: int, T: int, K: int, N: int, wtype: str = "q8_0",

@@ -233,27 +233,79 @@ def _sample_tokens(ids, n, seed):
     return np.array(sorted(pick))
 
 
-def test_skew_full_size_sampled():
+def test_skew_full():
+    """Zipf-skewed PP4096 layer (empty, tiny and oversized expert segments), every
+    token compared."""
     inp = synth.make_inputs("skew")
     got = run_ffn(upload_ffn(inp))
     torch.cuda.synchronize()
-    rows = _sample_tokens(inp["ids"], 160, 1)
-    err = normwise(got.cpu().numpy()[rows], oracle.ffn(inp, token_rows=rows))
-    print("skew sampled normwise error %.3g" % err)
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("skew normwise error %.3g" % err)
     assert err <= TOL_MFMA
-    assert torch.isfinite(got).all()
 
 
-def test_v3_full_size_sampled():
+def _segment_tokens(ids, n_experts, block=128):
+    """Tokens of the first and last row of every block-row stretch of every expert
+    segment, in the row-id order (token, then slot): every M tile of 64 or 128 rows of
+    every expert, its first and its last, holds a row of one of these tokens."""
+    _, dst, bounds = oracle.row_ids(ids, n_experts, 1)
+    k = ids.shape[1]
+    pick = set()
+    for e in range(n_experts):
+        lo, hi = int(bounds[e]), int(bounds[e + 1])
+        for a in range(lo, hi, block):
+            b = min(a + block, hi) - 1
+            pick.add(int(dst[a]) // k)
+            pick.add(int(dst[b]) // k)
+    return pick
+
+
+def test_v3_full_size_stratified():
+    """DeepSeek-V3-shaped PP8192 layer. The oracle runs on the tokens holding the first
+    and last row of every 128-row stretch of every expert's segment (so every M tile of
+    every expert, including each expert's partly filled last tile, has rows checked),
+    plus random tokens; the shared expert is part of every token's output."""
     inp = synth.make_inputs("v3")
     dv = upload_ffn(inp)
     got = run_ffn(dv).cpu().numpy()
-    rows = _sample_tokens(inp["ids"], 24, 2)
+    rows = _segment_tokens(inp["ids"], 256) | set(_sample_tokens(inp["ids"], 64, 2).tolist())
+    rows = np.array(sorted(rows))
     ref = oracle.ffn(inp, token_rows=rows)
     err = normwise(got[rows], ref)
-    print("v3 sampled normwise error %.3g" % err)
+    print("v3 normwise error %.3g over %d tokens" % (err, len(rows)))
+    assert len(rows) > 500
     assert err <= TOL_MFMA
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_v3_shaped_decode_wide(T):
+    """Decode batches of a DeepSeek-V3-shaped layer (n_embd 7168 > 4096): automatic
+    selection takes the GEMV path, on its block kernel for widths past the wave
+    kernels' 4096. Only the experts the batch routes to are drawn (nothing reads the
+    others)."""
+    inp = synth.make_custom_ffn(71 + T, 256, 8, T, 7168, 2048, 1, touched_only=True)
+    assert moe.moe_select_path(T, 8, 256, 7168) == moe.PATH_GEMV
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    assert moe.last_stage_count() == 3   # gate/up GEMV, down GEMV, reduce
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("v3-shaped decode T=%d normwise error %.3g" % (T, err))
+    assert err <= TOL_FP32
+
+
+@pytest.mark.parametrize("T", [11, 16, 42])
+def test_lite_widths_gemv_block_kernel(T):
+    """DeepSeek-Lite-shaped layer (shared experts included) at batches of 64 < T*k <=
+    256 slots: the GEMV path past the wave kernels' 64 slots runs the block kernel."""
+    inp = synth.make_custom_ffn(90 + T, 64, 6, T, 2048, 1408, 2, touched_only=True)
+    assert moe.moe_select_path(T, 6, 64, 2048) == moe.PATH_GEMV
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    assert moe.last_stage_count() == 3
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("lite widths T=%d (%d slots) normwise error %.3g" % (T, 6 * T, err))
+    assert err <= TOL_FP32
 
 
 # ------------------------------------------------------------------------- MXFP4 experts
