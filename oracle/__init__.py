@@ -57,8 +57,13 @@ def lib():
         _lib.oracle_ffn.argtypes = ([ctypes.c_int] + [P] * 6 + [I64] * 3 + [P] * 6 + [I64] * 2 +
                                     [P, ctypes.c_int, P, P, I64, I32, P])
         _lib.oracle_router_topk.argtypes = [P, I64, I32, I32, P, P]
+        _lib.oracle_quantize_act.argtypes = [ctypes.c_int, P, I64, I64, P, P]
+        _lib.oracle_mul_mat_id_q8act.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, P, I32, P, I64,
+                                                 I32, P, P]
+        _lib.oracle_ffn_q8act.argtypes = _lib.oracle_ffn.argtypes
         for f in (_lib.oracle_dequant, _lib.oracle_row_ids, _lib.oracle_mul_mat_id, _lib.oracle_ffn,
-                  _lib.oracle_router_topk):
+                  _lib.oracle_router_topk, _lib.oracle_quantize_act, _lib.oracle_mul_mat_id_q8act,
+                  _lib.oracle_ffn_q8act):
             f.restype = ctypes.c_int
     return _lib
 
@@ -160,10 +165,43 @@ def mul_mat_id(w, w_d, src1, src1_type: str, ids, route_w=None, src1_rows_per_to
     return out
 
 
-def ffn(inp: dict, token_rows=None) -> np.ndarray:
+def quantize_act(x, src_type: str = "bf16"):
+    """Quantized-activation format (per 32-column block: float32 scale d = max|x|/127,
+    int8 codes rint(x/d), decisions in float32): (q int8 [rows][K], d float32
+    [rows][K/32]) for x [rows][K] (bf16 bits as uint16, or float32)."""
+    st = _TYPES[src_type]
+    a = _c(x, np.float32 if st == F32 else np.uint16)
+    rows, K = a.shape
+    q = np.empty((rows, K), np.int8)
+    d = np.empty((rows, K // 32), np.float32)
+    rc = lib().oracle_quantize_act(st, _p(a), rows, K, _p(q), _p(d))
+    if rc:
+        raise ValueError("oracle_quantize_act rejected its arguments (%d)" % rc)
+    return q, d
+
+
+def mul_mat_id_q8act(w, w_d, q, d, ids, route_w=None, src1_rows_per_token: int = 1):
+    """mul_mat_id with quantized activations (q int8 [T*B][K], d float32 [T*B][K/32]):
+    per-slot float64 [T][k][N], or the route_w-weighted [T][N]."""
+    wt, wq, ws, (E, N, K) = _weights(w, w_d)
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    qa, da = _c(q, np.int8), _c(d, np.float32)
+    rw = _c(route_w, np.float32)
+    out = np.empty((T, N) if rw is not None else (T, k, N), np.float64)
+    rc = lib().oracle_mul_mat_id_q8act(wt, _p(wq), _p(ws), E, N, K, _p(qa), _p(da), src1_rows_per_token,
+                                       _p(ids), T, k, _p(rw), _p(out))
+    if rc:
+        raise ValueError("oracle_mul_mat_id_q8act rejected its arguments (%d)" % rc)
+    return out
+
+
+def ffn(inp: dict, token_rows=None, act_quant: bool = False) -> np.ndarray:
     """Fused MoE FFN output float64 [T][n_embd] for a workload dict from ``synth``.
     ``token_rows`` (optional index array) restricts the computation to those tokens;
-    every token's output depends only on its own row of x, ids and route_w."""
+    every token's output depends only on its own row of x, ids and route_w.
+    ``act_quant``: the quantized-activation path (x quantized before gate/up, each h
+    rounded to bf16 and quantized before down)."""
     ids, rw, x = inp["ids"], inp["route_w"], inp["x"]
     if token_rows is not None:
         token_rows = np.asarray(token_rows)
@@ -183,9 +221,10 @@ def ffn(inp: dict, token_rows=None) -> np.ndarray:
         _, su, sus, _ = _weights(inp["sh_up_qs"], inp.get("sh_up_d"))
         _, sd, sds, _ = _weights(inp["sh_down_qs"], inp.get("sh_down_d"))
     out = np.empty((T, n_embd), np.float64)
-    rc = lib().oracle_ffn(wt, _p(g), _p(gs), _p(u), _p(us), _p(dn), _p(dns), E, n_ff, n_embd,
-                          _p(sg), _p(sgs), _p(su), _p(sus), _p(sd), _p(sds), S, n_ff_sh,
-                          _p(x), xt, _p(ids), _p(rw), T, k, _p(out))
+    f = lib().oracle_ffn_q8act if act_quant else lib().oracle_ffn
+    rc = f(wt, _p(g), _p(gs), _p(u), _p(us), _p(dn), _p(dns), E, n_ff, n_embd,
+           _p(sg), _p(sgs), _p(su), _p(sus), _p(sd), _p(sds), S, n_ff_sh,
+           _p(x), xt, _p(ids), _p(rw), T, k, _p(out))
     if rc:
         raise ValueError("oracle_ffn rejected its arguments (%d)" % rc)
     return out

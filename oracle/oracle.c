@@ -423,3 +423,201 @@ int oracle_router_topk(const float *logits, int64_t T, int32_t E, int32_t k, int
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------------
+ * Quantized-activation path (the MMQ-style path: "CUDA: better MoE implementation",
+ * section 2.1, names mmq_id, the grouped product of quantized experts with quantized
+ * activations; the pages do not define the activation format, so it is a reading):
+ *
+ *   Each activation row is cut into blocks of 32 consecutive columns. A block's values
+ *   x (bf16 or fp32, widened exactly to fp32) get one float32 scale
+ *       d = max|x| / 127            (fp32 division, rounded to nearest-even)
+ *   and int8 codes
+ *       q = rint(x / d)             (fp32 division, then round to the nearest integer,
+ *                                    ties to even; clamped to [-127, 127])
+ *   A block of zeros has d = 0 and q = 0. The block's value is d * q.
+ *
+ *   The decisions are taken in float32 (the precision stated above), so any side that
+ *   follows the same float32 operations reaches the same codes. Activations must be
+ *   finite.
+ */
+
+/* bf16 RNE of a double, in one rounding: keep 8 significant bits. */
+static double round_to_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    double m = frexp(v, &e);           /* v = m * 2^e, 0.5 <= |m| < 1 */
+    double r = nearbyint(ldexp(m, 8)); /* 8 significant bits, ties to even */
+    return ldexp(r, e - 8);
+}
+
+/* One block of n <= 32 float32 values -> codes and scale, as defined above. */
+static void quantize_block(const float *x, int n, int8_t *q, float *d) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    volatile float dv = amax / 127.0f; /* float32 division, not contracted or widened */
+    float dd = dv;
+    *d = dd;
+    for (int i = 0; i < n; i++) {
+        if (dd == 0.0f) {
+            q[i] = 0;
+            continue;
+        }
+        volatile float t = x[i] / dd;
+        float r = rintf(t);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[i] = (int8_t)r;
+    }
+}
+
+/* Quantize rows x[rows][K] (type 0 float32, 1 bf16 bits) into q int8 [rows][K] and
+ * d float32 [rows][K/32]. K % 32 == 0. */
+int oracle_quantize_act(int type, const void *x, int64_t rows, int64_t K, int8_t *q, float *d) {
+    if (!x || !q || !d || rows < 0 || K <= 0 || K % 32) return -1;
+    if (type != OR_F32 && type != OR_BF16) return -1;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < K / 32; b++) {
+            float blk[32];
+            for (int i = 0; i < 32; i++) blk[i] = (float)act_at(type, x, r * K + b * 32 + i);
+            quantize_block(blk, 32, q + r * K + b * 32, d + r * (K / 32) + b);
+        }
+    return 0;
+}
+
+/* Dequantized quantized-activation row: out[c] = d[c/32] * q[c], exact in float64. */
+static void q8act_row(const int8_t *q, const float *d, int64_t K, double *out) {
+    for (int64_t c = 0; c < K; c++) out[c] = (double)d[c / 32] * (double)q[c];
+}
+
+/*
+ * mul_mat_id on quantized activations: as oracle_mul_mat_id (section 1.2 of the same
+ * page), with slot (t, s) reading the quantized row t*B + (s mod B) of (q, d):
+ *   dst[t][s][n] = sum_c w(ids[t][s], n, c) * d[row][c/32] * q[row][c], c ascending.
+ */
+int oracle_mul_mat_id_q8act(int w_type, const void *w_data, const void *w_scales, int64_t E,
+                            int64_t N, int64_t K, const int8_t *q, const float *d, int32_t B,
+                            const int32_t *ids, int64_t T, int32_t k, const float *route_w,
+                            double *dst) {
+    if (!w_data || !q || !d || !ids || !dst || E <= 0 || N <= 0 || K <= 0 || T < 0 || k <= 0)
+        return -1;
+    if (!is_quant(w_type) || !w_scales || K % 32) return -1;
+    if (B != 1 && B != k) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < T; t++) {
+        double *a = (double *)malloc(sizeof(double) * (size_t)K);
+        double *y = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!a || !y) {
+            bad = 1;
+            free(a);
+            free(y);
+            continue;
+        }
+        double *out_t = dst + t * (route_w ? N : (int64_t)k * N);
+        if (route_w)
+            for (int64_t n = 0; n < N; n++) out_t[n] = 0.0;
+        for (int32_t s = 0; s < k; s++) {
+            int32_t e = ids[t * k + s];
+            double *row = route_w ? y : out_t + (int64_t)s * N;
+            if (e < 0 || e >= E) {
+                if (!route_w)
+                    for (int64_t n = 0; n < N; n++) row[n] = 0.0;
+                continue;
+            }
+            int64_t r = t * B + s % B;
+            q8act_row(q + r * K, d + r * (K / 32), K, a);
+            matvec(w_type, w_data, w_scales, N, K, e, a, row);
+            if (route_w) {
+                double wt = (double)route_w[t * k + s];
+                for (int64_t n = 0; n < N; n++) out_t[n] += wt * y[n];
+            }
+        }
+        free(a);
+        free(y);
+    }
+    return bad ? -2 : 0;
+}
+
+/* One expert's FFN on a quantized activation row: g = Wg xq, u = Wu xq, h = silu(g)*u,
+ * h rounded to bf16 (the intermediate's storage type) and quantized as above, then
+ * y = Wd hq. */
+static void expert_ffn_q8act(int type, const void *g_data, const void *g_scales, const void *u_data,
+                             const void *u_scales, const void *d_data, const void *d_scales,
+                             int64_t n_ff, int64_t n_embd, int64_t e, const double *xq, double *g,
+                             double *u, float *hf, int8_t *hq, float *hd, double *y) {
+    matvec(type, g_data, g_scales, n_ff, n_embd, e, xq, g);
+    matvec(type, u_data, u_scales, n_ff, n_embd, e, xq, u);
+    for (int64_t i = 0; i < n_ff; i++) hf[i] = (float)round_to_bf16(g[i] / (1.0 + exp(-g[i])) * u[i]);
+    for (int64_t b = 0; b < n_ff / 32; b++) quantize_block(hf + b * 32, 32, hq + b * 32, hd + b);
+    q8act_row(hq, hd, n_ff, g);
+    matvec(type, d_data, d_scales, n_embd, n_ff, e, g, y);
+}
+
+/*
+ * Fused MoE FFN on the quantized-activation path: as oracle_ffn, with each token's x
+ * quantized (definition above) before the gate and up projections, and each expert's
+ * h rounded to bf16 and quantized before the down projection.
+ */
+int oracle_ffn_q8act(int w_type, const void *g_data, const void *g_scales, const void *u_data,
+                     const void *u_scales, const void *d_data, const void *d_scales, int64_t E,
+                     int64_t n_ff, int64_t n_embd, const void *sg_data, const void *sg_scales,
+                     const void *su_data, const void *su_scales, const void *sd_data,
+                     const void *sd_scales, int64_t S, int64_t n_ff_sh, const void *x, int x_type,
+                     const int32_t *ids, const float *route_w, int64_t T, int32_t k, double *out) {
+    if (!g_data || !u_data || !d_data || !x || !ids || !route_w || !out) return -1;
+    if (E <= 0 || n_ff <= 0 || n_embd <= 0 || T < 0 || k <= 0 || S < 0) return -1;
+    if (!is_quant(w_type) || x_type != OR_BF16) return -1;
+    if (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32) return -1;
+    if (S > 0 && (!sg_data || !su_data || !sd_data || !sg_scales || !su_scales || !sd_scales ||
+                  n_ff_sh <= 0 || n_ff_sh % 32))
+        return -1;
+    int64_t ffmax = n_ff > n_ff_sh ? n_ff : n_ff_sh;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < T; t++) {
+        double *xq = (double *)malloc(sizeof(double) * (size_t)n_embd);
+        int8_t *xc = (int8_t *)malloc((size_t)n_embd);
+        float *xd = (float *)malloc(sizeof(float) * (size_t)(n_embd / 32));
+        double *g = (double *)malloc(sizeof(double) * (size_t)ffmax);
+        double *u = (double *)malloc(sizeof(double) * (size_t)ffmax);
+        float *hf = (float *)malloc(sizeof(float) * (size_t)ffmax);
+        int8_t *hq = (int8_t *)malloc((size_t)ffmax);
+        float *hd = (float *)malloc(sizeof(float) * (size_t)(ffmax / 32 + 1));
+        double *y = (double *)malloc(sizeof(double) * (size_t)n_embd);
+        if (!xq || !xc || !xd || !g || !u || !hf || !hq || !hd || !y) {
+            bad = 1;
+        } else {
+            double *o = out + t * n_embd;
+            oracle_quantize_act(x_type, (const uint16_t *)x + t * n_embd, 1, n_embd, xc, xd);
+            q8act_row(xc, xd, n_embd, xq);
+            for (int64_t c = 0; c < n_embd; c++) o[c] = 0.0;
+            for (int32_t s = 0; s < k; s++) {
+                int32_t e = ids[t * k + s];
+                if (e < 0 || e >= E) continue;
+                expert_ffn_q8act(w_type, g_data, g_scales, u_data, u_scales, d_data, d_scales, n_ff,
+                                 n_embd, e, xq, g, u, hf, hq, hd, y);
+                double wt = (double)route_w[t * k + s];
+                for (int64_t c = 0; c < n_embd; c++) o[c] += wt * y[c];
+            }
+            for (int64_t j = 0; j < S; j++) {
+                expert_ffn_q8act(w_type, sg_data, sg_scales, su_data, su_scales, sd_data, sd_scales,
+                                 n_ff_sh, n_embd, j, xq, g, u, hf, hq, hd, y);
+                for (int64_t c = 0; c < n_embd; c++) o[c] += y[c];
+            }
+        }
+        free(xq);
+        free(xc);
+        free(xd);
+        free(g);
+        free(u);
+        free(hf);
+        free(hq);
+        free(hd);
+        free(y);
+    }
+    return bad ? -2 : 0;
+}

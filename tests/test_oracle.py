@@ -562,3 +562,114 @@ def test_router_non_finite_largest_pick():
     ids, w = oracle.router_topk(np.array([[1.0, inf, 3.0, inf, nan]], np.float32), 3)
     assert ids.tolist() == [[1, 3, 2]]
     assert w.tolist() == [[0.5, 0.5, 0.0]]
+
+
+# ------------------------------------------------------- quantized-activation path
+# Activation blocks of 32 columns: d = max|x|/127 (float32), q = rint(x/d) (float32,
+# ties to even), value d*q.
+
+def test_quantize_act_hand_derived():
+    """A block whose largest value is 508 = 127 * 4 has d = 4 exactly, so every code is
+    x/4 rounded by hand, ties to even: 63.5 -> 64, -0.5 -> 0, 1.5 -> 2, 2.5 -> 2,
+    3.5 -> 4. A block of zeros has d = 0 and q = 0. Values are exact in bf16."""
+    blk = [508.0, 254.0, -2.0, 3.0, 1.0, 2.5, -2.5, 3.5, 6.0, -6.0, 10.0, 14.0] + [0.0] * 20
+    want = [127, 64, 0, 1, 0, 1, -1, 1, 2, -2, 2, 4] + [0] * 20
+    x = np.array([blk + [0.0] * 32], np.float32)
+    for typ, arr in (("f32", x), ("bf16", synth.f32_to_bf16_bits(x))):
+        q, d = oracle.quantize_act(arr, typ)
+        assert d.tolist() == [[4.0, 0.0]], typ
+        assert q[0, :32].tolist() == want, typ
+        assert not q[0, 32:].any()
+
+
+def test_quantize_act_properties():
+    """On random blocks: the largest element gets code +-127, codes keep the sign,
+    |d*q - x| <= d/2 (rounding to the nearest code), and scaling a block by a power of
+    two scales d by it and keeps the codes."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((40, 256)) * rng.uniform(0.01, 100, size=(40, 1))).astype(np.float32)
+    q, d = oracle.quantize_act(x, "f32")
+    xb = x.reshape(40, 8, 32).astype(np.float64)
+    qb = q.reshape(40, 8, 32).astype(np.float64)
+    db = d.astype(np.float64)[:, :, None]
+    arg = np.abs(xb).argmax(axis=2)
+    assert np.all(np.abs(np.take_along_axis(qb, arg[:, :, None], 2)) == 127)
+    assert np.all((np.sign(qb) == np.sign(xb)) | (qb == 0))
+    assert np.all(np.abs(db * qb - xb) <= db / 2 * (1 + 1e-6))
+    assert np.abs(q).max() <= 127
+    q2, d2 = oracle.quantize_act(x * np.float32(8.0), "f32")
+    assert np.array_equal(q2, q) and np.array_equal(d2, d * np.float32(8.0))
+
+
+def test_mul_mat_id_q8act_reduces_to_plain_when_quantization_is_exact():
+    """Integer activations whose blocks each hold +-127 quantize exactly (d = 1, q = x),
+    so the quantized-activation mul_mat_id must equal the plain one bit for bit, per slot
+    and weighted, for one src1 row per token and one per slot."""
+    rng = np.random.default_rng(8)
+    E, k, T, K, N = 6, 3, 7, 96, 40
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[2, 1] = -1
+    inp = synth.make_custom_mmid(4, E, k, T, K, N, ids=ids)
+    for B in (1, k):
+        x = rng.integers(-127, 128, size=(T * B, K)).astype(np.float32)
+        x[:, ::32] = 127.0
+        q, d = oracle.quantize_act(x, "f32")
+        assert np.all(d == 1.0) and np.array_equal(q.astype(np.float32), x)
+        for rw in (None, inp["route_w"]):
+            got = oracle.mul_mat_id_q8act(inp["w_qs"], inp["w_d"], q, d, ids, rw, B)
+            ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "f32", ids, rw, B)
+            assert np.array_equal(got, ref), (B, rw is None)
+
+
+def test_mul_mat_id_q8act_equals_dense_masked_product():
+    """Random activations: equals the dense all-experts product of the dequantized
+    weights with the dequantized activations (numpy float64 matmul), masked by ids."""
+    rng = np.random.default_rng(9)
+    E, k, T, K, N = 5, 2, 9, 128, 24
+    inp = synth.make_custom_mmid(6, E, k, T, K, N)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    q, d = oracle.quantize_act(x, "bf16")
+    xa = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    W = oracle.dequant(inp["w_qs"], inp["w_d"])
+    dense = np.einsum("enc,tc->ten", W, xa)
+    want = np.stack([dense[t, inp["ids"][t]] for t in range(T)])
+    got = oracle.mul_mat_id_q8act(inp["w_qs"], inp["w_d"], q, d, inp["ids"])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def _bf16_round64(h):
+    m, e = np.frexp(h)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def test_ffn_q8act_composition():
+    """The quantized-activation FFN assembled from its steps with numpy: x quantized
+    (the pinned quantizer), gate/up products of the dequantized weights (numpy float64
+    matmul), silu(g)*u rounded to bf16 and quantized, the down product, the routing
+    weights, then the shared experts."""
+    E, k, T, n_embd, n_ff, S = 6, 2, 5, 96, 64, 1
+    ids = np.random.default_rng(3).integers(0, E, size=(T, k)).astype(np.int32)
+    ids[1, 1] = E + 2
+    inp = synth.make_custom_ffn(12, E, k, T, n_embd, n_ff, S, ids=ids)
+    got = oracle.ffn(inp, act_quant=True)
+    Wg, Wu, Wd = (oracle.dequant(inp[n + "_qs"], inp[n + "_d"]) for n in ("gate", "up", "down"))
+    Sg, Su, Sd = (oracle.dequant(inp["sh_" + n + "_qs"], inp["sh_" + n + "_d"]) for n in ("gate", "up", "down"))
+    deq = lambda q, d: q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    xq = deq(*oracle.quantize_act(inp["x"], "bf16"))
+
+    def expert(G, U, D, t):
+        g, u = G @ xq[t], U @ xq[t]
+        h = _bf16_round64(g / (1.0 + np.exp(-g)) * u).astype(np.float32)[None, :]
+        return D @ deq(*oracle.quantize_act(h, "f32"))[0]
+
+    want = np.zeros((T, n_embd))
+    for t in range(T):
+        for s in range(k):
+            e = ids[t, s]
+            if 0 <= e < E:
+                want[t] += float(inp["route_w"][t, s]) * expert(Wg[e], Wu[e], Wd[e], t)
+        want[t] += expert(Sg[0], Su[0], Sd[0], t)
+    assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
+    # and it stays close to the unquantized layer (8-bit codes on both activations)
+    plain = oracle.ffn(inp)
+    assert np.abs(got - plain).max() / np.abs(plain).max() < 2e-2
