@@ -174,6 +174,27 @@ moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const m
                          void *stream);
 
 /*
+ * moe_ffn_fused_noalloc -- moe_ffn_fused for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * arguments and results as moe_ffn_fused, without ws / ws_bytes: the workspace is a
+ * fixed array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every
+ * device it runs on, from the first call there until the process ends. Enough for a
+ * DeepSeek-Lite-shaped PP512 layer and any decode batch; a call needing more
+ * (moe_ffn_fused_workspace_size) is MOE_ELIMIT, with nothing enqueued. The call itself
+ * allocates nothing. All calls on one device share that device's array, so calls that
+ * overlap in time on one device (different streams, or different host threads) race
+ * and give undefined results: serialise them, e.g. on one stream. Its contents need no
+ * clearing between calls (the kernels overwrite what they read).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_ffn_fused_noalloc(const moe_weights *gate, const moe_weights *up,
+                                 const moe_weights *down, const moe_weights *sh_gate,
+                                 const moe_weights *sh_up, const moe_weights *sh_down,
+                                 const void *x, moe_dtype x_type, const int32_t *ids,
+                                 const float *route_w, int64_t n_tokens, int32_t n_used, float *out,
+                                 const moe_options *opt, void *stream);
+
+/*
  * moe_router_topk -- the step ahead of the op: the ids table the op consumes (section
  * 1.2 of the PR #283 write-up: ids names the experts each token uses) and routing
  * weights, from router logits.

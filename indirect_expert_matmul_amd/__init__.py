@@ -29,7 +29,9 @@ PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
            "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
            "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error",
-           "moe_last_stage_count")
+           "moe_last_stage_count", "moe_ffn_fused_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -61,7 +63,9 @@ def _load():
     lib.moe_mul_mat_id.argtypes = [W, P, ctypes.c_int, I32, P, I64, I32, P, P, O, P, SZ, P]
     lib.moe_ffn_fused.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P, SZ, P]
     lib.moe_router_topk.argtypes = [P, I64, I32, I32, P, P, P]
-    for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused, lib.moe_router_topk):
+    lib.moe_ffn_fused_noalloc.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P]
+    for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused, lib.moe_router_topk,
+              lib.moe_ffn_fused_noalloc):
         f.restype = ctypes.c_int
     lib.moe_row_ids_workspace_size.argtypes = [I64, I32, I32]
     lib.moe_mul_mat_id_workspace_size.argtypes = [W, ctypes.c_int, I32, I64, I32, O]
@@ -345,6 +349,34 @@ def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, id
                              ref[2], x.data_ptr(), _xtype(x), ids.data_ptr(), route_w.data_ptr(), T,
                              k, out.data_ptr(), ctypes.byref(opt), ws.data_ptr(),
                              ws.numel() * ws.element_size(), _stream(stream)), "moe_ffn_fused")
+    return out
+
+
+def moe_ffn_fused_noalloc(gate: Weights, up: Weights, down: Weights, x: torch.Tensor,
+                          ids: torch.Tensor, route_w: torch.Tensor,
+                          shared: Optional[Sequence[Weights]] = None, path: int = PATH_AUTO,
+                          tau: float = 0.0, out: Optional[torch.Tensor] = None, stream=None,
+                          events=None):
+    """The fused MoE FFN with the library's own fixed scratch array as workspace (the C
+    call allocates nothing; pass ``out`` to allocate nothing here either). Calls that
+    overlap in time on one device share that array and race."""
+    _check_ids(ids, route_w)
+    T, k = ids.shape
+    cg, cu, cd = gate.c(), up.c(), down.c()
+    _check_out(out, (T, cg.cols))
+    if x.dim() != 2 or tuple(x.shape) != (T, cg.cols):
+        raise ValueError("x must be [n_tokens][n_embd] = [%d][%d] (got %s)" % (T, cg.cols, tuple(x.shape)))
+    _dev_check(x, ids, route_w, out)
+    cs = [s.c() for s in shared] if shared else [None, None, None]
+    if out is None:
+        out = torch.empty((T, cg.cols), dtype=torch.float32, device=x.device)
+        _keep_alive(stream, out)
+    opt = _options(path, tau, events)
+    ref = [ctypes.byref(c) if c is not None else None for c in cs]
+    _check(lib.moe_ffn_fused_noalloc(ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd), ref[0], ref[1],
+                                     ref[2], x.data_ptr(), _xtype(x), ids.data_ptr(), route_w.data_ptr(),
+                                     T, k, out.data_ptr(), ctypes.byref(opt), _stream(stream)),
+           "moe_ffn_fused_noalloc")
     return out
 
 

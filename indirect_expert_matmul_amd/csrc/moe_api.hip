@@ -311,6 +311,8 @@ moe_status check_gemm_limits(const GemmArgs& g, int msub, int64_t gathered_rows,
 
 }  // namespace
 
+void moe::set_last_error(const char* msg) { g_err = msg; }
+
 extern "C" {
 
 const char* moe_status_string(moe_status s) {

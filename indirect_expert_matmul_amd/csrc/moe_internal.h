@@ -58,6 +58,9 @@ constexpr int kDecMaxSlots = 256;          // GEMV path: n_tokens * n_used
 constexpr int64_t kDecMaxWidth = 16384;    // GEMV path: widest staged activation row
 constexpr int kAlign = 256;                // workspace sub-buffer alignment
 
+// Sets the thread-local message moe_last_error() returns.
+void set_last_error(const char* msg);
+
 // ---------------------------------------------------------------- row ids (K1)
 struct RowIdsArgs {
     const int32_t* ids;   // [n] flattened [T][k]
