@@ -31,11 +31,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (the quantized-activation path)
 Q8_BYTES = 34.0 / 32.0      # Q8_0: 32 int8 + one fp16 scale per 32 weights
 MXFP4_BYTES = 17.0 / 32.0   # MXFP4: 32 four-bit codes + one E8M0 scale byte per 32 weights
 
 STAGES = {1: ["row_ids", "gemm_gate_up", "gemm_down", "reduce"],
-          2: ["gemv_gate_up", "gemv_down", "reduce"]}
+          2: ["gemv_gate_up", "gemv_down", "reduce"],
+          3: ["row_ids", "quant_x", "gemm_gate_up", "quant_h", "gemm_down", "reduce"]}
 
 
 def parse():
@@ -48,6 +50,8 @@ def parse():
     p.add_argument("--config", default="lite")
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
+    p.add_argument("--act-quant", type=int, default=0,
+                   help="1: quantized activations (int8 MFMA grouped GEMM, Q8_0 experts)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--graph", type=int, default=0,
                    help="1: time replays of one HIP graph per weight copy (each graph holds one "
@@ -307,7 +311,10 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
         return moe.weights_from_numpy(qs, d)
 
     path = moe.moe_select_path(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), path=args.path)
-    st = workload_stats(inp, cfg, 2 if path == 1 else 4)
+    aq = args.act_quant
+    if aq:
+        path = 3
+    st = workload_stats(inp, cfg, 4 if path == 2 else 2)
     R = args.rotate or (1 if st["bytes"] > 2e9 else max(4, int(np.ceil(1.2e9 / st["bytes"]))))
     sets = []
     base = [up(inp[n + "_qs"], inp[n + "_d"]) for n in ("gate", "up", "down")]
@@ -323,7 +330,8 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
     ids = torch.from_numpy(inp["ids"]).to(dev)
     rw = torch.from_numpy(inp["route_w"]).to(dev)
     out = torch.empty((T, cfg.n_embd), dtype=torch.float32, device=dev)
-    need = moe.moe_ffn_fused_workspace_size(base[0], sh[0] if sh else None, T, k, path=args.path)
+    need = moe.moe_ffn_fused_workspace_size(base[0], sh[0] if sh else None, T, k, path=args.path,
+                                            act_quant=aq)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     if args.calib_copy_mib:
@@ -336,7 +344,7 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
     def step(i, events=None):
         (g, u, d), s = sets[i % R]
         moe.moe_ffn_fused(g, u, d, x, ids, rw, shared=s, path=args.path, out=out, workspace=ws,
-                          stream=stream, events=events)
+                          stream=stream, events=events, act_quant=aq)
 
     pre = before_warmup() if before_warmup else None
     warmup = warm_up(step, warmup)
@@ -352,7 +360,7 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
                 with torch.cuda.graph(g, stream=cap):
                     (gw, uw, dw), sw_ = sets[r]
                     moe.moe_ffn_fused(gw, uw, dw, x, ids, rw, shared=sw_, path=args.path, out=out,
-                                      workspace=ws, stream=cap)
+                                      workspace=ws, stream=cap, act_quant=aq)
             graphs.append(g)
         torch.cuda.synchronize()
         run = lambda i: graphs[i % R].replay()
@@ -381,15 +389,16 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
     dom = max(stage_ms, key=stage_ms.get)
     kern = {"gemm_gate_up": "gate_up", "gemv_gate_up": "gate_up", "gemm_down": "down",
             "gemv_down": "down", "gemv_down_reduce": "down_reduce", "reduce": "reduce"}.get(dom)
-    mfma_bound = path == 1 and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = path in (1, 3) and st["flops"] / (BF16_PEAK_TFLOPS * 1e12) > st["bytes"] / (HBM_PEAK_GBS * 1e9)
     traffic = measured_traffic(name, dom)
     if kern is None:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": None, "traffic": None, "kernel": dom}
     elif mfma_bound:
         a = st[kern]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": a, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": a / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": dom,
+        pk, unit = (INT8_PEAK_TOPS, "TOP/s") if path == 3 else (BF16_PEAK_TFLOPS, "TFLOP/s")
+        roof = {"bound": "mfma", "achieved": a, "peak": pk, "unit": unit,
+                "frac": a / pk, "traffic": traffic, "kernel": dom,
                 "algorithmic_bytes": st[kern]["bytes"], "intermediate_bytes": st[kern]["intermediate_bytes"]}
     else:
         a = st[kern]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
@@ -398,13 +407,14 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
                 "algorithmic_bytes": st[kern]["bytes"], "intermediate_bytes": st[kern]["intermediate_bytes"]}
 
     res = {
-        "workload": cfg.desc, "name": name, "n_tokens": T, "path": "gemm" if path == 1 else "gemv",
+        "workload": cfg.desc, "name": name, "n_tokens": T,
+        "path": {1: "gemm", 2: "gemv", 3: "gemm, int8 activations"}[path],
         "weight_copies": R, "steps": steps, "warmup": warmup, "ms_per_step": ms,
         "tokens_per_s": T / (ms * 1e-3),
         "tflops": st["flops"] / (ms * 1e-3) / 1e12,
         "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
         "stage_ms": stage_ms, "roofline": roof,
-        "dtype": "bf16" if path == 1 else "f32",
+        "dtype": {1: "bf16", 2: "f32", 3: "int8"}[path],
         "cfg": cfg, "inp": inp, "stats": st, "stream": stream, "pre": pre,
     }
     if cpu_seconds > 0:

@@ -103,7 +103,14 @@ typedef struct {
 typedef struct {
     int32_t path; /* 0 auto, 1 force grouped GEMM, 2 force GEMV (decode)        */
     float tau;    /* <= 0 means the default, 1.0                                 */
-    int32_t reserved[6];
+    /* 1: quantized activations (the MMQ-style path; Q8_0 experts only): activation
+     * rows are quantized (moe_quantize_act's format) and the grouped GEMM runs int8
+     * MFMA with per-block scales, for every batch size (path must be 0 or 1). The
+     * fused FFN quantizes x before gate/up and h (rounded to bf16) before down.
+     * Kernel order for timing: row ids, quantize, grouped GEMM[, quantize h, down
+     * grouped GEMM], reduce / fix-up. 0 (default): bf16 activations. */
+    int32_t act_quant;
+    int32_t reserved[5];
     void *const *timing_events;
     int32_t n_timing_events;
     int32_t reserved2;
@@ -193,6 +200,22 @@ moe_status moe_ffn_fused_noalloc(const moe_weights *gate, const moe_weights *up,
                                  const void *x, moe_dtype x_type, const int32_t *ids,
                                  const float *route_w, int64_t n_tokens, int32_t n_used, float *out,
                                  const moe_options *opt, void *stream);
+
+/*
+ * moe_quantize_act -- the activation format of the quantized-activation path (the
+ * pages' mmq_id multiplies quantized experts with quantized activations, "CUDA: better
+ * MoE implementation", section 2.1; they do not define the format, so it is a
+ * reading): each row of x is cut into blocks of 32 columns; a block gets the float32
+ * scale d = max|x| / 127 and int8 codes q = x / d rounded to the nearest integer, ties
+ * to even (float32 division and rounding; clamped to [-127, 127]); a block of zeros has
+ * d = 0 and q = 0. Value = d * q. x must be finite.
+ *   x   device BF16 or F32 [rows][K], K % 32 == 0 (MOE_ELIMIT otherwise), 16-byte aligned
+ *   q   device int8 [rows][K] (written, 16-byte aligned); d device float32 [rows][K/32]
+ *       (written)
+ * rows = 0 is a no-op. No workspace. Deterministic.
+ */
+moe_status moe_quantize_act(const void *x, moe_dtype x_type, int64_t rows, int64_t K, int8_t *q,
+                            float *d, void *stream);
 
 /*
  * moe_router_topk -- the step ahead of the op: the ids table the op consumes (section

@@ -29,7 +29,7 @@ PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
            "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
            "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error",
-           "moe_last_stage_count", "moe_ffn_fused_noalloc")
+           "moe_last_stage_count", "moe_ffn_fused_noalloc", "moe_quantize_act")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -46,8 +46,8 @@ class c_moe_weights(ctypes.Structure):
 
 
 class c_moe_options(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("tau", ctypes.c_float),
-                ("reserved", ctypes.c_int32 * 6), ("timing_events", ctypes.POINTER(ctypes.c_void_p)),
+    _fields_ = [("path", ctypes.c_int32), ("tau", ctypes.c_float), ("act_quant", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5), ("timing_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_timing_events", ctypes.c_int32), ("reserved2", ctypes.c_int32)]
 
 
@@ -64,8 +64,9 @@ def _load():
     lib.moe_ffn_fused.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P, SZ, P]
     lib.moe_router_topk.argtypes = [P, I64, I32, I32, P, P, P]
     lib.moe_ffn_fused_noalloc.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P]
+    lib.moe_quantize_act.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
     for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused, lib.moe_router_topk,
-              lib.moe_ffn_fused_noalloc):
+              lib.moe_ffn_fused_noalloc, lib.moe_quantize_act):
         f.restype = ctypes.c_int
     lib.moe_row_ids_workspace_size.argtypes = [I64, I32, I32]
     lib.moe_mul_mat_id_workspace_size.argtypes = [W, ctypes.c_int, I32, I64, I32, O]
@@ -148,10 +149,12 @@ class Weights:
                              d.shape[0], d.shape[1], self.cols)
 
 
-def _options(path: int = PATH_AUTO, tau: float = 0.0, events: Optional[Sequence[int]] = None):
+def _options(path: int = PATH_AUTO, tau: float = 0.0, events: Optional[Sequence[int]] = None,
+             act_quant: int = 0):
     o = c_moe_options()
     o.path = path
     o.tau = tau
+    o.act_quant = act_quant
     if events:
         arr = (ctypes.c_void_p * len(events))(*events)
         o.timing_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
@@ -250,6 +253,21 @@ def moe_row_ids(ids: torch.Tensor, n_experts: int, src1_rows_per_token: int = 1,
     return s1, dd, b
 
 
+def moe_quantize_act(x: torch.Tensor, stream=None):
+    """(q int8 [rows][K], d float32 [rows][K/32]) for activations x [rows][K] (bf16 or its
+    16-bit patterns, or float32): the quantized-activation format of the int8 path."""
+    if x.dim() != 2 or x.shape[1] % 32:
+        raise ValueError("x must be [rows][K] with K % 32 == 0")
+    _dev_check(x)
+    rows, K = x.shape
+    q = torch.empty((rows, K), dtype=torch.int8, device=x.device)
+    d = torch.empty((rows, K // 32), dtype=torch.float32, device=x.device)
+    _keep_alive(stream, q, d)
+    _check(lib.moe_quantize_act(x.data_ptr(), _xtype(x), rows, K, q.data_ptr(), d.data_ptr(),
+                                _stream(stream)), "moe_quantize_act")
+    return q, d
+
+
 def moe_router_topk(logits: torch.Tensor, n_used: int, ids: Optional[torch.Tensor] = None,
                     route_w: Optional[torch.Tensor] = None, stream=None):
     """(ids int32 [T][k], route_w float32 [T][k]) from router logits float32 [T][E]:
@@ -277,17 +295,20 @@ def moe_router_topk(logits: torch.Tensor, n_used: int, ids: Optional[torch.Tenso
 
 def moe_mul_mat_id_workspace_size(w: Weights, src1_type: int, src1_rows_per_token: int,
                                   n_tokens: int, n_used: int, path: int = PATH_AUTO,
-                                  tau: float = 0.0) -> int:
+                                  tau: float = 0.0, act_quant: int = 0) -> int:
     cw = w.c()
     return lib.moe_mul_mat_id_workspace_size(ctypes.byref(cw), src1_type, src1_rows_per_token,
-                                             n_tokens, n_used, ctypes.byref(_options(path, tau)))
+                                             n_tokens, n_used,
+                                             ctypes.byref(_options(path, tau, act_quant=act_quant)))
 
 
 def moe_mul_mat_id(w: Weights, src1: torch.Tensor, ids: torch.Tensor,
                    route_w: Optional[torch.Tensor] = None, src1_rows_per_token: int = 1,
                    path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None, stream=None, events=None):
-    """GGML_OP_MUL_MAT_ID: float32 [T][k][N] per slot, or [T][N] weighted by route_w."""
+                   workspace: Optional[torch.Tensor] = None, stream=None, events=None,
+                   act_quant: int = 0):
+    """GGML_OP_MUL_MAT_ID: float32 [T][k][N] per slot, or [T][N] weighted by route_w.
+    ``act_quant=1``: the quantized-activation (int8 MFMA) grouped GEMM, Q8_0 experts."""
     _check_ids(ids, route_w)
     T, k = ids.shape
     cw = w.c()
@@ -302,7 +323,7 @@ def moe_mul_mat_id(w: Weights, src1: torch.Tensor, ids: torch.Tensor,
         out = torch.empty(shape, dtype=torch.float32, device=ids.device)
         _keep_alive(stream, out)
     st = _xtype(src1)
-    opt = _options(path, tau, events)
+    opt = _options(path, tau, events, act_quant)
     need = lib.moe_mul_mat_id_workspace_size(ctypes.byref(cw), st, src1_rows_per_token, T, k,
                                              ctypes.byref(opt))
     ws = _workspace(need, ids.device, workspace, stream)
@@ -315,19 +336,22 @@ def moe_mul_mat_id(w: Weights, src1: torch.Tensor, ids: torch.Tensor,
 
 
 def moe_ffn_fused_workspace_size(gate: Weights, sh_gate: Optional[Weights], n_tokens: int,
-                                 n_used: int, path: int = PATH_AUTO, tau: float = 0.0) -> int:
+                                 n_used: int, path: int = PATH_AUTO, tau: float = 0.0,
+                                 act_quant: int = 0) -> int:
     cg = gate.c()
     cs = sh_gate.c() if sh_gate is not None else None
     return lib.moe_ffn_fused_workspace_size(ctypes.byref(cg), ctypes.byref(cs) if cs else None,
                                             MOE_BF16, n_tokens, n_used,
-                                            ctypes.byref(_options(path, tau)))
+                                            ctypes.byref(_options(path, tau, act_quant=act_quant)))
 
 
 def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, ids: torch.Tensor,
                   route_w: torch.Tensor, shared: Optional[Sequence[Weights]] = None,
                   path: int = PATH_AUTO, tau: float = 0.0, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None, events=None):
-    """Fused MoE FFN: float32 [T][n_embd]."""
+                  workspace: Optional[torch.Tensor] = None, stream=None, events=None,
+                  act_quant: int = 0):
+    """Fused MoE FFN: float32 [T][n_embd]. ``act_quant=1``: the quantized-activation
+    (int8 MFMA) grouped GEMMs, Q8_0 experts."""
     _check_ids(ids, route_w)
     T, k = ids.shape
     cg, cu, cd = gate.c(), up.c(), down.c()
@@ -339,7 +363,7 @@ def moe_ffn_fused(gate: Weights, up: Weights, down: Weights, x: torch.Tensor, id
     if out is None:
         out = torch.empty((T, cg.cols), dtype=torch.float32, device=x.device)
         _keep_alive(stream, out)
-    opt = _options(path, tau, events)
+    opt = _options(path, tau, events, act_quant)
     need = lib.moe_ffn_fused_workspace_size(ctypes.byref(cg),
                                             ctypes.byref(cs[0]) if cs[0] is not None else None,
                                             MOE_BF16, T, k, ctypes.byref(opt))
@@ -356,7 +380,7 @@ def moe_ffn_fused_noalloc(gate: Weights, up: Weights, down: Weights, x: torch.Te
                           ids: torch.Tensor, route_w: torch.Tensor,
                           shared: Optional[Sequence[Weights]] = None, path: int = PATH_AUTO,
                           tau: float = 0.0, out: Optional[torch.Tensor] = None, stream=None,
-                          events=None):
+                          events=None, act_quant: int = 0):
     """The fused MoE FFN with the library's own fixed scratch array as workspace (the C
     call allocates nothing; pass ``out`` to allocate nothing here either). Calls that
     overlap in time on one device share that array and race."""
@@ -371,7 +395,7 @@ def moe_ffn_fused_noalloc(gate: Weights, up: Weights, down: Weights, x: torch.Te
     if out is None:
         out = torch.empty((T, cg.cols), dtype=torch.float32, device=x.device)
         _keep_alive(stream, out)
-    opt = _options(path, tau, events)
+    opt = _options(path, tau, events, act_quant)
     ref = [ctypes.byref(c) if c is not None else None for c in cs]
     _check(lib.moe_ffn_fused_noalloc(ctypes.byref(cg), ctypes.byref(cu), ctypes.byref(cd), ref[0], ref[1],
                                      ref[2], x.data_ptr(), _xtype(x), ids.data_ptr(), route_w.data_ptr(),

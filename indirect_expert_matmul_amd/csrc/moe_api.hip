@@ -137,6 +137,20 @@ int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4
     return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
 }
 
+// With options.act_quant = 1: 3 (the quantized-activation grouped GEMM, Q8_0 experts
+// only, whatever the batch size), else the choice above; or a negative status.
+int select_path_aq(int64_t T, int32_t k, int32_t E, int64_t act_width, int32_t wtype,
+                   const moe_options* o) {
+    const int32_t aq = o ? o->act_quant : 0;
+    if (aq != 0 && aq != 1) return fail(MOE_EINVAL, "options.act_quant must be 0 or 1 (got %d)", aq);
+    if (!aq) return select_path_fmt(T, k, E, act_width, wtype == MOE_MXFP4, o);
+    if (wtype != MOE_Q8_0) return fail(MOE_EINVAL, "quantized activations (act_quant = 1) need Q8_0 experts");
+    if (o->path != 0 && o->path != 1)
+        return fail(MOE_EINVAL, "quantized activations run on the grouped GEMM only: options.path must "
+                    "be 0 or 1 (got %d)", o->path);
+    return 3;
+}
+
 int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n : E); }
 
 // ---------------------------------------------------------------- workspace plans
@@ -179,13 +193,26 @@ struct FfnPlan {
     int msub;
     RowIdsPlan r;
     void *h, *hsh, *y, *ysh;
+    // quantized-activation path: codes and block scales of x, h and the shared h
+    int8_t *xq, *hq, *hshq;
+    float *xd, *hd, *hshd;
 };
 
 FfnPlan carve_ffn(Carve& c, const FfnDims& d, int path) {
     FfnPlan p{};
     p.path = path;
     const int64_t n = d.T * d.k;
-    if (path == 1) {
+    if (path == 3) {
+        p.r = carve_row_ids(c, n, d.E, true, kQ8aTileM);
+        p.xq = (int8_t*)c.take((size_t)d.T * d.n_embd);
+        p.xd = (float*)c.take((size_t)d.T * (d.n_embd / 32) * 4);
+        p.h = c.take((size_t)n * d.n_ff * 2);
+        p.hsh = c.take((size_t)d.S * d.T * d.n_ff_sh * 2);
+        p.hq = (int8_t*)c.take((size_t)n * d.n_ff);
+        p.hd = (float*)c.take((size_t)n * (d.n_ff / 32) * 4);
+        p.hshq = (int8_t*)c.take((size_t)d.S * d.T * d.n_ff_sh);
+        p.hshd = (float*)c.take((size_t)d.S * d.T * (d.n_ff_sh / 32) * 4);
+    } else if (path == 1) {
         p.msub = gemm_pick_msub((double)n / d.E);
         p.r = carve_row_ids(c, n, d.E, true, gemm_tile_m(p.msub));
         p.h = c.take((size_t)n * d.n_ff * 2);
@@ -204,13 +231,20 @@ struct MmidPlan {
     int msub;
     RowIdsPlan r;
     void* y;
+    int8_t* aq;   // quantized-activation path: src1 codes [T*B][K] and block scales
+    float* ad;
 };
 
-MmidPlan carve_mmid(Carve& c, int64_t T, int32_t k, int32_t E, int64_t N, bool weighted, bool q8, int path) {
+MmidPlan carve_mmid(Carve& c, int64_t T, int32_t k, int32_t E, int64_t N, bool weighted, bool q8, int path,
+                    int32_t B = 1, int64_t K = 0) {
     MmidPlan p{};
     p.path = path;
     const int64_t n = T * k;
-    if (!q8 || path == 1) {
+    if (path == 3) {
+        p.r = carve_row_ids(c, n, E, true, kQ8aTileM);
+        p.aq = (int8_t*)c.take((size_t)(T * B) * K);
+        p.ad = (float*)c.take((size_t)(T * B) * (K / 32) * 4);
+    } else if (!q8 || path == 1) {
         p.msub = gemm_pick_msub((double)n / E);
         p.r = carve_row_ids(c, n, E, true, q8 ? gemm_tile_m(p.msub) : 0);
     }
@@ -309,6 +343,26 @@ moe_status check_gemm_limits(const GemmArgs& g, int msub, int64_t gathered_rows,
     return MOE_OK;
 }
 
+moe_status check_q8a_limits(const GemmArgs& g, int64_t gathered_rows, int64_t K, const char* what) {
+    if (gathered_rows * K > k4GiB - 256)
+        return fail(MOE_ELIMIT, "%s: the gathered int8 activation tensor must be under 4 GiB "
+                    "(%lld rows x %lld columns)", what, (long long)gathered_rows, (long long)K);
+    if (gemm_q8a_max_threads(g) >= k4GiB)
+        return fail(MOE_ELIMIT, "%s: the grouped GEMM grid exceeds 2^32 work-items", what);
+    return MOE_OK;
+}
+
+// One activation quantization part: rows x K of bf16 -> codes and block scales.
+QuantPart qpart(const void* src, int64_t rows, int64_t K, int8_t* q, float* d) {
+    QuantPart p{};
+    p.src = src;
+    p.rows = rows;
+    p.K = K;
+    p.q = q;
+    p.d = d;
+    return p;
+}
+
 }  // namespace
 
 void moe::set_last_error(const char* msg) { g_err = msg; }
@@ -388,7 +442,7 @@ size_t moe_ffn_fused_workspace_size(const moe_weights* gate, const moe_weights* 
     if (validate_ffn(gate, &up, &down, (su ? sh_gate : nullptr), su, (su ? &sdown : nullptr),
                      x_type, n_tokens, n_used, &d))
         return 0;
-    const int path = select_path_fmt(d.T, d.k, d.E, ffn_act_width(d), d.fp4, opt);
+    const int path = select_path_aq(d.T, d.k, d.E, ffn_act_width(d), gate->type, opt);
     if (path < 0) return 0;
     Carve c(nullptr);
     carve_ffn(c, d, path);
@@ -410,7 +464,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         return MOE_OK;
     }
     if (!x || !ids || !route_w || !out) return fail(MOE_EINVAL, "NULL pointer argument");
-    const int path = select_path_fmt(d.T, d.k, d.E, ffn_act_width(d), d.fp4, opt);
+    const int path = select_path_aq(d.T, d.k, d.E, ffn_act_width(d), gate->type, opt);
     if (path < 0) return (moe_status)path;
     Carve sz(nullptr);
     carve_ffn(sz, d, path);
@@ -423,7 +477,112 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
     const bool shared = d.S > 0;
     bool reduced = false;
 
-    if (path == 1) {
+    if (path == 3) {
+        // quantized activations: row ids, x -> codes, gate/up int8 GEMM (h in bf16),
+        // h -> codes, down int8 GEMM, then the reduce below
+        const int bm = kQ8aTileM;
+        RowIdsArgs ra = row_ids_args(ids, n, d.k, d.E, 1, p.r);
+        ra.tile_off[0] = p.r.tile_a;
+        ra.tile_m[0] = bm;
+        ra.tile_tab[0] = p.r.tile_tab;
+        ra.tile_cap[0] = p.r.tile_cap;
+        QuantArgs qx{};
+        qx.src_bf16 = 1;
+        qx.n_part = 1;
+        qx.part[0] = qpart(x, d.T, d.n_embd, p.xq, p.xd);
+        GemmArgs g{};
+        g.mode = 1;
+        g.n_prob = shared ? 2 : 1;
+        GemmProblem& r = g.p[0];
+        r.qs1 = (const int8_t*)gate->data;
+        r.d1 = (const uint16_t*)gate->scales;
+        r.qs2 = (const int8_t*)up->data;
+        r.d2 = (const uint16_t*)up->scales;
+        r.N = d.n_ff;
+        r.K = d.n_embd;
+        r.bounds = p.r.bounds;
+        r.tile_off = p.r.tile_a;
+        r.tile_tab = p.r.tile_tab;
+        r.n_seg = d.E;
+        r.m_tiles_max = (int32_t)m_tiles_bound(n, d.E, bm);
+        r.Aq = p.xq;
+        r.Ad = p.xd;
+        r.a_rows = p.r.ids_src1;
+        r.out = p.h;
+        r.ldo = d.n_ff;
+        if (shared) {
+            GemmProblem& q = g.p[1];
+            q.qs1 = (const int8_t*)sh_gate->data;
+            q.d1 = (const uint16_t*)sh_gate->scales;
+            q.qs2 = (const int8_t*)sh_up->data;
+            q.d2 = (const uint16_t*)sh_up->scales;
+            q.N = d.n_ff_sh;
+            q.K = d.n_embd;
+            q.n_seg = d.S;
+            q.seg_len = (int32_t)d.T;
+            q.m_tiles_max = (int32_t)(d.S * ((d.T + bm - 1) / bm));
+            q.Aq = p.xq;
+            q.Ad = p.xd;
+            q.a_row_mod = (int32_t)d.T;
+            q.out = p.hsh;
+            q.ldo = d.n_ff_sh;
+        }
+        QuantArgs qh{};
+        qh.src_bf16 = 1;
+        qh.n_part = shared ? 2 : 1;
+        qh.part[0] = qpart(p.h, n, d.n_ff, p.hq, p.hd);
+        if (shared) qh.part[1] = qpart(p.hsh, (int64_t)d.S * d.T, d.n_ff_sh, p.hshq, p.hshd);
+        GemmArgs g2{};
+        g2.mode = 0;
+        g2.n_prob = shared ? 2 : 1;
+        GemmProblem& r2 = g2.p[0];
+        r2.qs1 = (const int8_t*)down->data;
+        r2.d1 = (const uint16_t*)down->scales;
+        r2.N = d.n_embd;
+        r2.K = d.n_ff;
+        r2.bounds = p.r.bounds;
+        r2.tile_off = p.r.tile_a;
+        r2.tile_tab = p.r.tile_tab;
+        r2.n_seg = d.E;
+        r2.m_tiles_max = r.m_tiles_max;
+        r2.Aq = p.hq;
+        r2.Ad = p.hd;
+        r2.out = p.y;
+        r2.ldo = d.n_embd;
+        r2.out_rows = p.r.ids_dst;
+        if (shared) {
+            GemmProblem& q = g2.p[1];
+            q.qs1 = (const int8_t*)sh_down->data;
+            q.d1 = (const uint16_t*)sh_down->scales;
+            q.N = d.n_embd;
+            q.K = d.n_ff_sh;
+            q.n_seg = d.S;
+            q.seg_len = (int32_t)d.T;
+            q.m_tiles_max = g.p[1].m_tiles_max;
+            q.Aq = p.hshq;
+            q.Ad = p.hshd;
+            q.out = p.ysh;
+            q.ldo = d.n_embd;
+        }
+        if ((uintptr_t)x % 16) return fail(MOE_EINVAL, "quantized activations: x must be 16-byte aligned");
+        if ((s = check_q8a_limits(g, d.T, d.n_embd, "gate/up"))) return s;
+        if ((s = check_q8a_limits(g2, 0, d.n_ff, "down"))) return s;
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_quant_act(qx, st), "quantize x"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8a(g, st), "gate/up grouped GEMM (int8)"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_quant_act(qh, st), "quantize h"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8a(g2, st), "down grouped GEMM (int8)"))) return s;
+        tm.end();
+    } else if (path == 1) {
         const int bm = gemm_tile_m(p.msub);
         RowIdsArgs ra = row_ids_args(ids, n, d.k, d.E, 1, p.r);
         ra.tile_off[0] = p.r.tile_a;
@@ -603,14 +762,13 @@ size_t moe_mul_mat_id_workspace_size(const moe_weights* w, moe_dtype src1_type,
                                      int32_t n_used, const moe_options* opt) {
     if (validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used)) return 0;
     const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
-    if (!q8 && opt && opt->path != 0 && opt->path != 1) return 0;
-    const int path = q8 ? select_path_fmt(n_tokens, n_used, (int32_t)w->n_mat, w->cols,
-                                          w->type == MOE_MXFP4, opt)
-                        : 1;
+    if (!q8 && opt && ((opt->path != 0 && opt->path != 1) || opt->act_quant)) return 0;
+    const int path = q8 ? select_path_aq(n_tokens, n_used, (int32_t)w->n_mat, w->cols, w->type, opt) : 1;
     if (path < 0) return 0;
     // the weighted and unweighted calls use the same plan size when weighted
     Carve c(nullptr);
-    carve_mmid(c, n_tokens, n_used, (int32_t)w->n_mat, w->rows, true, q8, path);
+    carve_mmid(c, n_tokens, n_used, (int32_t)w->n_mat, w->rows, true, q8, path, src1_rows_per_token,
+               w->cols);
     return c.off;
 }
 
@@ -632,22 +790,68 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     if (!q8 && opt && opt->path != 0 && opt->path != 1)
         return fail(MOE_EINVAL, "float32 experts run the grouped fp32 product only: options.path "
                     "must be 0 or 1 (got %d)", opt->path);
+    if (!q8 && opt && opt->act_quant)
+        return fail(MOE_EINVAL, "quantized activations (act_quant = 1) need Q8_0 experts");
     if (!q8 && n_tokens * k * (int64_t)N >= k4GiB - 256)
         return fail(MOE_ELIMIT, "float32 mul_mat_id: n_tokens * n_used * N must be under 2^32");
-    const int path = q8 ? select_path_fmt(n_tokens, k, E, K, w->type == MOE_MXFP4, opt) : 1;
+    const int path = q8 ? select_path_aq(n_tokens, k, E, K, w->type, opt) : 1;
     if (path < 0) return (moe_status)path;
     const bool weighted = route_w != nullptr;
     Carve sz(nullptr);
-    carve_mmid(sz, n_tokens, k, E, N, weighted, q8, path);
+    carve_mmid(sz, n_tokens, k, E, N, weighted, q8, path, B, K);
     if (sz.off > ws_bytes || (sz.off && !ws)) return fail(MOE_EWORKSPACE, "workspace needs %zu bytes", sz.off);
     Carve c(ws);
-    const MmidPlan p = carve_mmid(c, n_tokens, k, E, N, weighted, q8, path);
+    const MmidPlan p = carve_mmid(c, n_tokens, k, E, N, weighted, q8, path, B, K);
     const hipStream_t st = (hipStream_t)stream;
     Timer tm(opt, st);
     const int64_t n = n_tokens * k;
     float* slot_out = weighted ? (float*)p.y : dst;  // per-slot rows [T*k][N]
 
-    if (!q8 || path == 1) {
+    if (path == 3) {
+        // quantized activations: row ids, src1 -> codes, int8 grouped GEMM, then the
+        // reduce / zero fix-up below
+        const int bm = kQ8aTileM;
+        RowIdsArgs ra = row_ids_args(ids, n, k, E, B, p.r);
+        ra.tile_off[0] = p.r.tile_a;
+        ra.tile_m[0] = bm;
+        ra.tile_tab[0] = p.r.tile_tab;
+        ra.tile_cap[0] = p.r.tile_cap;
+        QuantArgs qa{};
+        qa.src_bf16 = 1;
+        qa.n_part = 1;
+        qa.part[0] = qpart(src1, n_tokens * B, K, p.aq, p.ad);
+        GemmArgs g{};
+        g.mode = 0;
+        g.n_prob = 1;
+        GemmProblem& r = g.p[0];
+        r.qs1 = (const int8_t*)w->data;
+        r.d1 = (const uint16_t*)w->scales;
+        r.N = N;
+        r.K = K;
+        r.bounds = p.r.bounds;
+        r.tile_off = p.r.tile_a;
+        r.tile_tab = p.r.tile_tab;
+        r.n_seg = E;
+        r.m_tiles_max = (int32_t)m_tiles_bound(n, E, bm);
+        r.Aq = p.aq;
+        r.Ad = p.ad;
+        r.a_rows = p.r.ids_src1;
+        r.out = slot_out;
+        r.ldo = N;
+        r.out_rows = p.r.ids_dst;
+        if ((uintptr_t)src1 % 16) return fail(MOE_EINVAL, "quantized activations: src1 must be 16-byte aligned");
+        if ((s = check_q8a_limits(g, n_tokens * B, K, "mul_mat_id"))) return s;
+        if (n_tokens * B * (K / 32) >= k4GiB) return fail(MOE_ELIMIT, "mul_mat_id: too many activation blocks");
+        tm.begin();
+        if ((s = hip_check(launch_row_ids(ra, st, nullptr), "row ids"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_quant_act(qa, st), "quantize src1"))) return s;
+        tm.end();
+        tm.begin();
+        if ((s = hip_check(launch_gemm_q8a(g, st), "grouped GEMM (int8)"))) return s;
+        tm.end();
+    } else if (!q8 || path == 1) {
         const int bm = gemm_tile_m(p.msub);
         RowIdsArgs ra = row_ids_args(ids, n, k, E, B, p.r);
         GemmArgs g{};
@@ -745,6 +949,24 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
     tm.end();
     g_stages = tm.stage;
     return MOE_OK;
+}
+
+moe_status moe_quantize_act(const void* x, moe_dtype x_type, int64_t rows, int64_t K, int8_t* q,
+                            float* d, void* stream) {
+    g_err.clear();
+    if (x_type != MOE_BF16 && x_type != MOE_F32) return fail(MOE_EINVAL, "x must be BF16 or F32");
+    if (rows < 0 || K <= 0) return fail(MOE_EINVAL, "rows must be >= 0 and K > 0");
+    if (K % 32) return fail(MOE_ELIMIT, "K must be a multiple of 32 (got %lld)", (long long)K);
+    if (rows > 0 && (!x || !q || !d)) return fail(MOE_EINVAL, "NULL pointer argument");
+    if (((uintptr_t)x | (uintptr_t)q) % 16 || (uintptr_t)d % 4)
+        return fail(MOE_EINVAL, "x and q must be 16-byte aligned, d 4-byte aligned");
+    if (rows > 0 && rows * (K / 32) >= k4GiB - 256)
+        return fail(MOE_ELIMIT, "rows * K / 32 must be under 2^32");
+    QuantArgs a{};
+    a.n_part = 1;
+    a.src_bf16 = x_type == MOE_BF16;
+    a.part[0] = qpart(x, rows, K, q, d);
+    return hip_check(launch_quant_act(a, (hipStream_t)stream), "quantize activations");
 }
 
 moe_status moe_router_topk(const float* logits, int64_t n_tokens, int32_t n_experts, int32_t n_used,

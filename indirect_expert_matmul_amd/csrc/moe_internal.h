@@ -103,6 +103,10 @@ struct GemmProblem {
     int32_t m_tiles_max;      // grid upper bound on M tiles of this problem
     const uint16_t* A;        // bf16 activations
     int64_t lda;
+    // quantized-activation GEMM only: int8 activation codes [rows][K] and float32
+    // scales [rows][K/32] (one per 32-column block); rows indexed as for A
+    const int8_t* Aq;
+    const float* Ad;
     const int32_t* a_rows;    // A row of position j, or nullptr: row (a_row_mod ? j % a_row_mod : j)
     int32_t a_row_mod;
     void* out;
@@ -130,6 +134,29 @@ hipError_t launch_gemm_q8(const GemmArgs& a, int msub, hipStream_t st);
 // Upper bound on the work-items launch_gemm_q8 would launch for these arguments (a
 // dispatch holds fewer than 2^32).
 int64_t gemm_q8_max_threads(const GemmArgs& a, int msub);
+
+// ---------------------------------------------------------------- quantized activations
+// Rows of 32-column blocks -> int8 codes and one float32 scale per block:
+// d = max|x| / 127, q = rint(x / d) (float32, ties to even), clamped to [-127, 127].
+struct QuantPart {
+    const void* src;   // [rows][K], bf16 bits (src_bf16) or float32
+    int64_t rows, K;   // K % 32 == 0
+    int8_t* q;         // [rows][K]
+    float* d;          // [rows][K/32]
+};
+struct QuantArgs {
+    QuantPart part[2]; // one launch quantizes up to two tensors (e.g. h and the shared h)
+    int32_t n_part;
+    int32_t src_bf16;
+    int64_t blocks0;   // set by the launcher: thread blocks of part 0
+};
+hipError_t launch_quant_act(const QuantArgs& a, hipStream_t st);
+// Grouped GEMM of Q8_0 experts with quantized activations (GemmProblem.Aq / Ad; fmt 0
+// weights; tile_tab required for routed problems; 128-row tiles: m_tiles_max and the
+// row-id pass's tile tables must use tile height 128).
+hipError_t launch_gemm_q8a(const GemmArgs& a, hipStream_t st);
+int64_t gemm_q8a_max_threads(const GemmArgs& a);
+constexpr int kQ8aTileM = 128;
 
 // ---------------------------------------------------------------- fp32 grouped matmul (Tiny)
 struct GemmF32Args {

@@ -211,3 +211,37 @@ def test_binding_rejects_wrong_dtypes_and_shapes():
     with pytest.raises(ValueError, match="x must be"):
         moe.moe_ffn_fused(w, w, moe.Weights(torch.zeros((4, 64, 32), dtype=torch.int8),
                                             torch.zeros((4, 64, 1), dtype=torch.int16)), x[:5], ids, rw)
+
+
+def test_act_quant_validation():
+    """Quantized activations: Q8_0 experts only, the grouped GEMM only (path 0 or 1),
+    act_quant 0 or 1; moe_quantize_act needs K % 32 == 0 and a bf16 or float32 input."""
+    fp4 = lambda **kw: _w(typ=moe.MOE_MXFP4, **kw)
+
+    def ffn(gate=None, up=None, down=None, path=0, aq=1, ws=16):
+        gate = gate or _w()
+        up = up or _w()
+        down = down or _w(rows=128, cols=64)
+        opt = moe._options(path, act_quant=aq)
+        return moe.lib.moe_ffn_fused(ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down), None, None,
+                                     None, FAKE, moe.MOE_BF16, FAKE, FAKE, 16, 2, FAKE, ctypes.byref(opt),
+                                     FAKE, ws, None)
+    assert ffn() == moe.MOE_EWORKSPACE                  # valid: stops at the fake workspace
+    assert ffn(path=1) == moe.MOE_EWORKSPACE
+    assert ffn(path=2) == moe.MOE_EINVAL
+    assert ffn(aq=2) == moe.MOE_EINVAL
+    assert ffn(gate=fp4(), up=fp4(), down=fp4(rows=128, cols=64)) == moe.MOE_EINVAL
+    g = _w(n_mat=64, rows=1408, cols=2048)
+    a = moe.lib.moe_ffn_fused_workspace_size(ctypes.byref(g), None, moe.MOE_BF16, 512, 6,
+                                              ctypes.byref(moe._options(0, act_quant=1)))
+    b = moe.lib.moe_ffn_fused_workspace_size(ctypes.byref(g), None, moe.MOE_BF16, 512, 6, None)
+    assert a > b > 0
+    f32 = _w(n_mat=8, rows=32, cols=64, typ=moe.MOE_F32)
+    opt = moe._options(0, act_quant=1)
+    assert moe.lib.moe_mul_mat_id(ctypes.byref(f32), FAKE, moe.MOE_F32, 1, FAKE, 16, 2, None, FAKE,
+                                  ctypes.byref(opt), FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    q = moe.lib.moe_quantize_act
+    assert q(FAKE, moe.MOE_BF16, 4, 100, FAKE, FAKE, None) == moe.MOE_ELIMIT
+    assert q(FAKE, moe.MOE_Q8_0, 4, 64, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert q(None, moe.MOE_BF16, 4, 64, FAKE, FAKE, None) == moe.MOE_EINVAL
+    assert q(None, moe.MOE_BF16, 0, 64, None, None, None) == moe.MOE_OK
