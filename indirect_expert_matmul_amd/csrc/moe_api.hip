@@ -55,10 +55,10 @@ struct Timer {
     Timer(const moe_options* o, hipStream_t s)
         : ev(o ? o->timing_events : nullptr), n(o ? o->n_timing_events : 0), st(s) {}
     void begin() {
-        if (ev && 2 * stage + 1 < n) hipEventRecord((hipEvent_t)ev[2 * stage], st);
+        if (ev && 2 * stage + 1 < n) (void)hipEventRecord((hipEvent_t)ev[2 * stage], st);
     }
     void end() {
-        if (ev && 2 * stage + 1 < n) hipEventRecord((hipEvent_t)ev[2 * stage + 1], st);
+        if (ev && 2 * stage + 1 < n) (void)hipEventRecord((hipEvent_t)ev[2 * stage + 1], st);
         stage++;
     }
 };
@@ -155,7 +155,8 @@ int64_t m_tiles_bound(int64_t n, int64_t E, int bm) { return n / bm + (n < E ? n
 
 // ---------------------------------------------------------------- workspace plans
 struct RowIdsPlan {
-    int32_t *ids_src1, *ids_dst, *bounds, *tile_a, *tile_tab, *chunk_cnt, *bucket_tot;
+    int32_t *ids_src1, *ids_dst, *bounds, *tile_a, *tile_tab;
+    void* scratch;   // multi-block scratch of the row-id pass (row_ids_scratch_bytes)
     int32_t tile_cap;
 };
 // tile_m > 0: also room for the GEMM's M-tile prefix and per-tile table (tiles of
@@ -174,11 +175,7 @@ RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, int tile_m) 
         p.tile_tab = (int32_t*)c.take(sizeof(int32_t) * 4 * (size_t)p.tile_cap);
     }
     const size_t sb = row_ids_scratch_bytes(n, E);
-    if (sb) {
-        const int64_t nc = (int64_t)(sb - (size_t)(E + 1) * sizeof(int32_t)) / sizeof(int32_t);
-        p.chunk_cnt = (int32_t*)c.take(sizeof(int32_t) * nc);
-        p.bucket_tot = (int32_t*)c.take(sizeof(int32_t) * (E + 1));
-    }
+    if (sb) p.scratch = c.take(sb);
     return p;
 }
 
@@ -323,8 +320,7 @@ RowIdsArgs row_ids_args(const int32_t* ids, int64_t n, int32_t k, int32_t E, int
     a.ids_src1 = p.ids_src1;
     a.ids_dst = p.ids_dst;
     a.bounds = p.bounds;
-    a.chunk_cnt = p.chunk_cnt;
-    a.bucket_tot = p.bucket_tot;
+    if (p.scratch) row_ids_carve_scratch(a, p.scratch);
     return a;
 }
 

@@ -76,12 +76,18 @@ struct RowIdsArgs {
     // bounds[e], rows of e}; tile_cap[i] entries of room (an upper bound on the count)
     int32_t* tile_tab[2];
     int32_t tile_cap[2];
-    int32_t* chunk_cnt;   // multi-block scratch [E + 1][n_chunks] (bucket-major)
-    int32_t* bucket_tot;  // multi-block scratch [E + 1]
+    // multi-block scratch (row_ids_carve_scratch places it in row_ids_scratch_bytes):
+    int32_t* chunk_cnt;   // [E + 1][n_chunks] per-chunk counts, then their prefix over chunks
+    int32_t* bucket_tot;  // [E + 1] bucket totals, then bucket starts
+    int32_t* wcnt;        // [n_chunks][waves][E + 1] per-wave counts of each chunk
+    uint16_t* rank16;     // [n] rank of each entry among its wave's entries of its bucket
     int64_t n_chunks;
     int64_t chunk;        // entries per chunk (multi-block)
+    uint32_t k_magic;     // ii / k == (ii * k_magic) >> k_shift for ii < 2^31
+    int32_t k_shift;
 };
 size_t row_ids_scratch_bytes(int64_t n, int32_t E);
+void row_ids_carve_scratch(RowIdsArgs& a, void* scratch);
 hipError_t launch_row_ids(const RowIdsArgs& a, hipStream_t st, int* n_launches);
 
 // ---------------------------------------------------------------- grouped GEMM (K3/K4)

@@ -18,6 +18,9 @@
 //   * Bucket E collects ids outside [0, E): they land after all expert segments.
 //   * Inputs up to kRowIdsOneBlockMax entries run as one 1024-thread workgroup (one
 //     launch); larger ones use count / scan-over-chunks / scan-over-buckets / place.
+//     The count pass already ranks every entry inside its (wave, bucket) group and
+//     stores that rank (16 bits) and each wave's counts, so the place pass needs no
+//     ballots: position = bucket start + chunk offset + wave offset + rank.
 #include "moe_internal.h"
 
 namespace moe {
@@ -305,17 +308,55 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
 }
 
 // ---------------------------------------------------------------- multi-block
+// Counts one chunk and ranks its entries: each wave walks its range, and every entry
+// gets its rank among the wave's earlier entries of the same bucket (stored as 16 bits:
+// a wave's range is at most kMaxBatchesPerWave * 64 entries). The wave's counts go to
+// wcnt (chunk-major) for the place pass, the chunk's totals to chunk_cnt (bucket-major)
+// for the scan over chunks.
 __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
     __shared__ int32_t cnt[kWaves * kMaxBuckets];
     const int NB = a.E + 1, nbits = bucket_bits(NB);
-    const int w = threadIdx.x >> 6;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
     __syncthreads();
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     const int64_t per = a.chunk / kWaves;
     const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
-    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
+    int32_t* run_w = cnt + w * NB;
+    // ranks one group of kPre batches starting at entry b0
+    auto rank_group = [&](const int (&bk)[kPre], int64_t b0) {
+#pragma unroll
+        for (int q = 0; q < kPre; q++) {
+            const int64_t bb = b0 + q * 64;
+            if (bb >= end) break;  // uniform
+            const bool act = bk[q] >= 0;
+            const int b = act ? bk[q] : 0;
+            const uint64_t m = match_bucket(b, __ballot(act), nbits);
+            int32_t prev = 0;
+            if (act) {
+                prev = run_w[b];
+                a.rank16[bb + lane] = (uint16_t)(prev + rank_below(m));
+            }
+            // every lane has read its counter before the group's leader bumps it
+            __builtin_amdgcn_wave_barrier();
+            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+    // two groups of batches in registers: the next group loads while this one is ranked
+    constexpr int64_t G = kPre * 64;
+    int bk0[kPre], bk1[kPre];
+    if (beg < end) load_batches(a.ids, beg, end, a.E, bk0);
+    for (int64_t b0 = beg; b0 < end; b0 += 2 * G) {
+        if (b0 + G < end) load_batches(a.ids, b0 + G, end, a.E, bk1);
+        rank_group(bk0, b0);
+        if (b0 + G >= end) break;
+        if (b0 + 2 * G < end) load_batches(a.ids, b0 + 2 * G, end, a.E, bk0);
+        rank_group(bk1, b0 + G);
+    }
     __syncthreads();
+    int32_t* wc = a.wcnt + (int64_t)blockIdx.x * kWaves * NB;
+    for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) wc[i] = cnt[i];
     for (int b = threadIdx.x; b < NB; b += kThreads) {
         int32_t s = 0;
         for (int v = 0; v < kWaves; v++) s += cnt[v * NB + b];
@@ -368,91 +409,88 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_scan_buckets(RowIdsArgs a)
     for (int b = threadIdx.x; b < NB; b += kThreads) a.bucket_tot[b] = bstart[b];
 }
 
-// Places one chunk. The chunk's entries are first put in bucket order in LDS (their
-// position inside the chunk: the bucket's start in the chunk + the wave's offset +
-// the running count + the rank in the batch), then every bucket's run is written out
+// Places one chunk from the count pass's ranks. The chunk's entries are first put in
+// bucket order in LDS (position inside the chunk: the bucket's start in the chunk + the
+// wave's offset + the entry's rank), then every bucket's run is written out
 // contiguously: consecutive output positions come from consecutive threads, instead of
 // each entry storing to a scattered position of its own.
 __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     __shared__ int32_t wsum[kWaves];
-    // LDS, sized for this launch: per-wave offsets (then running counts) [kWaves][NB],
-    // bucket starts inside the chunk [NB + 1], global start of each bucket's run [NB],
-    // and the chunk in bucket order: entry index [chunk], bucket [chunk]
+    // LDS, sized for this launch: per-wave offsets [kWaves][NB], bucket starts inside the
+    // chunk [NB + 1], global start of each bucket's run [NB], and the chunk in bucket
+    // order: bucket << 16 | index in the chunk [chunk]
     extern __shared__ __attribute__((aligned(16))) int32_t lds[];
-    const int NB = a.E + 1, nbits = bucket_bits(NB);
-    int32_t* cnt = lds;
-    int32_t* cstart = cnt + kWaves * NB;
+    const int NB = a.E + 1;
+    int32_t* woff = lds;
+    int32_t* cstart = woff + kWaves * NB;
     int32_t* gbase = cstart + NB + 1;
-    int32_t* st_i = gbase + NB;
-    uint16_t* st_bk = (uint16_t*)(st_i + a.chunk);
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    for (int i = tid; i < kWaves * NB; i += kThreads) cnt[i] = 0;
-    __syncthreads();
+    uint32_t* st = (uint32_t*)(gbase + NB);
+    const int tid = threadIdx.x;
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     const int64_t per = a.chunk / kWaves;
-    const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
-    wave_count(a.ids, beg, end, a.E, nbits, cnt + w * NB);
-    __syncthreads();
+    const int32_t* wc = a.wcnt + (int64_t)blockIdx.x * kWaves * NB;
     for (int b = tid; b < NB; b += kThreads) {
         int32_t run = 0;
         for (int v = 0; v < kWaves; v++) {
-            const int32_t t = cnt[v * NB + b];
-            cnt[v * NB + b] = run;
+            const int32_t t = wc[v * NB + b];
+            woff[v * NB + b] = run;
             run += t;
         }
         cstart[b] = run;
+        gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
     }
     __syncthreads();
     const int32_t chunk_n = block_scan(cstart, NB, wsum);
-    for (int b = tid; b < NB; b += kThreads)
-        gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
-    __syncthreads();
-    int32_t* run_w = cnt + w * NB;
-    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
-        int bk[kPre];
-        load_batches(a.ids, b0, end, a.E, bk);
-#pragma unroll
-        for (int q = 0; q < kPre; q++) {
-            const int64_t bb = b0 + q * 64;
-            if (bb >= end) break;  // uniform
-            const int64_t i = bb + lane;
-            const bool act = bk[q] >= 0;
-            const int b = act ? bk[q] : 0;
-            const uint64_t m = match_bucket(b, __ballot(act), nbits);
-            int32_t prev = 0;
-            if (act) {
-                prev = run_w[b];
-                const int32_t lp = cstart[b] + prev + rank_below(m);   // position in the chunk
-                st_i[lp] = (int32_t)i;  // n < 2^31 is a validated limit
-                st_bk[lp] = (uint16_t)b;
-                if (a.inv) a.inv[i] = gbase[b] + lp - cstart[b];
-            }
-            // every lane has read its counter before the group's leader bumps it
-            __builtin_amdgcn_wave_barrier();
-            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
-            __builtin_amdgcn_wave_barrier();
-        }
+    const int64_t cn = min(a.chunk, a.n - c0);
+    for (int64_t e = tid; e < cn; e += kThreads) {
+        const int b = bucket_of(a.ids[c0 + e], a.E);
+        const int v = (int)(e / per);
+        const int32_t lp = cstart[b] + woff[v * NB + b] + a.rank16[c0 + e];
+        st[lp] = ((uint32_t)b << 16) | (uint32_t)e;
     }
     __syncthreads();
     for (int32_t p = tid; p < chunk_n; p += kThreads) {
-        const int b = st_bk[p];
+        const uint32_t v = st[p];
+        const int b = (int)(v >> 16);
         const int32_t g = gbase[b] + p - cstart[b];
-        const int32_t ii = st_i[p];
-        const int32_t t = ii / a.k;
-        const int32_t s = ii - t * a.k;
-        a.ids_src1[g] = t * a.B + s % a.B;
-        a.ids_dst[g] = ii;
+        const uint32_t ii = (uint32_t)(c0 + (v & 0xffffu));   // n < 2^31 is a validated limit
+        const uint32_t t = (uint32_t)(((uint64_t)ii * a.k_magic) >> a.k_shift);   // ii / k
+        const uint32_t s = ii - t * (uint32_t)a.k;
+        a.ids_src1[g] = (int32_t)(t * a.B + s % a.B);
+        a.ids_dst[g] = (int32_t)ii;
+        if (a.inv) a.inv[ii] = g;
     }
 }
 
 }  // namespace
 
+namespace {
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+}  // namespace
+
+// Multi-block scratch, in this order: chunk_cnt [NB][n_chunks], bucket_tot [NB],
+// wcnt [n_chunks][kWaves][NB], rank16 [n].
 size_t row_ids_scratch_bytes(int64_t n, int32_t E) {
     if (n <= kRowIdsOneBlockMax) return 0;
     const int64_t ch = chunk_len(n);
     const int64_t nc = (n + ch - 1) / ch;
-    const size_t a = (size_t)nc * (size_t)(E + 1) * sizeof(int32_t);
-    return ((a + kAlign - 1) / kAlign) * kAlign + (size_t)(E + 1) * sizeof(int32_t);
+    const size_t NB = (size_t)E + 1;
+    return align_up((size_t)nc * NB * 4) + align_up(NB * 4) + align_up((size_t)nc * kWaves * NB * 4) +
+           align_up((size_t)n * 2);
+}
+
+void row_ids_carve_scratch(RowIdsArgs& a, void* scratch) {
+    const int64_t ch = chunk_len(a.n);
+    const int64_t nc = (a.n + ch - 1) / ch;
+    const size_t NB = (size_t)a.E + 1;
+    char* p = (char*)scratch;
+    a.chunk_cnt = (int32_t*)p;
+    p += align_up((size_t)nc * NB * 4);
+    a.bucket_tot = (int32_t*)p;
+    p += align_up(NB * 4);
+    a.wcnt = (int32_t*)p;
+    p += align_up((size_t)nc * kWaves * NB * 4);
+    a.rank16 = (uint16_t*)p;
 }
 
 hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches) {
@@ -468,13 +506,21 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
     }
     a.chunk = chunk_len(a.n);
     a.n_chunks = (a.n + a.chunk - 1) / a.chunk;
-    // the place kernel's LDS: counters and starts for NB buckets, then the chunk in
-    // bucket order (an int and a short per entry)
+    // ii / k as a multiply-high: M = floor(2^(31 + l) / k) + 1 with l = ceil(log2 k) is
+    // exact for every ii < 2^31
+    {
+        int l = 0;
+        while ((1 << l) < a.k) l++;
+        a.k_magic = (uint32_t)(((uint64_t)1 << (31 + l)) / (uint64_t)a.k + 1);
+        a.k_shift = 31 + l;
+    }
+    // the place kernel's LDS: wave offsets and starts for NB buckets, then the chunk in
+    // bucket order (one word per entry)
     const int64_t NB = a.E + 1;
-    const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 6;
+    const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 4;
     static PerDeviceOnce lds_cap;
     if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place,
-                                         (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 6)))
+                                         (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 4)))
         return e;
     k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
     k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
