@@ -26,16 +26,28 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_ROWIDS_CHUNKS
+#define MOE_ROWIDS_CHUNKS 2048   // chunks the multi-block pass aims at
+#endif
+#ifndef MOE_ROWIDS_MAXB
+#define MOE_ROWIDS_MAXB 16       // batches of 64 per wave per chunk, at most
+#endif
+#ifndef MOE_ROWIDS_PRE
+#define MOE_ROWIDS_PRE 8         // batches of ids loaded ahead of their use
+#endif
+
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kMaxBatchesPerWave = 16;
+constexpr int kMaxBatchesPerWave = MOE_ROWIDS_MAXB;
+static_assert(kMaxBatchesPerWave * 64 <= 65536, "ranks inside a wave's range are 16-bit");
 constexpr int64_t kMaxChunk = (int64_t)kThreads * kMaxBatchesPerWave;   // 8192 entries
 
-// Entries per chunk of the multi-block pass: about 2048 chunks, each wave walking 2 to
-// 16 batches of 64 (long enough walks keep the id loads ahead of their use, and few
-// chunks keep the per-chunk counts small).
+// Entries per chunk of the multi-block pass: about MOE_ROWIDS_CHUNKS chunks, each wave
+// walking 2 to kMaxBatchesPerWave batches of 64 (long enough walks keep the id loads
+// ahead of their use, and few chunks keep the per-chunk counts small).
 int64_t chunk_len(int64_t n) {
-    int64_t bpw = (n + 2048 * (int64_t)kThreads - 1) / (2048 * (int64_t)kThreads);
+    constexpr int64_t kTarget = MOE_ROWIDS_CHUNKS;
+    int64_t bpw = (n + kTarget * (int64_t)kThreads - 1) / (kTarget * (int64_t)kThreads);
     bpw = bpw < 2 ? 2 : (bpw > kMaxBatchesPerWave ? kMaxBatchesPerWave : bpw);
     return bpw * kThreads;
 }
@@ -65,7 +77,7 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-constexpr int kPre = 8;  // batches of ids loaded ahead of their use
+constexpr int kPre = MOE_ROWIDS_PRE;  // batches of ids loaded ahead of their use
 
 // Loads of batches [bb, bb + kPre*64): one id per lane per batch, bucket E past the end.
 __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, int64_t bb,
