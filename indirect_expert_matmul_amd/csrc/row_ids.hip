@@ -426,17 +426,26 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_scan_buckets(RowIdsArgs a)
 // wave's offset + the entry's rank), then every bucket's run is written out
 // contiguously: consecutive output positions come from consecutive threads, instead of
 // each entry storing to a scattered position of its own.
+// LOCAL: few chunks (kLocalScanChunks at most): every block scans the per-chunk counts
+// itself -- its bucket's prefix over the earlier chunks and the bucket totals -- so the
+// two scan launches are skipped; block 0 also writes the bounds and tile tables.
+constexpr int64_t kLocalScanChunks = 128;
+
+template <bool LOCAL>
 __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     __shared__ int32_t wsum[kWaves];
     // LDS, sized for this launch: per-wave offsets [kWaves][NB], bucket starts inside the
     // chunk [NB + 1], global start of each bucket's run [NB], and the chunk in bucket
-    // order: bucket << 16 | index in the chunk [chunk]
+    // order: bucket << 16 | index in the chunk [chunk]; LOCAL adds the bucket starts
+    // [NB + 1] and a tile-count scratch [NB + 1]
     extern __shared__ __attribute__((aligned(16))) int32_t lds[];
     const int NB = a.E + 1;
     int32_t* woff = lds;
     int32_t* cstart = woff + kWaves * NB;
     int32_t* gbase = cstart + NB + 1;
     uint32_t* st = (uint32_t*)(gbase + NB);
+    int32_t* bstart = (int32_t*)(st + a.chunk);
+    int32_t* tmp = bstart + NB + 1;
     const int tid = threadIdx.x;
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     const int64_t per = a.chunk / kWaves;
@@ -449,9 +458,32 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
             run += t;
         }
         cstart[b] = run;
-        gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
+        if constexpr (LOCAL) {
+            const int32_t* row = a.chunk_cnt + (int64_t)b * a.n_chunks;   // this bucket, chunk order
+            int32_t pre = 0, tot = 0;
+            const int nc = (int)a.n_chunks;
+#pragma unroll 8
+            for (int c = 0; c < nc; c++) {   // independent loads, kept in flight together
+                const int32_t t = row[c];
+                pre += c < (int)blockIdx.x ? t : 0;
+                tot += t;
+            }
+            gbase[b] = pre;
+            bstart[b] = tot;
+        } else {
+            gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
+        }
     }
     __syncthreads();
+    if constexpr (LOCAL) {
+        block_scan(bstart, NB, wsum);   // bucket totals -> bucket starts
+        for (int b = tid; b < NB; b += kThreads) gbase[b] += bstart[b];
+        if (blockIdx.x == 0) {   // block-uniform
+            bstart[NB] = a.n;     // (bounds past the valid buckets are never read)
+            write_bounds_and_tiles(a, bstart, tmp, wsum);
+        }
+        __syncthreads();
+    }
     const int32_t chunk_n = block_scan(cstart, NB, wsum);
     const int64_t cn = min(a.chunk, a.n - c0);
     for (int64_t e = tid; e < cn; e += kThreads) {
@@ -530,14 +562,24 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
     // bucket order (one word per entry)
     const int64_t NB = a.E + 1;
     const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 4;
+    const size_t stage_local = stage + (size_t)(2 * NB + 2) * 4;
+    constexpr int kCap = (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 4);
+    if (a.n_chunks <= kLocalScanChunks) {
+        static PerDeviceOnce lds_cap;
+        if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place<true>,
+                                             kCap + (2 * kMaxBuckets + 2) * 4))
+            return e;
+        k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
+        k_row_ids_place<true><<<(unsigned)a.n_chunks, kThreads, stage_local, st>>>(a);
+        if (n_launches) *n_launches = 2;
+        return hipGetLastError();
+    }
     static PerDeviceOnce lds_cap;
-    if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place,
-                                         (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 4)))
-        return e;
+    if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place<false>, kCap)) return e;
     k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
     k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
     k_row_ids_scan_buckets<<<1, kThreads, 0, st>>>(a);
-    k_row_ids_place<<<(unsigned)a.n_chunks, kThreads, stage, st>>>(a);
+    k_row_ids_place<false><<<(unsigned)a.n_chunks, kThreads, stage, st>>>(a);
     if (n_launches) *n_launches = 4;
     return hipGetLastError();
 }
