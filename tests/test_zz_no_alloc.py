@@ -62,3 +62,32 @@ def test_noalloc_refuses_calls_beyond_the_array():
     assert "scratch" in moe.last_error()
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
+
+
+@pytest.mark.parametrize("name,path", [("dec8", moe.PATH_AUTO), ("lite", moe.PATH_GEMM)])
+def test_noalloc_under_graph_capture(name, path):
+    """The callers it is for: the call captured into a HIP graph (no allocation happens
+    during capture) and replayed five times, with eager writes to the output and syncs
+    between replays; every replay must reproduce the workspace call's bytes."""
+    dv = upload_ffn(synth.make_inputs(name))
+    T, n_embd = dv["x"].shape
+    ref = moe.moe_ffn_fused(dv["gate"], dv["up"], dv["down"], dv["x"], dv["ids"], dv["route_w"],
+                            shared=dv["shared"], path=path)
+    out = torch.empty((T, n_embd), dtype=torch.float32, device="cuda")
+    args = (dv["gate"], dv["up"], dv["down"], dv["x"], dv["ids"], dv["route_w"])
+    moe.moe_ffn_fused_noalloc(*args, shared=dv["shared"], path=path, out=out)   # first call on the device
+    torch.cuda.synchronize()
+    assert _same_bytes(out, ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_ffn_fused_noalloc(*args, shared=dv["shared"], path=path, out=out, stream=side)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _same_bytes(out, ref)
