@@ -57,9 +57,10 @@ def parse():
                    help="1: time replays of one HIP graph per weight copy (each graph holds one "
                         "step); 0: eager calls")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--extra", default="skew,dec1,dec8",
+    p.add_argument("--extra", default="dec1,dec8,skew",
                    help="further workloads reported on the same line under 'workloads' "
-                        "(comma-separated; empty for none)")
+                        "(comma-separated, timed in this order before the headline one; "
+                        "empty for none)")
     p.add_argument("--extra-cpu-seconds", type=float, default=3.0,
                    help="CPU oracle budget for each further workload")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -290,12 +291,10 @@ def bench_row_ids(args):
     print(json.dumps(res), flush=True)
 
 
-def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=False,
-                     before_warmup=None):
-    """Time one FFN workload: warm-up, then `steps` timed steps (each one full layer
-    call on inputs resident in HBM, weights rotated through R copies), then one pass
-    with per-kernel HIP events. `before_warmup` (optional) runs once the inputs are on
-    the device, just before the warm-up. Returns the measurements as a dict."""
+def prepare_ffn_workload(args, name):
+    """Inputs of one FFN workload drawn and made resident in HBM: the weights in R
+    copies (rotated through by the steps, so the set a step reads is not served from
+    the 256 MB last-level cache), x, ids, route_w, output and workspace."""
     import torch
     import indirect_expert_matmul_amd as moe
     import synth
@@ -346,7 +345,21 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
         moe.moe_ffn_fused(g, u, d, x, ids, rw, shared=s, path=args.path, out=out, workspace=ws,
                           stream=stream, events=events, act_quant=aq)
 
-    pre = before_warmup() if before_warmup else None
+    return {"name": name, "cfg": cfg, "inp": inp, "st": st, "path": path, "R": R, "sets": sets,
+            "x": x, "ids": ids, "rw": rw, "out": out, "ws": ws, "stream": stream, "step": step}
+
+
+def time_ffn_workload(args, W, steps, warmup):
+    """Time a prepared FFN workload: warm-up, then `steps` timed steps (each one full
+    layer call), then one pass with per-kernel HIP events recorded by the library on
+    the stream its kernels run on. Returns the measurements as a dict."""
+    import torch
+    import indirect_expert_matmul_amd as moe
+
+    name, cfg, inp, st, path, R, sets = (W[n] for n in ("name", "cfg", "inp", "st", "path", "R", "sets"))
+    x, ids, rw, out, ws, stream, step = (W[n] for n in ("x", "ids", "rw", "out", "ws", "stream", "step"))
+    T = inp["ids"].shape[0]
+    aq = args.act_quant
     warmup = warm_up(step, warmup)
     run = step
     if args.graph:
@@ -415,51 +428,73 @@ def run_ffn_workload(args, name, steps, warmup, cpu_seconds, single_thread_cpu=F
         "gbps": st["bytes"] / (ms * 1e-3) / 1e9,
         "stage_ms": stage_ms, "roofline": roof,
         "dtype": {1: "bf16", 2: "f32", 3: "int8"}[path],
-        "cfg": cfg, "inp": inp, "stats": st, "stream": stream, "pre": pre,
+        "cfg": cfg, "inp": inp, "stats": st, "stream": stream,
     }
-    if cpu_seconds > 0:
-        fpt = st["flops"] / T
-        res["cpu_baseline"] = cpu_baseline(inp, cpu_seconds, fpt)
-        if single_thread_cpu:
-            res["cpu_baseline"]["single_thread"] = {
-                k2: v for k2, v in cpu_baseline(inp, min(cpu_seconds, 3.0), fpt, threads=1).items()
-                if k2 in ("value", "gflops_fp64", "sample")}
-    else:
-        res["cpu_baseline"] = None
+    res["cpu_baseline"] = None
     return res
 
 
-def time_router(cfg, stream, seconds=0.25):
+def attach_cpu_baseline(res, cpu_seconds, single_thread_cpu=False):
+    """The oracle timed on the host for a measured workload (run after all GPU timing,
+    so the GPU does not idle between its timed workloads while the host computes)."""
+    if cpu_seconds <= 0:
+        return
+    inp, st = res["inp"], res["stats"]
+    fpt = st["flops"] / res["n_tokens"]
+    res["cpu_baseline"] = cpu_baseline(inp, cpu_seconds, fpt)
+    if single_thread_cpu:
+        res["cpu_baseline"]["single_thread"] = {
+            k2: v for k2, v in cpu_baseline(inp, min(cpu_seconds, 3.0), fpt, threads=1).items()
+            if k2 in ("value", "gflops_fp64", "sample")}
+
+
+def time_router(cfg, stream, seconds=0.25, calls=64):
     """The router top-k that produces ids / route_w ahead of the layer (not part of the
-    step), timed on logits of the workload's shape for about `seconds` of back-to-back
-    calls, and reported beside the layer. It runs first: from idle the GPU clocks take
-    some milliseconds to ramp up, and this keeps them up for the layer's warm-up."""
+    step), timed on logits of the workload's shape and reported beside the layer.
+    One call is a few microseconds of GPU time, less than a Python call costs, so the
+    calls are captured into a graph of `calls` back-to-back launches that is replayed
+    for about `seconds`: the figure is GPU time per call, launch gaps inside the graph
+    included. It runs first: from idle the GPU clocks take some milliseconds to ramp
+    up, and the busy GPU keeps them up for the layer's warm-up."""
     import torch
     import indirect_expert_matmul_amd as moe
     import synth
     T, k = cfg.n_tokens, cfg.n_used
     dev = torch.device("cuda:0")
     lg = torch.from_numpy(synth.draw_router_logits(cfg.seed, T, cfg.n_experts)).to(dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    rw = torch.empty((T, k), dtype=torch.float32, device=dev)
     for _ in range(3):
-        moe.moe_router_topk(lg, k, stream=stream)
+        moe.moe_router_topk(lg, k, ids=ids, route_w=rw, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(calls):
+                moe.moe_router_topk(lg, k, ids=ids, route_w=rw, stream=cap)
     torch.cuda.synchronize()
     n_router, t0 = 0, time.perf_counter()
     r0, r1 = KernelEvent(), KernelEvent()
     r0.record(stream)
     while time.perf_counter() - t0 < seconds:
-        for _ in range(50):
-            moe.moe_router_topk(lg, k, stream=stream)
-        n_router += 50
+        for _ in range(8):
+            graph.replay()
+        n_router += 8 * calls
+        torch.cuda.synchronize()
     r1.record(stream)
     torch.cuda.synchronize()
     router_us = r0.elapsed_time(r1) * 1e3 / n_router
+    del graph
     return {"us": router_us, "gbps": (T * cfg.n_experts * 4 + T * k * 8) / (router_us * 1e-6) / 1e9,
-            "n_experts": cfg.n_experts, "n_used": k, "calls": n_router}
+            "n_experts": cfg.n_experts, "n_used": k, "calls": n_router,
+            "launch": "graph of %d back-to-back calls" % calls}
 
 
 def _public(r):
     """The JSON-ready part of a workload result."""
-    return {k: v for k, v in r.items() if k not in ("cfg", "inp", "stats", "stream", "pre")}
+    return {k: v for k, v in r.items() if k not in ("cfg", "inp", "stats", "stream")}
 
 
 def main():
@@ -479,24 +514,32 @@ def main():
     cfg = synth.CONFIGS[args.config]
     T, k = cfg.n_tokens, cfg.n_used
     stream = torch.cuda.current_stream()
-    r = run_ffn_workload(args, args.config, args.steps, args.warmup,
-                         0 if args.no_cpu else args.cpu_seconds,
-                         single_thread_cpu=cfg.n_tokens <= 16,
-                         before_warmup=lambda: time_router(cfg, stream))
-    router = r["pre"]
-
-    # the other workloads of the metric (PP4096 prefill, decode batches of 1 and 8), on
-    # the same line: each with its own dominant-kernel roofline
-    extras = {}
+    # Every workload's inputs are made resident first, then the GPU timing runs back
+    # to back: the routers, the further workloads of the metric (PP4096 prefill, decode
+    # batches of 1 and 8; each with its own dominant-kernel roofline), and the headline
+    # workload last. From idle or light load the GPU clocks take about 10 ms to ramp up,
+    # longer than a few warm-up steps of a 0.2 ms layer; timed last, the headline's
+    # warm-up starts from a GPU under load.
     names = [n for n in (args.extra.split(",") if args.extra else []) if n and n != args.config]
-    del r["inp"]
+    prep = {n: prepare_ffn_workload(args, n) for n in names + [args.config]}
+    routers = {n: time_router(prep[n]["cfg"], stream) for n in [args.config] + names}
+    extras = {}
     for n in names:
-        e = run_ffn_workload(args, n, max(10, args.steps // 2) if n in ("skew", "v3") else args.steps,
-                             args.warmup, 0 if args.no_cpu else args.extra_cpu_seconds,
-                             single_thread_cpu=synth.CONFIGS[n].n_tokens <= 16)
-        extras[n] = _public(e)
-        del e
-        torch.cuda.empty_cache()
+        extras[n] = time_ffn_workload(args, prep[n], max(10, args.steps // 2) if n in ("skew", "v3")
+                                      else args.steps, args.warmup)
+        extras[n]["router"] = routers[n]
+    r = time_ffn_workload(args, prep[args.config], args.steps, args.warmup)
+    router = routers[args.config]
+    del prep
+    torch.cuda.empty_cache()
+
+    # the CPU oracle, once the GPU timing is done
+    if not args.no_cpu:
+        attach_cpu_baseline(r, args.cpu_seconds, single_thread_cpu=cfg.n_tokens <= 16)
+        for n in names:
+            attach_cpu_baseline(extras[n], args.extra_cpu_seconds,
+                                single_thread_cpu=synth.CONFIGS[n].n_tokens <= 16)
+    extras = {n: _public(e) for n, e in extras.items()}
 
     ms = r["ms_per_step"]
     res = {
