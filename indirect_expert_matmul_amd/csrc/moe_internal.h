@@ -78,7 +78,7 @@ struct RowIdsArgs {
     int32_t tile_cap[2];
     // multi-block scratch (row_ids_carve_scratch places it in row_ids_scratch_bytes):
     int32_t* chunk_cnt;   // [E + 1][n_chunks] per-chunk counts, then their prefix over chunks
-    int32_t* bucket_tot;  // [E + 1] bucket totals, then bucket starts
+    int32_t* bucket_tot;  // [E + 1] bucket totals
     int32_t* wcnt;        // [n_chunks][waves][E + 1] per-wave counts of each chunk
     uint16_t* rank16;     // [n] rank of each entry among its wave's entries of its bucket
     int64_t n_chunks;

@@ -7,17 +7,22 @@
 //
 // gfx950 design: a stable counting sort built from wavefront primitives.
 //   * Each wave owns a contiguous range of entries (t*k + s order) and walks it 64
-//     at a time. Lanes holding the same bucket find each other with one ballot per
-//     bit of the bucket id; the group's lowest lane adds the group size to the
-//     wave's LDS counter (one writer per counter, so no atomics), and a lane's rank
-//     inside its group is a masked bit count (mbcnt).
+//     at a time. Lanes holding the same bucket find each other -- in the one-workgroup
+//     pass with one ballot per bit of the bucket id, in the multi-block count pass
+//     through a per-bucket 64-bit mask in LDS that every lane of the group ORs its
+//     bit into (OR is order-independent, so the mask is the same on every run) --;
+//     the group's lowest lane adds the group size to the wave's LDS counter (one
+//     writer per counter, no atomic counter), and a lane's rank inside its group is a
+//     masked bit count (mbcnt).
 //   * Per-bucket exclusive scans over waves (and, for large inputs, over
 //     workgroups), then over buckets, give every (wave, bucket) its first output
 //     position; a second walk over the same range places every entry. Entries keep
 //     their (t, s) order inside a bucket, so the result is unique.
 //   * Bucket E collects ids outside [0, E): they land after all expert segments.
 //   * Inputs up to kRowIdsOneBlockMax entries run as one 1024-thread workgroup (one
-//     launch); larger ones use count / scan-over-chunks / scan-over-buckets / place.
+//     launch); larger ones use count / scan-over-chunks / place, where every place
+//     block scans the bucket totals itself (with at most kLocalScanChunks chunks it
+//     also sums the per-chunk counts, and the scan over chunks is skipped).
 //     The count pass already ranks every entry inside its (wave, bucket) group and
 //     stores that rank (16 bits) and each wave's counts, so the place pass needs no
 //     ballots: position = bucket start + chunk offset + wave offset + rank.
@@ -79,15 +84,19 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 
 constexpr int kPre = MOE_ROWIDS_PRE;  // batches of ids loaded ahead of their use
 
-// Loads of batches [bb, bb + kPre*64): one id per lane per batch, bucket E past the end.
+// Loads of batches [bb, bb + kPre*64): one id per lane per batch, -1 past the end.
+// Only batches that start before the end are loaded (a wave-uniform test), and in the
+// last one every lane loads (past the end it re-reads entry end-1), so all the loads
+// are in flight before the first result is used; a load under a lane condition would
+// be waited for inside its branch, one round trip per batch.
 __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, int64_t bb,
                                              int64_t end, int32_t E, int (&b)[kPre]) {
     const int lane = threadIdx.x & 63;
+    int32_t raw[kPre];
 #pragma unroll
-    for (int q = 0; q < kPre; q++) {
-        const int64_t i = bb + q * 64 + lane;
-        b[q] = i < end ? bucket_of(ids[i], E) : -1;
-    }
+    for (int q = 0; q < kPre; q++) raw[q] = bb + q * 64 < end ? ids[min(bb + q * 64 + lane, end - 1)] : 0;
+#pragma unroll
+    for (int q = 0; q < kPre; q++) b[q] = bb + q * 64 + lane < end ? bucket_of(raw[q], E) : -1;
 }
 
 // Histogram of the loaded batches starting at entry b0 (entries from `end` on are
@@ -124,9 +133,13 @@ __device__ __forceinline__ void place_batches(const RowIdsArgs& a, const int (&b
             prev = run_w[b];
             const int32_t pos = base[b] + prev + rank_below(m);
             const int32_t ii = (int32_t)i;  // n < 2^31 is a validated limit
-            const int32_t t = ii / a.k;
-            const int32_t s = ii - t * a.k;
-            a.ids_src1[pos] = t * a.B + s % a.B;
+            // src1 row t*B + s % B: ii itself when B = k, t when B = 1
+            int32_t src = ii;
+            if (a.B != a.k) {   // uniform
+                const int32_t t = ii / a.k;
+                src = a.B == 1 ? t : t * a.B + (ii - t * a.k) % a.B;
+            }
+            a.ids_src1[pos] = src;
             a.ids_dst[pos] = ii;
             if (a.inv) a.inv[i] = pos;
         }
@@ -326,34 +339,57 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
 // wcnt (chunk-major) for the place pass, the chunk's totals to chunk_cnt (bucket-major)
 // for the scan over chunks.
 __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
-    __shared__ int32_t cnt[kWaves * kMaxBuckets];
-    const int NB = a.E + 1, nbits = bucket_bits(NB);
+    // LDS, sized for this launch: per wave, a group mask per bucket [kWaves][NB] and the
+    // running count per bucket [kWaves][NB]
+    extern __shared__ __attribute__((aligned(16))) uint64_t count_lds[];
+    const int NB = a.E + 1;
+    uint64_t* msk = count_lds;
+    int32_t* cnt = (int32_t*)(count_lds + kWaves * NB);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int i = threadIdx.x; i < kWaves * NB; i += kThreads) cnt[i] = 0;
     __syncthreads();
+    uint64_t* msk_w = msk + w * NB;
     const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
     const int64_t per = a.chunk / kWaves;
     const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
     int32_t* run_w = cnt + w * NB;
-    // ranks one group of kPre batches starting at entry b0
+    // Ranks one group of kPre batches starting at entry b0 (ids past the range are -1),
+    // in three phases whose LDS instructions are issued back to back, batch after
+    // batch, with one wait per phase (a wave's LDS instructions execute in order):
+    //   masks: the lanes of batch q holding bucket b each clear b's mask word, then OR
+    //     their own bit into it and read it back; batch q's read precedes batch q+1's
+    //     clear. OR does not depend on the order of the lanes, so the mask is the same
+    //     on every run;
+    //   counts: the group's lowest lane adds the group size to the wave's counter of b
+    //     and gets the counter's previous value; the batches' adds to one counter run in
+    //     batch order, and within a batch every counter has one adder;
+    //   ranks: each lane takes that previous value from its group's lowest lane.
     auto rank_group = [&](const int (&bk)[kPre], int64_t b0) {
+        uint64_t m[kPre];
 #pragma unroll
         for (int q = 0; q < kPre; q++) {
-            const int64_t bb = b0 + q * 64;
-            if (bb >= end) break;  // uniform
-            const bool act = bk[q] >= 0;
-            const int b = act ? bk[q] : 0;
-            const uint64_t m = match_bucket(b, __ballot(act), nbits);
-            int32_t prev = 0;
-            if (act) {
-                prev = run_w[b];
-                a.rank16[bb + lane] = (uint16_t)(prev + rank_below(m));
+            m[q] = 0;
+            if (bk[q] >= 0) {
+                msk_w[bk[q]] = 0;
+                __hip_atomic_fetch_or(msk_w + bk[q], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                m[q] = __hip_atomic_load(msk_w + bk[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-            // every lane has read its counter before the group's leader bumps it
-            __builtin_amdgcn_wave_barrier();
-            if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
-            __builtin_amdgcn_wave_barrier();
         }
+        int32_t prev[kPre];
+#pragma unroll
+        for (int q = 0; q < kPre; q++) {
+            prev[q] = 0;
+            if (bk[q] >= 0 && rank_below(m[q]) == 0)
+                prev[q] = __hip_atomic_fetch_add(run_w + bk[q], __popcll(m[q]), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        int32_t base[kPre];
+#pragma unroll
+        for (int q = 0; q < kPre; q++)
+            base[q] = __shfl(prev[q], bk[q] >= 0 ? __ffsll((unsigned long long)m[q]) - 1 : lane);
+#pragma unroll
+        for (int q = 0; q < kPre; q++)
+            if (bk[q] >= 0) a.rank16[b0 + q * 64 + lane] = (uint16_t)(base[q] + rank_below(m[q]));
     };
     // two groups of batches in registers: the next group loads while this one is ranked
     constexpr int64_t G = kPre * 64;
@@ -408,27 +444,17 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_scan_chunks(RowIdsArgs a) 
     if (tid == 0) a.bucket_tot[b] = total;
 }
 
-// Single block: bucket starts, bounds, tile prefixes; bucket_tot becomes the starts.
-__global__ __launch_bounds__(kThreads) void k_row_ids_scan_buckets(RowIdsArgs a) {
-    __shared__ int32_t bstart[kMaxBuckets + 1];
-    __shared__ int32_t tmp[kMaxBuckets + 1];
-    __shared__ int32_t wsum[kWaves];
-    const int NB = a.E + 1;
-    for (int b = threadIdx.x; b < NB; b += kThreads) bstart[b] = a.bucket_tot[b];
-    __syncthreads();
-    block_scan(bstart, NB, wsum);
-    write_bounds_and_tiles(a, bstart, tmp, wsum);
-    for (int b = threadIdx.x; b < NB; b += kThreads) a.bucket_tot[b] = bstart[b];
-}
-
 // Places one chunk from the count pass's ranks. The chunk's entries are first put in
 // bucket order in LDS (position inside the chunk: the bucket's start in the chunk + the
 // wave's offset + the entry's rank), then every bucket's run is written out
 // contiguously: consecutive output positions come from consecutive threads, instead of
 // each entry storing to a scattered position of its own.
-// LOCAL: few chunks (kLocalScanChunks at most): every block scans the per-chunk counts
-// itself -- its bucket's prefix over the earlier chunks and the bucket totals -- so the
-// two scan launches are skipped; block 0 also writes the bounds and tile tables.
+// Every block turns the bucket totals into bucket starts itself (a block scan over
+// E + 1 values), and block 0 also writes the bounds and tile tables, so no launch sits
+// between the scan over chunks and this one. LOCAL: few chunks (kLocalScanChunks at
+// most): each block also sums the per-chunk counts itself -- its bucket's prefix over
+// the earlier chunks and the bucket totals -- so the scan over chunks is skipped too.
+// Otherwise both come from the scan over chunks.
 constexpr int64_t kLocalScanChunks = 128;
 
 template <bool LOCAL>
@@ -436,8 +462,8 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     __shared__ int32_t wsum[kWaves];
     // LDS, sized for this launch: per-wave offsets [kWaves][NB], bucket starts inside the
     // chunk [NB + 1], global start of each bucket's run [NB], and the chunk in bucket
-    // order: bucket << 16 | index in the chunk [chunk]; LOCAL adds the bucket starts
-    // [NB + 1] and a tile-count scratch [NB + 1]
+    // order: bucket << 16 | index in the chunk [chunk], the bucket starts [NB + 1] and a
+    // tile-count scratch [NB + 1]
     extern __shared__ __attribute__((aligned(16))) int32_t lds[];
     const int NB = a.E + 1;
     int32_t* woff = lds;
@@ -470,20 +496,19 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
             }
             gbase[b] = pre;
             bstart[b] = tot;
-        } else {
-            gbase[b] = a.bucket_tot[b] + a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
+        } else {   // from the scan over chunks: this chunk's prefix, the bucket total
+            gbase[b] = a.chunk_cnt[(int64_t)b * a.n_chunks + blockIdx.x];
+            bstart[b] = a.bucket_tot[b];
         }
     }
     __syncthreads();
-    if constexpr (LOCAL) {
-        block_scan(bstart, NB, wsum);   // bucket totals -> bucket starts
-        for (int b = tid; b < NB; b += kThreads) gbase[b] += bstart[b];
-        if (blockIdx.x == 0) {   // block-uniform
-            bstart[NB] = a.n;     // (bounds past the valid buckets are never read)
-            write_bounds_and_tiles(a, bstart, tmp, wsum);
-        }
-        __syncthreads();
+    block_scan(bstart, NB, wsum);   // bucket totals -> bucket starts
+    for (int b = tid; b < NB; b += kThreads) gbase[b] += bstart[b];
+    if (blockIdx.x == 0) {   // block-uniform
+        bstart[NB] = a.n;     // (bounds past the valid buckets are never read)
+        write_bounds_and_tiles(a, bstart, tmp, wsum);
     }
+    __syncthreads();
     const int32_t chunk_n = block_scan(cstart, NB, wsum);
     const int64_t cn = min(a.chunk, a.n - c0);
     for (int64_t e = tid; e < cn; e += kThreads) {
@@ -499,8 +524,12 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
         const int32_t g = gbase[b] + p - cstart[b];
         const uint32_t ii = (uint32_t)(c0 + (v & 0xffffu));   // n < 2^31 is a validated limit
         const uint32_t t = (uint32_t)(((uint64_t)ii * a.k_magic) >> a.k_shift);   // ii / k
-        const uint32_t s = ii - t * (uint32_t)a.k;
-        a.ids_src1[g] = (int32_t)(t * a.B + s % a.B);
+        // src1 row t*B + s % B: ii itself when B = k, t when B = 1 (no division)
+        uint32_t src;
+        if (a.B == a.k) src = ii;         // block-uniform
+        else if (a.B == 1) src = t;
+        else src = t * a.B + (ii - t * (uint32_t)a.k) % a.B;
+        a.ids_src1[g] = (int32_t)src;
         a.ids_dst[g] = (int32_t)ii;
         if (a.inv) a.inv[ii] = g;
     }
@@ -550,6 +579,13 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
     }
     a.chunk = chunk_len(a.n);
     a.n_chunks = (a.n + a.chunk - 1) / a.chunk;
+    const size_t count_lds = (size_t)kWaves * (a.E + 1) * (sizeof(uint64_t) + sizeof(int32_t));
+    {
+        static PerDeviceOnce cap;   // the count kernel's dynamic LDS cap, once per device
+        if (const hipError_t e = set_lds_cap(cap, (const void*)k_row_ids_count,
+                                             kWaves * kMaxBuckets * (int)(sizeof(uint64_t) + sizeof(int32_t))))
+            return e;
+    }
     // ii / k as a multiply-high: M = floor(2^(31 + l) / k) + 1 with l = ceil(log2 k) is
     // exact for every ii < 2^31
     {
@@ -561,26 +597,22 @@ hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches)
     // the place kernel's LDS: wave offsets and starts for NB buckets, then the chunk in
     // bucket order (one word per entry)
     const int64_t NB = a.E + 1;
-    const size_t stage = (size_t)(kWaves * NB + 2 * NB + 1) * 4 + (size_t)a.chunk * 4;
-    const size_t stage_local = stage + (size_t)(2 * NB + 2) * 4;
-    constexpr int kCap = (int)((kWaves * kMaxBuckets + 2 * kMaxBuckets + 1) * 4 + kMaxChunk * 4);
+    const size_t stage = (size_t)(kWaves * NB + 4 * NB + 3) * 4 + (size_t)a.chunk * 4;
+    constexpr int kCap = (int)((kWaves * kMaxBuckets + 4 * kMaxBuckets + 3) * 4 + kMaxChunk * 4);
     if (a.n_chunks <= kLocalScanChunks) {
         static PerDeviceOnce lds_cap;
-        if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place<true>,
-                                             kCap + (2 * kMaxBuckets + 2) * 4))
-            return e;
-        k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
-        k_row_ids_place<true><<<(unsigned)a.n_chunks, kThreads, stage_local, st>>>(a);
+        if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place<true>, kCap)) return e;
+        k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, count_lds, st>>>(a);
+        k_row_ids_place<true><<<(unsigned)a.n_chunks, kThreads, stage, st>>>(a);
         if (n_launches) *n_launches = 2;
         return hipGetLastError();
     }
     static PerDeviceOnce lds_cap;
     if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_place<false>, kCap)) return e;
-    k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, 0, st>>>(a);
+    k_row_ids_count<<<(unsigned)a.n_chunks, kThreads, count_lds, st>>>(a);
     k_row_ids_scan_chunks<<<(unsigned)(a.E + 1), kThreads, 0, st>>>(a);
-    k_row_ids_scan_buckets<<<1, kThreads, 0, st>>>(a);
     k_row_ids_place<false><<<(unsigned)a.n_chunks, kThreads, stage, st>>>(a);
-    if (n_launches) *n_launches = 4;
+    if (n_launches) *n_launches = 3;
     return hipGetLastError();
 }
 
