@@ -857,6 +857,12 @@ __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_
     const int v = lane_expert(a, lane);
     const int D = count_experts(v, a.E);
     const int S = a.sw.n_mat;
+    // route weight of slot `lane`: loaded now, so its round trip runs under the units'
+    // work, and parked in LDS by wave 0 for the weighted sum at the end (loading the
+    // weights there, slot after slot, put one round trip per slot after the units)
+    __shared__ float s_w[kFuseSlots];
+    __shared__ int32_t s_ok[kFuseSlots];
+    const float w_l = (wv == 0 && lane < a.T * a.k && a.route_w) ? a.route_w[lane] : 1.0f;
     uint8_t* ring = smem + wv * (G::NR * G::BYTES);
     for (int u = wv; u < D + S; u += 4) {
         if (u < D) {
@@ -876,6 +882,10 @@ __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_
                 unit_regs<0, P, XBF16, NIT, FMT>(a, false, j, 0, a.T, n_lo, n_hi, emit);
         }
     }
+    if (wv == 0) {
+        s_w[lane] = w_l;
+        s_ok[lane] = v >= 0;   // slot `lane` names an expert in [0, E)
+    }
     __syncthreads();
     for (int i = tid; i < a.T * R; i += 256) {
         const int t = i / R, r = i - t * R, n = n_lo + r;
@@ -883,9 +893,7 @@ __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_
         float acc = 0.f;
         for (int s = 0; s < a.k; s++) {
             const int slot = t * a.k + s;
-            const int32_t e = a.ids[slot];
-            if (e >= 0 && e < a.E)
-                acc = fmaf(a.route_w ? a.route_w[slot] : 1.0f, s_part[slot * kFuseRows + r], acc);
+            if (s_ok[slot]) acc = fmaf(s_w[slot], s_part[slot * kFuseRows + r], acc);
         }
         for (int j = 0; j < S; j++) acc += s_shp[(j * a.T + t) * kFuseRows + r];
         a.out_tok[(int64_t)t * N + n] = acc;

@@ -32,10 +32,10 @@ namespace moe {
 namespace {
 
 #ifndef MOE_ROWIDS_CHUNKS
-#define MOE_ROWIDS_CHUNKS 2048   // chunks the multi-block pass aims at
+#define MOE_ROWIDS_CHUNKS 1024   // chunks the multi-block pass aims at
 #endif
 #ifndef MOE_ROWIDS_MAXB
-#define MOE_ROWIDS_MAXB 16       // batches of 64 per wave per chunk, at most
+#define MOE_ROWIDS_MAXB 32       // batches of 64 per wave per chunk, at most
 #endif
 #ifndef MOE_ROWIDS_PRE
 #define MOE_ROWIDS_PRE 8         // batches of ids loaded ahead of their use
@@ -45,7 +45,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxBatchesPerWave = MOE_ROWIDS_MAXB;
 static_assert(kMaxBatchesPerWave * 64 <= 65536, "ranks inside a wave's range are 16-bit");
-constexpr int64_t kMaxChunk = (int64_t)kThreads * kMaxBatchesPerWave;   // 8192 entries
+constexpr int64_t kMaxChunk = (int64_t)kThreads * kMaxBatchesPerWave;   // 16384 entries
 
 // Entries per chunk of the multi-block pass: about MOE_ROWIDS_CHUNKS chunks, each wave
 // walking 2 to kMaxBatchesPerWave batches of 64 (long enough walks keep the id loads
