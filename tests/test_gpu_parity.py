@@ -98,6 +98,23 @@ def test_q8_mul_mat_id_tall_tiles(E, k, T, K, N, bad):
     assert np.all(g[invalid] == 0.0)
 
 
+def test_q8_mul_mat_id_many_chunks():
+    """160000 rows (T = 20000, k = 8, E = 64): more than 128 chunks, so the row-id pass
+    runs its scan over chunks and its place kernel writes the bounds and the tile table
+    the GEMM reads; invalid ids included."""
+    E, k, T, K, N = 64, 8, 20000, 64, 72
+    ids = synth.draw_ids_uniform(23, T, E, k)
+    ids[5, 2], ids[T - 3, 7] = -1, E + 1
+    inp = synth.make_custom_mmid(29, E, k, T, K, N, ids=ids)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(31).standard_normal((T, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                             path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], 1)
+    assert normwise(got.cpu().numpy(), ref) <= TOL_MFMA
+
+
 # ------------------------------------------------------------------------- FFN
 
 @pytest.mark.parametrize("path", [moe.PATH_GEMM, moe.PATH_GEMV])

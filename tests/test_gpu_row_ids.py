@@ -49,6 +49,9 @@ def test_row_ids_configs_bit_exact(name, B_is_k):
     (64, 512, 8, -1, 65, 9),     # 4096 entries: the largest one-workgroup input (4 batches a wave)
     (1024, 1024, 4, 0, 1024, 10),  # 4096 entries over 1025 buckets: 17 buckets per lane in the scan
     (64, 4097, 1, 0, 64, 11),    # 4097 entries: the smallest multi-workgroup input
+    (64, 20000, 8, -2, 66, 12),     # 160000 entries: more than 128 chunks (the scan over chunks runs)
+    (1024, 40000, 4, -1, 1025, 13), # the same with the most buckets: the count pass's largest LDS
+    (1, 150000, 1, 0, 1, 14),       # one expert: every entry in one bucket, across chunks
 ])
 def test_row_ids_random_shapes(E, T, k, lo, hi, seed):
     ids = np.random.default_rng(seed).integers(lo, hi, size=(T, k)).astype(np.int32)
