@@ -249,6 +249,11 @@ def bench_row_ids(args):
     ids = torch.from_numpy(ids_np).to(dev)
     ws = torch.empty(moe.lib.moe_row_ids_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     args.warmup = warm_up(lambda i: moe.moe_row_ids(ids, E, workspace=ws, stream=stream), args.warmup)
     e0, e1 = KernelEvent(), KernelEvent()
     t0 = time.perf_counter()
@@ -285,7 +290,8 @@ def bench_row_ids(args):
                    "n_experts": E, "n_used": k, "parallelism": "single GPU"},
         "entries_per_s": T * k / (ev_ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "row_ids"},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("rowids", "row_ids"),
+                     "kernel": "row_ids", "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
