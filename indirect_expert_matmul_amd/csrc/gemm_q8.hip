@@ -598,9 +598,13 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     const GemmProblem& P = args.p[pi];
     const int N = P.N, K = P.K;
     const int n_nt = (N + NTW - 1) / NTW;
+    // tile stride TM: the 160-row form (MSUB = 5) runs 128-row tiles whose segment-last
+    // tile may hold up to tile_x = 32 rows more; the row-id pass counts tiles the same way
+    constexpr int TM = MSUB == 5 ? 128 : BM;
+    const int tx = MSUB == 5 ? P.tile_x : 0;
     int e, m0, m_len, nt;
     {
-        const int m_tiles = P.bounds ? P.tile_off[P.n_seg] : P.n_seg * ((P.seg_len + BM - 1) / BM);
+        const int m_tiles = P.bounds ? P.tile_off[P.n_seg] : P.n_seg * tiles_of(P.seg_len, TM, tx);
         const int total = m_tiles * n_nt;
         const int part = (total + 7) >> 3;
         const int q = b >> 3;
@@ -626,9 +630,9 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
                 row0 = P.bounds[e];
                 rows = P.bounds[e + 1] - row0;
             }
-            tiles = (rows + BM - 1) / BM;
+            tiles = tiles_of(rows, TM, tx);
         } else {
-            tiles = (P.seg_len + BM - 1) / BM;
+            tiles = tiles_of(P.seg_len, TM, tx);
             e = t / (n_nt * tiles);
             first = e * tiles;
             row0 = e * P.seg_len;
@@ -640,8 +644,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         const int rr = r - c * kMChunk * n_nt;
         nt = rr / g;
         const int j = c * kMChunk + (rr - nt * g);
-        m0 = row0 + j * BM;
-        m_len = min(BM, rows - j * BM);
+        m0 = row0 + j * TM;
+        m_len = j == tiles - 1 ? rows - j * TM : TM;
     }
 
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -797,7 +801,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
             const i32x4& v = q[c][ss >> 1];
             return (ss & 1) ? dequant8(v[2], v[3], d[c]) : dequant8(v[0], v[1], d[c]);
         };
-        bf16x8 af[2][4], bf[2][2];
+        bf16x8 af[2][MSUB], bf[2][2];
 #pragma unroll
         for (int i = 0; i < MACT; i++) af[0][i] = afrag(i, 0);
         bf[0][0] = deq(0, 0);
@@ -867,6 +871,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     };
     const int mact = (m_len + 31) >> 5;   // block-uniform
     if (mact >= MSUB) k_loop(std::integral_constant<int, MSUB>{});
+    else if (MSUB > 4 && mact == 4) k_loop(std::integral_constant<int, (MSUB > 4 ? 4 : 1)>{});
     else if (MSUB > 3 && mact == 3) k_loop(std::integral_constant<int, (MSUB > 3 ? 3 : 1)>{});
     else if (MSUB > 2 && mact == 2) k_loop(std::integral_constant<int, (MSUB > 2 ? 2 : 1)>{});
     else k_loop(std::integral_constant<int, 1>{});
@@ -1052,6 +1057,13 @@ int gemm_pick_msub(double avg_rows) {
 }
 int gemm_tile_m(int msub) { return 32 * msub; }
 
+#ifndef MOE_GEMM_TALL_LAST
+#define MOE_GEMM_TALL_LAST 1   // 0: 128-row tiles only (no 160-row segment-last tiles)
+#endif
+int gemm_tile_x(int msub, int fmt, int64_t K) {
+    return (MOE_GEMM_TALL_LAST && msub == 4 && fmt == 0 && K % wide::KS == 0) ? 32 : 0;
+}
+
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     GemmArgs a = a0;
     if (a.n_prob < 2) a.p[1] = GemmProblem{};
@@ -1060,6 +1072,17 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
 #ifdef MOE_GEMM_NO_WIDE
     wide_ok = false;
 #endif
+    // segment-last tiles of 128 + 32 rows: only the 160-row wide kernel takes them, and
+    // the tile tables were built for them, so any other choice is a caller error
+    bool tall = false;
+    for (int i = 0; i < a.n_prob; i++) {
+        if (a.p[i].tile_x != 0 && a.p[i].tile_x != 32) return hipErrorInvalidValue;
+        tall = tall || a.p[i].tile_x == 32;
+    }
+    if (tall) {
+        if (a.fmt != 0 || msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        return a.mode == 1 ? launch_wide<1, 5, 4, 2>(a, st) : launch_wide<0, 5, 4, 2>(a, st);
+    }
     if (a.fmt == 1) {   // MXFP4 experts: 64-row tiles on the narrow kernel, 128-row on the wide one
         switch (msub) {
             case 2:

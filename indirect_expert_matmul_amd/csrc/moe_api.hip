@@ -662,6 +662,14 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
             q.ldo = d.n_embd;
             q.w_once = d.T <= bm;
         }
+        // segment-last tiles of up to 160 rows where both GEMMs (and the shared ones they
+        // launch with) run the wide kernel: the two share the row-id pass's tile table
+        int tx = gemm_tile_x(p.msub, g.fmt, d.n_embd);
+        if (gemm_tile_x(p.msub, g.fmt, d.n_ff) == 0 || (shared && gemm_tile_x(p.msub, g.fmt, d.n_ff_sh) == 0))
+            tx = 0;
+        ra.tile_x[0] = tx;
+        r.tile_x = tx;
+        r2.tile_x = tx;
         // x is gathered through the row map; h and the shared rows are read in order
         if ((s = check_gemm_limits(g, p.msub, d.T, d.n_embd, "gate/up"))) return s;
         if ((s = check_gemm_limits(g2, p.msub, 0, d.n_ff, "down"))) return s;
@@ -876,6 +884,8 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
+            r.tile_x = gemm_tile_x(p.msub, g.fmt, K);
+            ra.tile_x[0] = r.tile_x;
             if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
         }
         tm.begin();

@@ -72,6 +72,10 @@ struct RowIdsArgs {
     int32_t* inv;         // optional [n]: position of entry i in the sorted order
     int32_t* tile_off[2]; // optional [E + 1]: exclusive prefix of ceil(count_e / tile_m[i])
     int32_t tile_m[2];
+    // extra rows the last M tile of an expert may hold beyond tile_m (0, or 32 when the
+    // GEMM's tiles have room for tile_m + 32 rows): an expert with up to tile_m + 32 rows
+    // past its full tiles gets one tile fewer
+    int32_t tile_x[2];
     // optional, with tile_off[i]: per M tile j, {expert e owning it, tile_off[e],
     // bounds[e], rows of e}; tile_cap[i] entries of room (an upper bound on the count)
     int32_t* tile_tab[2];
@@ -107,6 +111,7 @@ struct GemmProblem {
     int32_t n_seg;
     int32_t seg_len;          // uniform segments
     int32_t m_tiles_max;      // grid upper bound on M tiles of this problem
+    int32_t tile_x;           // extra rows of a segment's last M tile (as RowIdsArgs::tile_x)
     const uint16_t* A;        // bf16 activations
     int64_t lda;
     // quantized-activation GEMM only: int8 activation codes [rows][K] and float32
@@ -136,6 +141,17 @@ struct GemmArgs {
 // Block tile height for a given average rows-per-expert (host heuristic).
 int gemm_pick_msub(double avg_rows);
 int gemm_tile_m(int msub);
+// Extra rows (0 or 32) the last M tile of an expert may hold on the GEMM path for this
+// tile choice, weight format and K: 32 where the 128-row wide kernel runs, whose
+// 160-row variant takes such tiles.
+int gemm_tile_x(int msub, int fmt, int64_t K);
+// M tiles of a segment of `rows` rows: tiles of tm rows, the last one holding up to
+// tm + tx (at least one tile for a non-empty segment).
+inline __host__ __device__ int tiles_of(int rows, int tm, int tx) {
+    if (rows <= 0) return 0;
+    const int t = (rows - tx + tm - 1) / tm;
+    return t > 1 ? t : 1;
+}
 hipError_t launch_gemm_q8(const GemmArgs& a, int msub, hipStream_t st);
 // Upper bound on the work-items launch_gemm_q8 would launch for these arguments (a
 // dispatch holds fewer than 2^32).

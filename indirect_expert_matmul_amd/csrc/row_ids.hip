@@ -222,9 +222,9 @@ __device__ void write_tile_tab(const RowIdsArgs& a, int q, const int32_t* bstart
 template <int NT = kThreads>
 __device__ void write_tiles(const RowIdsArgs& a, int q, const int32_t* bstart, int32_t* tmp, int32_t* wsum) {
     const int E = a.E, NB = E + 1;
-    const int tm = a.tile_m[q];
+    const int tm = a.tile_m[q], tx = a.tile_x[q];
     for (int b = threadIdx.x; b < NB; b += NT)
-        tmp[b] = b < E ? (bstart[b + 1] - bstart[b] + tm - 1) / tm : 0;
+        tmp[b] = b < E ? tiles_of(bstart[b + 1] - bstart[b], tm, tx) : 0;
     __syncthreads();
     block_scan<NT>(tmp, NB, wsum);
     for (int b = threadIdx.x; b < NB; b += NT) a.tile_off[q][b] = tmp[b];
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
     // wave 0 alone: exclusive scans of the bucket counts (into bucket starts and bounds)
     // and, for the first tile table, of the experts' M-tile counts, with shuffles and no
     // block barrier (two block-wide scans took about 2 us of the pass)
-    const int tm0 = a.tile_off[0] ? a.tile_m[0] : 0;
+    const int tm0 = a.tile_off[0] ? a.tile_m[0] : 0, tx0 = a.tile_x[0];
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const int per = (NB + 63) >> 6;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
         for (int b = b0; b < b1; b++) {
             const int32_t c = bstart[b];
             sc += c;
-            if (tm0 && b < a.E) stl += (c + tm0 - 1) / tm0;
+            if (tm0 && b < a.E) stl += tiles_of(c, tm0, tx0);
         }
         int32_t xc = sc, xt = stl;
 #pragma unroll
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
             if (tm0) {
                 tmp[b] = rt;
                 a.tile_off[0][b] = rt;
-                if (b < a.E) rt += (c + tm0 - 1) / tm0;
+                if (b < a.E) rt += tiles_of(c, tm0, tx0);
             }
         }
     }
