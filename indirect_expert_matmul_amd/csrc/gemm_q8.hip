@@ -598,9 +598,10 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     const GemmProblem& P = args.p[pi];
     const int N = P.N, K = P.K;
     const int n_nt = (N + NTW - 1) / NTW;
-    // tile stride TM: the 160-row form (MSUB = 5) runs 128-row tiles whose segment-last
-    // tile may hold up to tile_x = 32 rows more; the row-id pass counts tiles the same way
-    constexpr int TM = MSUB == 5 ? 128 : BM;
+    // tile height TM: the 160-row form (MSUB = 5) runs tiles of P.tile_m rows (128 or
+    // 160) whose segment-last tile may hold up to tile_x rows more (0 or 32; never past
+    // 160); the row-id pass counts tiles the same way
+    const int TM = MSUB == 5 ? (P.tile_m ? P.tile_m : 128) : BM;
     const int tx = MSUB == 5 ? P.tile_x : 0;
     int e, m0, m_len, nt;
     {
@@ -1063,6 +1064,15 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 int gemm_tile_x(int msub, int fmt, int64_t K) {
     return (MOE_GEMM_TALL_LAST && msub == 4 && fmt == 0 && K % wide::KS == 0) ? 32 : 0;
 }
+#ifndef MOE_GEMM_TILE160
+#define MOE_GEMM_TILE160 0   // 1: the 160-row kernel runs 160-row tiles instead of 128 + 32
+#endif
+void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q) {
+    p.tile_m = MOE_GEMM_TILE160 ? 160 : 128;
+    p.tile_x = MOE_GEMM_TILE160 ? 0 : 32;
+    r.tile_m[q] = p.tile_m;
+    r.tile_x[q] = p.tile_x;
+}
 
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     GemmArgs a = a0;
@@ -1076,8 +1086,11 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     // the tile tables were built for them, so any other choice is a caller error
     bool tall = false;
     for (int i = 0; i < a.n_prob; i++) {
-        if (a.p[i].tile_x != 0 && a.p[i].tile_x != 32) return hipErrorInvalidValue;
-        tall = tall || a.p[i].tile_x == 32;
+        const GemmProblem& p = a.p[i];
+        if ((p.tile_x != 0 && p.tile_x != 32) || (p.tile_m != 0 && p.tile_m != 128 && p.tile_m != 160) ||
+            (p.tile_m ? p.tile_m : 128) + p.tile_x > 160)
+            return hipErrorInvalidValue;
+        tall = tall || p.tile_x != 0 || p.tile_m == 160;
     }
     if (tall) {
         if (a.fmt != 0 || msub != 4 || !wide_ok) return hipErrorInvalidValue;

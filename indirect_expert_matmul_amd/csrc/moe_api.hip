@@ -667,9 +667,10 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         int tx = gemm_tile_x(p.msub, g.fmt, d.n_embd);
         if (gemm_tile_x(p.msub, g.fmt, d.n_ff) == 0 || (shared && gemm_tile_x(p.msub, g.fmt, d.n_ff_sh) == 0))
             tx = 0;
-        ra.tile_x[0] = tx;
-        r.tile_x = tx;
-        r2.tile_x = tx;
+        if (tx) {
+            gemm_set_tall(r, ra, 0);
+            gemm_set_tall(r2, ra, 0);
+        }
         // x is gathered through the row map; h and the shared rows are read in order
         if ((s = check_gemm_limits(g, p.msub, d.T, d.n_embd, "gate/up"))) return s;
         if ((s = check_gemm_limits(g2, p.msub, 0, d.n_ff, "down"))) return s;
@@ -884,8 +885,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
-            r.tile_x = gemm_tile_x(p.msub, g.fmt, K);
-            ra.tile_x[0] = r.tile_x;
+            if (gemm_tile_x(p.msub, g.fmt, K)) gemm_set_tall(r, ra, 0);
             if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
         }
         tm.begin();

@@ -112,6 +112,8 @@ struct GemmProblem {
     int32_t seg_len;          // uniform segments
     int32_t m_tiles_max;      // grid upper bound on M tiles of this problem
     int32_t tile_x;           // extra rows of a segment's last M tile (as RowIdsArgs::tile_x)
+    int32_t tile_m;           // 160-row wide kernel only: M-tile height (128 with tile_x = 32,
+                              // or 160); 0 elsewhere
     const uint16_t* A;        // bf16 activations
     int64_t lda;
     // quantized-activation GEMM only: int8 activation codes [rows][K] and float32
@@ -145,6 +147,8 @@ int gemm_tile_m(int msub);
 // tile choice, weight format and K: 32 where the 128-row wide kernel runs, whose
 // 160-row variant takes such tiles.
 int gemm_tile_x(int msub, int fmt, int64_t K);
+// Puts routed problem p and tile table q of the row-id pass on the 160-row kernel's tiles.
+void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q);
 // M tiles of a segment of `rows` rows: tiles of tm rows, the last one holding up to
 // tm + tx (at least one tile for a non-empty segment).
 inline __host__ __device__ int tiles_of(int rows, int tm, int tx) {
