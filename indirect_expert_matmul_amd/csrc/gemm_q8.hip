@@ -1061,8 +1061,9 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 #ifndef MOE_GEMM_TALL_LAST
 #define MOE_GEMM_TALL_LAST 1   // 0: 128-row tiles only (no 160-row segment-last tiles)
 #endif
-int gemm_tile_x(int msub, int fmt, int64_t K) {
-    return (MOE_GEMM_TALL_LAST && msub == 4 && fmt == 0 && K % wide::KS == 0) ? 32 : 0;
+int gemm_tile_x(int msub, int fmt, int64_t K, bool fp4_scales_even) {
+    // MXFP4 takes the wide kernel only with its scale rows at even addresses
+    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && (fmt == 0 || fp4_scales_even)) ? 32 : 0;
 }
 #ifndef MOE_GEMM_TILE160
 #define MOE_GEMM_TILE160 0   // 1: the 160-row kernel runs 160-row tiles instead of 128 + 32
@@ -1093,7 +1094,13 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
         tall = tall || p.tile_x != 0 || p.tile_m == 160;
     }
     if (tall) {
-        if (a.fmt != 0 || msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        if (msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        if (a.fmt == 1) {
+            for (int i = 0; i < a.n_prob; i++)
+                if (((uintptr_t)a.p[i].d1 & 1) || (a.mode == 1 && ((uintptr_t)a.p[i].d2 & 1)))
+                    return hipErrorInvalidValue;
+            return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2>(a, st);
+        }
         return a.mode == 1 ? launch_wide<1, 5, 4, 2>(a, st) : launch_wide<0, 5, 4, 2>(a, st);
     }
     if (a.fmt == 1) {   // MXFP4 experts: 64-row tiles on the narrow kernel, 128-row on the wide one

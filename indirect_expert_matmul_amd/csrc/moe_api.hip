@@ -664,8 +664,12 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         }
         // segment-last tiles of up to 160 rows where both GEMMs (and the shared ones they
         // launch with) run the wide kernel: the two share the row-id pass's tile table
-        int tx = gemm_tile_x(p.msub, g.fmt, d.n_embd);
-        if (gemm_tile_x(p.msub, g.fmt, d.n_ff) == 0 || (shared && gemm_tile_x(p.msub, g.fmt, d.n_ff_sh) == 0))
+        bool even = true;   // MXFP4: every scale tensor at an even address
+        for (const moe_weights* w : {gate, up, down, sh_gate, sh_up, sh_down})
+            if (w && ((uintptr_t)w->scales & 1)) even = false;
+        int tx = gemm_tile_x(p.msub, g.fmt, d.n_embd, even);
+        if (gemm_tile_x(p.msub, g.fmt, d.n_ff, even) == 0 ||
+            (shared && gemm_tile_x(p.msub, g.fmt, d.n_ff_sh, even) == 0))
             tx = 0;
         if (tx) {
             gemm_set_tall(r, ra, 0);
@@ -885,7 +889,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
-            if (gemm_tile_x(p.msub, g.fmt, K)) gemm_set_tall(r, ra, 0);
+            if (gemm_tile_x(p.msub, g.fmt, K, ((uintptr_t)w->scales & 1) == 0)) gemm_set_tall(r, ra, 0);
             if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
         }
         tm.begin();

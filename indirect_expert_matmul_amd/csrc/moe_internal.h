@@ -145,8 +145,9 @@ int gemm_pick_msub(double avg_rows);
 int gemm_tile_m(int msub);
 // Extra rows (0 or 32) the last M tile of an expert may hold on the GEMM path for this
 // tile choice, weight format and K: 32 where the 128-row wide kernel runs, whose
-// 160-row variant takes such tiles.
-int gemm_tile_x(int msub, int fmt, int64_t K);
+// 160-row variant takes such tiles (MXFP4: when every scale tensor of the launch
+// starts at an even address).
+int gemm_tile_x(int msub, int fmt, int64_t K, bool fp4_scales_even);
 // Puts routed problem p and tile table q of the row-id pass on the 160-row kernel's tiles.
 void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q);
 // M tiles of a segment of `rows` rows: tiles of tm rows, the last one holding up to
