@@ -115,6 +115,53 @@ def test_q8_mul_mat_id_many_chunks():
     assert normwise(got.cpu().numpy(), ref) <= TOL_MFMA
 
 
+# Segment lengths around the 128-row tile and its last-tile allowance of 32 more rows
+# (128-row tiles, the last one holding up to 160): 160 rows make one tile, 161 two,
+# 288 two, 289 three. One expert per length, in a seeded token order, k = 1.
+_SEG_ROWS = [0, 1, 31, 32, 33, 127, 128, 129, 159, 160, 161, 255, 256, 257, 287, 288, 289, 416]
+
+
+def _ids_with_segments(seed):
+    ids = np.repeat(np.arange(len(_SEG_ROWS), dtype=np.int32), _SEG_ROWS)
+    np.random.default_rng(seed).shuffle(ids)
+    return ids.reshape(-1, 1)
+
+
+@pytest.mark.parametrize("wtype,K,N", [("q8_0", 256, 200), ("q8_0", 192, 72), ("mxfp4", 256, 200)])
+def test_mul_mat_id_segment_lengths_at_tile_edges(wtype, K, N):
+    ids = _ids_with_segments(41)
+    E, T = len(_SEG_ROWS), ids.shape[0]
+    inp = synth.make_custom_mmid(43, E, 1, T, K, N, wtype=wtype, ids=ids)
+    x = synth.f32_to_bf16_bits(np.random.default_rng(47).standard_normal((T, K)).astype(np.float32))
+    w = moe.weights_from_numpy(inp["w_qs"], inp["w_d"])
+    got = moe.moe_mul_mat_id(w, dev_bf16(x), dev_i32(ids), route_w=dev_f32(inp["route_w"]),
+                             path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    ref = oracle.mul_mat_id(inp["w_qs"], inp["w_d"], x, "bf16", ids, inp["route_w"], 1)
+    g = got.cpu().numpy()
+    assert normwise(g, ref) <= TOL_MFMA
+    # every segment, the last tile's rows included, on its own
+    for e in range(E):
+        sel = ids[:, 0] == e
+        if sel.any():
+            assert normwise(g[sel], ref[sel]) <= TOL_MFMA, e
+
+
+@pytest.mark.parametrize("wtype", ["q8_0", "mxfp4"])
+def test_ffn_segment_lengths_at_tile_edges(wtype):
+    ids = _ids_with_segments(53)
+    E, T = len(_SEG_ROWS), ids.shape[0]
+    inp = synth.make_custom_ffn(59, E, 1, T, 256, 192, 1, ids=ids, wtype=wtype)
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMM)
+    torch.cuda.synchronize()
+    g, ref = got.cpu().numpy(), oracle.ffn(inp)
+    assert normwise(g, ref) <= TOL_MFMA
+    for e in range(E):
+        sel = ids[:, 0] == e
+        if sel.any():
+            assert normwise(g[sel], ref[sel]) <= TOL_MFMA, e
+
+
 # ------------------------------------------------------------------------- FFN
 
 @pytest.mark.parametrize("path", [moe.PATH_GEMM, moe.PATH_GEMV])
