@@ -38,7 +38,10 @@ namespace {
 #define MOE_ROWIDS_MAXB 32       // batches of 64 per wave per chunk, at most
 #endif
 #ifndef MOE_ROWIDS_PRE
-#define MOE_ROWIDS_PRE 8         // batches of ids loaded ahead of their use
+#define MOE_ROWIDS_PRE 8         // batches of ids loaded ahead of their use (one-workgroup pass)
+#endif
+#ifndef MOE_ROWIDS_COUNT_PRE
+#define MOE_ROWIDS_COUNT_PRE 4   // batches per group in the count pass (two groups in flight)
 #endif
 
 constexpr int kWaves = 8;
@@ -83,20 +86,22 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 }
 
 constexpr int kPre = MOE_ROWIDS_PRE;  // batches of ids loaded ahead of their use
+constexpr int kCountPre = MOE_ROWIDS_COUNT_PRE;
 
-// Loads of batches [bb, bb + kPre*64): one id per lane per batch, -1 past the end.
+// Loads of batches [bb, bb + NP*64): one id per lane per batch, -1 past the end.
 // Only batches that start before the end are loaded (a wave-uniform test), and in the
 // last one every lane loads (past the end it re-reads entry end-1), so all the loads
 // are in flight before the first result is used; a load under a lane condition would
 // be waited for inside its branch, one round trip per batch.
+template <int NP>
 __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, int64_t bb,
-                                             int64_t end, int32_t E, int (&b)[kPre]) {
+                                             int64_t end, int32_t E, int (&b)[NP]) {
     const int lane = threadIdx.x & 63;
-    int32_t raw[kPre];
+    int32_t raw[NP];
 #pragma unroll
-    for (int q = 0; q < kPre; q++) raw[q] = bb + q * 64 < end ? ids[min(bb + q * 64 + lane, end - 1)] : 0;
+    for (int q = 0; q < NP; q++) raw[q] = bb + q * 64 < end ? ids[min(bb + q * 64 + lane, end - 1)] : 0;
 #pragma unroll
-    for (int q = 0; q < kPre; q++) b[q] = bb + q * 64 + lane < end ? bucket_of(raw[q], E) : -1;
+    for (int q = 0; q < NP; q++) b[q] = bb + q * 64 + lane < end ? bucket_of(raw[q], E) : -1;
 }
 
 // Histogram of the loaded batches starting at entry b0 (entries from `end` on are
@@ -147,26 +152,6 @@ __device__ __forceinline__ void place_batches(const RowIdsArgs& a, const int (&b
         __builtin_amdgcn_wave_barrier();
         if (act && lane == __ffsll((unsigned long long)m) - 1) run_w[b] = prev + __popcll(m);
         __builtin_amdgcn_wave_barrier();
-    }
-}
-
-// Histogram of entries [beg, end) into this wave's counter row.
-__device__ void wave_count(const int32_t* __restrict__ ids, int64_t beg, int64_t end, int32_t E,
-                           int nbits, int32_t* cnt_w) {
-    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
-        int bk[kPre];
-        load_batches(ids, b0, end, E, bk);
-        count_batches(bk, b0, end, nbits, cnt_w);
-    }
-}
-
-// Places entries [beg, end).
-__device__ void wave_place(const RowIdsArgs& a, int64_t beg, int64_t end, int nbits,
-                           const int32_t* base, int32_t* run_w) {
-    for (int64_t b0 = beg; b0 < end; b0 += kPre * 64) {
-        int bk[kPre];
-        load_batches(a.ids, b0, end, a.E, bk);
-        place_batches(a, bk, b0, end, nbits, base, run_w);
     }
 }
 
@@ -337,8 +322,9 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
 // gets its rank among the wave's earlier entries of the same bucket (stored as 16 bits:
 // a wave's range is at most kMaxBatchesPerWave * 64 entries). The wave's counts go to
 // wcnt (chunk-major) for the place pass, the chunk's totals to chunk_cnt (bucket-major)
-// for the scan over chunks.
-__global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
+// for the scan over chunks. Registers are held to 64 per lane so that four blocks (eight
+// waves per SIMD) fit a CU: 1024 chunks then run in one round instead of one and a third.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void k_row_ids_count(RowIdsArgs a) {
     // LDS, sized for this launch: per wave, a group mask per bucket [kWaves][NB] and the
     // running count per bucket [kWaves][NB]
     extern __shared__ __attribute__((aligned(16))) uint64_t count_lds[];
@@ -353,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
     const int64_t per = a.chunk / kWaves;
     const int64_t beg = min(c0 + w * per, a.n), end = min(beg + per, a.n);
     int32_t* run_w = cnt + w * NB;
-    // Ranks one group of kPre batches starting at entry b0 (ids past the range are -1),
+    // Ranks one group of kCountPre batches starting at entry b0 (ids past the range are -1),
     // in three phases whose LDS instructions are issued back to back, batch after
     // batch, with one wait per phase (a wave's LDS instructions execute in order):
     //   masks: the lanes of batch q holding bucket b each clear b's mask word, then OR
@@ -364,10 +350,10 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
     //     and gets the counter's previous value; the batches' adds to one counter run in
     //     batch order, and within a batch every counter has one adder;
     //   ranks: each lane takes that previous value from its group's lowest lane.
-    auto rank_group = [&](const int (&bk)[kPre], int64_t b0) {
-        uint64_t m[kPre];
+    auto rank_group = [&](const int (&bk)[kCountPre], int64_t b0) {
+        uint64_t m[kCountPre];
 #pragma unroll
-        for (int q = 0; q < kPre; q++) {
+        for (int q = 0; q < kCountPre; q++) {
             m[q] = 0;
             if (bk[q] >= 0) {
                 msk_w[bk[q]] = 0;
@@ -375,25 +361,25 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_count(RowIdsArgs a) {
                 m[q] = __hip_atomic_load(msk_w + bk[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
-        int32_t prev[kPre];
+        int32_t prev[kCountPre];
 #pragma unroll
-        for (int q = 0; q < kPre; q++) {
+        for (int q = 0; q < kCountPre; q++) {
             prev[q] = 0;
             if (bk[q] >= 0 && rank_below(m[q]) == 0)
                 prev[q] = __hip_atomic_fetch_add(run_w + bk[q], __popcll(m[q]), __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        int32_t base[kPre];
+        int32_t base[kCountPre];
 #pragma unroll
-        for (int q = 0; q < kPre; q++)
+        for (int q = 0; q < kCountPre; q++)
             base[q] = __shfl(prev[q], bk[q] >= 0 ? __ffsll((unsigned long long)m[q]) - 1 : lane);
 #pragma unroll
-        for (int q = 0; q < kPre; q++)
+        for (int q = 0; q < kCountPre; q++)
             if (bk[q] >= 0) a.rank16[b0 + q * 64 + lane] = (uint16_t)(base[q] + rank_below(m[q]));
     };
     // two groups of batches in registers: the next group loads while this one is ranked
-    constexpr int64_t G = kPre * 64;
-    int bk0[kPre], bk1[kPre];
+    constexpr int64_t G = kCountPre * 64;
+    int bk0[kCountPre], bk1[kCountPre];
     if (beg < end) load_batches(a.ids, beg, end, a.E, bk0);
     for (int64_t b0 = beg; b0 < end; b0 += 2 * G) {
         if (b0 + G < end) load_batches(a.ids, b0 + G, end, a.E, bk1);
