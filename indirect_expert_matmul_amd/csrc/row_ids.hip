@@ -496,12 +496,38 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     }
     __syncthreads();
     const int32_t chunk_n = block_scan(cstart, NB, wsum);
-    const int64_t cn = min(a.chunk, a.n - c0);
-    for (int64_t e = tid; e < cn; e += kThreads) {
-        const int b = bucket_of(a.ids[c0 + e], a.E);
-        const int v = (int)(e / per);
-        const int32_t lp = cstart[b] + woff[v * NB + b] + a.rank16[c0 + e];
-        st[lp] = ((uint32_t)b << 16) | (uint32_t)e;
+    // Each wave puts the range the count pass ranked with it (so its offsets are one row
+    // of woff) in bucket order, kPre batches of ids and ranks loaded together: unclamped
+    // per-lane loads would be waited for one batch at a time.
+    {
+        const int w = tid >> 6, lane = tid & 63;
+        const int32_t cn = (int32_t)min(a.chunk, a.n - c0);   // chunk-relative, < 2^16
+        const int32_t wbeg = min(w * (int32_t)per, cn), wend = min(wbeg + (int32_t)per, cn);
+        const int32_t* idc = a.ids + c0;
+        const uint16_t* rkc = a.rank16 + c0;
+        const int32_t* wo = woff + w * NB;
+        for (int32_t e0 = wbeg; e0 < wend; e0 += kPre * 64) {
+            int32_t id[kPre];
+            uint32_t rk[kPre];
+#pragma unroll
+            for (int q = 0; q < kPre; q++) {
+                id[q] = 0;
+                rk[q] = 0;
+                if (e0 + q * 64 < wend) {   // uniform; past the end a lane re-reads entry wend-1
+                    const int32_t e = min(e0 + q * 64 + lane, wend - 1);
+                    id[q] = idc[e];
+                    rk[q] = rkc[e];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kPre; q++) {
+                const int32_t e = e0 + q * 64 + lane;
+                if (e < wend) {
+                    const int b = bucket_of(id[q], a.E);
+                    st[cstart[b] + wo[b] + (int32_t)rk[q]] = ((uint32_t)b << 16) | (uint32_t)e;
+                }
+            }
+        }
     }
     __syncthreads();
     for (int32_t p = tid; p < chunk_n; p += kThreads) {
