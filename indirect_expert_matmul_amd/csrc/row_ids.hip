@@ -88,11 +88,30 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 constexpr int kPre = MOE_ROWIDS_PRE;  // batches of ids loaded ahead of their use
 constexpr int kCountPre = MOE_ROWIDS_COUNT_PRE;
 
-// Loads of batches [bb, bb + NP*64): one id per lane per batch, -1 past the end.
-// Only batches that start before the end are loaded (a wave-uniform test), and in the
-// last one every lane loads (past the end it re-reads entry end-1), so all the loads
-// are in flight before the first result is used; a load under a lane condition would
-// be waited for inside its branch, one round trip per batch.
+// load_raw only issues the loads, every lane of every batch (past the end a lane
+// re-reads entry end-1; the caller guarantees bb < end), so that no value is merged
+// with a default and nothing waits for them until their group is ranked; to_buckets
+// turns them into buckets.
+template <int NP>
+__device__ __forceinline__ void load_raw(const int32_t* __restrict__ ids, int64_t bb, int64_t end,
+                                         int32_t (&raw)[NP]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < NP; q++) raw[q] = ids[min(bb + q * 64 + lane, end - 1)];
+}
+template <int NP>
+__device__ __forceinline__ void to_buckets(const int32_t (&raw)[NP], int64_t bb, int64_t end, int32_t E,
+                                           int (&b)[NP]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < NP; q++) b[q] = bb + q * 64 + lane < end ? bucket_of(raw[q], E) : -1;
+}
+// Loads of batches [bb, bb + NP*64) as buckets: one per lane per batch, -1 past the end.
+// Only batches that start before the end are loaded (a wave-uniform test, so a wave
+// with an empty range loads nothing), and in the last one every lane loads (past the
+// end it re-reads entry end-1), so all the loads are in flight before the first
+// result is used; a load under a lane condition would be waited for inside its
+// branch, one round trip per batch.
 template <int NP>
 __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, int64_t bb,
                                              int64_t end, int32_t E, int (&b)[NP]) {
@@ -100,8 +119,7 @@ __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, in
     int32_t raw[NP];
 #pragma unroll
     for (int q = 0; q < NP; q++) raw[q] = bb + q * 64 < end ? ids[min(bb + q * 64 + lane, end - 1)] : 0;
-#pragma unroll
-    for (int q = 0; q < NP; q++) b[q] = bb + q * 64 + lane < end ? bucket_of(raw[q], E) : -1;
+    to_buckets(raw, bb, end, E, b);
 }
 
 // Histogram of the loaded batches starting at entry b0 (entries from `end` on are
@@ -350,7 +368,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
     //     and gets the counter's previous value; the batches' adds to one counter run in
     //     batch order, and within a batch every counter has one adder;
     //   ranks: each lane takes that previous value from its group's lowest lane.
-    auto rank_group = [&](const int (&bk)[kCountPre], int64_t b0) {
+    auto rank_group = [&](const int32_t (&raw)[kCountPre], int64_t b0) {
+        int bk[kCountPre];
+        to_buckets(raw, b0, end, a.E, bk);
         uint64_t m[kCountPre];
 #pragma unroll
         for (int q = 0; q < kCountPre; q++) {
@@ -377,16 +397,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         for (int q = 0; q < kCountPre; q++)
             if (bk[q] >= 0) a.rank16[b0 + q * 64 + lane] = (uint16_t)(base[q] + rank_below(m[q]));
     };
-    // two groups of batches in registers: the next group loads while this one is ranked
+    // two groups of batches in registers: the next group's ids load while this one is
+    // ranked (they are turned into buckets only when their group is ranked). The loads
+    // are issued without a condition (a group past the end re-reads entry end-1): a
+    // path that skipped them would make the compiler wait for every load in flight
+    // where the paths join.
     constexpr int64_t G = kCountPre * 64;
-    int bk0[kCountPre], bk1[kCountPre];
-    if (beg < end) load_batches(a.ids, beg, end, a.E, bk0);
-    for (int64_t b0 = beg; b0 < end; b0 += 2 * G) {
-        if (b0 + G < end) load_batches(a.ids, b0 + G, end, a.E, bk1);
-        rank_group(bk0, b0);
-        if (b0 + G >= end) break;
-        if (b0 + 2 * G < end) load_batches(a.ids, b0 + 2 * G, end, a.E, bk0);
-        rank_group(bk1, b0 + G);
+    if (beg < end) {   // uniform
+        int32_t r0[kCountPre], r1[kCountPre];
+        load_raw(a.ids, beg, end, r0);
+        for (int64_t b0 = beg; b0 < end; b0 += 2 * G) {
+            load_raw(a.ids, b0 + G, end, r1);
+            rank_group(r0, b0);
+            if (b0 + G >= end) break;
+            load_raw(a.ids, b0 + 2 * G, end, r0);
+            rank_group(r1, b0 + G);
+        }
     }
     __syncthreads();
     int32_t* wc = a.wcnt + (int64_t)blockIdx.x * kWaves * NB;
