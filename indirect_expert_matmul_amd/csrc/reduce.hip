@@ -45,6 +45,20 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
         f32x4 v[kU];
         float w[kU];
         bool okv[kU];
+        // Every slot row of the batch is loaded at once, whatever its id (rows past k
+        // re-read slot k-1, rows of invalid ids are read and not used): the loads do not
+        // wait for the ids, and no load sits under a condition whose join would make the
+        // compiler wait for it there.
+#pragma unroll
+        for (int u = 0; u < kU; u++) {
+            const int s = min(s0 + u, a.k - 1);
+            const float* y = a.y + (tk + s) * a.N + c;
+            if (VEC) {
+                v[u] = __builtin_nontemporal_load((const f32x4*)y);
+            } else {
+                for (int q = 0; q < 4; q++) v[u][q] = y[min(q, a.N - 1 - c)];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kU; u++) {
             const int s = s0 + u;
@@ -52,12 +66,6 @@ __global__ __launch_bounds__(kThreads) void k_reduce_weighted(ReduceArgs a) {
             const bool ok = e >= 0 && e < a.E;
             okv[u] = ok;
             w[u] = ok ? (a.route_w ? a.route_w[tk + s] : 1.0f) : 0.f;
-            const float* y = a.y + (tk + (ok ? s : 0)) * a.N + c;
-            if (VEC) {
-                v[u] = ok ? __builtin_nontemporal_load((const f32x4*)y) : f32x4{0.f, 0.f, 0.f, 0.f};
-            } else {
-                for (int q = 0; q < 4; q++) v[u][q] = (ok && c + q < a.N) ? y[q] : 0.f;
-            }
         }
 #pragma unroll
         for (int u = 0; u < kU; u++) {
