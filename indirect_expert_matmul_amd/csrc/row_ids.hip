@@ -473,9 +473,9 @@ template <bool LOCAL>
 __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     __shared__ int32_t wsum[kWaves];
     // LDS, sized for this launch: per-wave offsets [kWaves][NB], bucket starts inside the
-    // chunk [NB + 1], global start of each bucket's run [NB], and the chunk in bucket
-    // order: bucket << 16 | index in the chunk [chunk], the bucket starts [NB + 1] and a
-    // tile-count scratch [NB + 1]
+    // chunk [NB + 1], global start of each bucket's run [NB] (then output position minus
+    // position in the chunk), and the chunk in bucket order: bucket << 16 | index in the
+    // chunk [chunk], the bucket starts [NB + 1] and a tile-count scratch [NB + 1]
     extern __shared__ __attribute__((aligned(16))) int32_t lds[];
     const int NB = a.E + 1;
     int32_t* woff = lds;
@@ -522,6 +522,8 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     }
     __syncthreads();
     const int32_t chunk_n = block_scan(cstart, NB, wsum);
+    // gbase becomes the offset from a position in the chunk to its output position
+    for (int b = tid; b < NB; b += kThreads) gbase[b] -= cstart[b];
     // Each wave puts the range the count pass ranked with it (so its offsets are one row
     // of woff) in bucket order, kPre batches of ids and ranks loaded together: unclamped
     // per-lane loads would be waited for one batch at a time.
@@ -559,7 +561,7 @@ __global__ __launch_bounds__(kThreads) void k_row_ids_place(RowIdsArgs a) {
     for (int32_t p = tid; p < chunk_n; p += kThreads) {
         const uint32_t v = st[p];
         const int b = (int)(v >> 16);
-        const int32_t g = gbase[b] + p - cstart[b];
+        const int32_t g = gbase[b] + p;
         const uint32_t ii = (uint32_t)(c0 + (v & 0xffffu));   // n < 2^31 is a validated limit
         const uint32_t t = (uint32_t)(((uint64_t)ii * a.k_magic) >> a.k_shift);   // ii / k
         // src1 row t*B + s % B: ii itself when B = k, t when B = 1 (no division)
