@@ -355,17 +355,27 @@ def prepare_ffn_workload(args, name):
             "x": x, "ids": ids, "rw": rw, "out": out, "ws": ws, "stream": stream, "step": step}
 
 
+def make_stage_events(W, steps):
+    """The HIP events of a workload's per-stage pass (made before any timing starts)."""
+    W["evs"] = [[KernelEvent() for _ in range(2 * len(STAGES[W["path"]]))] for _ in range(steps)]
+
+
 def time_ffn_workload(args, W, steps, warmup):
     """Time a prepared FFN workload: warm-up, then `steps` timed steps (each one full
     layer call), then one pass with per-kernel HIP events recorded by the library on
-    the stream its kernels run on. Returns the measurements as a dict."""
+    the stream its kernels run on. Only GPU work and its launches happen here (the
+    events come from make_stage_events); finish_ffn_workload turns the result into
+    measurements once all GPU timing is done, so the GPU does not idle between
+    workloads."""
     import torch
     import indirect_expert_matmul_amd as moe
 
     name, cfg, inp, st, path, R, sets = (W[n] for n in ("name", "cfg", "inp", "st", "path", "R", "sets"))
     x, ids, rw, out, ws, stream, step = (W[n] for n in ("x", "ids", "rw", "out", "ws", "stream", "step"))
-    T = inp["ids"].shape[0]
     aq = args.act_quant
+    names = STAGES[path]
+    evs = W["evs"]
+    assert len(evs) == steps
     warmup = warm_up(step, warmup)
     run = step
     if args.graph:
@@ -394,15 +404,20 @@ def time_ffn_workload(args, W, steps, warmup):
 
     # per-kernel durations: HIP events recorded by the library around each stage, on
     # the stream the kernels run on
-    names = STAGES[path]
-    evs = [[KernelEvent() for _ in range(2 * len(names))] for _ in range(steps)]
-    torch.cuda.synchronize()
     for i in range(steps):
         step(i, events=[e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
     if moe.last_stage_count() < len(names):
         # small decode batches: the down GEMV does the weighted reduce itself
         names = names[:1] + ["gemv_down_reduce"]
+    return {"W": W, "steps": steps, "warmup": warmup, "ms": ms, "evs": evs, "names": names}
+
+
+def finish_ffn_workload(raw):
+    """Measurements of a timed FFN workload (see time_ffn_workload) as a dict."""
+    W, steps, warmup, ms, evs, names = (raw[n] for n in ("W", "steps", "warmup", "ms", "evs", "names"))
+    name, cfg, inp, st, path, R, stream = (W[n] for n in ("name", "cfg", "inp", "st", "path", "R", "stream"))
+    T = inp["ids"].shape[0]
     stage_ms = {n: float(np.mean([evs[i][2 * j].elapsed_time(evs[i][2 * j + 1])
                                   for i in range(steps)])) for j, n in enumerate(names)}
     dom = max(stage_ms, key=stage_ms.get)
@@ -529,12 +544,17 @@ def main():
     names = [n for n in (args.extra.split(",") if args.extra else []) if n and n != args.config]
     prep = {n: prepare_ffn_workload(args, n) for n in names + [args.config]}
     routers = {n: time_router(prep[n]["cfg"], stream) for n in [args.config] + names}
+    steps = {n: max(10, args.steps // 2) if n in ("skew", "v3") else args.steps for n in names}
+    steps[args.config] = args.steps
+    for n in steps:
+        make_stage_events(prep[n], steps[n])
+    raw = {n: time_ffn_workload(args, prep[n], steps[n], args.warmup) for n in names}
+    r = finish_ffn_workload(time_ffn_workload(args, prep[args.config], steps[args.config], args.warmup))
     extras = {}
     for n in names:
-        extras[n] = time_ffn_workload(args, prep[n], max(10, args.steps // 2) if n in ("skew", "v3")
-                                      else args.steps, args.warmup)
+        extras[n] = finish_ffn_workload(raw[n])
         extras[n]["router"] = routers[n]
-    r = time_ffn_workload(args, prep[args.config], args.steps, args.warmup)
+    del raw
     router = routers[args.config]
     del prep
     torch.cuda.empty_cache()
