@@ -45,8 +45,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=None,
-                   help="untimed warm-up steps (default: at least 20 steps and 0.2 s of them, "
-                        "so the GPU clocks have ramped up; the count is reported)")
+                   help="untimed warm-up steps of the headline workload (default: at least 20 "
+                        "steps and 0.2 s of them, so the GPU clocks have ramped up; the count is "
+                        "reported). The further workloads (--extra) always warm up that long.")
     p.add_argument("--config", default="lite")
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
@@ -539,8 +540,10 @@ def main():
     # to back: the routers, the further workloads of the metric (PP4096 prefill, decode
     # batches of 1 and 8; each with its own dominant-kernel roofline), and the headline
     # workload last. From idle or light load the GPU clocks take about 10 ms to ramp up,
-    # longer than a few warm-up steps of a 0.2 ms layer; timed last, the headline's
-    # warm-up starts from a GPU under load.
+    # longer than a few warm-up steps of a 0.2 ms layer. The further workloads each warm
+    # up for at least 20 steps and 0.2 s whatever --warmup says, so their figures are
+    # steady-state ones; the headline runs exactly --warmup untimed steps, and timed
+    # last, its warm-up starts from a GPU under load.
     names = [n for n in (args.extra.split(",") if args.extra else []) if n and n != args.config]
     prep = {n: prepare_ffn_workload(args, n) for n in names + [args.config]}
     routers = {n: time_router(prep[n]["cfg"], stream) for n in [args.config] + names}
@@ -548,7 +551,7 @@ def main():
     steps[args.config] = args.steps
     for n in steps:
         make_stage_events(prep[n], steps[n])
-    raw = {n: time_ffn_workload(args, prep[n], steps[n], args.warmup) for n in names}
+    raw = {n: time_ffn_workload(args, prep[n], steps[n], None) for n in names}
     r = finish_ffn_workload(time_ffn_workload(args, prep[args.config], steps[args.config], args.warmup))
     extras = {}
     for n in names:
