@@ -7,10 +7,10 @@
 //
 // gfx950 design: a stable counting sort built from wavefront primitives.
 //   * Each wave owns a contiguous range of entries (t*k + s order) and walks it 64
-//     at a time. Lanes holding the same bucket find each other -- in the one-workgroup
-//     pass with one ballot per bit of the bucket id, in the multi-block count pass
-//     through a per-bucket 64-bit mask in LDS that every lane of the group ORs its
-//     bit into (OR is order-independent, so the mask is the same on every run) --;
+//     at a time. Lanes holding the same bucket find each other through a per-bucket
+//     64-bit mask in LDS that every lane of the group ORs its bit into (OR is
+//     order-independent, so the mask is the same on every run; the one-workgroup pass
+//     with more than 512 buckets uses one ballot per bit of the bucket id instead);
 //     the group's lowest lane adds the group size to the wave's LDS counter (one
 //     writer per counter, no atomic counter), and a lane's rank inside its group is a
 //     masked bit count (mbcnt).
@@ -85,6 +85,21 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// The same lane set through this wave's LDS mask words (one per bucket): each active
+// lane clears its bucket's word, ORs its own bit into it and reads it back. A wave's
+// LDS instructions execute in order (every clear before any OR, every OR before any
+// read) and OR does not depend on the order of the lanes, so the mask is exact and the
+// same on every run. Three LDS instructions instead of one ballot per bucket-id bit.
+__device__ __forceinline__ uint64_t match_bucket_lds(int b, bool act, uint64_t* msk_w) {
+    uint64_t m = 0;
+    if (act) {
+        msk_w[b] = 0;
+        __hip_atomic_fetch_or(msk_w + b, 1ull << (threadIdx.x & 63), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        m = __hip_atomic_load(msk_w + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    return m;
+}
+
 constexpr int kPre = MOE_ROWIDS_PRE;  // batches of ids loaded ahead of their use
 constexpr int kCountPre = MOE_ROWIDS_COUNT_PRE;
 
@@ -124,16 +139,17 @@ __device__ __forceinline__ void load_batches(const int32_t* __restrict__ ids, in
 
 // Histogram of the loaded batches starting at entry b0 (entries from `end` on are
 // skipped) into this wave's counter row. No atomics: each bucket present in a batch
-// has exactly one leader lane.
+// has exactly one leader lane. Lanes of a bucket are found through this wave's LDS mask
+// words when msk_w is given, otherwise with ballots.
 __device__ __forceinline__ void count_batches(const int (&bk)[kPre], int64_t b0, int64_t end, int nbits,
-                                              int32_t* cnt_w) {
+                                              int32_t* cnt_w, uint64_t* msk_w) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < kPre; q++) {
         if (b0 + q * 64 >= end) break;  // uniform
         const bool act = bk[q] >= 0;
         const int b = act ? bk[q] : 0;
-        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        const uint64_t m = msk_w ? match_bucket_lds(b, act, msk_w) : match_bucket(b, __ballot(act), nbits);
         if (act && lane == __ffsll((unsigned long long)m) - 1) cnt_w[b] += __popcll(m);
     }
 }
@@ -141,7 +157,8 @@ __device__ __forceinline__ void count_batches(const int (&bk)[kPre], int64_t b0,
 // Places the loaded batches starting at entry b0: position = base[b] + running[b] +
 // rank in batch.
 __device__ __forceinline__ void place_batches(const RowIdsArgs& a, const int (&bk)[kPre], int64_t b0,
-                                              int64_t end, int nbits, const int32_t* base, int32_t* run_w) {
+                                              int64_t end, int nbits, const int32_t* base, int32_t* run_w,
+                                              uint64_t* msk_w) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int q = 0; q < kPre; q++) {
@@ -150,7 +167,7 @@ __device__ __forceinline__ void place_batches(const RowIdsArgs& a, const int (&b
         const int64_t i = bb + lane;
         const bool act = bk[q] >= 0;
         const int b = act ? bk[q] : 0;
-        const uint64_t m = match_bucket(b, __ballot(act), nbits);
+        const uint64_t m = msk_w ? match_bucket_lds(b, act, msk_w) : match_bucket(b, __ballot(act), nbits);
         int32_t prev = 0;
         if (act) {
             prev = run_w[b];
@@ -254,16 +271,25 @@ constexpr int kSingleWaves = 16;
 static_assert(kRowIdsOneBlockMax <= (int64_t)kSingleWaves * 64 * kPre,
               "the one-workgroup pass keeps each wave's ids in kPre registers");
 
-// LDS of the one-workgroup pass: per-wave counters [kSingleWaves][NB], then bucket
-// starts [NB + 1] and tile counts [NB + 1].
-size_t single_lds_bytes(int NB) { return ((size_t)kSingleWaves * NB + 2 * ((size_t)NB + 1)) * sizeof(int32_t); }
+// LDS of the one-workgroup pass: with MASK, per-wave group mask words [kSingleWaves][NB]
+// (64-bit) first; then per-wave counters [kSingleWaves][NB], bucket starts [NB + 1] and
+// tile counts [NB + 1].
+size_t single_lds_bytes(int NB, bool mask) {
+    return (mask ? (size_t)kSingleWaves * NB * sizeof(uint64_t) : 0) +
+           ((size_t)kSingleWaves * NB + 2 * ((size_t)NB + 1)) * sizeof(int32_t);
+}
+// The mask words are used up to this many buckets (about 100 KB of LDS); beyond, the
+// lanes of a bucket are found with one ballot per bit of the bucket id.
+constexpr int kSingleMaskBuckets = 512;
 
+template <bool MASK>
 __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs a) {
     constexpr int NW = kSingleWaves, NT = NW * 64;
-    extern __shared__ __attribute__((aligned(16))) int32_t lds_single[];
+    extern __shared__ __attribute__((aligned(16))) uint64_t lds_single[];
     __shared__ int32_t wsum[NW];
     const int NB = a.E + 1, nbits = bucket_bits(NB);
-    int32_t* cnt = lds_single;
+    uint64_t* msk_w = MASK ? lds_single + (threadIdx.x >> 6) * NB : nullptr;
+    int32_t* cnt = (int32_t*)(lds_single + (MASK ? NW * NB : 0));
     int32_t* bstart = cnt + NW * NB;
     int32_t* tmp = bstart + NB + 1;
     const int w = threadIdx.x >> 6;
@@ -273,7 +299,7 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
     const int64_t beg = min((int64_t)w * per, a.n), end = min(beg + per, a.n);
     int bk[kPre];   // this wave's ids (per <= kPre batches), kept for the placement
     load_batches(a.ids, beg, end, a.E, bk);
-    count_batches(bk, beg, end, nbits, cnt + w * NB);
+    count_batches(bk, beg, end, nbits, cnt + w * NB, msk_w);
     __syncthreads();
     // per bucket, exclusive scan of the wave counters: 16 consecutive lanes hold one
     // bucket's counters (wave order) and scan them with shuffles
@@ -332,7 +358,7 @@ __global__ __launch_bounds__(kSingleWaves * 64) void k_row_ids_single(RowIdsArgs
         __syncthreads();
         write_tiles<NT>(a, 1, bstart, tmp, wsum);
     }
-    place_batches(a, bk, beg, end, nbits, bstart, cnt + w * NB);
+    place_batches(a, bk, beg, end, nbits, bstart, cnt + w * NB, msk_w);
 }
 
 // ---------------------------------------------------------------- multi-block
@@ -609,11 +635,18 @@ void row_ids_carve_scratch(RowIdsArgs& a, void* scratch) {
 hipError_t launch_row_ids(const RowIdsArgs& a0, hipStream_t st, int* n_launches) {
     RowIdsArgs a = a0;
     if (a.n <= kRowIdsOneBlockMax) {
-        static PerDeviceOnce lds_cap;   // raise the dynamic LDS cap once per device
-        if (const hipError_t e = set_lds_cap(lds_cap, (const void*)k_row_ids_single,
-                                             (int)single_lds_bytes(kMaxBuckets)))
-            return e;
-        k_row_ids_single<<<1, kSingleWaves * 64, single_lds_bytes(a.E + 1), st>>>(a);
+        static PerDeviceOnce lds_cap_mask, lds_cap_ballot;   // dynamic LDS caps, once per device
+        if (a.E + 1 <= kSingleMaskBuckets) {
+            if (const hipError_t e = set_lds_cap(lds_cap_mask, (const void*)k_row_ids_single<true>,
+                                                 (int)single_lds_bytes(kSingleMaskBuckets, true)))
+                return e;
+            k_row_ids_single<true><<<1, kSingleWaves * 64, single_lds_bytes(a.E + 1, true), st>>>(a);
+        } else {
+            if (const hipError_t e = set_lds_cap(lds_cap_ballot, (const void*)k_row_ids_single<false>,
+                                                 (int)single_lds_bytes(kMaxBuckets, false)))
+                return e;
+            k_row_ids_single<false><<<1, kSingleWaves * 64, single_lds_bytes(a.E + 1, false), st>>>(a);
+        }
         if (n_launches) *n_launches = 1;
         return hipGetLastError();
     }
