@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, Q8_0, MXFP4 = 0, 1, 2, 3
+F32, BF16, Q8_0, MXFP4, IQ4_NL = 0, 1, 2, 3, 4
 _TYPES = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
 
 
@@ -50,6 +50,8 @@ def lib():
         _lib.oracle_e2m1_to_double.argtypes = [ctypes.c_int]
         _lib.oracle_e8m0_to_double.restype = ctypes.c_double
         _lib.oracle_e8m0_to_double.argtypes = [ctypes.c_int]
+        _lib.oracle_iq4nl_level.restype = ctypes.c_double
+        _lib.oracle_iq4nl_level.argtypes = [ctypes.c_int]
         _lib.oracle_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P]
         _lib.oracle_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P]
         _lib.oracle_mul_mat_id.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, ctypes.c_int, I32,
@@ -92,17 +94,29 @@ def e8m0_to_double(x: int) -> float:
     return lib().oracle_e8m0_to_double(int(x) & 0xFF)
 
 
+def iq4nl_level(code: int) -> float:
+    return lib().oracle_iq4nl_level(int(code))
+
+
 def dequant(qs_or_w, d=None) -> np.ndarray:
-    """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]) or MXFP4
-    (codes uint8 [..][rows][cols/2], E8M0 scales uint8 [..][rows][cols/32]), or widen
-    float32 weights, to float64 [..][rows][cols]."""
+    """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]), MXFP4
+    (codes uint8 [..][rows][cols/2], E8M0 scales uint8 [..][rows][cols/32]) or IQ4_NL
+    (codes uint8 [..][rows][cols/2], fp16 scales [..][rows][cols/32]), or widen float32
+    weights, to float64 [..][rows][cols]."""
     a = np.asarray(qs_or_w)
     if d is not None and a.dtype == np.uint8:
         shape = a.shape[:-1] + (2 * a.shape[-1],)
         a3 = _c(a.reshape((-1,) + a.shape[-2:]), np.uint8)
         out = np.empty((a3.shape[0], a3.shape[1], 2 * a3.shape[2]), np.float64)
-        s = _c(np.asarray(d).reshape(a3.shape[0], a3.shape[1], -1), np.uint8)
-        rc = lib().oracle_dequant(MXFP4, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2], _p(out))
+        d = np.asarray(d)
+        if d.dtype == np.float16:
+            s = _c(d.view(np.uint16).reshape(a3.shape[0], a3.shape[1], -1), np.uint16)
+            rc = lib().oracle_dequant(IQ4_NL, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2],
+                                      _p(out))
+        else:
+            s = _c(d.reshape(a3.shape[0], a3.shape[1], -1), np.uint8)
+            rc = lib().oracle_dequant(MXFP4, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2],
+                                      _p(out))
         if rc:
             raise ValueError("oracle_dequant rejected its arguments (%d)" % rc)
         return out.reshape(shape)
@@ -135,13 +149,17 @@ def row_ids(ids: np.ndarray, n_experts: int, src1_rows_per_token: int = 1):
 
 
 def _weights(qs_or_w, d):
-    """(type, data, scales, logical shape). MXFP4 is told apart by its uint8 codes."""
+    """(type, data, scales, logical shape). 4-bit codes come as uint8; their scales'
+    dtype tells MXFP4 (uint8 E8M0) from IQ4_NL (float16)."""
     if d is None:
         w = _c(qs_or_w, np.float32)
         return F32, w, None, w.shape
     if np.asarray(qs_or_w).dtype == np.uint8:
         q = _c(qs_or_w, np.uint8)
-        return MXFP4, q, _c(d, np.uint8), q.shape[:-1] + (2 * q.shape[-1],)
+        shape = q.shape[:-1] + (2 * q.shape[-1],)
+        if np.asarray(d).dtype == np.float16:
+            return IQ4_NL, q, _c(np.asarray(d).view(np.uint16), np.uint16), shape
+        return MXFP4, q, _c(d, np.uint8), shape
     q = _c(qs_or_w, np.int8)
     return Q8_0, q, _c(np.asarray(d).view(np.uint16), np.uint16), q.shape
 
@@ -149,7 +167,7 @@ def _weights(qs_or_w, d):
 def mul_mat_id(w, w_d, src1, src1_type: str, ids, route_w=None, src1_rows_per_token: int = 1):
     """Per-slot dst float64 [T][k][N], or the route_w-weighted [T][N].
     ``w`` is float32 [E][N][K] (w_d None), Q8_0 qs [E][N][K] with scales w_d, or MXFP4
-    codes [E][N][K/2] with E8M0 scales w_d. ``src1`` is [T*B][K] (float32, or bf16 bits
+    (IQ4_NL) codes [E][N][K/2] with E8M0 (fp16) scales w_d. ``src1`` is [T*B][K] (float32, or bf16 bits
     as uint16)."""
     wt, wq, ws, (E, N, K) = _weights(w, w_d)
     ids = _c(ids, np.int32)

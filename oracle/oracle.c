@@ -25,6 +25,12 @@
  *    "Q8_0 / MXFP4"; the pages do not define the format, so it is taken from the
  *    OCP Microscaling (MX) v1.0 specification): blocks of 32 FP4 E2M1 elements
  *    sharing one E8M0 scale, value = fp4(code) * 2^(scale - 127). Exact in float64.
+ *  - Experts may be IQ4_NL, the 4-bit member of the IQ series the pages name (the
+ *    TensorSharp MoE-offload page's models ship as UD-IQ4_XS, whose 4-bit codes are
+ *    IQ4_NL's; the ik_llama.cpp write-up, section 3.2, runs IQ2_K_R4). The pages do
+ *    not define the format, so it is taken from ggml's definition of IQ4_NL: blocks
+ *    of 32 4-bit indices into a fixed non-uniform table of 16 signed integers, one
+ *    fp16 scale per block, value = d * table[code]. Exact in float64.
  *  - The fused MoE FFN applies gate and up projections, SiLU(gate) * up, then the
  *    down projection (section 4.2 names the fused up/gate MoE forward), weights each
  *    routed slot's result by its routing weight and adds always-on shared experts,
@@ -48,6 +54,9 @@
  * 3 = MXFP4 (two 4-bit codes per byte + one uint8 E8M0 scale per 32 elements). MXFP4
  * storage (a reading; the pages fix none): codes [E][rows][cols/2] bytes, element 2i
  * of a row in bits 0-3 of byte i and element 2i+1 in bits 4-7; scales [E][rows][cols/32].
+ * 4 = IQ4_NL: codes packed exactly as MXFP4's (a reading: ggml's own block packs the
+ * low nibbles of a block's 16 bytes first; only the values are the format's), with
+ * fp16 scales d[E][rows][cols/32] as for Q8_0.
  * All entry points return 0 on success and a negative value on bad arguments.
  */
 #include <math.h>
@@ -59,6 +68,18 @@
 #define OR_BF16 1
 #define OR_Q8_0 2
 #define OR_MXFP4 3
+#define OR_IQ4_NL 4
+
+/* IQ4_NL's 16 levels, index = the 4-bit code: ggml's non-linear table for the type
+ * (kvalues_iq4nl in ggml-common.h). */
+static const int8_t iq4nl_levels[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                        1,    13,   25,  38,  53,  69,  89,  113};
+
+/* Level of one IQ4_NL code (0..15), as a double; other inputs return NaN. */
+double oracle_iq4nl_level(int code) {
+    if (code < 0 || code > 15) return NAN;
+    return (double)iq4nl_levels[code];
+}
 
 /* IEEE binary16 -> double, written from the format's definition
  * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits). */
@@ -101,7 +122,7 @@ double oracle_e8m0_to_double(int x) {
     return ldexp(1.0, (x & 0xff) - 127);
 }
 
-static int is_quant(int type) { return type == OR_Q8_0 || type == OR_MXFP4; }
+static int is_quant(int type) { return type == OR_Q8_0 || type == OR_MXFP4 || type == OR_IQ4_NL; }
 
 /* One weight element w(e, n, c) of a stacked matrix, as a double. */
 static double weight_at(int type, const void *data, const void *scales, int64_t rows,
@@ -115,6 +136,13 @@ static double weight_at(int type, const void *data, const void *scales, int64_t 
         int code = (c & 1) ? (b >> 4) : (b & 15);
         uint8_t x = ((const uint8_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
         return oracle_e2m1_to_double(code) * oracle_e8m0_to_double(x);
+    }
+    if (type == OR_IQ4_NL) {
+        /* codes packed as MXFP4's; value = d * level, one fp16 d per 32 columns */
+        uint8_t b = ((const uint8_t *)data)[(e * rows + n) * (cols / 2) + c / 2];
+        int code = (c & 1) ? (b >> 4) : (b & 15);
+        uint16_t d = ((const uint16_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
+        return oracle_half_to_double(d) * oracle_iq4nl_level(code);
     }
     /* Q8_0: value = d * q, one fp16 scale per 32 consecutive columns of a row. */
     int8_t q = ((const int8_t *)data)[idx];
@@ -195,7 +223,7 @@ static void matvec(int type, const void *data, const void *scales, int64_t rows,
         }
         return;
     }
-    if (type == OR_MXFP4) {
+    if (type == OR_MXFP4 || type == OR_IQ4_NL) {
         for (; n < rows; n++) {
             double acc = 0.0;
             for (int64_t c = 0; c < cols; c++) acc += weight_at(type, data, scales, rows, cols, e, n, c) * a[c];

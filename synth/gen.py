@@ -21,6 +21,9 @@ Storage conventions (row-major, last index contiguous):
     [E][rows][cols // 2], two 4-bit E2M1 codes per byte (column 2i in the low nibble,
     2i+1 in the high one), codes uniform over all 16; ``d`` uint8 [E][rows][cols // 32]
     E8M0 scales uniform in {118, ..., 121} (2^-9 .. 2^-6), value = fp4(code) * 2^(d-127).
+  * IQ4_NL weights (the 4-bit codes of the IQ series): ``qs`` uint8 [E][rows][cols // 2]
+    packed as MXFP4's, codes uniform over all 16; ``d`` float16 [E][rows][cols // 32]
+    drawn as Q8_0's, value = d * level(code) with ggml's 16-level IQ4_NL table.
   * bf16 tensors are stored as their uint16 bit patterns (numpy has no bfloat16),
     rounded to nearest-even from float32.
   * ids int32 [T][k]; route_w float32 [T][k], softmax over each token's k picks
@@ -55,7 +58,7 @@ class Config:
     n_embd: int
     n_ff: int
     n_shared: int = 0
-    wtype: str = "q8_0"          # 'q8_0', 'mxfp4' or 'f32'
+    wtype: str = "q8_0"          # 'q8_0', 'mxfp4', 'iq4_nl' or 'f32'
     routing: str = "uniform"     # 'uniform' or 'zipf'
     zipf_s: float = 1.1
     seed: int = 0
@@ -83,6 +86,13 @@ CONFIGS = {
     # GPT-OSS-20B-shaped prefill, PP4096, MXFP4 experts.
     "ppx": Config("ppx", "ffn", 32, 4, 4096, 2880, 2880, wtype="mxfp4", seed=7,
                   desc="GPT-OSS-20B-shaped prefill: E32 k4 T4096 n_embd=n_ff=2880 MXFP4"),
+    # The GPT-OSS-20B shapes with IQ4_NL experts (the 4-bit codes of the IQ series).
+    "dec1n": Config("dec1n", "ffn", 32, 4, 1, 2880, 2880, wtype="iq4_nl", seed=3,
+                    desc="GPT-OSS-20B-shaped decode: E32 k4 T1 n_embd=n_ff=2880 IQ4_NL"),
+    "dec8n": Config("dec8n", "ffn", 32, 4, 8, 2880, 2880, wtype="iq4_nl", seed=3,
+                    desc="GPT-OSS-20B-shaped decode: E32 k4 T8 n_embd=n_ff=2880 IQ4_NL"),
+    "ppn": Config("ppn", "ffn", 32, 4, 4096, 2880, 2880, wtype="iq4_nl", seed=7,
+                  desc="GPT-OSS-20B-shaped prefill: E32 k4 T4096 n_embd=n_ff=2880 IQ4_NL"),
     # Zipf(1.1)-skewed prefill, PP4096.
     "skew": Config("skew", "ffn", 128, 8, 4096, 2048, 768, routing="zipf", seed=4,
                    desc="Skewed prefill: E128 k8 T4096 n_embd2048 n_ff768 Zipf(1.1) Q8_0"),
@@ -175,6 +185,16 @@ def draw_mxfp4(rng: np.random.Generator, rows: int, cols: int):
     return qs, d
 
 
+def draw_iq4_nl(rng: np.random.Generator, rows: int, cols: int):
+    """One IQ4_NL matrix: packed codes uint8 [rows][cols/2] (two uniform 4-bit codes per
+    byte), d float16 [rows][cols/32] ~ U(0.5, 1.5) * 1e-3 (rounded to fp16)."""
+    if cols % 32:
+        raise ValueError("IQ4_NL needs cols % 32 == 0")
+    qs = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    d = (rng.uniform(0.5, 1.5, size=(rows, cols // 32)) * 1e-3).astype(np.float16)
+    return qs, d
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -182,15 +202,16 @@ def _threads() -> int:
 def draw_q8_0_stack(seed: int, stream: int, which: int, n_mat: int, rows: int, cols: int,
                     qs_out: np.ndarray | None = None, d_out: np.ndarray | None = None,
                     wtype: str = "q8_0", only=None):
-    """n_mat stacked Q8_0 (or MXFP4) matrices; matrix e comes from stream
+    """n_mat stacked Q8_0 (MXFP4, IQ4_NL) matrices; matrix e comes from stream
     (seed, stream, e, which). ``only`` (optional) lists the matrices to draw; the
     others are left zero (a drawn matrix has the same values either way)."""
     fp4 = wtype == "mxfp4"
+    nib = fp4 or wtype == "iq4_nl"   # two 4-bit codes per byte
     alloc = np.empty if only is None else np.zeros
-    qs = qs_out if qs_out is not None else (alloc((n_mat, rows, cols // 2), np.uint8) if fp4
+    qs = qs_out if qs_out is not None else (alloc((n_mat, rows, cols // 2), np.uint8) if nib
                                              else alloc((n_mat, rows, cols), np.int8))
     d = d_out if d_out is not None else alloc((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
-    draw = draw_mxfp4 if fp4 else draw_q8_0
+    draw = draw_mxfp4 if fp4 else (draw_iq4_nl if nib else draw_q8_0)
 
     def one(e):
         q, s = draw(_rng(seed, stream, e, which), rows, cols)

@@ -3,7 +3,10 @@
   * number formats: hand-derived bit patterns (tests/golden) and numpy's own
     float16 / float32 decoders over all 65536 patterns; MXFP4 (OCP Microscaling v1.0,
     which the pages name but do not define): the E2M1 value table, the same codes
-    embedded in FP8 E4M3 and decoded by torch, and torch's own E8M0 decoder;
+    embedded in FP8 E4M3 and decoded by torch, and torch's own E8M0 decoder; IQ4_NL
+    (ggml's type, which the pages name as an IQ-series format but do not define): the
+    published 16-level table (tests/golden), a hand-worked row, and the reduction of an
+    IQ4_NL product to the Q8_0 product on the same levels;
   * row-id maps: exhaustive brute force by a stable sort on tiny inputs, numpy's
     stable argsort on random ones, and the invariants of the maps;
   * mul_mat_id: the dense all-experts product (numpy matmul) masked by ids, plain
@@ -186,7 +189,18 @@ def _e8m0_torch(x):
     return t.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
 
 
+def _iq4nl_levels():
+    """The 16 IQ4_NL levels from the golden file (ggml's table, cited there)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "iq4nl_levels.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    assert [int(r[0]) for r in rows] == list(range(16))
+    return np.array([float(r[1]) for r in rows])
+
+
 def _numpy_dequant(qs, d):
+    if qs.dtype == np.uint8 and d.dtype == np.float16:   # IQ4_NL: MXFP4 packing, fp16 scale
+        codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(qs.shape[:-1] + (2 * qs.shape[-1],))
+        return _iq4nl_levels()[codes] * np.repeat(d.astype(np.float64), 32, axis=-1)
     if qs.dtype == np.uint8:   # MXFP4: low nibble = even column; table lookup; torch E8M0
         codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(qs.shape[:-1] + (2 * qs.shape[-1],))
         table = np.array(_E2M1 + tuple(-v for v in _E2M1))
@@ -232,6 +246,53 @@ def test_mxfp4_dequant_layout_and_values():
     assert np.all(w[32:] == 6.0 * 4)     # code 7 = 6, scale 2^(129-127)
     qs, dd = synth.gen.draw_q8_0_stack(5, 2, 1, 3, 7, 96, wtype="mxfp4")
     assert np.array_equal(oracle.dequant(qs, dd), _numpy_dequant(qs, dd))
+
+
+def test_iq4nl_levels_match_golden():
+    """Every code's level against the published table (golden file), and the table's
+    shape: strictly increasing, one level per code, ends at -127 and 113."""
+    lv = _iq4nl_levels()
+    assert np.array_equal([oracle.iq4nl_level(c) for c in range(16)], lv)
+    assert np.all(np.diff(lv) > 0) and lv[0] == -127 and lv[15] == 113
+    assert math.isnan(oracle.iq4nl_level(16)) and math.isnan(oracle.iq4nl_level(-1))
+
+
+def test_iq4nl_dequant_worked_example():
+    """Hand-worked row of 64 columns: byte 0 = 0x8F holds column 0 (low nibble, code 15,
+    level 113) and column 1 (code 8, level 1); byte 1 = 0x07 holds column 2 (code 7,
+    level -10) and column 3 (code 0, level -127); block 0's scale is fp16 0x3800 = 0.5.
+    Block 1's bytes are all 0x9A (even columns code 10 = 25, odd ones code 9 = 13) with
+    scale 0x4000 = 2: 50 and 26."""
+    q = np.array([[0x8F, 0x07] + [0] * 14 + [0x9A] * 16], dtype=np.uint8)
+    d = np.array([[0x3800, 0x4000]], dtype=np.uint16).view(np.float16)
+    w = oracle.dequant(q[None], d[None])[0, 0]
+    assert w.shape == (64,)
+    assert (w[0], w[1], w[2], w[3]) == (56.5, 0.5, -5.0, -63.5)
+    assert np.all(w[4:32:2] == -63.5) and np.all(w[5:32:2] == -63.5)   # zero bytes: code 0
+    assert np.all(w[32::2] == 50.0) and np.all(w[33::2] == 26.0)
+    qs, dd = synth.gen.draw_q8_0_stack(5, 2, 1, 3, 7, 96, wtype="iq4_nl")
+    assert qs.dtype == np.uint8 and dd.dtype == np.float16 and qs.shape == (3, 7, 48)
+    assert np.array_equal(oracle.dequant(qs, dd), _numpy_dequant(qs, dd))
+
+
+@pytest.mark.parametrize("B_is_k", [False, True])
+def test_mul_mat_id_iq4nl_is_q8_0_on_the_levels(B_is_k):
+    """IQ4_NL with codes c and scales d is Q8_0 with q = level(c) and the same d: the
+    oracle's IQ4_NL product must equal its (separately pinned) Q8_0 product bit for bit."""
+    rng = np.random.default_rng(13)
+    E, N, K, T, k = 5, 24, 128, 7, 2
+    qs, d = synth.gen.draw_q8_0_stack(10, 2, 0, E, N, K, wtype="iq4_nl")
+    codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(E, N, K)
+    q8 = _iq4nl_levels()[codes].astype(np.int8)
+    B = k if B_is_k else 1
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T * B, K)).astype(np.float32))
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    rw = synth.draw_route_w(5, T, k)
+    for r in (None, rw):
+        got = oracle.mul_mat_id(qs, d, x, "bf16", ids, r, B)
+        assert np.array_equal(got, oracle.mul_mat_id(q8, d, x, "bf16", ids, r, B))
+    ref = _dense_masked(_numpy_dequant(qs, d), synth.bf16_bits_to_f32(x).astype(np.float64), ids, B)
+    assert normwise(oracle.mul_mat_id(qs, d, x, "bf16", ids, None, B), ref) < 1e-13
 
 
 def _dense_masked(W, X, ids, B):
@@ -355,6 +416,13 @@ def test_ffn_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
 def test_ffn_mxfp4_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
     inp = synth.make_custom_ffn(31 + E, E, k, T, n_embd, n_ff, S, wtype="mxfp4")
     assert inp["gate_qs"].dtype == np.uint8 and inp["gate_qs"].shape == (E, n_ff, n_embd // 2)
+    assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
+
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [(4, 2, 5, 64, 96, 1), (8, 4, 3, 128, 64, 0)])
+def test_ffn_iq4nl_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
+    inp = synth.make_custom_ffn(41 + E, E, k, T, n_embd, n_ff, S, wtype="iq4_nl")
+    assert inp["gate_qs"].dtype == np.uint8 and inp["gate_d"].dtype == np.float16
     assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
 
 
