@@ -23,6 +23,12 @@
  *            codes[n_mat][rows][cols/2], two FP4 E2M1 codes per byte, column 2i in
  *            bits 0-3 and column 2i+1 in bits 4-7, plus uint8 E8M0 scales
  *            x[n_mat][rows][cols/32], value = e2m1(code) * 2^(x - 127) (x = 255: NaN).
+ *            IQ4_NL (the 4-bit codes of the IQ-series types the pages name: IQ2_K_R4
+ *            in the PR #283 write-up, section 3.2, UD-IQ4_XS models on the TensorSharp
+ *            page; defined by ggml): uint8 codes[n_mat][rows][cols/2] packed as MXFP4's,
+ *            plus fp16 scales d[n_mat][rows][cols/32] as Q8_0's, value = d * level(code)
+ *            with ggml's 16 IQ4_NL levels (-127 -104 -83 -65 -49 -35 -22 -10 1 13 25
+ *            38 53 69 89 113).
  *   ids      int32 [n_tokens][n_used]; route_w float32 [n_tokens][n_used].
  *   src1     [n_tokens][B][K] with B = src1_rows_per_token in {1, n_used}:
  *            slot s of token t reads row t*B + (s mod B).
@@ -52,7 +58,7 @@
  *
  * Limits (MOE_ELIMIT): n_tokens < 2^22 and n_used < 2^10 (the bounds the page
  * above quotes for safe 32-bit packing, section 2.1), n_tokens * n_used < 2^31,
- * n_experts <= 1024, Q8_0 and MXFP4 cols % 32 == 0. On the grouped GEMM path the
+ * n_experts <= 1024, Q8_0, MXFP4 and IQ4_NL cols % 32 == 0. On the grouped GEMM path the
  * activation tensor whose rows are gathered through the row map (moe_ffn_fused: x;
  * moe_mul_mat_id: src1) must be under 4 GiB, and each GEMM launch must hold fewer
  * than 2^32 work-items; float32 moe_mul_mat_id needs n_tokens * n_used * N < 2^32.
@@ -75,14 +81,14 @@ typedef enum {
     MOE_EHIP = -4        /* a HIP launch failed                                    */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3, MOE_IQ4_NL = 4 } moe_dtype;
 
 /* n_mat stacked matrices of rows x cols. */
 typedef struct {
-    moe_dtype type;     /* MOE_F32, MOE_Q8_0 or MOE_MXFP4                        */
+    moe_dtype type;     /* MOE_F32, MOE_Q8_0, MOE_MXFP4 or MOE_IQ4_NL            */
     const void *data;   /* F32: float[n_mat][rows][cols]; Q8_0: int8 qs[...];    */
-                        /* MXFP4: uint8 codes[n_mat][rows][cols/2]               */
-    const void *scales; /* Q8_0: uint16 (fp16) d[n_mat][rows][cols/32];          */
+                        /* MXFP4, IQ4_NL: uint8 codes[n_mat][rows][cols/2]       */
+    const void *scales; /* Q8_0, IQ4_NL: uint16 (fp16) d[n_mat][rows][cols/32];  */
                         /* MXFP4: uint8 E8M0 x[n_mat][rows][cols/32]; F32: NULL  */
     int64_t n_mat, rows, cols;
 } moe_weights;
@@ -135,9 +141,10 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
 /*
  * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
  *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
- *            src1) or (MXFP4 w, BF16 src1) on the MFMA grouped GEMM or the GEMV path
- *            (MXFP4 on the GEMV path: n_tokens * n_used <= 64 and K <= 4096, else the
- *            GEMM path is taken, and forcing the GEMV path is MOE_EINVAL); (F32 w, F32
+ *            src1), (MXFP4 w, BF16 src1) or (IQ4_NL w, BF16 src1) on the MFMA grouped
+ *            GEMM or the GEMV path (MXFP4 and IQ4_NL on the GEMV path: n_tokens *
+ *            n_used <= 64 and K <= 4096, else the GEMM path is taken, and forcing the
+ *            GEMV path is MOE_EINVAL); (F32 w, F32
  *            src1), which has one path, the fp32 grouped product: opt->path must be
  *            0 or 1 (else MOE_EINVAL).
  *   src1     device [n_tokens][B][K], B = src1_rows_per_token in {1, n_used}
@@ -163,14 +170,15 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
  *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
  *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
  *   sh_gate, sh_up Q8_0 [S][n_ff_sh][n_embd]; sh_down Q8_0 [S][n_embd][n_ff_sh];
- *             or all of them MXFP4 (its GEMV path needs n_tokens * n_used <= 64 and
- *             n_embd, n_ff, n_ff_sh <= 4096; larger calls take the grouped GEMM);
+ *             or all of them MXFP4, or all IQ4_NL (their GEMV path needs n_tokens *
+ *             n_used <= 64 and n_embd, n_ff, n_ff_sh <= 4096; larger calls take the
+ *             grouped GEMM);
  *             all three NULL (or n_mat == 0) = no shared experts; giving only some of
  *             them is MOE_EINVAL.
  *   x         device BF16 [n_tokens][n_embd]; ids, route_w as above.
  *   out       device float32 [n_tokens][n_embd] (overwritten).
  * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights (Q8_0: d*q
- * rounded to nearest-even; MXFP4: exact), bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
+ * rounded to nearest-even; MXFP4: exact; IQ4_NL: d*level rounded to nearest-even), bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
  * results; GEMV path -- weights exact, fp32 accumulate throughout.
  */
 moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const moe_weights *down,

@@ -20,12 +20,16 @@
 //   * Two per pass: the activations fill the register file, so the rows stream
 //     through a per-wave ring in LDS with direct global-to-LDS copies (the bytes in
 //     flight cost no registers).
+//   * 4-bit experts (MXFP4, IQ4_NL): a lane takes one whole block of 32 codes (16
+//     bytes) per 2048-wide K piece; MXFP4 codes convert in hardware, IQ4_NL codes
+//     through a byte-permute lookup of the 16 levels (iq4nl.h).
 //   * For larger batches or K a block kernel (4 waves per chunk of rows, activations
-//     staged in LDS) takes over.
+//     staged in LDS) takes over (Q8_0 only).
 //   * Results are written per slot; the fixed-order weighted reduction runs in the
 //     reduce kernel.
 #include <type_traits>
 
+#include "iq4nl.h"
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -117,6 +121,9 @@ template <> struct Fmt<0> {   // Q8_0: int8 codes, one fp16 scale per 32
 template <> struct Fmt<1> {   // MXFP4: two E2M1 codes per byte (even column low), one E8M0 byte per 32
     static constexpr int VPL = 32, PIECE = 2048, SB = 1;
 };
+template <> struct Fmt<2> {   // IQ4_NL: two codes per byte (even column low), one fp16 scale per 32
+    static constexpr int VPL = 32, PIECE = 2048, SB = 2;
+};
 
 // E8M0 scale byte -> 2^(x - 127) (x = 0 is the subnormal 2^-127; x = 255 is NaN).
 __device__ __forceinline__ float e8m0_to_float(uint32_t x) {
@@ -172,21 +179,69 @@ __device__ __forceinline__ float dot32_fp4_bf16(const i32x4& q, const uint32_t* 
     return s;
 }
 
-// Activations of one lane's piece in registers: MXFP4 with bf16 activations keeps them as
-// packed pairs (VPL / 2 dwords); otherwise VPL exact fp32 values.
+// 32 IQ4_NL codes (16 bytes) dotted with 32 floats: the codes become their levels (exact
+// signed bytes, ggml's table), each converted exactly to fp32; the caller multiplies the
+// sum by the block's fp16 scale.
+__device__ __forceinline__ float dot32_nl(const i32x4& q, const float* x) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t c03, c47;
+        nl_levels8((uint32_t)q[w], c03, c47);
+#pragma unroll
+        for (int j = 0; j < 4; j++) s = fmaf((float)(int8_t)(c03 >> (8 * j)), x[8 * w + j], s);
+#pragma unroll
+        for (int j = 0; j < 4; j++) s = fmaf((float)(int8_t)(c47 >> (8 * j)), x[8 * w + 4 + j], s);
+    }
+    return s;
+}
+
+// Two signed byte levels (bits 0-7 and 8-15 of v) -> an exact bf16 pair (a level has at
+// most 7 significant bits, so the top half of its fp32 form is exact).
+__device__ __forceinline__ uint32_t nl_bf16_pair(uint32_t v) {
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(int8_t)v);
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)(int8_t)(v >> 8));
+    return __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+}
+
+// 32 IQ4_NL codes dotted with 32 bf16 activations held as 16 packed pairs: each pair of
+// levels becomes an exact bf16 pair for one dot2 instruction (fp32 accumulate).
+__device__ __forceinline__ float dot32_nl_bf16(const i32x4& q, const uint32_t* xv) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        uint32_t c03, c47;
+        nl_levels8((uint32_t)q[w], c03, c47);
+        const uint32_t p[4] = {nl_bf16_pair(c03), nl_bf16_pair(c03 >> 16), nl_bf16_pair(c47),
+                               nl_bf16_pair(c47 >> 16)};
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[j]),
+                                                __builtin_bit_cast(bf16x2, xv[4 * w + j]), s, false);
+    }
+    return s;
+}
+
+// Activations of one lane's piece in registers: 4-bit formats with bf16 activations keep
+// them as packed pairs (VPL / 2 dwords); otherwise VPL exact fp32 values.
 template <int FMT, bool XBF16>
 struct XRegs {
-    static constexpr bool PACKED = FMT == 1 && XBF16;
+    static constexpr bool PACKED = FMT != 0 && XBF16;
     static constexpr int N = PACKED ? Fmt<FMT>::VPL / 2 : Fmt<FMT>::VPL;
     using T = std::conditional_t<PACKED, uint32_t, float>;
 };
 
 // One lane's share of a row piece: acc + scale * (codes q . activations xv), with one
 // rounding for the scaling add (fma). sb holds the raw scale bits (fp16 for Q8_0, E8M0
-// for MXFP4); pieces past K get a zero scale.
+// for MXFP4, fp16 for IQ4_NL); pieces past K get a zero scale.
 template <int FMT, bool PACKED, class XT>
 __device__ __forceinline__ float piece_fma(const i32x4& q, const XT* xv, uint32_t sb, bool in, float acc) {
-    if constexpr (PACKED) {
+    if constexpr (FMT == 2) {
+        const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
+        if constexpr (PACKED) return fmaf(dd, dot32_nl_bf16(q, xv), acc);
+        else return fmaf(dd, dot32_nl(q, xv), acc);
+    } else if constexpr (PACKED) {
         const float sc = in ? e8m0_to_float(sb & 255u) : 0.f;
         return fmaf(sc, dot32_fp4_bf16(q, xv), acc);
     } else if constexpr (FMT == 0) {
@@ -522,7 +577,7 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
                 const i32x4* qp = (const i32x4*)(qr + kc[i] * 16 / F::VPL);
                 if constexpr (kDecWeightsNT) w.q[m][i] = __builtin_nontemporal_load(qp);
                 else w.q[m][i] = *qp;
-                if constexpr (FMT == 0) w.d[m][i] = *(const uint16_t*)(dr + 2 * (kc[i] >> 5));
+                if constexpr (FMT != 1) w.d[m][i] = *(const uint16_t*)(dr + 2 * (kc[i] >> 5));
                 else w.d[m][i] = dr[kc[i] >> 5];
             }
         }
@@ -790,7 +845,7 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
                     const int s0 = (int)((uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * F::SB) & 3);
                     const i32x4 q = *(const i32x4*)(mp + (i << 10) + (lane << 4));
                     const uint8_t* sp = mp + NIT * 1024 + s0 + F::SB * (kc[i] >> 5);
-                    const uint32_t sb = FMT == 0 ? (uint32_t)*(const uint16_t*)sp : (uint32_t)*sp;
+                    const uint32_t sb = FMT != 1 ? (uint32_t)*(const uint16_t*)sp : (uint32_t)*sp;
 #pragma unroll
                     for (int p = 0; p < P; p++)   // lanes past K add 0 through a zero scale
                         acc[m][p] = piece_fma<FMT, XR::PACKED>(q, x[p][i], sb, kin[i], acc[m][p]);
@@ -1010,7 +1065,7 @@ template <int MODE, bool XBF16, int FMT>
 hipError_t launch_wave(const DecArgs& a, int slots_max, bool fuse, hipStream_t st) {
     const int kmax = max(a.rw.K, a.sw.n_mat > 0 ? a.sw.K : 0);
     const int pieces = (kmax + Fmt<FMT>::PIECE - 1) / Fmt<FMT>::PIECE;
-    if constexpr (FMT == 1) {
+    if constexpr (FMT != 0) {   // 2048-column pieces: K <= 4096 takes two
         return pieces <= 1 ? launch_wave_nit<MODE, XBF16, 1, FMT>(a, slots_max, fuse, st)
                            : launch_wave_nit<MODE, XBF16, 2, FMT>(a, slots_max, fuse, st);
     } else {
@@ -1046,10 +1101,11 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced) {
                           a.d_max + S <= 4 * MOE_DEC_FUSE_UPW;
         if (same_type) {
             if (reduced) *reduced = fuse;
+            if (a.rw.fmt == 2) return launch_wave_fmt<2>(a, slots, fuse, st);
             return a.rw.fmt == 1 ? launch_wave_fmt<1>(a, slots, fuse, st) : launch_wave_fmt<0>(a, slots, fuse, st);
         }
     }
-    if (a.rw.fmt != 0) return hipErrorInvalidValue;   // MXFP4: the wave kernels only
+    if (a.rw.fmt != 0) return hipErrorInvalidValue;   // MXFP4, IQ4_NL: the wave kernels only
     const int nb_r = a.d_max * ((a.rw.N + kR - 1) / kR);
     const int nb_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kR - 1) / kR) : 0;
     const int grid = nb_r + nb_s;

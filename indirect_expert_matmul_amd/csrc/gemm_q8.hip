@@ -37,6 +37,7 @@
 //     tile count exit at once.
 #include <type_traits>
 
+#include "iq4nl.h"
 #include "lds_dma.h"
 
 #include "moe_internal.h"
@@ -119,14 +120,16 @@ constexpr int kMChunk = MOE_GEMM_MCHUNK;   // M tiles sharing each weight slab i
 // as 32 bytes per row into a two-slot ring, a quarter of the memory requests; one word
 // per row per stage costs as many requests as the weight rows themselves.
 // FMT = 1: MXFP4 experts (64-byte weight rows per stage, E8M0 scale bytes, SG = 1).
+// FMT = 2: IQ4_NL experts (the same 64-byte rows of 4-bit codes, fp16 scales, SG = 1):
+// the codes become their levels (signed bytes) and then take the Q8_0 dequant.
 template <int MSUB, int MODE, int W, int NS, int SG, int FMT>
 __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int BM = 32 * MSUB;
     constexpr int NTW = out_cols<MODE, W>();     // output columns per block
     constexpr int A_BYTES = BM * 256;
-    constexpr int WROW = FMT == 1 ? 64 : 128;    // weight bytes per row per stage
+    constexpr int WROW = FMT != 0 ? 64 : 128;    // weight bytes per row per stage
     constexpr int B_BYTES = W * 32 * WROW;
-    static_assert(FMT == 0 || SG == 1, "MXFP4 scales come one word per block per stage");
+    static_assert(FMT == 0 || SG == 1, "4-bit formats' scales come one word per block per stage");
     constexpr int S_BYTES = SG == 1 ? W * 32 * 16 : 0;
     constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     constexpr int SGROUP = W * 32 * 32;          // SG = 4: one group, 32 bytes per row
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int NA = BM / (4 * W);             // activation copies (1 KB) per wave per stage
     // copies per wave per stage with per-stage scales: NA activation, the weight copies
     // and two scale-word copies
-    constexpr int VM_STAGE = NA + (FMT == 1 ? 2 : 4) + 2;
+    constexpr int VM_STAGE = NA + (FMT != 0 ? 2 : 4) + 2;
     static_assert(NS == 2 || (NS == 3 && SG == 1),
                   "a two-slot ring, or a three-slot one with a fixed copy count per stage");
     static_assert(NA * 4 * W == BM, "activation rows must split evenly over the waves");
@@ -250,18 +253,18 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     }
     // weights: copy i covers local rows 8i..8i+7 (8 lanes x 16 B per row); in gate/up
     // mode copies 0-1 read gate rows and 2-3 up rows
-    // (MXFP4: copy i covers local rows 16i..16i+15, 4 lanes x 16 B per row; copy 0 the
-    // gate rows and 1 the up rows)
-    constexpr int NB = FMT == 1 ? 2 : 4;           // weight copies per wave per stage
-    const int64_t RB = FMT == 1 ? K / 2 : K;       // bytes per weight row
+    // (4-bit codes: copy i covers local rows 16i..16i+15, 4 lanes x 16 B per row; copy 0
+    // the gate rows and 1 the up rows)
+    constexpr int NB = FMT != 0 ? 2 : 4;           // weight copies per wave per stage
+    const int64_t RB = FMT != 0 ? K / 2 : K;       // bytes per weight row
     const int8_t* b_base1 = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * RB);
     const int8_t* b_base2 = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * RB) : b_base1;
     uint32_t b_off[NB];
     int b_lc[NB];
 #pragma unroll
     for (int i = 0; i < NB; i++) {
-        const int l = FMT == 1 ? 16 * i + (lane >> 2) : 8 * i + (lane >> 3);
-        const int lc = FMT == 1 ? (lane & 3) ^ swz_b4(wv * 32 + l) : (lane & 7) ^ swz_b(wv * 32 + l);
+        const int l = FMT != 0 ? 16 * i + (lane >> 2) : 8 * i + (lane >> 3);
+        const int lc = FMT != 0 ? (lane & 3) ^ swz_b4(wv * 32 + l) : (lane & 7) ^ swz_b(wv * 32 + l);
         b_off[i] = (uint32_t)((int64_t)wrow(l) * RB + lc * 16);
         b_lc[i] = lc;
     }
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     {
         const int l = lane >> 1;
         const uint16_t* dt = (MODE == 1 && l >= 16) ? P.d2 : P.d1;
-        sg_ptr = FMT == 1 ? nullptr : (const uint8_t*)(dt + ((int64_t)e * N + wrow(l)) * KB) + 16 * (lane & 1);
+        sg_ptr = FMT != 0 ? nullptr : (const uint8_t*)(dt + ((int64_t)e * N + wrow(l)) * KB) + 16 * (lane & 1);
     }
     const uint32_t sring = lds0 + (uint32_t)(NS * STAGE);
 
@@ -320,8 +323,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             }
 #pragma unroll
             for (int i = 0; i < NB; i++) {
-                // chunk lc holds columns k0 + lc*16 (Q8_0) or k0 + lc*32 (MXFP4) on
-                const uint32_t adj = (k0 + b_lc[i] * (FMT == 1 ? 32 : 16) >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
+                // chunk lc holds columns k0 + lc*16 (Q8_0) or k0 + lc*32 (4-bit codes) on
+                const uint32_t adj = (k0 + b_lc[i] * (FMT != 0 ? 32 : 16) >= K) ? (uint32_t)(b_lc[i] * 16) : 0u;
                 dma16_w(w_once, ((MODE == 1 && i >= NB / 2) ? b_base2 : b_base1) + k0 * WROW / 128, b_off[i] - adj,
                         st + A_BYTES + wv * 32 * WROW + i * 1024);
             }
@@ -390,6 +393,13 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 d[u] = __builtin_bit_cast(float, ((sw >> s_sh[u]) & 255u) << 23);
                 if constexpr (CHECK_K)
                     if (!(k0 + 64 * u + 32 * h < K)) q[u][0] = i32x4{0, 0, 0, 0};
+            } else if constexpr (FMT == 2) {
+                // one 16-byte chunk = this lane's block of 32 codes; the block's fp16 scale
+                // from the stage's scale words as for Q8_0 (zero past K)
+                q[u][0] = *(const i32x4*)(st + b_rd + (((2 * u + h) ^ swz_b4(lrow)) << 4));
+                const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
+                d[u] = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
+                if constexpr (CHECK_K) d[u] = (k0 + 64 * u + 32 * h < K) ? d[u] : 0.f;
             } else {
                 q[u][0] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
                 q[u][1] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
@@ -409,6 +419,11 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         // the compiler issues all of a stage's dequant work before its MFMAs)
         auto deq = [&](int t) -> bf16x8 {
             if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[t >> 2][0][t & 3], d[t >> 2]);
+            if constexpr (FMT == 2) {
+                uint32_t c03, c47;
+                nl_levels8((uint32_t)q[t >> 2][0][t & 3], c03, c47);
+                return dequant8((int)c03, (int)c47, d[t >> 2]);
+            }
             const i32x4& v = q[t >> 2][(t & 3) >> 1];
             return (t & 1) ? dequant8(v[2], v[3], d[t >> 2]) : dequant8(v[0], v[1], d[t >> 2]);
         };
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur], acc[i], 0, 0, 0);
 #ifndef MOE_GEMM_NO_SCHED
             if (t < 7) {
-                constexpr int VPM = ((FMT == 1 ? 4 : 20) + MSUB - 1) / MSUB;   // dequant VALU per MFMA
+                constexpr int VPM = ((FMT == 1 ? 4 : FMT == 2 ? 36 : 20) + MSUB - 1) / MSUB;   // dequant VALU per MFMA
 #pragma unroll
                 for (int m = 0; m < MSUB; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -549,13 +564,15 @@ constexpr int KS = 64;
 __device__ __forceinline__ int swz_wa(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_wb(int r) { return (r >> 2) & 3; }
 // Block tile 32*MSUB activation rows x 64*W weight rows, W waves, NS ring slots; FMT = 1
-// for MXFP4 weights (32-byte rows per stage, two E8M0 scale bytes per row per stage).
+// for MXFP4 weights (32-byte rows per stage, two E8M0 scale bytes per row per stage);
+// FMT = 2 for IQ4_NL (the same 32-byte rows of codes, the stage's two fp16 scales in one
+// aligned word as for Q8_0).
 template <int MSUB, int W, int NS, int FMT = 0>
 struct Cfg {
     static constexpr int BM = 32 * MSUB;
     static constexpr int BN = 64 * W;                 // weight rows per block
     static constexpr int A_BYTES = BM * KS * 2;       // 128-byte rows, 8 chunks
-    static constexpr int WROW = FMT == 1 ? KS / 2 : KS;   // weight bytes per row per stage
+    static constexpr int WROW = FMT != 0 ? KS / 2 : KS;   // weight bytes per row per stage
     static constexpr int B_BYTES = BN * WROW;         // 64-byte rows, 4 chunks (MXFP4: 32, 2)
     static constexpr int NA = BM / (8 * W);           // activation copies (8 rows) per wave
     static constexpr int SGROUP = BN * 16;            // SG = 4: one group of scales
@@ -573,7 +590,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     using namespace wide;
     using C = Cfg<MSUB, W, NS, FMT>;
     static_assert(NS == 2 || NS == 3, "two- or three-slot ring");
-    static_assert(FMT == 0 || (SG == 1 && NS == 2), "MXFP4: per-stage scale words, two slots");
+    static_assert(FMT == 0 || (SG == 1 && NS == 2), "4-bit codes: per-stage scale words, two slots");
     constexpr int BM = C::BM, A_BYTES = C::A_BYTES, B_BYTES = C::B_BYTES, NA = C::NA;
     constexpr int SGROUP = C::SGROUP;
     constexpr int NTW = C::template out_cols<MODE>();
@@ -581,7 +598,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     static_assert(NA * 8 * W == BM, "activation rows must split evenly over the waves");
     // copies per wave per stage: NA activation + 4 weight (+ 1 scale word if SG = 1);
     // with SG = 4 every fourth stage also carries one scale-group copy
-    constexpr int VM_STAGE = NA + (FMT == 1 ? 2 : 4) + (SG == 1 ? 1 : 0);
+    constexpr int VM_STAGE = NA + (FMT != 0 ? 2 : 4) + (SG == 1 ? 1 : 0);
     static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -677,7 +694,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     }
     // weights: copy i of wave w covers rows 64w + 16i .. +15 (4 lanes x 16 B per row);
     // in gate/up mode odd copies hold up rows
-    const int64_t RB = FMT == 1 ? K / 2 : K;   // bytes per weight row
+    const int64_t RB = FMT != 0 ? K / 2 : K;   // bytes per weight row
     const int8_t* qg = (const int8_t*)uniform_ptr(P.qs1 + (int64_t)e * N * RB);
     const int8_t* qu = MODE == 1 ? (const int8_t*)uniform_ptr(P.qs2 + (int64_t)e * N * RB) : qg;
     uint32_t b_off[4];
@@ -728,10 +745,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         const int k0 = s * KS;
 #pragma unroll
         for (int i = 0; i < NA; i++) dma16(a_base + (int64_t)k0 * 2, a_off[i], st + (wv * NA + i) * 1024);
-        if constexpr (FMT == 1) {
+        if constexpr (FMT != 0) {
 #pragma unroll
             for (int i = 0; i < 2; i++) dma16v(b_ptr[i] + k0 / 2, st + A_BYTES + (wv * 2 + i) * 1024);
-            dma4v((const void*)((uintptr_t)(s_ptr + 2 * s) & ~(uintptr_t)3), st + A_BYTES + B_BYTES + wv * 256);
+            if constexpr (FMT == 1)
+                dma4v((const void*)((uintptr_t)(s_ptr + 2 * s) & ~(uintptr_t)3), st + A_BYTES + B_BYTES + wv * 256);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -785,6 +803,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
                 const uint32_t sw = *(const uint32_t*)(sg + lr * 4);
                 const int sh = ((s_al[c] + 2 * s) & 3) * 8 + 8 * h;
                 d[c] = __builtin_bit_cast(float, ((sw >> sh) & 255u) << 23);
+            } else if constexpr (FMT == 2) {
+                // the 32 codes as for MXFP4; block 2s + h's fp16 scale from the stage's word
+                q[c][0] = *(const i32x4*)(st + A_BYTES + lr * 32 + 16 * h);
+                const uint32_t sw = *(const uint32_t*)(sg + lr * 4);
+                d[c] = half_bits_to_float((uint16_t)(sw >> (16 * h)));
             } else {
                 const uint8_t* rowp = st + A_BYTES + lr * 64;
                 q[c][0] = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
@@ -799,6 +822,11 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         };
         auto deq = [&](int c, int ss) -> bf16x8 {
             if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[c][0][ss], d[c]);
+            if constexpr (FMT == 2) {
+                uint32_t c03, c47;
+                nl_levels8((uint32_t)q[c][0][ss], c03, c47);
+                return dequant8((int)c03, (int)c47, d[c]);
+            }
             const i32x4& v = q[c][ss >> 1];
             return (ss & 1) ? dequant8(v[2], v[3], d[c]) : dequant8(v[0], v[1], d[c]);
         };
@@ -833,8 +861,8 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
 #ifndef MOE_GEMM_NO_SCHED
             if (ss < 3) {
                 // 2*MACT MFMAs share the sub-step's dequant instructions (Q8_0: 40,
-                // MXFP4: 8)
-                constexpr int VPM = ((FMT == 1 ? 8 : 40) + 2 * MACT - 1) / (2 * MACT);
+                // MXFP4: 8, IQ4_NL: about 72)
+                constexpr int VPM = ((FMT == 1 ? 8 : FMT == 2 ? 72 : 40) + 2 * MACT - 1) / (2 * MACT);
 #pragma unroll
                 for (int m = 0; m < 2 * MACT; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -938,10 +966,10 @@ hipError_t launch_wide_sg(const GemmArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-// MXFP4 experts on the wide kernel (per-stage scale words only).
-template <int MODE, int MSUB, int W, int NS>
+// MXFP4 (FMT = 1) or IQ4_NL (FMT = 2) experts on the wide kernel (per-stage scale words only).
+template <int MODE, int MSUB, int W, int NS, int FMT = 1>
 hipError_t launch_wide_fp4(const GemmArgs& a, hipStream_t st) {
-    constexpr int ntw = wide::Cfg<MSUB, W, NS, 1>::template out_cols<MODE>();
+    constexpr int ntw = wide::Cfg<MSUB, W, NS, FMT>::template out_cols<MODE>();
     int64_t total = 0;
     for (int i = 0; i < a.n_prob; i++) {
         const GemmProblem& p = a.p[i];
@@ -950,7 +978,7 @@ hipError_t launch_wide_fp4(const GemmArgs& a, hipStream_t st) {
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    return launch_wide_sg<MODE, 1, MSUB, W, NS, 1>(g, (int)total, st);
+    return launch_wide_sg<MODE, 1, MSUB, W, NS, FMT>(g, (int)total, st);
 }
 
 template <int MODE, int MSUB, int W, int NS>
@@ -973,7 +1001,7 @@ hipError_t launch_wide(const GemmArgs& a, hipStream_t st) {
 
 template <int MSUB, int W, int NS, int SG, int FMT>
 constexpr int stage_lds() {
-    return NS * (32 * MSUB * 256 + W * 32 * (FMT == 1 ? 64 : 128) + (SG == 1 ? W * 32 * 16 : 0)) +
+    return NS * (32 * MSUB * 256 + W * 32 * (FMT != 0 ? 64 : 128) + (SG == 1 ? W * 32 * 16 : 0)) +
            (SG == 4 ? 2 * W * 32 * 32 : 0);
 }
 
@@ -1003,14 +1031,15 @@ int64_t narrow_grid(const GemmArgs& a) {
 
 // MXFP4 experts: the same kernel with 64-byte weight rows and per-stage scale words.
 // An MXFP4 stage is small enough for a three-slot ring at two 4-wave blocks per CU.
-template <int MSUB, int W, int NS>
+// IQ4_NL experts (FMT = 2) take the same launch shapes.
+template <int MSUB, int W, int NS, int FMT = 1>
 hipError_t launch_cfg_fp4(const GemmArgs& a, hipStream_t st) {
     const int64_t total = narrow_grid<W>(a);
     if (total <= 0) return hipSuccess;
     GemmArgs g = a;
     g.grid_real = (int32_t)total;
-    return a.mode == 1 ? launch_one<MSUB, 1, W, NS, 1, 1>(g, (int)total, st)
-                       : launch_one<MSUB, 0, W, NS, 1, 1>(g, (int)total, st);
+    return a.mode == 1 ? launch_one<MSUB, 1, W, NS, 1, FMT>(g, (int)total, st)
+                       : launch_one<MSUB, 0, W, NS, 1, FMT>(g, (int)total, st);
 }
 
 template <int MSUB, int W, int NS>
@@ -1061,9 +1090,10 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 #ifndef MOE_GEMM_TALL_LAST
 #define MOE_GEMM_TALL_LAST 1   // 0: 128-row tiles only (no 160-row segment-last tiles)
 #endif
-int gemm_tile_x(int msub, int fmt, int64_t K, bool fp4_scales_even) {
-    // MXFP4 takes the wide kernel only with its scale rows at even addresses
-    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && (fmt == 0 || fp4_scales_even)) ? 32 : 0;
+int gemm_tile_x(int msub, int fmt, int64_t K, bool scales_aligned) {
+    // MXFP4 takes the wide kernel only with its scale rows at even addresses, IQ4_NL
+    // only with its scale tensors 4-byte aligned
+    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && (fmt == 0 || scales_aligned)) ? 32 : 0;
 }
 #ifndef MOE_GEMM_TILE160
 #define MOE_GEMM_TILE160 0   // 1: the 160-row kernel runs 160-row tiles instead of 128 + 32
@@ -1073,6 +1103,13 @@ void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q) {
     p.tile_x = MOE_GEMM_TILE160 ? 0 : 32;
     r.tile_m[q] = p.tile_m;
     r.tile_x[q] = p.tile_x;
+}
+
+// Every problem's scale tensors start at an address with (address & mask) == 0.
+static bool scales_aligned(const GemmArgs& a, uintptr_t mask) {
+    for (int i = 0; i < a.n_prob; i++)
+        if (((uintptr_t)a.p[i].d1 & mask) || (a.mode == 1 && ((uintptr_t)a.p[i].d2 & mask))) return false;
+    return true;
 }
 
 hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
@@ -1095,6 +1132,10 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
     }
     if (tall) {
         if (msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        if (a.fmt == 2) {
+            if (!scales_aligned(a, 3)) return hipErrorInvalidValue;
+            return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2, 2>(a, st);
+        }
         if (a.fmt == 1) {
             for (int i = 0; i < a.n_prob; i++)
                 if (((uintptr_t)a.p[i].d1 & 1) || (a.mode == 1 && ((uintptr_t)a.p[i].d2 & 1)))
@@ -1102,6 +1143,19 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
             return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2>(a, st);
         }
         return a.mode == 1 ? launch_wide<1, 5, 4, 2>(a, st) : launch_wide<0, 5, 4, 2>(a, st);
+    }
+    if (a.fmt == 2) {   // IQ4_NL experts: MXFP4's launch shapes
+        switch (msub) {
+            case 2:
+                if (narrow_grid<8>(a) >= 2048) return launch_cfg_fp4<2, 8, 3, 2>(a, st);
+                return launch_cfg_fp4<2, 4, 3, 2>(a, st);
+            case 4:
+                // the wide kernel reads each stage's two fp16 scales as one aligned word
+                if (wide_ok && scales_aligned(a, 3))
+                    return a.mode == 1 ? launch_wide_fp4<1, 4, 4, 2, 2>(a, st) : launch_wide_fp4<0, 4, 4, 2, 2>(a, st);
+                return launch_cfg_fp4<4, 8, 2, 2>(a, st);
+            default: return hipErrorInvalidValue;
+        }
     }
     if (a.fmt == 1) {   // MXFP4 experts: 64-row tiles on the narrow kernel, 128-row on the wide one
         switch (msub) {

@@ -91,8 +91,8 @@ moe_status check_weights(const moe_weights* w, const char* name, bool allow_f32)
         return fail(MOE_EINVAL, "%s: sizes must be > 0", name);
     if (w->rows > INT32_MAX || w->cols > INT32_MAX)
         return fail(MOE_ELIMIT, "%s: rows and cols must fit in int32", name);
-    if (w->type == MOE_Q8_0 || w->type == MOE_MXFP4) {
-        const char* fmt = w->type == MOE_Q8_0 ? "Q8_0" : "MXFP4";
+    if (w->type == MOE_Q8_0 || w->type == MOE_MXFP4 || w->type == MOE_IQ4_NL) {
+        const char* fmt = w->type == MOE_Q8_0 ? "Q8_0" : w->type == MOE_MXFP4 ? "MXFP4" : "IQ4_NL";
         if (!w->scales) return fail(MOE_EINVAL, "%s: %s scales are NULL", name, fmt);
         if (w->cols % 32)
             return fail(MOE_ELIMIT, "%s: %s needs cols %% 32 == 0 (got %lld)", name, fmt, (long long)w->cols);
@@ -121,7 +121,7 @@ int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_op
     return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
 }
 
-// MXFP4 experts: the GEMV path only through its wave-level kernels (n_tokens * n_used
+// 4-bit experts (MXFP4, IQ4_NL): the GEMV path only through its wave-level kernels (n_tokens * n_used
 // <= 64 and every activation width <= 4096); otherwise the grouped GEMM.
 int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4, const moe_options* o) {
     if (!fp4) return select_path(T, k, E, act_width, o);
@@ -130,7 +130,8 @@ int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4
     if (force == 1) return 1;
     if (force == 2) {
         if (!dec_ok)
-            return fail(MOE_EINVAL, "GEMV path with MXFP4 experts needs n_tokens*n_used <= 64 and widths <= 4096");
+            return fail(MOE_EINVAL, "GEMV path with 4-bit (MXFP4, IQ4_NL) experts needs n_tokens*n_used <= 64 "
+                        "and widths <= 4096");
         return 2;
     }
     if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
@@ -143,7 +144,7 @@ int select_path_aq(int64_t T, int32_t k, int32_t E, int64_t act_width, int32_t w
                    const moe_options* o) {
     const int32_t aq = o ? o->act_quant : 0;
     if (aq != 0 && aq != 1) return fail(MOE_EINVAL, "options.act_quant must be 0 or 1 (got %d)", aq);
-    if (!aq) return select_path_fmt(T, k, E, act_width, wtype == MOE_MXFP4, o);
+    if (!aq) return select_path_fmt(T, k, E, act_width, wtype == MOE_MXFP4 || wtype == MOE_IQ4_NL, o);
     if (wtype != MOE_Q8_0) return fail(MOE_EINVAL, "quantized activations (act_quant = 1) need Q8_0 experts");
     if (o->path != 0 && o->path != 1)
         return fail(MOE_EINVAL, "quantized activations run on the grouped GEMM only: options.path must "
@@ -182,7 +183,7 @@ RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, int tile_m) 
 struct FfnDims {
     int64_t T;
     int32_t k, E, n_embd, n_ff, S, n_ff_sh;
-    bool fp4;   // MXFP4 experts (else Q8_0)
+    int32_t fmt;   // kernel weight format: 0 Q8_0, 1 MXFP4, 2 IQ4_NL
 };
 
 struct FfnPlan {
@@ -269,7 +270,7 @@ moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const mo
     d->E = (int32_t)gate->n_mat;
     d->n_ff = (int32_t)gate->rows;
     d->n_embd = (int32_t)gate->cols;
-    d->fp4 = gate->type == MOE_MXFP4;
+    d->fmt = gate->type == MOE_MXFP4 ? 1 : gate->type == MOE_IQ4_NL ? 2 : 0;
     const bool any_sh = (sg && sg->n_mat) || (su && su->n_mat) || (sd && sd->n_mat);
     d->S = 0;
     d->n_ff_sh = 0;
@@ -305,6 +306,7 @@ moe_status validate_mmid(const moe_weights* w, moe_dtype st, int32_t B, int64_t 
     if (B != 1 && B != k) return fail(MOE_EINVAL, "src1_rows_per_token must be 1 or n_used (got %d)", B);
     if (w->type == MOE_Q8_0 && st != MOE_BF16) return fail(MOE_EINVAL, "Q8_0 weights need BF16 src1");
     if (w->type == MOE_MXFP4 && st != MOE_BF16) return fail(MOE_EINVAL, "MXFP4 weights need BF16 src1");
+    if (w->type == MOE_IQ4_NL && st != MOE_BF16) return fail(MOE_EINVAL, "IQ4_NL weights need BF16 src1");
     if (w->type == MOE_F32 && st != MOE_F32) return fail(MOE_EINVAL, "F32 weights need F32 src1");
     return MOE_OK;
 }
@@ -588,7 +590,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
 
         GemmArgs g{};
         g.mode = 1;
-        g.fmt = d.fp4 ? 1 : 0;
+        g.fmt = d.fmt;
         g.n_prob = shared ? 2 : 1;
         GemmProblem& r = g.p[0];
         r.qs1 = (const int8_t*)gate->data;
@@ -664,9 +666,11 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         }
         // segment-last tiles of up to 160 rows where both GEMMs (and the shared ones they
         // launch with) run the wide kernel: the two share the row-id pass's tile table
-        bool even = true;   // MXFP4: every scale tensor at an even address
+        // MXFP4: every scale tensor at an even address; IQ4_NL: 4-byte aligned
+        const uintptr_t smask = g.fmt == 2 ? 3 : 1;
+        bool even = true;
         for (const moe_weights* w : {gate, up, down, sh_gate, sh_up, sh_down})
-            if (w && ((uintptr_t)w->scales & 1)) even = false;
+            if (w && ((uintptr_t)w->scales & smask)) even = false;
         int tx = gemm_tile_x(p.msub, g.fmt, d.n_embd, even);
         if (gemm_tile_x(p.msub, g.fmt, d.n_ff, even) == 0 ||
             (shared && gemm_tile_x(p.msub, g.fmt, d.n_ff_sh, even) == 0))
@@ -694,7 +698,7 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         a.T = (int32_t)d.T;
         a.k = d.k;
         a.E = d.E;
-        const int32_t fmt = d.fp4 ? 1 : 0;
+        const int32_t fmt = d.fmt;
         a.rw = DecWeights{(const int8_t*)gate->data, (const uint16_t*)gate->scales,
                           (const int8_t*)up->data, (const uint16_t*)up->scales, d.E, d.n_ff, d.n_embd, fmt};
         if (shared)
@@ -770,7 +774,7 @@ size_t moe_mul_mat_id_workspace_size(const moe_weights* w, moe_dtype src1_type,
                                      int32_t src1_rows_per_token, int64_t n_tokens,
                                      int32_t n_used, const moe_options* opt) {
     if (validate_mmid(w, src1_type, src1_rows_per_token, n_tokens, n_used)) return 0;
-    const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
+    const bool q8 = w->type != MOE_F32;   // quantized experts
     if (!q8 && opt && ((opt->path != 0 && opt->path != 1) || opt->act_quant)) return 0;
     const int path = q8 ? select_path_aq(n_tokens, n_used, (int32_t)w->n_mat, w->cols, w->type, opt) : 1;
     if (path < 0) return 0;
@@ -793,7 +797,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         return MOE_OK;
     }
     if (!src1 || !ids || !dst) return fail(MOE_EINVAL, "NULL pointer argument");
-    const bool q8 = w->type == MOE_Q8_0 || w->type == MOE_MXFP4;   // quantized experts
+    const bool q8 = w->type != MOE_F32;   // quantized experts
     const int32_t E = (int32_t)w->n_mat, N = (int32_t)w->rows, K = (int32_t)w->cols;
     const int32_t B = src1_rows_per_token, k = n_used;
     if (!q8 && opt && opt->path != 0 && opt->path != 1)
@@ -870,7 +874,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             ra.tile_tab[0] = p.r.tile_tab;
             ra.tile_cap[0] = p.r.tile_cap;
             g.mode = 0;
-            g.fmt = w->type == MOE_MXFP4 ? 1 : 0;
+            g.fmt = w->type == MOE_MXFP4 ? 1 : w->type == MOE_IQ4_NL ? 2 : 0;
             g.n_prob = 1;
             GemmProblem& r = g.p[0];
             r.qs1 = (const int8_t*)w->data;
@@ -889,7 +893,8 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
-            if (gemm_tile_x(p.msub, g.fmt, K, ((uintptr_t)w->scales & 1) == 0)) gemm_set_tall(r, ra, 0);
+            if (gemm_tile_x(p.msub, g.fmt, K, ((uintptr_t)w->scales & (g.fmt == 2 ? 3 : 1)) == 0))
+                gemm_set_tall(r, ra, 0);
             if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
         }
         tm.begin();
@@ -923,7 +928,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         a.k = k;
         a.E = E;
         a.rw = DecWeights{(const int8_t*)w->data, (const uint16_t*)w->scales, nullptr, nullptr, E, N, K,
-                          w->type == MOE_MXFP4 ? 1 : 0};
+                          w->type == MOE_MXFP4 ? 1 : w->type == MOE_IQ4_NL ? 2 : 0};
         a.act = src1;
         a.act_type = 1;
         a.act_B = B;

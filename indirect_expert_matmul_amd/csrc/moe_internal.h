@@ -137,7 +137,8 @@ struct GemmArgs {
     int32_t mode;             // 0: fp32 out = acc; 1: bf16 out = silu(acc_gate) * acc_up
     int32_t grid_real;        // blocks carrying tiles (before padding to a multiple of 8)
     // 0: Q8_0 experts; 1: MXFP4 -- qs1/qs2 hold two E2M1 codes per byte ([n_mat][N][K/2],
-    // even column in the low nibble), d1/d2 the E8M0 scale bytes ([n_mat][N][K/32])
+    // even column in the low nibble), d1/d2 the E8M0 scale bytes ([n_mat][N][K/32]);
+    // 2: IQ4_NL -- codes packed as MXFP4's, d1/d2 fp16 scales as Q8_0's
     int32_t fmt;
 };
 // Block tile height for a given average rows-per-expert (host heuristic).
@@ -146,8 +147,8 @@ int gemm_tile_m(int msub);
 // Extra rows (0 or 32) the last M tile of an expert may hold on the GEMM path for this
 // tile choice, weight format and K: 32 where the 128-row wide kernel runs, whose
 // 160-row variant takes such tiles (MXFP4: when every scale tensor of the launch
-// starts at an even address).
-int gemm_tile_x(int msub, int fmt, int64_t K, bool fp4_scales_even);
+// starts at an even address; IQ4_NL: at a 4-byte aligned one).
+int gemm_tile_x(int msub, int fmt, int64_t K, bool scales_aligned);
 // Puts routed problem p and tile table q of the row-id pass on the 160-row kernel's tiles.
 void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q);
 // M tiles of a segment of `rows` rows: tiles of tm rows, the last one holding up to
@@ -206,7 +207,8 @@ struct DecWeights {
     int32_t n_mat, N, K;
     // 0: Q8_0 (int8 codes, fp16 scales); 1: MXFP4 -- qs holds two E2M1 codes per byte
     // ([n_mat][N][K/2], even column in the low nibble) and d the E8M0 scale bytes
-    // ([n_mat][N][K/32]); the pointers are read as bytes
+    // ([n_mat][N][K/32]); the pointers are read as bytes; 2: IQ4_NL -- codes as MXFP4's,
+    // fp16 scales as Q8_0's
     int32_t fmt;
 };
 struct DecArgs {

@@ -33,17 +33,17 @@ def test_status_strings():
 
 
 def _w(n_mat=8, rows=64, cols=128, typ=moe.MOE_Q8_0, data=FAKE, scales=FAKE):
-    return moe.c_moe_weights(typ, data, scales if typ in (moe.MOE_Q8_0, moe.MOE_MXFP4) else None,
+    return moe.c_moe_weights(typ, data, scales if typ in (moe.MOE_Q8_0, moe.MOE_MXFP4, moe.MOE_IQ4_NL) else None,
                              n_mat, rows, cols)
 
 
 def _ffn(gate=None, up=None, down=None, sh=(None, None, None), T=16, k=2, x_type=moe.MOE_BF16,
-         ws_bytes=1 << 40, ids=FAKE, out=FAKE, path=0):
+         ws_bytes=1 << 40, ids=FAKE, out=FAKE, path=0, aq=0):
     gate = gate or _w()
     up = up or _w()
     down = down or _w(rows=128, cols=64)
     ref = lambda w: ctypes.byref(w) if w is not None else None
-    opt = moe._options(path)
+    opt = moe._options(path, act_quant=aq)
     return moe.lib.moe_ffn_fused(ref(gate), ref(up), ref(down), ref(sh[0]), ref(sh[1]), ref(sh[2]),
                                  FAKE, x_type, ids, FAKE, T, k, out, ctypes.byref(opt), FAKE,
                                  ws_bytes, None)
@@ -108,6 +108,28 @@ def test_mxfp4_validation():
     assert mm(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) > 0              # the GEMM path
     assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
                                   None, FAKE, 1 << 30, None) == moe.MOE_EINVAL   # needs BF16 src1
+
+
+def test_iq4nl_validation():
+    """IQ4_NL experts: both paths validate (the calls stop at the workspace check here),
+    the GEMV path forced past its wave-kernel bound, mixed types, missing scales, cols not
+    a multiple of 32 and float32 src1 are refused."""
+    nl = lambda **kw: _w(typ=moe.MOE_IQ4_NL, **kw)
+    dn = lambda **kw: nl(rows=128, cols=64, **kw)
+    assert _ffn(gate=nl(), up=nl(), down=dn(), T=4, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=nl(), up=nl(), down=dn(), T=40, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=nl(), up=nl(), down=dn(), T=40, k=2, path=2) == moe.MOE_EINVAL   # 80 slots
+    assert "IQ4_NL" in moe.last_error()
+    assert _ffn(gate=nl(), up=_w(typ=moe.MOE_MXFP4), down=dn(), T=4, k=2) == moe.MOE_EINVAL
+    assert _ffn(gate=nl(scales=None), up=nl(), down=dn(), T=4, k=2) == moe.MOE_EINVAL
+    assert _ffn(gate=nl(cols=100), up=nl(cols=100), down=nl(rows=100, cols=64), T=4, k=2) == moe.MOE_ELIMIT
+    assert _ffn(gate=nl(), up=nl(), down=dn(), T=4, k=2, aq=1) == moe.MOE_EINVAL     # act_quant: Q8_0 only
+    w = nl()
+    mm = moe.lib.moe_mul_mat_id_workspace_size
+    assert mm(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) > 0
+    assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
+                                  None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
+    assert "IQ4_NL" in moe.last_error()
 
 
 def test_row_ids_validation():

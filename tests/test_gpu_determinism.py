@@ -21,7 +21,8 @@ def _same_bytes(a: torch.Tensor, b: torch.Tensor) -> bool:
                                        ("dec8", moe.PATH_AUTO), ("dec8", moe.PATH_GEMM),
                                        ("skew", moe.PATH_AUTO), ("v3", moe.PATH_AUTO),
                                        ("dec1x", moe.PATH_AUTO), ("dec8x", moe.PATH_AUTO),
-                                       ("ppx", moe.PATH_AUTO)])
+                                       ("ppx", moe.PATH_AUTO), ("dec1n", moe.PATH_AUTO),
+                                       ("dec8n", moe.PATH_AUTO), ("ppn", moe.PATH_AUTO)])
 def test_ffn_ten_runs_bit_identical(name, path):
     inp = synth.make_inputs(name)
     dv = upload_ffn(inp)
