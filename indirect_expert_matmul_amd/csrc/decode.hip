@@ -12,17 +12,19 @@
 // sized for an upper bound on them.
 //   * One wave owns (one distinct expert, a chunk of R rows); R comes from the
 //     kernel's resident-wave count. Each lane takes 16 contiguous int8 of a row per
-//     1024-wide K piece, converts them exactly to fp32 and does fp32 FMAs against the
-//     slot's activations held in registers; the per-block scale multiplies the
-//     16-term partial sum. Lane sums use DPP; lane 63 writes the result.
+//     1024-wide K piece and multiplies them exactly with the slot's activations held in
+//     registers: bf16 activations as packed pairs against exact bf16 weight pairs
+//     (dot2, fp32 accumulate), fp32 ones (the down projection's h) with fp32 FMAs. The
+//     per-block scale multiplies the 16-term partial sum. Lane sums use DPP; lane 63
+//     writes the result.
 //   * One activation row per pass (single-token decode): rows are double-buffered in
 //     registers, which leaves room for two or more waves per SIMD.
 //   * Two per pass: the activations fill the register file, so the rows stream
 //     through a per-wave ring in LDS with direct global-to-LDS copies (the bytes in
 //     flight cost no registers).
 //   * 4-bit experts (MXFP4, IQ4_NL): a lane takes one whole block of 32 codes (16
-//     bytes) per 2048-wide K piece; MXFP4 codes convert in hardware, IQ4_NL codes
-//     through a byte-permute lookup of the 16 levels (iq4nl.h).
+//     bytes) per 2048-wide K piece; MXFP4 codes convert in hardware, IQ4_NL code pairs
+//     through 256-entry tables of level pairs in LDS.
 //   * For larger batches or K a block kernel (4 waves per chunk of rows, activations
 //     staged in LDS) takes over (Q8_0 only).
 //   * Results are written per slot; the fixed-order weighted reduction runs in the
@@ -179,55 +181,99 @@ __device__ __forceinline__ float dot32_fp4_bf16(const i32x4& q, const uint32_t* 
     return s;
 }
 
-// 32 IQ4_NL codes (16 bytes) dotted with 32 floats: the codes become their levels (exact
-// signed bytes, ggml's table), each converted exactly to fp32; the caller multiplies the
-// sum by the block's fp16 scale.
+// IQ4_NL lookup tables in LDS, format constants each block builds at its start
+// (nl_tables_init): for every byte value b (two codes; b & 15 is the even column's) the
+// levels of its two codes as an exact bf16 pair (one dword) and as two fp32. A lane then
+// turns two codes into operands with one LDS read (about two VALU instructions for the
+// address) instead of picking levels out of registers and converting them.
+__shared__ uint32_t nl_tab_bf16[256];
+__shared__ __attribute__((aligned(8))) float nl_tab_f32[512];
+
+__device__ __forceinline__ int nl_level(int c) {
+    const uint32_t w = c < 4 ? kNL0 : (c < 8 ? kNL1 : (c < 12 ? kNL2 : kNL3));
+    return (int8_t)(w >> (8 * (c & 3)));
+}
+
+// Fills the tables (blocks of 256 threads; FMT 2 only) and waits for the whole block.
+template <int FMT>
+__device__ __forceinline__ void nl_tables_init() {
+    if constexpr (FMT == 2) {
+        const int t = threadIdx.x;
+        const float lo = (float)nl_level(t & 15), hi = (float)nl_level(t >> 4);
+        // a level has at most 7 significant bits: the top half of its fp32 form is exact
+        nl_tab_bf16[t] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+        nl_tab_f32[2 * t] = lo;
+        nl_tab_f32[2 * t + 1] = hi;
+        __syncthreads();
+    }
+}
+
+// 32 IQ4_NL codes (16 bytes) dotted with 32 floats, fp32 FMAs on the exact levels; the
+// caller multiplies the sum by the block's fp16 scale.
 __device__ __forceinline__ float dot32_nl(const i32x4& q, const float* x) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; w++) {
-        uint32_t c03, c47;
-        nl_levels8((uint32_t)q[w], c03, c47);
+        const uint32_t u = (uint32_t)q[w];
 #pragma unroll
-        for (int j = 0; j < 4; j++) s = fmaf((float)(int8_t)(c03 >> (8 * j)), x[8 * w + j], s);
-#pragma unroll
-        for (int j = 0; j < 4; j++) s = fmaf((float)(int8_t)(c47 >> (8 * j)), x[8 * w + 4 + j], s);
+        for (int i = 0; i < 4; i++) {
+            const f32x2 v = *(const f32x2*)&nl_tab_f32[2 * ((u >> (8 * i)) & 255u)];
+            s = fmaf(v[0], x[8 * w + 2 * i], s);
+            s = fmaf(v[1], x[8 * w + 2 * i + 1], s);
+        }
     }
     return s;
 }
 
-// Two signed byte levels (bits 0-7 and 8-15 of v) -> an exact bf16 pair (a level has at
-// most 7 significant bits, so the top half of its fp32 form is exact).
-__device__ __forceinline__ uint32_t nl_bf16_pair(uint32_t v) {
-    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(int8_t)v);
-    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)(int8_t)(v >> 8));
-    return __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-}
-
-// 32 IQ4_NL codes dotted with 32 bf16 activations held as 16 packed pairs: each pair of
-// levels becomes an exact bf16 pair for one dot2 instruction (fp32 accumulate).
+// 32 IQ4_NL codes dotted with 32 bf16 activations held as 16 packed pairs: byte j of the
+// codes is columns 2j and 2j+1, whose bf16 level pair meets activation pair j in one dot2
+// instruction (fp32 accumulate).
 __device__ __forceinline__ float dot32_nl_bf16(const i32x4& q, const uint32_t* xv) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; w++) {
-        uint32_t c03, c47;
-        nl_levels8((uint32_t)q[w], c03, c47);
-        const uint32_t p[4] = {nl_bf16_pair(c03), nl_bf16_pair(c03 >> 16), nl_bf16_pair(c47),
-                               nl_bf16_pair(c47 >> 16)};
+        const uint32_t u = (uint32_t)q[w];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[j]),
-                                                __builtin_bit_cast(bf16x2, xv[4 * w + j]), s, false);
+        for (int i = 0; i < 4; i++)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, nl_tab_bf16[(u >> (8 * i)) & 255u]),
+                                                __builtin_bit_cast(bf16x2, xv[4 * w + i]), s, false);
     }
     return s;
 }
 
-// Activations of one lane's piece in registers: 4-bit formats with bf16 activations keep
-// them as packed pairs (VPL / 2 dwords); otherwise VPL exact fp32 values.
+// 16 int8 in q (four dwords) dotted with 16 bf16 activations held as 8 packed pairs:
+// each pair of int8 becomes an exact bf16 pair (two conversions and one pick; |q| <= 127
+// has at most 7 significant bits) for one dot2 instruction, fp32 accumulate.
+__device__ __forceinline__ float dot16_bf16(const i32x4& q, const uint32_t* xv) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const uint32_t u = (uint32_t)q[w];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)(int8_t)(u >> (16 * i)));
+            const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)(int8_t)(u >> (16 * i + 8)));
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(f1, f0, 0x07060302u)),
+                                                __builtin_bit_cast(bf16x2, xv[2 * w + i]), s, false);
+        }
+    }
+    return s;
+}
+
+// bf16 activations of Q8_0 rows kept as packed pairs too (half the registers of fp32
+// copies, so more waves fit a SIMD)
+#ifndef MOE_DEC_Q8_PACKED
+#define MOE_DEC_Q8_PACKED 1
+#endif
+
+// Activations of one lane's piece in registers: bf16 activations are kept as packed
+// pairs (VPL / 2 dwords); fp32 ones (the down projection's h) as VPL values.
 template <int FMT, bool XBF16>
 struct XRegs {
-    static constexpr bool PACKED = FMT != 0 && XBF16;
+    static constexpr bool PACKED = (FMT != 0 || MOE_DEC_Q8_PACKED) && XBF16;
     static constexpr int N = PACKED ? Fmt<FMT>::VPL / 2 : Fmt<FMT>::VPL;
     using T = std::conditional_t<PACKED, uint32_t, float>;
 };
@@ -241,9 +287,12 @@ __device__ __forceinline__ float piece_fma(const i32x4& q, const XT* xv, uint32_
         const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
         if constexpr (PACKED) return fmaf(dd, dot32_nl_bf16(q, xv), acc);
         else return fmaf(dd, dot32_nl(q, xv), acc);
-    } else if constexpr (PACKED) {
+    } else if constexpr (FMT == 1 && PACKED) {
         const float sc = in ? e8m0_to_float(sb & 255u) : 0.f;
         return fmaf(sc, dot32_fp4_bf16(q, xv), acc);
+    } else if constexpr (FMT == 0 && PACKED) {
+        const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
+        return fmaf(dd, dot16_bf16(q, xv), acc);
     } else if constexpr (FMT == 0) {
         const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
         return fmaf(dd, dot16(q, f32x4{xv[0], xv[1], xv[2], xv[3]}, f32x4{xv[4], xv[5], xv[6], xv[7]},
@@ -585,7 +634,7 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
 
     for (int p0 = 0; p0 < cnt; p0 += P) {
         const int pc = min(P, cnt - p0);
-        // activations of this pass's slots, exact fp32
+        // activations of this pass's slots: bf16 ones as packed pairs, fp32 ones as they are
         using XR = XRegs<FMT, XBF16>;
         typename XR::T x[P][NIT][XR::N];
 #pragma unroll
@@ -676,6 +725,7 @@ struct EmitGlobal {
 // One wave per unit, register-staged rows.
 template <int MODE, int P, bool XBF16, int NIT, int FMT>
 __global__ __launch_bounds__(256) void k_decode_wave(DecArgs a) {
+    nl_tables_init<FMT>();
     const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
     bool routed;
     int e, cnt, n_lo, n_hi;
@@ -792,7 +842,7 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
 
     for (int p0 = 0; p0 < cnt; p0 += P) {
         const int pc = min(P, cnt - p0);
-        // activations of this pass's slots, exact fp32
+        // activations of this pass's slots: bf16 ones as packed pairs, fp32 ones as they are
         using XR = XRegs<FMT, XBF16>;
         typename XR::T x[P][NIT][XR::N];
 #pragma unroll
@@ -878,6 +928,7 @@ template <int MODE, int P, bool XBF16, int NIT, int FMT>
 __global__ __launch_bounds__(256, MOE_DEC_MINB) void k_decode_stream(DecArgs a) {
     using G = StreamSlot<MODE, NIT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    nl_tables_init<FMT>();
     const int gw = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));  // global wave
     bool routed;
     int e, cnt, n_lo, n_hi;
@@ -902,6 +953,7 @@ constexpr int kFuseSlots = 64;   // routed slots, and shared (expert, token) pai
 template <int P, bool XBF16, int NIT, bool STREAM, int FMT>
 __global__ __launch_bounds__(256, STREAM ? MOE_DEC_MINB : 1) void k_decode_down_reduce(DecArgs a) {
     using G = StreamSlot<0, NIT>;
+    nl_tables_init<FMT>();
     __shared__ float s_part[kFuseSlots * kFuseRows];   // routed slot s, row r at s*kFuseRows + r
     __shared__ float s_shp[kFuseSlots * kFuseRows];    // shared j, token t at (j*T + t)*kFuseRows + r
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];

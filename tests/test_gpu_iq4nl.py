@@ -52,16 +52,15 @@ def test_ffn_iq4nl_gemv_zero_scales_and_invalid_ids():
     assert normwise(got.cpu().numpy(), oracle.ffn(inp)) <= TOL_FP32
 
 
-@pytest.mark.parametrize("path", [moe.PATH_GEMV, moe.PATH_GEMM])
-@pytest.mark.parametrize("E,k,T,K,N,B_is_k,bad", [
-    (6, 3, 9, 96, 40, False, True),      # one 2048 piece, mostly past K; invalid ids
-    (8, 4, 5, 3008, 70, True, False),    # one src1 row per slot, K in the second piece
-    (6, 3, 50, 96, 45, False, True),     # GEMM: single partial stage, odd N
-    (8, 2, 200, 640, 200, True, False),  # GEMM: one src1 row per slot, ragged last stage
+@pytest.mark.parametrize("path,E,k,T,K,N,B_is_k,bad", [
+    (moe.PATH_GEMV, 6, 3, 9, 96, 40, False, True),     # one 2048 piece, mostly past K; invalid ids
+    (moe.PATH_GEMV, 8, 4, 5, 3008, 70, True, False),   # one src1 row per slot, K in the second piece
+    (moe.PATH_GEMM, 6, 3, 9, 96, 40, False, True),     # the same shapes on the grouped GEMM
+    (moe.PATH_GEMM, 8, 4, 5, 3008, 70, True, False),
+    (moe.PATH_GEMM, 6, 3, 50, 96, 45, False, True),    # single partial stage, odd N
+    (moe.PATH_GEMM, 8, 2, 200, 640, 200, True, False), # one src1 row per slot, ragged last stage
 ])
 def test_iq4nl_mul_mat_id(path, E, k, T, K, N, B_is_k, bad):
-    if path == moe.PATH_GEMV and T * k > 64:
-        pytest.skip("GEMV path bound for 4-bit experts")
     rng = np.random.default_rng(E * 100 + T + K)
     ids = synth.draw_ids_uniform(5, T, E, k)
     if bad:
