@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, Q8_0, MXFP4, IQ4_NL = 0, 1, 2, 3, 4
+F32, BF16, Q8_0, MXFP4, IQ4_NL, IQ4_XS = 0, 1, 2, 3, 4, 5
 _TYPES = {"f32": F32, "bf16": BF16, "q8_0": Q8_0}
 
 
@@ -52,6 +52,8 @@ def lib():
         _lib.oracle_e8m0_to_double.argtypes = [ctypes.c_int]
         _lib.oracle_iq4nl_level.restype = ctypes.c_double
         _lib.oracle_iq4nl_level.argtypes = [ctypes.c_int]
+        _lib.oracle_iq4xs_block_scale.restype = ctypes.c_double
+        _lib.oracle_iq4xs_block_scale.argtypes = [ctypes.c_void_p, ctypes.c_int]
         _lib.oracle_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P]
         _lib.oracle_row_ids.argtypes = [P, I64, I32, I32, I32, P, P, P]
         _lib.oracle_mul_mat_id.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, ctypes.c_int, I32,
@@ -98,18 +100,30 @@ def iq4nl_level(code: int) -> float:
     return lib().oracle_iq4nl_level(int(code))
 
 
+def iq4xs_block_scale(record, j: int) -> float:
+    """Scale of block j (0..7) of one IQ4_XS super-block record (8 bytes)."""
+    r = np.ascontiguousarray(record, dtype=np.uint8)
+    assert r.size == 8
+    return lib().oracle_iq4xs_block_scale(_p(r), int(j))
+
+
 def dequant(qs_or_w, d=None) -> np.ndarray:
     """Dequantize Q8_0 (qs int8 [..][rows][cols], d fp16 [..][rows][cols/32]), MXFP4
     (codes uint8 [..][rows][cols/2], E8M0 scales uint8 [..][rows][cols/32]) or IQ4_NL
-    (codes uint8 [..][rows][cols/2], fp16 scales [..][rows][cols/32]), or widen float32
-    weights, to float64 [..][rows][cols]."""
+    (codes uint8 [..][rows][cols/2], fp16 scales [..][rows][cols/32]), IQ4_XS (codes as
+    IQ4_NL's, super-block records uint8 [..][rows][cols/256][8]), or widen float32 weights,
+    to float64 [..][rows][cols]."""
     a = np.asarray(qs_or_w)
     if d is not None and a.dtype == np.uint8:
         shape = a.shape[:-1] + (2 * a.shape[-1],)
         a3 = _c(a.reshape((-1,) + a.shape[-2:]), np.uint8)
         out = np.empty((a3.shape[0], a3.shape[1], 2 * a3.shape[2]), np.float64)
         d = np.asarray(d)
-        if d.dtype == np.float16:
+        if d.dtype == np.uint8 and d.ndim == a.ndim + 1:   # IQ4_XS super-block records
+            s = _c(d.reshape(a3.shape[0], a3.shape[1], -1), np.uint8)
+            rc = lib().oracle_dequant(IQ4_XS, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2],
+                                      _p(out))
+        elif d.dtype == np.float16:
             s = _c(d.view(np.uint16).reshape(a3.shape[0], a3.shape[1], -1), np.uint16)
             rc = lib().oracle_dequant(IQ4_NL, _p(a3), _p(s), out.shape[0], out.shape[1], out.shape[2],
                                       _p(out))
@@ -149,8 +163,9 @@ def row_ids(ids: np.ndarray, n_experts: int, src1_rows_per_token: int = 1):
 
 
 def _weights(qs_or_w, d):
-    """(type, data, scales, logical shape). 4-bit codes come as uint8; their scales'
-    dtype tells MXFP4 (uint8 E8M0) from IQ4_NL (float16)."""
+    """(type, data, scales, logical shape). 4-bit codes come as uint8; their scales tell
+    MXFP4 (uint8 E8M0, one per 32), IQ4_NL (float16) and IQ4_XS (uint8 records of 8 bytes
+    per 256 columns, one more dimension) apart."""
     if d is None:
         w = _c(qs_or_w, np.float32)
         return F32, w, None, w.shape
@@ -159,6 +174,8 @@ def _weights(qs_or_w, d):
         shape = q.shape[:-1] + (2 * q.shape[-1],)
         if np.asarray(d).dtype == np.float16:
             return IQ4_NL, q, _c(np.asarray(d).view(np.uint16), np.uint16), shape
+        if np.asarray(d).ndim == q.ndim + 1:
+            return IQ4_XS, q, _c(d, np.uint8), shape
         return MXFP4, q, _c(d, np.uint8), shape
     q = _c(qs_or_w, np.int8)
     return Q8_0, q, _c(np.asarray(d).view(np.uint16), np.uint16), q.shape

@@ -31,6 +31,11 @@
  *    not define the format, so it is taken from ggml's definition of IQ4_NL: blocks
  *    of 32 4-bit indices into a fixed non-uniform table of 16 signed integers, one
  *    fp16 scale per block, value = d * table[code]. Exact in float64.
+ *  - Experts may be IQ4_XS (the type of those UD-IQ4_XS models), also from ggml's
+ *    definition: IQ4_NL's codes and levels in super-blocks of 256 weights that share
+ *    one fp16 scale d, each block of 32 carrying a 6-bit sub-scale ls (its low 4 bits
+ *    in a nibble of scales_l, its high 2 bits in scales_h); value = d * (ls - 32) *
+ *    level[code]. Exact in float64.
  *  - The fused MoE FFN applies gate and up projections, SiLU(gate) * up, then the
  *    down projection (section 4.2 names the fused up/gate MoE forward), weights each
  *    routed slot's result by its routing weight and adds always-on shared experts,
@@ -57,6 +62,11 @@
  * 4 = IQ4_NL: codes packed exactly as MXFP4's (a reading: ggml's own block packs the
  * low nibbles of a block's 16 bytes first; only the values are the format's), with
  * fp16 scales d[E][rows][cols/32] as for Q8_0.
+ * 5 = IQ4_XS: codes as IQ4_NL's; per super-block of 256 columns one 8-byte record in
+ * scales[E][rows][cols/256][8]: fp16 d (bytes 0-1), uint16 scales_h (bytes 2-3; bits
+ * 2j, 2j+1 are the high bits of block j's ls), uint8 scales_l[4] (bytes 4-7; byte j/2,
+ * nibble j%2 (low first) holds the low 4 bits of block j's ls), ggml's field order
+ * without the codes. cols % 256 == 0.
  * All entry points return 0 on success and a negative value on bad arguments.
  */
 #include <math.h>
@@ -69,6 +79,7 @@
 #define OR_Q8_0 2
 #define OR_MXFP4 3
 #define OR_IQ4_NL 4
+#define OR_IQ4_XS 5
 
 /* IQ4_NL's 16 levels, index = the 4-bit code: ggml's non-linear table for the type
  * (kvalues_iq4nl in ggml-common.h). */
@@ -122,7 +133,20 @@ double oracle_e8m0_to_double(int x) {
     return ldexp(1.0, (x & 0xff) - 127);
 }
 
-static int is_quant(int type) { return type == OR_Q8_0 || type == OR_MXFP4 || type == OR_IQ4_NL; }
+static int is_quant(int type) {
+    return type == OR_Q8_0 || type == OR_MXFP4 || type == OR_IQ4_NL || type == OR_IQ4_XS;
+}
+/* columns per scale unit of a quantized type (IQ4_XS: its super-block) */
+static int64_t quant_cols(int type) { return type == OR_IQ4_XS ? 256 : 32; }
+
+/* IQ4_XS: the scale of block j (0..7) of one super-block record, as a double. */
+double oracle_iq4xs_block_scale(const uint8_t *rec, int j) {
+    uint16_t d = (uint16_t)(rec[0] | (rec[1] << 8));
+    unsigned sh = (unsigned)(rec[2] | (rec[3] << 8));
+    int lo = (rec[4 + j / 2] >> (4 * (j % 2))) & 15;
+    int hi = (sh >> (2 * j)) & 3;
+    return oracle_half_to_double(d) * (double)((lo | (hi << 4)) - 32);
+}
 
 /* One weight element w(e, n, c) of a stacked matrix, as a double. */
 static double weight_at(int type, const void *data, const void *scales, int64_t rows,
@@ -144,6 +168,13 @@ static double weight_at(int type, const void *data, const void *scales, int64_t 
         uint16_t d = ((const uint16_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
         return oracle_half_to_double(d) * oracle_iq4nl_level(code);
     }
+    if (type == OR_IQ4_XS) {
+        /* codes packed as MXFP4's; value = (block scale) * level */
+        uint8_t b = ((const uint8_t *)data)[(e * rows + n) * (cols / 2) + c / 2];
+        int code = (c & 1) ? (b >> 4) : (b & 15);
+        const uint8_t *rec = (const uint8_t *)scales + ((e * rows + n) * (cols / 256) + c / 256) * 8;
+        return oracle_iq4xs_block_scale(rec, (int)((c % 256) / 32)) * oracle_iq4nl_level(code);
+    }
     /* Q8_0: value = d * q, one fp16 scale per 32 consecutive columns of a row. */
     int8_t q = ((const int8_t *)data)[idx];
     uint16_t d = ((const uint16_t *)scales)[(e * rows + n) * (cols / 32) + c / 32];
@@ -160,7 +191,7 @@ static double act_at(int type, const void *src, int64_t idx) {
 int oracle_dequant(int type, const void *data, const void *scales, int64_t n_mat, int64_t rows,
                    int64_t cols, double *out) {
     if (!data || !out || (type != OR_F32 && !is_quant(type))) return -1;
-    if (is_quant(type) && (!scales || cols % 32)) return -1;
+    if (is_quant(type) && (!scales || cols % quant_cols(type))) return -1;
     for (int64_t e = 0; e < n_mat; e++)
         for (int64_t n = 0; n < rows; n++)
             for (int64_t c = 0; c < cols; c++)
@@ -223,7 +254,7 @@ static void matvec(int type, const void *data, const void *scales, int64_t rows,
         }
         return;
     }
-    if (type == OR_MXFP4 || type == OR_IQ4_NL) {
+    if (type == OR_MXFP4 || type == OR_IQ4_NL || type == OR_IQ4_XS) {
         for (; n < rows; n++) {
             double acc = 0.0;
             for (int64_t c = 0; c < cols; c++) acc += weight_at(type, data, scales, rows, cols, e, n, c) * a[c];
@@ -277,7 +308,7 @@ int oracle_mul_mat_id(int w_type, const void *w_data, const void *w_scales, int6
                       int64_t T, int32_t k, const float *route_w, double *dst) {
     if (!w_data || !src1 || !ids || !dst || E <= 0 || N <= 0 || K <= 0 || T < 0 || k <= 0) return -1;
     if (w_type != OR_F32 && !is_quant(w_type)) return -1;
-    if (is_quant(w_type) && (!w_scales || K % 32)) return -1;
+    if (is_quant(w_type) && (!w_scales || K % quant_cols(w_type))) return -1;
     if (src1_type != OR_F32 && src1_type != OR_BF16) return -1;
     if (B != 1 && B != k) return -1;
     int bad = 0;
@@ -344,10 +375,11 @@ int oracle_ffn(int w_type, const void *g_data, const void *g_scales, const void 
     if (E <= 0 || n_ff <= 0 || n_embd <= 0 || T < 0 || k <= 0 || S < 0) return -1;
     if (w_type != OR_F32 && !is_quant(w_type)) return -1;
     if (x_type != OR_F32 && x_type != OR_BF16) return -1;
-    if (is_quant(w_type) && (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32))
+    if (is_quant(w_type) && (!g_scales || !u_scales || !d_scales || n_embd % quant_cols(w_type) ||
+                              n_ff % quant_cols(w_type)))
         return -1;
     if (S > 0 && (!sg_data || !su_data || !sd_data || n_ff_sh <= 0)) return -1;
-    if (S > 0 && is_quant(w_type) && (!sg_scales || !su_scales || !sd_scales || n_ff_sh % 32))
+    if (S > 0 && is_quant(w_type) && (!sg_scales || !su_scales || !sd_scales || n_ff_sh % quant_cols(w_type)))
         return -1;
     int64_t ffmax = n_ff > n_ff_sh ? n_ff : n_ff_sh;
     int bad = 0;
@@ -532,7 +564,7 @@ int oracle_mul_mat_id_q8act(int w_type, const void *w_data, const void *w_scales
                             double *dst) {
     if (!w_data || !q || !d || !ids || !dst || E <= 0 || N <= 0 || K <= 0 || T < 0 || k <= 0)
         return -1;
-    if (!is_quant(w_type) || !w_scales || K % 32) return -1;
+    if (!is_quant(w_type) || !w_scales || K % quant_cols(w_type)) return -1;
     if (B != 1 && B != k) return -1;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic)
@@ -599,9 +631,10 @@ int oracle_ffn_q8act(int w_type, const void *g_data, const void *g_scales, const
     if (!g_data || !u_data || !d_data || !x || !ids || !route_w || !out) return -1;
     if (E <= 0 || n_ff <= 0 || n_embd <= 0 || T < 0 || k <= 0 || S < 0) return -1;
     if (!is_quant(w_type) || x_type != OR_BF16) return -1;
-    if (!g_scales || !u_scales || !d_scales || n_embd % 32 || n_ff % 32) return -1;
+    const int64_t qc = quant_cols(w_type);
+    if (!g_scales || !u_scales || !d_scales || n_embd % qc || n_ff % qc) return -1;
     if (S > 0 && (!sg_data || !su_data || !sd_data || !sg_scales || !su_scales || !sd_scales ||
-                  n_ff_sh <= 0 || n_ff_sh % 32))
+                  n_ff_sh <= 0 || n_ff_sh % qc))
         return -1;
     int64_t ffmax = n_ff > n_ff_sh ? n_ff : n_ff_sh;
     int bad = 0;

@@ -24,6 +24,10 @@ Storage conventions (row-major, last index contiguous):
   * IQ4_NL weights (the 4-bit codes of the IQ series): ``qs`` uint8 [E][rows][cols // 2]
     packed as MXFP4's, codes uniform over all 16; ``d`` float16 [E][rows][cols // 32]
     drawn as Q8_0's, value = d * level(code) with ggml's 16-level IQ4_NL table.
+  * IQ4_XS weights: codes as IQ4_NL's; ``d`` uint8 [E][rows][cols // 256][8], one record per
+    super-block of 256 columns: fp16 d (bytes 0-1) ~ U(0.5, 1.5) * 1e-4, then six uniform
+    random bytes (scales_h, scales_l[4]: every bit pattern is a valid set of 6-bit
+    sub-scales).
   * bf16 tensors are stored as their uint16 bit patterns (numpy has no bfloat16),
     rounded to nearest-even from float32.
   * ids int32 [T][k]; route_w float32 [T][k], softmax over each token's k picks
@@ -58,7 +62,7 @@ class Config:
     n_embd: int
     n_ff: int
     n_shared: int = 0
-    wtype: str = "q8_0"          # 'q8_0', 'mxfp4', 'iq4_nl' or 'f32'
+    wtype: str = "q8_0"          # 'q8_0', 'mxfp4', 'iq4_nl', 'iq4_xs' or 'f32'
     routing: str = "uniform"     # 'uniform' or 'zipf'
     zipf_s: float = 1.1
     seed: int = 0
@@ -93,6 +97,14 @@ CONFIGS = {
                     desc="GPT-OSS-20B-shaped decode: E32 k4 T8 n_embd=n_ff=2880 IQ4_NL"),
     "ppn": Config("ppn", "ffn", 32, 4, 4096, 2880, 2880, wtype="iq4_nl", seed=7,
                   desc="GPT-OSS-20B-shaped prefill: E32 k4 T4096 n_embd=n_ff=2880 IQ4_NL"),
+    # IQ4_XS experts (super-blocks of 256 columns) on a layer whose widths are multiples of
+    # 256: E128 k8, n_embd 2048, n_ff 768 (the skewed layer's shape, uniform routing).
+    "dec1s": Config("dec1s", "ffn", 128, 8, 1, 2048, 768, wtype="iq4_xs", seed=8,
+                    desc="E128 k8 T1 n_embd2048 n_ff768 decode, IQ4_XS"),
+    "dec8s": Config("dec8s", "ffn", 128, 8, 8, 2048, 768, wtype="iq4_xs", seed=8,
+                    desc="E128 k8 T8 n_embd2048 n_ff768 decode, IQ4_XS"),
+    "pps": Config("pps", "ffn", 128, 8, 4096, 2048, 768, wtype="iq4_xs", seed=9,
+                  desc="E128 k8 T4096 n_embd2048 n_ff768 prefill, IQ4_XS"),
     # Zipf(1.1)-skewed prefill, PP4096.
     "skew": Config("skew", "ffn", 128, 8, 4096, 2048, 768, routing="zipf", seed=4,
                    desc="Skewed prefill: E128 k8 T4096 n_embd2048 n_ff768 Zipf(1.1) Q8_0"),
@@ -195,6 +207,19 @@ def draw_iq4_nl(rng: np.random.Generator, rows: int, cols: int):
     return qs, d
 
 
+def draw_iq4_xs(rng: np.random.Generator, rows: int, cols: int):
+    """One IQ4_XS matrix: packed codes uint8 [rows][cols/2] (two uniform 4-bit codes per
+    byte) and super-block records uint8 [rows][cols/256][8]: fp16 d ~ U(0.5, 1.5) * 1e-4,
+    then six uniform bytes."""
+    if cols % 256:
+        raise ValueError("IQ4_XS needs cols % 256 == 0")
+    qs = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    rec = rng.integers(0, 256, size=(rows, cols // 256, 8), dtype=np.uint8)
+    d = (rng.uniform(0.5, 1.5, size=(rows, cols // 256)) * 1e-4).astype(np.float16)
+    rec[:, :, 0:2] = d.view(np.uint8).reshape(rows, cols // 256, 2)
+    return qs, rec
+
+
 def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
@@ -206,12 +231,18 @@ def draw_q8_0_stack(seed: int, stream: int, which: int, n_mat: int, rows: int, c
     (seed, stream, e, which). ``only`` (optional) lists the matrices to draw; the
     others are left zero (a drawn matrix has the same values either way)."""
     fp4 = wtype == "mxfp4"
-    nib = fp4 or wtype == "iq4_nl"   # two 4-bit codes per byte
+    xs = wtype == "iq4_xs"
+    nib = fp4 or xs or wtype == "iq4_nl"   # two 4-bit codes per byte
     alloc = np.empty if only is None else np.zeros
     qs = qs_out if qs_out is not None else (alloc((n_mat, rows, cols // 2), np.uint8) if nib
                                              else alloc((n_mat, rows, cols), np.int8))
-    d = d_out if d_out is not None else alloc((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
-    draw = draw_mxfp4 if fp4 else (draw_iq4_nl if nib else draw_q8_0)
+    if d_out is not None:
+        d = d_out
+    elif xs:
+        d = alloc((n_mat, rows, cols // 256, 8), np.uint8)
+    else:
+        d = alloc((n_mat, rows, cols // 32), np.uint8 if fp4 else np.float16)
+    draw = draw_mxfp4 if fp4 else (draw_iq4_xs if xs else (draw_iq4_nl if nib else draw_q8_0))
 
     def one(e):
         q, s = draw(_rng(seed, stream, e, which), rows, cols)

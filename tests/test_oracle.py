@@ -6,7 +6,9 @@
     embedded in FP8 E4M3 and decoded by torch, and torch's own E8M0 decoder; IQ4_NL
     (ggml's type, which the pages name as an IQ-series format but do not define): the
     published 16-level table (tests/golden), a hand-worked row, and the reduction of an
-    IQ4_NL product to the Q8_0 product on the same levels;
+    IQ4_NL product to the Q8_0 product on the same levels; IQ4_XS (ggml's super-block
+    packing of those codes): a hand-built record exercising every sub-scale bit, and the
+    reduction of an IQ4_XS product to the IQ4_NL product on its block scales;
   * row-id maps: exhaustive brute force by a stable sort on tiny inputs, numpy's
     stable argsort on random ones, and the invariants of the maps;
   * mul_mat_id: the dense all-experts product (numpy matmul) masked by ids, plain
@@ -197,7 +199,23 @@ def _iq4nl_levels():
     return np.array([float(r[1]) for r in rows])
 
 
+def _numpy_iq4xs_scales(rec):
+    """Per-block scales [..][rows][cols/32] of IQ4_XS records [..][rows][cols/256][8], read
+    field by field: fp16 d, scales_h (2 bits per block), scales_l (a nibble per block)."""
+    d = rec[..., 0:2].copy().view(np.float16)[..., 0].astype(np.float64)
+    sh = rec[..., 2].astype(np.int64) | (rec[..., 3].astype(np.int64) << 8)
+    out = np.empty(rec.shape[:-1] + (8,))
+    for j in range(8):
+        lo = (rec[..., 4 + j // 2] >> (4 * (j % 2))) & 15
+        hi = (sh >> (2 * j)) & 3
+        out[..., j] = d * ((lo | (hi << 4)).astype(np.int64) - 32)
+    return out.reshape(rec.shape[:-2] + (rec.shape[-2] * 8,))
+
+
 def _numpy_dequant(qs, d):
+    if qs.dtype == np.uint8 and d.ndim == qs.ndim + 1:   # IQ4_XS: IQ4_NL codes, super-blocks
+        codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(qs.shape[:-1] + (2 * qs.shape[-1],))
+        return _iq4nl_levels()[codes] * np.repeat(_numpy_iq4xs_scales(d), 32, axis=-1)
     if qs.dtype == np.uint8 and d.dtype == np.float16:   # IQ4_NL: MXFP4 packing, fp16 scale
         codes = np.stack([qs & 15, qs >> 4], axis=-1).reshape(qs.shape[:-1] + (2 * qs.shape[-1],))
         return _iq4nl_levels()[codes] * np.repeat(d.astype(np.float64), 32, axis=-1)
@@ -293,6 +311,47 @@ def test_mul_mat_id_iq4nl_is_q8_0_on_the_levels(B_is_k):
         assert np.array_equal(got, oracle.mul_mat_id(q8, d, x, "bf16", ids, r, B))
     ref = _dense_masked(_numpy_dequant(qs, d), synth.bf16_bits_to_f32(x).astype(np.float64), ids, B)
     assert normwise(oracle.mul_mat_id(qs, d, x, "bf16", ids, None, B), ref) < 1e-13
+
+
+# Hand-built IQ4_XS super-block record: d = 1 (fp16 0x3C00); the 6-bit sub-scales of
+# blocks 0..7 are 0, 1, 31, 32, 33, 47, 48, 63: low nibbles 0 1 15 0 1 15 0 15 (scales_l
+# bytes 0x10 0x0F 0xF1 0xF0, low nibble first) and high bit pairs 0 0 1 2 2 2 3 3 (scales_h
+# = 0xFA90); block scales d * (ls - 32) = -32 -31 -1 0 1 15 16 31.
+_XS_REC = np.array([0x00, 0x3C, 0x90, 0xFA, 0x10, 0x0F, 0xF1, 0xF0], dtype=np.uint8)
+_XS_SCALES = (-32.0, -31.0, -1.0, 0.0, 1.0, 15.0, 16.0, 31.0)
+
+
+def test_iq4xs_block_scales_worked_example():
+    assert tuple(oracle.iq4xs_block_scale(_XS_REC, j) for j in range(8)) == _XS_SCALES
+    # one row of 256 columns: code 8 (level 1) everywhere but block 7, whose bytes are 0xF0
+    # (even columns code 0 = -127, odd columns code 15 = 113)
+    q = np.full((1, 1, 128), 0x88, dtype=np.uint8)
+    q[0, 0, 112:] = 0xF0
+    w = oracle.dequant(q, _XS_REC.reshape(1, 1, 1, 8))[0, 0]
+    for j in range(7):
+        assert np.all(w[32 * j:32 * j + 32] == _XS_SCALES[j])
+    assert np.all(w[224::2] == -127 * 31.0) and np.all(w[225::2] == 113 * 31.0)
+    qs, dd = synth.gen.draw_q8_0_stack(6, 2, 1, 3, 5, 512, wtype="iq4_xs")
+    assert dd.shape == (3, 5, 2, 8) and dd.dtype == np.uint8
+    assert np.array_equal(oracle.dequant(qs, dd), _numpy_dequant(qs, dd))
+
+
+def test_mul_mat_id_iq4xs_is_iq4nl_on_the_block_scales():
+    """With d a power of two (2^-8), every block scale d * (ls - 32) is exact in fp16, so an
+    IQ4_XS matrix is the IQ4_NL matrix with those per-block scales and the same codes: the
+    two oracle products must agree bit for bit."""
+    rng = np.random.default_rng(14)
+    E, N, K, T, k = 4, 12, 512, 6, 2
+    qs, rec = synth.gen.draw_q8_0_stack(11, 2, 0, E, N, K, wtype="iq4_xs")
+    rec[..., 0:2] = np.array([0x00, 0x1C], dtype=np.uint8)   # fp16 0x1C00 = 2^-8
+    nl_d = _numpy_iq4xs_scales(rec).astype(np.float16)
+    assert np.array_equal(nl_d.astype(np.float64), _numpy_iq4xs_scales(rec))
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    rw = synth.draw_route_w(6, T, k)
+    for r in (None, rw):
+        got = oracle.mul_mat_id(qs, rec, x, "bf16", ids, r, 1)
+        assert np.array_equal(got, oracle.mul_mat_id(qs, nl_d, x, "bf16", ids, r, 1))
 
 
 def _dense_masked(W, X, ids, B):
@@ -423,6 +482,13 @@ def test_ffn_mxfp4_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
 def test_ffn_iq4nl_vs_torch_dense_moe(E, k, T, n_embd, n_ff, S):
     inp = synth.make_custom_ffn(41 + E, E, k, T, n_embd, n_ff, S, wtype="iq4_nl")
     assert inp["gate_qs"].dtype == np.uint8 and inp["gate_d"].dtype == np.float16
+    assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
+
+
+@pytest.mark.parametrize("E,k,T,S", [(4, 2, 5, 1), (8, 4, 3, 0)])
+def test_ffn_iq4xs_vs_torch_dense_moe(E, k, T, S):
+    inp = synth.make_custom_ffn(45 + E, E, k, T, 256, 512, S, wtype="iq4_xs")
+    assert inp["gate_d"].shape == (E, 512, 1, 8) and inp["down_d"].shape == (E, 256, 2, 8)
     assert normwise(oracle.ffn(inp), _torch_dense_moe(inp)) < 1e-12
 
 
