@@ -2,7 +2,7 @@
 """Benchmark of the MoE indirect matmul hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config lite|dec1|dec8|skew|v3|dec1x|dec8x|ppx|dec1n|dec8n|ppn|rowids]
+                    [--config lite|dec1|dec8|skew|v3|dec1x|dec8x|ppx|dec1n|dec8n|ppn|dec1s|dec8s|pps|rowids]
 
 A step is one full pass of the hot path -- row ids, gate/up grouped GEMM, down
 grouped GEMM, fixed-order reduce (or the GEMV decode kernels) -- over one batch of
@@ -36,6 +36,7 @@ INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA (the quantized-activation p
 Q8_BYTES = 34.0 / 32.0      # Q8_0: 32 int8 + one fp16 scale per 32 weights
 MXFP4_BYTES = 17.0 / 32.0   # MXFP4: 32 four-bit codes + one E8M0 scale byte per 32 weights
 IQ4NL_BYTES = 18.0 / 32.0   # IQ4_NL: 32 four-bit codes + one fp16 scale per 32 weights
+IQ4XS_BYTES = 136.0 / 256.0  # IQ4_XS: 256 four-bit codes + one 8-byte record per 256 weights
 
 STAGES = {1: ["row_ids", "gemm_gate_up", "gemm_down", "reduce"],
           2: ["gemv_gate_up", "gemv_down", "reduce"],
@@ -85,7 +86,7 @@ def workload_stats(inp, cfg, h_bytes=2):
     rows_routed = int(((ids >= 0) & (ids < E)).sum())
     rows = rows_routed + T * S                      # routed slots + shared-expert rows
     flops = 2.0 * rows * 3 * n_embd * n_ff
-    wb = {"mxfp4": MXFP4_BYTES, "iq4_nl": IQ4NL_BYTES}.get(cfg.wtype, Q8_BYTES)
+    wb = {"mxfp4": MXFP4_BYTES, "iq4_nl": IQ4NL_BYTES, "iq4_xs": IQ4XS_BYTES}.get(cfg.wtype, Q8_BYTES)
     w_gu = (touched + S) * 2 * n_ff * n_embd * wb
     w_dn = (touched + S) * n_embd * n_ff * wb
     x_b = T * n_embd * 2                            # bf16 input

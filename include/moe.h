@@ -29,6 +29,12 @@
  *            plus fp16 scales d[n_mat][rows][cols/32] as Q8_0's, value = d * level(code)
  *            with ggml's 16 IQ4_NL levels (-127 -104 -83 -65 -49 -35 -22 -10 1 13 25
  *            38 53 69 89 113).
+ *            IQ4_XS (ggml's super-block form of those codes): codes as IQ4_NL's, plus one
+ *            8-byte record per 256 columns, uint8 scales[n_mat][rows][cols/256][8] (8-byte
+ *            aligned): fp16 d (bytes 0-1), uint16 scales_h (bytes 2-3), uint8 scales_l[4]
+ *            (bytes 4-7); block j (0..7) of the 256 has the 6-bit sub-scale ls = (nibble
+ *            j%2 of scales_l[j/2], low nibble first) | ((scales_h >> 2j) & 3) << 4, and
+ *            value = d * (ls - 32) * level(code). cols % 256 == 0.
  *   ids      int32 [n_tokens][n_used]; route_w float32 [n_tokens][n_used].
  *   src1     [n_tokens][B][K] with B = src1_rows_per_token in {1, n_used}:
  *            slot s of token t reads row t*B + (s mod B).
@@ -58,7 +64,7 @@
  *
  * Limits (MOE_ELIMIT): n_tokens < 2^22 and n_used < 2^10 (the bounds the page
  * above quotes for safe 32-bit packing, section 2.1), n_tokens * n_used < 2^31,
- * n_experts <= 1024, Q8_0, MXFP4 and IQ4_NL cols % 32 == 0. On the grouped GEMM path the
+ * n_experts <= 1024, Q8_0, MXFP4 and IQ4_NL cols % 32 == 0, IQ4_XS cols % 256 == 0. On the grouped GEMM path the
  * activation tensor whose rows are gathered through the row map (moe_ffn_fused: x;
  * moe_mul_mat_id: src1) must be under 4 GiB, and each GEMM launch must hold fewer
  * than 2^32 work-items; float32 moe_mul_mat_id needs n_tokens * n_used * N < 2^32.
@@ -81,15 +87,16 @@ typedef enum {
     MOE_EHIP = -4        /* a HIP launch failed                                    */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3, MOE_IQ4_NL = 4 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q8_0 = 2, MOE_MXFP4 = 3, MOE_IQ4_NL = 4, MOE_IQ4_XS = 5 } moe_dtype;
 
 /* n_mat stacked matrices of rows x cols. */
 typedef struct {
-    moe_dtype type;     /* MOE_F32, MOE_Q8_0, MOE_MXFP4 or MOE_IQ4_NL            */
+    moe_dtype type;     /* MOE_F32, MOE_Q8_0, MOE_MXFP4, MOE_IQ4_NL, MOE_IQ4_XS  */
     const void *data;   /* F32: float[n_mat][rows][cols]; Q8_0: int8 qs[...];    */
-                        /* MXFP4, IQ4_NL: uint8 codes[n_mat][rows][cols/2]       */
+                        /* MXFP4, IQ4_NL, IQ4_XS: uint8 codes[n_mat][rows][cols/2] */
     const void *scales; /* Q8_0, IQ4_NL: uint16 (fp16) d[n_mat][rows][cols/32];  */
-                        /* MXFP4: uint8 E8M0 x[n_mat][rows][cols/32]; F32: NULL  */
+                        /* MXFP4: uint8 E8M0 x[n_mat][rows][cols/32];            */
+                        /* IQ4_XS: uint8 records[n_mat][rows][cols/256][8]; F32: NULL */
     int64_t n_mat, rows, cols;
 } moe_weights;
 
@@ -141,8 +148,8 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
 /*
  * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
  *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
- *            src1), (MXFP4 w, BF16 src1) or (IQ4_NL w, BF16 src1) on the MFMA grouped
- *            GEMM or the GEMV path (MXFP4 and IQ4_NL on the GEMV path: n_tokens *
+ *            src1), (MXFP4, IQ4_NL or IQ4_XS w, BF16 src1) on the MFMA grouped
+ *            GEMM or the GEMV path (the 4-bit types on the GEMV path: n_tokens *
  *            n_used <= 64 and K <= 4096, else the GEMM path is taken, and forcing the
  *            GEMV path is MOE_EINVAL); (F32 w, F32
  *            src1), which has one path, the fp32 grouped product: opt->path must be
@@ -170,7 +177,7 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
  *            e = ids[t][s];  then + sum_{j ascending} Sd_j (silu(Sg_j x_t) * (Su_j x_t)).
  *   gate, up  Q8_0 [n_experts][n_ff][n_embd]; down Q8_0 [n_experts][n_embd][n_ff]
  *   sh_gate, sh_up Q8_0 [S][n_ff_sh][n_embd]; sh_down Q8_0 [S][n_embd][n_ff_sh];
- *             or all of them MXFP4, or all IQ4_NL (their GEMV path needs n_tokens *
+ *             or all of them MXFP4, all IQ4_NL or all IQ4_XS (their GEMV path needs n_tokens *
  *             n_used <= 64 and n_embd, n_ff, n_ff_sh <= 4096; larger calls take the
  *             grouped GEMM);
  *             all three NULL (or n_mat == 0) = no shared experts; giving only some of
@@ -178,7 +185,7 @@ moe_status moe_mul_mat_id(const moe_weights *w, const void *src1, moe_dtype src1
  *   x         device BF16 [n_tokens][n_embd]; ids, route_w as above.
  *   out       device float32 [n_tokens][n_embd] (overwritten).
  * silu(z) = z / (1 + exp(-z)). Intermediates: GEMM path -- bf16 weights (Q8_0: d*q
- * rounded to nearest-even; MXFP4: exact; IQ4_NL: d*level rounded to nearest-even), bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
+ * rounded to nearest-even; MXFP4: exact; IQ4_NL, IQ4_XS: scale*level rounded to nearest-even), bf16 activations, fp32 accumulate, bf16 SiLU*up, fp32 down
  * results; GEMV path -- weights exact, fp32 accumulate throughout.
  */
 moe_status moe_ffn_fused(const moe_weights *gate, const moe_weights *up, const moe_weights *down,

@@ -22,7 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ELIMIT, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_Q8_0, MOE_MXFP4, MOE_IQ4_NL = 0, 1, 2, 3, 4
+MOE_F32, MOE_BF16, MOE_Q8_0, MOE_MXFP4, MOE_IQ4_NL, MOE_IQ4_XS = 0, 1, 2, 3, 4, 5
 PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 
 # Every symbol include/moe.h declares.
@@ -113,8 +113,9 @@ class Weights:
     ``scales`` float16 (or its uint16 bits) [n_mat][rows][cols/32]; MXFP4: ``data`` uint8
     [n_mat][rows][cols/2] (two E2M1 codes per byte, even column in the low nibble) and
     ``scales`` uint8 E8M0 [n_mat][rows][cols/32]; IQ4_NL: ``data`` uint8 codes packed as
-    MXFP4's and ``scales`` float16 (or its 16 bits) [n_mat][rows][cols/32]; F32: ``data``
-    float32 [n_mat][rows][cols] and ``scales`` None."""
+    MXFP4's and ``scales`` float16 (or its 16 bits) [n_mat][rows][cols/32]; IQ4_XS: ``data``
+    as IQ4_NL's and ``scales`` uint8 super-block records [n_mat][rows][cols/256][8]; F32:
+    ``data`` float32 [n_mat][rows][cols] and ``scales`` None."""
     data: torch.Tensor
     scales: Optional[torch.Tensor] = None
 
@@ -123,12 +124,14 @@ class Weights:
         if self.scales is None:
             return MOE_F32
         if self.data.dtype == torch.uint8:
-            return MOE_MXFP4 if self.scales.element_size() == 1 else MOE_IQ4_NL
+            if self.scales.element_size() != 1:
+                return MOE_IQ4_NL
+            return MOE_IQ4_XS if self.scales.dim() == 4 else MOE_MXFP4
         return MOE_Q8_0
 
     @property
     def cols(self) -> int:
-        return self.data.shape[2] * (2 if self.type in (MOE_MXFP4, MOE_IQ4_NL) else 1)
+        return self.data.shape[2] * (2 if self.type in (MOE_MXFP4, MOE_IQ4_NL, MOE_IQ4_XS) else 1)
 
     def c(self) -> c_moe_weights:
         d = self.data
@@ -140,8 +143,12 @@ class Weights:
         else:
             if d.dtype == torch.uint8:
                 if self.scales.dtype != torch.uint8 and self.scales.element_size() != 2:
-                    raise ValueError("4-bit weights: uint8 codes with uint8 E8M0 (MXFP4) or 16-bit "
-                                     "fp16 (IQ4_NL) scales")
+                    raise ValueError("4-bit weights: uint8 codes with uint8 E8M0 (MXFP4), 16-bit "
+                                     "fp16 (IQ4_NL) scales or uint8 super-block records (IQ4_XS)")
+                if self.scales.dim() == 4 and (self.scales.dtype != torch.uint8 or
+                                               tuple(self.scales.shape) != (d.shape[0], d.shape[1],
+                                                                            2 * d.shape[2] // 256, 8)):
+                    raise ValueError("IQ4_XS records must be uint8 [n_mat][rows][cols/256][8]")
             elif d.dtype != torch.int8 or self.scales.element_size() != 2:
                 raise ValueError("Q8_0 weights: int8 qs with 16-bit scales")
             if not self.scales.is_contiguous():
@@ -410,8 +417,8 @@ def moe_ffn_fused_noalloc(gate: Weights, up: Weights, down: Weights, x: torch.Te
 
 def weights_from_numpy(qs_or_w, d=None, device="cuda") -> Weights:
     """Upload numpy weights (from ``synth``) as a Weights pair: float32; Q8_0 (int8 qs,
-    fp16 scales); MXFP4 (uint8 codes, uint8 E8M0 scales); or IQ4_NL (uint8 codes, fp16
-    scales)."""
+    fp16 scales); MXFP4 (uint8 codes, uint8 E8M0 scales); IQ4_NL (uint8 codes, fp16
+    scales); or IQ4_XS (uint8 codes, uint8 records [..][cols/256][8])."""
     import numpy as np
     if d is None:
         return Weights(torch.from_numpy(np.ascontiguousarray(qs_or_w, dtype=np.float32)).to(device))

@@ -22,9 +22,9 @@
 //   * Two per pass: the activations fill the register file, so the rows stream
 //     through a per-wave ring in LDS with direct global-to-LDS copies (the bytes in
 //     flight cost no registers).
-//   * 4-bit experts (MXFP4, IQ4_NL): a lane takes one whole block of 32 codes (16
-//     bytes) per 2048-wide K piece; MXFP4 codes convert in hardware, IQ4_NL code pairs
-//     through 256-entry tables of level pairs in LDS.
+//   * 4-bit experts (MXFP4, IQ4_NL, IQ4_XS): a lane takes one whole block of 32 codes (16
+//     bytes) per 2048-wide K piece; MXFP4 codes convert in hardware, IQ4_NL / IQ4_XS code
+//     pairs through 256-entry tables of level pairs in LDS.
 //   * For larger batches or K a block kernel (4 waves per chunk of rows, activations
 //     staged in LDS) takes over (Q8_0 only).
 //   * Results are written per slot; the fixed-order weighted reduction runs in the
@@ -126,6 +126,20 @@ template <> struct Fmt<1> {   // MXFP4: two E2M1 codes per byte (even column low
 template <> struct Fmt<2> {   // IQ4_NL: two codes per byte (even column low), one fp16 scale per 32
     static constexpr int VPL = 32, PIECE = 2048, SB = 2;
 };
+// IQ4_XS: IQ4_NL's codes; per 256 columns one 8-byte record (fp16 d, scales_h, scales_l[4]),
+// i.e. one scale byte per 32 columns. Lane l's block is block l % 8 of its super-block.
+template <> struct Fmt<3> {
+    static constexpr int VPL = 32, PIECE = 2048, SB = 1;
+};
+
+// IQ4_XS: the scale of block j (0..7) of a super-block from its 8-byte record r (bytes
+// 0-1 fp16 d, 2-3 scales_h with block j's high sub-scale bits at 2j, 4-7 scales_l with its
+// low four at 4j): d * (ls - 32), exact in fp32.
+__device__ __forceinline__ float iq4xs_scale(uint64_t r, int j) {
+    const uint32_t lo = (uint32_t)(r >> (32 + 4 * j)) & 15u;
+    const uint32_t hi = (uint32_t)(r >> (16 + 2 * j)) & 3u;
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)r) * (float)((int)(lo | (hi << 4)) - 32);
+}
 
 // E8M0 scale byte -> 2^(x - 127) (x = 0 is the subnormal 2^-127; x = 255 is NaN).
 __device__ __forceinline__ float e8m0_to_float(uint32_t x) {
@@ -194,10 +208,10 @@ __device__ __forceinline__ int nl_level(int c) {
     return (int8_t)(w >> (8 * (c & 3)));
 }
 
-// Fills the tables (blocks of 256 threads; FMT 2 only) and waits for the whole block.
+// Fills the tables (blocks of 256 threads; IQ4_NL and IQ4_XS only) and waits for the whole block.
 template <int FMT>
 __device__ __forceinline__ void nl_tables_init() {
-    if constexpr (FMT == 2) {
+    if constexpr (FMT == 2 || FMT == 3) {
         const int t = threadIdx.x;
         const float lo = (float)nl_level(t & 15), hi = (float)nl_level(t >> 4);
         // a level has at most 7 significant bits: the top half of its fp32 form is exact
@@ -280,11 +294,12 @@ struct XRegs {
 
 // One lane's share of a row piece: acc + scale * (codes q . activations xv), with one
 // rounding for the scaling add (fma). sb holds the raw scale bits (fp16 for Q8_0, E8M0
-// for MXFP4, fp16 for IQ4_NL); pieces past K get a zero scale.
+// for MXFP4, fp16 for IQ4_NL, the super-block record for IQ4_XS); pieces past K get a zero
+// scale.
 template <int FMT, bool PACKED, class XT>
-__device__ __forceinline__ float piece_fma(const i32x4& q, const XT* xv, uint32_t sb, bool in, float acc) {
-    if constexpr (FMT == 2) {
-        const float dd = in ? half_bits_to_float((uint16_t)sb) : 0.f;
+__device__ __forceinline__ float piece_fma(const i32x4& q, const XT* xv, uint64_t sb, bool in, float acc) {
+    if constexpr (FMT == 2 || FMT == 3) {
+        const float dd = in ? (FMT == 2 ? half_bits_to_float((uint16_t)sb) : iq4xs_scale(sb, threadIdx.x & 7)) : 0.f;
         if constexpr (PACKED) return fmaf(dd, dot32_nl_bf16(q, xv), acc);
         else return fmaf(dd, dot32_nl(q, xv), acc);
     } else if constexpr (FMT == 1 && PACKED) {
@@ -614,7 +629,7 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
     // one weight row (pair): NIT 16-byte pieces per matrix and their scales
     struct Row {
         i32x4 q[M][NIT];
-        uint32_t d[M][NIT];
+        std::conditional_t<FMT == 3, uint64_t, uint32_t> d[M][NIT];
     };
     auto load_row = [&](int n, Row& w) {
 #pragma unroll
@@ -626,7 +641,8 @@ __device__ __forceinline__ void unit_regs(const DecArgs& a, bool routed, int e, 
                 const i32x4* qp = (const i32x4*)(qr + kc[i] * 16 / F::VPL);
                 if constexpr (kDecWeightsNT) w.q[m][i] = __builtin_nontemporal_load(qp);
                 else w.q[m][i] = *qp;
-                if constexpr (FMT != 1) w.d[m][i] = *(const uint16_t*)(dr + 2 * (kc[i] >> 5));
+                if constexpr (FMT == 3) w.d[m][i] = *(const uint64_t*)(dr + 8 * (kc[i] >> 8));
+                else if constexpr (FMT != 1) w.d[m][i] = *(const uint16_t*)(dr + 2 * (kc[i] >> 5));
                 else w.d[m][i] = dr[kc[i] >> 5];
             }
         }
@@ -894,8 +910,9 @@ __device__ __forceinline__ void unit_stream(const DecArgs& a, bool routed, int e
                     const uint8_t* mp = sl + m * MAT;
                     const int s0 = (int)((uintptr_t)((m == 0 ? d1 : d2) + (int64_t)n * KB * F::SB) & 3);
                     const i32x4 q = *(const i32x4*)(mp + (i << 10) + (lane << 4));
-                    const uint8_t* sp = mp + NIT * 1024 + s0 + F::SB * (kc[i] >> 5);
-                    const uint32_t sb = FMT != 1 ? (uint32_t)*(const uint16_t*)sp : (uint32_t)*sp;
+                    const uint8_t* sp = mp + NIT * 1024 + s0 + (FMT == 3 ? 8 * (kc[i] >> 8) : F::SB * (kc[i] >> 5));
+                    const uint64_t sb = FMT == 3 ? *(const uint64_t*)sp
+                                                 : (FMT != 1 ? (uint64_t)*(const uint16_t*)sp : (uint64_t)*sp);
 #pragma unroll
                     for (int p = 0; p < P; p++)   // lanes past K add 0 through a zero scale
                         acc[m][p] = piece_fma<FMT, XR::PACKED>(q, x[p][i], sb, kin[i], acc[m][p]);
@@ -1154,10 +1171,11 @@ hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced) {
         if (same_type) {
             if (reduced) *reduced = fuse;
             if (a.rw.fmt == 2) return launch_wave_fmt<2>(a, slots, fuse, st);
+            if (a.rw.fmt == 3) return launch_wave_fmt<3>(a, slots, fuse, st);
             return a.rw.fmt == 1 ? launch_wave_fmt<1>(a, slots, fuse, st) : launch_wave_fmt<0>(a, slots, fuse, st);
         }
     }
-    if (a.rw.fmt != 0) return hipErrorInvalidValue;   // MXFP4, IQ4_NL: the wave kernels only
+    if (a.rw.fmt != 0) return hipErrorInvalidValue;   // MXFP4, IQ4_NL, IQ4_XS: the wave kernels only
     const int nb_r = a.d_max * ((a.rw.N + kR - 1) / kR);
     const int nb_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + kR - 1) / kR) : 0;
     const int grid = nb_r + nb_s;

@@ -122,6 +122,8 @@ constexpr int kMChunk = MOE_GEMM_MCHUNK;   // M tiles sharing each weight slab i
 // FMT = 1: MXFP4 experts (64-byte weight rows per stage, E8M0 scale bytes, SG = 1).
 // FMT = 2: IQ4_NL experts (the same 64-byte rows of 4-bit codes, fp16 scales, SG = 1):
 // the codes become their levels (signed bytes) and then take the Q8_0 dequant.
+// FMT = 3: IQ4_XS experts (IQ4_NL's codes; a stage is half of a 256-column super-block,
+// whose 8-byte record of scales comes as two words per row; K % 256 == 0, two slots).
 template <int MSUB, int MODE, int W, int NS, int SG, int FMT>
 __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int BM = 32 * MSUB;
@@ -130,6 +132,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     constexpr int WROW = FMT != 0 ? 64 : 128;    // weight bytes per row per stage
     constexpr int B_BYTES = W * 32 * WROW;
     static_assert(FMT == 0 || SG == 1, "4-bit formats' scales come one word per block per stage");
+    static_assert(FMT != 3 || NS == 2, "IQ4_XS: a stage's half of the super-block follows from s % 2");
     constexpr int S_BYTES = SG == 1 ? W * 32 * 16 : 0;
     constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     constexpr int SGROUP = W * 32 * 32;          // SG = 4: one group, 32 bytes per row
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     }
     // scales: copy t covers local rows 16t..16t+15, lane -> (row 16t + lane/4, block
     // lane%4 of the stage); the copy fetches the aligned word holding that fp16
-    constexpr int SB = FMT == 1 ? 1 : 2;          // scale bytes per block
+    constexpr int SB = (FMT == 1 || FMT == 3) ? 1 : 2;   // scale bytes per block
     const uint8_t* s_base1 = (const uint8_t*)uniform_ptr((const uint8_t*)P.d1 + (int64_t)e * N * KB * SB);
     const uint8_t* s_base2 =
         MODE == 1 ? (const uint8_t*)uniform_ptr((const uint8_t*)P.d2 + (int64_t)e * N * KB * SB) : s_base1;
@@ -281,6 +284,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
     for (int t = 0; t < 2; t++) {
         s_row[t] = wrow(16 * t + (lane >> 2));
         s_word[t] = (uint32_t)(((int64_t)s_row[t] * KB + s_blk) * SB) & ~3u;
+        // IQ4_XS: word s_blk & 1 of the super-block record (stage s adds 8 * (s / 2) bytes)
+        if constexpr (FMT == 3) s_word[t] = (uint32_t)((int64_t)s_row[t] * KB + 4 * (s_blk & 1));
     }
     // SG = 4: lane l fetches 16 bytes (half l&1 of the group's 32) of local row l>>1,
     // from the row's own tensor (gate and up rows sit in different tensors)
@@ -310,7 +315,8 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             if (SG == 1) {
 #pragma unroll
                 for (int t = 0; t < 2; t++)
-                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, s_word[t] + 4 * SB * s,
+                    dma4((MODE == 1 && t == 1) ? s_base2 : s_base1,
+                         s_word[t] + (FMT == 3 ? 8 * (s >> 1) : 4 * SB * s),
                          st + A_BYTES + B_BYTES + wv * 512 + t * 256);
             } else if ((s & 3) == 0) {
                 dma16v(sg_ptr + 8 * s, sring + (uint32_t)(((s >> 2) & 1) * SGROUP) + wv * 1024);
@@ -328,10 +334,10 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 dma16_w(w_once, ((MODE == 1 && i >= NB / 2) ? b_base2 : b_base1) + k0 * WROW / 128, b_off[i] - adj,
                         st + A_BYTES + wv * 32 * WROW + i * 1024);
             }
-            if (SG == 1) {   // (SG = 4 needs K % 512 == 0: no partial stage)
+            if (SG == 1) {   // (SG = 4 needs K % 512 == 0, IQ4_XS K % 256 == 0: no partial stage)
 #pragma unroll
                 for (int t = 0; t < 2; t++) {
-                    const int blk = min(4 * s + s_blk, KB - 1);
+                    const int blk = FMT == 3 ? 0 : min(4 * s + s_blk, KB - 1);
                     const uint32_t byte = (uint32_t)(((int64_t)s_row[t] * KB + blk) * SB);
                     dma4((MODE == 1 && t == 1) ? s_base2 : s_base1, byte & ~3u,
                          st + A_BYTES + B_BYTES + wv * 512 + t * 256);
@@ -400,6 +406,16 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 const uint32_t sw = *(const uint32_t*)(st + s_rd + (2 * u + h) * 4);
                 d[u] = half_bits_to_float((uint16_t)(sw >> s_sh[u]));
                 if constexpr (CHECK_K) d[u] = (k0 + 64 * u + 32 * h < K) ? d[u] : 0.f;
+            } else if constexpr (FMT == 3) {
+                // the codes as for IQ4_NL; block j = 4 (s % 2) + 2u + h of the super-block:
+                // d * (ls - 32), ls's low four bits at bit 4j of scales_l (word 1), its high
+                // two at bit 16 + 2j of word 0 (after the fp16 d)
+                q[u][0] = *(const i32x4*)(st + b_rd + (((2 * u + h) ^ swz_b4(lrow)) << 4));
+                const uint32_t w0 = *(const uint32_t*)(st + s_rd);
+                const uint32_t w1 = *(const uint32_t*)(st + s_rd + 4);
+                const int j = 4 * (s & 1) + 2 * u + h;
+                const uint32_t ls = ((w1 >> (4 * j)) & 15u) | (((w0 >> (16 + 2 * j)) & 3u) << 4);
+                d[u] = half_bits_to_float((uint16_t)w0) * (float)((int)ls - 32);
             } else {
                 q[u][0] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h) ^ swz_b(lrow)) << 4));
                 q[u][1] = *(const i32x4*)(st + b_rd + (((4 * u + 2 * h + 1) ^ swz_b(lrow)) << 4));
@@ -419,7 +435,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
         // the compiler issues all of a stage's dequant work before its MFMAs)
         auto deq = [&](int t) -> bf16x8 {
             if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[t >> 2][0][t & 3], d[t >> 2]);
-            if constexpr (FMT == 2) {
+            if constexpr (FMT == 2 || FMT == 3) {
                 uint32_t c03, c47;
                 nl_levels8((uint32_t)q[t >> 2][0][t & 3], c03, c47);
                 return dequant8((int)c03, (int)c47, d[t >> 2]);
@@ -452,7 +468,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
                 acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur], acc[i], 0, 0, 0);
 #ifndef MOE_GEMM_NO_SCHED
             if (t < 7) {
-                constexpr int VPM = ((FMT == 1 ? 4 : FMT == 2 ? 36 : 20) + MSUB - 1) / MSUB;   // dequant VALU per MFMA
+                constexpr int VPM = ((FMT == 1 ? 4 : FMT >= 2 ? 36 : 20) + MSUB - 1) / MSUB;   // dequant VALU per MFMA
 #pragma unroll
                 for (int m = 0; m < MSUB; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1093,7 +1109,8 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 int gemm_tile_x(int msub, int fmt, int64_t K, bool scales_aligned) {
     // MXFP4 takes the wide kernel only with its scale rows at even addresses, IQ4_NL
     // only with its scale tensors 4-byte aligned
-    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && (fmt == 0 || scales_aligned)) ? 32 : 0;
+    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && fmt != 3 && (fmt == 0 || scales_aligned))
+               ? 32 : 0;
 }
 #ifndef MOE_GEMM_TILE160
 #define MOE_GEMM_TILE160 0   // 1: the 160-row kernel runs 160-row tiles instead of 128 + 32
@@ -1131,7 +1148,7 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
         tall = tall || p.tile_x != 0 || p.tile_m == 160;
     }
     if (tall) {
-        if (msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        if (msub != 4 || !wide_ok || a.fmt == 3) return hipErrorInvalidValue;
         if (a.fmt == 2) {
             if (!scales_aligned(a, 3)) return hipErrorInvalidValue;
             return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2, 2>(a, st);
@@ -1143,6 +1160,15 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
             return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2>(a, st);
         }
         return a.mode == 1 ? launch_wide<1, 5, 4, 2>(a, st) : launch_wide<0, 5, 4, 2>(a, st);
+    }
+    if (a.fmt == 3) {   // IQ4_XS experts: the narrow kernel with two slots
+        switch (msub) {
+            case 2:
+                if (narrow_grid<8>(a) >= 2048) return launch_cfg_fp4<2, 8, 2, 3>(a, st);
+                return launch_cfg_fp4<2, 4, 2, 3>(a, st);
+            case 4: return launch_cfg_fp4<4, 8, 2, 3>(a, st);
+            default: return hipErrorInvalidValue;
+        }
     }
     if (a.fmt == 2) {   // IQ4_NL experts: MXFP4's launch shapes
         switch (msub) {

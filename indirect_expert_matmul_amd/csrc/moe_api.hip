@@ -91,17 +91,27 @@ moe_status check_weights(const moe_weights* w, const char* name, bool allow_f32)
         return fail(MOE_EINVAL, "%s: sizes must be > 0", name);
     if (w->rows > INT32_MAX || w->cols > INT32_MAX)
         return fail(MOE_ELIMIT, "%s: rows and cols must fit in int32", name);
-    if (w->type == MOE_Q8_0 || w->type == MOE_MXFP4 || w->type == MOE_IQ4_NL) {
-        const char* fmt = w->type == MOE_Q8_0 ? "Q8_0" : w->type == MOE_MXFP4 ? "MXFP4" : "IQ4_NL";
+    if (w->type == MOE_Q8_0 || w->type == MOE_MXFP4 || w->type == MOE_IQ4_NL || w->type == MOE_IQ4_XS) {
+        const char* fmt = w->type == MOE_Q8_0 ? "Q8_0"
+                          : w->type == MOE_MXFP4 ? "MXFP4" : w->type == MOE_IQ4_NL ? "IQ4_NL" : "IQ4_XS";
+        const int64_t unit = w->type == MOE_IQ4_XS ? 256 : 32;   // columns per scale unit
         if (!w->scales) return fail(MOE_EINVAL, "%s: %s scales are NULL", name, fmt);
-        if (w->cols % 32)
-            return fail(MOE_ELIMIT, "%s: %s needs cols %% 32 == 0 (got %lld)", name, fmt, (long long)w->cols);
+        if (w->cols % unit)
+            return fail(MOE_ELIMIT, "%s: %s needs cols %% %lld == 0 (got %lld)", name, fmt, (long long)unit,
+                        (long long)w->cols);
+        if (w->type == MOE_IQ4_XS && ((uintptr_t)w->scales & 7))
+            return fail(MOE_EINVAL, "%s: IQ4_XS super-block records must be 8-byte aligned", name);
     } else if (w->type == MOE_F32) {
         if (!allow_f32) return fail(MOE_EINVAL, "%s: float32 weights are not supported here", name);
     } else {
         return fail(MOE_EINVAL, "%s: unsupported weight type %d", name, (int)w->type);
     }
     return MOE_OK;
+}
+
+// Weight format code of the kernels: 0 Q8_0, 1 MXFP4, 2 IQ4_NL, 3 IQ4_XS.
+int32_t kernel_fmt(moe_dtype t) {
+    return t == MOE_MXFP4 ? 1 : t == MOE_IQ4_NL ? 2 : t == MOE_IQ4_XS ? 3 : 0;
 }
 
 float tau_of(const moe_options* o) { return (o && o->tau > 0.f) ? o->tau : 1.0f; }
@@ -130,7 +140,7 @@ int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4
     if (force == 1) return 1;
     if (force == 2) {
         if (!dec_ok)
-            return fail(MOE_EINVAL, "GEMV path with 4-bit (MXFP4, IQ4_NL) experts needs n_tokens*n_used <= 64 "
+            return fail(MOE_EINVAL, "GEMV path with 4-bit (MXFP4, IQ4_NL, IQ4_XS) experts needs n_tokens*n_used <= 64 "
                         "and widths <= 4096");
         return 2;
     }
@@ -144,7 +154,9 @@ int select_path_aq(int64_t T, int32_t k, int32_t E, int64_t act_width, int32_t w
                    const moe_options* o) {
     const int32_t aq = o ? o->act_quant : 0;
     if (aq != 0 && aq != 1) return fail(MOE_EINVAL, "options.act_quant must be 0 or 1 (got %d)", aq);
-    if (!aq) return select_path_fmt(T, k, E, act_width, wtype == MOE_MXFP4 || wtype == MOE_IQ4_NL, o);
+    if (!aq)
+        return select_path_fmt(T, k, E, act_width,
+                               wtype == MOE_MXFP4 || wtype == MOE_IQ4_NL || wtype == MOE_IQ4_XS, o);
     if (wtype != MOE_Q8_0) return fail(MOE_EINVAL, "quantized activations (act_quant = 1) need Q8_0 experts");
     if (o->path != 0 && o->path != 1)
         return fail(MOE_EINVAL, "quantized activations run on the grouped GEMM only: options.path must "
@@ -183,7 +195,7 @@ RowIdsPlan carve_row_ids(Carve& c, int64_t n, int32_t E, bool maps, int tile_m) 
 struct FfnDims {
     int64_t T;
     int32_t k, E, n_embd, n_ff, S, n_ff_sh;
-    int32_t fmt;   // kernel weight format: 0 Q8_0, 1 MXFP4, 2 IQ4_NL
+    int32_t fmt;   // kernel weight format: 0 Q8_0, 1 MXFP4, 2 IQ4_NL, 3 IQ4_XS
 };
 
 struct FfnPlan {
@@ -270,7 +282,7 @@ moe_status validate_ffn(const moe_weights* gate, const moe_weights* up, const mo
     d->E = (int32_t)gate->n_mat;
     d->n_ff = (int32_t)gate->rows;
     d->n_embd = (int32_t)gate->cols;
-    d->fmt = gate->type == MOE_MXFP4 ? 1 : gate->type == MOE_IQ4_NL ? 2 : 0;
+    d->fmt = kernel_fmt(gate->type);
     const bool any_sh = (sg && sg->n_mat) || (su && su->n_mat) || (sd && sd->n_mat);
     d->S = 0;
     d->n_ff_sh = 0;
@@ -307,6 +319,7 @@ moe_status validate_mmid(const moe_weights* w, moe_dtype st, int32_t B, int64_t 
     if (w->type == MOE_Q8_0 && st != MOE_BF16) return fail(MOE_EINVAL, "Q8_0 weights need BF16 src1");
     if (w->type == MOE_MXFP4 && st != MOE_BF16) return fail(MOE_EINVAL, "MXFP4 weights need BF16 src1");
     if (w->type == MOE_IQ4_NL && st != MOE_BF16) return fail(MOE_EINVAL, "IQ4_NL weights need BF16 src1");
+    if (w->type == MOE_IQ4_XS && st != MOE_BF16) return fail(MOE_EINVAL, "IQ4_XS weights need BF16 src1");
     if (w->type == MOE_F32 && st != MOE_F32) return fail(MOE_EINVAL, "F32 weights need F32 src1");
     return MOE_OK;
 }
@@ -874,7 +887,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             ra.tile_tab[0] = p.r.tile_tab;
             ra.tile_cap[0] = p.r.tile_cap;
             g.mode = 0;
-            g.fmt = w->type == MOE_MXFP4 ? 1 : w->type == MOE_IQ4_NL ? 2 : 0;
+            g.fmt = kernel_fmt(w->type);
             g.n_prob = 1;
             GemmProblem& r = g.p[0];
             r.qs1 = (const int8_t*)w->data;
@@ -928,7 +941,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
         a.k = k;
         a.E = E;
         a.rw = DecWeights{(const int8_t*)w->data, (const uint16_t*)w->scales, nullptr, nullptr, E, N, K,
-                          w->type == MOE_MXFP4 ? 1 : w->type == MOE_IQ4_NL ? 2 : 0};
+                          kernel_fmt(w->type)};
         a.act = src1;
         a.act_type = 1;
         a.act_B = B;

@@ -138,7 +138,8 @@ struct GemmArgs {
     int32_t grid_real;        // blocks carrying tiles (before padding to a multiple of 8)
     // 0: Q8_0 experts; 1: MXFP4 -- qs1/qs2 hold two E2M1 codes per byte ([n_mat][N][K/2],
     // even column in the low nibble), d1/d2 the E8M0 scale bytes ([n_mat][N][K/32]);
-    // 2: IQ4_NL -- codes packed as MXFP4's, d1/d2 fp16 scales as Q8_0's
+    // 2: IQ4_NL -- codes packed as MXFP4's, d1/d2 fp16 scales as Q8_0's; 3: IQ4_XS --
+    // codes as IQ4_NL's, d1/d2 8-byte super-block records ([n_mat][N][K/256][8])
     int32_t fmt;
 };
 // Block tile height for a given average rows-per-expert (host heuristic).
@@ -208,7 +209,7 @@ struct DecWeights {
     // 0: Q8_0 (int8 codes, fp16 scales); 1: MXFP4 -- qs holds two E2M1 codes per byte
     // ([n_mat][N][K/2], even column in the low nibble) and d the E8M0 scale bytes
     // ([n_mat][N][K/32]); the pointers are read as bytes; 2: IQ4_NL -- codes as MXFP4's,
-    // fp16 scales as Q8_0's
+    // fp16 scales as Q8_0's; 3: IQ4_XS -- codes as MXFP4's, 8-byte super-block records
     int32_t fmt;
 };
 struct DecArgs {

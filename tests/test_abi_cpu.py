@@ -33,7 +33,8 @@ def test_status_strings():
 
 
 def _w(n_mat=8, rows=64, cols=128, typ=moe.MOE_Q8_0, data=FAKE, scales=FAKE):
-    return moe.c_moe_weights(typ, data, scales if typ in (moe.MOE_Q8_0, moe.MOE_MXFP4, moe.MOE_IQ4_NL) else None,
+    return moe.c_moe_weights(typ, data, scales if typ in (moe.MOE_Q8_0, moe.MOE_MXFP4, moe.MOE_IQ4_NL,
+                                                           moe.MOE_IQ4_XS) else None,
                              n_mat, rows, cols)
 
 
@@ -130,6 +131,27 @@ def test_iq4nl_validation():
     assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
                                   None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
     assert "IQ4_NL" in moe.last_error()
+
+
+def test_iq4xs_validation():
+    """IQ4_XS experts: widths must be multiples of 256 (MOE_ELIMIT), the super-block records
+    8-byte aligned (MOE_EINVAL); both paths validate otherwise (the calls stop at the
+    workspace check here), the GEMV path forced past its bound and float32 src1 are refused."""
+    xs = lambda **kw: _w(typ=moe.MOE_IQ4_XS, cols=kw.pop("cols", 256), **kw)
+    dn = lambda **kw: xs(rows=256, cols=64 * 4, **kw)
+    g = lambda **kw: xs(rows=256, **kw)
+    assert _ffn(gate=g(), up=g(), down=dn(), T=4, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=g(), up=g(), down=dn(), T=40, k=2, ws_bytes=16) == moe.MOE_EWORKSPACE
+    assert _ffn(gate=g(), up=g(), down=dn(), T=40, k=2, path=2) == moe.MOE_EINVAL   # 80 slots
+    assert _ffn(gate=g(cols=128), up=g(cols=128), down=xs(rows=128, cols=256), T=4, k=2) == moe.MOE_ELIMIT
+    assert "IQ4_XS" in moe.last_error() and "256" in moe.last_error()
+    assert _ffn(gate=g(scales=FAKE + 4), up=g(), down=dn(), T=4, k=2) == moe.MOE_EINVAL
+    assert "aligned" in moe.last_error()
+    assert _ffn(gate=g(), up=_w(typ=moe.MOE_IQ4_NL, rows=256, cols=256), down=dn(), T=4, k=2) == moe.MOE_EINVAL
+    w = g()
+    assert moe.lib.moe_mul_mat_id_workspace_size(ctypes.byref(w), moe.MOE_BF16, 1, 100, 2, None) > 0
+    assert moe.lib.moe_mul_mat_id(ctypes.byref(w), FAKE, moe.MOE_F32, 1, FAKE, 4, 2, None, FAKE,
+                                  None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
 
 
 def test_row_ids_validation():

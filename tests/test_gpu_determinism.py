@@ -22,7 +22,9 @@ def _same_bytes(a: torch.Tensor, b: torch.Tensor) -> bool:
                                        ("skew", moe.PATH_AUTO), ("v3", moe.PATH_AUTO),
                                        ("dec1x", moe.PATH_AUTO), ("dec8x", moe.PATH_AUTO),
                                        ("ppx", moe.PATH_AUTO), ("dec1n", moe.PATH_AUTO),
-                                       ("dec8n", moe.PATH_AUTO), ("ppn", moe.PATH_AUTO)])
+                                       ("dec8n", moe.PATH_AUTO), ("ppn", moe.PATH_AUTO),
+                                       ("dec1s", moe.PATH_AUTO), ("dec8s", moe.PATH_AUTO),
+                                       ("pps", moe.PATH_AUTO)])
 def test_ffn_ten_runs_bit_identical(name, path):
     inp = synth.make_inputs(name)
     dv = upload_ffn(inp)
