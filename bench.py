@@ -2,7 +2,7 @@
 """Benchmark of the MoE indirect matmul hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--config lite|dec1|dec8|skew|v3|dec1x|dec8x|ppx|dec1n|dec8n|ppn|dec1s|dec8s|pps|rowids]
+                    [--config lite|dec1|dec8|skew|v3|dec1x|dec8x|ppx|dec1n|dec8n|ppn|dec1s|dec8s|pps|rowids|gather]
 
 A step is one full pass of the hot path -- row ids, gate/up grouped GEMM, down
 grouped GEMM, fixed-order reduce (or the GEMV decode kernels) -- over one batch of
@@ -301,6 +301,67 @@ def bench_row_ids(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_gather(args):
+    """The standalone row gather (moe_gather_rows) at the skewed PP4096 and the V3-shaped
+    PP8192 shapes: the bf16 layer input copied into expert order by the row-id pass's first
+    map. Algorithmic bytes = the T input rows read once + the T*k gathered rows written.
+    The value is the V3-shaped rate; both shapes are on the line."""
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    shapes = {}
+    for name in ("skew", "v3"):
+        cfg = synth.CONFIGS[name]
+        T, k, E, K = cfg.n_tokens, cfg.n_used, cfg.n_experts, cfg.n_embd
+        ids_np = (synth.draw_ids_zipf(cfg.seed, T, E, k, cfg.zipf_s) if cfg.routing == "zipf"
+                  else synth.draw_ids_uniform(cfg.seed, T, E, k))
+        x = torch.from_numpy(synth.gen.draw_x_bf16(cfg.seed, T, K).view(np.int16)).to(dev)
+        s1, _, _ = moe.moe_row_ids(torch.from_numpy(ids_np).to(dev), E)
+        outs = [torch.empty((T * k, K), dtype=x.dtype, device=dev) for _ in range(2)]
+        shapes[name] = (cfg, T, k, K, x, s1, outs)
+    torch.cuda.synchronize()
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    res_shapes = {}
+    for name, (cfg, T, k, K, x, s1, outs) in shapes.items():
+        run = lambda i: moe.moe_gather_rows(x, s1, out=outs[i % 2], stream=stream)
+        warm = warm_up(run, args.warmup)
+        e0, e1 = KernelEvent(), KernelEvent()
+        e0.record(stream)
+        for i in range(args.steps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ev_ms = e0.elapsed_time(e1) / args.steps
+        nbytes = (T + T * k) * K * 2.0
+        gbs = nbytes / (ev_ms * 1e-3) / 1e9
+        res_shapes[name] = {"workload": cfg.desc, "rows": T * k, "row_bytes": K * 2, "us": ev_ms * 1e3,
+                            "gbps": gbs, "frac": gbs / HBM_PEAK_GBS, "warmup": warm,
+                            "algorithmic_bytes": nbytes}
+    v = res_shapes["v3"]
+    res = {
+        "metric": "MoE row gather GB/s (src1 rows into expert order), 1 MI355X",
+        "value": v["gbps"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": v["warmup"], "ms_per_step": v["us"] * 1e-3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gather of the DeepSeek-V3-shaped PP8192 input (8192 x 7168 bf16, k8)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": v["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": v["frac"], "traffic": None, "kernel": "gather",
+                     "algorithmic_bytes": v["algorithmic_bytes"]},
+        "shapes": res_shapes,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def prepare_ffn_workload(args, name):
     """Inputs of one FFN workload drawn and made resident in HBM: the weights in R
     copies (rotated through by the steps, so the set a step reads is not served from
@@ -531,6 +592,9 @@ def main():
         sys.exit(2)
     if args.config == "rowids":
         bench_row_ids(args)
+        return
+    if args.config == "gather":
+        bench_gather(args)
         return
     import torch
     import indirect_expert_matmul_amd as moe

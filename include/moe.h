@@ -146,6 +146,22 @@ moe_status moe_row_ids(const int32_t *ids, int64_t n_tokens, int32_t n_used, int
                        int32_t *expert_bounds, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_gather_rows -- the src1 rows copied into expert order by the first map of
+ * moe_row_ids (section 2.1 of the PR #283 write-up: ids_src1 names the src1 row each
+ * position of the expert-grouped buffer reads; section 2 shows the atomic-slot copy
+ * k_copy_src1_to_contiguous this replaces): dst[j][:] = src1[ids_src1[j]][:].
+ *   src1      device BF16 or F32 [src1_rows][K]
+ *   ids_src1  device int32 [n] (moe_row_ids' ids_src1 with n = n_tokens * n_used)
+ *   dst       device [n][K] of src1's type (written; a position whose index is outside
+ *             [0, src1_rows) gets a zero row)
+ * The fused calls never need it (their grouped GEMM gathers the rows into LDS itself);
+ * it is for callers that want the expert-contiguous copy. No workspace. n = 0 is a
+ * no-op. MOE_ELIMIT: src1_rows >= 2^31 or n >= 2^33.
+ */
+moe_status moe_gather_rows(const void *src1, moe_dtype src1_type, int64_t src1_rows, int64_t K,
+                           const int32_t *ids_src1, int64_t n, void *dst, void *stream);
+
+/*
  * moe_mul_mat_id -- GGML_OP_MUL_MAT_ID (section 1.2 of the PR #283 write-up).
  *   w        n_mat = n_experts, rows = N, cols = K. Supported pairs: (Q8_0 w, BF16
  *            src1), (MXFP4, IQ4_NL or IQ4_XS w, BF16 src1) on the MFMA grouped

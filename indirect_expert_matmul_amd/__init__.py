@@ -29,7 +29,7 @@ PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
            "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
            "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error",
-           "moe_last_stage_count", "moe_ffn_fused_noalloc", "moe_quantize_act")
+           "moe_last_stage_count", "moe_ffn_fused_noalloc", "moe_quantize_act", "moe_gather_rows")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -65,8 +65,9 @@ def _load():
     lib.moe_router_topk.argtypes = [P, I64, I32, I32, P, P, P]
     lib.moe_ffn_fused_noalloc.argtypes = [W, W, W, W, W, W, P, ctypes.c_int, P, P, I64, I32, P, O, P]
     lib.moe_quantize_act.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
+    lib.moe_gather_rows.argtypes = [P, ctypes.c_int, I64, I64, P, I64, P, P]
     for f in (lib.moe_row_ids, lib.moe_mul_mat_id, lib.moe_ffn_fused, lib.moe_router_topk,
-              lib.moe_ffn_fused_noalloc, lib.moe_quantize_act):
+              lib.moe_ffn_fused_noalloc, lib.moe_quantize_act, lib.moe_gather_rows):
         f.restype = ctypes.c_int
     lib.moe_row_ids_workspace_size.argtypes = [I64, I32, I32]
     lib.moe_mul_mat_id_workspace_size.argtypes = [W, ctypes.c_int, I32, I64, I32, O]
@@ -262,6 +263,30 @@ def moe_row_ids(ids: torch.Tensor, n_experts: int, src1_rows_per_token: int = 1,
                            dd.data_ptr(), b.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_row_ids")
     return s1, dd, b
+
+
+def moe_gather_rows(src1: torch.Tensor, ids_src1: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """dst[j] = src1[ids_src1[j]] for src1 [rows][K] (bf16 or its 16-bit patterns, or
+    float32) and int32 ids_src1 [n] (moe_row_ids' first map): the rows in expert order."""
+    if src1.dim() != 2:
+        raise ValueError("src1 must be [rows][K]")
+    if ids_src1.dtype != torch.int32 or ids_src1.dim() != 1:
+        raise ValueError("ids_src1 must be int32 [n]")
+    _dev_check(src1)
+    _dev_check(ids_src1)
+    if not src1.is_contiguous() or not ids_src1.is_contiguous():
+        raise ValueError("src1 and ids_src1 must be contiguous")
+    rows, K = src1.shape
+    n = ids_src1.numel()
+    if out is None:
+        out = torch.empty((n, K), dtype=src1.dtype, device=src1.device)
+    elif out.dtype != src1.dtype or tuple(out.shape) != (n, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n][K] tensor of src1's dtype")
+    _keep_alive(stream, out)
+    _check(lib.moe_gather_rows(src1.data_ptr(), _xtype(src1), rows, K, ids_src1.data_ptr(), n,
+                               out.data_ptr(), _stream(stream)), "moe_gather_rows")
+    return out
 
 
 def moe_quantize_act(x: torch.Tensor, stream=None):

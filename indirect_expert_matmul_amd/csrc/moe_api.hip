@@ -410,6 +410,20 @@ size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_ex
     return c.off;
 }
 
+moe_status moe_gather_rows(const void* src1, moe_dtype src1_type, int64_t src1_rows, int64_t K,
+                           const int32_t* ids_src1, int64_t n, void* dst, void* stream) {
+    g_err.clear();
+    if (src1_type != MOE_BF16 && src1_type != MOE_F32)
+        return fail(MOE_EINVAL, "gather: src1_type must be BF16 or F32");
+    if (src1_rows <= 0 || K <= 0 || n < 0) return fail(MOE_EINVAL, "gather: sizes must be > 0 (n >= 0)");
+    if (src1_rows > INT32_MAX) return fail(MOE_ELIMIT, "gather: src1_rows must fit in int32");
+    if (n > (int64_t)INT32_MAX * 4) return fail(MOE_ELIMIT, "gather: too many rows for one launch");
+    if (n == 0) return MOE_OK;
+    if (!src1 || !ids_src1 || !dst) return fail(MOE_EINVAL, "NULL pointer argument");
+    GatherArgs a{src1, src1_rows, K * (src1_type == MOE_BF16 ? 2 : 4), ids_src1, n, dst};
+    return hip_check(launch_gather(a, (hipStream_t)stream), "gather");
+}
+
 moe_status moe_row_ids(const int32_t* ids, int64_t n_tokens, int32_t n_used, int32_t n_experts,
                        int32_t src1_rows_per_token, int32_t* ids_src1, int32_t* ids_dst,
                        int32_t* expert_bounds, void* ws, size_t ws_bytes, void* stream) {

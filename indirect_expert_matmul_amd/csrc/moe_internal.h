@@ -235,6 +235,17 @@ struct DecArgs {
 // false the per-slot rows are in out / sout and the reduce kernel still has to run.
 hipError_t launch_decode(const DecArgs& a, hipStream_t st, bool* reduced = nullptr);
 
+// ---------------------------------------------------------------- row gather (K2)
+struct GatherArgs {
+    const void* src;      // [src_rows][row_bytes]
+    int64_t src_rows;
+    int64_t row_bytes;    // a multiple of 2
+    const int32_t* idx;   // [n]
+    int64_t n;
+    void* dst;            // [n][row_bytes]
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- router top-k
 struct RouterArgs {
     const float* logits;  // [T][E]

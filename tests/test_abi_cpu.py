@@ -154,6 +154,15 @@ def test_iq4xs_validation():
                                   None, FAKE, 1 << 30, None) == moe.MOE_EINVAL
 
 
+def test_gather_validation():
+    g = moe.lib.moe_gather_rows
+    assert g(FAKE, moe.MOE_Q8_0, 10, 64, FAKE, 5, FAKE, None) == moe.MOE_EINVAL      # type
+    assert g(FAKE, moe.MOE_BF16, 0, 64, FAKE, 5, FAKE, None) == moe.MOE_EINVAL       # no rows
+    assert g(FAKE, moe.MOE_BF16, 10, 64, None, 5, FAKE, None) == moe.MOE_EINVAL      # NULL map
+    assert g(FAKE, moe.MOE_F32, 1 << 31, 64, FAKE, 5, FAKE, None) == moe.MOE_ELIMIT
+    assert g(None, moe.MOE_BF16, 10, 64, None, 0, None, None) == moe.MOE_OK         # n = 0
+
+
 def test_row_ids_validation():
     f = moe.lib.moe_row_ids
     assert f(FAKE, 16, 2, 8, 3, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == moe.MOE_EINVAL
