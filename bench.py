@@ -67,6 +67,8 @@ def parse():
                         "empty for none)")
     p.add_argument("--extra-cpu-seconds", type=float, default=3.0,
                    help="CPU oracle budget for each further workload")
+    p.add_argument("--gather-shapes", default="skew,v3",
+                   help="--config gather: the input shapes timed (skew, v3; the value is the last one)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run one device-to-device copy of this many MiB (a known-size "
                         "kernel for scaling HBM byte counters)")
@@ -313,7 +315,8 @@ def bench_gather(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     shapes = {}
-    for name in ("skew", "v3"):
+    names = [n for n in args.gather_shapes.split(",") if n]
+    for name in names:
         cfg = synth.CONFIGS[name]
         T, k, E, K = cfg.n_tokens, cfg.n_used, cfg.n_experts, cfg.n_embd
         ids_np = (synth.draw_ids_zipf(cfg.seed, T, E, k, cfg.zipf_s) if cfg.routing == "zipf"
@@ -344,17 +347,18 @@ def bench_gather(args):
         res_shapes[name] = {"workload": cfg.desc, "rows": T * k, "row_bytes": K * 2, "us": ev_ms * 1e3,
                             "gbps": gbs, "frac": gbs / HBM_PEAK_GBS, "warmup": warm,
                             "algorithmic_bytes": nbytes}
-    v = res_shapes["v3"]
+    v = res_shapes[names[-1]]
     res = {
         "metric": "MoE row gather GB/s (src1 rows into expert order), 1 MI355X",
         "value": v["gbps"], "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": v["warmup"], "ms_per_step": v["us"] * 1e-3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "gather of the DeepSeek-V3-shaped PP8192 input (8192 x 7168 bf16, k8)",
+        "config": {"workload": "gather of the %s input (rows in expert order)" % shapes[names[-1]][0].desc,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": v["gbps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": v["frac"], "traffic": None, "kernel": "gather",
+                     "frac": v["frac"], "traffic": measured_traffic("gather_" + names[-1], "gather"),
+                     "kernel": "gather",
                      "algorithmic_bytes": v["algorithmic_bytes"]},
         "shapes": res_shapes,
         "cpu_baseline": None,
