@@ -14,8 +14,9 @@ is not served from the 256 MB last-level cache.
 Prints ONE JSON line: tokens/s (value), TFLOP/s, GB/s, a roofline entry for the
 dominant kernel (timed with HIP events on the launch stream) and the CPU oracle
 timed on a bounded sample of the same workload on this host. The same line carries,
-under "workloads", the Zipf-skewed PP4096 prefill and the GPT-OSS-20B-shaped decode
-batches of 1 and 8 tokens (--extra), each with its own dominant-kernel roofline.
+under "workloads", the Zipf-skewed PP4096 prefill, the DeepSeek-V3-shaped PP8192 layer and
+the GPT-OSS-20B-shaped decode batches of 1 and 8 tokens (--extra), each with its own
+dominant-kernel roofline.
 """
 from __future__ import annotations
 
@@ -61,7 +62,7 @@ def parse():
                    help="1: time replays of one HIP graph per weight copy (each graph holds one "
                         "step); 0: eager calls")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--extra", default="dec1,dec8,skew",
+    p.add_argument("--extra", default="dec1,dec8,skew,v3",
                    help="further workloads reported on the same line under 'workloads' "
                         "(comma-separated, timed in this order before the headline one; "
                         "empty for none)")
