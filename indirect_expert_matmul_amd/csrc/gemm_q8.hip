@@ -42,6 +42,17 @@
 
 #include "moe_internal.h"
 
+// Wave priority (s_setprio) while a step issues its MFMAs, so that of the two waves on a
+// SIMD the one in its multiply phase issues first. Measured (same box, A/B, two runs):
+// Q8_0 on the wide kernel V3-shaped gate/up 4,763 -> 4,440 us, Skew gate/up 294 -> 285 us
+// (priority 3; 1 gives nearly the same); the narrow kernel's Q8_0 down (Lite) 64.5 -> 62.2
+// us with priority 1, but its gate/up 117.8 -> 121.5 us, and MXFP4 on the wide kernel
+// 0.7-1% slower, so only those two forms raise it.
+template <bool WIDE, int MODE, int FMT>
+constexpr int mfma_prio() {
+    if constexpr (FMT != 0) return 0;
+    else return WIDE ? 3 : (MODE == 0 ? 1 : 0);
+}
 #ifndef MOE_GEMM_CFG2
 #define MOE_GEMM_CFG2 4, 2   // waves, pipeline stages: 64-row tiles
 #endif
@@ -455,6 +466,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
 #ifndef MOE_GEMM_NO_SCHED
         __builtin_amdgcn_sched_barrier(0);
 #endif
+        if constexpr (mfma_prio<false, MODE, FMT>() > 0) __builtin_amdgcn_s_setprio(mfma_prio<false, MODE, FMT>());
 #pragma unroll
         for (int t = 0; t < 8; t++) {
             const int cur = t & 1, nxt = cur ^ 1;
@@ -479,6 +491,7 @@ __global__ __launch_bounds__(64 * W) void k_gemm_q8(GemmArgs args) {
             __builtin_amdgcn_sched_barrier(0);
 #endif
         }
+        if constexpr (mfma_prio<false, MODE, FMT>() > 0) __builtin_amdgcn_s_setprio(0);
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
@@ -860,6 +873,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
 #ifndef MOE_GEMM_NO_SCHED
         __builtin_amdgcn_sched_barrier(0);
 #endif
+        if constexpr (mfma_prio<true, MODE, FMT>() > 0) __builtin_amdgcn_s_setprio(mfma_prio<true, MODE, FMT>());
 #pragma unroll
         for (int ss = 0; ss < 4; ss++) {
             const int cur = ss & 1, nxt = cur ^ 1;
@@ -889,6 +903,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
             __builtin_amdgcn_sched_barrier(0);
 #endif
         }
+        if constexpr (mfma_prio<true, MODE, FMT>() > 0) __builtin_amdgcn_s_setprio(0);
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
