@@ -606,7 +606,7 @@ struct Cfg {
     static constexpr int NA = BM / (8 * W);           // activation copies (8 rows) per wave
     static constexpr int SGROUP = BN * 16;            // SG = 4: one group of scales
     template <int SG>
-    static constexpr int stage_bytes() { return A_BYTES + B_BYTES + (SG == 1 ? BN * 4 : 0); }
+    static constexpr int stage_bytes() { return A_BYTES + B_BYTES + (SG == 1 ? BN * (FMT == 3 ? 8 : 4) : 0); }
     template <int SG>
     static constexpr int lds_bytes() { return NS * stage_bytes<SG>() + (SG == 4 ? 2 * SGROUP : 0); }
     template <int MODE>
@@ -627,7 +627,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     static_assert(NA * 8 * W == BM, "activation rows must split evenly over the waves");
     // copies per wave per stage: NA activation + 4 weight (+ 1 scale word if SG = 1);
     // with SG = 4 every fourth stage also carries one scale-group copy
-    constexpr int VM_STAGE = NA + (FMT != 0 ? 2 : 4) + (SG == 1 ? 1 : 0);
+    constexpr int VM_STAGE = NA + (FMT != 0 ? 2 : 4) + (SG == 1 ? (FMT == 3 ? 2 : 1) : 0);
     static_assert(SG == 1 || SG == 4, "scale groups of one or four stages");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
     {
         const int R = wv * 64 + lane;
         const uint16_t* dt = (MODE == 1 && (R & 16)) ? P.d2 : P.d1;
-        s_ptr = FMT == 1 ? (const uint8_t*)dt + ((int64_t)e * N + wrow(R)) * KB
+        s_ptr = (FMT == 1 || FMT == 3) ? (const uint8_t*)dt + ((int64_t)e * N + wrow(R)) * KB
                          : (const uint8_t*)(dt + ((int64_t)e * N + wrow(R)) * KB);
     }
     // MXFP4: where the scale row of this lane's weight row in column group c sits
@@ -779,12 +779,16 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
             for (int i = 0; i < 2; i++) dma16v(b_ptr[i] + k0 / 2, st + A_BYTES + (wv * 2 + i) * 1024);
             if constexpr (FMT == 1)
                 dma4v((const void*)((uintptr_t)(s_ptr + 2 * s) & ~(uintptr_t)3), st + A_BYTES + B_BYTES + wv * 256);
+            if constexpr (FMT == 3) {   // both words of the row's super-block record (stage s: record s / 4)
+                dma4v(s_ptr + 8 * (s >> 2), st + A_BYTES + B_BYTES + wv * 256);
+                dma4v(s_ptr + 8 * (s >> 2) + 4, st + A_BYTES + B_BYTES + C::BN * 4 + wv * 256);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 dma16(((MODE == 1 && (i & 1)) ? qu : qg) + k0, b_off[i], st + A_BYTES + (wv * 4 + i) * 1024);
         }
-        if (FMT == 1) {
+        if (FMT == 1 || FMT == 3) {
         } else if (SG == 1) {
             dma4v(s_ptr + 4 * s, st + A_BYTES + B_BYTES + wv * 256);
         } else if ((s & 3) == 0) {
@@ -837,6 +841,16 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
                 q[c][0] = *(const i32x4*)(st + A_BYTES + lr * 32 + 16 * h);
                 const uint32_t sw = *(const uint32_t*)(sg + lr * 4);
                 d[c] = half_bits_to_float((uint16_t)(sw >> (16 * h)));
+            } else if constexpr (FMT == 3) {
+                // IQ4_XS: the codes as for IQ4_NL; block j = 2 (s % 4) + h of the super-block
+                // takes d * (ls - 32) from the record's words (word 0: fp16 d, scales_h;
+                // word 1: scales_l)
+                q[c][0] = *(const i32x4*)(st + A_BYTES + lr * 32 + 16 * h);
+                const uint32_t w0 = *(const uint32_t*)(sg + lr * 4);
+                const uint32_t w1 = *(const uint32_t*)(sg + C::BN * 4 + lr * 4);
+                const int j = 2 * (s & 3) + h;
+                const uint32_t ls = ((w1 >> (4 * j)) & 15u) | (((w0 >> (16 + 2 * j)) & 3u) << 4);
+                d[c] = half_bits_to_float((uint16_t)w0) * (float)((int)ls - 32);
             } else {
                 const uint8_t* rowp = st + A_BYTES + lr * 64;
                 q[c][0] = *(const i32x4*)(rowp + (((2 * h) ^ swz_wb(lr)) << 4));
@@ -851,7 +865,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
         };
         auto deq = [&](int c, int ss) -> bf16x8 {
             if constexpr (FMT == 1) return dequant8_fp4((uint32_t)q[c][0][ss], d[c]);
-            if constexpr (FMT == 2) {
+            if constexpr (FMT == 2 || FMT == 3) {
                 uint32_t c03, c47;
                 nl_levels8((uint32_t)q[c][0][ss], c03, c47);
                 return dequant8((int)c03, (int)c47, d[c]);
@@ -892,7 +906,7 @@ __global__ __launch_bounds__(64 * W, W == 4 ? 2 : 1) void k_gemm_q8w(GemmArgs ar
             if (ss < 3) {
                 // 2*MACT MFMAs share the sub-step's dequant instructions (Q8_0: 40,
                 // MXFP4: 8, IQ4_NL: about 72)
-                constexpr int VPM = ((FMT == 1 ? 8 : FMT == 2 ? 72 : 40) + 2 * MACT - 1) / (2 * MACT);
+                constexpr int VPM = ((FMT == 1 ? 8 : FMT >= 2 ? 72 : 40) + 2 * MACT - 1) / (2 * MACT);
 #pragma unroll
                 for (int m = 0; m < 2 * MACT; m++) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1124,8 +1138,7 @@ int gemm_tile_m(int msub) { return 32 * msub; }
 int gemm_tile_x(int msub, int fmt, int64_t K, bool scales_aligned) {
     // MXFP4 takes the wide kernel only with its scale rows at even addresses, IQ4_NL
     // only with its scale tensors 4-byte aligned
-    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && fmt != 3 && (fmt == 0 || scales_aligned))
-               ? 32 : 0;
+    return (MOE_GEMM_TALL_LAST && msub == 4 && K % wide::KS == 0 && (fmt == 0 || scales_aligned)) ? 32 : 0;
 }
 #ifndef MOE_GEMM_TILE160
 #define MOE_GEMM_TILE160 0   // 1: the 160-row kernel runs 160-row tiles instead of 128 + 32
@@ -1163,7 +1176,11 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
         tall = tall || p.tile_x != 0 || p.tile_m == 160;
     }
     if (tall) {
-        if (msub != 4 || !wide_ok || a.fmt == 3) return hipErrorInvalidValue;
+        if (msub != 4 || !wide_ok) return hipErrorInvalidValue;
+        if (a.fmt == 3) {
+            if (!scales_aligned(a, 7)) return hipErrorInvalidValue;
+            return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2, 3>(a, st) : launch_wide_fp4<0, 5, 4, 2, 3>(a, st);
+        }
         if (a.fmt == 2) {
             if (!scales_aligned(a, 3)) return hipErrorInvalidValue;
             return a.mode == 1 ? launch_wide_fp4<1, 5, 4, 2, 2>(a, st) : launch_wide_fp4<0, 5, 4, 2, 2>(a, st);
@@ -1176,12 +1193,15 @@ hipError_t launch_gemm_q8(const GemmArgs& a0, int msub, hipStream_t st) {
         }
         return a.mode == 1 ? launch_wide<1, 5, 4, 2>(a, st) : launch_wide<0, 5, 4, 2>(a, st);
     }
-    if (a.fmt == 3) {   // IQ4_XS experts: the narrow kernel with two slots
+    if (a.fmt == 3) {   // IQ4_XS experts: 64-row tiles on the narrow kernel, 128-row on the wide one
         switch (msub) {
             case 2:
                 if (narrow_grid<8>(a) >= 2048) return launch_cfg_fp4<2, 8, 2, 3>(a, st);
                 return launch_cfg_fp4<2, 4, 2, 3>(a, st);
-            case 4: return launch_cfg_fp4<4, 8, 2, 3>(a, st);
+            case 4:
+                if (wide_ok && scales_aligned(a, 7))
+                    return a.mode == 1 ? launch_wide_fp4<1, 4, 4, 2, 3>(a, st) : launch_wide_fp4<0, 4, 4, 2, 3>(a, st);
+                return launch_cfg_fp4<4, 8, 2, 3>(a, st);
             default: return hipErrorInvalidValue;
         }
     }

@@ -693,8 +693,8 @@ moe_status moe_ffn_fused(const moe_weights* gate, const moe_weights* up, const m
         }
         // segment-last tiles of up to 160 rows where both GEMMs (and the shared ones they
         // launch with) run the wide kernel: the two share the row-id pass's tile table
-        // MXFP4: every scale tensor at an even address; IQ4_NL: 4-byte aligned
-        const uintptr_t smask = g.fmt == 2 ? 3 : 1;
+        // MXFP4: every scale tensor at an even address; IQ4_NL: 4-byte, IQ4_XS: 8-byte aligned
+        const uintptr_t smask = g.fmt == 3 ? 7 : (g.fmt == 2 ? 3 : 1);
         bool even = true;
         for (const moe_weights* w : {gate, up, down, sh_gate, sh_up, sh_down})
             if (w && ((uintptr_t)w->scales & smask)) even = false;
@@ -920,7 +920,7 @@ moe_status moe_mul_mat_id(const moe_weights* w, const void* src1, moe_dtype src1
             r.ldo = N;
             r.out_rows = p.r.ids_dst;
             r.w_once = n <= (int64_t)E * bm;   // at most one M tile per expert on average
-            if (gemm_tile_x(p.msub, g.fmt, K, ((uintptr_t)w->scales & (g.fmt == 2 ? 3 : 1)) == 0))
+            if (gemm_tile_x(p.msub, g.fmt, K, ((uintptr_t)w->scales & (g.fmt == 3 ? 7 : (g.fmt == 2 ? 3 : 1))) == 0))
                 gemm_set_tall(r, ra, 0);
             if ((s = check_gemm_limits(g, p.msub, n_tokens * B, K, "mul_mat_id"))) return s;
         }

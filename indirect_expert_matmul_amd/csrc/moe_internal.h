@@ -148,7 +148,7 @@ int gemm_tile_m(int msub);
 // Extra rows (0 or 32) the last M tile of an expert may hold on the GEMM path for this
 // tile choice, weight format and K: 32 where the 128-row wide kernel runs, whose
 // 160-row variant takes such tiles (MXFP4: when every scale tensor of the launch
-// starts at an even address; IQ4_NL: at a 4-byte aligned one).
+// starts at an even address; IQ4_NL: at a 4-byte aligned one; IQ4_XS: 8-byte).
 int gemm_tile_x(int msub, int fmt, int64_t K, bool scales_aligned);
 // Puts routed problem p and tile table q of the row-id pass on the 160-row kernel's tiles.
 void gemm_set_tall(GemmProblem& p, RowIdsArgs& r, int q);
