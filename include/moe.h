@@ -102,7 +102,8 @@ typedef struct {
 
 /* Path selection (the pages' backend picks its quantized grouped path by comparing
  * the token count with a threshold times the expert count, section 2.1):
- * GEMM when n_tokens >= tau * n_experts, else the GEMV (decode) path.
+ * GEMM when n_tokens >= tau * n_experts, else the GEMV (decode) path within the
+ * bounds that moe_select_path states.
  * Optional per-kernel timing: when timing_events is non-NULL it points to
  * n_timing_events hipEvent_t handles; the call records events[2i] before and
  * events[2i+1] after its i-th kernel launch on `stream` (while 2i+1 <
@@ -283,8 +284,11 @@ size_t moe_ffn_fused_workspace_size(const moe_weights *gate, const moe_weights *
 /* Which path a call with these sizes takes: 1 grouped GEMM, 2 GEMV (decode), or a
  * negative moe_status for invalid arguments. act_width is the widest activation
  * row a GEMV kernel would stage (mul_mat_id: K; FFN: max(n_embd, n_ff, n_ff_sh)).
- * Auto: GEMV when n_tokens < tau * n_experts, n_tokens * n_used <= 256 and
- * act_width <= 16384; forcing GEMV outside the last two bounds is MOE_EINVAL.
+ * Auto (Q8_0): GEMV when n_tokens < tau * n_experts and either n_tokens * n_used <= 48
+ * with act_width <= 4096, or n_tokens == 1 with n_used <= 256 and act_width <= 16384;
+ * else GEMM. 4-bit experts: GEMV when n_tokens < tau * n_experts, n_tokens * n_used
+ * <= 64 and act_width <= 4096. Forcing GEMV is allowed up to n_tokens * n_used <= 256
+ * and act_width <= 16384 (Q8_0; 64 and 4096 for 4-bit), else MOE_EINVAL.
  * Pure host function. */
 int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
                         const moe_options *opt);

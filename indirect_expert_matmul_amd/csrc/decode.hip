@@ -50,7 +50,10 @@ constexpr bool kDecWeightsNT = MOE_DEC_W_NT != 0;
 
 constexpr int kThreads = 256;
 constexpr int kR = 8;    // weight rows (row pairs for gate/up) per block
-constexpr int kSP = 1;   // token slots per pass
+#ifndef MOE_DEC_SP
+#define MOE_DEC_SP 1
+#endif
+constexpr int kSP = MOE_DEC_SP;   // token slots per pass
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -554,34 +557,45 @@ __device__ __forceinline__ int count_experts(int v, int E) {
 // The unit of global wave gw when every wave owns one unit of R rows: routed units
 // first (distinct expert d = gw / chunks), then the shared ones. Returns false for waves
 // past the last unit.
+#ifndef MOE_DEC_SHARED_FIRST
+#define MOE_DEC_SHARED_FIRST 1
+#endif
 __device__ __forceinline__ bool wave_unit(const DecArgs& a, int gw, int R, bool& routed, int& e,
                                           uint64_t& smask, int& cnt, int& n_lo, int& n_hi) {
     const int lane = threadIdx.x & 63;
+    const int Rs = a.rows_shared > 0 ? a.rows_shared : R;
     const int nch_r = (a.rw.N + R - 1) / R;
     const int nw_r = a.d_max * nch_r;
-    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0;
+    const int nw_s = a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + Rs - 1) / Rs) : 0;
     if (gw >= nw_r + nw_s) return false;
-    routed = gw < nw_r;
+    // shared-expert units (several passes each) take the first waves, so they start in
+    // the first round instead of forming the launch's tail. Measured per layer call on
+    // one MI355X: Lite-shaped T = 8 107 -> 95 us, GPT-OSS-shaped with a shared expert T = 8
+    // 162 -> 155 us, but T = 10 and 16 slower (126 -> 134, 262 -> 286 us), so only up to 8.
+    const bool sh_first = MOE_DEC_SHARED_FIRST && a.T > 1 && a.T <= 8;
+    const int gr = sh_first ? gw - nw_s : gw;   // index among the routed units
+    routed = sh_first ? gw >= nw_s : gw < nw_r;
     int chunk;
     if (routed) {
-        const int d = gw / nch_r;
-        chunk = gw - d * nch_r;
+        const int d = gr / nch_r;
+        chunk = gr - d * nch_r;
         const int v = lane_expert(a, lane);
         e = nth_expert(v, a.E, d);
         if (e < 0) return false;  // fewer distinct experts than the grid allows for
         smask = __ballot(v == e);
         cnt = __popcll(smask);
     } else {
-        const int nch_s = (a.sw.N + R - 1) / R;
-        const int b = gw - nw_r;
+        const int nch_s = (a.sw.N + Rs - 1) / Rs;
+        const int b = sh_first ? gw : gw - nw_r;
         e = b / nch_s;
         chunk = b - e * nch_s;
         smask = 0;
         cnt = a.T;
     }
     const int N = routed ? a.rw.N : a.sw.N;
-    n_lo = chunk * R;
-    n_hi = min(n_lo + R, N);
+    const int Ru = routed ? R : Rs;
+    n_lo = chunk * Ru;
+    n_hi = min(n_lo + Ru, N);
     return true;
 }
 
@@ -1053,6 +1067,19 @@ int rows_per_wave(const DecArgs& a, int waves) {
     return (int)(r < 4 ? 4 : (r > 32 ? 32 : r));
 }
 
+// Rows per shared-expert unit. A routed unit usually serves one pass of slots; a shared
+// unit serves all T tokens in ceil(T / P) passes over its rows, so its rows are cut by
+// that many passes (at least one row) to keep it about as long as a routed unit.
+#ifndef MOE_DEC_SHARED_SPLIT
+#define MOE_DEC_SHARED_SPLIT 1
+#endif
+int shared_rows(int R, int T, int P) {
+    if (!MOE_DEC_SHARED_SPLIT) return R;
+    const int passes = (T + P - 1) / P;
+    const int r = (R + passes - 1) / passes;
+    return r < 1 ? 1 : r;
+}
+
 // Units per wave (routed experts plus shared experts over 4 waves) up to which the fused
 // down + reduce kernel is used; beyond it each wave would restart its row stream too often
 // and the per-unit kernels with the standalone reduce are faster.
@@ -1074,9 +1101,10 @@ hipError_t launch_stream(DecArgs a, hipStream_t st) {
     int waves = 0;
     if (hipError_t e = resident_waves(k_decode_stream<MODE, P, XBF16, NIT, FMT>, lds, occ, &waves)) return e;
     a.rows_per_block = rows_per_wave(a, waves);
-    const int R = a.rows_per_block;
+    a.rows_shared = shared_rows(a.rows_per_block, a.T, P);
+    const int R = a.rows_per_block, Rs = a.rows_shared;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
-                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
+                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + Rs - 1) / Rs) : 0);
     if (nw <= 0) return hipSuccess;
     const int grid = (nw + 3) / 4;
     k_decode_stream<MODE, P, XBF16, NIT, FMT><<<grid, 256, lds, st>>>(a);
@@ -1089,9 +1117,10 @@ hipError_t launch_regs(DecArgs a, hipStream_t st) {
     int waves = 0;
     if (hipError_t e = resident_waves(k_decode_wave<MODE, 1, XBF16, NIT, FMT>, 0, occ, &waves)) return e;
     a.rows_per_block = rows_per_wave(a, waves);
-    const int R = a.rows_per_block;
+    a.rows_shared = shared_rows(a.rows_per_block, a.T, 1);
+    const int R = a.rows_per_block, Rs = a.rows_shared;
     const int nw = a.d_max * ((a.rw.N + R - 1) / R) +
-                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + R - 1) / R) : 0);
+                   (a.sw.n_mat > 0 ? a.sw.n_mat * ((a.sw.N + Rs - 1) / Rs) : 0);
     if (nw <= 0) return hipSuccess;
     k_decode_wave<MODE, 1, XBF16, NIT, FMT><<<(nw + 3) / 4, 256, 0, st>>>(a);
     return hipGetLastError();

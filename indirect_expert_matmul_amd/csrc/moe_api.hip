@@ -128,7 +128,14 @@ int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_op
         return 2;
     }
     if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
-    return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
+    // Automatic choice: the GEMV's wave-level kernels up to kDecAutoSlots slots, its block
+    // kernel (wider rows, more slots) for a single token only. Past those the block kernel
+    // streams an expert's rows once per slot and the grouped GEMM wins (measured on one
+    // MI355X, Q8_0, GEMV against GEMM per layer call: V3-shaped T = 2 155 / 156 us, T = 16
+    // 2,868 / 941 us; Lite-shaped T = 10 126 / 106 us, T = 42 1,249 / 149 us; GPT-OSS-shaped
+    // T = 16 235 / 225 us; T = 8 127 / 153 us).
+    const bool wave_ok = T * (int64_t)k <= kDecAutoSlots && act_width <= 4096;
+    return ((double)T < (double)tau_of(o) * (double)E && dec_ok && (wave_ok || T == 1)) ? 2 : 1;
 }
 
 // 4-bit experts (MXFP4, IQ4_NL): the GEMV path only through its wave-level kernels (n_tokens * n_used

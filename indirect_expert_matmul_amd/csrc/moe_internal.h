@@ -56,6 +56,7 @@ constexpr int kMaxBuckets = kMaxExperts + 1;  // + one bucket for out-of-range i
 constexpr int64_t kRowIdsOneBlockMax = 4096;   // entries handled by the single-workgroup pass
 constexpr int kDecMaxSlots = 256;          // GEMV path: n_tokens * n_used
 constexpr int64_t kDecMaxWidth = 16384;    // GEMV path: widest staged activation row
+constexpr int kDecAutoSlots = 48;          // automatic GEMV choice, wave kernels: n_tokens * n_used
 constexpr int kAlign = 256;                // workspace sub-buffer alignment
 
 // Sets the thread-local message moe_last_error() returns.
@@ -226,6 +227,10 @@ struct DecArgs {
     int32_t mode;           // 0 raw, 1 silu(gate) * up
     int32_t d_max;          // upper bound on distinct experts (grid)
     int32_t rows_per_block;
+    // wave kernels: rows per shared-expert unit (0: rows_per_block). A shared unit serves
+    // every token, so it streams its rows once per pass of P tokens; fewer rows per unit
+    // keep its length near a routed unit's.
+    int32_t rows_shared;
     // down mode, optional: the weighted sum over each token's slots (route_w, or weight 1
     // when null) plus the shared experts, written to out_tok [T][N] by the GEMV itself
     const float* route_w;

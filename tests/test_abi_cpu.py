@@ -184,6 +184,15 @@ def test_path_selection():
     assert moe.moe_select_path(64, 2, 64, 2048, path=moe.PATH_GEMV) == moe.PATH_GEMV
     assert moe.moe_select_path(64, 2, 16, 2048) == moe.PATH_GEMM                 # T >= tau*E
     assert moe.moe_select_path(20, 4, 32, 2880, tau=0.5) == moe.PATH_GEMM
+    # automatic GEMV: wave kernels up to 48 slots, the block kernel for one token only
+    assert moe.moe_select_path(16, 4, 32, 2880) == moe.PATH_GEMM         # 64 slots
+    assert moe.moe_select_path(8, 6, 64, 2048) == moe.PATH_GEMV          # 48 slots
+    assert moe.moe_select_path(10, 6, 64, 2048) == moe.PATH_GEMM         # 60 slots
+    assert moe.moe_select_path(42, 6, 64, 2048) == moe.PATH_GEMM
+    assert moe.moe_select_path(1, 8, 256, 7168) == moe.PATH_GEMV         # width > 4096, one token
+    assert moe.moe_select_path(2, 8, 256, 7168) == moe.PATH_GEMM
+    assert moe.moe_select_path(42, 6, 64, 2048, path=moe.PATH_GEMV) == moe.PATH_GEMV
+    assert moe.moe_select_path(8, 8, 256, 7168, path=moe.PATH_GEMV) == moe.PATH_GEMV
     with pytest.raises(moe.MoeError):
         moe.moe_select_path(100, 8, 256, 7168, path=moe.PATH_GEMV)
 

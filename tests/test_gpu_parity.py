@@ -344,13 +344,13 @@ def test_v3_full_size_stratified():
 
 @pytest.mark.parametrize("T", [1, 8])
 def test_v3_shaped_decode_wide(T):
-    """Decode batches of a DeepSeek-V3-shaped layer (n_embd 7168 > 4096): automatic
-    selection takes the GEMV path, on its block kernel for widths past the wave
-    kernels' 4096. Only the experts the batch routes to are drawn (nothing reads the
-    others)."""
+    """Decode batches of a DeepSeek-V3-shaped layer (n_embd 7168 > 4096) on the GEMV
+    path's block kernel for widths past the wave kernels' 4096: automatic selection
+    takes it for one token, and it is forced for eight. Only the experts the batch
+    routes to are drawn (nothing reads the others)."""
     inp = synth.make_custom_ffn(71 + T, 256, 8, T, 7168, 2048, 1, touched_only=True)
-    assert moe.moe_select_path(T, 8, 256, 7168) == moe.PATH_GEMV
-    got = run_ffn(upload_ffn(inp))
+    assert moe.moe_select_path(T, 8, 256, 7168) == (moe.PATH_GEMV if T == 1 else moe.PATH_GEMM)
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
     torch.cuda.synchronize()
     assert moe.last_stage_count() == 3   # gate/up GEMV, down GEMV, reduce
     err = normwise(got.cpu().numpy(), oracle.ffn(inp))
@@ -361,14 +361,33 @@ def test_v3_shaped_decode_wide(T):
 @pytest.mark.parametrize("T", [11, 16, 42])
 def test_lite_widths_gemv_block_kernel(T):
     """DeepSeek-Lite-shaped layer (shared experts included) at batches of 64 < T*k <=
-    256 slots: the GEMV path past the wave kernels' 64 slots runs the block kernel."""
+    256 slots: the GEMV path (forced; automatic selection takes the grouped GEMM here)
+    past the wave kernels' 64 slots runs the block kernel."""
     inp = synth.make_custom_ffn(90 + T, 64, 6, T, 2048, 1408, 2, touched_only=True)
-    assert moe.moe_select_path(T, 6, 64, 2048) == moe.PATH_GEMV
-    got = run_ffn(upload_ffn(inp))
+    assert moe.moe_select_path(T, 6, 64, 2048) == moe.PATH_GEMM
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
     torch.cuda.synchronize()
     assert moe.last_stage_count() == 3
     err = normwise(got.cpu().numpy(), oracle.ffn(inp))
     print("lite widths T=%d (%d slots) normwise error %.3g" % (T, 6 * T, err))
+    assert err <= TOL_FP32
+
+
+@pytest.mark.parametrize("E,k,T,n_embd,n_ff,S", [
+    (64, 6, 8, 2048, 1408, 2),    # Lite-shaped, 48 slots: shared units split in rows and run first
+    (64, 6, 10, 2048, 1408, 2),   # 60 slots: shared units split, in the usual order
+    (32, 4, 5, 2880, 2880, 1),    # odd T: three passes of two tokens per shared unit
+    (16, 2, 3, 512, 256, 3),      # three shared experts, two passes each
+])
+def test_ffn_gemv_shared_units_split(E, k, T, n_embd, n_ff, S):
+    """Wave-kernel GEMV with shared experts over several tokens: a shared unit serves
+    every token in several passes, so it gets fewer rows than a routed unit (and, up
+    to 8 tokens, the first waves). Every output row compared with the oracle."""
+    inp = synth.make_custom_ffn(130 + T, E, k, T, n_embd, n_ff, S, touched_only=True)
+    got = run_ffn(upload_ffn(inp), path=moe.PATH_GEMV)
+    torch.cuda.synchronize()
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    print("gemv shared split E%d k%d T%d S%d normwise error %.3g" % (E, k, T, S, err))
     assert err <= TOL_FP32
 
 
