@@ -287,7 +287,7 @@ size_t moe_ffn_fused_workspace_size(const moe_weights *gate, const moe_weights *
  * Auto (Q8_0): GEMV when n_tokens < tau * n_experts and either n_tokens * n_used <= 48
  * with act_width <= 4096, or n_tokens == 1 with n_used <= 256 and act_width <= 16384;
  * else GEMM. 4-bit experts: GEMV when n_tokens < tau * n_experts, n_tokens * n_used
- * <= 64 and act_width <= 4096. Forcing GEMV is allowed up to n_tokens * n_used <= 256
+ * <= 64 (MXFP4: 32) and act_width <= 4096. Forcing GEMV is allowed up to n_tokens * n_used <= 256
  * and act_width <= 16384 (Q8_0; 64 and 4096 for 4-bit), else MOE_EINVAL.
  * Pure host function. */
 int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,

@@ -138,9 +138,14 @@ int select_path(int64_t T, int32_t k, int32_t E, int64_t act_width, const moe_op
     return ((double)T < (double)tau_of(o) * (double)E && dec_ok && (wave_ok || T == 1)) ? 2 : 1;
 }
 
-// 4-bit experts (MXFP4, IQ4_NL): the GEMV path only through its wave-level kernels (n_tokens * n_used
-// <= 64 and every activation width <= 4096); otherwise the grouped GEMM.
-int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4, const moe_options* o) {
+// 4-bit experts (MXFP4, IQ4_NL, IQ4_XS): the GEMV path only through its wave-level kernels
+// (n_tokens * n_used <= 64 and every activation width <= 4096); otherwise the grouped GEMM.
+// Automatically up to auto_slots slots: MXFP4 32 (GPT-OSS-shaped, GEMV against GEMM per layer
+// call on one MI355X: 16 slots 79 / 91 us, 32 slots 119 / 112, 48 slots 165 / 141, 64 slots
+// 200 / 162), the IQ formats 64 (IQ4_XS E128 k8 at 64 slots 70 / 77 us; IQ4_NL
+// GPT-OSS-shaped at 48 and 64 slots 189 / 189 and 227 / 219, Lite-shaped at 48 84 / 93).
+int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4, const moe_options* o,
+                    int auto_slots = 64) {
     if (!fp4) return select_path(T, k, E, act_width, o);
     const int32_t force = o ? o->path : 0;
     const bool dec_ok = T * (int64_t)k <= 64 && act_width <= 4096;
@@ -152,7 +157,7 @@ int select_path_fmt(int64_t T, int32_t k, int32_t E, int64_t act_width, bool fp4
         return 2;
     }
     if (force != 0) return fail(MOE_EINVAL, "options.path must be 0, 1 or 2 (got %d)", force);
-    return ((double)T < (double)tau_of(o) * (double)E && dec_ok) ? 2 : 1;
+    return ((double)T < (double)tau_of(o) * (double)E && dec_ok && T * (int64_t)k <= auto_slots) ? 2 : 1;
 }
 
 // With options.act_quant = 1: 3 (the quantized-activation grouped GEMM, Q8_0 experts
@@ -163,7 +168,8 @@ int select_path_aq(int64_t T, int32_t k, int32_t E, int64_t act_width, int32_t w
     if (aq != 0 && aq != 1) return fail(MOE_EINVAL, "options.act_quant must be 0 or 1 (got %d)", aq);
     if (!aq)
         return select_path_fmt(T, k, E, act_width,
-                               wtype == MOE_MXFP4 || wtype == MOE_IQ4_NL || wtype == MOE_IQ4_XS, o);
+                               wtype == MOE_MXFP4 || wtype == MOE_IQ4_NL || wtype == MOE_IQ4_XS, o,
+                               wtype == MOE_MXFP4 ? 32 : 64);
     if (wtype != MOE_Q8_0) return fail(MOE_EINVAL, "quantized activations (act_quant = 1) need Q8_0 experts");
     if (o->path != 0 && o->path != 1)
         return fail(MOE_EINVAL, "quantized activations run on the grouped GEMM only: options.path must "

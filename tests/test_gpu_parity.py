@@ -451,6 +451,19 @@ def test_mxfp4_mul_mat_id_gemv(E, k, T, K, N, B_is_k, bad):
     assert np.all(g[(ids < 0) | (ids >= E)] == 0.0)
 
 
+@pytest.mark.parametrize("T,want_gemm", [(8, False), (12, True)])
+def test_mxfp4_automatic_path_bound(T, want_gemm):
+    """MXFP4 experts take the GEMV automatically up to 32 slots, the grouped GEMM
+    beyond (GPT-OSS-shaped layer, n_used 4)."""
+    inp = synth.make_custom_ffn(140 + T, 32, 4, T, 640, 512, 0, wtype="mxfp4", touched_only=True)
+    got = run_ffn(upload_ffn(inp))
+    torch.cuda.synchronize()
+    stages = moe.last_stage_count()
+    assert (stages == 4) == want_gemm   # GEMM: row ids, gate/up, down, reduce
+    err = normwise(got.cpu().numpy(), oracle.ffn(inp))
+    assert err <= (TOL_MFMA if want_gemm else TOL_FP32)
+
+
 @pytest.mark.parametrize("name", ["dec1x", "dec8x"])
 def test_decode_mxfp4_full(name):
     inp = synth.make_inputs(name)
