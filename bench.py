@@ -385,10 +385,11 @@ def prepare_ffn_workload(args, name):
     def up(qs, d):
         return moe.weights_from_numpy(qs, d)
 
-    path = moe.moe_select_path(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), path=args.path)
+    wtype = {"q8_0": moe.MOE_Q8_0, "mxfp4": moe.MOE_MXFP4, "iq4_nl": moe.MOE_IQ4_NL,
+             "iq4_xs": moe.MOE_IQ4_XS}[cfg.wtype]
     aq = args.act_quant
-    if aq:
-        path = 3
+    path = moe.moe_select_path_typed(T, k, cfg.n_experts, max(cfg.n_embd, cfg.n_ff), wtype,
+                                     path=args.path, act_quant=aq)
     st = workload_stats(inp, cfg, 4 if path == 2 else 2)
     R = args.rotate or (1 if st["bytes"] > 2e9 else max(4, int(np.ceil(1.2e9 / st["bytes"]))))
     sets = []

@@ -293,6 +293,14 @@ size_t moe_ffn_fused_workspace_size(const moe_weights *gate, const moe_weights *
 int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
                         const moe_options *opt);
 
+/* The path moe_mul_mat_id / moe_ffn_fused take for experts of weight_type (MOE_Q8_0,
+ * MOE_MXFP4, MOE_IQ4_NL or MOE_IQ4_XS) under opt: 1 grouped GEMM, 2 GEMV, 3 the grouped
+ * GEMM over quantized activations (opt->act_quant = 1, Q8_0 only), or a negative
+ * moe_status (MOE_EINVAL for other weight types, or for options the call would reject).
+ * Q8_0 gives the same answer as moe_select_path. Pure host function. */
+int32_t moe_select_path_typed(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
+                              moe_dtype weight_type, const moe_options *opt);
+
 const char *moe_status_string(moe_status s);
 const char *moe_last_error(void); /* thread-local detail of the last failure ("" if none) */
 /* Kernels (timing-event pairs, see moe_options) enqueued by the last successful

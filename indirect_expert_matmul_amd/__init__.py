@@ -28,7 +28,8 @@ PATH_AUTO, PATH_GEMM, PATH_GEMV = 0, 1, 2
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_row_ids", "moe_mul_mat_id", "moe_ffn_fused", "moe_router_topk",
            "moe_row_ids_workspace_size", "moe_mul_mat_id_workspace_size",
-           "moe_ffn_fused_workspace_size", "moe_select_path", "moe_status_string", "moe_last_error",
+           "moe_ffn_fused_workspace_size", "moe_select_path", "moe_select_path_typed",
+           "moe_status_string", "moe_last_error",
            "moe_last_stage_count", "moe_ffn_fused_noalloc", "moe_quantize_act", "moe_gather_rows")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
@@ -77,6 +78,8 @@ def _load():
         f.restype = SZ
     lib.moe_select_path.argtypes = [I64, I32, I32, I64, O]
     lib.moe_select_path.restype = I32
+    lib.moe_select_path_typed.argtypes = [I64, I32, I32, I64, ctypes.c_int, O]
+    lib.moe_select_path_typed.restype = I32
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
@@ -243,6 +246,15 @@ def moe_select_path(n_tokens: int, n_used: int, n_experts: int, act_width: int,
     r = lib.moe_select_path(n_tokens, n_used, n_experts, act_width, ctypes.byref(_options(path, tau)))
     if r < 0:
         raise MoeError(r, "moe_select_path", last_error())
+    return r
+
+
+def moe_select_path_typed(n_tokens: int, n_used: int, n_experts: int, act_width: int, weight_type: int,
+                          path: int = PATH_AUTO, tau: float = 0.0, act_quant: int = 0) -> int:
+    r = lib.moe_select_path_typed(n_tokens, n_used, n_experts, act_width, weight_type,
+                                  ctypes.byref(_options(path, tau, act_quant=act_quant)))
+    if r < 0:
+        raise MoeError(r, "moe_select_path_typed", last_error())
     return r
 
 

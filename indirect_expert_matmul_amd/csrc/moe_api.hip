@@ -416,6 +416,18 @@ int32_t moe_select_path(int64_t n_tokens, int32_t n_used, int32_t n_experts, int
     return select_path(n_tokens, n_used, n_experts, act_width, opt);
 }
 
+int32_t moe_select_path_typed(int64_t n_tokens, int32_t n_used, int32_t n_experts, int64_t act_width,
+                              moe_dtype weight_type, const moe_options* opt) {
+    moe_status s;
+    if ((s = check_tokens(n_tokens, n_used))) return s;
+    if ((s = check_experts(n_experts))) return s;
+    if (act_width <= 0) return fail(MOE_EINVAL, "act_width must be > 0");
+    if (weight_type != MOE_Q8_0 && weight_type != MOE_MXFP4 && weight_type != MOE_IQ4_NL &&
+        weight_type != MOE_IQ4_XS)
+        return fail(MOE_EINVAL, "weight_type must be Q8_0, MXFP4, IQ4_NL or IQ4_XS (got %d)", (int)weight_type);
+    return select_path_aq(n_tokens, n_used, n_experts, act_width, weight_type, opt);
+}
+
 size_t moe_row_ids_workspace_size(int64_t n_tokens, int32_t n_used, int32_t n_experts) {
     if (check_tokens(n_tokens, n_used) || check_experts(n_experts)) return 0;
     Carve c(nullptr);

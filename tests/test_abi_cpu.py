@@ -193,6 +193,22 @@ def test_path_selection():
     assert moe.moe_select_path(2, 8, 256, 7168) == moe.PATH_GEMM
     assert moe.moe_select_path(42, 6, 64, 2048, path=moe.PATH_GEMV) == moe.PATH_GEMV
     assert moe.moe_select_path(8, 8, 256, 7168, path=moe.PATH_GEMV) == moe.PATH_GEMV
+    # by weight type: 4-bit experts use the wave kernels only (MXFP4 up to 32 slots, the
+    # IQ formats up to 64); quantized activations need Q8_0
+    typed = moe.moe_select_path_typed
+    assert typed(8, 8, 128, 2048, moe.MOE_IQ4_XS) == moe.PATH_GEMV       # 64 slots
+    assert typed(8, 8, 128, 2048, moe.MOE_Q8_0) == moe.PATH_GEMM
+    assert typed(8, 4, 32, 2880, moe.MOE_MXFP4) == moe.PATH_GEMV         # 32 slots
+    assert typed(12, 4, 32, 2880, moe.MOE_MXFP4) == moe.PATH_GEMM
+    assert typed(12, 4, 32, 2880, moe.MOE_IQ4_NL) == moe.PATH_GEMV
+    assert typed(1, 8, 256, 7168, moe.MOE_IQ4_NL) == moe.PATH_GEMM       # width > 4096
+    assert typed(1, 8, 256, 7168, moe.MOE_Q8_0) == moe.PATH_GEMV
+    assert typed(8, 4, 32, 2880, moe.MOE_Q8_0, act_quant=1) == 3
+    for bad in ((8, 4, 32, 2880, moe.MOE_MXFP4), (8, 4, 32, 2880, moe.MOE_F32)):
+        with pytest.raises(moe.MoeError):
+            typed(*bad, act_quant=1 if bad[4] == moe.MOE_MXFP4 else 0)
+    with pytest.raises(moe.MoeError):
+        typed(1, 8, 256, 7168, moe.MOE_IQ4_XS, path=moe.PATH_GEMV)
     with pytest.raises(moe.MoeError):
         moe.moe_select_path(100, 8, 256, 7168, path=moe.PATH_GEMV)
 
