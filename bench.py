@@ -52,7 +52,8 @@ def parse():
                    help="untimed warm-up steps of the headline workload (default: at least 20 "
                         "steps and 0.2 s of them, so the GPU clocks have ramped up; the count is "
                         "reported). The further workloads (--extra) always warm up that long.")
-    p.add_argument("--config", default="lite")
+    p.add_argument("--config", default="lite",
+                   help="a workload of synth.CONFIGS, rowids, gather, or crossover (GEMV against GEMM)")
     p.add_argument("--rotate", type=int, default=0, help="weight copies (0 = auto)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 GEMM, 2 GEMV")
     p.add_argument("--act-quant", type=int, default=0,
@@ -589,6 +590,60 @@ def _public(r):
     return {k: v for k, v in r.items() if k not in ("cfg", "inp", "stats", "stream")}
 
 
+# Decode-to-small-prefill batches on which the automatic path choice was measured: each
+# shape's GEMV (forced, where its bounds allow) against its grouped GEMM, per layer call.
+CROSSOVER = ([("v3", 256, 8, T, 7168, 2048, 1, "q8_0") for T in (1, 2, 8, 16, 32)] +
+             [("lite", 64, 6, T, 2048, 1408, 2, "q8_0") for T in (1, 4, 8, 10, 42)] +
+             [("gptoss", 32, 4, T, 2880, 2880, 0, "q8_0") for T in (8, 16)] +
+             [("gptoss", 32, 4, T, 2880, 2880, 0, "mxfp4") for T in (8, 12, 16)] +
+             [("e128", 128, 8, T, 2048, 768, 0, "iq4_xs") for T in (4, 8)])
+
+
+def bench_crossover(args):
+    """GEMV against grouped GEMM per layer call on the CROSSOVER shapes (weights resident,
+    only the experts each batch routes to drawn). One JSON line."""
+    import torch
+    import indirect_expert_matmul_amd as moe
+    import synth
+    wt = {"q8_0": moe.MOE_Q8_0, "mxfp4": moe.MOE_MXFP4, "iq4_xs": moe.MOE_IQ4_XS}
+    dev = lambda a, dt, view=None: torch.from_numpy(np.ascontiguousarray(a, dtype=dt) if view is None
+                                                    else np.ascontiguousarray(a, dtype=dt).view(view)).cuda()
+    res = []
+    for name, E, k, T, ne, nf, S, w in CROSSOVER:
+        inp = synth.make_custom_ffn(600 + T, E, k, T, ne, nf, S, wtype=w, touched_only=True)
+        W = [moe.weights_from_numpy(inp[n + "_qs"], inp[n + "_d"]) for n in ("gate", "up", "down")]
+        sh = ([moe.weights_from_numpy(inp["sh_" + n + "_qs"], inp["sh_" + n + "_d"]) for n in ("gate", "up", "down")]
+              if S else None)
+        x, ids, rw = dev(inp["x"], np.uint16, np.int16), dev(inp["ids"], np.int32), dev(inp["route_w"], np.float32)
+        call = lambda p: moe.moe_ffn_fused(W[0], W[1], W[2], x, ids, rw, shared=sh, path=p)
+        row = {"shape": name, "wtype": w, "T": T, "slots": T * k,
+               "auto": moe.moe_select_path_typed(T, k, E, max(ne, nf), wt[w])}
+        for p, key in ((moe.PATH_GEMV, "gemv_us"), (moe.PATH_GEMM, "gemm_us")):
+            try:
+                moe.moe_select_path_typed(T, k, E, max(ne, nf), wt[w], path=p)
+            except moe.MoeError:
+                row[key] = None
+                continue
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.3:
+                for _ in range(10):
+                    call(p)
+                torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(50):
+                call(p)
+            b.record()
+            torch.cuda.synchronize()
+            row[key] = round(a.elapsed_time(b) * 1000 / 50, 1)
+        print("crossover: %s" % json.dumps(row), file=sys.stderr, flush=True)
+        res.append(row)
+        del W, sh, x, ids, rw
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "MoE FFN layer call, GEMV against grouped GEMM", "unit": "us", "n_gpus": 1,
+                      "data": "synthetic", "higher_is_better": False, "results": res}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -601,6 +656,9 @@ def main():
         return
     if args.config == "gather":
         bench_gather(args)
+        return
+    if args.config == "crossover":
+        bench_crossover(args)
         return
     import torch
     import indirect_expert_matmul_amd as moe
